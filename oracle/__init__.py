@@ -1,0 +1,167 @@
+"""Plain fp64 CPU oracle for Kimi Delta Attention (KDA).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may import this package.  The product path
+(the HIP library and its binding) never imports it, and it imports nothing
+from the product path.
+
+Two independent formulations live here:
+
+* :func:`recurrence` / :func:`decode_step` / :func:`segment_transition` call
+  the C file ``kda_oracle.c`` -- the per-token recurrence of
+  "Kimi K3.1 Pro 架构完全拆解" §3.1, evaluated in the u-form of
+  "Kimi K3 的架構" (hao.cnyes.com) §六, in fp64, threaded over
+  (sequence, head).  This is the oracle the GPU path is compared with.
+* :mod:`oracle.chunk_form` -- the chunkwise matrix form of "Kimi K3 的架構"
+  §六 written out in numpy fp64, used only to pin the recurrence (the two
+  must agree to rounding).
+
+Pins (tests marked ``not gpu``) tie the oracle to facts the pages and the
+mathematics fix: the literal product form, beta = 0 pure decay, linear
+attention, the delta rule's exact retrieval, the segment identity
+S = S~ + M S_in, and a hand-expanded dk = dv = 2 example.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+_lock = threading.Lock()
+
+
+def build(force: bool = True) -> str:
+    """Compile ``kda_oracle.c`` into ``libkda_oracle.so`` with gcc (no fast-math)."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-std=c99", "-D_POSIX_C_SOURCE=200809L",
+           "-o", tmp, _SRC, "-lm", "-lpthread"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lp = ctypes.POINTER(ctypes.c_int64)
+        i32 = ctypes.c_int32
+        lib.kda_oracle_recurrence.restype = i32
+        lib.kda_oracle_recurrence.argtypes = [i32, lp, i32, i32, i32, dp, dp, dp, dp, dp, dp,
+                                              dp, dp, dp, i32]
+        lib.kda_oracle_segment.restype = i32
+        lib.kda_oracle_segment.argtypes = [i32, lp, i32, i32, i32, dp, dp, dp, dp, dp, dp, i32]
+        lib.kda_oracle_threads.restype = i32
+        lib.kda_oracle_threads.argtypes = [i32]
+        _lib = lib
+        return lib
+
+
+def _f64(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # a torch tensor: widen exactly, on the host
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _cu(cu_seqlens, T):
+    if cu_seqlens is None:
+        cu = np.array([0, T], dtype=np.int64)
+    else:
+        if hasattr(cu_seqlens, "detach"):
+            cu_seqlens = cu_seqlens.detach().cpu().numpy()
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    if cu.ndim != 1 or cu.size < 1 or cu[0] != 0 or np.any(np.diff(cu) < 0) or cu[-1] != T:
+        raise ValueError("cu_seqlens must start at 0, be nondecreasing and end at T_total")
+    return cu
+
+
+def threads_used(threads: int = 0) -> int:
+    return int(_load().kda_oracle_threads(int(threads)))
+
+
+def recurrence(q, k, v, g, beta, cu_seqlens=None, initial_state=None, beta_write=None,
+               want_o=True, want_final=True, threads: int = 0):
+    """fp64 per-token KDA recurrence over packed sequences.
+
+    Shapes: q, k, g ``[T, H, dk]``; v ``[T, H, dv]``; beta ``[T, H]``;
+    initial_state ``[N, H, dk, dv]`` or None (zeros).  ``beta_write`` (test
+    only) separates the write coefficient from the erase coefficient.
+    Returns ``(o [T, H, dv] or None, final [N, H, dk, dv] or None)``.
+    """
+    k = _f64(k); v = _f64(v); g = _f64(g); beta = _f64(beta)
+    q = _f64(q) if want_o else None
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    if v.shape[:2] != (T, H) or g.shape != (T, H, dk) or beta.shape != (T, H):
+        raise ValueError("inconsistent shapes")
+    if q is not None and q.shape != (T, H, dk):
+        raise ValueError("q shape")
+    cu = _cu(cu_seqlens, T)
+    N = cu.size - 1
+    init = _f64(initial_state)
+    if init is not None and init.shape != (N, H, dk, dv):
+        raise ValueError("initial_state shape")
+    bw = _f64(beta_write)
+    if bw is not None and bw.shape != (T, H):
+        raise ValueError("beta_write shape")
+    o = np.zeros((T, H, dv), dtype=np.float64) if want_o else None
+    fin = np.zeros((N, H, dk, dv), dtype=np.float64) if want_final else None
+    rc = _load().kda_oracle_recurrence(
+        N, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, dk, dv,
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(bw), _ptr(init),
+        _ptr(o), _ptr(fin), int(threads))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_recurrence failed (%d)" % rc)
+    return o, fin
+
+
+def decode_step(state, q, k, v, g, beta, threads: int = 0):
+    """One decode step for N sequences: inputs ``[N, H, d]``, beta ``[N, H]``.
+
+    A decode step is the recurrence over N sequences of length one.
+    Returns ``(o [N, H, dv], new_state [N, H, dk, dv])``.
+    """
+    k = _f64(k)
+    N = k.shape[0]
+    cu = np.arange(N + 1, dtype=np.int64)
+    return recurrence(q, k, v, g, beta, cu_seqlens=cu, initial_state=state, threads=threads)
+
+
+def segment_transition(k, v, g, beta, cu_seglens=None, threads: int = 0):
+    """(M, S~) per packed segment: M ``[S, H, dk, dk]`` = M_T...M_1 by explicit
+    products; S~ ``[S, H, dk, dv]`` = state after the segment from S = 0."""
+    k = _f64(k); v = _f64(v); g = _f64(g); beta = _f64(beta)
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    cu = _cu(cu_seglens, T)
+    S = cu.size - 1
+    M = np.zeros((S, H, dk, dk), dtype=np.float64)
+    St = np.zeros((S, H, dk, dv), dtype=np.float64)
+    rc = _load().kda_oracle_segment(
+        S, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, dk, dv,
+        _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(M), _ptr(St), int(threads))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_segment failed (%d)" % rc)
+    return M, St

@@ -1,0 +1,220 @@
+"""Pins of the fp64 oracle to facts the pages and the mathematics fix.
+
+Each test ties the oracle to something other than itself:
+  * a hand-expanded 2 x 2 example (tests/golden/kda_2x2_hand.txt);
+  * the literal product form of the recurrence vs the oracle's u-form;
+  * an independent chunkwise formulation (oracle/chunk_form.py);
+  * closed forms: beta = 0 pure decay, plain causal linear attention,
+    delta-rule exact retrieval;
+  * the segment identity S = S~ + M S_in and its associativity;
+  * boundary semantics: resume, packing, decode == prefill.
+A plausible mistake (a dropped decay, a wrong sign, decay on columns instead
+of rows, the pre- instead of post-update state in o, exp2 for exp, an
+exclusive cumsum, M multiplied in the wrong order) fails at least one of them.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import chunk_form
+from gated_delta_rule_19_amd import workloads as wl
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def rand_inputs(T, H, dk, dv, seed, decay="config", unit=True):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((T, H, dk))
+    k = rng.standard_normal((T, H, dk))
+    if unit:
+        q /= np.linalg.norm(q, axis=-1, keepdims=True)
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, H, dv))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((T, H))))
+    z = 1.0 / (1.0 + np.exp(-rng.standard_normal((T, H, dk))))
+    g = {"config": -5.0 * z, "mild": -0.01 * z, "none": 0.0 * z}[decay]
+    return q, k, v, g, beta
+
+
+def rel(a, b):
+    return np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300)
+
+
+def load_golden(name):
+    vals = {}
+    with open(os.path.join(HERE, "golden", name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            parts = line.split()
+            vals[parts[0]] = np.array([float(x) for x in parts[1:]])
+    return vals
+
+
+def test_hand_expanded_2x2():
+    gd = load_golden("kda_2x2_hand.txt")
+    k = gd["k"].reshape(2, 1, 2)
+    v = gd["v"].reshape(2, 1, 2)
+    q = gd["q"].reshape(2, 1, 2)
+    beta = gd["beta"].reshape(2, 1)
+    g = np.log(gd["alpha"]).reshape(2, 1, 2)
+    o, fin = oracle.recurrence(q, k, v, g, beta)
+    np.testing.assert_allclose(o.reshape(-1), gd["o"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(fin.reshape(-1), gd["S_final"], rtol=0, atol=1e-14)
+    M, St = oracle.segment_transition(k, v, g, beta)
+    np.testing.assert_allclose(M.reshape(-1), gd["M"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(St.reshape(-1), gd["S_final"], rtol=0, atol=1e-14)
+
+
+def test_literal_product_form_matches_u_form():
+    T, H, dk, dv = 23, 2, 8, 6
+    q, k, v, g, beta = rand_inputs(T, H, dk, dv, 1, decay="mild")
+    S0 = np.random.default_rng(2).standard_normal((1, H, dk, dv))
+    o, fin = oracle.recurrence(q, k, v, g, beta, initial_state=S0)
+    for h in range(H):
+        S = S0[0, h].copy()
+        for t in range(T):
+            kt = k[t, h][:, None]
+            A = np.eye(dk) - beta[t, h] * (kt @ kt.T)
+            S = A @ np.diag(np.exp(g[t, h])) @ S + beta[t, h] * kt @ v[t, h][None, :]
+            np.testing.assert_allclose(o[t, h], S.T @ q[t, h], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(fin[0, h], S, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("C", [1, 4, 16, 64])
+@pytest.mark.parametrize("decay", ["config", "mild"])
+def test_chunk_form_equals_recurrence(C, decay):
+    lengths = [1, 70, 129, 0, 37]  # partial chunks, an empty sequence
+    cu = wl.cu_from_lengths(lengths)
+    T, H, dk, dv = int(cu[-1]), 2, 128, 128
+    q, k, v, g, beta = rand_inputs(T, H, dk, dv, 10 + C, decay=decay)
+    S0 = 0.1 * np.random.default_rng(3).standard_normal((len(lengths), H, dk, dv))
+    o1, f1 = oracle.recurrence(q, k, v, g, beta, cu_seqlens=cu, initial_state=S0)
+    o2, f2 = chunk_form.chunk_prefill(q, k, v, g, beta, cu_seqlens=cu, initial_state=S0,
+                                      chunk=C)
+    assert rel(o2, o1) < 1e-12
+    assert rel(f2, f1) < 1e-12
+
+
+def test_beta_zero_is_pure_per_channel_decay():
+    T, H, dk, dv = 40, 3, 16, 12
+    q, k, v, g, beta = rand_inputs(T, H, dk, dv, 4, decay="config")
+    beta[:] = 0.0
+    S0 = np.random.default_rng(5).standard_normal((1, H, dk, dv))
+    o, fin = oracle.recurrence(q, k, v, g, beta, initial_state=S0)
+    G = np.cumsum(g, axis=0)  # inclusive: the token's own decay applies before its output
+    for h in range(H):
+        expect_o = (np.exp(G[:, h, :]) * q[:, h, :]) @ S0[0, h]
+        # per token, relative to that token's own scale (it shrinks like e^{-2.5 t})
+        err = np.max(np.abs(o[:, h] - expect_o), axis=1)
+        assert np.all(err <= 1e-12 * np.max(np.abs(expect_o), axis=1))
+        np.testing.assert_allclose(fin[0, h], np.exp(G[-1, h])[:, None] * S0[0, h],
+                                   rtol=1e-12, atol=1e-300)
+
+
+def test_no_erase_unit_write_no_decay_is_linear_attention():
+    T, H, dk, dv = 50, 2, 16, 8
+    q, k, v, g, _ = rand_inputs(T, H, dk, dv, 6, decay="none", unit=False)
+    erase = np.zeros((T, H))
+    write = np.ones((T, H))
+    S0 = np.random.default_rng(7).standard_normal((1, H, dk, dv))
+    o, fin = oracle.recurrence(q, k, v, g, erase, initial_state=S0, beta_write=write)
+    for h in range(H):
+        Q, K, V = q[:, h], k[:, h], v[:, h]
+        expect = np.tril(Q @ K.T) @ V + Q @ S0[0, h]  # diagonal kept: post-update state
+        np.testing.assert_allclose(o[:, h], expect, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(fin[0, h], S0[0, h] + K.T @ V, rtol=1e-12, atol=1e-12)
+
+
+def test_delta_rule_unit_beta_retrieves_current_value():
+    # beta = 1 and a unit key: S_t^T k_t = v_t right after step t, whatever alpha is.
+    T, H, dk, dv = 30, 2, 32, 16
+    q, k, v, g, beta = rand_inputs(T, H, dk, dv, 8, decay="config")
+    beta[:] = 1.0
+    S0 = np.random.default_rng(9).standard_normal((1, H, dk, dv))
+    o, _ = oracle.recurrence(k, k, v, g, beta, initial_state=S0)  # q = k reads S_t^T k_t
+    np.testing.assert_allclose(o, v, rtol=0, atol=1e-12)
+
+
+def test_delta_rule_orthonormal_keys_store_all_values():
+    # alpha = 1, beta = 1, n <= dk orthonormal keys: S_n^T k_t = v_t for every t.
+    dk, dv, n = 64, 24, 64
+    rng = np.random.default_rng(11)
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    K = Qm[:, :n].T.copy()  # rows are orthonormal keys
+    V = rng.standard_normal((n, dv))
+    k = K[:, None, :]
+    v = V[:, None, :]
+    g = np.zeros((n, 1, dk))
+    beta = np.ones((n, 1))
+    _, fin = oracle.recurrence(k, k, v, g, beta)
+    np.testing.assert_allclose(K @ fin[0, 0], V, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("decay", ["config", "mild"])
+def test_segment_identity_and_associativity(decay):
+    T, H, dk, dv = 45, 2, 16, 12
+    q, k, v, g, beta = rand_inputs(T, H, dk, dv, 12, decay=decay)
+    cu = np.array([0, 17, 17, 45])  # two segments around an empty one
+    M, St = oracle.segment_transition(k, v, g, beta, cu_seglens=cu)
+    Sin = np.random.default_rng(13).standard_normal((H, dk, dv))
+    for s in range(3):
+        a, b = cu[s], cu[s + 1]
+        _, fin = oracle.recurrence(q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b],
+                                   initial_state=Sin[None], want_o=False)
+        for h in range(H):
+            np.testing.assert_allclose(fin[0, h], St[s, h] + M[s, h] @ Sin[h], rtol=1e-11,
+                                       atol=1e-13)
+    assert np.allclose(M[1], np.eye(dk)[None]) and np.all(St[1] == 0)
+    Mw, Sw = oracle.segment_transition(k, v, g, beta)  # the whole range as one segment
+    for h in range(H):
+        np.testing.assert_allclose(Mw[0, h], M[2, h] @ M[0, h], rtol=1e-11, atol=1e-14)
+        np.testing.assert_allclose(Sw[0, h], St[2, h] + M[2, h] @ St[0, h], rtol=1e-11,
+                                   atol=1e-13)
+
+
+def test_resume_packing_and_decode_equivalence():
+    lengths = [33, 64, 7]
+    cu = wl.cu_from_lengths(lengths)
+    T, H, dk, dv = int(cu[-1]), 2, 16, 16
+    q, k, v, g, beta = rand_inputs(T, H, dk, dv, 14, decay="mild")
+    S0 = np.random.default_rng(15).standard_normal((3, H, dk, dv))
+    o, fin = oracle.recurrence(q, k, v, g, beta, cu_seqlens=cu, initial_state=S0)
+    for n in range(3):  # packed == separate
+        a, b = cu[n], cu[n + 1]
+        o1, f1 = oracle.recurrence(q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b],
+                                   initial_state=S0[n:n + 1])
+        assert np.array_equal(o1, o[a:b]) and np.array_equal(f1[0], fin[n])
+    a, b, tau = cu[1], cu[2], 20  # resume at tau
+    _, fa = oracle.recurrence(q[a:a + tau], k[a:a + tau], v[a:a + tau], g[a:a + tau],
+                              beta[a:a + tau], initial_state=S0[1:2])
+    ob, fb = oracle.recurrence(q[a + tau:b], k[a + tau:b], v[a + tau:b], g[a + tau:b],
+                               beta[a + tau:b], initial_state=fa)
+    assert rel(ob, o[a + tau:b]) < 1e-13 and rel(fb[0], fin[1]) < 1e-13
+    state = S0[1:2].copy()  # token-by-token decode == prefill
+    for t in range(a, b):
+        ot, state = oracle.decode_step(state, q[t:t + 1], k[t:t + 1], v[t:t + 1], g[t:t + 1],
+                                       beta[t:t + 1])
+        assert rel(ot[0], o[t]) < 1e-13
+    assert rel(state[0], fin[1]) < 1e-13
+
+
+def test_zero_length_sequences_copy_state():
+    H, dk, dv = 2, 8, 8
+    q, k, v, g, beta = rand_inputs(5, H, dk, dv, 16)
+    cu = np.array([0, 0, 5, 5])
+    S0 = np.random.default_rng(17).standard_normal((3, H, dk, dv))
+    _, fin = oracle.recurrence(q, k, v, g, beta, cu_seqlens=cu, initial_state=S0)
+    assert np.array_equal(fin[0], S0[0]) and np.array_equal(fin[2], S0[2])
+
+
+def test_decay_lower_bound_range():
+    # With g >= -5 a 16-token cumulative log-decay stays above -80, whose
+    # reciprocal factor e^80 is finite in fp32/bf16 ("Kimi K3.1 Pro 架构完全拆解"
+    # §3.2; the orkas.ai page's lower-bound section).
+    assert 16 * wl.G_MIN == -80.0
+    assert np.isfinite(np.float32(np.exp(80.0)))
+    assert np.exp(80.0) < 3.38e38
