@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = one ``kda_chunk_prefill`` call over the whole batch of the
+one-layer workload (B=1, T=8192, H=96, dk=dv=128, bf16 inputs, fp32 state,
+chunk 64), inputs already resident in HBM.  ``value`` is prefill tokens/s.
+
+The same run also times the in-place fp32 decode step (256 sequences x 96
+heads, 64 consecutive steps) and reports its state bandwidth, and times the
+fp64 CPU oracle on a bounded sample of the prefill workload as a baseline.
+
+Roofline (prefill): model FLOPs per chunk-head 12C^3 + 8C^2D + 6CD^2
+("Kimi K3 的架構" (hao.cnyes.com), complexity analysis of §六) over the
+measured duration of the prefill launch sequence, against the bf16 dense MFMA
+peak of MI355X (2.5 PFLOP/s).  Decode: 8 D^2 bytes of fp32 state per head per
+token over the measured step time, against 8 TB/s HBM.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s (H=96,D=128) + decode state GB/s, % of MFMA/HBM peak"
+C, D = 64, 128
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+FLOP_PER_CHUNK_HEAD = 12 * C ** 3 + 8 * C ** 2 * D + 6 * C * D ** 2  # 13,631,488
+DECODE_BYTES_PER_HEAD_TOKEN = 8 * D * D                              # fp32 state read + write
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_19_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def time_prefill(kda, wl, name, steps, warmup, split_hint, dev):
+    import torch
+    w = wl.WORKLOADS[name]
+    d = wl.prefill_case(w, device=dev)
+    cu = d["cu"]
+    N, H = len(w.lengths), w.H
+    T = int(cu[-1])
+    o = torch.empty((T, H, D), dtype=w.dtype, device=dev)
+    fin = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    nbytes = kda.prefill_workspace_size(cu, H, w.dtype, split_hint)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu,
+                          initial_state=d["init"], split_hint=split_hint, o=o,
+                          final_state=fin, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    ms = sum(per) / steps
+    chunk_heads = sum((L + C - 1) // C for L in w.lengths) * H
+    flops = chunk_heads * FLOP_PER_CHUNK_HEAD
+    tflops = flops / (ms * 1e-3) / 1e12
+    res = {
+        "workload": name, "T": T, "H": H, "N": N, "dtype": str(w.dtype).replace("torch.", ""),
+        "ms_per_step": ms, "ms_min": min(per), "wall_ms_per_step": wall / steps * 1e3,
+        "tokens_per_s": T / (ms * 1e-3), "chunk_heads": chunk_heads, "model_flops": flops,
+        "tflops": tflops, "mfma_frac": tflops / PEAK_BF16_TFLOPS,
+        "segments_auto": [kda.plan_num_segments(L, N, H, split_hint) for L in w.lengths[:1]],
+    }
+    del d, o, fin, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def time_decode(kda, wl, dev, steps_block=64, warmup_blocks=1):
+    import torch
+    w = wl.WORKLOADS["decode_f32_N256_H96_x64"]
+    d = wl.decode_case(w, device=dev)
+    N, H = w.lengths[0], w.H
+    state = d["state"]
+    o = torch.empty((N, H, D), dtype=w.dtype, device=dev)
+
+    def block():
+        for s in range(w.steps):
+            kda.decode_step(state, d["q"][s], d["k"][s], d["v"][s], d["g"][s], d["beta"][s],
+                            o=o)
+
+    for _ in range(warmup_blocks):
+        block()
+    torch.cuda.synchronize(dev)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    block()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1)
+    us_step = ms * 1e3 / w.steps
+    gbs = DECODE_BYTES_PER_HEAD_TOKEN * N * H / (us_step * 1e-6) / 1e9
+    del d, state, o
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "us_per_step": us_step, "state_GB_per_s": gbs,
+            "hbm_frac": gbs / PEAK_HBM_GBS, "tokens_per_s": N / (us_step * 1e-6),
+            "model_bytes_per_step": DECODE_BYTES_PER_HEAD_TOKEN * N * H}
+
+
+def cpu_baseline(wl, name, budget_s=12.0):
+    """The fp64 oracle, as it stands, on whole heads of the workload until the
+    time budget is spent.  Returns tokens/s scaled to the full workload."""
+    import torch
+    import oracle
+    w = wl.WORKLOADS[name]
+    d = wl.prefill_case(w, device="cpu")
+    cu = d["cu"]
+    T, H = int(cu[-1]), w.H
+    threads = oracle.default_threads()
+    heads_done, compute_s, copy_s = 0, 0.0, 0.0
+    while heads_done < H and compute_s < budget_s:
+        h1 = min(H, heads_done + threads)
+        t0 = time.perf_counter()
+        sl = {n: d[n][:, heads_done:h1].double().numpy().copy()
+              for n in ("q", "k", "v", "g", "beta")}
+        init = None if d["init"] is None else d["init"][:, heads_done:h1].double().numpy()
+        t1 = time.perf_counter()
+        oracle.recurrence(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], cu_seqlens=cu,
+                          initial_state=init, threads=threads)
+        t2 = time.perf_counter()
+        copy_s += t1 - t0
+        compute_s += t2 - t1
+        heads_done = h1
+    del d
+    tok_s = T * heads_done / H / compute_s
+    return {"value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%s: %d of %d heads, all %d tokens, fp64 per-token recurrence; "
+                      "compute %.1f s (host copies %.1f s, not counted)"
+                      % (name, heads_done, H, T, compute_s, copy_s)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_bf16_T8192_H96")
+    ap.add_argument("--split", type=int, default=0, help="split_hint (0 = automatic)")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all", action="store_true",
+                    help="also time the long-context and packed-resume prefill workloads")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_19_amd as kda
+    from gated_delta_rule_19_amd import workloads as wl
+
+    kda.load()
+    dev = torch.device("cuda:0")
+    main_res = time_prefill(kda, wl, args.workload, args.steps, args.warmup, args.split, dev)
+    print("prefill %s: %.3f ms/step, %.3g tokens/s, %.1f TFLOP/s (%.1f%% of bf16 MFMA peak)"
+          % (args.workload, main_res["ms_per_step"], main_res["tokens_per_s"],
+             main_res["tflops"], 100 * main_res["mfma_frac"]), file=sys.stderr, flush=True)
+    extra = {}
+    if args.all:
+        for name in ("prefill_bf16_T131072_H12", "prefill_bf16_varlen64_H96_resume",
+                     "prefill_f32_T256_H2"):
+            if name == args.workload:
+                continue
+            r = time_prefill(kda, wl, name, max(3, args.steps // 2), 1, 0, dev)
+            extra[name] = r
+            print("prefill %s: %.3f ms/step, %.3g tokens/s, %.1f%% MFMA"
+                  % (name, r["ms_per_step"], r["tokens_per_s"], 100 * r["mfma_frac"]),
+                  file=sys.stderr, flush=True)
+    dec = None
+    if not args.no_decode:
+        dec = time_decode(kda, wl, dev)
+        print("decode: %.1f us/step, %.0f GB/s state (%.1f%% of HBM peak)"
+              % (dec["us_per_step"], dec["state_GB_per_s"], 100 * dec["hbm_frac"]),
+              file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.workload)
+        print("cpu oracle: %.3g tokens/s on %d threads" % (cpu["value"], cpu["cores"]),
+              file=sys.stderr, flush=True)
+
+    w = wl.WORKLOADS[args.workload]
+    traffic = stored_traffic(args.workload)
+    line = {
+        "metric": METRIC,
+        "value": main_res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": len(w.lengths),
+                   "seq_len": int(sum(w.lengths)), "heads": w.H, "head_dim": D, "chunk": C,
+                   "state": "fp32", "split_hint": args.split},
+        "roofline": {"bound": "mfma", "achieved": main_res["tflops"],
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": main_res["mfma_frac"], "traffic": traffic,
+                     "kernel": "prefill launch sequence (chunk prep + state chain)"},
+        "cpu_baseline": cpu,
+        "prefill": main_res,
+        "decode": dec,
+        "extra": extra or None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,259 @@
+"""ctypes binding of ``libkda.so`` -- argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI
+declared in ``include/kda.h``; this module only checks tensor shapes, allocates
+outputs and the workspace with torch, and passes raw pointers plus torch's
+current HIP stream.  There is no fallback: if the library is missing, every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import numpy as np
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+
+KDA_OK = 0
+KDA_ERR_INVALID_ARG = -1
+KDA_ERR_UNSUPPORTED = -2
+KDA_ERR_WORKSPACE = -3
+KDA_ERR_HIP = -4
+KDA_F32 = 0
+KDA_BF16 = 1
+CHUNK = 64
+HEAD_DIM = 128
+
+# Every symbol include/kda.h declares.
+EXPORTED = (
+    "kda_status_string",
+    "kda_version",
+    "kda_plan_num_segments",
+    "kda_chunk_prefill_workspace_size",
+    "kda_chunk_prefill",
+    "kda_decode_step",
+    "kda_segment_transition_workspace_size",
+    "kda_segment_transition",
+)
+
+_lib = None
+_lock = threading.Lock()
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (where, status_string(status), status))
+
+
+def load():
+    """Load ``libkda.so`` (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libkda.so is not built (%s); run __graft_entry__.build()"
+                               % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        lp = ctypes.POINTER(ctypes.c_int64)
+        lib.kda_status_string.restype = ctypes.c_char_p
+        lib.kda_status_string.argtypes = [i32]
+        lib.kda_version.restype = i32
+        lib.kda_version.argtypes = []
+        lib.kda_plan_num_segments.restype = i32
+        lib.kda_plan_num_segments.argtypes = [i64, i32, i32, i32]
+        lib.kda_chunk_prefill_workspace_size.restype = sz
+        lib.kda_chunk_prefill_workspace_size.argtypes = [i32, lp, i32, i32, i32, i32, i32]
+        lib.kda_chunk_prefill.restype = i32
+        lib.kda_chunk_prefill.argtypes = [i32, lp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                          vp, vp, i32, vp, sz, vp]
+        lib.kda_decode_step.restype = i32
+        lib.kda_decode_step.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.kda_segment_transition_workspace_size.restype = sz
+        lib.kda_segment_transition_workspace_size.argtypes = [i32, lp, i32, i32, i32, i32]
+        lib.kda_segment_transition.restype = i32
+        lib.kda_segment_transition.argtypes = [i32, lp, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                               vp, vp, sz, vp]
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load().kda_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(load().kda_version())
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return KDA_F32
+    if t == torch.bfloat16:
+        return KDA_BF16
+    raise TypeError("KDA inputs must be float32 or bfloat16, got %s" % t)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _host_cu(cu, T: int) -> np.ndarray:
+    if cu is None:
+        return np.array([0, T], dtype=np.int64)
+    if isinstance(cu, torch.Tensor):
+        cu = cu.detach().cpu().numpy()
+    cu = np.ascontiguousarray(np.asarray(cu, dtype=np.int64))
+    if cu.ndim != 1 or cu.size < 1:
+        raise ValueError("cu_seqlens must be a 1-D sequence of N+1 offsets")
+    return cu
+
+
+def _cu_ptr(cu: np.ndarray):
+    return cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def _check_device(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("KDA tensors must live on a HIP device")
+        if not t.is_contiguous():
+            raise ValueError("KDA tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all KDA tensors must be on one device")
+    return dev
+
+
+def plan_num_segments(seq_len: int, num_seqs: int, H: int, split_hint: int = 0) -> int:
+    r = int(load().kda_plan_num_segments(int(seq_len), int(num_seqs), int(H), int(split_hint)))
+    if r < 0:
+        raise KdaError(r, "kda_plan_num_segments")
+    return r
+
+
+def prefill_workspace_size(cu_seqlens, H: int, dtype: torch.dtype, split_hint: int = 0) -> int:
+    cu = _host_cu(cu_seqlens, 0)
+    return int(load().kda_chunk_prefill_workspace_size(cu.size - 1, _cu_ptr(cu), H, HEAD_DIM,
+                                                       HEAD_DIM, _dtype_code(dtype),
+                                                       split_hint))
+
+
+def chunk_prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None,
+                  output_final_state: bool = True, split_hint: int = 0, o=None,
+                  final_state=None, workspace=None):
+    """Chunked KDA prefill (``kda_chunk_prefill``).
+
+    q, k, g: ``[T, H, 128]`` (or ``[B, T, H, 128]`` for B fixed-length
+    sequences when ``cu_seqlens`` is None); v likewise; beta ``[T, H]`` or
+    ``[B, T, H]``.  initial_state ``[N, H, 128, 128]`` fp32 or None.
+    Returns ``(o, final_state or None)``.  ``final_state`` may be passed in
+    (it may be ``initial_state`` itself for an in-place resume).
+    """
+    lib = load()
+    if q.dim() == 4:
+        if cu_seqlens is not None and q.shape[0] != 1:
+            raise ValueError("cu_seqlens requires B == 1")
+        B, T = q.shape[0], q.shape[1]
+        q, k, v, g = (x.reshape(B * T, *x.shape[2:]) for x in (q, k, v, g))
+        beta = beta.reshape(B * T, beta.shape[-1])
+        if cu_seqlens is None:
+            cu_seqlens = np.arange(B + 1, dtype=np.int64) * T
+    T, H, dk = k.shape
+    dv = v.shape[-1]
+    if q.shape != (T, H, dk) or g.shape != (T, H, dk) or v.shape[:2] != (T, H) \
+            or beta.shape != (T, H):
+        raise ValueError("inconsistent q/k/v/g/beta shapes")
+    dt = q.dtype
+    for x in (k, v, g, beta):
+        if x.dtype != dt:
+            raise TypeError("q, k, v, g and beta must share one dtype")
+    cu = _host_cu(cu_seqlens, T)
+    N = cu.size - 1
+    if cu[-1] != T:
+        raise ValueError("cu_seqlens[-1] must equal the number of tokens")
+    dev = _check_device(q, k, v, g, beta, initial_state, final_state, o)
+    if initial_state is not None and (initial_state.dtype != torch.float32
+                                      or initial_state.shape != (N, H, dk, dv)):
+        raise ValueError("initial_state must be fp32 [N, H, dk, dv]")
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=dt, device=dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    code = _dtype_code(dt)
+    nbytes = int(lib.kda_chunk_prefill_workspace_size(N, _cu_ptr(cu), H, dk, dv, code,
+                                                      split_hint))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    st = lib.kda_chunk_prefill(N, _cu_ptr(cu), H, dk, dv, code, _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
+                               _ptr(final_state), int(split_hint), _ptr(workspace),
+                               workspace.numel(), _stream_ptr(dev))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_chunk_prefill")
+    return o, final_state
+
+
+def decode_step(state, q, k, v, g, beta, o=None):
+    """One in-place decode step (``kda_decode_step``): inputs ``[N, H, 128]``,
+    beta ``[N, H]``, state ``[N, H, 128, 128]`` fp32 (updated).  Returns o."""
+    lib = load()
+    N, H, dk = k.shape
+    dv = v.shape[-1]
+    if state.dtype != torch.float32 or state.shape != (N, H, dk, dv):
+        raise ValueError("state must be fp32 [N, H, dk, dv]")
+    dt = q.dtype
+    for x in (k, v, g, beta):
+        if x.dtype != dt:
+            raise TypeError("q, k, v, g and beta must share one dtype")
+    dev = _check_device(state, q, k, v, g, beta, o)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=dt, device=dev)
+    st = lib.kda_decode_step(N, H, dk, dv, _dtype_code(dt), _ptr(q), _ptr(k), _ptr(v),
+                             _ptr(g), _ptr(beta), _ptr(state), _ptr(o), _stream_ptr(dev))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_decode_step")
+    return o
+
+
+def segment_transition(k, v, g, beta, cu_seglens=None, M=None, S_tilde=None, workspace=None):
+    """(M, S~) per packed segment (``kda_segment_transition``)."""
+    lib = load()
+    T, H, dk = k.shape
+    dv = v.shape[-1]
+    dt = k.dtype
+    for x in (v, g, beta):
+        if x.dtype != dt:
+            raise TypeError("k, v, g and beta must share one dtype")
+    cu = _host_cu(cu_seglens, T)
+    S = cu.size - 1
+    if cu[-1] != T:
+        raise ValueError("cu_seglens[-1] must equal the number of tokens")
+    dev = _check_device(k, v, g, beta, M, S_tilde)
+    if M is None:
+        M = torch.empty((S, H, dk, dk), dtype=torch.float32, device=dev)
+    if S_tilde is None:
+        S_tilde = torch.empty((S, H, dk, dv), dtype=torch.float32, device=dev)
+    code = _dtype_code(dt)
+    nbytes = int(lib.kda_segment_transition_workspace_size(S, _cu_ptr(cu), H, dk, dv, code))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    st = lib.kda_segment_transition(S, _cu_ptr(cu), H, dk, dv, code, _ptr(k), _ptr(v),
+                                    _ptr(g), _ptr(beta), _ptr(M), _ptr(S_tilde),
+                                    _ptr(workspace), workspace.numel(), _stream_ptr(dev))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_segment_transition")
+    return M, S_tilde

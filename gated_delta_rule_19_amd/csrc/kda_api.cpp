@@ -1,0 +1,433 @@
+// Host side of the KDA C ABI: argument validation, the sequence-split planner,
+// workspace layout, schedule upload and kernel launches.
+//
+// The planner follows "部署 Kimi K3：从 KDA Kernel 到 Fleet 调度", §1.2 (an
+// intra-device context-parallel planner: cut a long sequence into segments,
+// compute each segment's transition without knowing its entry state, then
+// recover every entry state exactly) and §二 (the (M, S~) decomposition
+// S = S~ + M S_in and its associative composition).  Work that would leave
+// the device mostly idle -- a few heads of one long sequence -- is cut into
+// chunk-aligned segments:
+//   1. segment pass : for every segment but the last, its (M, S~) pair, by
+//                     running the state-carrying kernel over [S~ | M] from
+//                     [0 | I] with values [V | 0];
+//   2. scan         : Sin[0] = S_0, Sin[j+1] = S~_j + M_j Sin[j];
+//   3. replay       : every segment from its true entry state, writing o.
+#include "kda.h"
+#include "kda_internal.h"
+
+#include <algorithm>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+using namespace kda;
+
+namespace {
+
+// Automatic split policy: split only when the unsplit state-carrying work
+// has fewer than kAutoMinChains workgroups, then aim for kAutoSegments
+// segments of at least kAutoMinSegChunks chunks each.
+constexpr int64_t kAutoMinChains = 128;
+constexpr int64_t kAutoSegments = 64;
+constexpr int64_t kAutoMinSegChunks = 4;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned_elt(const void *p, kda_dtype dt) {
+  return ((uintptr_t)p & (dt == KDA_BF16 ? 1u : 3u)) == 0;
+}
+
+int64_t plan_nseg(int64_t len, int32_t num_seqs, int32_t H, int32_t split_hint) {
+  if (len <= 0)
+    return 1;
+  const int64_t nch = (len + kC - 1) / kC;
+  if (split_hint == 1)
+    return 1;
+  if (split_hint > 1)
+    return std::min<int64_t>(split_hint, nch);
+  const int64_t chains = (int64_t)num_seqs * H * (kD / kBV);
+  if (chains >= kAutoMinChains)
+    return 1;
+  return std::max<int64_t>(1, std::min<int64_t>(kAutoSegments, nch / kAutoMinSegChunks));
+}
+
+// The schedule for one call, built on the host.
+struct Plan {
+  std::vector<ChunkDesc> chunks;
+  std::vector<ChainDesc> chains;    // prefill / replay (width dv, writes o)
+  std::vector<ChainDesc> segchains; // segment pass (width dk + dv)
+  std::vector<ScanDesc> scans;
+  int64_t npairs = 0, nsin = 0;
+  // workspace layout
+  size_t off_chunks = 0, off_chains = 0, off_seg = 0, off_scan = 0, table_bytes = 0;
+  size_t off_rec = 0, off_M = 0, off_St = 0, off_Sin = 0, total = 0;
+};
+
+void layout(Plan &p, int32_t H, size_t es) {
+  size_t o = 0;
+  p.off_chunks = o;
+  o = align_up(o + p.chunks.size() * sizeof(ChunkDesc));
+  p.off_chains = o;
+  o = align_up(o + p.chains.size() * sizeof(ChainDesc));
+  p.off_seg = o;
+  o = align_up(o + p.segchains.size() * sizeof(ChainDesc));
+  p.off_scan = o;
+  o = align_up(o + p.scans.size() * sizeof(ScanDesc));
+  p.table_bytes = o;
+  p.off_rec = o;
+  o = align_up(o + p.chunks.size() * (size_t)H * k1_record_bytes(es));
+  const size_t mat = (size_t)kD * kD * sizeof(float);
+  p.off_M = o;
+  o = align_up(o + (size_t)p.npairs * H * mat);
+  p.off_St = o;
+  o = align_up(o + (size_t)p.npairs * H * mat);
+  p.off_Sin = o;
+  o = align_up(o + (size_t)p.nsin * H * mat);
+  p.total = o;
+}
+
+// Prefill schedule.  Returns false on bad cu_seqlens.
+bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_hint,
+                        bool has_init, bool has_final, size_t es, Plan &p) {
+  if (!cu || cu[0] != 0)
+    return false;
+  for (int32_t n = 0; n < N; ++n)
+    if (cu[n + 1] < cu[n])
+      return false;
+  for (int32_t n = 0; n < N; ++n) {
+    const int64_t len = cu[n + 1] - cu[n];
+    const int64_t nch = (len + kC - 1) / kC;
+    const int64_t c0 = (int64_t)p.chunks.size();
+    for (int64_t i = 0; i < nch; ++i) {
+      ChunkDesc d;
+      d.tok0 = cu[n] + i * kC;
+      d.len = (int32_t)std::min<int64_t>(kC, cu[n + 1] - d.tok0);
+      d.seq = n;
+      p.chunks.push_back(d);
+    }
+    const int64_t nseg = plan_nseg(len, N, H, split_hint);
+    if (nseg <= 1) {
+      p.chains.push_back(ChainDesc{(int32_t)c0, (int32_t)nch, has_init ? n : -1,
+                                   has_final ? n : -1});
+      continue;
+    }
+    const int64_t q = nch / nseg, r = nch % nseg;
+    const int64_t pair0 = p.npairs, sin0 = p.nsin;
+    for (int64_t j = 0; j < nseg; ++j) {
+      const int64_t s0 = c0 + j * q + std::min(j, r);
+      const int64_t cnt = q + (j < r ? 1 : 0);
+      if (j + 1 < nseg)
+        p.segchains.push_back(ChainDesc{(int32_t)s0, (int32_t)cnt, -1, (int32_t)(pair0 + j)});
+      const bool last = j + 1 == nseg;
+      p.chains.push_back(ChainDesc{(int32_t)s0, (int32_t)cnt, (int32_t)(-2 - (sin0 + j)),
+                                   (last && has_final) ? n : -1});
+    }
+    p.scans.push_back(ScanDesc{(int32_t)pair0, (int32_t)nseg, (int32_t)sin0,
+                               has_init ? n : -1});
+    p.npairs += nseg - 1;
+    p.nsin += nseg;
+  }
+  // longest chains first, so the tail of the launch is short work
+  auto longer = [](const ChainDesc &a, const ChainDesc &b) { return a.nchunks > b.nchunks; };
+  std::stable_sort(p.chains.begin(), p.chains.end(), longer);
+  std::stable_sort(p.segchains.begin(), p.segchains.end(), longer);
+  layout(p, H, es);
+  return true;
+}
+
+// Segment-transition schedule: every segment is one segment-pass chain whose
+// exit pair goes to the caller's (S_tilde, M) at the segment's index.
+bool build_segment_plan(int32_t S, const int64_t *cu, int32_t H, size_t es, Plan &p) {
+  if (!cu || cu[0] != 0)
+    return false;
+  for (int32_t s = 0; s < S; ++s)
+    if (cu[s + 1] < cu[s])
+      return false;
+  for (int32_t s = 0; s < S; ++s) {
+    const int64_t len = cu[s + 1] - cu[s];
+    const int64_t nch = (len + kC - 1) / kC;
+    const int64_t c0 = (int64_t)p.chunks.size();
+    for (int64_t i = 0; i < nch; ++i) {
+      ChunkDesc d;
+      d.tok0 = cu[s] + i * kC;
+      d.len = (int32_t)std::min<int64_t>(kC, cu[s + 1] - d.tok0);
+      d.seq = s;
+      p.chunks.push_back(d);
+    }
+    p.segchains.push_back(ChainDesc{(int32_t)c0, (int32_t)nch, -1, s});
+  }
+  std::stable_sort(p.segchains.begin(), p.segchains.end(),
+                   [](const ChainDesc &a, const ChainDesc &b) { return a.nchunks > b.nchunks; });
+  layout(p, H, es);
+  return true;
+}
+
+size_t elt_size(kda_dtype dt) { return dt == KDA_BF16 ? 2 : 4; }
+
+// Limits that keep every index inside the kernels' int32 / grid ranges.
+bool plan_fits(const Plan &p, int32_t H) {
+  const int64_t lim = (int64_t)1 << 30;
+  return (int64_t)p.chunks.size() < lim && (int64_t)p.chains.size() < lim &&
+         (int64_t)p.segchains.size() < lim && (int64_t)p.scans.size() < lim &&
+         H <= 65535 && p.npairs < lim && p.nsin < lim;
+}
+
+// ---- pinned staging for the schedule upload --------------------------------
+// A pinned host buffer may only be reused once the copy that read it has
+// finished; each buffer carries an event recorded right after its copy.
+struct Staging {
+  void *host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  int device = -1;
+  bool in_use = false;
+};
+std::mutex g_staging_mu;
+std::vector<Staging *> g_staging;
+
+Staging *staging_acquire(size_t bytes, int device) {
+  std::lock_guard<std::mutex> lk(g_staging_mu);
+  for (Staging *s : g_staging) {
+    if (s->in_use || s->device != device || s->cap < bytes)
+      continue;
+    if (hipEventQuery(s->ev) != hipSuccess)
+      continue;
+    s->in_use = true;
+    return s;
+  }
+  Staging *s = new Staging();
+  s->device = device;
+  s->cap = std::max<size_t>(bytes, 64 * 1024);
+  if (hipHostMalloc(&s->host, s->cap, hipHostMallocDefault) != hipSuccess) {
+    delete s;
+    return nullptr;
+  }
+  if (hipEventCreateWithFlags(&s->ev, hipEventDisableTiming) != hipSuccess) {
+    (void)hipHostFree(s->host);
+    delete s;
+    return nullptr;
+  }
+  s->in_use = true;
+  g_staging.push_back(s);
+  return s;
+}
+
+void staging_release(Staging *s) {
+  std::lock_guard<std::mutex> lk(g_staging_mu);
+  s->in_use = false;
+}
+
+// Copy the plan's tables into the workspace on `stream`.
+hipError_t upload_tables(const Plan &p, void *ws, hipStream_t stream) {
+  if (p.table_bytes == 0)
+    return hipSuccess;
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess)
+    return e;
+  Staging *st = staging_acquire(p.table_bytes, device);
+  if (!st)
+    return hipErrorOutOfMemory;
+  uint8_t *h = (uint8_t *)st->host;
+  std::memset(h, 0, p.table_bytes);
+  if (!p.chunks.empty())
+    std::memcpy(h + p.off_chunks, p.chunks.data(), p.chunks.size() * sizeof(ChunkDesc));
+  if (!p.chains.empty())
+    std::memcpy(h + p.off_chains, p.chains.data(), p.chains.size() * sizeof(ChainDesc));
+  if (!p.segchains.empty())
+    std::memcpy(h + p.off_seg, p.segchains.data(), p.segchains.size() * sizeof(ChainDesc));
+  if (!p.scans.empty())
+    std::memcpy(h + p.off_scan, p.scans.data(), p.scans.size() * sizeof(ScanDesc));
+  e = hipMemcpyAsync(ws, h, p.table_bytes, hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess)
+    e = hipEventRecord(st->ev, stream);
+  staging_release(st);
+  return e;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *kda_status_string(kda_status s) {
+  switch (s) {
+  case KDA_OK:
+    return "KDA_OK";
+  case KDA_ERR_INVALID_ARG:
+    return "KDA_ERR_INVALID_ARG";
+  case KDA_ERR_UNSUPPORTED:
+    return "KDA_ERR_UNSUPPORTED";
+  case KDA_ERR_WORKSPACE:
+    return "KDA_ERR_WORKSPACE";
+  case KDA_ERR_HIP:
+    return "KDA_ERR_HIP";
+  default:
+    return "KDA_ERR_UNKNOWN";
+  }
+}
+
+int32_t kda_version(void) { return 100; }
+
+int32_t kda_plan_num_segments(int64_t seq_len, int32_t num_seqs, int32_t H, int32_t split_hint) {
+  if (num_seqs < 0 || H < 1 || split_hint < 0)
+    return KDA_ERR_INVALID_ARG;
+  const int64_t n = plan_nseg(seq_len, num_seqs, H, split_hint);
+  return (int32_t)std::min<int64_t>(n, INT32_MAX);
+}
+
+size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, const int64_t *cu_seqlens_host,
+                                        int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
+                                        int32_t split_hint) {
+  if (num_seqs < 0 || H < 1 || dk != kD || dv != kD || (dt != KDA_F32 && dt != KDA_BF16) ||
+      split_hint < 0)
+    return 0;
+  Plan p;
+  // has_init / has_final do not change the layout
+  if (!build_prefill_plan(num_seqs, cu_seqlens_host, H, split_hint, false, true, elt_size(dt),
+                          p))
+    return 0;
+  return p.total;
+}
+
+kda_status kda_chunk_prefill(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_t H,
+                             int32_t dk, int32_t dv, kda_dtype dt, const void *q, const void *k,
+                             const void *v, const void *g, const void *beta,
+                             const float *initial_state, void *o, float *final_state,
+                             int32_t split_hint, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+  if (dk != kD || dv != kD || (dt != KDA_F32 && dt != KDA_BF16))
+    return KDA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || H < 1 || split_hint < 0 || !cu_seqlens_host)
+    return KDA_ERR_INVALID_ARG;
+  Plan p;
+  if (!build_prefill_plan(num_seqs, cu_seqlens_host, H, split_hint, initial_state != nullptr,
+                          final_state != nullptr, elt_size(dt), p))
+    return KDA_ERR_INVALID_ARG;
+  if (!plan_fits(p, H))
+    return KDA_ERR_INVALID_ARG;
+  const int64_t T = cu_seqlens_host[num_seqs];
+  if (T > 0) {
+    if (!q || !k || !v || !g || !beta || !o)
+      return KDA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) ||
+        !aligned_elt(beta, dt) || !aligned16(o))
+      return KDA_ERR_INVALID_ARG;
+  }
+  if (!aligned16(initial_state) || !aligned16(final_state))
+    return KDA_ERR_INVALID_ARG;
+  if (num_seqs == 0)
+    return KDA_OK;
+  if (p.total > 0) {
+    if (!workspace || workspace_bytes < p.total || ((uintptr_t)workspace % kAlign) != 0)
+      return KDA_ERR_WORKSPACE;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *ws = (uint8_t *)workspace;
+  const int elt = dt == KDA_BF16 ? 1 : 0;
+  const ChunkDesc *d_chunks = (const ChunkDesc *)(ws + p.off_chunks);
+  hipError_t e = upload_tables(p, ws, s);
+  if (e == hipSuccess)
+    e = launch_k1(elt, d_chunks, (int32_t)p.chunks.size(), H, q, k, g, beta, ws + p.off_rec, s);
+  if (e == hipSuccess && !p.segchains.empty()) {
+    e = launch_k2(elt, 1, (const ChainDesc *)(ws + p.off_seg), (int32_t)p.segchains.size(),
+                  d_chunks, H, ws + p.off_rec, v, nullptr, nullptr, nullptr,
+                  (float *)(ws + p.off_St), (float *)(ws + p.off_M), s);
+    if (e == hipSuccess)
+      e = launch_scan((const ScanDesc *)(ws + p.off_scan), (int32_t)p.scans.size(), H,
+                      (const float *)(ws + p.off_M), (const float *)(ws + p.off_St),
+                      initial_state, (float *)(ws + p.off_Sin), s);
+  }
+  if (e == hipSuccess)
+    e = launch_k2(elt, 0, (const ChainDesc *)(ws + p.off_chains), (int32_t)p.chains.size(),
+                  d_chunks, H, ws + p.off_rec, v, o, initial_state,
+                  (const float *)(ws + p.off_Sin), final_state, nullptr, s);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_step(int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
+                           const void *q, const void *k, const void *v, const void *g,
+                           const void *beta, float *state, void *o, void *stream) {
+  if (dk != kD || dv != kD || (dt != KDA_F32 && dt != KDA_BF16))
+    return KDA_ERR_UNSUPPORTED;
+  if (N < 0 || H < 1)
+    return KDA_ERR_INVALID_ARG;
+  if ((int64_t)N * H >= ((int64_t)1 << 31))
+    return KDA_ERR_INVALID_ARG;
+  if (N == 0)
+    return KDA_OK;
+  if (!q || !k || !v || !g || !beta || !state || !o)
+    return KDA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) ||
+      !aligned_elt(beta, dt) || !aligned16(state) || !aligned16(o))
+    return KDA_ERR_INVALID_ARG;
+  const hipError_t e = launch_decode(dt == KDA_BF16 ? 1 : 0, N, H, q, k, v, g, beta, state, o,
+                                     (hipStream_t)stream);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+size_t kda_segment_transition_workspace_size(int32_t num_segs,
+                                             const int64_t *cu_seglens_host, int32_t H,
+                                             int32_t dk, int32_t dv, kda_dtype dt) {
+  if (num_segs < 0 || H < 1 || dk != kD || dv != kD || (dt != KDA_F32 && dt != KDA_BF16))
+    return 0;
+  Plan p;
+  if (!build_segment_plan(num_segs, cu_seglens_host, H, elt_size(dt), p))
+    return 0;
+  return p.total;
+}
+
+kda_status kda_segment_transition(int32_t num_segs, const int64_t *cu_seglens_host, int32_t H,
+                                  int32_t dk, int32_t dv, kda_dtype dt, const void *k,
+                                  const void *v, const void *g, const void *beta, float *M,
+                                  float *S_tilde, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+  if (dk != kD || dv != kD || (dt != KDA_F32 && dt != KDA_BF16))
+    return KDA_ERR_UNSUPPORTED;
+  if (num_segs < 0 || H < 1 || !cu_seglens_host)
+    return KDA_ERR_INVALID_ARG;
+  Plan p;
+  if (!build_segment_plan(num_segs, cu_seglens_host, H, elt_size(dt), p))
+    return KDA_ERR_INVALID_ARG;
+  if (!plan_fits(p, H))
+    return KDA_ERR_INVALID_ARG;
+  const int64_t T = cu_seglens_host[num_segs];
+  if (T > 0) {
+    if (!k || !v || !g || !beta)
+      return KDA_ERR_INVALID_ARG;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned_elt(beta, dt))
+      return KDA_ERR_INVALID_ARG;
+  }
+  if (num_segs > 0 && (!M || !S_tilde))
+    return KDA_ERR_INVALID_ARG;
+  if (!aligned16(M) || !aligned16(S_tilde))
+    return KDA_ERR_INVALID_ARG;
+  if (num_segs > 0) {
+    const size_t bytes = (size_t)num_segs * H * kD * kD * sizeof(float);
+    const uint8_t *a = (const uint8_t *)M, *b = (const uint8_t *)S_tilde;
+    if (a < b + bytes && b < a + bytes)
+      return KDA_ERR_INVALID_ARG;
+  }
+  if (num_segs == 0)
+    return KDA_OK;
+  if (p.total > 0) {
+    if (!workspace || workspace_bytes < p.total || ((uintptr_t)workspace % kAlign) != 0)
+      return KDA_ERR_WORKSPACE;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *ws = (uint8_t *)workspace;
+  const int elt = dt == KDA_BF16 ? 1 : 0;
+  const ChunkDesc *d_chunks = (const ChunkDesc *)(ws + p.off_chunks);
+  hipError_t e = upload_tables(p, ws, s);
+  if (e == hipSuccess)
+    e = launch_k1(elt, d_chunks, (int32_t)p.chunks.size(), H, nullptr, k, g, beta,
+                  ws + p.off_rec, s);
+  if (e == hipSuccess)
+    e = launch_k2(elt, 1, (const ChainDesc *)(ws + p.off_seg), (int32_t)p.segchains.size(),
+                  d_chunks, H, ws + p.off_rec, v, nullptr, nullptr, nullptr, S_tilde, M, s);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+} // extern "C"

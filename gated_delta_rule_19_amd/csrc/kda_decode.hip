@@ -1,0 +1,118 @@
+// KDA decode step: one token per sequence, fp32 state updated in place.
+//
+// Follows the alternative ("u") form of the recurrence that the pages'
+// decode kernel follows ("Kimi K3 的架構" (hao.cnyes.com), §六 FlashKDA 演算法;
+// cost model in its 複雜度分析 part: about 7 D^2 FLOPs and 8 D^2 bytes of
+// fp32 state traffic per head per token):
+//     DS = Diag(exp g) S,  w = DS^T k,  y = DS^T q,
+//     u  = beta (v - w),   S' = DS + k u^T,   o = S'^T q = y + (k . q) u.
+//
+// The kernel is HBM-bound.  One 256-thread workgroup owns one (sequence,
+// head) state of 128 x 128 fp32 (64 KiB).  Thread t holds rows
+// 16*(t/32) .. +15 of the four columns 4*(t%32) .. +3 in registers, so the
+// state is read once and written once, with each wave touching two full
+// 512-byte rows per instruction.  Both reductions (DS^T k and DS^T q) come out
+// of the same pass; the column sums cross the eight row groups through LDS.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <typename T>
+__global__ __launch_bounds__(256) void decode_kernel(const T *__restrict__ q,
+                                                     const T *__restrict__ k,
+                                                     const T *__restrict__ v,
+                                                     const T *__restrict__ g,
+                                                     const T *__restrict__ beta,
+                                                     float *__restrict__ state,
+                                                     T *__restrict__ o) {
+  const int64_t nh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int cg = tid & 31; // column group: columns 4*cg .. 4*cg+3
+  const int rg = tid >> 5; // row group: rows 16*rg .. 16*rg+15
+
+  __shared__ float s_k[kD], s_q[kD], s_a[kD], s_v[kD], s_u[kD];
+  __shared__ float s_w[8][kD], s_y[8][kD];
+  __shared__ float s_kq, s_beta;
+
+  float *S = state + nh * (int64_t)(kD * kD);
+  f32x4 s[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    s[i] = __builtin_nontemporal_load(
+        reinterpret_cast<const f32x4 *>(S + (16 * rg + i) * kD + 4 * cg));
+
+  if (tid < kD) {
+    const int64_t off = nh * kD + tid;
+    s_k[tid] = to_f32(k[off]);
+    s_q[tid] = to_f32(q[off]);
+    s_a[tid] = __expf(to_f32(g[off]));
+    s_v[tid] = to_f32(v[off]);
+  }
+  if (tid == 0)
+    s_beta = to_f32(beta[nh]);
+  __syncthreads();
+
+  // k . q, reduced inside wave 0
+  if (tid < 64) {
+    float p = s_k[tid] * s_q[tid] + s_k[tid + 64] * s_q[tid + 64];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+      p += __shfl_xor(p, m);
+    if (tid == 0)
+      s_kq = p;
+  }
+
+  f32x4 w = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 16 * rg + i;
+    s[i] *= s_a[r];
+    w += s_k[r] * s[i];
+    y += s_q[r] * s[i];
+  }
+  *reinterpret_cast<f32x4 *>(&s_w[rg][4 * cg]) = w;
+  *reinterpret_cast<f32x4 *>(&s_y[rg][4 * cg]) = y;
+  __syncthreads();
+
+  if (tid < kD) {
+    float ws = 0.f, ys = 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      ws += s_w[r][tid];
+      ys += s_y[r][tid];
+    }
+    const float u = s_beta * (s_v[tid] - ws);
+    s_u[tid] = u;
+    o[nh * kD + tid] = from_f32<T>(ys + s_kq * u);
+  }
+  __syncthreads();
+
+  const f32x4 u4 = *reinterpret_cast<const f32x4 *>(&s_u[4 * cg]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 16 * rg + i;
+    const f32x4 nv = s[i] + s_k[r] * u4;
+    __builtin_nontemporal_store(nv, reinterpret_cast<f32x4 *>(S + r * kD + 4 * cg));
+  }
+}
+
+hipError_t launch_decode(int elt, int32_t N, int32_t H, const void *q, const void *k,
+                         const void *v, const void *g, const void *beta, float *state, void *o,
+                         hipStream_t s) {
+  const int64_t nh = (int64_t)N * H;
+  if (nh == 0)
+    return hipSuccess;
+  dim3 grid((unsigned)nh), block(256);
+  if (elt == 1)
+    decode_kernel<bf16><<<grid, block, 0, s>>>(
+        (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (const bf16 *)g,
+        (const bf16 *)beta, state, (bf16 *)o);
+  else
+    decode_kernel<float><<<grid, block, 0, s>>>(
+        (const float *)q, (const float *)k, (const float *)v, (const float *)g,
+        (const float *)beta, state, (float *)o);
+  return hipGetLastError();
+}
+
+} // namespace kda

@@ -1,0 +1,75 @@
+// Host/device shared schedule records and kernel launchers (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kC = 64;  // chunk length
+constexpr int kD = 128; // dk = dv
+
+// One C-token chunk of one sequence (or segment).
+struct ChunkDesc {
+  int64_t tok0;  // first token (packed index)
+  int32_t len;   // 1..64 valid tokens
+  int32_t seq;   // owning sequence
+};
+static_assert(sizeof(ChunkDesc) == 16, "ChunkDesc layout");
+
+// One state-carrying chain: a run of consecutive chunks of one sequence,
+// processed in order from an entry state to an exit state.
+//   init_idx >= 0  : entry state = user initial_state[init_idx]
+//   init_idx == -1 : entry state = 0 (segment pass: [0 | I])
+//   init_idx <= -2 : entry state = planner entry state Sin[-2 - init_idx]
+//   final_idx >= 0 : exit state written at index final_idx of the output base
+struct ChainDesc {
+  int32_t chunk0;
+  int32_t nchunks;
+  int32_t init_idx;
+  int32_t final_idx;
+};
+static_assert(sizeof(ChainDesc) == 16, "ChainDesc layout");
+
+// One split sequence for the planner's prefix scan.
+struct ScanDesc {
+  int32_t pair0;    // index of segment 0's (M, S~) pair
+  int32_t nseg;     // segments of this sequence (>= 2)
+  int32_t sin0;     // index of segment 0's entry state in Sin
+  int32_t init_idx; // user initial_state index, or -1 for zero
+};
+static_assert(sizeof(ScanDesc) == 16, "ScanDesc layout");
+
+// Bytes of the chunk-prep record for one (chunk, head), element size es:
+//   Q_decay [C][D], K_decay [C][D], K_restore^T [D][C], INV*Diag(beta) [C][C],
+//   M_qk [C][C] (all of the element type), a_last [D] fp32; 256-aligned.
+constexpr size_t k1_record_bytes(size_t es) {
+  return ((3 * 64 * 128 + 2 * 64 * 64) * es + 128 * 4 + 255) / 256 * 256;
+}
+
+// Column block of the state-carrying kernel (columns of S per workgroup).
+constexpr int kBV = 64;
+// Column block of the planner scan kernel.
+constexpr int kScanBV = 8;
+
+// Launchers (enqueue only; return the hipGetLastError of the launch).
+hipError_t launch_k1(int elt, const ChunkDesc *chunks, int32_t nchunks, int32_t H,
+                     const void *q, const void *k, const void *g, const void *beta, void *ws,
+                     hipStream_t s);
+
+// mode 0: prefill/replay (width dv, writes o and exit states);
+// mode 1: segment pass (width dk + dv: [S~ | M], no o).
+hipError_t launch_k2(int elt, int mode, const ChainDesc *chains, int32_t nchains,
+                     const ChunkDesc *chunks, int32_t H, const void *ws, const void *v, void *o,
+                     const float *init, const float *sin, float *final_a, float *final_b,
+                     hipStream_t s);
+
+hipError_t launch_scan(const ScanDesc *descs, int32_t ndesc, int32_t H, const float *Mseg,
+                       const float *Stseg, const float *init, float *sin, hipStream_t s);
+
+hipError_t launch_decode(int elt, int32_t N, int32_t H, const void *q, const void *k,
+                         const void *v, const void *g, const void *beta, float *state, void *o,
+                         hipStream_t s);
+
+} // namespace kda

@@ -1,0 +1,182 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library.
+ *
+ * KDA is the gated delta-rule linear-attention layer.  Per sequence and head,
+ * with a dk x dv state S and tokens t in order:
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t,        alpha_t = exp(g_t) per key channel
+ *
+ *   ("Kimi K3.1 Pro 架构完全拆解", §3.1 single-head recurrence; §3.2 for
+ *    the bounded log-decay g in (-5, 0) and alpha = exp(g).)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every buffer is a caller-owned DEVICE pointer unless its name ends in
+ *   _host.  The library allocates no device memory; it keeps no pointer after
+ *   a call returns, except a small pool of pinned host staging buffers it
+ *   uses to upload its own schedule (freed at process exit).
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   Every call validates its arguments on the host first; on failure it
+ *   returns a negative status and enqueues nothing.  On success the work is
+ *   enqueued asynchronously on `stream`; no call synchronises.
+ * - dk = dv = 128 and the chunk length C = 64 are fixed in this build.
+ * - Element type of q, k, v, g, beta and o is `dt`: KDA_F32 (fp32) or
+ *   KDA_BF16 (bfloat16).  States, M and S~ are always fp32.  All arithmetic
+ *   accumulates in fp32; with KDA_BF16 the matrix products take bf16
+ *   operands, with KDA_F32 fp32 operands.
+ * - Layouts are row-major, last index fastest:
+ *       q, k, g : [T_total, H, dk]     v, o : [T_total, H, dv]
+ *       beta    : [T_total, H]         states : [num_seqs, H, dk, dv]
+ *   A batch of B fixed-length sequences of length T is the packed layout
+ *   with cu_seqlens = {0, T, 2T, ..., BT}.
+ * - Every device pointer must be 16-byte aligned, except beta, which needs
+ *   only the alignment of its element type (so [T, H] beta can be sliced by
+ *   token).
+ * - Preconditions NOT checked (results are unspecified if violated):
+ *   g in [-5, 0] (the gate's bound that keeps every 16-token cumulative
+ *   log-decay above -80, "Kimi K3.1 Pro 架构完全拆解" §3.2) and finite
+ *   inputs.  q and k are
+ *   used as given (the layer L2-normalises them before this call); no
+ *   1/sqrt(dk) scale is applied.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kda_status;
+
+#define KDA_OK 0
+#define KDA_ERR_INVALID_ARG (-1) /* NULL required pointer, bad size, bad cu_seqlens, misaligned */
+#define KDA_ERR_UNSUPPORTED (-2) /* dk/dv other than 128, unknown dtype */
+#define KDA_ERR_WORKSPACE (-3)   /* workspace NULL or smaller than the size query returned */
+#define KDA_ERR_HIP (-4)         /* a HIP runtime call or launch failed; outputs undefined */
+
+typedef int32_t kda_dtype;
+#define KDA_F32 0
+#define KDA_BF16 1
+
+#define KDA_CHUNK 64
+#define KDA_HEAD_DIM 128
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *kda_status_string(kda_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t kda_version(void);
+
+/*
+ * Planner query (host only, no HIP calls): how many segments the chunked
+ * prefill will cut sequence `seq_len` into, for a batch whose total
+ * (sequence, head) count is `num_seqs * H`.
+ *   split_hint = 0 : automatic (split long sequences only when the
+ *                    unsplit work would leave most compute units idle);
+ *   split_hint = 1 : never split;
+ *   split_hint = n > 1 : cut every sequence longer than one chunk into
+ *                    min(n, number of its chunks) chunk-aligned segments.
+ * Returns >= 1 (or 1 for seq_len <= 0), or a negative status for bad input.
+ * The sequence-split planner follows "部署 Kimi K3：从 KDA Kernel 到 Fleet
+ * 调度", §1.2 (intra-device, SM-level context parallelism).
+ */
+int32_t kda_plan_num_segments(int64_t seq_len, int32_t num_seqs, int32_t H, int32_t split_hint);
+
+/*
+ * Chunked prefill over packed variable-length sequences.
+ *
+ * Computes, for each sequence n (tokens [cu[n], cu[n+1])) and head h, the
+ * recurrence above from S_0 = initial_state[n,h] (or zero), writes o for
+ * every token and, if final_state != NULL, the state after the last token.
+ * It uses the chunkwise form ("Kimi K3 的架構" (hao.cnyes.com), §六 FlashKDA
+ * 演算法): a chunk-prep step per (chunk, head) builds the decayed operands,
+ * L = StrictTril(Diag(beta) K_decay K_inv^T), INV = (I + L)^-1 and
+ * M_qk = tril(Q_decay K_inv^T); a state-carrying step per (sequence, head)
+ * walks the chunks in order:
+ *     U = INV Diag(beta)(V - K_decay S);  O = Q_decay S + M_qk U;
+ *     S = Diag(a_last) S + K_restore^T U.
+ * Chunks restart at every sequence start; a sequence's last chunk may be
+ * shorter than 64 tokens.  Long sequences may be cut into segments whose
+ * transition pairs are combined by a prefix scan and then replayed (see
+ * kda_plan_num_segments and kda_segment_transition); the result is the same
+ * up to fp32 rounding.
+ *
+ *   num_seqs         : N >= 0 sequences.
+ *   cu_seqlens_host  : HOST, N+1 int64, cu[0] = 0, nondecreasing.  The
+ *                      library derives its schedule from it and uploads that
+ *                      schedule into `workspace` with an async copy.
+ *   H, dk, dv, dt    : heads (>= 1), 128, 128, element type.
+ *   q, k, v, g, beta : inputs (layouts above); g is a natural-log decay.
+ *   initial_state    : [N, H, dk, dv] fp32, or NULL for zeros.
+ *   o                : [T_total, H, dv] output of type dt.
+ *   final_state      : [N, H, dk, dv] fp32 output, or NULL (not written).
+ *                      final_state == initial_state is allowed (in-place
+ *                      resume); any other overlap between outputs and
+ *                      inputs is not.
+ *   split_hint       : as in kda_plan_num_segments.
+ *   workspace        : DEVICE scratch of at least the queried size, 256-byte
+ *                      aligned; contents are undefined after the call.
+ * A length-0 sequence writes its initial state (or zeros) to final_state.
+ */
+size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, const int64_t *cu_seqlens_host,
+                                        int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
+                                        int32_t split_hint);
+
+kda_status kda_chunk_prefill(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_t H,
+                             int32_t dk, int32_t dv,
+                             kda_dtype dt, const void *q, const void *k, const void *v,
+                             const void *g, const void *beta, const float *initial_state,
+                             void *o, float *final_state, int32_t split_hint, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step for N independent sequences, updating the state IN PLACE
+ * ("Kimi K3 的架構" (hao.cnyes.com), §六, the alternative form the decode
+ * kernel follows; "Kimi K3.1 Pro 架构完全拆解" §3.4, state updated in place):
+ *     DS = Diag(exp(g)) S;  u = beta (v - DS^T k);  S = DS + k u^T;
+ *     o = S^T q  (= DS^T q + (k . q) u)
+ *
+ *   q, k, g : [N, H, dk] of type dt;  v : [N, H, dv];  beta : [N, H].
+ *   state   : [N, H, dk, dv] fp32, read and overwritten.
+ *   o       : [N, H, dv] of type dt; must not overlap any input or state.
+ * N = 0 is a no-op.
+ */
+kda_status kda_decode_step(int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
+                           const void *q, const void *k, const void *v, const void *g,
+                           const void *beta, float *state, void *o, void *stream);
+
+/*
+ * Segment transition pairs ("部署 Kimi K3：从 KDA Kernel 到 Fleet 调度", §二,
+ * the KCP decomposition): for each packed segment s (tokens
+ * [cu[s], cu[s+1])) and head h,
+ *     M[s,h]       = M_T ... M_1,  M_r = (I - beta_r k_r k_r^T) Diag(exp(g_r))
+ *     S_tilde[s,h] = the state after the segment when it starts from S = 0
+ * so that the state after the segment from any entry state S_in is
+ * S_tilde + M S_in, and pairs compose associatively:
+ * (M2, S2) after (M1, S1) = (M2 M1, S2 + M2 S1).
+ *
+ *   cu_seglens_host : HOST, num_segs+1 int64, as cu_seqlens_host above.
+ *   k, v, g, beta : as for kda_chunk_prefill (q is not needed).
+ *   M       : [num_segs, H, dk, dk] fp32 output.
+ *   S_tilde : [num_segs, H, dk, dv] fp32 output; must not overlap M.
+ *   workspace : DEVICE scratch of at least the queried size.
+ * A length-0 segment gives M = I and S_tilde = 0.
+ */
+size_t kda_segment_transition_workspace_size(int32_t num_segs,
+                                             const int64_t *cu_seglens_host, int32_t H,
+                                             int32_t dk, int32_t dv, kda_dtype dt);
+
+kda_status kda_segment_transition(int32_t num_segs, const int64_t *cu_seglens_host,
+                                  int32_t H, int32_t dk, int32_t dv, kda_dtype dt, const void *k, const void *v,
+                                  const void *g, const void *beta, float *M, float *S_tilde,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,175 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the device.
+None of these calls reaches a HIP API (they run on a machine with no GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from gated_delta_rule_19_amd import _native as nat
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(nat.LIB_PATH):
+        from gated_delta_rule_19_amd import build
+        build.build()
+    return nat.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(nat.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(lib):
+    assert nat.status_string(0) == "KDA_OK"
+    assert nat.status_string(-1) == "KDA_ERR_INVALID_ARG"
+    assert nat.status_string(-2) == "KDA_ERR_UNSUPPORTED"
+    assert nat.status_string(-3) == "KDA_ERR_WORKSPACE"
+    assert nat.status_string(-4) == "KDA_ERR_HIP"
+    assert nat.status_string(7) == "KDA_ERR_UNKNOWN"
+    assert nat.version() >= 100
+
+
+def test_planner_policy(lib):
+    # never / forced splits
+    assert nat.plan_num_segments(131072, 1, 12, 1) == 1
+    assert nat.plan_num_segments(131072, 1, 12, 128) == 128
+    assert nat.plan_num_segments(100, 1, 12, 128) == 2        # at most one segment per chunk
+    assert nat.plan_num_segments(0, 1, 12, 64) == 1
+    # automatic: few heads of one long sequence -> split; a full layer -> not
+    assert nat.plan_num_segments(131072, 1, 12, 0) == 64
+    assert nat.plan_num_segments(8192, 1, 96, 0) == 1
+    assert nat.plan_num_segments(256, 1, 2, 0) == 1
+    with pytest.raises(nat.KdaError):
+        nat.plan_num_segments(10, 1, 0, 0)
+    with pytest.raises(nat.KdaError):
+        nat.plan_num_segments(10, 1, 1, -1)
+
+
+def cu(*xs):
+    a = np.array(xs, dtype=np.int64)
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def test_workspace_sizes(lib):
+    a, p = cu(0, 256)
+    ws32 = lib.kda_chunk_prefill_workspace_size(1, p, 2, 128, 128, nat.KDA_F32, 0)
+    ws16 = lib.kda_chunk_prefill_workspace_size(1, p, 2, 128, 128, nat.KDA_BF16, 0)
+    assert ws32 > ws16 > 4 * 2 * 64 * 1024  # 4 chunks x 2 heads of chunk-prep records
+    a2, p2 = cu(0, 256, 256)
+    assert lib.kda_chunk_prefill_workspace_size(2, p2, 2, 128, 128, nat.KDA_BF16, 0) >= ws16
+    # a split adds the planner's state buffers
+    a3, p3 = cu(0, 64 * 64)
+    nosplit = lib.kda_chunk_prefill_workspace_size(1, p3, 1, 128, 128, nat.KDA_BF16, 1)
+    split = lib.kda_chunk_prefill_workspace_size(1, p3, 1, 128, 128, nat.KDA_BF16, 8)
+    assert split >= nosplit + (7 * 2 + 8) * 128 * 128 * 4
+    # invalid arguments -> 0
+    assert lib.kda_chunk_prefill_workspace_size(1, p, 2, 64, 128, nat.KDA_F32, 0) == 0
+    assert lib.kda_chunk_prefill_workspace_size(1, p, 0, 128, 128, nat.KDA_F32, 0) == 0
+    assert lib.kda_chunk_prefill_workspace_size(1, p, 2, 128, 128, 5, 0) == 0
+    b, pb = cu(0, 10, 5)
+    assert lib.kda_chunk_prefill_workspace_size(2, pb, 2, 128, 128, nat.KDA_F32, 0) == 0
+    assert lib.kda_chunk_prefill_workspace_size(1, None, 2, 128, 128, nat.KDA_F32, 0) == 0
+    s, ps = cu(0, 64, 64, 100)
+    assert lib.kda_segment_transition_workspace_size(3, ps, 2, 128, 128, nat.KDA_BF16) > 0
+    assert lib.kda_segment_transition_workspace_size(3, ps, 2, 100, 128, nat.KDA_BF16) == 0
+
+
+FAKE = ctypes.c_void_p(0x100000)       # a well-aligned address that is never dereferenced
+MISALIGNED = ctypes.c_void_p(0x100008)
+
+
+def prefill(lib, n=1, cuv=(0, 128), H=2, dk=128, dv=128, dt=nat.KDA_BF16, q=FAKE, k=FAKE,
+            v=FAKE, g=FAKE, beta=FAKE, init=None, o=FAKE, fin=FAKE, split=0, ws=None,
+            wsb=0):
+    a, p = cu(*cuv)
+    return lib.kda_chunk_prefill(n, p, H, dk, dv, dt, q, k, v, g, beta, init, o, fin, split,
+                                 ws, wsb, None)
+
+
+def test_prefill_argument_errors(lib):
+    E = nat
+    assert prefill(lib, dk=64) == E.KDA_ERR_UNSUPPORTED
+    assert prefill(lib, dv=256) == E.KDA_ERR_UNSUPPORTED
+    assert prefill(lib, dt=3) == E.KDA_ERR_UNSUPPORTED
+    assert prefill(lib, H=0) == E.KDA_ERR_INVALID_ARG
+    assert prefill(lib, n=-1, cuv=(0,)) == E.KDA_ERR_INVALID_ARG
+    assert prefill(lib, split=-2) == E.KDA_ERR_INVALID_ARG
+    assert prefill(lib, n=2, cuv=(0, 100, 50)) == E.KDA_ERR_INVALID_ARG   # decreasing
+    assert prefill(lib, cuv=(5, 128)) == E.KDA_ERR_INVALID_ARG           # cu[0] != 0
+    assert prefill(lib, q=None) == E.KDA_ERR_INVALID_ARG
+    assert prefill(lib, beta=None) == E.KDA_ERR_INVALID_ARG
+    assert prefill(lib, o=None) == E.KDA_ERR_INVALID_ARG
+    assert prefill(lib, v=MISALIGNED) == E.KDA_ERR_INVALID_ARG
+    assert prefill(lib, init=MISALIGNED) == E.KDA_ERR_INVALID_ARG
+    assert prefill(lib, fin=MISALIGNED) == E.KDA_ERR_INVALID_ARG
+    # workspace missing, too small, or not 256-byte aligned
+    assert prefill(lib) == E.KDA_ERR_WORKSPACE
+    assert prefill(lib, ws=FAKE, wsb=1024) == E.KDA_ERR_WORKSPACE
+    a, p = cu(0, 128)
+    need = lib.kda_chunk_prefill_workspace_size(1, p, 2, 128, 128, nat.KDA_BF16, 0)
+    assert prefill(lib, ws=ctypes.c_void_p(0x100010), wsb=need + 256) == E.KDA_ERR_WORKSPACE
+    # nothing to do
+    assert prefill(lib, n=0, cuv=(0,)) == E.KDA_OK
+
+
+def test_decode_argument_errors(lib):
+    E = nat
+
+    def dec(N=4, H=2, dk=128, dv=128, dt=nat.KDA_F32, q=FAKE, k=FAKE, v=FAKE, g=FAKE,
+            beta=FAKE, state=FAKE, o=FAKE):
+        return lib.kda_decode_step(N, H, dk, dv, dt, q, k, v, g, beta, state, o, None)
+
+    assert dec(dk=127) == E.KDA_ERR_UNSUPPORTED
+    assert dec(dt=9) == E.KDA_ERR_UNSUPPORTED
+    assert dec(N=-1) == E.KDA_ERR_INVALID_ARG
+    assert dec(H=0) == E.KDA_ERR_INVALID_ARG
+    assert dec(state=None) == E.KDA_ERR_INVALID_ARG
+    assert dec(o=None) == E.KDA_ERR_INVALID_ARG
+    assert dec(g=MISALIGNED) == E.KDA_ERR_INVALID_ARG
+    assert dec(N=1 << 30, H=4) == E.KDA_ERR_INVALID_ARG
+    assert dec(N=0) == E.KDA_OK
+
+
+def test_segment_transition_argument_errors(lib):
+    E = nat
+    a, p = cu(0, 64, 100)
+    M = ctypes.c_void_p(0x10000000)
+    S = ctypes.c_void_p(0x20000000)
+
+    def seg(n=2, pp=p, H=1, dk=128, k=FAKE, M=M, S=S, ws=None, wsb=0):
+        return lib.kda_segment_transition(n, pp, H, dk, 128, nat.KDA_BF16, k, FAKE, FAKE,
+                                          FAKE, M, S, ws, wsb, None)
+
+    assert seg(dk=64) == E.KDA_ERR_UNSUPPORTED
+    assert seg(H=0) == E.KDA_ERR_INVALID_ARG
+    assert seg(pp=None) == E.KDA_ERR_INVALID_ARG
+    assert seg(k=None) == E.KDA_ERR_INVALID_ARG
+    assert seg(M=None) == E.KDA_ERR_INVALID_ARG
+    # M and S_tilde overlap (2 segments x 1 head x 64 KiB each)
+    assert seg(S=ctypes.c_void_p(0x10000000 + 65536)) == E.KDA_ERR_INVALID_ARG
+    assert seg() == E.KDA_ERR_WORKSPACE
+    b, pb = cu(0)
+    assert seg(n=0, pp=pb) == E.KDA_OK
+
+
+def test_binding_rejects_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(4, 2, 128)
+    with pytest.raises(ValueError):
+        nat.chunk_prefill(x, x, x, x, torch.zeros(4, 2))
