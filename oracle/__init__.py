@@ -97,8 +97,18 @@ def _cu(cu_seqlens, T):
     return cu
 
 
+def default_threads() -> int:
+    """Threads the oracle uses by default: the CPUs this process may run on,
+    capped at 16 (a one-GPU machine's CPU share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def threads_used(threads: int = 0) -> int:
-    return int(_load().kda_oracle_threads(int(threads)))
+    return int(threads) if threads > 0 else default_threads()
 
 
 def recurrence(q, k, v, g, beta, cu_seqlens=None, initial_state=None, beta_write=None,
@@ -131,7 +141,7 @@ def recurrence(q, k, v, g, beta, cu_seqlens=None, initial_state=None, beta_write
     rc = _load().kda_oracle_recurrence(
         N, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, dk, dv,
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(bw), _ptr(init),
-        _ptr(o), _ptr(fin), int(threads))
+        _ptr(o), _ptr(fin), threads_used(threads))
     if rc != 0:
         raise RuntimeError("kda_oracle_recurrence failed (%d)" % rc)
     return o, fin
@@ -161,7 +171,7 @@ def segment_transition(k, v, g, beta, cu_seglens=None, threads: int = 0):
     St = np.zeros((S, H, dk, dv), dtype=np.float64)
     rc = _load().kda_oracle_segment(
         S, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, dk, dv,
-        _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(M), _ptr(St), int(threads))
+        _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(M), _ptr(St), threads_used(threads))
     if rc != 0:
         raise RuntimeError("kda_oracle_segment failed (%d)" % rc)
     return M, St
