@@ -17,6 +17,7 @@
 #include "kda_internal.h"
 
 #include <algorithm>
+#include <climits>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -52,6 +53,18 @@ int64_t plan_nseg(int64_t len, int32_t num_seqs, int32_t H, int32_t split_hint) 
   if (chains >= kAutoMinChains)
     return 1;
   return std::max<int64_t>(1, std::min<int64_t>(kAutoSegments, nch / kAutoMinSegChunks));
+}
+
+ChainDesc chain(int64_t tok0, int64_t ntok, int64_t chunk0, int64_t init_idx,
+                int64_t final_idx) {
+  ChainDesc c;
+  c.tok0 = tok0;
+  c.ntok = (int32_t)ntok;
+  c.chunk0 = (int32_t)chunk0;
+  c.init_idx = (int32_t)init_idx;
+  c.final_idx = (int32_t)final_idx;
+  c.pad0 = c.pad1 = 0;
+  return c;
 }
 
 // The schedule for one call, built on the host.
@@ -95,7 +108,7 @@ bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_h
   if (!cu || cu[0] != 0)
     return false;
   for (int32_t n = 0; n < N; ++n)
-    if (cu[n + 1] < cu[n])
+    if (cu[n + 1] < cu[n] || cu[n + 1] - cu[n] > INT32_MAX)
       return false;
   for (int32_t n = 0; n < N; ++n) {
     const int64_t len = cu[n + 1] - cu[n];
@@ -110,20 +123,20 @@ bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_h
     }
     const int64_t nseg = plan_nseg(len, N, H, split_hint);
     if (nseg <= 1) {
-      p.chains.push_back(ChainDesc{(int32_t)c0, (int32_t)nch, has_init ? n : -1,
-                                   has_final ? n : -1});
+      p.chains.push_back(chain(cu[n], len, c0, has_init ? n : -1, has_final ? n : -1));
       continue;
     }
     const int64_t q = nch / nseg, r = nch % nseg;
     const int64_t pair0 = p.npairs, sin0 = p.nsin;
     for (int64_t j = 0; j < nseg; ++j) {
-      const int64_t s0 = c0 + j * q + std::min(j, r);
+      const int64_t s0 = j * q + std::min(j, r);  // first chunk, relative to the sequence
       const int64_t cnt = q + (j < r ? 1 : 0);
+      const int64_t t0 = cu[n] + s0 * kC;
+      const int64_t nt = std::min<int64_t>(cnt * kC, cu[n + 1] - t0);
       if (j + 1 < nseg)
-        p.segchains.push_back(ChainDesc{(int32_t)s0, (int32_t)cnt, -1, (int32_t)(pair0 + j)});
+        p.segchains.push_back(chain(t0, nt, c0 + s0, -1, pair0 + j));
       const bool last = j + 1 == nseg;
-      p.chains.push_back(ChainDesc{(int32_t)s0, (int32_t)cnt, (int32_t)(-2 - (sin0 + j)),
-                                   (last && has_final) ? n : -1});
+      p.chains.push_back(chain(t0, nt, c0 + s0, -2 - (sin0 + j), (last && has_final) ? n : -1));
     }
     p.scans.push_back(ScanDesc{(int32_t)pair0, (int32_t)nseg, (int32_t)sin0,
                                has_init ? n : -1});
@@ -131,7 +144,7 @@ bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_h
     p.nsin += nseg;
   }
   // longest chains first, so the tail of the launch is short work
-  auto longer = [](const ChainDesc &a, const ChainDesc &b) { return a.nchunks > b.nchunks; };
+  auto longer = [](const ChainDesc &a, const ChainDesc &b) { return a.ntok > b.ntok; };
   std::stable_sort(p.chains.begin(), p.chains.end(), longer);
   std::stable_sort(p.segchains.begin(), p.segchains.end(), longer);
   layout(p, H, es);
@@ -144,7 +157,7 @@ bool build_segment_plan(int32_t S, const int64_t *cu, int32_t H, size_t es, Plan
   if (!cu || cu[0] != 0)
     return false;
   for (int32_t s = 0; s < S; ++s)
-    if (cu[s + 1] < cu[s])
+    if (cu[s + 1] < cu[s] || cu[s + 1] - cu[s] > INT32_MAX)
       return false;
   for (int32_t s = 0; s < S; ++s) {
     const int64_t len = cu[s + 1] - cu[s];
@@ -157,10 +170,10 @@ bool build_segment_plan(int32_t S, const int64_t *cu, int32_t H, size_t es, Plan
       d.seq = s;
       p.chunks.push_back(d);
     }
-    p.segchains.push_back(ChainDesc{(int32_t)c0, (int32_t)nch, -1, s});
+    p.segchains.push_back(chain(cu[s], len, c0, -1, s));
   }
   std::stable_sort(p.segchains.begin(), p.segchains.end(),
-                   [](const ChainDesc &a, const ChainDesc &b) { return a.nchunks > b.nchunks; });
+                   [](const ChainDesc &a, const ChainDesc &b) { return a.ntok > b.ntok; });
   layout(p, H, es);
   return true;
 }
@@ -332,18 +345,18 @@ kda_status kda_chunk_prefill(int32_t num_seqs, const int64_t *cu_seqlens_host, i
   if (e == hipSuccess)
     e = launch_k1(elt, d_chunks, (int32_t)p.chunks.size(), H, q, k, g, beta, ws + p.off_rec, s);
   if (e == hipSuccess && !p.segchains.empty()) {
-    e = launch_k2(elt, 1, (const ChainDesc *)(ws + p.off_seg), (int32_t)p.segchains.size(),
-                  d_chunks, H, ws + p.off_rec, v, nullptr, nullptr, nullptr,
-                  (float *)(ws + p.off_St), (float *)(ws + p.off_M), s);
+    e = launch_k2(elt, 1, (const ChainDesc *)(ws + p.off_seg), (int32_t)p.segchains.size(), H,
+                  ws + p.off_rec, v, nullptr, nullptr, nullptr, (float *)(ws + p.off_St),
+                  (float *)(ws + p.off_M), s);
     if (e == hipSuccess)
       e = launch_scan((const ScanDesc *)(ws + p.off_scan), (int32_t)p.scans.size(), H,
                       (const float *)(ws + p.off_M), (const float *)(ws + p.off_St),
                       initial_state, (float *)(ws + p.off_Sin), s);
   }
   if (e == hipSuccess)
-    e = launch_k2(elt, 0, (const ChainDesc *)(ws + p.off_chains), (int32_t)p.chains.size(),
-                  d_chunks, H, ws + p.off_rec, v, o, initial_state,
-                  (const float *)(ws + p.off_Sin), final_state, nullptr, s);
+    e = launch_k2(elt, 0, (const ChainDesc *)(ws + p.off_chains), (int32_t)p.chains.size(), H,
+                  ws + p.off_rec, v, o, initial_state, (const float *)(ws + p.off_Sin),
+                  final_state, nullptr, s);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -425,8 +438,8 @@ kda_status kda_segment_transition(int32_t num_segs, const int64_t *cu_seglens_ho
     e = launch_k1(elt, d_chunks, (int32_t)p.chunks.size(), H, nullptr, k, g, beta,
                   ws + p.off_rec, s);
   if (e == hipSuccess)
-    e = launch_k2(elt, 1, (const ChainDesc *)(ws + p.off_seg), (int32_t)p.segchains.size(),
-                  d_chunks, H, ws + p.off_rec, v, nullptr, nullptr, nullptr, S_tilde, M, s);
+    e = launch_k2(elt, 1, (const ChainDesc *)(ws + p.off_seg), (int32_t)p.segchains.size(), H,
+                  ws + p.off_rec, v, nullptr, nullptr, nullptr, S_tilde, M, s);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -19,18 +19,21 @@ struct ChunkDesc {
 static_assert(sizeof(ChunkDesc) == 16, "ChunkDesc layout");
 
 // One state-carrying chain: a run of consecutive chunks of one sequence,
-// processed in order from an entry state to an exit state.
+// tokens [tok0, tok0 + ntok), processed in order from an entry state to an
+// exit state.  Its chunks' prep records are chunk0, chunk0 + 1, ...
 //   init_idx >= 0  : entry state = user initial_state[init_idx]
 //   init_idx == -1 : entry state = 0 (segment pass: [0 | I])
 //   init_idx <= -2 : entry state = planner entry state Sin[-2 - init_idx]
 //   final_idx >= 0 : exit state written at index final_idx of the output base
 struct ChainDesc {
+  int64_t tok0;
+  int32_t ntok;
   int32_t chunk0;
-  int32_t nchunks;
   int32_t init_idx;
   int32_t final_idx;
+  int32_t pad0, pad1;
 };
-static_assert(sizeof(ChainDesc) == 16, "ChainDesc layout");
+static_assert(sizeof(ChainDesc) == 32, "ChainDesc layout");
 
 // One split sequence for the planner's prefix scan.
 struct ScanDesc {
@@ -60,10 +63,9 @@ hipError_t launch_k1(int elt, const ChunkDesc *chunks, int32_t nchunks, int32_t 
 
 // mode 0: prefill/replay (width dv, writes o and exit states);
 // mode 1: segment pass (width dk + dv: [S~ | M], no o).
-hipError_t launch_k2(int elt, int mode, const ChainDesc *chains, int32_t nchains,
-                     const ChunkDesc *chunks, int32_t H, const void *ws, const void *v, void *o,
-                     const float *init, const float *sin, float *final_a, float *final_b,
-                     hipStream_t s);
+hipError_t launch_k2(int elt, int mode, const ChainDesc *chains, int32_t nchains, int32_t H,
+                     const void *ws, const void *v, void *o, const float *init,
+                     const float *sin, float *final_a, float *final_b, hipStream_t s);
 
 hipError_t launch_scan(const ScanDesc *descs, int32_t ndesc, int32_t H, const float *Mseg,
                        const float *Stseg, const float *init, float *sin, hipStream_t s);

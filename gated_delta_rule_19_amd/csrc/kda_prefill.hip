@@ -59,11 +59,20 @@ __device__ __constant__ int kUpJ[6] = {1, 2, 3, 2, 3, 3};
 
 template <typename T> constexpr int pad_elems() { return 16 / (int)sizeof(T) * 2; }
 
+// Workgroup barrier that orders LDS only: outstanding global loads stay in
+// flight across it (a full __syncthreads() would wait for them too).
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 } // namespace
 
 // ---------------------------------------------------------------------------
-// K1: chunk prep.  One workgroup per (chunk, head), chunk-parallel.  q may be
-// NULL (segment transitions need no outputs): Q_decay and M_qk are then 0.
+// K1: chunk prep.  One workgroup per (chunk, head), chunk-parallel.  With
+// has_q == 0 (segment transitions need no outputs) q is not a real input:
+// Q_decay and M_qk are then 0.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k1_kernel(const ChunkDesc *__restrict__ chunks,
@@ -71,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void k1_kernel(const ChunkDesc *__restric
                                                       const T *__restrict__ k,
                                                       const T *__restrict__ g,
                                                       const T *__restrict__ beta,
-                                                      uint8_t *__restrict__ ws) {
+                                                      uint8_t *__restrict__ ws, int has_q) {
   constexpr int P = pad_elems<T>();
   constexpr int LD = kD + P;                 // operand row stride (elements)
   constexpr size_t OPB = (size_t)kC * LD * sizeof(T);
@@ -108,24 +117,38 @@ __global__ __launch_bounds__(kThreads) void k1_kernel(const ChunkDesc *__restric
   T *Mqk = reinterpret_cast<T *>(rec + off.mqk);
   float *ac = reinterpret_cast<float *>(rec + off.ac);
 
+  // ---- loads: every row index is clamped into the chunk, so all loads are
+  // unconditional and in flight together; padded rows are zeroed afterwards.
+  T graw[32], qraw[32], kraw[32];
+  {
+    const int64_t base = cd.tok0 * rowstride + (int64_t)h * kD + c;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int rr = min(half * 32 + i, len - 1);
+      const int64_t off = base + (int64_t)rr * rowstride;
+      graw[i] = g[off];
+      kraw[i] = k[off];
+      qraw[i] = q[off];
+    }
+  }
+  const float bval = to_f32(beta[(cd.tok0 + min(tid & (kC - 1), len - 1)) * H + h]);
+  if (tid < kC)
+    sBeta[tid] = (tid < len) ? bval : 0.f;
+
   // ---- phase 1: inclusive cumulative log-decay per channel -------------
   float G[32];
   {
-    const T *gp = g + (cd.tok0 + half * 32) * rowstride + (int64_t)h * kD + c;
     float run = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      const int r = half * 32 + i;
-      const float gv = (r < len) ? to_f32(gp[(int64_t)i * rowstride]) : 0.f;
+      const float gv = (half * 32 + i < len) ? to_f32(graw[i]) : 0.f;
       run += gv;
       G[i] = run;
     }
     if (half == 0)
       sTot[c] = run;
   }
-  if (tid < kC)
-    sBeta[tid] = (tid < len) ? to_f32(beta[(cd.tok0 + tid) * H + h]) : 0.f;
-  __syncthreads();
+  lds_sync();
   if (half == 1) {
     const float base = sTot[c];
 #pragma unroll
@@ -138,12 +161,10 @@ __global__ __launch_bounds__(kThreads) void k1_kernel(const ChunkDesc *__restric
     sP[1][c] = G[15];
     sP[2][c] = G[31];
   }
-  __syncthreads();
+  lds_sync();
 
   // ---- phase 2: decayed operands ----------------------------------------
   {
-    const T *qp = q + (cd.tok0 + half * 32) * rowstride + (int64_t)h * kD + c;
-    const T *kp = k + (cd.tok0 + half * 32) * rowstride + (int64_t)h * kD + c;
     const float pC = sP[4][c];
     float krv[32];
 #pragma unroll
@@ -157,8 +178,8 @@ __global__ __launch_bounds__(kThreads) void k1_kernel(const ChunkDesc *__restric
         const int i = tt * 16 + ii;
         const int r = half * 32 + i;
         const bool ok = r < len;
-        const float qv = (ok && q) ? to_f32(qp[(int64_t)i * rowstride]) : 0.f;
-        const float kv = ok ? to_f32(kp[(int64_t)i * rowstride]) : 0.f;
+        const float qv = (ok && has_q) ? to_f32(qraw[i]) : 0.f;
+        const float kv = ok ? to_f32(kraw[i]) : 0.f;
         const float eloc = __expf(G[i] - pI);  // (e^-80, 1]
         const float est = __expf(pI - G[i]);   // [1, e^80)
         const float eend = __expf(pI1 - G[i]); // (e^-80, 1]
@@ -188,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void k1_kernel(const ChunkDesc *__restric
     for (int p = half; p < 6; p += 2)
       sF[p][c] = __expf(sP[kOffI[p]][c] - sP[kOffJ[p] + 1][c]);
   }
-  __syncthreads();
+  lds_sync();
 
   // ---- phase 3: L and M_qk tiles on MFMA ---------------------------------
   const int wv = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
@@ -223,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void k1_kernel(const ChunkDesc *__restric
       }
     }
   }
-  __syncthreads(); // operand region is now free for L / INV
+  lds_sync(); // operand region is now free for L / INV
 
   // L (beta-scaled rows, strictly lower) to LDS; M_qk (lower incl. diagonal)
   // straight to the record.
@@ -249,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void k1_kernel(const ChunkDesc *__restric
     sInv[row][col] = 0.f;
     Mqk[row * kC + col] = from_f32<T>(0.f);
   }
-  __syncthreads();
+  lds_sync();
 
   // ---- phase 4: INV = (I + L)^-1 by blocked forward substitution ---------
   if (tid < 64) {
@@ -268,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void k1_kernel(const ChunkDesc *__restric
     for (int i = 0; i < 16; ++i)
       sInv[16 * b + i][16 * b + j] = x[i];
   }
-  __syncthreads();
+  lds_sync();
   for (int bi = 1; bi < 4; ++bi) {
     // T_j = sum_{m=j}^{bi-1} L[bi][m] INV[m][j]   for j < bi
     for (int e = tid; e < bi * 256; e += kThreads) {
@@ -280,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void k1_kernel(const ChunkDesc *__restric
           acc += sL[16 * bi + r][16 * m + u] * sInv[16 * m + u][16 * j + cc];
       sTmp[r][16 * j + cc] = acc;
     }
-    __syncthreads();
+    lds_sync();
     // INV[bi][j] = -INV[bi][bi] T_j
     for (int e = tid; e < bi * 256; e += kThreads) {
       const int j = e >> 8, r = (e >> 4) & 15, cc = e & 15;
@@ -290,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void k1_kernel(const ChunkDesc *__restric
         acc += sInv[16 * bi + r][16 * bi + u] * sTmp[u][16 * j + cc];
       sInv[16 * bi + r][16 * j + cc] = -acc;
     }
-    __syncthreads();
+    lds_sync();
   }
 
   // INV * Diag(beta) to the record, 16 contiguous elements per thread
@@ -316,18 +337,64 @@ __global__ __launch_bounds__(kThreads) void k1_kernel(const ChunkDesc *__restric
 //   MODE 0: prefill / replay, width dv; writes o and the exit state.
 //   MODE 1: segment pass, width dk + dv of [S~ | M] from [0 | I] with values
 //           [V | 0]; the exit state's S~ part goes to out_a, M part to out_b.
+// The loop is latency-bound (S -> W -> U -> S per chunk), so every global
+// operand of chunk i+1 is loaded into registers while chunk i is computed,
+// and the workgroup barriers order LDS only.
 // ---------------------------------------------------------------------------
+template <typename T, int NCT> struct ChunkOps {
+  Frag<T> kd[4], qd[4], invb[2], mqk[2], krt[2][2];
+  f32x4 ac[2];
+  T v[NCT][4];
+};
+
+template <typename T, int MODE, int NCT>
+__device__ __forceinline__ void load_chunk_ops(ChunkOps<T, NCT> &op, const uint8_t *rec,
+                                               const T *vbase, int len, int64_t rowstride,
+                                               int wv, int lr, int lg) {
+  constexpr RecOff off(sizeof(T));
+  const T *Qd = reinterpret_cast<const T *>(rec + off.qd);
+  const T *Kd = reinterpret_cast<const T *>(rec + off.kd);
+  const T *KrT = reinterpret_cast<const T *>(rec + off.krt);
+  const T *INVb = reinterpret_cast<const T *>(rec + off.invb);
+  const T *Mqk = reinterpret_cast<const T *>(rec + off.mqk);
+  const float *ac = reinterpret_cast<const float *>(rec + off.ac);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    op.kd[s] = load_frag(Kd + (16 * wv + lr) * kD + 32 * s + 8 * lg);
+    if (MODE == 0)
+      op.qd[s] = load_frag(Qd + (16 * wv + lr) * kD + 32 * s + 8 * lg);
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    op.invb[s] = load_frag(INVb + (16 * wv + lr) * kC + 32 * s + 8 * lg);
+    if (MODE == 0)
+      op.mqk[s] = load_frag(Mqk + (16 * wv + lr) * kC + 32 * s + 8 * lg);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+      op.krt[rt][s] = load_frag(KrT + (16 * (2 * wv + rt) + lr) * kC + 32 * s + 8 * lg);
+  }
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+    op.ac[rt] = *reinterpret_cast<const f32x4 *>(ac + 16 * (2 * wv + rt) + 4 * lg);
+  // V rows clamped into the chunk (rows past its end are zeroed at use)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rr = min(16 * wv + 4 * lg + i, len - 1);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+      op.v[ct][i] = vbase[(int64_t)rr * rowstride + 16 * ct + lr];
+  }
+}
+
 template <typename T, int MODE>
 __global__ __launch_bounds__(kThreads) void k2_kernel(
-    const ChainDesc *__restrict__ chains, const ChunkDesc *__restrict__ chunks, int32_t H,
-    const uint8_t *__restrict__ ws, const T *__restrict__ v, T *__restrict__ o,
-    const float *__restrict__ init, const float *__restrict__ sin, float *__restrict__ out_a,
-    float *__restrict__ out_b) {
+    const ChainDesc *__restrict__ chains, int32_t H, const uint8_t *__restrict__ ws,
+    const T *__restrict__ v, T *__restrict__ o, const float *__restrict__ init,
+    const float *__restrict__ sin, float *__restrict__ out_a, float *__restrict__ out_b) {
   constexpr int P = pad_elems<T>();
   constexpr int LDS_S = kD + P; // Sb row stride: [col][channel]
   constexpr int LDS_C = kC + P; // VWb / Ub row stride: [col][token]
   constexpr int NCT = kBV / 16;
-  constexpr RecOff off(sizeof(T));
   constexpr size_t RB = k1_record_bytes(sizeof(T));
   __shared__ __attribute__((aligned(16))) T Sb[kBV][LDS_S];
   __shared__ __attribute__((aligned(16))) T VWb[kBV][LDS_C];
@@ -340,6 +407,7 @@ __global__ __launch_bounds__(kThreads) void k2_kernel(
   const int vcol0 = mpart ? col0 - kD : col0;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int64_t rowstride = (int64_t)H * kD;
+  const int nch = (cd.ntok + kC - 1) / kC;
 
   // state rows 16*(2wv+rt) + 4lg + i, columns vcol0 + 16ct + lr
   f32x4 sacc[2][NCT];
@@ -363,127 +431,123 @@ __global__ __launch_bounds__(kThreads) void k2_kernel(
         }
   }
 
-  for (int ch = 0; ch < cd.nchunks; ++ch) {
-    const int gci = cd.chunk0 + ch;
-    const ChunkDesc chd = chunks[gci];
-    const uint8_t *rec = ws + ((int64_t)gci * H + h) * RB;
-    const T *Qd = reinterpret_cast<const T *>(rec + off.qd);
-    const T *Kd = reinterpret_cast<const T *>(rec + off.kd);
-    const T *KrT = reinterpret_cast<const T *>(rec + off.krt);
-    const T *INVb = reinterpret_cast<const T *>(rec + off.invb);
-    const T *Mqk = reinterpret_cast<const T *>(rec + off.mqk);
-    const float *ac = reinterpret_cast<const float *>(rec + off.ac);
+  if (nch > 0) {
+    const T *vchain = v + cd.tok0 * rowstride + (int64_t)h * kD + vcol0;
+    const uint8_t *rec0 = ws + ((int64_t)cd.chunk0 * H + h) * RB;
+    ChunkOps<T, NCT> cur, nxt;
+    load_chunk_ops<T, MODE, NCT>(cur, rec0, vchain, min(kC, cd.ntok), rowstride, wv, lr, lg);
 
-    // (1) S -> Sb (MFMA B operand, K = channel)
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-        store4(&Sb[16 * ct + lr][16 * (2 * wv + rt) + 4 * lg], sacc[rt][ct][0],
-               sacc[rt][ct][1], sacc[rt][ct][2], sacc[rt][ct][3]);
-    __syncthreads();
+    for (int ch = 0; ch < nch; ++ch) {
+      const int len = min(kC, cd.ntok - ch * kC);
+      const int64_t tok = cd.tok0 + (int64_t)ch * kC;
+      {
+        // prefetch chunk ch+1 (the last chunk reloads itself; harmless)
+        const int cn = min(ch + 1, nch - 1);
+        load_chunk_ops<T, MODE, NCT>(nxt, rec0 + (int64_t)cn * H * RB,
+                                     vchain + (int64_t)cn * kC * rowstride,
+                                     min(kC, cd.ntok - cn * kC), rowstride, wv, lr, lg);
+      }
 
-    // (2) W = K_decay S and (mode 0) O = Q_decay S for token tile wv
-    f32x4 W[NCT], Oa[NCT];
+      // (1) S -> Sb (MFMA B operand, K = channel)
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      W[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      Oa[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+      for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int kb = 32 * s + 8 * lg;
-      const Frag<T> akd = load_frag(Kd + (16 * wv + lr) * kD + kb);
-      Frag<T> aqd;
-      if (MODE == 0)
-        aqd = load_frag(Qd + (16 * wv + lr) * kD + kb);
+        for (int ct = 0; ct < NCT; ++ct)
+          store4(&Sb[16 * ct + lr][16 * (2 * wv + rt) + 4 * lg], sacc[rt][ct][0],
+                 sacc[rt][ct][1], sacc[rt][ct][2], sacc[rt][ct][3]);
+      lds_sync();
+
+      // (2) W = K_decay S and (mode 0) O = Q_decay S for token tile wv
+      f32x4 W[NCT], Oa[NCT];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const Frag<T> b = load_frag(&Sb[16 * ct + lr][kb]);
-        mma(W[ct], akd, b);
-        if (MODE == 0)
-          mma(Oa[ct], aqd, b);
+        W[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Oa[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-    }
-
-    // (3) V - W -> VWb (B operand, K = token)
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const int col = 16 * ct + lr;
-      float x[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * wv + 4 * lg + i;
-        float vv = 0.f;
-        if (!mpart && row < chd.len)
-          vv = to_f32(v[(chd.tok0 + row) * rowstride + (int64_t)h * kD + vcol0 + col]);
-        x[i] = vv - W[ct][i];
-      }
-      store4(&VWb[col][16 * wv + 4 * lg], x[0], x[1], x[2], x[3]);
-    }
-    __syncthreads();
-
-    // (4) U = INV Diag(beta) (V - W)
-    f32x4 U[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-      U[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int kb = 32 * s + 8 * lg;
-      const Frag<T> a = load_frag(INVb + (16 * wv + lr) * kC + kb);
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const Frag<T> b = load_frag(&VWb[16 * ct + lr][kb]);
-        mma(U[ct], a, b);
-      }
-    }
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-      store4(&Ub[16 * ct + lr][16 * wv + 4 * lg], U[ct][0], U[ct][1], U[ct][2], U[ct][3]);
-    __syncthreads();
-
-    // (5) O = Q_decay S + M_qk U
-    if (MODE == 0) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int s = 0; s < 4; ++s) {
         const int kb = 32 * s + 8 * lg;
-        const Frag<T> a = load_frag(Mqk + (16 * wv + lr) * kC + kb);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-          const Frag<T> b = load_frag(&Ub[16 * ct + lr][kb]);
-          mma(Oa[ct], a, b);
+          const Frag<T> b = load_frag(&Sb[16 * ct + lr][kb]);
+          mma(W[ct], cur.kd[s], b);
+          if (MODE == 0)
+            mma(Oa[ct], cur.qd[s], b);
         }
       }
+
+      // (3) V - W -> VWb (B operand, K = token)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
+      for (int ct = 0; ct < NCT; ++ct) {
+        float x[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = 16 * wv + 4 * lg + i;
-          if (row < chd.len)
-            o[(chd.tok0 + row) * rowstride + (int64_t)h * kD + vcol0 + 16 * ct + lr] =
-                from_f32<T>(Oa[ct][i]);
+          const float vv = (!mpart && row < len) ? to_f32(cur.v[ct][i]) : 0.f;
+          x[i] = vv - W[ct][i];
         }
-    }
+        store4(&VWb[16 * ct + lr][16 * wv + 4 * lg], x[0], x[1], x[2], x[3]);
+      }
+      lds_sync();
 
-    // (6) S = Diag(a_last) S + K_restore^T U
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int r0 = 16 * (2 * wv + rt);
-      const f32x4 a4 = *reinterpret_cast<const f32x4 *>(ac + r0 + 4 * lg);
+      // (4) U = INV Diag(beta) (V - W)
+      f32x4 U[NCT];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
-        sacc[rt][ct] *= a4;
+        U[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int kb = 32 * s + 8 * lg;
-        const Frag<T> a = load_frag(KrT + (r0 + lr) * kC + kb);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-          const Frag<T> b = load_frag(&Ub[16 * ct + lr][kb]);
-          mma(sacc[rt][ct], a, b);
+          const Frag<T> b = load_frag(&VWb[16 * ct + lr][kb]);
+          mma(U[ct], cur.invb[s], b);
         }
       }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+        store4(&Ub[16 * ct + lr][16 * wv + 4 * lg], U[ct][0], U[ct][1], U[ct][2], U[ct][3]);
+      lds_sync();
+
+      // (5) O = Q_decay S + M_qk U
+      if (MODE == 0) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int kb = 32 * s + 8 * lg;
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) {
+            const Frag<T> b = load_frag(&Ub[16 * ct + lr][kb]);
+            mma(Oa[ct], cur.mqk[s], b);
+          }
+        }
+        T *orow = o + tok * rowstride + (int64_t)h * kD + vcol0;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 16 * wv + 4 * lg + i;
+            if (row < len)
+              orow[(int64_t)row * rowstride + 16 * ct + lr] = from_f32<T>(Oa[ct][i]);
+          }
+      }
+
+      // (6) S = Diag(a_last) S + K_restore^T U
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+          sacc[rt][ct] *= cur.ac[rt];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int kb = 32 * s + 8 * lg;
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) {
+            const Frag<T> b = load_frag(&Ub[16 * ct + lr][kb]);
+            mma(sacc[rt][ct], cur.krt[rt][s], b);
+          }
+        }
+      }
+      cur = nxt;
     }
   }
 
@@ -563,21 +627,23 @@ hipError_t launch_k1(int elt, const ChunkDesc *chunks, int32_t nchunks, int32_t 
   if (nchunks == 0)
     return hipSuccess;
   dim3 grid((unsigned)nchunks, (unsigned)H), block(kThreads);
+  // without q, k stands in as a readable buffer of the same shape
+  const int has_q = q != nullptr;
+  const void *qq = has_q ? q : k;
   if (elt == 1)
-    k1_kernel<bf16><<<grid, block, 0, s>>>(chunks, H, (const bf16 *)q, (const bf16 *)k,
+    k1_kernel<bf16><<<grid, block, 0, s>>>(chunks, H, (const bf16 *)qq, (const bf16 *)k,
                                            (const bf16 *)g, (const bf16 *)beta,
-                                           (uint8_t *)ws);
+                                           (uint8_t *)ws, has_q);
   else
-    k1_kernel<float><<<grid, block, 0, s>>>(chunks, H, (const float *)q, (const float *)k,
+    k1_kernel<float><<<grid, block, 0, s>>>(chunks, H, (const float *)qq, (const float *)k,
                                             (const float *)g, (const float *)beta,
-                                            (uint8_t *)ws);
+                                            (uint8_t *)ws, has_q);
   return hipGetLastError();
 }
 
-hipError_t launch_k2(int elt, int mode, const ChainDesc *chains, int32_t nchains,
-                     const ChunkDesc *chunks, int32_t H, const void *ws, const void *v, void *o,
-                     const float *init, const float *sin, float *final_a, float *final_b,
-                     hipStream_t s) {
+hipError_t launch_k2(int elt, int mode, const ChainDesc *chains, int32_t nchains, int32_t H,
+                     const void *ws, const void *v, void *o, const float *init,
+                     const float *sin, float *final_a, float *final_b, hipStream_t s) {
   if (nchains == 0)
     return hipSuccess;
   const unsigned width = mode == 1 ? 2 * kD : kD;
@@ -585,17 +651,17 @@ hipError_t launch_k2(int elt, int mode, const ChainDesc *chains, int32_t nchains
   const uint8_t *w = (const uint8_t *)ws;
   if (elt == 1) {
     if (mode == 1)
-      k2_kernel<bf16, 1><<<grid, block, 0, s>>>(chains, chunks, H, w, (const bf16 *)v,
+      k2_kernel<bf16, 1><<<grid, block, 0, s>>>(chains, H, w, (const bf16 *)v,
                                                 (bf16 *)o, init, sin, final_a, final_b);
     else
-      k2_kernel<bf16, 0><<<grid, block, 0, s>>>(chains, chunks, H, w, (const bf16 *)v,
+      k2_kernel<bf16, 0><<<grid, block, 0, s>>>(chains, H, w, (const bf16 *)v,
                                                 (bf16 *)o, init, sin, final_a, final_b);
   } else {
     if (mode == 1)
-      k2_kernel<float, 1><<<grid, block, 0, s>>>(chains, chunks, H, w, (const float *)v,
+      k2_kernel<float, 1><<<grid, block, 0, s>>>(chains, H, w, (const float *)v,
                                                  (float *)o, init, sin, final_a, final_b);
     else
-      k2_kernel<float, 0><<<grid, block, 0, s>>>(chains, chunks, H, w, (const float *)v,
+      k2_kernel<float, 0><<<grid, block, 0, s>>>(chains, H, w, (const float *)v,
                                                  (float *)o, init, sin, final_a, final_b);
   }
   return hipGetLastError();
