@@ -74,6 +74,8 @@ struct Plan {
   std::vector<ChainDesc> segchains; // segment pass (width dk + dv)
   std::vector<ScanDesc> scans;
   int64_t npairs = 0, nsin = 0;
+  // bf16 without a planner split runs the fused kernel: no chunk-prep records
+  bool fused = false;
   // workspace layout
   size_t off_chunks = 0, off_chains = 0, off_seg = 0, off_scan = 0, table_bytes = 0;
   size_t off_rec = 0, off_M = 0, off_St = 0, off_Sin = 0, total = 0;
@@ -91,7 +93,8 @@ void layout(Plan &p, int32_t H, size_t es) {
   o = align_up(o + p.scans.size() * sizeof(ScanDesc));
   p.table_bytes = o;
   p.off_rec = o;
-  o = align_up(o + p.chunks.size() * (size_t)H * k1_record_bytes(es));
+  if (!p.fused)
+    o = align_up(o + p.chunks.size() * (size_t)H * k1_record_bytes(es));
   const size_t mat = (size_t)kD * kD * sizeof(float);
   p.off_M = o;
   o = align_up(o + (size_t)p.npairs * H * mat);
@@ -147,6 +150,7 @@ bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_h
   auto longer = [](const ChainDesc &a, const ChainDesc &b) { return a.ntok > b.ntok; };
   std::stable_sort(p.chains.begin(), p.chains.end(), longer);
   std::stable_sort(p.segchains.begin(), p.segchains.end(), longer);
+  p.fused = es == 2 && p.segchains.empty();
   layout(p, H, es);
   return true;
 }
@@ -342,6 +346,12 @@ kda_status kda_chunk_prefill(int32_t num_seqs, const int64_t *cu_seqlens_host, i
   const int elt = dt == KDA_BF16 ? 1 : 0;
   const ChunkDesc *d_chunks = (const ChunkDesc *)(ws + p.off_chunks);
   hipError_t e = upload_tables(p, ws, s);
+  if (p.fused) {
+    if (e == hipSuccess)
+      e = launch_fused((const ChainDesc *)(ws + p.off_chains), (int32_t)p.chains.size(), H, q,
+                       k, v, g, beta, o, initial_state, nullptr, final_state, s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  }
   if (e == hipSuccess)
     e = launch_k1(elt, d_chunks, (int32_t)p.chunks.size(), H, q, k, g, beta, ws + p.off_rec, s);
   if (e == hipSuccess && !p.segchains.empty()) {

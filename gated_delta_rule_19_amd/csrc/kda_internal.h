@@ -67,6 +67,12 @@ hipError_t launch_k2(int elt, int mode, const ChainDesc *chains, int32_t nchains
                      const void *ws, const void *v, void *o, const float *init,
                      const float *sin, float *final_a, float *final_b, hipStream_t s);
 
+// Fused chunk prep + state chain (bf16, width dv): writes o and exit states.
+hipError_t launch_fused(const ChainDesc *chains, int32_t nchains, int32_t H, const void *q,
+                        const void *k, const void *v, const void *g, const void *beta, void *o,
+                        const float *init, const float *sin, float *final_state,
+                        hipStream_t s);
+
 hipError_t launch_scan(const ScanDesc *descs, int32_t ndesc, int32_t H, const float *Mseg,
                        const float *Stseg, const float *init, float *sin, hipStream_t s);
 
