@@ -27,9 +27,9 @@ using namespace kda;
 namespace {
 
 // Automatic split policy: split only when the unsplit state-carrying work
-// has fewer than kAutoMinChains workgroups, then aim for kAutoSegments
-// segments of at least kAutoMinSegChunks chunks each.
-constexpr int64_t kAutoMinChains = 128;
+// has fewer than kAutoMinChains workgroups (one per sequence-head), then aim
+// for kAutoSegments segments of at least kAutoMinSegChunks chunks each.
+constexpr int64_t kAutoMinChains = 64;
 constexpr int64_t kAutoSegments = 64;
 constexpr int64_t kAutoMinSegChunks = 4;
 
@@ -49,7 +49,7 @@ int64_t plan_nseg(int64_t len, int32_t num_seqs, int32_t H, int32_t split_hint) 
     return 1;
   if (split_hint > 1)
     return std::min<int64_t>(split_hint, nch);
-  const int64_t chains = (int64_t)num_seqs * H * (kD / kBV);
+  const int64_t chains = (int64_t)num_seqs * H;
   if (chains >= kAutoMinChains)
     return 1;
   return std::max<int64_t>(1, std::min<int64_t>(kAutoSegments, nch / kAutoMinSegChunks));
@@ -150,7 +150,9 @@ bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_h
   auto longer = [](const ChainDesc &a, const ChainDesc &b) { return a.ntok > b.ntok; };
   std::stable_sort(p.chains.begin(), p.chains.end(), longer);
   std::stable_sort(p.segchains.begin(), p.segchains.end(), longer);
-  p.fused = es == 2 && p.segchains.empty();
+  // the fused kernel is kept out of the dispatch while it is slower than the
+  // chunk-prep + state-chain pair
+  p.fused = false;
   layout(p, H, es);
   return true;
 }

@@ -44,15 +44,31 @@ struct ScanDesc {
 };
 static_assert(sizeof(ScanDesc) == 16, "ScanDesc layout");
 
+// Column order of the chunk-prep record's MFMA A operands.  Inside each group
+// of 32 logical columns k the element sits at physical position
+//   p(k) = 8 * ((k % 16) / 4) + 4 * (k / 16) + k % 4,
+// so the 8 consecutive elements at 8g .. 8g+7 hold logical columns
+// 4g .. 4g+3 and 16+4g .. 16+4g+3.  Those are exactly the rows that lane
+// group g holds in two stacked 16-row MFMA accumulator tiles, so an
+// accumulator can be fed back as the B operand of the next product without
+// moving data between lanes.
+__host__ __device__ constexpr int kperm(int k) {
+  return (k & ~31) | (((k & 15) >> 2) << 3) | ((k & 16) >> 2) | (k & 3);
+}
+
 // Bytes of the chunk-prep record for one (chunk, head), element size es:
 //   Q_decay [C][D], K_decay [C][D], K_restore^T [D][C], INV*Diag(beta) [C][C],
-//   M_qk [C][C] (all of the element type), a_last [D] fp32; 256-aligned.
+//   M_qk [C][C] (all of the element type, columns in kperm order), a_last
+//   [D] fp32; 256-aligned.
 constexpr size_t k1_record_bytes(size_t es) {
   return ((3 * 64 * 128 + 2 * 64 * 64) * es + 128 * 4 + 255) / 256 * 256;
 }
 
-// Column block of the state-carrying kernel (columns of S per workgroup).
-constexpr int kBV = 64;
+// Column block of the state-carrying kernel (columns of S per workgroup),
+// and the 16-column tiles each of its waves carries.
+constexpr int kBV = 128;
+constexpr int kK2ColTiles = 1;
+constexpr int kK2Threads = kBV / (16 * kK2ColTiles) * 64;
 // Column block of the planner scan kernel.
 constexpr int kScanBV = 8;
 

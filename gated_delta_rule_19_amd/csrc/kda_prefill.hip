@@ -188,21 +188,18 @@ __global__ __launch_bounds__(kThreads) void k1_kernel(const ChunkDesc *__restric
         sKs[r][c] = from_f32<T>(kv * est);
         sKe[r][c] = from_f32<T>(kv * eend);
         const float ga = eloc * eP;            // exp(G_r)
-        Qd[r * kD + c] = from_f32<T>(qv * ga);
-        Kd[r * kD + c] = from_f32<T>(kv * ga);
+        Qd[r * kD + kperm(c)] = from_f32<T>(qv * ga);
+        Kd[r * kD + kperm(c)] = from_f32<T>(kv * ga);
         krv[i] = kv * (eend * eR);             // exp(G_last - G_r) k
       }
     }
-    // K_restore^T row c, tokens half*32 .. +31 (contiguous)
-    T *kr = KrT + c * kC + half * 32;
+    // K_restore^T row c, tokens half*32 .. +31: runs of 4 logical columns
+    // stay contiguous under kperm
+    T *kr = KrT + c * kC;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        x[e] = krv[8 * j + e];
-      store8(kr + 8 * j, x);
-    }
+    for (int j = 0; j < 8; ++j)
+      store4(kr + kperm(half * 32 + 4 * j), krv[4 * j], krv[4 * j + 1], krv[4 * j + 2],
+             krv[4 * j + 3]);
     if (half == 0)
       ac[c] = __expf(pC);
     // off-diagonal factors exp(p_I - p_{J+1}), I > J: 6 pairs x 128 channels
@@ -258,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void k1_kernel(const ChunkDesc *__restric
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * I + 4 * lg + i;
         sL[row][col] = (col < row) ? sBeta[row] * accL[pp][i] : 0.f;
-        Mqk[row * kC + col] = from_f32<T>((col <= row) ? accM[pp][i] : 0.f);
+        Mqk[row * kC + kperm(col)] = from_f32<T>((col <= row) ? accM[pp][i] : 0.f);
       }
     }
   }
@@ -268,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void k1_kernel(const ChunkDesc *__restric
     const int row = 16 * kUpI[t] + r, col = 16 * kUpJ[t] + cc;
     sL[row][col] = 0.f;
     sInv[row][col] = 0.f;
-    Mqk[row * kC + col] = from_f32<T>(0.f);
+    Mqk[row * kC + kperm(col)] = from_f32<T>(0.f);
   }
   lds_sync();
 
@@ -314,103 +311,168 @@ __global__ __launch_bounds__(kThreads) void k1_kernel(const ChunkDesc *__restric
     lds_sync();
   }
 
-  // INV * Diag(beta) to the record, 16 contiguous elements per thread
+  // INV * Diag(beta) to the record, 16 logical columns per thread in runs
+  // of 4 (contiguous under kperm)
   {
     const int row = tid >> 2, c0 = (tid & 3) * 16;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int col = c0 + 8 * j + e;
-        x[e] = sInv[row][col] * sBeta[col];
-      }
-      store8(INVb + row * kC + c0 + 8 * j, x);
+    for (int j = 0; j < 4; ++j) {
+      const int col = c0 + 4 * j;
+      store4(INVb + row * kC + kperm(col), sInv[row][col] * sBeta[col],
+             sInv[row][col + 1] * sBeta[col + 1], sInv[row][col + 2] * sBeta[col + 2],
+             sInv[row][col + 3] * sBeta[col + 3]);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 // K2: state-carrying chain.  One workgroup per (chain, head, column block of
-// kBV state columns).  The columns of V, U, O and S are independent, so a
-// head's state splits across column blocks with no exchange.
+// kBV = 128 state columns); wave w owns the kK2ColTiles 16-column tiles
+// starting at vcol0 + 16 kK2ColTiles w, so one workgroup reads each chunk
+// record once for the whole head, and each A fragment a wave reads from LDS
+// serves all of its column tiles.
+// The columns of V, U, O and S are independent, so each wave carries its own
+// 128-row slice of S through the chunks with no exchange: the state, W, U
+// and O stay in MFMA accumulators, and each accumulator feeds the next
+// product as its B operand directly (the record's A operands are stored in
+// kperm column order to match).  The chunk records are copied into LDS once
+// per workgroup (double-buffered: chunk i+1's record is in flight while
+// chunk i is computed), so the only barrier is one per chunk.
 //   MODE 0: prefill / replay, width dv; writes o and the exit state.
 //   MODE 1: segment pass, width dk + dv of [S~ | M] from [0 | I] with values
 //           [V | 0]; the exit state's S~ part goes to out_a, M part to out_b.
-// The loop is latency-bound (S -> W -> U -> S per chunk), so every global
-// operand of chunk i+1 is loaded into registers while chunk i is computed,
-// and the workgroup barriers order LDS only.
 // ---------------------------------------------------------------------------
-template <typename T, int NCT> struct ChunkOps {
-  Frag<T> kd[4], qd[4], invb[2], mqk[2], krt[2][2];
-  f32x4 ac[2];
-  T v[NCT][4];
-};
-
-template <typename T, int MODE, int NCT>
-__device__ __forceinline__ void load_chunk_ops(ChunkOps<T, NCT> &op, const uint8_t *rec,
-                                               const T *vbase, int len, int64_t rowstride,
-                                               int wv, int lr, int lg) {
-  constexpr RecOff off(sizeof(T));
-  const T *Qd = reinterpret_cast<const T *>(rec + off.qd);
-  const T *Kd = reinterpret_cast<const T *>(rec + off.kd);
-  const T *KrT = reinterpret_cast<const T *>(rec + off.krt);
-  const T *INVb = reinterpret_cast<const T *>(rec + off.invb);
-  const T *Mqk = reinterpret_cast<const T *>(rec + off.mqk);
-  const float *ac = reinterpret_cast<const float *>(rec + off.ac);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    op.kd[s] = load_frag(Kd + (16 * wv + lr) * kD + 32 * s + 8 * lg);
-    if (MODE == 0)
-      op.qd[s] = load_frag(Qd + (16 * wv + lr) * kD + 32 * s + 8 * lg);
-  }
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    op.invb[s] = load_frag(INVb + (16 * wv + lr) * kC + 32 * s + 8 * lg);
-    if (MODE == 0)
-      op.mqk[s] = load_frag(Mqk + (16 * wv + lr) * kC + 32 * s + 8 * lg);
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-      op.krt[rt][s] = load_frag(KrT + (16 * (2 * wv + rt) + lr) * kC + 32 * s + 8 * lg);
-  }
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-    op.ac[rt] = *reinterpret_cast<const f32x4 *>(ac + 16 * (2 * wv + rt) + 4 * lg);
-  // V rows clamped into the chunk (rows past its end are zeroed at use)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rr = min(16 * wv + 4 * lg + i, len - 1);
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-      op.v[ct][i] = vbase[(int64_t)rr * rowstride + 16 * ct + lr];
-  }
+template <typename T>
+__device__ __forceinline__ Frag<T> pack_acc_pair(const f32x4 &lo, const f32x4 &hi) {
+  const float x[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return frag_from_f32<T>(x);
 }
 
+// LDS image of a chunk record: the same sections, each row padded by 16
+// bytes so that the 16 rows one wave reads per MFMA fragment start in
+// different LDS banks (a 256- or 128-byte row stride would put them all in
+// the same banks).
+template <typename T> struct RecLds {
+  static constexpr int es = sizeof(T);
+  static constexpr int rowD = kD * es, rowC = kC * es;     // global row bytes
+  static constexpr int padD = rowD + 16, padC = rowC + 16; // LDS row bytes
+  static constexpr int qd = 0;
+  static constexpr int kd = qd + kC * padD;
+  static constexpr int krt = kd + kC * padD;
+  static constexpr int invb = krt + kD * padC;
+  static constexpr int mqk = invb + kC * padC;
+  static constexpr int ac = mqk + kC * padC;
+  static constexpr int bytes = ac + kD * 4;
+  static constexpr int blocks = (bytes + 1023) / 1024;
+};
+
+// Gather offset inside one padded section: LDS byte q of a section with
+// PAD-byte rows holds record byte base_g + r ROW + c (r = q / PAD, c = q % PAD);
+// padding bytes (c >= ROW) read record byte 0.
+template <int PAD, int ROW>
+__device__ __forceinline__ int section_src(int q, int base_g) {
+  const int r = q / PAD, c = q - r * PAD;
+  return c < ROW ? base_g + r * ROW + c : 0;
+}
+
+// Raw buffer resource over `bytes` bytes at p: loads past the end read 0,
+// stores past the end are dropped, and offsets are 32-bit.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l reads at byte
+// voff (its own) and writes LDS bytes 16 l .. 16 l + 15 after the
+// wave-uniform LDS base.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, int voff, uint8_t *lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void *)lds_base, 16, voff, 0, 0, 0);
+}
+
+// One element to a buffer at byte voff + soff (soff wave-uniform).
+__device__ __forceinline__ void buffer_store(__amdgpu_buffer_rsrc_t r, bf16 x, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, x), r, voff, soff, 0);
+}
+__device__ __forceinline__ void buffer_store(__amdgpu_buffer_rsrc_t r, float x, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, x), r, voff, soff, 0);
+}
+
+// Copy of one chunk record (global) into its padded LDS image with
+// direct-to-LDS loads: wave w fills 1 KiB blocks w, w + NW, ...; lane l of a
+// block writes LDS bytes 16 l .. 16 l + 15, gathered from wherever they live
+// in the record.  Every section of the image starts on a 1 KiB boundary, so
+// a block lies in one section, chosen by a wave-uniform branch.  Completion
+// is awaited with vmcnt(0).
+template <typename T, int NW> struct RecordCopy {
+  using L = RecLds<T>;
+  static_assert(L::kd % 1024 == 0 && L::krt % 1024 == 0 && L::invb % 1024 == 0 &&
+                    L::mqk % 1024 == 0 && L::ac % 1024 == 0,
+                "sections must start on 1 KiB blocks");
+  __device__ __forceinline__ static void issue(uint8_t *lds, const uint8_t *src, int wv,
+                                               int lane) {
+    constexpr RecOff off(sizeof(T));
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(src, (uint32_t)k1_record_bytes(sizeof(T)));
+#pragma unroll
+    for (int j = 0; j < (L::blocks + NW - 1) / NW; ++j) {
+      const int b = wv + j * NW; // wave-uniform
+      if (b >= L::blocks)
+        break;
+      const int p = b * 1024 + lane * 16;
+      int g;
+      if (b * 1024 < L::kd)
+        g = section_src<L::padD, L::rowD>(p - L::qd, (int)off.qd);
+      else if (b * 1024 < L::krt)
+        g = section_src<L::padD, L::rowD>(p - L::kd, (int)off.kd);
+      else if (b * 1024 < L::invb)
+        g = section_src<L::padC, L::rowC>(p - L::krt, (int)off.krt);
+      else if (b * 1024 < L::mqk)
+        g = section_src<L::padC, L::rowC>(p - L::invb, (int)off.invb);
+      else if (b * 1024 < L::ac)
+        g = section_src<L::padC, L::rowC>(p - L::mqk, (int)off.mqk);
+      else
+        g = p - L::ac < kD * 4 ? (int)off.ac + (p - L::ac) : 0;
+      lds_load16(r, g, lds + b * 1024);
+    }
+  }
+};
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 template <typename T, int MODE>
-__global__ __launch_bounds__(kThreads) void k2_kernel(
+__global__ __launch_bounds__(kK2Threads) void k2_kernel(
     const ChainDesc *__restrict__ chains, int32_t H, const uint8_t *__restrict__ ws,
     const T *__restrict__ v, T *__restrict__ o, const float *__restrict__ init,
     const float *__restrict__ sin, float *__restrict__ out_a, float *__restrict__ out_b) {
-  constexpr int P = pad_elems<T>();
-  constexpr int LDS_S = kD + P; // Sb row stride: [col][channel]
-  constexpr int LDS_C = kC + P; // VWb / Ub row stride: [col][token]
-  constexpr int NCT = kBV / 16;
-  constexpr size_t RB = k1_record_bytes(sizeof(T));
-  __shared__ __attribute__((aligned(16))) T Sb[kBV][LDS_S];
-  __shared__ __attribute__((aligned(16))) T VWb[kBV][LDS_C];
-  __shared__ __attribute__((aligned(16))) T Ub[kBV][LDS_C];
+  constexpr int NW = kK2Threads / 64;
+  constexpr int NCT = kK2ColTiles;
+  using L = RecLds<T>;
+  constexpr int RB = (int)k1_record_bytes(sizeof(T));
+  constexpr int RBP = L::blocks * 1024; // LDS image, whole 1 KiB blocks
+  constexpr int NBUF = 2 * RBP <= 160 * 1024 ? 2 : 1;
+  constexpr int LD = L::padD / (int)sizeof(T); // padded row length, 128-wide rows
+  constexpr int LC = L::padC / (int)sizeof(T); // padded row length, 64-wide rows
+  __shared__ __attribute__((aligned(1024))) uint8_t srecA[RBP];
+  __shared__ __attribute__((aligned(1024))) uint8_t srecB[NBUF == 2 ? RBP : 1];
+  // bf16: each wave's own 64 x VW slice of the chunk's v also goes through
+  // LDS (direct-to-LDS loads, 16 bytes per lane); fp32 keeps it in registers
+  // (its record is single-buffered and leaves no room).
+  constexpr bool VLDS = NBUF == 2;
+  constexpr int VW = 16 * NCT;
+  __shared__ __attribute__((aligned(16))) T sv[VLDS ? NW : 1][VLDS ? kC * VW : 1];
 
   const ChainDesc cd = chains[blockIdx.x];
   const int h = blockIdx.y;
   const int col0 = blockIdx.z * kBV;
   const bool mpart = (MODE == 1) && (col0 >= kD);
   const int vcol0 = mpart ? col0 - kD : col0;
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wcol = vcol0 + 16 * NCT * wv + lr; // this lane's column in tile c: wcol + 16c
   const int64_t rowstride = (int64_t)H * kD;
   const int nch = (cd.ntok + kC - 1) / kC;
 
-  // state rows 16*(2wv+rt) + 4lg + i, columns vcol0 + 16ct + lr
-  f32x4 sacc[2][NCT];
+  // S[c][ct]: rows 16 ct + 4 lg + i (ct = 0..7), column wcol + 16 c
+  f32x4 S[NCT][8];
   {
     const float *ip = nullptr;
     if (MODE == 0) {
@@ -420,134 +482,307 @@ __global__ __launch_bounds__(kThreads) void k2_kernel(
         ip = sin + ((int64_t)(-2 - cd.init_idx) * H + h) * (kD * kD);
     }
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int c = 0; c < NCT; ++c)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
+      for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = 16 * (2 * wv + rt) + 4 * lg + i;
-          const int col = vcol0 + 16 * ct + lr;
-          sacc[rt][ct][i] = ip ? ip[row * kD + col] : ((mpart && row == col) ? 1.f : 0.f);
+          const int row = 16 * ct + 4 * lg + i, col = wcol + 16 * c;
+          S[c][ct][i] = ip ? ip[row * kD + col] : ((mpart && row == col) ? 1.f : 0.f);
         }
   }
 
   if (nch > 0) {
-    const T *vchain = v + cd.tok0 * rowstride + (int64_t)h * kD + vcol0;
     const uint8_t *rec0 = ws + ((int64_t)cd.chunk0 * H + h) * RB;
-    ChunkOps<T, NCT> cur, nxt;
-    load_chunk_ops<T, MODE, NCT>(cur, rec0, vchain, min(kC, cd.ntok), rowstride, wv, lr, lg);
-
-    for (int ch = 0; ch < nch; ++ch) {
-      const int len = min(kC, cd.ntok - ch * kC);
-      const int64_t tok = cd.tok0 + (int64_t)ch * kC;
-      {
-        // prefetch chunk ch+1 (the last chunk reloads itself; harmless)
-        const int cn = min(ch + 1, nch - 1);
-        load_chunk_ops<T, MODE, NCT>(nxt, rec0 + (int64_t)cn * H * RB,
-                                     vchain + (int64_t)cn * kC * rowstride,
-                                     min(kC, cd.ntok - cn * kC), rowstride, wv, lr, lg);
-      }
-
-      // (1) S -> Sb (MFMA B operand, K = channel)
+    const int64_t rec_step = (int64_t)H * RB;
+    const T *vchain = v + cd.tok0 * rowstride + (int64_t)h * kD + wcol;
+    // v of one chunk for this lane: rows 16 tt + 4 lg + i (clamped into the
+    // chunk), column wcol + 16 c
+    auto load_v = [&](T (&dst)[NCT][4][4], int chunk) {
+      const int len = min(kC, cd.ntok - chunk * kC);
+      const T *vb = vchain + (int64_t)chunk * kC * rowstride;
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-          store4(&Sb[16 * ct + lr][16 * (2 * wv + rt) + 4 * lg], sacc[rt][ct][0],
-                 sacc[rt][ct][1], sacc[rt][ct][2], sacc[rt][ct][3]);
-      lds_sync();
-
-      // (2) W = K_decay S and (mode 0) O = Q_decay S for token tile wv
-      f32x4 W[NCT], Oa[NCT];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        W[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-        Oa[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int kb = 32 * s + 8 * lg;
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          const Frag<T> b = load_frag(&Sb[16 * ct + lr][kb]);
-          mma(W[ct], cur.kd[s], b);
-          if (MODE == 0)
-            mma(Oa[ct], cur.qd[s], b);
-        }
-      }
-
-      // (3) V - W -> VWb (B operand, K = token)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        float x[4];
+      for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = 16 * wv + 4 * lg + i;
-          const float vv = (!mpart && row < len) ? to_f32(cur.v[ct][i]) : 0.f;
-          x[i] = vv - W[ct][i];
+          const T *vr = vb + (int64_t)min(16 * tt + 4 * lg + i, len - 1) * rowstride;
+#pragma unroll
+          for (int c = 0; c < NCT; ++c)
+            dst[c][tt][i] = vr[16 * c];
         }
-        store4(&VWb[16 * ct + lr][16 * wv + 4 * lg], x[0], x[1], x[2], x[3]);
-      }
-      lds_sync();
-
-      // (4) U = INV Diag(beta) (V - W)
-      f32x4 U[NCT];
+    };
+    // bf16 path: rows 0..63 of this wave's VW columns of one chunk into its
+    // LDS slice; lane l of instruction j moves 16 bytes (8 columns) of row
+    // (64 j + l) / (2 NCT); rows past the chunk end read as 0
+    auto v_to_lds = [&](int chunk) {
+      if constexpr (VLDS) {
+        if (mpart)
+          return;
+        const int clen = min(kC, cd.ntok - chunk * kC);
+        const T *vb = v + (cd.tok0 + (int64_t)chunk * kC) * rowstride + (int64_t)h * kD +
+                      vcol0 + VW * wv;
+        const __amdgpu_buffer_rsrc_t rv =
+            buffer_rsrc(vb, (uint32_t)((clen - 1) * rowstride + VW) * sizeof(T));
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-        U[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int kb = 32 * s + 8 * lg;
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          const Frag<T> b = load_frag(&VWb[16 * ct + lr][kb]);
-          mma(U[ct], cur.invb[s], b);
+        for (int j = 0; j < 2 * NCT; ++j) {
+          const int u = 64 * j + lane, r = u / (2 * NCT), q = u % (2 * NCT);
+          lds_load16(rv, (int)((r * rowstride + 8 * q) * sizeof(T)),
+                     reinterpret_cast<uint8_t *>(&sv[wv][0]) + 1024 * j);
         }
       }
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-        store4(&Ub[16 * ct + lr][16 * wv + 4 * lg], U[ct][0], U[ct][1], U[ct][2], U[ct][3]);
-      lds_sync();
+    };
+    using RCopy = RecordCopy<T, NW>;
+    RCopy::issue(srecA, rec0, wv, lane);
+    T vcur[VLDS ? 1 : NCT][4][4];
+    if constexpr (VLDS)
+      v_to_lds(0);
+    else
+      load_v(vcur, 0);
+    wait_vmem();
+    __syncthreads();
 
-      // (5) O = Q_decay S + M_qk U
-      if (MODE == 0) {
+    // One chunk: computes from the record image in `cur` while chunk ch+1's
+    // record goes into `nxt`.  The buffers are distinct LDS objects and the
+    // loop is unrolled by two, so every access names its buffer statically
+    // and the compiler does not make reads of `cur` wait for the copy.
+    auto chunk_step = [&](const int ch, uint8_t *cur, uint8_t *nxt)
+                          __attribute__((always_inline)) {
+      const int len = min(kC, cd.ntok - ch * kC);
+      const int64_t tok = cd.tok0 + (int64_t)ch * kC;
+      const bool more = ch + 1 < nch;
+      // chunk ch+1: its record straight into the other LDS buffer (fp32:
+      // its v into registers); in flight while chunk ch is computed
+      T vnxt[VLDS ? 1 : NCT][4][4];
+      // (v first: a wait the compiler places before these register loads
+      // must not cover the record copy)
+      if (more) {
+        if constexpr (!VLDS)
+          load_v(vnxt, ch + 1);
+        if (NBUF == 2)
+          RCopy::issue(nxt, rec0 + (int64_t)(ch + 1) * rec_step, wv, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0); // keep the loads issued here, ahead of the math
+
+      const uint8_t *R = cur;
+      const T *Qd = reinterpret_cast<const T *>(R + L::qd);
+      const T *Kd = reinterpret_cast<const T *>(R + L::kd);
+      const T *KrT = reinterpret_cast<const T *>(R + L::krt);
+      const T *INVb = reinterpret_cast<const T *>(R + L::invb);
+      const T *Mqk = reinterpret_cast<const T *>(R + L::mqk);
+      const float *ac = reinterpret_cast<const float *>(R + L::ac);
+
+      // Every product runs its k-steps in the outer loop, so the 4 to 8
+      // accumulators of a step are independent MFMAs, and the A fragments of
+      // the next step (or phase) are read from LDS before the current step's
+      // MFMAs are issued.
+      auto frag = [&](const T *base, int ld, int tile, int s) {
+        return load_frag(base + (16 * tile + lr) * ld + 32 * s + 8 * lg);
+      };
+
+      // W = K_decay S, O = Q_decay S (K = channels, B operand = S)
+      Frag<T> bs[NCT][4];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int kb = 32 * s + 8 * lg;
+      for (int c = 0; c < NCT; ++c)
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) {
-            const Frag<T> b = load_frag(&Ub[16 * ct + lr][kb]);
-            mma(Oa[ct], cur.mqk[s], b);
+        for (int s = 0; s < 4; ++s)
+          bs[c][s] = pack_acc_pair<T>(S[c][2 * s], S[c][2 * s + 1]);
+      f32x4 W[NCT][4], Oa[NCT][4];
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          W[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          Oa[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      Frag<T> ak[4], aq[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        ak[tt] = frag(Kd, LD, tt, 0);
+        if (MODE == 0)
+          aq[tt] = frag(Qd, LD, tt, 0);
+      }
+      Frag<T> ai[2][4]; // INV Diag(beta) fragments, read during the last step
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        Frag<T> nk[4], nq[4];
+        if (s < 3) {
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            nk[tt] = frag(Kd, LD, tt, s + 1);
+            if (MODE == 0)
+              nq[tt] = frag(Qd, LD, tt, s + 1);
+          }
+        } else {
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            ai[0][tt] = frag(INVb, LC, tt, 0);
+            ai[1][tt] = frag(INVb, LC, tt, 1);
           }
         }
-        T *orow = o + tok * rowstride + (int64_t)h * kD + vcol0;
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int c = 0; c < NCT; ++c) {
+            mma(W[c][tt], ak[tt], bs[c][s]);
+            if (MODE == 0)
+              mma(Oa[c][tt], aq[tt], bs[c][s]);
+          }
+        if (s < 3) {
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            ak[tt] = nk[tt];
+            aq[tt] = nq[tt];
+          }
+        }
+      }
+      // V - W, then U = INV Diag(beta) (V - W)  (K = tokens)
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int row = 16 * wv + 4 * lg + i;
-            if (row < len)
-              orow[(int64_t)row * rowstride + 16 * ct + lr] = from_f32<T>(Oa[ct][i]);
+            const int row = 16 * tt + 4 * lg + i;
+            float vv;
+            if constexpr (VLDS)
+              vv = to_f32(sv[wv][row * VW + 16 * c + lr]);
+            else
+              vv = to_f32(vcur[c][tt][i]);
+            W[c][tt][i] = (!mpart && row < len ? vv : 0.f) - W[c][tt][i];
+          }
+      // bf16: this wave's slice of v is consumed; chunk ch+1's goes in now
+      if constexpr (VLDS) {
+        if (more) {
+          __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0): the slice reads have returned
+          v_to_lds(ch + 1);
+        }
+      }
+      Frag<T> bw[NCT][2];
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          bw[c][s] = pack_acc_pair<T>(W[c][2 * s], W[c][2 * s + 1]);
+      Frag<T> am[2][4]; // M_qk fragments, read while U is computed
+      if (MODE == 0) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          am[0][tt] = frag(Mqk, LC, tt, 0);
+          am[1][tt] = frag(Mqk, LC, tt, 1);
+        }
+      }
+      f32x4 U[NCT][4];
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          U[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int c = 0; c < NCT; ++c)
+            mma(U[c][tt], ai[s][tt], bw[c][s]);
+      Frag<T> bu[NCT][2];
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          bu[c][s] = pack_acc_pair<T>(U[c][2 * s], U[c][2 * s + 1]);
+      // K_restore^T fragments of the first half of the state update, read
+      // while O is finished
+      Frag<T> ar[2][4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        ar[0][ct] = frag(KrT, LC, ct, 0);
+        ar[1][ct] = frag(KrT, LC, ct, 1);
+      }
+      // O = Q_decay S + M_qk U
+      if (MODE == 0) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int c = 0; c < NCT; ++c)
+              mma(Oa[c][tt], am[s][tt], bu[c][s]);
+        // rows past the chunk end fall outside the buffer and are dropped
+        const __amdgpu_buffer_rsrc_t ro =
+            buffer_rsrc(o + tok * rowstride + (int64_t)h * kD,
+                        (uint32_t)((len - 1) * rowstride + kD) * sizeof(T));
+        const int vo = (int)((4 * lg * rowstride + wcol) * sizeof(T));
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int so = (int)((16 * tt + i) * rowstride * sizeof(T)); // wave-uniform
+#pragma unroll
+            for (int c = 0; c < NCT; ++c)
+              buffer_store(ro, from_f32<T>(Oa[c][tt][i]), vo + 16 * c * (int)sizeof(T), so);
           }
       }
-
-      // (6) S = Diag(a_last) S + K_restore^T U
+      // S = Diag(a_last) S + K_restore^T U, in two halves of 4 row tiles
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
+      for (int hf = 0; hf < 2; ++hf) {
+        Frag<T> nr[2][4];
+        if (hf == 0) {
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-          sacc[rt][ct] *= cur.ac[rt];
+          for (int ct = 0; ct < 4; ++ct) {
+            nr[0][ct] = frag(KrT, LC, ct + 4, 0);
+            nr[1][ct] = frag(KrT, LC, ct + 4, 1);
+          }
+        }
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int kb = 32 * s + 8 * lg;
+        for (int ct = 0; ct < 4; ++ct) {
+          const f32x4 a4 = *reinterpret_cast<const f32x4 *>(ac + 16 * (4 * hf + ct) + 4 * lg);
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) {
-            const Frag<T> b = load_frag(&Ub[16 * ct + lr][kb]);
-            mma(sacc[rt][ct], cur.krt[rt][s], b);
+          for (int c = 0; c < NCT; ++c)
+            S[c][4 * hf + ct] *= a4;
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int c = 0; c < NCT; ++c)
+              mma(S[c][4 * hf + ct], ar[s][ct], bu[c][s]);
+        if (hf == 0) {
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            ar[0][ct] = nr[0][ct];
+            ar[1][ct] = nr[1][ct];
           }
         }
       }
-      cur = nxt;
+
+      if (more) {
+        if (NBUF == 1) {
+          __syncthreads(); // every wave is done with the record
+          RCopy::issue(cur, rec0 + (int64_t)(ch + 1) * rec_step, wv, lane);
+        }
+        wait_vmem();
+        __syncthreads();
+        if constexpr (!VLDS) {
+#pragma unroll
+          for (int c = 0; c < NCT; ++c)
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                vcur[c][tt][i] = vnxt[c][tt][i];
+        }
+      }
+    };
+    if constexpr (NBUF == 2) {
+      for (int ch = 0; ch < nch; ch += 2) {
+        chunk_step(ch, srecA, srecB);
+        if (ch + 1 < nch)
+          chunk_step(ch + 1, srecB, srecA);
+      }
+    } else {
+      for (int ch = 0; ch < nch; ++ch)
+        chunk_step(ch, srecA, srecA);
     }
   }
 
@@ -558,14 +793,12 @@ __global__ __launch_bounds__(kThreads) void k2_kernel(
   }
   if (fp) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int c = 0; c < NCT; ++c)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
+      for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * (2 * wv + rt) + 4 * lg + i;
-          fp[row * kD + vcol0 + 16 * ct + lr] = sacc[rt][ct][i];
-        }
+        for (int i = 0; i < 4; ++i)
+          fp[(16 * ct + 4 * lg + i) * kD + wcol + 16 * c] = S[c][ct][i];
   }
 }
 
@@ -647,7 +880,7 @@ hipError_t launch_k2(int elt, int mode, const ChainDesc *chains, int32_t nchains
   if (nchains == 0)
     return hipSuccess;
   const unsigned width = mode == 1 ? 2 * kD : kD;
-  dim3 grid((unsigned)nchains, (unsigned)H, width / kBV), block(kThreads);
+  dim3 grid((unsigned)nchains, (unsigned)H, width / kBV), block(kK2Threads);
   const uint8_t *w = (const uint8_t *)ws;
   if (elt == 1) {
     if (mode == 1)
