@@ -64,11 +64,16 @@ constexpr size_t k1_record_bytes(size_t es) {
   return ((3 * 64 * 128 + 2 * 64 * 64) * es + 128 * 4 + 255) / 256 * 256;
 }
 
-// Column block of the state-carrying kernel (columns of S per workgroup),
-// and the 16-column tiles each of its waves carries.
-constexpr int kBV = 128;
+// Column blocks of the state-carrying kernel (columns of S per workgroup;
+// each of its waves carries kK2ColTiles 16-column tiles).  The wide block
+// reads each chunk record once per head; the narrow one doubles the
+// workgroups (each record is then read twice) for launches with too few
+// chains to give every compute unit one workgroup.
+constexpr int kBVWide = 128;
+constexpr int kBVNarrow = 64;
 constexpr int kK2ColTiles = 1;
-constexpr int kK2Threads = kBV / (16 * kK2ColTiles) * 64;
+constexpr int k2_threads(int bv) { return bv / (16 * kK2ColTiles) * 64; }
+constexpr int kComputeUnits = 256;
 // Column block of the planner scan kernel.
 constexpr int kScanBV = 8;
 

@@ -327,9 +327,9 @@ __global__ __launch_bounds__(kThreads) void k1_kernel(const ChunkDesc *__restric
 
 // ---------------------------------------------------------------------------
 // K2: state-carrying chain.  One workgroup per (chain, head, column block of
-// kBV = 128 state columns); wave w owns the kK2ColTiles 16-column tiles
+// BV = 128 or 64 state columns); wave w owns the kK2ColTiles 16-column tiles
 // starting at vcol0 + 16 kK2ColTiles w, so one workgroup reads each chunk
-// record once for the whole head, and each A fragment a wave reads from LDS
+// record once for its BV columns, and each A fragment a wave reads from LDS
 // serves all of its column tiles.
 // The columns of V, U, O and S are independent, so each wave carries its own
 // 128-row slice of S through the chunks with no exchange: the state, W, U
@@ -438,12 +438,12 @@ template <typename T, int NW> struct RecordCopy {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <typename T, int MODE>
-__global__ __launch_bounds__(kK2Threads) void k2_kernel(
+template <typename T, int MODE, int BV>
+__global__ __launch_bounds__(k2_threads(BV)) void k2_kernel(
     const ChainDesc *__restrict__ chains, int32_t H, const uint8_t *__restrict__ ws,
     const T *__restrict__ v, T *__restrict__ o, const float *__restrict__ init,
     const float *__restrict__ sin, float *__restrict__ out_a, float *__restrict__ out_b) {
-  constexpr int NW = kK2Threads / 64;
+  constexpr int NW = k2_threads(BV) / 64;
   constexpr int NCT = kK2ColTiles;
   using L = RecLds<T>;
   constexpr int RB = (int)k1_record_bytes(sizeof(T));
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(kK2Threads) void k2_kernel(
 
   const ChainDesc cd = chains[blockIdx.x];
   const int h = blockIdx.y;
-  const int col0 = blockIdx.z * kBV;
+  const int col0 = blockIdx.z * BV;
   const bool mpart = (MODE == 1) && (col0 >= kD);
   const int vcol0 = mpart ? col0 - kD : col0;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
@@ -874,29 +874,44 @@ hipError_t launch_k1(int elt, const ChunkDesc *chunks, int32_t nchunks, int32_t 
   return hipGetLastError();
 }
 
+template <int BV>
+static void launch_k2_bv(int elt, int mode, const ChainDesc *chains, int32_t nchains,
+                         int32_t H, const uint8_t *w, const void *v, void *o,
+                         const float *init, const float *sin, float *final_a, float *final_b,
+                         hipStream_t s) {
+  const unsigned width = mode == 1 ? 2 * kD : kD;
+  dim3 grid((unsigned)nchains, (unsigned)H, width / BV), block(k2_threads(BV));
+  if (elt == 1) {
+    if (mode == 1)
+      k2_kernel<bf16, 1, BV><<<grid, block, 0, s>>>(chains, H, w, (const bf16 *)v,
+                                                    (bf16 *)o, init, sin, final_a, final_b);
+    else
+      k2_kernel<bf16, 0, BV><<<grid, block, 0, s>>>(chains, H, w, (const bf16 *)v,
+                                                    (bf16 *)o, init, sin, final_a, final_b);
+  } else {
+    if (mode == 1)
+      k2_kernel<float, 1, BV><<<grid, block, 0, s>>>(chains, H, w, (const float *)v,
+                                                     (float *)o, init, sin, final_a, final_b);
+    else
+      k2_kernel<float, 0, BV><<<grid, block, 0, s>>>(chains, H, w, (const float *)v,
+                                                     (float *)o, init, sin, final_a, final_b);
+  }
+}
+
 hipError_t launch_k2(int elt, int mode, const ChainDesc *chains, int32_t nchains, int32_t H,
                      const void *ws, const void *v, void *o, const float *init,
                      const float *sin, float *final_a, float *final_b, hipStream_t s) {
   if (nchains == 0)
     return hipSuccess;
-  const unsigned width = mode == 1 ? 2 * kD : kD;
-  dim3 grid((unsigned)nchains, (unsigned)H, width / kBV), block(kK2Threads);
+  const int64_t width = mode == 1 ? 2 * kD : kD;
+  const int64_t wide_groups = (int64_t)nchains * H * (width / kBVWide);
   const uint8_t *w = (const uint8_t *)ws;
-  if (elt == 1) {
-    if (mode == 1)
-      k2_kernel<bf16, 1><<<grid, block, 0, s>>>(chains, H, w, (const bf16 *)v,
-                                                (bf16 *)o, init, sin, final_a, final_b);
-    else
-      k2_kernel<bf16, 0><<<grid, block, 0, s>>>(chains, H, w, (const bf16 *)v,
-                                                (bf16 *)o, init, sin, final_a, final_b);
-  } else {
-    if (mode == 1)
-      k2_kernel<float, 1><<<grid, block, 0, s>>>(chains, H, w, (const float *)v,
-                                                 (float *)o, init, sin, final_a, final_b);
-    else
-      k2_kernel<float, 0><<<grid, block, 0, s>>>(chains, H, w, (const float *)v,
-                                                 (float *)o, init, sin, final_a, final_b);
-  }
+  if (wide_groups < kComputeUnits)
+    launch_k2_bv<kBVNarrow>(elt, mode, chains, nchains, H, w, v, o, init, sin, final_a,
+                            final_b, s);
+  else
+    launch_k2_bv<kBVWide>(elt, mode, chains, nchains, H, w, v, o, init, sin, final_a,
+                          final_b, s);
   return hipGetLastError();
 }
 

@@ -80,6 +80,13 @@ def test_prefill_packed_varlen(dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+def test_prefill_many_chains(dtype):
+    # 3 sequences x 96 heads: enough chains for the 128-column state blocks
+    # (the small cases above run the 64-column ones); partial last chunks
+    prefill_vs_oracle([70, 130, 65], 96, dtype, 34, init=True)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_prefill_mild_decay_initial_state_matters(dtype):
     # with mild decay the initial state still weighs on the last outputs
     prefill_vs_oracle([300, 129], 2, dtype, 32, decay="mild", init=True)
