@@ -129,4 +129,84 @@ __device__ __forceinline__ void store8(float *p, const float (&x)[8]) {
   *reinterpret_cast<f32x4 *>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
 }
 
+// Raw buffer resource over `bytes` bytes at p: loads past the end read 0,
+// stores past the end are dropped, and offsets are 32-bit.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l reads at byte
+// voff (its own) and writes LDS bytes 16 l .. 16 l + 15 after the
+// wave-uniform LDS base.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, int voff, uint8_t *lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void *)lds_base, 16, voff, 0, 0, 0);
+}
+
+// One element to a buffer at byte voff + soff (soff wave-uniform).
+__device__ __forceinline__ void buffer_store(__amdgpu_buffer_rsrc_t r, bf16 x, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, x), r, voff, soff, 0);
+}
+__device__ __forceinline__ void buffer_store(__amdgpu_buffer_rsrc_t r, float x, int voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, x), r, voff, soff, 0);
+}
+
+// 4 consecutive elements (8-byte aligned for bf16, 16 for fp32) from a
+// buffer at byte voff, widened to fp32; past the end they read 0.
+__device__ __forceinline__ void buffer_load4(__amdgpu_buffer_rsrc_t r, int voff, const bf16 *,
+                                             float *x) {
+  auto w = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+  x[0] = __builtin_bit_cast(float, w[0] << 16);
+  x[1] = __builtin_bit_cast(float, w[0] & 0xffff0000u);
+  x[2] = __builtin_bit_cast(float, w[1] << 16);
+  x[3] = __builtin_bit_cast(float, w[1] & 0xffff0000u);
+}
+// (the whole vector is bit-cast: this compiler mis-handles a bit-cast of a
+// single vector element, reading element 0 whatever the index)
+__device__ __forceinline__ void buffer_load4(__amdgpu_buffer_rsrc_t r, int voff, const float *,
+                                             float *x) {
+  const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    x[j] = v[j];
+}
+// One element from a buffer at byte voff, widened to fp32 (0 past the end).
+__device__ __forceinline__ float buffer_load1(__amdgpu_buffer_rsrc_t r, int voff, const bf16 *) {
+  const unsigned short w = __builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0);
+  return __builtin_bit_cast(float, (unsigned)w << 16);
+}
+__device__ __forceinline__ float buffer_load1(__amdgpu_buffer_rsrc_t r, int voff, const float *) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
+
+// acc += A * B for 16 x 16 fp32 blocks on v_mfma_f32_16x16x4f32.  A is read
+// from LDS (row-major, 16-byte aligned rows): lane (lr, lg) loads
+// A[lr][4lg .. 4lg+3].  B is held in the MFMA accumulator layout (lane holds
+// B[4lg + i][lr] in element i), which is also a valid B operand: in step i
+// every lane supplies K-index 4lg + i on both sides.  So a product's result
+// feeds the next product directly.  sign = -1 negates A.
+// B is taken by value: acc and B may be the same variable (Y <- Y + A Y).
+__device__ __forceinline__ void mm16_lds_acc(f32x4 &acc, const float *A, int lda, const f32x4 B,
+                                             int lr, int lg, float sign = 1.f) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(A + lr * lda + 4 * lg) * sign;
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], B[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], B[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], B[2], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], B[3], acc, 0, 0, 0);
+}
+
+// Store / load a 16 x 16 fp32 block in the accumulator layout.
+__device__ __forceinline__ void acc_store(float *D, int ld, const f32x4 &x, int lr, int lg) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    D[(4 * lg + i) * ld + lr] = x[i];
+}
+__device__ __forceinline__ f32x4 acc_load(const float *D, int ld, int lr, int lg) {
+  f32x4 x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    x[i] = D[(4 * lg + i) * ld + lr];
+  return x;
+}
+
 } // namespace kda

@@ -151,36 +151,6 @@ __device__ __forceinline__ void prep_load_qk(PrepRaw &raw, const bf16 *q, const 
   }
 }
 
-// acc += A * B for 16 x 16 fp32 blocks on v_mfma_f32_16x16x4f32.  A is read
-// from LDS (row-major, 16-byte aligned rows): lane (lr, lg) loads
-// A[lr][4lg .. 4lg+3].  B is held in the MFMA accumulator layout (lane holds
-// B[4lg + i][lr] in element i), which is also a valid B operand: in step i
-// every lane supplies K-index 4lg + i on both sides.  So a product's result
-// feeds the next product directly.  sign = -1 negates A.
-// B is taken by value: acc and B may be the same variable (Y <- Y + A Y).
-__device__ __forceinline__ void mm16_lds_acc(f32x4 &acc, const float *A, int lda, const f32x4 B,
-                                             int lr, int lg, float sign = 1.f) {
-  const f32x4 a = *reinterpret_cast<const f32x4 *>(A + lr * lda + 4 * lg) * sign;
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], B[0], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], B[1], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], B[2], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], B[3], acc, 0, 0, 0);
-}
-
-// Store / load a 16 x 16 fp32 block in the accumulator layout.
-__device__ __forceinline__ void acc_store(float *D, int ld, const f32x4 &x, int lr, int lg) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    D[(4 * lg + i) * ld + lr] = x[i];
-}
-__device__ __forceinline__ f32x4 acc_load(const float *D, int ld, int lr, int lg) {
-  f32x4 x;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    x[i] = D[(4 * lg + i) * ld + lr];
-  return x;
-}
-
 } // namespace
 
 // ---------------------------------------------------------------------------

@@ -57,7 +57,6 @@ __device__ __constant__ int kOffJ[6] = {0, 0, 1, 0, 1, 2};
 __device__ __constant__ int kUpI[6] = {0, 0, 0, 1, 1, 2};
 __device__ __constant__ int kUpJ[6] = {1, 2, 3, 2, 3, 3};
 
-template <typename T> constexpr int pad_elems() { return 16 / (int)sizeof(T) * 2; }
 
 // Workgroup barrier that orders LDS only: outstanding global loads stay in
 // flight across it (a full __syncthreads() would wait for them too).
@@ -67,48 +66,134 @@ __device__ __forceinline__ void lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// 4 consecutive input elements kept as raw dwords between load and use.
+template <typename T> struct Raw4;
+template <> struct Raw4<bf16> {
+  typedef unsigned int type __attribute__((ext_vector_type(2)));
+  __device__ __forceinline__ static type load(__amdgpu_buffer_rsrc_t r, int voff) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+  }
+  __device__ __forceinline__ static void widen(type w, float *x) {
+    x[0] = __builtin_bit_cast(float, w[0] << 16);
+    x[1] = __builtin_bit_cast(float, w[0] & 0xffff0000u);
+    x[2] = __builtin_bit_cast(float, w[1] << 16);
+    x[3] = __builtin_bit_cast(float, w[1] & 0xffff0000u);
+  }
+};
+template <> struct Raw4<float> {
+  typedef unsigned int type __attribute__((ext_vector_type(4)));
+  __device__ __forceinline__ static type load(__amdgpu_buffer_rsrc_t r, int voff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+  }
+  // (the whole vector is bit-cast: a bit-cast of one element of a vector
+  // reads element 0 whatever the index with this compiler)
+  __device__ __forceinline__ static void widen(type w, float *x) {
+    const f32x4 v = __builtin_bit_cast(f32x4, w);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      x[j] = v[j];
+  }
+};
+
 } // namespace
 
 // ---------------------------------------------------------------------------
-// K1: chunk prep.  One workgroup per (chunk, head), chunk-parallel.  With
-// has_q == 0 (segment transitions need no outputs) q is not a real input:
-// Q_decay and M_qk are then 0.
+// K1: chunk prep, chunk-parallel.  A persistent grid: workgroup b handles
+// (chunk, head) items b, b + grid, ..., and the inputs of its next item are
+// loaded while the MFMA, inverse and store phases of the current one run.
+// With has_q == 0 (segment transitions need no outputs) q is not a real
+// input: Q_decay and M_qk are then 0.
+//
+// Thread t owns rows 4 (t / 16) .. + 3 of the chunk and the 8 channels that
+// the record stores at positions 8 (t % 16) .. + 7 (kperm order: logical
+// channels lc0 .. lc0 + 3 and lc0 + 16 .. lc0 + 19), so record rows go out
+// as 16-byte stores.  Wave w holds exactly row tile w, so the 16-token
+// reference points are sums of per-wave column totals.  The LDS operands of
+// the L / M_qk products keep the same (permuted) channel order on both
+// sides, which leaves the sums over channels unchanged.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k1_kernel(const ChunkDesc *__restrict__ chunks,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k1_kernel(const ChunkDesc *__restrict__ chunks,
                                                       int32_t H, const T *__restrict__ q,
                                                       const T *__restrict__ k,
                                                       const T *__restrict__ g,
                                                       const T *__restrict__ beta,
-                                                      uint8_t *__restrict__ ws, int has_q) {
-  constexpr int P = pad_elems<T>();
-  constexpr int LD = kD + P;                 // operand row stride (elements)
+                                                      uint8_t *__restrict__ ws, int has_q,
+                                                      int32_t nitems) {
+  constexpr int LD = kD + 16 / (int)sizeof(T); // operand row stride: rows 16 B apart in banks
   constexpr size_t OPB = (size_t)kC * LD * sizeof(T);
   constexpr RecOff off(sizeof(T));
-  // Operand region: Q_loc, K_loc, K_start, K_end (4 x [C][LD] of T).  After
-  // the MFMA phase it is reused for L, INV and a scratch block (fp32).
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * OPB];
-  __shared__ float sP[5][kD];   // reference log-decays p_0..p_3 and G_last
-  __shared__ float sF[6][kD];   // exp(p_I - p_{J+1}) for off-diagonal pairs
+  // Operand region: Q_loc, K_loc, K_start (3 x [C][LD] of T).  After the
+  // MFMA phase it is reused for L (fp32), per-wave powers of its diagonal
+  // block, the inverted diagonal blocks, and M_qk and INV Diag(beta) staged
+  // in record layout.
+  __shared__ __attribute__((aligned(16))) uint8_t smem[3 * OPB];
+  __shared__ __attribute__((aligned(16))) float sWT[4][kD]; // per-wave totals of g
+  __shared__ __attribute__((aligned(16))) float sF[6][kD];  // exp(p_I - p_J), I > J
   __shared__ float sBeta[kC];
-  __shared__ float sTot[kD];
 
   T(*sQl)[LD] = reinterpret_cast<T(*)[LD]>(smem);
   T(*sKl)[LD] = reinterpret_cast<T(*)[LD]>(smem + OPB);
   T(*sKs)[LD] = reinterpret_cast<T(*)[LD]>(smem + 2 * OPB);
-  T(*sKe)[LD] = reinterpret_cast<T(*)[LD]>(smem + 3 * OPB);
-  constexpr int LF = kC + 1;
+  constexpr int LF = kC + 4;  // fp32 rows, 16-byte aligned
+  constexpr int LB = 20;      // 16 x 16 fp32 blocks, 16-byte aligned rows
+  constexpr int LM = kC + 16 / (int)sizeof(T);
+  constexpr size_t POW0 = (size_t)kC * LF * 4;
+  constexpr size_t DINV0 = POW0 + (size_t)4 * 2 * 16 * LB * 4;
+  constexpr size_t MQ0 = DINV0 + (size_t)4 * 16 * LB * 4;
+  constexpr size_t IB0 = MQ0 + (size_t)kC * LM * sizeof(T);
   float(*sL)[LF] = reinterpret_cast<float(*)[LF]>(smem);
-  float(*sInv)[LF] = reinterpret_cast<float(*)[LF]>(smem + kC * LF * 4);
-  float(*sTmp)[LF] = reinterpret_cast<float(*)[LF]>(smem + 2 * kC * LF * 4);
-  static_assert((2 * kC + 16) * LF * 4 <= 4 * OPB, "aliasing fits");
+  float(*sPow)[2][16][LB] = reinterpret_cast<float(*)[2][16][LB]>(smem + POW0);
+  float(*sDinv)[16][LB] = reinterpret_cast<float(*)[16][LB]>(smem + DINV0);
+  T(*sMq)[LM] = reinterpret_cast<T(*)[LM]>(smem + MQ0);
+  T(*sIb)[LM] = reinterpret_cast<T(*)[LM]>(smem + IB0);
+  static_assert(IB0 + (size_t)kC * LM * sizeof(T) <= 3 * OPB, "aliasing fits");
 
-  const int ci = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int wv = tid >> 6, lane = tid & 63, lgp = lane >> 4;
+  const int cg = tid & 15, row0 = 4 * (tid >> 4);
+  const int lc0 = 32 * (cg >> 2) + 4 * (cg & 3);
+  const int64_t rowstride = (int64_t)H * kD;
+  // logical channel of this thread's e-th record position
+  auto lch = [&](int e) { return e < 4 ? lc0 + e : lc0 + 12 + e; };
+
+  // raw inputs of one item: 4 rows x (2 runs of 4 channels) of g, k, q, and
+  // beta of row tid (tid < C); buffers over rows 0..len-1 of the (chunk,
+  // head), so rows past the chunk end read 0 (no decay, no key, no query)
+  using Raw = typename Raw4<T>::type;
+  Raw rwg[4][2], rwk[4][2], rwq[4][2];
+  float rbeta = 0.f;
+  auto issue_loads = [&](int item) {
+    const int ci = item / H, h = item - ci * H;
+    const ChunkDesc cd = chunks[ci];
+    const int64_t base = cd.tok0 * rowstride + (int64_t)h * kD;
+    const uint32_t nbytes = (uint32_t)(((cd.len - 1) * rowstride + kD) * sizeof(T));
+    const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(g + base, nbytes);
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + base, nbytes);
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(q + base, nbytes);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int vo = (int)(((row0 + j) * rowstride + lc0 + 16 * u) * sizeof(T));
+        rwg[j][u] = Raw4<T>::load(rg, vo);
+        rwk[j][u] = Raw4<T>::load(rk, vo);
+        if (has_q)
+          rwq[j][u] = Raw4<T>::load(rq, vo);
+      }
+    if (tid < kC) {
+      const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(
+          beta + cd.tok0 * H + h, (uint32_t)(((cd.len - 1) * (int64_t)H + 1) * sizeof(T)));
+      rbeta = buffer_load1(rb, (int)(tid * H * (int)sizeof(T)), beta);
+    }
+  };
+
+  if ((int)blockIdx.x < nitems)
+    issue_loads(blockIdx.x);
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+  const int ci = item / H, h = item - ci * H;
   const ChunkDesc cd = chunks[ci];
   const int len = cd.len;
-  const int c = tid & (kD - 1);
-  const int half = tid >> 7;
-  const int64_t rowstride = (int64_t)H * kD;
   uint8_t *rec = ws + ((int64_t)ci * H + h) * k1_record_bytes(sizeof(T));
   T *Qd = reinterpret_cast<T *>(rec + off.qd);
   T *Kd = reinterpret_cast<T *>(rec + off.kd);
@@ -117,99 +202,161 @@ __global__ __launch_bounds__(kThreads) void k1_kernel(const ChunkDesc *__restric
   T *Mqk = reinterpret_cast<T *>(rec + off.mqk);
   float *ac = reinterpret_cast<float *>(rec + off.ac);
 
-  // ---- loads: every row index is clamped into the chunk, so all loads are
-  // unconditional and in flight together; padded rows are zeroed afterwards.
-  T graw[32], qraw[32], kraw[32];
-  {
-    const int64_t base = cd.tok0 * rowstride + (int64_t)h * kD + c;
+  lds_sync(); // the previous item's last LDS reads are done
+  // g is widened now; k and q stay raw until their row is used (registers)
+  float gv[4][8];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int rr = min(half * 32 + i, len - 1);
-      const int64_t off = base + (int64_t)rr * rowstride;
-      graw[i] = g[off];
-      kraw[i] = k[off];
-      qraw[i] = q[off];
-    }
-  }
-  const float bval = to_f32(beta[(cd.tok0 + min(tid & (kC - 1), len - 1)) * H + h]);
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      Raw4<T>::widen(rwg[j][u], &gv[j][4 * u]);
   if (tid < kC)
-    sBeta[tid] = (tid < len) ? bval : 0.f;
+    sBeta[tid] = rbeta;
 
   // ---- phase 1: inclusive cumulative log-decay per channel -------------
-  float G[32];
-  {
+  // own rows, then the 4 row groups of the wave (lanes 16 apart), then the
+  // waves before this one (per-wave totals through LDS)
+  float G[4][8], ex[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
     float run = 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const float gv = (half * 32 + i < len) ? to_f32(graw[i]) : 0.f;
-      run += gv;
-      G[i] = run;
+    for (int j = 0; j < 4; ++j) {
+      run += gv[j][e];
+      G[j][e] = run;
     }
-    if (half == 0)
-      sTot[c] = run;
+    float x = run;
+    float y = __shfl_up(x, 16);
+    if (lgp >= 1)
+      x += y;
+    y = __shfl_up(x, 32);
+    if (lgp >= 2)
+      x += y;
+    ex[e] = x - run;
+    if (lgp == 3)
+      sWT[wv][8 * cg + e] = x;
   }
   lds_sync();
-  if (half == 1) {
-    const float base = sTot[c];
+  // p_own = p_wv (before this tile), p_next = p_{wv+1}, p_last = G_last
+  float pown[8], pnext[8], plast[8];
 #pragma unroll
-    for (int i = 0; i < 32; ++i)
-      G[i] += base;
-    sP[3][c] = G[15];
-    sP[4][c] = G[31];
-  } else {
-    sP[0][c] = 0.f;
-    sP[1][c] = G[15];
-    sP[2][c] = G[31];
+  for (int e = 0; e < 8; ++e) {
+    pown[e] = 0.f;
+    pnext[e] = 0.f;
+    plast[e] = 0.f;
   }
-  lds_sync();
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const f32x4 t0 = *reinterpret_cast<const f32x4 *>(&sWT[w][8 * cg]);
+    const f32x4 t1 = *reinterpret_cast<const f32x4 *>(&sWT[w][8 * cg + 4]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float t = e < 4 ? t0[e] : t1[e - 4];
+      if (w < wv)
+        pown[e] += t;
+      if (w <= wv)
+        pnext[e] += t;
+      plast[e] += t;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      G[j][e] += pown[e] + ex[e];
+
+  // off-diagonal factors exp(p_I - p_J) for the 6 tile pairs I > J, pair
+  // p = row group p (I = 1,2,2,3,3,3; J = 0,0,1,0,1,2): the B operand of pair
+  // (I, J) is K_start of tile J times this factor, k_t exp(p_I - G_t) <= 1
+  {
+    const int p = tid >> 4;
+    if (p < 6) {
+      const int I = p < 1 ? 1 : (p < 3 ? 2 : 3);
+      const int J = p - I * (I - 1) / 2;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        x[e] = 0.f;
+#pragma unroll
+      for (int w = 0; w < 3; ++w) {
+        // w < I adds into p_I, w < J subtracts p_J
+        const f32x4 t0 = *reinterpret_cast<const f32x4 *>(&sWT[w][8 * cg]);
+        const f32x4 t1 = *reinterpret_cast<const f32x4 *>(&sWT[w][8 * cg + 4]);
+        const float sgn = (w < I ? 1.f : 0.f) - (w < J ? 1.f : 0.f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          x[e] += sgn * (e < 4 ? t0[e] : t1[e - 4]);
+      }
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        f[e] = __expf(x[e]);
+      *reinterpret_cast<f32x4 *>(&sF[p][8 * cg]) = f32x4{f[0], f[1], f[2], f[3]};
+      *reinterpret_cast<f32x4 *>(&sF[p][8 * cg + 4]) = f32x4{f[4], f[5], f[6], f[7]};
+    }
+  }
+  if (tid < 16) { // a_last per logical channel
+    float a[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      a[e] = __expf(plast[e]);
+    store4(ac + lc0, a[0], a[1], a[2], a[3]);
+    store4(ac + lc0 + 16, a[4], a[5], a[6], a[7]);
+  }
 
   // ---- phase 2: decayed operands ----------------------------------------
-  {
-    const float pC = sP[4][c];
-    float krv[32];
+  // two passes, one per run of 4 channels (fewer live registers), each
+  // writing 8-byte pieces of the record rows and LDS operand rows
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int I = half * 2 + tt;
-      const float pI = sP[I][c], pI1 = sP[I + 1][c];
-      const float eP = __expf(pI);         // exp(p_I)           <= 1
-      const float eR = __expf(pC - pI1);   // exp(G_last - p_I+1) <= 1
+  for (int u = 0; u < 2; ++u) {
+    float eP[4], eR[4];
 #pragma unroll
-      for (int ii = 0; ii < 16; ++ii) {
-        const int i = tt * 16 + ii;
-        const int r = half * 32 + i;
-        const bool ok = r < len;
-        const float qv = (ok && has_q) ? to_f32(qraw[i]) : 0.f;
-        const float kv = ok ? to_f32(kraw[i]) : 0.f;
-        const float eloc = __expf(G[i] - pI);  // (e^-80, 1]
-        const float est = __expf(pI - G[i]);   // [1, e^80)
-        const float eend = __expf(pI1 - G[i]); // (e^-80, 1]
-        sQl[r][c] = from_f32<T>(qv * eloc);
-        sKl[r][c] = from_f32<T>(kv * eloc);
-        sKs[r][c] = from_f32<T>(kv * est);
-        sKe[r][c] = from_f32<T>(kv * eend);
-        const float ga = eloc * eP;            // exp(G_r)
-        Qd[r * kD + kperm(c)] = from_f32<T>(qv * ga);
-        Kd[r * kD + kperm(c)] = from_f32<T>(kv * ga);
-        krv[i] = kv * (eend * eR);             // exp(G_last - G_r) k
-      }
+    for (int e = 0; e < 4; ++e) {
+      eP[e] = __expf(pown[4 * u + e]);                   // exp(p_I)            <= 1
+      eR[e] = __expf(plast[4 * u + e] - pnext[4 * u + e]); // exp(G_last - p_I+1) <= 1
     }
-    // K_restore^T row c, tokens half*32 .. +31: runs of 4 logical columns
-    // stay contiguous under kperm
-    T *kr = KrT + c * kC;
+    float kr[4][4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      store4(kr + kperm(half * 32 + 4 * j), krv[4 * j], krv[4 * j + 1], krv[4 * j + 2],
-             krv[4 * j + 3]);
-    if (half == 0)
-      ac[c] = __expf(pC);
-    // off-diagonal factors exp(p_I - p_{J+1}), I > J: 6 pairs x 128 channels
-    for (int p = half; p < 6; p += 2)
-      sF[p][c] = __expf(sP[kOffI[p]][c] - sP[kOffJ[p] + 1][c]);
+    for (int j = 0; j < 4; ++j) {
+      const int r = row0 + j;
+      float kv[4], qv[4];
+      Raw4<T>::widen(rwk[j][u], kv);
+      if (has_q)
+        Raw4<T>::widen(rwq[j][u], qv);
+      else
+        qv[0] = qv[1] = qv[2] = qv[3] = 0.f;
+      float xq[4], xk[4], xs[4], xQ[4], xK[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float Gv = G[j][4 * u + e], po = pown[4 * u + e];
+        const float eloc = __expf(Gv - po);                 // (e^-80, 1]
+        const float est = __expf(po - Gv);                  // [1, e^80)
+        const float eend = __expf(pnext[4 * u + e] - Gv);   // (e^-80, 1]
+        xq[e] = qv[e] * eloc;
+        xk[e] = kv[e] * eloc;
+        xs[e] = kv[e] * est;
+        const float ga = eloc * eP[e]; // exp(G_r)
+        xQ[e] = qv[e] * ga;
+        xK[e] = kv[e] * ga;
+        kr[e][j] = kv[e] * (eend * eR[e]); // exp(G_last - G_r) k
+      }
+      const int pc = 8 * cg + 4 * u; // record / operand position of channel run u
+      store4(&sQl[r][pc], xq[0], xq[1], xq[2], xq[3]);
+      store4(&sKl[r][pc], xk[0], xk[1], xk[2], xk[3]);
+      store4(&sKs[r][pc], xs[0], xs[1], xs[2], xs[3]);
+      store4(Qd + r * kD + pc, xQ[0], xQ[1], xQ[2], xQ[3]);
+      store4(Kd + r * kD + pc, xK[0], xK[1], xK[2], xK[3]);
+    }
+    // K_restore^T: row = logical channel, this thread's 4 tokens are
+    // contiguous under kperm
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      store4(KrT + lch(4 * u + e) * kC + kperm(row0), kr[e][0], kr[e][1], kr[e][2], kr[e][3]);
   }
   lds_sync();
 
   // ---- phase 3: L and M_qk tiles on MFMA ---------------------------------
-  const int wv = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int lr = lane & 15, lg = lane >> 4;
   f32x4 accL[3], accM[3];
 #pragma unroll
   for (int pp = 0; pp < 3; ++pp) {
@@ -227,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void k1_kernel(const ChunkDesc *__restric
         if (I == J) {
           b = load_frag(&sKs[16 * J + lr][kb]);
         } else {
-          const Frag<T> e = load_frag(&sKe[16 * J + lr][kb]);
+          const Frag<T> e = load_frag(&sKs[16 * J + lr][kb]);
           float x[8];
           frag_to_f32(e, x);
           const float *f = &sF[kOffIdx[p]][kb];
@@ -243,8 +390,8 @@ __global__ __launch_bounds__(kThreads) void k1_kernel(const ChunkDesc *__restric
   }
   lds_sync(); // operand region is now free for L / INV
 
-  // L (beta-scaled rows, strictly lower) to LDS; M_qk (lower incl. diagonal)
-  // straight to the record.
+  // L (beta-scaled rows, strictly lower) and M_qk (lower incl. diagonal, in
+  // record layout) to LDS.
 #pragma unroll
   for (int pp = 0; pp < 3; ++pp) {
     const int p = wv + 4 * pp;
@@ -255,74 +402,103 @@ __global__ __launch_bounds__(kThreads) void k1_kernel(const ChunkDesc *__restric
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * I + 4 * lg + i;
         sL[row][col] = (col < row) ? sBeta[row] * accL[pp][i] : 0.f;
-        Mqk[row * kC + kperm(col)] = from_f32<T>((col <= row) ? accM[pp][i] : 0.f);
+        sMq[row][kperm(col)] = from_f32<T>((col <= row) ? accM[pp][i] : 0.f);
       }
     }
   }
-  // zero the upper tiles (J > I) of L, INV and M_qk
+  // zero the upper tiles (J > I) of M_qk and INV Diag(beta)
   for (int e = tid; e < 6 * 256; e += kThreads) {
     const int t = e >> 8, r = (e >> 4) & 15, cc = e & 15;
     const int row = 16 * kUpI[t] + r, col = 16 * kUpJ[t] + cc;
-    sL[row][col] = 0.f;
-    sInv[row][col] = 0.f;
-    Mqk[row * kC + kperm(col)] = from_f32<T>(0.f);
+    sMq[row][kperm(col)] = from_f32<T>(0.f);
+    sIb[row][kperm(col)] = from_f32<T>(0.f);
   }
   lds_sync();
 
-  // ---- phase 4: INV = (I + L)^-1 by blocked forward substitution ---------
-  if (tid < 64) {
-    // diagonal block b, column j:  x = (I + L_bb)^-1 e_j
-    const int b = tid >> 4, j = tid & 15;
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float acc = (i == j) ? 1.f : 0.f;
-#pragma unroll
-      for (int m = 0; m < i; ++m)
-        acc -= sL[16 * b + i][16 * b + m] * x[m];
-      x[i] = acc;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      sInv[16 * b + i][16 * b + j] = x[i];
-  }
-  lds_sync();
-  for (int bi = 1; bi < 4; ++bi) {
-    // T_j = sum_{m=j}^{bi-1} L[bi][m] INV[m][j]   for j < bi
-    for (int e = tid; e < bi * 256; e += kThreads) {
-      const int j = e >> 8, r = (e >> 4) & 15, cc = e & 15;
-      float acc = 0.f;
-      for (int m = j; m < bi; ++m)
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-          acc += sL[16 * bi + r][16 * m + u] * sInv[16 * m + u][16 * j + cc];
-      sTmp[r][16 * j + cc] = acc;
-    }
-    lds_sync();
-    // INV[bi][j] = -INV[bi][bi] T_j
-    for (int e = tid; e < bi * 256; e += kThreads) {
-      const int j = e >> 8, r = (e >> 4) & 15, cc = e & 15;
-      float acc = 0.f;
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        acc += sInv[16 * bi + r][16 * bi + u] * sTmp[u][16 * j + cc];
-      sInv[16 * bi + r][16 * j + cc] = -acc;
-    }
-    lds_sync();
-  }
+  // the next item's inputs are in flight during the rest of this one
+  if (item + (int)gridDim.x < nitems)
+    issue_loads(item + gridDim.x);
 
-  // INV * Diag(beta) to the record, 16 logical columns per thread in runs
-  // of 4 (contiguous under kperm)
+  // ---- phase 4: INV = (I + L)^-1 by 16 x 16 blocks on fp32 MFMA ----------
+  // Level 0 (wave b): D_b = I + N with N = L_bb strictly lower, so
+  // D_b^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) exactly (N^16 = 0).
+  // Level 1 (wave j): block forward substitution down column block j,
+  // X_ij = -D_i^-1 sum_{m=j}^{i-1} L_im X_mj, from its own earlier blocks,
+  // L and the D_i^-1 of level 0.  Blocks stay in accumulator layout
+  // (lane (lr, lg) holds rows 4 lg .. + 3 of column lr), which is also a
+  // valid B operand, so each product feeds the next.
   {
-    const int row = tid >> 2, c0 = (tid & 3) * 16;
+    const int lr = lane & 15, lg = lane >> 4;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 X[4];
+    // INV Diag(beta) block (I, J) into the staged record layout
+    auto put = [&](int I, int J, const f32x4 &x) {
+      const float bcol = sBeta[16 * J + lr];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = c0 + 4 * j;
-      store4(INVb + row * kC + kperm(col), sInv[row][col] * sBeta[col],
-             sInv[row][col + 1] * sBeta[col + 1], sInv[row][col + 2] * sBeta[col + 2],
-             sInv[row][col + 3] * sBeta[col + 3]);
+      for (int i = 0; i < 4; ++i)
+        sIb[16 * I + 4 * lg + i][kperm(16 * J + lr)] = from_f32<T>(x[i] * bcol);
+    };
+    {
+      const int b = wv;
+      const float *N = &sL[16 * b][16 * b];
+      float *P2 = &sPow[b][0][0][0];
+      float *P4 = &sPow[b][1][0][0];
+      const f32x4 n1 = acc_load(N, LF, lr, lg);
+      f32x4 n2 = zero, n4 = zero, y = zero;
+      mm16_lds_acc(n2, N, LF, n1, lr, lg); // N^2
+      acc_store(P2, LB, n2, lr, lg);
+      mm16_lds_acc(n4, P2, LB, n2, lr, lg); // N^4
+      acc_store(P4, LB, n4, lr, lg);
+      mm16_lds_acc(y, P4, LB, n4, lr, lg); // N^8
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        y[i] += (4 * lg + i == lr) ? 1.f : 0.f; // I + N^8
+      mm16_lds_acc(y, P4, LB, y, lr, lg);       // (I + N^4) Y
+      mm16_lds_acc(y, P2, LB, y, lr, lg);       // (I + N^2) Y
+      mm16_lds_acc(y, N, LF, y, lr, lg, -1.f);  // (I - N) Y
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (t == b)
+          X[t] = y; // static register index
+      acc_store(&sDinv[b][0][0], LB, y, lr, lg);
+      put(b, b, y);
+    }
+    lds_sync(); // every D_i^-1 is in LDS
+    {
+      const int j = wv;
+#pragma unroll
+      for (int i = 1; i < 4; ++i) {
+        if (i > j) {
+          f32x4 t = zero;
+#pragma unroll
+          for (int m = 0; m < 3; ++m)
+            if (m >= j && m < i)
+              mm16_lds_acc(t, &sL[16 * i][16 * m], LF, X[m], lr, lg);
+          f32x4 x = zero;
+          mm16_lds_acc(x, &sDinv[i][0][0], LB, t, lr, lg, -1.f);
+          X[i] = x;
+          put(i, j, x);
+        }
+      }
     }
   }
+  lds_sync();
+
+  // M_qk and INV Diag(beta) from their staging blocks to the record, 16
+  // bytes per store
+  {
+    constexpr int UPR = kC * (int)sizeof(T) / 16; // 16-byte units per row
+    constexpr int EPU = 16 / (int)sizeof(T);      // elements per unit
+#pragma unroll
+    for (int u = tid; u < kC * UPR; u += kThreads) {
+      const int row = u / UPR, c0 = (u % UPR) * EPU;
+      *reinterpret_cast<uint4 *>(Mqk + row * kC + c0) =
+          *reinterpret_cast<const uint4 *>(&sMq[row][c0]);
+      *reinterpret_cast<uint4 *>(INVb + row * kC + c0) =
+          *reinterpret_cast<const uint4 *>(&sIb[row][c0]);
+    }
+  }
+  } // item loop
 }
 
 // ---------------------------------------------------------------------------
@@ -375,27 +551,6 @@ __device__ __forceinline__ int section_src(int q, int base_g) {
   return c < ROW ? base_g + r * ROW + c : 0;
 }
 
-// Raw buffer resource over `bytes` bytes at p: loads past the end read 0,
-// stores past the end are dropped, and offsets are 32-bit.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
-}
-
-// 16 bytes per lane from a buffer straight into LDS: lane l reads at byte
-// voff (its own) and writes LDS bytes 16 l .. 16 l + 15 after the
-// wave-uniform LDS base.
-__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, int voff, uint8_t *lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      r, (__attribute__((address_space(3))) void *)lds_base, 16, voff, 0, 0, 0);
-}
-
-// One element to a buffer at byte voff + soff (soff wave-uniform).
-__device__ __forceinline__ void buffer_store(__amdgpu_buffer_rsrc_t r, bf16 x, int voff, int soff) {
-  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(short, x), r, voff, soff, 0);
-}
-__device__ __forceinline__ void buffer_store(__amdgpu_buffer_rsrc_t r, float x, int voff, int soff) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, x), r, voff, soff, 0);
-}
 
 // Copy of one chunk record (global) into its padded LDS image with
 // direct-to-LDS loads: wave w fills 1 KiB blocks w, w + NW, ...; lane l of a
@@ -859,18 +1014,22 @@ hipError_t launch_k1(int elt, const ChunkDesc *chunks, int32_t nchunks, int32_t 
                      hipStream_t s) {
   if (nchunks == 0)
     return hipSuccess;
-  dim3 grid((unsigned)nchunks, (unsigned)H), block(kThreads);
+  // persistent grid: as many workgroups as are resident at once (LDS
+  // limits bf16 to 2 per compute unit, fp32 to 1), each walking its items
+  const int64_t nitems = (int64_t)nchunks * H;
+  const int64_t resident = (int64_t)kComputeUnits * (elt == 1 ? 2 : 1);
+  dim3 grid((unsigned)std::min(nitems, resident)), block(kThreads);
   // without q, k stands in as a readable buffer of the same shape
   const int has_q = q != nullptr;
   const void *qq = has_q ? q : k;
   if (elt == 1)
     k1_kernel<bf16><<<grid, block, 0, s>>>(chunks, H, (const bf16 *)qq, (const bf16 *)k,
                                            (const bf16 *)g, (const bf16 *)beta,
-                                           (uint8_t *)ws, has_q);
+                                           (uint8_t *)ws, has_q, (int32_t)nitems);
   else
     k1_kernel<float><<<grid, block, 0, s>>>(chunks, H, (const float *)qq, (const float *)k,
                                             (const float *)g, (const float *)beta,
-                                            (uint8_t *)ws, has_q);
+                                            (uint8_t *)ws, has_q, (int32_t)nitems);
   return hipGetLastError();
 }
 
