@@ -58,6 +58,104 @@ def stored_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+COPY_PROBE_FLOATS = 256 << 20   # 1 GiB fp32 read + 1 GiB written by the calibration copy
+
+
+def traffic_probe(kda, wl, name, dev):
+    """One prefill call and one decode step bracketed by a plain elementwise
+    copy of known size, for rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE):
+    the copy's counter reading calibrates the counters to bytes."""
+    import torch
+    w = wl.WORKLOADS[name]
+    d = wl.prefill_case(w, device=dev)
+    cu = d["cu"]
+    N, H = len(w.lengths), w.H
+    T = int(cu[-1])
+    o = torch.empty((T, H, D), dtype=w.dtype, device=dev)
+    fin = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(kda.prefill_workspace_size(cu, H, w.dtype, 0), 1), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu,
+                          initial_state=d["init"], o=o, final_state=fin, workspace=ws)
+
+    step()                                   # warm (first-touch, schedule upload)
+    torch.cuda.synchronize(dev)
+    src = torch.ones(COPY_PROBE_FLOATS, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize(dev)
+    torch.mul(src, 1.0, out=dst)             # the calibration copy
+    torch.cuda.synchronize(dev)
+    del src, dst
+    step()                                   # the measured prefill call
+    torch.cuda.synchronize(dev)
+    del d, o, fin, ws
+    torch.cuda.empty_cache()
+    wd = wl.WORKLOADS["decode_f32_N256_H96_x64"]
+    dd = wl.decode_case(wd, device=dev)
+    od = torch.empty((wd.lengths[0], wd.H, D), dtype=wd.dtype, device=dev)
+    for _ in range(2):                       # warm, then the measured step
+        kda.decode_step(dd["state"], dd["q"][0], dd["k"][0], dd["v"][0], dd["g"][0],
+                        dd["beta"][0], o=od)
+        torch.cuda.synchronize(dev)
+    chunk_heads = sum((L + C - 1) // C for L in w.lengths) * H
+    print(json.dumps({"probe": name, "copy_bytes_read": 4 * COPY_PROBE_FLOATS,
+                      "copy_bytes_written": 4 * COPY_PROBE_FLOATS,
+                      "chunk_heads": chunk_heads}), flush=True)
+
+
+def traffic_from_counters(fetch_csv, write_csv, workload, command):
+    """Per-dispatch HBM bytes of the prefill kernels and the decode kernel
+    from two rocprofv3 counter files (FETCH_SIZE and WRITE_SIZE, KiB per
+    dispatch), each scaled so that the calibration copy reads/writes exactly
+    its known size.  The last dispatch of each kernel is the measured one."""
+    import csv
+
+    def per_dispatch(path, counter):
+        rows = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = int(r["Dispatch_Id"])
+                name = r["Kernel_Name"]
+                rows.setdefault(key, [name, 0.0])
+                rows[key][1] += float(r["Counter_Value"])
+        return [rows[k] for k in sorted(rows)]
+
+    out = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
+           "command": command, "counters": {}}
+    for counter, path, known in (("FETCH_SIZE", fetch_csv, 4 * COPY_PROBE_FLOATS),
+                                 ("WRITE_SIZE", write_csv, 4 * COPY_PROBE_FLOATS)):
+        disp = per_dispatch(path, counter)
+        copies = [v for n, v in disp if "elementwise" in n.lower()]
+        copy_kib = max(copies)
+        scale = known / (copy_kib * 1024.0)
+        last = {}
+        for n, v in disp:
+            for tag in ("k1_kernel", "k2_kernel", "scan_kernel", "decode_kernel"):
+                if tag in n:
+                    last.setdefault(tag, []).append(v)
+        out["counters"][counter] = {
+            "copy_kib": copy_kib, "scale": scale,
+            "kib_per_dispatch": {t: v[-1] for t, v in last.items()},
+            "bytes_per_dispatch": {t: v[-1] * 1024.0 * scale for t, v in last.items()}}
+    f, w = out["counters"]["FETCH_SIZE"], out["counters"]["WRITE_SIZE"]
+    prefill_tags = [t for t in ("k1_kernel", "k2_kernel", "scan_kernel")
+                    if t in f["bytes_per_dispatch"]]
+    out["hbm_bytes_per_launch"] = sum(f["bytes_per_dispatch"][t] + w["bytes_per_dispatch"].get(t, 0.0)
+                                      for t in prefill_tags)
+    if "decode_kernel" in f["bytes_per_dispatch"]:
+        out["decode_hbm_bytes_per_step"] = (f["bytes_per_dispatch"]["decode_kernel"] +
+                                            w["bytes_per_dispatch"].get("decode_kernel", 0.0))
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    with open(path, "w") as fo:
+        json.dump(out, fo, indent=1)
+        fo.write("\n")
+    print(json.dumps(out, indent=1))
+
+
 def time_prefill(kda, wl, name, steps, warmup, split_hint, dev):
     import torch
     w = wl.WORKLOADS[name]
@@ -136,6 +234,30 @@ def time_decode(kda, wl, dev, steps_block=64, warmup_blocks=1):
             "model_bytes_per_step": DECODE_BYTES_PER_HEAD_TOKEN * N * H}
 
 
+def copy_reference(dev, reps=5):
+    """Achievable HBM bandwidth: a plain elementwise copy of 1 GiB (read 1 GiB,
+    write 1 GiB), best of `reps`, as the reference next to the nominal peak."""
+    import torch
+    src = torch.ones(COPY_PROBE_FLOATS, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize(dev)
+    best = None
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        torch.mul(src, 1.0, out=dst)
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes": 8 * COPY_PROBE_FLOATS, "us": best * 1e3,
+            "GB_per_s": 8 * COPY_PROBE_FLOATS / (best * 1e-3) / 1e9}
+
+
 def cpu_baseline(wl, name, budget_s=12.0):
     """The fp64 oracle, as it stands, on whole heads of the workload until the
     time budget is spent.  Returns tokens/s scaled to the full workload."""
@@ -179,7 +301,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true",
                     help="also time the long-context and packed-resume prefill workloads")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run one calibration copy, one prefill call and one decode step "
+                         "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs) and exit")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two counter_collection.csv files of --traffic-probe runs into "
+                         "profiles/traffic_<workload>.json (no GPU needed)")
+    ap.add_argument("--traffic-command", default="",
+                    help="the command line that produced the counter files (recorded)")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from_counters(args.traffic_from[0], args.traffic_from[1], args.workload,
+                              args.traffic_command)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -192,6 +326,9 @@ def main():
 
     kda.load()
     dev = torch.device("cuda:0")
+    if args.traffic_probe:
+        traffic_probe(kda, wl, args.workload, dev)
+        return
     main_res = time_prefill(kda, wl, args.workload, args.steps, args.warmup, args.split, dev)
     print("prefill %s: %.3f ms/step, %.3g tokens/s, %.1f TFLOP/s (%.1f%% of bf16 MFMA peak)"
           % (args.workload, main_res["ms_per_step"], main_res["tokens_per_s"],
@@ -207,6 +344,10 @@ def main():
             print("prefill %s: %.3f ms/step, %.3g tokens/s, %.1f%% MFMA"
                   % (name, r["ms_per_step"], r["tokens_per_s"], 100 * r["mfma_frac"]),
                   file=sys.stderr, flush=True)
+    copy_ref = copy_reference(dev)
+    print("plain copy: %.0f GB/s achievable (%.1f%% of the %.0f GB/s HBM peak)"
+          % (copy_ref["GB_per_s"], 100 * copy_ref["GB_per_s"] / PEAK_HBM_GBS, PEAK_HBM_GBS),
+          file=sys.stderr, flush=True)
     dec = None
     if not args.no_decode:
         dec = time_decode(kda, wl, dev)
@@ -240,7 +381,11 @@ def main():
         "roofline": {"bound": "mfma", "achieved": main_res["tflops"],
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": main_res["mfma_frac"], "traffic": traffic,
-                     "kernel": "prefill launch sequence (chunk prep + state chain)"},
+                     "kernel": "kda_chunk_prefill launch sequence (chunk prep K1 + state "
+                               "chain K2), model FLOPs per call / event-timed call duration",
+                     "hbm_GB_per_s": (traffic / (main_res["ms_per_step"] * 1e-3) / 1e9
+                                      if traffic else None)},
+        "hbm_reference": {"peak_GB_per_s": PEAK_HBM_GBS, "copy": copy_ref},
         "cpu_baseline": cpu,
         "prefill": main_res,
         "decode": dec,
