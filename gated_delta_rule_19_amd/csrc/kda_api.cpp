@@ -150,9 +150,9 @@ bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_h
   auto longer = [](const ChainDesc &a, const ChainDesc &b) { return a.ntok > b.ntok; };
   std::stable_sort(p.chains.begin(), p.chains.end(), longer);
   std::stable_sort(p.segchains.begin(), p.segchains.end(), longer);
-  // the fused kernel is kept out of the dispatch while it is slower than the
-  // chunk-prep + state-chain pair
-  p.fused = false;
+  // bf16 without a planner split: chunk prep and state carry run fused in
+  // one kernel, and no chunk-prep records go through memory
+  p.fused = es == 2 && p.segchains.empty();
   layout(p, H, es);
   return true;
 }

@@ -1,36 +1,53 @@
-// KDA chunked prefill, chunk prep and state carry fused in one kernel (bf16).
+// KDA chunked prefill with chunk prep and state carry fused in one kernel
+// (bf16 inputs, fp32 state and accumulation).
 //
-// Same mathematics as the two-kernel path (kda_prefill.hip): the FlashKDA
-// chunk form of "Kimi K3 的架構" (hao.cnyes.com) §六 with the 16-token
+// The mathematics is the two-kernel path's (kda_prefill.hip): the FlashKDA
+// chunk form of "Kimi K3 的架構" (hao.cnyes.com) §六, with the 16-token
 // reference points that the decay's lower bound allows ("Kimi K3.1 Pro
-// 架构完全拆解" §3.2).  The difference is where the chunk-prep results live:
-// here they never leave the compute unit.
+// 架构完全拆解" §3.2).  What changes is where the chunk-prep results live:
+// here they never leave the compute unit, so the only HBM traffic is the
+// layer's own inputs and outputs (q, k, v, g, beta in; o and states out).
 //
-// One workgroup of 8 waves owns one (chain, head, 64-column block of S):
-//   waves 0-3 ("state") walk the chunks in order and keep their 128 x 64 slice
-//   of S in MFMA accumulators:  W = K_decay S,  U = INV Diag(beta)(V - W),
-//   O = Q_decay S + M_qk U,  S = Diag(a_last) S + K_restore^T U;
-//   waves 4-7 ("prep") build the operands of the NEXT chunk meanwhile:
-//   cumulative log-decay, decayed q/k, L and M_qk on MFMA, INV = (I + L)^-1.
-// The prep results pass to the state waves through LDS ("hand-off" arrays);
-// a chunk's q, k, g and beta are loaded one chunk before the prep needs them,
-// and v one chunk before the state needs it.  Per chunk the only HBM traffic
-// is the layer's own inputs and outputs.
+// One workgroup of 8 waves owns one (chain, head, column block of 64 NCT
+// state columns).  The waves have two roles that run side by side, two waves
+// per SIMD:
+//   waves 0-3, state: wave w carries columns 16 NCT w .. 16 NCT w + 16 NCT - 1
+//     of the column block through the chunks, S in MFMA accumulators:
+//       W = K_decay S,  O = Q_decay S,  U = INV Diag(beta) (V - W),
+//       O += M_qk U,  S = Diag(a_last) S + K_restore^T U;
+//   waves 4-7, prep: wave p owns token tile p (16 tokens) of chunk c and
+//     builds its part of that chunk's record: cumulative log-decay, decayed
+//     q / k, K_restore, L and M_qk on MFMA, INV = (I + L)^-1.
+// A chunk step is four stages separated by workgroup barriers.  Every record
+// region is rewritten by the prep only in a stage after the one in which the
+// state waves read it, so one record buffer serves both roles:
+//   stage | state waves                            | prep waves (chunk c)
+//   A     | -                                      | tile scan, Q_loc/K_loc/K_start, diagonal L, M_qk tiles
+//   B     | U, O += M_qk U, store o, S update      | factors, K_decay/Q_decay -> record, off-diagonal tiles
+//         |   (chunk c - 1)                        |
+//   C     | -                                      | L, M_qk, K_restore^T, a_last -> record; diagonal INV blocks
+//   D     | W = K_decay S, O = Q_decay S (chunk c) | off-diagonal blocks of INV -> record
 //
-// Prep lane layout: prep wave pw owns token tile pw (rows 16pw .. 16pw+15);
-// lane (lr, lg) holds row 16pw + lr and channels 32s + 8lg .. +7 for
-// s = 0..3, which is exactly the MFMA fragment layout, so the decayed
-// operands of the L / M_qk products are built in registers.  The cumulative
-// sum over rows inside a tile is a DPP scan across the 16 lanes of a row.
+// Prep lane layout: prep wave p, lane (lr, lg) = (lane % 16, lane / 16) holds
+// token 16 p + lr and, for k-step s = 0..3, channels 32 s + 8 lg .. + 7: one
+// 16-byte load per input and k-step, the MFMA A-fragment layout of the L /
+// M_qk products, and one 16-byte row piece of Q_decay / K_decay.  The tile's
+// cumulative sum of g runs across the 16 lanes of a DPP row.
 //
-// Numerics (log-decay kept in log2 units, g * log2(e)):
-//   G_loc  = inclusive cumsum of g inside the 16-token tile, in (-80/ln2, 0]
-//   p_I    = cumulative log-decay before tile I,  p_4 = whole chunk
-//   K_loc  = k 2^{G_loc},  Q_loc = q 2^{G_loc}          (A side, <= 1)
-//   K_st   = k 2^{-G_loc}                               (diagonal B, <= e^80)
-//   K_end  = K_st 2^{p_{I+1} - p_I}                     (<= 1)
-//   B(I,J) = K_end(J) 2^{p_I - p_{J+1}}  for J < I       (<= 1)
-//   K_decay = K_loc 2^{p_I},  Q_decay = Q_loc 2^{p_I},  K_restore = K_end 2^{p_4 - p_{I+1}}
+// State row order: the state waves keep channel kperm(p) in accumulator row
+// p (p = 16 ct + 4 lg + i).  Packing two stacked accumulator tiles then gives
+// exactly channels 32 s + 8 lg .. + 7 in lane (., lg), the B operand of the
+// K = channels products, so the state feeds W and O without moving data
+// between lanes.  K_restore^T and a_last are stored in the same row order.
+//
+// Numerics, with G the inclusive cumulative log-decay from the chunk start,
+// p_I = G before token tile I, G_loc = G - p_I and G_C the chunk total:
+//   Q_loc = q e^{G_loc},  K_loc = k e^{G_loc}            (<= |q|, |k|)
+//   K_st  = k e^{-G_loc}                                 (<= e^80 |k|)
+//   L_IJ  = K_loc,I (K_st,J e^{p_I - p_J})^T  for J < I;  K_loc,I K_st,I^T on the diagonal
+//   Q_decay = q e^{G_loc + p_I},  K_decay = k e^{G_loc + p_I},  K_restore = k e^{G_C - p_I - G_loc}
+// Every exponent is <= 0 except K_st's (< 80); a factor that underflows does
+// so only where the exact product is below e^-20 of its neighbours.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -38,68 +55,99 @@ namespace kda {
 
 namespace {
 
-constexpr int kFThreads = 512;
-constexpr int kFBV = 64;           // state columns per workgroup
-constexpr int kNCT = kFBV / 16;    // 16-column tiles of the state slice
-constexpr int kLdD = kD + 8;       // padded row length, 128-wide bf16 arrays
-constexpr int kLdC = kC + 8;       // padded row length, 64-wide bf16 arrays
-constexpr int kLdL = kC + 4;       // padded row length, fp32 L / INV (16-byte rows)
-constexpr int kLdB = 20;           // padded row length, fp32 16 x 16 blocks (16-byte rows)
+constexpr int kFWaves = 8;
+constexpr int kFThreads = 64 * kFWaves;
+constexpr int kLdD = kD + 8; // bf16 rows of 128 (272 B: 16 rows of a fragment read hit distinct banks)
+constexpr int kLdC = kC + 8; // bf16 rows of 64 (144 B)
+constexpr int kLdL = kC + 4; // fp32 rows of 64
+constexpr int kLdB = 20;     // fp32 16 x 16 blocks
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kStagesPerChunk = 5; // barriers per chunk, identical in both roles
 
-struct FusedSmem {
-  // state working set; Sb's bytes also hold the fp32 L / D^-1 matrix while
-  // the prep inverts it (the state waves do not touch Sb then)
-  bf16 Sb[kFBV][kLdD];
-  bf16 VWb[kFBV][kLdC];
-  bf16 Ub[kFBV][kLdC];
-  // hand-off, prep -> state
-  bf16 hKd[kC][kLdD];
-  bf16 hQd[kC][kLdD];
-  bf16 hKrT[kD][kLdC];
-  bf16 hINVb[kC][kLdC];
-  bf16 hMqk[kC][kLdC];
-  float hAc[kD];
-  // prep working set
-  bf16 sKe[kC][kLdD];
-  float sTot[4][kD];
-  float sEp[4][kD], sEs[4][kD], sEr[4][kD];
-  float sF[6][kD];
-  float sBeta[kC];
-  float sD[4][16][kLdB];      // D_b^-1, the inverted diagonal blocks of I + L
-  float sPow[4][2][16][kLdB]; // per prep wave: N^2 and N^4 of its diagonal block
-};
-static_assert(sizeof(FusedSmem) <= 160 * 1024, "LDS budget");
-static_assert(sizeof(float) * kC * kLdL <= sizeof(bf16) * kFBV * kLdD, "L fits in Sb");
-
-// off-diagonal tile pairs (I > J): index of exp(p_I - p_{J+1}) in sF
-__device__ __forceinline__ int off_pair(int I, int J) {
-  // (1,0)->0 (2,0)->1 (2,1)->2 (3,0)->3 (3,1)->4 (3,2)->5
-  return (I * (I - 1)) / 2 + J;
+// The 6 off-diagonal tile pairs (I, J), I > J, and the prep wave that
+// computes each (two waves take two pairs, two take one).  A pair's A
+// operand (K_loc / Q_loc rows of tile I) is in registers when the wave owns
+// tile I, else it comes from the copy tile 3 leaves in LDS.
+//   wave 0: (3,0)   wave 1: (1,0) (3,1)   wave 2: (2,0) (2,1)   wave 3: (3,2)
+__host__ __device__ constexpr int pair_count(int w) { return (w == 1 || w == 2) ? 2 : 1; }
+__host__ __device__ constexpr int pair_I(int w, int n) {
+  return w == 0 ? 3 : (w == 1 ? (n == 0 ? 1 : 3) : (w == 2 ? 2 : 3));
+}
+__host__ __device__ constexpr int pair_J(int w, int n) {
+  return w == 0 ? 0 : (w == 1 ? (n == 0 ? 0 : 1) : (w == 2 ? (n == 0 ? 0 : 1) : 2));
 }
 
-// Lane index as an opaque value: the compiler cannot hoist lane-dependent
-// address arithmetic built on it out of the chunk loop, which would keep
-// dozens of loop-invariant LDS addresses alive in registers across stages.
+template <int NCT> struct FusedSmem {
+  // the chunk record (state waves read it, prep waves rewrite it)
+  bf16 Qd[kC][kLdD];   // Q_decay, rows = tokens, columns = channels
+  bf16 Kd[kC][kLdD];   // K_decay
+  bf16 KrT[kD][kLdC];  // K_restore^T, row p = channel kperm(p), columns kperm(token)
+  bf16 INVb[kC][kLdC]; // INV Diag(beta), columns kperm(token)
+  bf16 Mqk[kC][kLdC];  // M_qk, columns kperm(token)
+  float aL[kD];        // a_last, entry p = channel kperm(p)
+  // v of each state wave's columns: 64 rows x 16 NCT columns
+  bf16 sv[4][kC * 16 * NCT];
+  // prep scratch
+  float Tot[4][kD]; // per-tile totals of g
+  union {
+    struct {
+      bf16 Kst[4][16][kLdD]; // K_start per tile (stage A -> B)
+      bf16 Aq3[2][16][kLdD]; // K_loc, Q_loc of tile 3 (stage A -> B)
+    } ab;
+    float Pow[4][2][16][kLdB]; // per prep wave: N^2, N^4 of its diagonal block (stage C)
+  } x;
+  float L[kC][kLdL];       // L = StrictTril(Diag(beta) K_decay K_inv^T), fp32
+  float Dinv[4][16][kLdB]; // inverted diagonal blocks of I + L
+  float Beta[kC];
+  float Fac[4][2][kD];     // per tile, log2 units: p_I, G_C - p_I
+  float Foff[6][kD];       // e^{p_I - p_J} for the off-diagonal pairs
+};
+
+// index of the tile pair (I, J), I > J, among the 6 off-diagonal pairs
+__device__ __forceinline__ int off_pair(int I, int J) { return I * (I - 1) / 2 + J; }
+
+// state row holding channel c (inverse of kperm)
+__device__ __forceinline__ int kperm_inv(int p) {
+  return (p & ~31) | ((p & 4) << 2) | ((p & 24) >> 1) | (p & 3);
+}
+
+// Workgroup barrier ordering LDS only; global loads stay in flight across it.
+__device__ __forceinline__ void fsync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Lane index as an opaque value: lane-dependent addresses built on it are
+// recomputed where they are used instead of being hoisted out of the chunk
+// loop and kept alive (or spilled) across all of its stages.
 __device__ __forceinline__ int opaque_lane() {
   int l;
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
   return l;
 }
 
-// Stage boundary: LDS-ordering barrier that the instruction scheduler may
-// not move work across (each stage's register live ranges stay inside it).
-__device__ __forceinline__ void fsync() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  __builtin_amdgcn_sched_barrier(0);
+// LDS writes of this wave are complete and visible to its own later reads.
+__device__ __forceinline__ void wave_lds_fence() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 8 bf16 (raw dwords) -> fp32
+__device__ __forceinline__ void widen8(u32x4 w, float *x) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    x[2 * d] = __builtin_bit_cast(float, w[d] << 16);
+    x[2 * d + 1] = __builtin_bit_cast(float, w[d] & 0xffff0000u);
+  }
+}
+
+// Inclusive prefix sum over the 16 lanes of each DPP row (row_shr with
+// bound_ctrl: lanes before the row start contribute 0).
 __device__ __forceinline__ float dpp_shr(float x, int n) {
-  int v = __builtin_bit_cast(int, x);
+  const int v = __builtin_bit_cast(int, x);
   int r;
   switch (n) {
   case 1: r = __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true); break;
@@ -109,9 +157,6 @@ __device__ __forceinline__ float dpp_shr(float x, int n) {
   }
   return __builtin_bit_cast(float, r);
 }
-
-// Inclusive prefix sum over the 16 lanes of each DPP row (row_shr with
-// bound_ctrl: lanes before the row start read 0).
 __device__ __forceinline__ float row_scan16(float x) {
   x += dpp_shr(x, 1);
   x += dpp_shr(x, 2);
@@ -120,88 +165,68 @@ __device__ __forceinline__ float row_scan16(float x) {
   return x;
 }
 
-// Raw inputs of one chunk, in the prep lane layout.
-struct PrepRaw {
-  bf16x8 q[4], k[4], g[4];
-  float beta;
-};
-
-// g and beta (needed first) and q, k (needed two stages later) are loaded
-// separately to keep their register live ranges short.
-__device__ __forceinline__ void prep_load_g(PrepRaw &raw, const bf16 *g, const bf16 *beta,
-                                            int64_t tok0, int len, int H, int h,
-                                            int64_t rowstride, int pw, int lr, int lg) {
-  const int rr = min(16 * pw + lr, len - 1);
-  const int64_t base = (tok0 + rr) * rowstride + (int64_t)h * kD + 8 * lg;
+__device__ __forceinline__ Frag<bf16> pack8(const float *x) {
+  Frag<bf16> f;
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
-    raw.g[s] = *reinterpret_cast<const bf16x8 *>(g + base + 32 * s);
-  raw.beta = static_cast<float>(beta[(tok0 + rr) * H + h]);
+  for (int j = 0; j < 8; ++j)
+    f.v[j] = static_cast<bf16>(x[j]);
+  return f;
 }
 
-__device__ __forceinline__ void prep_load_qk(PrepRaw &raw, const bf16 *q, const bf16 *k,
-                                             int64_t tok0, int len, int h, int64_t rowstride,
-                                             int pw, int lr, int lg) {
-  const int rr = min(16 * pw + lr, len - 1);
-  const int64_t base = (tok0 + rr) * rowstride + (int64_t)h * kD + 8 * lg;
+__device__ __forceinline__ Frag<bf16> pack_acc2(const f32x4 &lo, const f32x4 &hi) {
+  Frag<bf16> f;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    raw.k[s] = *reinterpret_cast<const bf16x8 *>(k + base + 32 * s);
-    raw.q[s] = *reinterpret_cast<const bf16x8 *>(q + base + 32 * s);
+  for (int i = 0; i < 4; ++i) {
+    f.v[i] = static_cast<bf16>(lo[i]);
+    f.v[4 + i] = static_cast<bf16>(hi[i]);
   }
+  return f;
 }
+
+__device__ __forceinline__ void load8f(const float *p, float *x) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+  x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+  x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+}
+
 
 } // namespace
 
-// ---------------------------------------------------------------------------
+template <int NCT>
 __global__ __launch_bounds__(kFThreads) void fused_kernel(
     const ChainDesc *__restrict__ chains, int32_t H, const bf16 *__restrict__ q,
     const bf16 *__restrict__ k, const bf16 *__restrict__ v, const bf16 *__restrict__ g,
     const bf16 *__restrict__ beta, bf16 *__restrict__ o, const float *__restrict__ init,
     const float *__restrict__ sin, float *__restrict__ final_state) {
-  __shared__ __attribute__((aligned(16))) FusedSmem sm;
-  float(*sL)[kLdL] = reinterpret_cast<float(*)[kLdL]>(&sm.Sb[0][0]);
+  using Sm = FusedSmem<NCT>;
+  __shared__ __attribute__((aligned(16))) Sm sm;
+  constexpr int VW = 16 * NCT; // state columns per state wave
 
   const ChainDesc cd = chains[blockIdx.x];
   const int h = blockIdx.y;
-  const int vcol0 = blockIdx.z * kFBV;
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int col0 = blockIdx.z * (4 * VW);
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t rowstride = (int64_t)H * kD;
   const int nch = (cd.ntok + kC - 1) / kC;
 
-  // zero the upper 16 x 16 blocks of INV*Diag(beta) and M_qk once; the prep
-  // only ever writes their lower blocks
+  // The upper 16 x 16 tiles of M_qk and INV Diag(beta) are zero and are
+  // never written again.
   for (int e = tid; e < 6 * 256; e += kFThreads) {
     const int t = e >> 8, r = (e >> 4) & 15, c = e & 15;
     const int bi = t < 3 ? 0 : (t < 5 ? 1 : 2);
     const int bj = t < 3 ? t + 1 : (t < 5 ? t - 1 : 3);
-    sm.hINVb[16 * bi + r][16 * bj + c] = static_cast<bf16>(0.f);
-    sm.hMqk[16 * bi + r][16 * bj + c] = static_cast<bf16>(0.f);
+    sm.INVb[16 * bi + r][kperm(16 * bj + c)] = static_cast<bf16>(0.f);
+    sm.Mqk[16 * bi + r][kperm(16 * bj + c)] = static_cast<bf16>(0.f);
   }
+  fsync();
 
-  const bf16 *vchain = v + cd.tok0 * rowstride + (int64_t)h * kD + vcol0;
-  // The role is uniform per wave; readfirstlane makes the branch scalar, so
-  // each wave runs exactly one side and both sides pass the same barriers.
-  const int wvu = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (wvu < 4) {
-    // ===================== state waves =====================
-    f32x4 sacc[2][kNCT];
-    Frag<bf16> mqk[2], krt[2][2];
-    f32x4 acv[2];
-    bf16 vcur[kNCT][4], vnxt[kNCT][4];
-  auto load_v = [&](bf16 (&dst)[kNCT][4], int chunk) {
-      const int len = min(kC, cd.ntok - chunk * kC);
-      const bf16 *vb = vchain + (int64_t)chunk * kC * rowstride;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = min(16 * wv + 4 * lg + i, len - 1);
-#pragma unroll
-        for (int ct = 0; ct < kNCT; ++ct)
-          dst[ct][i] = vb[(int64_t)rr * rowstride + 16 * ct + lr];
-      }
-    };
-
-
+  if (wv < 4) {
+    // =========================== state waves ===========================
+    const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int wcol = col0 + VW * wv + lr; // this lane's column in tile c: wcol + 16 c
+    f32x4 S[NCT][8];                      // rows p = 16 ct + 4 lg + i: channel kperm(p)
     {
       const float *ip = nullptr;
       if (cd.init_idx >= 0)
@@ -209,403 +234,523 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
       else if (cd.init_idx <= -2)
         ip = sin + ((int64_t)(-2 - cd.init_idx) * H + h) * (kD * kD);
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+      for (int c = 0; c < NCT; ++c)
 #pragma unroll
-        for (int ct = 0; ct < kNCT; ++ct)
+        for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = 16 * (2 * wv + rt) + 4 * lg + i;
-            sacc[rt][ct][i] = ip ? ip[row * kD + vcol0 + 16 * ct + lr] : 0.f;
-          }
+          for (int i = 0; i < 4; ++i)
+            S[c][ct][i] = ip ? ip[kperm(16 * ct + 4 * lg + i) * kD + wcol + 16 * c] : 0.f;
     }
-    if (nch > 0) {
-      load_v(vcur, 0);
-      for (int b = 0; b < kStagesPerChunk; ++b) // the prep builds chunk 0
-        fsync();
-    }
-    for (int ch = 0; ch < nch; ++ch) {
-      const int len = min(kC, cd.ntok - ch * kC);
-      // ---- stage 1: copy the small hand-off arrays, S -> Sb, prefetch v
+    uint8_t *svw = reinterpret_cast<uint8_t *>(&sm.sv[wv][0]);
+    // rows 0..63 of this wave's VW columns of one chunk into its LDS slice:
+    // lane l of instruction j moves 16 bytes (8 columns) of row
+    // (64 j + l) / (2 NCT); rows past the chunk end read as 0
+    auto v_to_lds = [&](int chunk) {
+      const int clen = min(kC, cd.ntok - chunk * kC);
+      const bf16 *vb =
+          v + (cd.tok0 + (int64_t)chunk * kC) * rowstride + (int64_t)h * kD + col0 + VW * wv;
+      const __amdgpu_buffer_rsrc_t rv =
+          buffer_rsrc(vb, (uint32_t)(((clen - 1) * rowstride + VW) * sizeof(bf16)));
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        mqk[s] = load_frag(&sm.hMqk[16 * wv + lr][32 * s + 8 * lg]);
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-          krt[rt][s] = load_frag(&sm.hKrT[16 * (2 * wv + rt) + lr][32 * s + 8 * lg]);
-      }
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-        acv[rt] = *reinterpret_cast<const f32x4 *>(&sm.hAc[16 * (2 * wv + rt) + 4 * lg]);
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < kNCT; ++ct)
-          store4(&sm.Sb[16 * ct + lr][16 * (2 * wv + rt) + 4 * lg], sacc[rt][ct][0],
-                 sacc[rt][ct][1], sacc[rt][ct][2], sacc[rt][ct][3]);
-      if (ch + 1 < nch)
-        load_v(vnxt, ch + 1);
-      fsync();
-      // ---- stage 2: W = K_decay S, O = Q_decay S, V - W -> VWb
-      f32x4 Oa[kNCT];
-      {
-        f32x4 W[kNCT];
-#pragma unroll
-        for (int ct = 0; ct < kNCT; ++ct) {
-          W[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-          Oa[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int kb = 32 * s + 8 * lg;
-          const Frag<bf16> akd = load_frag(&sm.hKd[16 * wv + lr][kb]);
-          const Frag<bf16> aqd = load_frag(&sm.hQd[16 * wv + lr][kb]);
-#pragma unroll
-          for (int ct = 0; ct < kNCT; ++ct) {
-            const Frag<bf16> b = load_frag(&sm.Sb[16 * ct + lr][kb]);
-            mma(W[ct], akd, b);
-            mma(Oa[ct], aqd, b);
-          }
-        }
-#pragma unroll
-        for (int ct = 0; ct < kNCT; ++ct) {
-          float x[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = 16 * wv + 4 * lg + i;
-            const float vv = row < len ? static_cast<float>(vcur[ct][i]) : 0.f;
-            x[i] = vv - W[ct][i];
-          }
-          store4(&sm.VWb[16 * ct + lr][16 * wv + 4 * lg], x[0], x[1], x[2], x[3]);
-        }
-      }
-      fsync();
-      // ---- stage 3: U = INV Diag(beta) (V - W) -> Ub
-      {
-        f32x4 U[kNCT];
-#pragma unroll
-        for (int ct = 0; ct < kNCT; ++ct)
-          U[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int kb = 32 * s + 8 * lg;
-          const Frag<bf16> a = load_frag(&sm.hINVb[16 * wv + lr][kb]);
-#pragma unroll
-          for (int ct = 0; ct < kNCT; ++ct) {
-            const Frag<bf16> b = load_frag(&sm.VWb[16 * ct + lr][kb]);
-            mma(U[ct], a, b);
-          }
-        }
-#pragma unroll
-        for (int ct = 0; ct < kNCT; ++ct)
-          store4(&sm.Ub[16 * ct + lr][16 * wv + 4 * lg], U[ct][0], U[ct][1], U[ct][2],
-                 U[ct][3]);
-      }
-      fsync();
-      // ---- stage 4: O = Q_decay S + M_qk U (stored), S = Diag(a) S + K_restore^T U
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int kb = 32 * s + 8 * lg;
-#pragma unroll
-        for (int ct = 0; ct < kNCT; ++ct) {
-          const Frag<bf16> b = load_frag(&sm.Ub[16 * ct + lr][kb]);
-          mma(Oa[ct], mqk[s], b);
-        }
-      }
-      bf16 *orow = o + (cd.tok0 + (int64_t)ch * kC) * rowstride + (int64_t)h * kD + vcol0;
-#pragma unroll
-      for (int ct = 0; ct < kNCT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * wv + 4 * lg + i;
-          if (row < len)
-            orow[(int64_t)row * rowstride + 16 * ct + lr] = static_cast<bf16>(Oa[ct][i]);
-        }
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-        for (int ct = 0; ct < kNCT; ++ct)
-          sacc[rt][ct] *= acv[rt];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int kb = 32 * s + 8 * lg;
-#pragma unroll
-          for (int ct = 0; ct < kNCT; ++ct) {
-            const Frag<bf16> b = load_frag(&sm.Ub[16 * ct + lr][kb]);
-            mma(sacc[rt][ct], krt[rt][s], b);
-          }
-        }
-      }
-#pragma unroll
-      for (int ct = 0; ct < kNCT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          vcur[ct][i] = vnxt[ct][i];
-      fsync();
-      // ---- stages 5-7: the prep finishes INV for the next chunk
-      for (int b = 4; b < kStagesPerChunk; ++b)
-        fsync();
-    }
-    if (cd.final_idx >= 0) {
-      float *fp = final_state + ((int64_t)cd.final_idx * H + h) * (kD * kD);
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < kNCT; ++ct)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = 16 * (2 * wv + rt) + 4 * lg + i;
-            fp[row * kD + vcol0 + 16 * ct + lr] = sacc[rt][ct][i];
-          }
-    }
-  } else {
-    // ===================== prep waves =====================
-    const int pw = wvu - 4;
-    PrepRaw raw;
-    Frag<bf16> aK[4], aQ[4], bS[4];
-    float gl[32];
-    f32x4 accL[4], accM[4];
-  // The prep pipeline for one chunk, split into the stages that line up with
-    // the state waves' stages (every stage ends with a workgroup barrier).
-    // Stage P1: cumulative decay inside each tile, tile totals, beta.
-    auto prep_scan = [&](int chunk) {
-      const int lane_ = opaque_lane(), lr = lane_ & 15, lg = lane_ >> 4;
-      const int len = min(kC, cd.ntok - chunk * kC);
-      const int r = 16 * pw + lr;
-      const bool ok = r < len;
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float x = ok ? static_cast<float>(raw.g[s][j]) * kLog2e : 0.f;
-          gl[8 * s + j] = row_scan16(x);
-        }
-      if (lr == 15) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          *reinterpret_cast<f32x4 *>(&sm.sTot[pw][32 * s + 8 * lg]) =
-              f32x4{gl[8 * s], gl[8 * s + 1], gl[8 * s + 2], gl[8 * s + 3]};
-          *reinterpret_cast<f32x4 *>(&sm.sTot[pw][32 * s + 8 * lg + 4]) =
-              f32x4{gl[8 * s + 4], gl[8 * s + 5], gl[8 * s + 6], gl[8 * s + 7]};
-        }
-      }
-      if (lg == 0)
-        sm.sBeta[r] = ok ? raw.beta : 0.f;
-    };
-    // Stage P2: per-channel factor tables from the tile totals.
-    auto prep_tables = [&]() {
-      const int pt = tid - 256;
-      const int c = pt & (kD - 1);
-      const float t0 = sm.sTot[0][c], t1 = sm.sTot[1][c], t2 = sm.sTot[2][c], t3 = sm.sTot[3][c];
-      const float p[5] = {0.f, t0, t0 + t1, t0 + t1 + t2, t0 + t1 + t2 + t3};
-      if (pt < 128) {
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          sm.sEp[I][c] = __builtin_amdgcn_exp2f(p[I]);
-          sm.sEs[I][c] = __builtin_amdgcn_exp2f(p[I + 1] - p[I]);
-        }
-        sm.hAc[c] = __builtin_amdgcn_exp2f(p[4]);
-      } else {
-#pragma unroll
-        for (int I = 0; I < 4; ++I)
-          sm.sEr[I][c] = __builtin_amdgcn_exp2f(p[4] - p[I + 1]);
-        sm.sF[0][c] = __builtin_amdgcn_exp2f(p[1] - p[1]);
-        sm.sF[1][c] = __builtin_amdgcn_exp2f(p[2] - p[1]);
-        sm.sF[2][c] = __builtin_amdgcn_exp2f(p[2] - p[2]);
-        sm.sF[3][c] = __builtin_amdgcn_exp2f(p[3] - p[1]);
-        sm.sF[4][c] = __builtin_amdgcn_exp2f(p[3] - p[2]);
-        sm.sF[5][c] = __builtin_amdgcn_exp2f(p[3] - p[3]);
+      for (int j = 0; j < 2 * NCT; ++j) {
+        const int u = 64 * j + lane, r = u / (2 * NCT), qq = u % (2 * NCT);
+        lds_load16(rv, (int)((r * rowstride + 8 * qq) * sizeof(bf16)), svw + 1024 * j);
       }
     };
-    // Stage P3: decayed operands of this lane's row, produced two channels at
-    // a time and packed to bf16 at once so few fp32 temporaries are live.
-    auto prep_elem = [&](int chunk) {
-      const int lane_ = opaque_lane(), lr = lane_ & 15, lg = lane_ >> 4;
-      const int len = min(kC, cd.ntok - chunk * kC);
-      const int r = 16 * pw + lr;
-      const bool ok = r < len;
+    f32x4 W[NCT][4], Oa[NCT][4]; // of the chunk whose record is current
+
+    // W = K_decay S and O = Q_decay S (K = channels)
+    auto stage_wo = [&]() {
+      const int ln = opaque_lane(), lr = ln & 15, lg = ln >> 4;
+      auto frag = [&](const bf16 *base, int ld, int tile, int s) {
+        return load_frag(base + (16 * tile + lr) * ld + 32 * s + 8 * lg);
+      };
+      Frag<bf16> bs[NCT][4];
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          bs[c][s] = pack_acc2(S[c][2 * s], S[c][2 * s + 1]);
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          W[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          Oa[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int c0 = 32 * s + 8 * lg;
-        bf16x8 vkl, vql, vks, vke, vkd, vqd;
+        Frag<bf16> ak[4], aq[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float kv = ok ? static_cast<float>(raw.k[s][j]) : 0.f;
-          const float qv = ok ? static_cast<float>(raw.q[s][j]) : 0.f;
-          const float el = __builtin_amdgcn_exp2f(gl[8 * s + j]);   // (e^-80, 1]
-          const float es_ = __builtin_amdgcn_exp2f(-gl[8 * s + j]); // [1, e^80)
-          const float ep = sm.sEp[pw][c0 + j];
-          const float kl = kv * el, ql = qv * el, ks = kv * es_;
-          const float ke = ks * sm.sEs[pw][c0 + j];
-          vkl[j] = static_cast<bf16>(kl);
-          vql[j] = static_cast<bf16>(ql);
-          vks[j] = static_cast<bf16>(ks);
-          vke[j] = static_cast<bf16>(ke);
-          vkd[j] = static_cast<bf16>(kl * ep);
-          vqd[j] = static_cast<bf16>(ql * ep);
-          // K_restore^T: column r of row c0 + j
-          sm.hKrT[c0 + j][r] = static_cast<bf16>(ke * sm.sEr[pw][c0 + j]);
+        for (int tt = 0; tt < 4; ++tt) {
+          ak[tt] = frag(&sm.Kd[0][0], kLdD, tt, s);
+          aq[tt] = frag(&sm.Qd[0][0], kLdD, tt, s);
         }
-        aK[s].v = vkl;
-        aQ[s].v = vql;
-        bS[s].v = vks;
-        *reinterpret_cast<bf16x8 *>(&sm.sKe[r][c0]) = vke;
-        *reinterpret_cast<bf16x8 *>(&sm.hKd[r][c0]) = vkd;
-        *reinterpret_cast<bf16x8 *>(&sm.hQd[r][c0]) = vqd;
-        // one channel group at a time keeps the temporaries' live ranges short
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int c = 0; c < NCT; ++c) {
+            mma(W[c][tt], ak[tt], bs[c][s]);
+            mma(Oa[c][tt], aq[tt], bs[c][s]);
+          }
       }
     };
-    // Stage P4: L and M_qk tiles of row tile pw on MFMA.
-    auto prep_mfma = [&]() {
-      const int lane_ = opaque_lane(), lr = lane_ & 15, lg = lane_ >> 4;
+
+    // U = INV Diag(beta) (V - W), O += M_qk U and store o, for chunk ch;
+    // U is left packed in bu for the state update
+    Frag<bf16> bu[NCT][2];
+    auto stage_u = [&](int ch) {
+      const int ln = opaque_lane(), lr = ln & 15, lg = ln >> 4;
+      const int wcol = col0 + VW * wv + lr;
+      auto frag = [&](const bf16 *base, int ld, int tile, int s) {
+        return load_frag(base + (16 * tile + lr) * ld + 32 * s + 8 * lg);
+      };
+      const int len = min(kC, cd.ntok - ch * kC);
+      const int64_t tok = cd.tok0 + (int64_t)ch * kC;
+      wait_vmem_all(); // this chunk's v is in the wave's LDS slice
+      const bf16 *svb = &sm.sv[wv][0];
 #pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        accL[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-        accM[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (J <= pw) {
+      for (int c = 0; c < NCT; ++c)
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            Frag<bf16> b;
-            if (J == pw) {
-              b = bS[s];
-            } else {
-              const int c0 = 32 * s + 8 * lg;
-              const Frag<bf16> e = load_frag(&sm.sKe[16 * J + lr][c0]);
-              const float *f = &sm.sF[off_pair(pw, J)][c0];
-              float x[8];
-              frag_to_f32(e, x);
-#pragma unroll
-              for (int j = 0; j < 8; ++j)
-                x[j] *= f[j];
-              b = frag_from_f32<bf16>(x);
-            }
-            mma(accL[J], aK[s], b);
-            mma(accM[J], aQ[s], b);
-          }
-        }
-      }
-      // M_qk (diagonal kept) to the hand-off; lower tiles only
-#pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        if (J <= pw) {
-          const int col = 16 * J + lr;
+        for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int row = 16 * pw + 4 * lg + i;
-            sm.hMqk[row][col] = static_cast<bf16>(col <= row ? accM[J][i] : 0.f);
+            const int row = 16 * tt + 4 * lg + i;
+            W[c][tt][i] = static_cast<float>(svb[row * VW + 16 * c + lr]) - W[c][tt][i];
           }
-        }
+      if (ch + 1 < nch) {
+        __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0): the slice reads have returned
+        v_to_lds(ch + 1);
       }
-    };
-    // Stage P5: L = StrictTril(Diag(beta) ...) into the fp32 matrix (in Sb).
-    auto prep_store_L = [&]() {
-      const int lane_ = opaque_lane(), lr = lane_ & 15, lg = lane_ >> 4;
+      Frag<bf16> bw[NCT][2];
 #pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        if (J <= pw) {
-          const int col = 16 * J + lr;
+      for (int c = 0; c < NCT; ++c)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = 16 * pw + 4 * lg + i;
-            sL[row][col] = col < row ? sm.sBeta[row] * accL[J][i] : 0.f;
-          }
-        }
+        for (int s = 0; s < 2; ++s)
+          bw[c][s] = pack_acc2(W[c][2 * s], W[c][2 * s + 1]);
+      f32x4 U[NCT][4];
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          U[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        Frag<bf16> ai[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          ai[tt] = frag(&sm.INVb[0][0], kLdC, tt, s);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int c = 0; c < NCT; ++c)
+            mma(U[c][tt], ai[tt], bw[c][s]);
       }
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          bu[c][s] = pack_acc2(U[c][2 * s], U[c][2 * s + 1]);
+      // O += M_qk U
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        Frag<bf16> am[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          am[tt] = frag(&sm.Mqk[0][0], kLdC, tt, s);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int c = 0; c < NCT; ++c)
+            mma(Oa[c][tt], am[tt], bu[c][s]);
+      }
+      // rows past the chunk end fall outside the buffer and are dropped
+      const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(
+          o + tok * rowstride + (int64_t)h * kD, (uint32_t)((len - 1) * rowstride + kD) * 2);
+      const int vo = (int)((4 * lg * rowstride + wcol) * 2);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int so = (int)((16 * tt + i) * rowstride * 2); // wave-uniform
+#pragma unroll
+          for (int c = 0; c < NCT; ++c)
+            buffer_store(ro, static_cast<bf16>(Oa[c][tt][i]), vo + 32 * c, so);
+        }
     };
-    // INV = (I + L)^-1 by 16 x 16 blocks, all products on fp32 MFMA.
-    // Level 0 (wave b, no cross-wave data): D_b = I + N with N = L_bb strictly
-    // lower, so D_b^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) exactly (N^16 = 0).
-    // X_bb = D_b^-1 stays in registers as this wave's first block of its
-    // column block of INV.
-    f32x4 X[4];
-    auto inv_level0 = [&]() {
-      const int lane_ = opaque_lane(), lr = lane_ & 15, lg = lane_ >> 4;
-      const int b = pw;
-      const float *N = &sL[16 * b][16 * b];
-      float *P2 = &sm.sPow[b][0][0][0];
-      float *P4 = &sm.sPow[b][1][0][0];
-      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-      const f32x4 n1 = acc_load(N, kLdL, lr, lg);
-      f32x4 n2 = zero, n4 = zero, y = zero;
-      mm16_lds_acc(n2, N, kLdL, n1, lr, lg);          // N^2
-      acc_store(P2, kLdB, n2, lr, lg);
-      mm16_lds_acc(n4, P2, kLdB, n2, lr, lg);         // N^4
-      acc_store(P4, kLdB, n4, lr, lg);
-      mm16_lds_acc(y, P4, kLdB, n4, lr, lg);          // N^8
+
+    // S = Diag(a_last) S + K_restore^T U (K = tokens), for the chunk whose
+    // U was packed into bu by stage_u
+    auto stage_s = [&]() {
+      const int ln = opaque_lane(), lr = ln & 15, lg = ln >> 4;
+      auto frag = [&](const bf16 *base, int ld, int tile, int s) {
+        return load_frag(base + (16 * tile + lr) * ld + 32 * s + 8 * lg);
+      };
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        y[i] += (4 * lg + i == lr) ? 1.f : 0.f;        // I + N^8
-      mm16_lds_acc(y, P4, kLdB, y, lr, lg);           // (I + N^4) Y
-      mm16_lds_acc(y, P2, kLdB, y, lr, lg);           // (I + N^2) Y
-      mm16_lds_acc(y, N, kLdL, y, lr, lg, -1.f);      // (I - N) Y
+      for (int ct = 0; ct < 8; ++ct) {
+        const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&sm.aL[16 * ct + 4 * lg]);
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (t == b)
-          X[t] = y; // static register index
-      acc_store(&sm.sD[b][0][0], kLdB, y, lr, lg);
-      const float bcol = sm.sBeta[16 * b + lr];
+        for (int c = 0; c < NCT; ++c)
+          S[c][ct] *= a4;
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sm.hINVb[16 * b + 4 * lg + i][16 * b + lr] = static_cast<bf16>(y[i] * bcol);
-    };
-    // Level 1: wave j walks down its column block of INV by block forward
-    // substitution, X_ij = -D_i^-1 sum_{m=j}^{i-1} L_im X_mj, using only its
-    // own earlier blocks, the shared L and the D_i^-1 of level 0.
-    auto inv_level1 = [&]() {
-      const int lane_ = opaque_lane(), lr = lane_ & 15, lg = lane_ >> 4;
-      const int j = pw;
-      const float bcol = sm.sBeta[16 * j + lr];
+      for (int s = 0; s < 2; ++s) {
 #pragma unroll
-      for (int i = 1; i < 4; ++i) {
-        if (i > j) {
-          f32x4 t = {0.f, 0.f, 0.f, 0.f};
+        for (int hf = 0; hf < 2; ++hf) {
+          Frag<bf16> ar[4];
 #pragma unroll
-          for (int m = 0; m < 3; ++m)
-            if (m >= j && m < i)
-              mm16_lds_acc(t, &sL[16 * i][16 * m], kLdL, X[m], lr, lg);
-          f32x4 x = {0.f, 0.f, 0.f, 0.f};
-          mm16_lds_acc(x, &sm.sD[i][0][0], kLdB, t, lr, lg, -1.f);
-          X[i] = x;
+          for (int ct = 0; ct < 4; ++ct)
+            ar[ct] = frag(&sm.KrT[0][0], kLdC, 4 * hf + ct, s);
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            sm.hINVb[16 * i + 4 * lg + r][16 * j + lr] = static_cast<bf16>(x[r] * bcol);
+          for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int c = 0; c < NCT; ++c)
+              mma(S[c][4 * hf + ct], ar[ct], bu[c][s]);
         }
       }
     };
 
-    // One chunk's preparation, in kStagesPerChunk barrier-separated stages.
-    // Its raw inputs must already be in `raw`; the next chunk's inputs are
-    // loaded as soon as these are consumed.
-    auto prep_chunk = [&](int chunk, bool active) {
-      const bool more = chunk + 1 < nch;
-      const int64_t ntok0 = cd.tok0 + (int64_t)(chunk + 1) * kC;
-      const int nlen = min(kC, cd.ntok - (chunk + 1) * kC);
-      if (active) prep_scan(chunk);
+    // D_b^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) for N = L_bb (N^16 = 0), b =
+    // this wave's index: the diagonal blocks of INV = (I + L)^-1 of the chunk
+    // being prepared, to LDS (for the prep's off-diagonal blocks) and to the
+    // record as INV Diag(beta)
+    auto stage_inv = [&]() {
+      const int ln = opaque_lane(), lr = ln & 15, lg = ln >> 4;
+      const int b = wv;
+      const float *N = &sm.L[16 * b][16 * b];
+      float *P2 = &sm.x.Pow[b][0][0][0];
+      float *P4 = &sm.x.Pow[b][1][0][0];
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 n1 = acc_load(N, kLdL, lr, lg);
+      f32x4 n2 = zero, n4 = zero, y = zero;
+      mm16_lds_acc(n2, N, kLdL, n1, lr, lg); // N^2
+      acc_store(P2, kLdB, n2, lr, lg);
+      wave_lds_fence();
+      mm16_lds_acc(n4, P2, kLdB, n2, lr, lg); // N^4
+      acc_store(P4, kLdB, n4, lr, lg);
+      wave_lds_fence();
+      mm16_lds_acc(y, P4, kLdB, n4, lr, lg); // N^8
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        y[i] += (4 * lg + i == lr) ? 1.f : 0.f; // I + N^8
+      mm16_lds_acc(y, P4, kLdB, y, lr, lg);      // (I + N^4) Y
+      mm16_lds_acc(y, P2, kLdB, y, lr, lg);      // (I + N^2) Y
+      mm16_lds_acc(y, N, kLdL, y, lr, lg, -1.f); // (I - N) Y
+      acc_store(&sm.Dinv[b][0][0], kLdB, y, lr, lg);
+      const float bcol = sm.Beta[16 * b + lr];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sm.INVb[16 * b + 4 * lg + i][kperm(16 * b + lr)] = static_cast<bf16>(y[i] * bcol);
+    };
+
+    // chunk steps 0 .. nch, four barriers each (the ends of stages A-D):
+    // step it finishes chunk it - 1 in stages A and B, inverts the diagonal
+    // blocks of chunk it in stage C and starts chunk it in stage D
+    if (nch == 0) {
+      for (int b = 0; b < 4; ++b)
+        fsync();
+    } else {
+      v_to_lds(0);
       fsync();
-      if (active) prep_tables();
       fsync();
-      if (active) prep_elem(chunk);
+      stage_inv();
       fsync();
-      if (more)
-        prep_load_g(raw, g, beta, ntok0, nlen, H, h, rowstride, pw, lr, lg);
-      if (active) {
-        prep_mfma();
-        prep_store_L(); // sL rows of tile pw: read below by this wave only
-        inv_level0();
+      stage_wo();
+      fsync();
+      for (int ch = 0; ch + 1 < nch; ++ch) {
+        stage_u(ch);
+        fsync();
+        stage_s();
+        fsync();
+        stage_inv();
+        fsync();
+        stage_wo();
+        fsync();
+      }
+      stage_u(nch - 1);
+      fsync();
+      stage_s();
+      fsync();
+      fsync();
+      fsync();
+    }
+    if (cd.final_idx >= 0) {
+      float *fp = final_state + ((int64_t)cd.final_idx * H + h) * (kD * kD);
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            fp[kperm(16 * ct + 4 * lg + i) * kD + wcol + 16 * c] = S[c][ct][i];
+    }
+  } else {
+    // ============================ prep waves ============================
+    const int pw = wv - 4; // token tile
+    // raw inputs of the chunk being prepared: channels 32 s + 8 lg .. + 7 of
+    // this lane's token, per k-step s
+    u32x4 rg[4], rq[4], rk[4];
+    // beta stays raw until it is used: widening it where it is loaded would
+    // make the wave wait for every load in flight
+    unsigned short rbeta = 0;
+    auto issue = [&](int chunk) {
+      const int ln = opaque_lane(), lr = ln & 15, lg = ln >> 4, r = 16 * pw + lr;
+      const int len = min(kC, cd.ntok - chunk * kC);
+      const int64_t tok = cd.tok0 + (int64_t)chunk * kC;
+      const int64_t base = tok * rowstride + (int64_t)h * kD;
+      const uint32_t nbytes = (uint32_t)(((len - 1) * rowstride + kD) * 2);
+      const __amdgpu_buffer_rsrc_t bg = buffer_rsrc(g + base, nbytes);
+      const __amdgpu_buffer_rsrc_t bk = buffer_rsrc(k + base, nbytes);
+      const __amdgpu_buffer_rsrc_t bq = buffer_rsrc(q + base, nbytes);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int vo = (int)((r * rowstride + 32 * s + 8 * lg) * 2);
+        rg[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(bg, vo, 0, 0));
+        rk[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(bk, vo, 0, 0));
+        rq[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(bq, vo, 0, 0));
+      }
+      if (lg == 0) {
+        const __amdgpu_buffer_rsrc_t bb =
+            buffer_rsrc(beta + tok * H + h, (uint32_t)(((len - 1) * (int64_t)H + 1) * 2));
+        rbeta = __builtin_amdgcn_raw_buffer_load_b16(bb, (int)(r * H * 2), 0, 0);
+      }
+    };
+    if (nch > 0)
+      issue(0);
+
+    float xg[4][8];            // G_loc log2(e) per record channel
+    Frag<bf16> fq[4], fk[4];   // Q_loc, K_loc fragments
+    f32x4 accLd, accMd;        // diagonal tile pair (L, M_qk)
+    f32x4 accLp[2], accMp[2];  // this wave's off-diagonal pairs
+    Frag<bf16> kr[4];          // K_restore of this lane's token, record order
+    float aLr[2] = {0.f, 0.f}; // a_last of two channels (wave 0)
+
+    for (int it = 0; it < nch; ++it) {
+      // ---- stage A: tile scan, Q_loc / K_loc / K_start, diagonal tile pair ----
+      {
+        const int lane = opaque_lane(), lr = lane & 15, lg = lane >> 4, r = 16 * pw + lr;
+        // inclusive cumulative sum over the tile's tokens, then the tile
+        // totals (lane 15 of each row) to LDS
+        float G[4][8];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          widen8(rg[s], G[s]);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            G[s][j] = row_scan16(G[s][j]);
+        }
+        if (lr == 15) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            *reinterpret_cast<f32x4 *>(&sm.Tot[pw][32 * s + 8 * lg]) =
+                f32x4{G[s][0], G[s][1], G[s][2], G[s][3]};
+            *reinterpret_cast<f32x4 *>(&sm.Tot[pw][32 * s + 8 * lg + 4]) =
+                f32x4{G[s][4], G[s][5], G[s][6], G[s][7]};
+          }
+        }
+        if (lg == 0)
+          sm.Beta[r] = __builtin_bit_cast(float, (unsigned)rbeta << 16);
+        accLd = f32x4{0.f, 0.f, 0.f, 0.f};
+        accMd = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          float qv[8], kv[8], xq[8], xk[8], xs[8];
+          widen8(rq[s], qv);
+          widen8(rk[s], kv);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float x = G[s][j] * kLog2e;
+            xg[s][j] = x;
+            const float e1 = __builtin_amdgcn_exp2f(x);
+            xq[j] = qv[j] * e1;
+            xk[j] = kv[j] * e1;
+            xs[j] = kv[j] * __builtin_amdgcn_exp2f(-x);
+          }
+          fq[s] = pack8(xq);
+          fk[s] = pack8(xk);
+          const Frag<bf16> fs = pack8(xs);
+          *reinterpret_cast<bf16x8 *>(&sm.x.ab.Kst[pw][lr][32 * s + 8 * lg]) = fs.v;
+          if (pw == 3) {
+            *reinterpret_cast<bf16x8 *>(&sm.x.ab.Aq3[0][lr][32 * s + 8 * lg]) = fk[s].v;
+            *reinterpret_cast<bf16x8 *>(&sm.x.ab.Aq3[1][lr][32 * s + 8 * lg]) = fq[s].v;
+          }
+          mma(accLd, fk[s], fs);
+          mma(accMd, fq[s], fs);
+        }
+        // the diagonal L tile (beta-scaled rows, strictly lower) for the
+        // state waves' inversion of the diagonal blocks in stage C
+        wave_lds_fence(); // this wave's beta entries are in LDS
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * pw + 4 * lg + i, col = 16 * pw + lr;
+          sm.L[row][col] = col < row ? sm.Beta[row] * accLd[i] : 0.f;
+        }
       }
       fsync();
-      if (more)
-        prep_load_qk(raw, q, k, ntok0, nlen, h, rowstride, pw, lr, lg);
-      if (active) inv_level1();
+      // ---- stage B: factors, Q_decay / K_decay / K_restore, off-diagonal pairs ----
+      {
+        const int lane = opaque_lane(), lr = lane & 15, lg = lane >> 4, r = 16 * pw + lr;
+        {
+          // this tile's factors for two record-order channels per lane
+          const int c0 = 2 * lane;
+          float t[4][2];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float2 x = *reinterpret_cast<const float2 *>(&sm.Tot[w][c0]);
+            t[w][0] = x.x;
+            t[w][1] = x.y;
+          }
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            float pI = 0.f, gc = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              pI += w < pw ? t[w][e] : 0.f;
+              gc += t[w][e];
+            }
+            sm.Fac[pw][0][c0 + e] = pI * kLog2e;
+            sm.Fac[pw][1][c0 + e] = (gc - pI) * kLog2e;
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+              if (n < pair_count(pw)) {
+                const int I = pair_I(pw, n), J = pair_J(pw, n);
+                float sum = 0.f; // p_I - p_J = t_J + ... + t_{I-1} <= 0
+#pragma unroll
+                for (int w = 0; w < 3; ++w)
+                  sum += (w >= J && w < I) ? t[w][e] : 0.f;
+                sm.Foff[off_pair(I, J)][c0 + e] = __builtin_amdgcn_exp2f(sum * kLog2e);
+              }
+            }
+            if (pw == 0)
+              aLr[e] = __builtin_amdgcn_exp2f(gc * kLog2e);
+          }
+        }
+        wave_lds_fence();
+        // Q_decay and K_decay rows to the record, K_restore to registers
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          float xp[8], xc[8], qv[8], kv[8], yq[8], yk[8], yr[8];
+          load8f(&sm.Fac[pw][0][32 * s + 8 * lg], xp);
+          load8f(&sm.Fac[pw][1][32 * s + 8 * lg], xc);
+          widen8(rq[s], qv);
+          widen8(rk[s], kv);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float a = __builtin_amdgcn_exp2f(xg[s][j] + xp[j]); // e^{G}
+            const float b = __builtin_amdgcn_exp2f(xc[j] - xg[s][j]); // e^{G_C - G}
+            yq[j] = qv[j] * a;
+            yk[j] = kv[j] * a;
+            yr[j] = kv[j] * b;
+          }
+          *reinterpret_cast<bf16x8 *>(&sm.Qd[r][32 * s + 8 * lg]) = pack8(yq).v;
+          *reinterpret_cast<bf16x8 *>(&sm.Kd[r][32 * s + 8 * lg]) = pack8(yk).v;
+          kr[s] = pack8(yr);
+        }
+        // off-diagonal pairs (I, J): B = K_start of tile J times e^{p_I - p_J}
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          accLp[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+          accMp[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (n < pair_count(pw)) {
+            const int I = pair_I(pw, n), J = pair_J(pw, n);
+            const int pi = off_pair(I, J);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              const Frag<bf16> e = load_frag(&sm.x.ab.Kst[J][lr][32 * s + 8 * lg]);
+              float xs[8], fo[8];
+              frag_to_f32(e, xs);
+              load8f(&sm.Foff[pi][32 * s + 8 * lg], fo);
+#pragma unroll
+              for (int j = 0; j < 8; ++j)
+                xs[j] *= fo[j];
+              const Frag<bf16> b = pack8(xs);
+              Frag<bf16> ak, aq;
+              if (I == pw) {
+                ak = fk[s];
+                aq = fq[s];
+              } else {
+                ak = load_frag(&sm.x.ab.Aq3[0][lr][32 * s + 8 * lg]);
+                aq = load_frag(&sm.x.ab.Aq3[1][lr][32 * s + 8 * lg]);
+              }
+              mma(accLp[n], ak, b);
+              mma(accMp[n], aq, b);
+            }
+          }
+        }
+        // the next chunk's inputs are in flight from here on
+        if (it + 1 < nch)
+          issue(it + 1);
+      }
       fsync();
-    };
-    if (nch > 0) {
-      prep_load_g(raw, g, beta, cd.tok0, min(kC, cd.ntok), H, h, rowstride, pw, lr, lg);
-      prep_load_qk(raw, q, k, cd.tok0, min(kC, cd.ntok), h, rowstride, pw, lr, lg);
-      prep_chunk(0, true);
+      // ---- stage C: L / M_qk tiles, K_restore^T, a_last -------------------------
+      {
+        const int lane = opaque_lane(), lr = lane & 15, lg = lane >> 4, r = 16 * pw + lr;
+        // off-diagonal tiles (I > J: no mask) and the diagonal M_qk tile
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+          if (n < pair_count(pw)) {
+            const int I = pair_I(pw, n), J = pair_J(pw, n), col = 16 * J + lr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int row = 16 * I + 4 * lg + i;
+              sm.L[row][col] = sm.Beta[row] * accLp[n][i];
+              sm.Mqk[row][kperm(col)] = static_cast<bf16>(accMp[n][i]);
+            }
+          }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * pw + 4 * lg + i, col = 16 * pw + lr;
+          sm.Mqk[row][kperm(col)] = static_cast<bf16>(col <= row ? accMd[i] : 0.f);
+        }
+        // K_restore^T: row kperm_inv(channel), column kperm(token)
+        {
+          const int kc = kperm(r);
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              sm.KrT[kperm_inv(32 * s + 8 * lg + e)][kc] = kr[s].v[e];
+        }
+        if (pw == 0) {
+          sm.aL[kperm_inv(2 * lane)] = aLr[0];
+          sm.aL[kperm_inv(2 * lane + 1)] = aLr[1];
+        }
+      }
+      fsync();
+      // ---- stage D: off-diagonal blocks of INV ---------------------------------
+      {
+        const int lane = opaque_lane(), lr = lane & 15, lg = lane >> 4;
+        // column block j = pw: X_ij = -D_i^-1 sum_{m=j}^{i-1} L_im X_mj
+        const int j = pw;
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        f32x4 X[4];
+        const f32x4 dj = acc_load(&sm.Dinv[j][0][0], kLdB, lr, lg);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          X[t] = (t == j) ? dj : zero;
+        const float bcol = sm.Beta[16 * j + lr];
+#pragma unroll
+        for (int i = 1; i < 4; ++i) {
+          if (i > j) {
+            f32x4 t = zero;
+#pragma unroll
+            for (int m = 0; m < 3; ++m)
+              if (m >= j && m < i)
+                mm16_lds_acc(t, &sm.L[16 * i][16 * m], kLdL, X[m], lr, lg);
+            f32x4 x = zero;
+            mm16_lds_acc(x, &sm.Dinv[i][0][0], kLdB, t, lr, lg, -1.f);
+            X[i] = x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sm.INVb[16 * i + 4 * lg + e][kperm(16 * j + lr)] = static_cast<bf16>(x[e] * bcol);
+          }
+        }
+      }
+      fsync();
     }
-    for (int ch = 0; ch < nch; ++ch)
-      prep_chunk(ch + 1, ch + 1 < nch);
+    // the last chunk step only consumes the last record
+    for (int b = 0; b < 4; ++b)
+      fsync();
   }
 }
 
@@ -615,10 +760,12 @@ hipError_t launch_fused(const ChainDesc *chains, int32_t nchains, int32_t H, con
                         hipStream_t s) {
   if (nchains == 0)
     return hipSuccess;
-  dim3 grid((unsigned)nchains, (unsigned)H, kD / kFBV), block(kFThreads);
-  fused_kernel<<<grid, block, 0, s>>>(chains, H, (const bf16 *)q, (const bf16 *)k,
-                                      (const bf16 *)v, (const bf16 *)g, (const bf16 *)beta,
-                                      (bf16 *)o, init, sin, final_state);
+  // one workgroup per (chain, head) carries all 128 state columns
+  constexpr int NCT = 2;
+  dim3 grid((unsigned)nchains, (unsigned)H, kD / (64 * NCT)), block(kFThreads);
+  fused_kernel<NCT><<<grid, block, 0, s>>>(chains, H, (const bf16 *)q, (const bf16 *)k,
+                                           (const bf16 *)v, (const bf16 *)g, (const bf16 *)beta,
+                                           (bf16 *)o, init, sin, final_state);
   return hipGetLastError();
 }
 
