@@ -25,10 +25,14 @@ def hipcc() -> str:
 
 
 def compile_flags() -> list[str]:
-    # Packed-fp32 instructions are disabled for all device code.
+    # Packed-fp32 instructions are disabled for all device code.  MFMA
+    # accumulators stay in ordinary VGPRs: the kernels feed them straight back
+    # into VALU work (packing, scaling), and accumulator-register copies in
+    # between would cost one extra VALU op per element.
     return ["-O3", "-fPIC", "-std=c++17", "--offload-arch=" + ARCH, "-I" + INCLUDE, "-I" + CSRC,
             "-Wall", "-Wno-unused-function",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def build(verbose: bool = False) -> str:

@@ -18,6 +18,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -32,6 +33,8 @@ namespace {
 constexpr int64_t kAutoMinChains = 64;
 constexpr int64_t kAutoSegments = 64;
 constexpr int64_t kAutoMinSegChunks = 4;
+// Fewest (sequence, head) chains for the fused prefill kernel.
+constexpr int64_t kFusedMinChainHeads = 512;
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -39,6 +42,15 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned_elt(const void *p, kda_dtype dt) {
   return ((uintptr_t)p & (dt == KDA_BF16 ? 1u : 3u)) == 0;
+}
+
+// KDA_FUSED_PREFILL=1 forces the fused bf16 prefill kernel, =0 the two-kernel
+// path (unsplit bf16 calls only); unset or any other value: automatic.
+int fused_override() {
+  const char *e = std::getenv("KDA_FUSED_PREFILL");
+  if (!e || !e[0] || e[1])
+    return -1;
+  return e[0] == '1' ? 1 : (e[0] == '0' ? 0 : -1);
 }
 
 int64_t plan_nseg(int64_t len, int32_t num_seqs, int32_t H, int32_t split_hint) {
@@ -150,9 +162,18 @@ bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_h
   auto longer = [](const ChainDesc &a, const ChainDesc &b) { return a.ntok > b.ntok; };
   std::stable_sort(p.chains.begin(), p.chains.end(), longer);
   std::stable_sort(p.segchains.begin(), p.segchains.end(), longer);
-  // bf16 without a planner split: chunk prep and state carry run fused in
-  // one kernel, and no chunk-prep records go through memory
-  p.fused = es == 2 && p.segchains.empty();
+  // bf16 without a planner split and with enough chains to give every
+  // compute unit a few (sequence, head) pairs: chunk prep and state carry
+  // run fused in one kernel and no chunk-prep records go through memory.
+  // With fewer chains the chunk-parallel prep kernel keeps the whole chip
+  // busy and the two-kernel path is faster.
+  p.fused = es == 2 && p.segchains.empty() &&
+            (int64_t)p.chains.size() * H >= kFusedMinChainHeads;
+  if (es == 2 && p.segchains.empty()) {
+    const int force = fused_override();
+    if (force >= 0)
+      p.fused = force == 1;
+  }
   layout(p, H, es);
   return true;
 }

@@ -563,18 +563,19 @@ template <typename T, int NW> struct RecordCopy {
   static_assert(L::kd % 1024 == 0 && L::krt % 1024 == 0 && L::invb % 1024 == 0 &&
                     L::mqk % 1024 == 0 && L::ac % 1024 == 0,
                 "sections must start on 1 KiB blocks");
-  __device__ __forceinline__ static void issue(uint8_t *lds, const uint8_t *src, int wv,
-                                               int lane) {
+  static constexpr int kPerWave = (L::blocks + NW - 1) / NW;
+  // This lane's record byte offset for each of its wave's blocks; the same
+  // for every chunk, so it is computed once per workgroup.
+  __device__ __forceinline__ static void offsets(int (&goff)[kPerWave], int wv, int lane) {
     constexpr RecOff off(sizeof(T));
-    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(src, (uint32_t)k1_record_bytes(sizeof(T)));
 #pragma unroll
-    for (int j = 0; j < (L::blocks + NW - 1) / NW; ++j) {
+    for (int j = 0; j < kPerWave; ++j) {
       const int b = wv + j * NW; // wave-uniform
-      if (b >= L::blocks)
-        break;
       const int p = b * 1024 + lane * 16;
-      int g;
-      if (b * 1024 < L::kd)
+      int g = 0;
+      if (b >= L::blocks)
+        g = 0;
+      else if (b * 1024 < L::kd)
         g = section_src<L::padD, L::rowD>(p - L::qd, (int)off.qd);
       else if (b * 1024 < L::krt)
         g = section_src<L::padD, L::rowD>(p - L::kd, (int)off.kd);
@@ -586,7 +587,18 @@ template <typename T, int NW> struct RecordCopy {
         g = section_src<L::padC, L::rowC>(p - L::mqk, (int)off.mqk);
       else
         g = p - L::ac < kD * 4 ? (int)off.ac + (p - L::ac) : 0;
-      lds_load16(r, g, lds + b * 1024);
+      goff[j] = g;
+    }
+  }
+  __device__ __forceinline__ static void issue(uint8_t *lds, const uint8_t *src,
+                                               const int (&goff)[kPerWave], int wv) {
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(src, (uint32_t)k1_record_bytes(sizeof(T)));
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j) {
+      const int b = wv + j * NW; // wave-uniform
+      if (b >= L::blocks)
+        break;
+      lds_load16(r, goff[j], lds + b * 1024);
     }
   }
 };
@@ -687,7 +699,9 @@ __global__ __launch_bounds__(k2_threads(BV)) void k2_kernel(
       }
     };
     using RCopy = RecordCopy<T, NW>;
-    RCopy::issue(srecA, rec0, wv, lane);
+    int goff[RCopy::kPerWave];
+    RCopy::offsets(goff, wv, lane);
+    RCopy::issue(srecA, rec0, goff, wv);
     T vcur[VLDS ? 1 : NCT][4][4];
     if constexpr (VLDS)
       v_to_lds(0);
@@ -714,7 +728,7 @@ __global__ __launch_bounds__(k2_threads(BV)) void k2_kernel(
         if constexpr (!VLDS)
           load_v(vnxt, ch + 1);
         if (NBUF == 2)
-          RCopy::issue(nxt, rec0 + (int64_t)(ch + 1) * rec_step, wv, lane);
+          RCopy::issue(nxt, rec0 + (int64_t)(ch + 1) * rec_step, goff, wv);
       }
       __builtin_amdgcn_sched_barrier(0); // keep the loads issued here, ahead of the math
 
@@ -798,12 +812,14 @@ __global__ __launch_bounds__(k2_threads(BV)) void k2_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int row = 16 * tt + 4 * lg + i;
+            // (bf16: rows past the chunk end were loaded as 0; fp32 loads
+            // clamp the row and are masked here)
             float vv;
             if constexpr (VLDS)
-              vv = to_f32(sv[wv][row * VW + 16 * c + lr]);
+              vv = mpart ? 0.f : to_f32(sv[wv][row * VW + 16 * c + lr]);
             else
-              vv = to_f32(vcur[c][tt][i]);
-            W[c][tt][i] = (!mpart && row < len ? vv : 0.f) - W[c][tt][i];
+              vv = (!mpart && row < len) ? to_f32(vcur[c][tt][i]) : 0.f;
+            W[c][tt][i] = vv - W[c][tt][i];
           }
       // bf16: this wave's slice of v is consumed; chunk ch+1's goes in now
       if constexpr (VLDS) {
@@ -914,7 +930,7 @@ __global__ __launch_bounds__(k2_threads(BV)) void k2_kernel(
       if (more) {
         if (NBUF == 1) {
           __syncthreads(); // every wave is done with the record
-          RCopy::issue(cur, rec0 + (int64_t)(ch + 1) * rec_step, wv, lane);
+          RCopy::issue(cur, rec0 + (int64_t)(ch + 1) * rec_step, goff, wv);
         }
         wait_vmem();
         __syncthreads();

@@ -104,6 +104,14 @@ int32_t kda_plan_num_segments(int64_t seq_len, int32_t num_seqs, int32_t H, int3
  * transition pairs are combined by a prefix scan and then replayed (see
  * kda_plan_num_segments and kda_segment_transition); the result is the same
  * up to fp32 rounding.
+ * Two implementations compute the same result.  With KDA_BF16, no split and
+ * at least 512 (sequence, head) pairs, one fused kernel builds each chunk's
+ * operands on chip while it carries the state (the workspace then holds only
+ * the schedule); otherwise a chunk-parallel prep kernel writes the per-chunk
+ * operands to the workspace and a state-carrying kernel reads them.  The
+ * environment variable KDA_FUSED_PREFILL=1 (or 0) forces the fused (or the
+ * two-kernel) path for unsplit bf16 calls; it must not change between the
+ * workspace-size query and the call.
  *
  *   num_seqs         : N >= 0 sequences.
  *   cu_seqlens_host  : HOST, N+1 int64, cu[0] = 0, nondecreasing.  The

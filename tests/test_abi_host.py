@@ -70,11 +70,14 @@ def test_workspace_sizes(lib):
     a, p = cu(0, 256)
     ws32 = lib.kda_chunk_prefill_workspace_size(1, p, 2, 128, 128, nat.KDA_F32, 0)
     ws16 = lib.kda_chunk_prefill_workspace_size(1, p, 2, 128, 128, nat.KDA_BF16, 0)
-    # fp32: 4 chunks x 2 heads of chunk-prep records (128.5 KiB each); bf16
-    # without a split runs the fused kernel, which keeps its records on chip
-    # and needs only the schedule tables
+    # 4 chunks x 2 heads of chunk-prep records (128.5 KiB fp32, 64.5 KiB bf16)
     assert ws32 > 4 * 2 * 128 * 1024
-    assert 0 < ws16 < 4096
+    assert ws32 > ws16 > 4 * 2 * 64 * 1024
+    # bf16 with at least 512 (sequence, head) chains runs the fused kernel,
+    # which keeps its records on chip and needs only the schedule tables
+    a4, p4 = cu(*[256 * i for i in range(65)])
+    ws_many = lib.kda_chunk_prefill_workspace_size(64, p4, 8, 128, 128, nat.KDA_BF16, 0)
+    assert 0 < ws_many < 64 * 1024
     a2, p2 = cu(0, 256, 256)
     assert lib.kda_chunk_prefill_workspace_size(2, p2, 2, 128, 128, nat.KDA_F32, 0) >= ws32
     # a split adds the planner's state buffers

@@ -86,6 +86,67 @@ def test_prefill_many_chains(dtype):
     prefill_vs_oracle([70, 130, 65], 96, dtype, 34, init=True)
 
 
+@pytest.fixture(params=["fused", "two_kernel"])
+def bf16_path(request, monkeypatch):
+    """Run a bf16 test through one prefill implementation (the library reads
+    KDA_FUSED_PREFILL at every call)."""
+    monkeypatch.setenv("KDA_FUSED_PREFILL", "1" if request.param == "fused" else "0")
+    say("bf16 prefill path:", request.param)
+    return request.param
+
+
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 63, 64, 65, 200, 1000])
+def test_bf16_paths_lengths(T, bf16_path):
+    prefill_vs_oracle([T], 3 if T % 2 else 1, torch.bfloat16, 300 + T, init=(T % 3 == 0))
+
+
+def test_bf16_paths_packed_varlen(bf16_path):
+    prefill_vs_oracle([0, 1, 64, 130, 0, 77, 255], 2, torch.bfloat16, 331, init=True)
+
+
+def test_bf16_paths_mild_decay_initial_state(bf16_path):
+    prefill_vs_oracle([300, 129], 2, torch.bfloat16, 332, decay="mild", init=True)
+
+
+def test_bf16_paths_many_short_sequences(bf16_path):
+    # 64 sequences x 8 heads (the automatic choice picks the fused kernel),
+    # lengths 1..300 with partial last chunks, nonzero initial states
+    rng = np.random.default_rng(333)
+    lengths = [int(x) for x in rng.integers(1, 301, size=64)]
+    prefill_vs_oracle(lengths, 8, torch.bfloat16, 334, init=True)
+
+
+def test_bf16_paths_max_decay(bf16_path):
+    say("max decay (bf16 path test)")
+    T, H = 200, 2
+    d = wl.token_inputs(T, H, torch.bfloat16, 335, device=DEV)
+    d["g"].fill_(-5.0)
+    o, fin = kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"])
+    torch.cuda.synchronize()
+    o_ref, f_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], d["beta"])
+    assert rel_err(o, o_ref) <= TOL[torch.bfloat16]
+    assert rel_err(fin, f_ref) <= TOL[torch.bfloat16]
+
+
+def test_bf16_paths_inplace_resume(bf16_path):
+    # final_state aliasing initial_state: every (sequence, head) reads its
+    # state before writing it
+    say("in-place resume (bf16 path test)")
+    lengths, H = [100, 64, 1], 3
+    cu = wl.cu_from_lengths(lengths)
+    d = wl.token_inputs(int(cu[-1]), H, torch.bfloat16, 336, device=DEV, decay="mild")
+    S = wl.states(len(lengths), H, 337, device=DEV)
+    S_ref = S.detach().cpu().double().numpy().copy()
+    o, fin = kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu,
+                               initial_state=S, final_state=S)
+    torch.cuda.synchronize()
+    o_ref, f_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu,
+                                     initial_state=S_ref)
+    assert fin.data_ptr() == S.data_ptr()
+    assert rel_err(o, o_ref) <= TOL[torch.bfloat16]
+    assert rel_err(S, f_ref) <= TOL[torch.bfloat16]
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_prefill_mild_decay_initial_state_matters(dtype):
     # with mild decay the initial state still weighs on the last outputs
