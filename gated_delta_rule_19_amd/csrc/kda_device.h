@@ -195,6 +195,19 @@ __device__ __forceinline__ void mm16_lds_acc(f32x4 &acc, const float *A, int lda
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], B[3], acc, 0, 0, 0);
 }
 
+// acc += A B for 16 x 16 fp32 blocks with both operands in registers.  A
+// block is held either in the accumulator ("column") layout, lane (lr, lg)
+// element i = X[4 lg + i][lr], or in the row layout, element i = X[lr][4 lg + i]
+// (the column layout of X^T).  a is A in the row layout, b is B in the column
+// layout; the result is in the column layout.  Passing (B column, A row)
+// instead yields B^T A^T in the column layout, i.e. A B in the row layout.
+__device__ __forceinline__ void mm16_rr(f32x4 &acc, const f32x4 a, const f32x4 b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
+}
+
 // Store / load a 16 x 16 fp32 block in the accumulator layout.
 __device__ __forceinline__ void acc_store(float *D, int ld, const f32x4 &x, int lr, int lg) {
 #pragma unroll
@@ -207,6 +220,86 @@ __device__ __forceinline__ f32x4 acc_load(const float *D, int ld, int lr, int lg
   for (int i = 0; i < 4; ++i)
     x[i] = D[(4 * lg + i) * ld + lr];
   return x;
+}
+
+// Workgroup barrier ordering LDS only; global loads stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Lane index as an opaque value: lane-dependent addresses built on it are
+// recomputed where they are used instead of being hoisted out of the chunk
+// loop and kept alive (or spilled) across all of its stages.
+__device__ __forceinline__ int opaque_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// LDS writes of this wave are complete and visible to its own later reads.
+__device__ __forceinline__ void wave_lds_fence() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 8 bf16 (raw dwords) -> fp32
+__device__ __forceinline__ void widen8(u32x4 w, float *x) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    x[2 * d] = __builtin_bit_cast(float, w[d] << 16);
+    x[2 * d + 1] = __builtin_bit_cast(float, w[d] & 0xffff0000u);
+  }
+}
+
+// Inclusive prefix sum over the 16 lanes of each DPP row (row_shr with
+// bound_ctrl: lanes before the row start contribute 0).
+__device__ __forceinline__ float dpp_shr(float x, int n) {
+  const int v = __builtin_bit_cast(int, x);
+  int r;
+  switch (n) {
+  case 1: r = __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true); break;
+  case 2: r = __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true); break;
+  case 4: r = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true); break;
+  default: r = __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true); break;
+  }
+  return __builtin_bit_cast(float, r);
+}
+__device__ __forceinline__ float row_scan16(float x) {
+  x += dpp_shr(x, 1);
+  x += dpp_shr(x, 2);
+  x += dpp_shr(x, 4);
+  x += dpp_shr(x, 8);
+  return x;
+}
+
+__device__ __forceinline__ Frag<bf16> pack8(const float *x) {
+  Frag<bf16> f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    f.v[j] = static_cast<bf16>(x[j]);
+  return f;
+}
+
+__device__ __forceinline__ Frag<bf16> pack_acc2(const f32x4 &lo, const f32x4 &hi) {
+  Frag<bf16> f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f.v[i] = static_cast<bf16>(lo[i]);
+    f.v[4 + i] = static_cast<bf16>(hi[i]);
+  }
+  return f;
+}
+
+__device__ __forceinline__ void load8f(const float *p, float *x) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+  x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+  x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
 }
 
 } // namespace kda

@@ -105,90 +105,6 @@ template <int NCT> struct FusedSmem {
 // index of the tile pair (I, J), I > J, among the 6 off-diagonal pairs
 __device__ __forceinline__ int off_pair(int I, int J) { return I * (I - 1) / 2 + J; }
 
-// state row holding channel c (inverse of kperm)
-__device__ __forceinline__ int kperm_inv(int p) {
-  return (p & ~31) | ((p & 4) << 2) | ((p & 24) >> 1) | (p & 3);
-}
-
-// Workgroup barrier ordering LDS only; global loads stay in flight across it.
-__device__ __forceinline__ void fsync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// Lane index as an opaque value: lane-dependent addresses built on it are
-// recomputed where they are used instead of being hoisted out of the chunk
-// loop and kept alive (or spilled) across all of its stages.
-__device__ __forceinline__ int opaque_lane() {
-  int l;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
-  return l;
-}
-
-// LDS writes of this wave are complete and visible to its own later reads.
-__device__ __forceinline__ void wave_lds_fence() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-}
-
-__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// 8 bf16 (raw dwords) -> fp32
-__device__ __forceinline__ void widen8(u32x4 w, float *x) {
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    x[2 * d] = __builtin_bit_cast(float, w[d] << 16);
-    x[2 * d + 1] = __builtin_bit_cast(float, w[d] & 0xffff0000u);
-  }
-}
-
-// Inclusive prefix sum over the 16 lanes of each DPP row (row_shr with
-// bound_ctrl: lanes before the row start contribute 0).
-__device__ __forceinline__ float dpp_shr(float x, int n) {
-  const int v = __builtin_bit_cast(int, x);
-  int r;
-  switch (n) {
-  case 1: r = __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true); break;
-  case 2: r = __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true); break;
-  case 4: r = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true); break;
-  default: r = __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true); break;
-  }
-  return __builtin_bit_cast(float, r);
-}
-__device__ __forceinline__ float row_scan16(float x) {
-  x += dpp_shr(x, 1);
-  x += dpp_shr(x, 2);
-  x += dpp_shr(x, 4);
-  x += dpp_shr(x, 8);
-  return x;
-}
-
-__device__ __forceinline__ Frag<bf16> pack8(const float *x) {
-  Frag<bf16> f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    f.v[j] = static_cast<bf16>(x[j]);
-  return f;
-}
-
-__device__ __forceinline__ Frag<bf16> pack_acc2(const f32x4 &lo, const f32x4 &hi) {
-  Frag<bf16> f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f.v[i] = static_cast<bf16>(lo[i]);
-    f.v[4 + i] = static_cast<bf16>(hi[i]);
-  }
-  return f;
-}
-
-__device__ __forceinline__ void load8f(const float *p, float *x) {
-  const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
-  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
-  x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
-  x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
-}
 
 
 } // namespace
@@ -220,7 +136,7 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
     sm.INVb[16 * bi + r][kperm(16 * bj + c)] = static_cast<bf16>(0.f);
     sm.Mqk[16 * bi + r][kperm(16 * bj + c)] = static_cast<bf16>(0.f);
   }
-  fsync();
+  lds_barrier();
 
   if (wv < 4) {
     // =========================== state waves ===========================
@@ -448,31 +364,31 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
     // blocks of chunk it in stage C and starts chunk it in stage D
     if (nch == 0) {
       for (int b = 0; b < 4; ++b)
-        fsync();
+        lds_barrier();
     } else {
       v_to_lds(0);
-      fsync();
-      fsync();
+      lds_barrier();
+      lds_barrier();
       stage_inv();
-      fsync();
+      lds_barrier();
       stage_wo();
-      fsync();
+      lds_barrier();
       for (int ch = 0; ch + 1 < nch; ++ch) {
         stage_u(ch);
-        fsync();
+        lds_barrier();
         stage_s();
-        fsync();
+        lds_barrier();
         stage_inv();
-        fsync();
+        lds_barrier();
         stage_wo();
-        fsync();
+        lds_barrier();
       }
       stage_u(nch - 1);
-      fsync();
+      lds_barrier();
       stage_s();
-      fsync();
-      fsync();
-      fsync();
+      lds_barrier();
+      lds_barrier();
+      lds_barrier();
     }
     if (cd.final_idx >= 0) {
       float *fp = final_state + ((int64_t)cd.final_idx * H + h) * (kD * kD);
@@ -586,7 +502,7 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
           sm.L[row][col] = col < row ? sm.Beta[row] * accLd[i] : 0.f;
         }
       }
-      fsync();
+      lds_barrier();
       // ---- stage B: factors, Q_decay / K_decay / K_restore, off-diagonal pairs ----
       {
         const int lane = opaque_lane(), lr = lane & 15, lg = lane >> 4, r = 16 * pw + lr;
@@ -681,7 +597,7 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
         if (it + 1 < nch)
           issue(it + 1);
       }
-      fsync();
+      lds_barrier();
       // ---- stage C: L / M_qk tiles, K_restore^T, a_last -------------------------
       {
         const int lane = opaque_lane(), lr = lane & 15, lg = lane >> 4, r = 16 * pw + lr;
@@ -716,7 +632,7 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
           sm.aL[kperm_inv(2 * lane + 1)] = aLr[1];
         }
       }
-      fsync();
+      lds_barrier();
       // ---- stage D: off-diagonal blocks of INV ---------------------------------
       {
         const int lane = opaque_lane(), lr = lane & 15, lg = lane >> 4;
@@ -746,11 +662,11 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
           }
         }
       }
-      fsync();
+      lds_barrier();
     }
     // the last chunk step only consumes the last record
     for (int b = 0; b < 4; ++b)
-      fsync();
+      lds_barrier();
   }
 }
 

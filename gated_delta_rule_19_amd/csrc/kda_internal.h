@@ -56,6 +56,11 @@ __host__ __device__ constexpr int kperm(int k) {
   return (k & ~31) | (((k & 15) >> 2) << 3) | ((k & 16) >> 2) | (k & 3);
 }
 
+// Inverse of kperm: the logical column held at physical position p.
+__host__ __device__ constexpr int kperm_inv(int p) {
+  return (p & ~31) | ((p & 4) << 2) | ((p & 24) >> 1) | (p & 3);
+}
+
 // Bytes of the chunk-prep record for one (chunk, head), element size es:
 //   Q_decay [C][D], K_decay [C][D], K_restore^T [D][C], INV*Diag(beta) [C][C],
 //   M_qk [C][C] (all of the element type, columns in kperm order), a_last
@@ -81,6 +86,13 @@ constexpr int kScanBV = 8;
 hipError_t launch_k1(int elt, const ChunkDesc *chunks, int32_t nchunks, int32_t H,
                      const void *q, const void *k, const void *g, const void *beta, void *ws,
                      hipStream_t s);
+
+// Chunk prep for bf16 inputs (the records launch_k1 writes for elt == 1):
+// Q_decay / K_decay columns in channel order, state rows (K_restore^T rows,
+// a_last) in kperm order.
+hipError_t launch_prep_bf16(const ChunkDesc *chunks, int32_t nchunks, int32_t H, const void *q,
+                            const void *k, const void *g, const void *beta, void *ws,
+                            hipStream_t s);
 
 // mode 0: prefill/replay (width dv, writes o and exit states);
 // mode 1: segment pass (width dk + dv: [S~ | M], no o).

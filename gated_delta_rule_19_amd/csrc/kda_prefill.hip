@@ -58,14 +58,6 @@ __device__ __constant__ int kUpI[6] = {0, 0, 0, 1, 1, 2};
 __device__ __constant__ int kUpJ[6] = {1, 2, 3, 2, 3, 3};
 
 
-// Workgroup barrier that orders LDS only: outstanding global loads stay in
-// flight across it (a full __syncthreads() would wait for them too).
-__device__ __forceinline__ void lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // 4 consecutive input elements kept as raw dwords between load and use.
 template <typename T> struct Raw4;
 template <> struct Raw4<bf16> {
@@ -202,7 +194,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   T *Mqk = reinterpret_cast<T *>(rec + off.mqk);
   float *ac = reinterpret_cast<float *>(rec + off.ac);
 
-  lds_sync(); // the previous item's last LDS reads are done
+  lds_barrier(); // the previous item's last LDS reads are done
   // g is widened now; k and q stay raw until their row is used (registers)
   float gv[4][8];
 #pragma unroll
@@ -236,7 +228,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if (lgp == 3)
       sWT[wv][8 * cg + e] = x;
   }
-  lds_sync();
+  lds_barrier();
   // p_own = p_wv (before this tile), p_next = p_{wv+1}, p_last = G_last
   float pown[8], pnext[8], plast[8];
 #pragma unroll
@@ -353,7 +345,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int e = 0; e < 4; ++e)
       store4(KrT + lch(4 * u + e) * kC + kperm(row0), kr[e][0], kr[e][1], kr[e][2], kr[e][3]);
   }
-  lds_sync();
+  lds_barrier();
 
   // ---- phase 3: L and M_qk tiles on MFMA ---------------------------------
   const int lr = lane & 15, lg = lane >> 4;
@@ -388,7 +380,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
     }
   }
-  lds_sync(); // operand region is now free for L / INV
+  lds_barrier(); // operand region is now free for L / INV
 
   // L (beta-scaled rows, strictly lower) and M_qk (lower incl. diagonal, in
   // record layout) to LDS.
@@ -413,7 +405,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     sMq[row][kperm(col)] = from_f32<T>(0.f);
     sIb[row][kperm(col)] = from_f32<T>(0.f);
   }
-  lds_sync();
+  lds_barrier();
 
   // the next item's inputs are in flight during the rest of this one
   if (item + (int)gridDim.x < nitems)
@@ -463,7 +455,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       acc_store(&sDinv[b][0][0], LB, y, lr, lg);
       put(b, b, y);
     }
-    lds_sync(); // every D_i^-1 is in LDS
+    lds_barrier(); // every D_i^-1 is in LDS
     {
       const int j = wv;
 #pragma unroll
@@ -482,7 +474,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
     }
   }
-  lds_sync();
+  lds_barrier();
 
   // M_qk and INV Diag(beta) from their staging blocks to the record, 16
   // bytes per store
@@ -638,7 +630,11 @@ __global__ __launch_bounds__(k2_threads(BV)) void k2_kernel(
   const int64_t rowstride = (int64_t)H * kD;
   const int nch = (cd.ntok + kC - 1) / kC;
 
-  // S[c][ct]: rows 16 ct + 4 lg + i (ct = 0..7), column wcol + 16 c
+  // S[c][ct]: rows 16 ct + 4 lg + i (ct = 0..7), column wcol + 16 c.  Row p
+  // holds channel srow(p): the channel itself for fp32 records, kperm(p)
+  // for bf16 ones (whose K_decay / Q_decay columns are in channel order).
+  constexpr bool kPermRows = sizeof(T) == 2;
+  auto srow = [](int p) { return kPermRows ? kperm(p) : p; };
   f32x4 S[NCT][8];
   {
     const float *ip = nullptr;
@@ -655,7 +651,7 @@ __global__ __launch_bounds__(k2_threads(BV)) void k2_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = 16 * ct + 4 * lg + i, col = wcol + 16 * c;
-          S[c][ct][i] = ip ? ip[row * kD + col] : ((mpart && row == col) ? 1.f : 0.f);
+          S[c][ct][i] = ip ? ip[srow(row) * kD + col] : ((mpart && srow(row) == col) ? 1.f : 0.f);
         }
   }
 
@@ -969,7 +965,7 @@ __global__ __launch_bounds__(k2_threads(BV)) void k2_kernel(
       for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          fp[(16 * ct + 4 * lg + i) * kD + wcol + 16 * c] = S[c][ct][i];
+          fp[srow(16 * ct + 4 * lg + i) * kD + wcol + 16 * c] = S[c][ct][i];
   }
 }
 
@@ -1030,20 +1026,17 @@ hipError_t launch_k1(int elt, const ChunkDesc *chunks, int32_t nchunks, int32_t 
                      hipStream_t s) {
   if (nchunks == 0)
     return hipSuccess;
+  if (elt == 1)
+    return launch_prep_bf16(chunks, nchunks, H, q, k, g, beta, ws, s);
   // persistent grid: as many workgroups as are resident at once (LDS
-  // limits bf16 to 2 per compute unit, fp32 to 1), each walking its items
+  // limits fp32 to 1 per compute unit), each walking its items
   const int64_t nitems = (int64_t)nchunks * H;
-  const int64_t resident = (int64_t)kComputeUnits * (elt == 1 ? 2 : 1);
+  const int64_t resident = (int64_t)kComputeUnits;
   dim3 grid((unsigned)std::min(nitems, resident)), block(kThreads);
   // without q, k stands in as a readable buffer of the same shape
   const int has_q = q != nullptr;
   const void *qq = has_q ? q : k;
-  if (elt == 1)
-    k1_kernel<bf16><<<grid, block, 0, s>>>(chunks, H, (const bf16 *)qq, (const bf16 *)k,
-                                           (const bf16 *)g, (const bf16 *)beta,
-                                           (uint8_t *)ws, has_q, (int32_t)nitems);
-  else
-    k1_kernel<float><<<grid, block, 0, s>>>(chunks, H, (const float *)qq, (const float *)k,
+  k1_kernel<float><<<grid, block, 0, s>>>(chunks, H, (const float *)qq, (const float *)k,
                                             (const float *)g, (const float *)beta,
                                             (uint8_t *)ws, has_q, (int32_t)nitems);
   return hipGetLastError();
