@@ -63,8 +63,11 @@ __host__ __device__ constexpr int kperm_inv(int p) {
 
 // Bytes of the chunk-prep record for one (chunk, head), element size es:
 //   Q_decay [C][D], K_decay [C][D], K_restore^T [D][C], INV*Diag(beta) [C][C],
-//   M_qk [C][C] (all of the element type, columns in kperm order), a_last
-//   [D] fp32; 256-aligned.
+//   M_qk [C][C] (all of the element type, token columns in kperm order),
+//   a_last [D] fp32; 256-aligned.  fp32 records keep Q_decay / K_decay
+//   columns in kperm order and the state rows in channel order; bf16 records
+//   the reverse, and store Q_decay, K_decay and M_qk in 16-byte pieces in
+//   the order the bf16 prep writes them (kda_prep.hip).
 constexpr size_t k1_record_bytes(size_t es) {
   return ((3 * 64 * 128 + 2 * 64 * 64) * es + 128 * 4 + 255) / 256 * 256;
 }
@@ -87,9 +90,7 @@ hipError_t launch_k1(int elt, const ChunkDesc *chunks, int32_t nchunks, int32_t 
                      const void *q, const void *k, const void *g, const void *beta, void *ws,
                      hipStream_t s);
 
-// Chunk prep for bf16 inputs (the records launch_k1 writes for elt == 1):
-// Q_decay / K_decay columns in channel order, state rows (K_restore^T rows,
-// a_last) in kperm order.
+// Chunk prep for bf16 inputs (the records launch_k1 writes for elt == 1).
 hipError_t launch_prep_bf16(const ChunkDesc *chunks, int32_t nchunks, int32_t H, const void *q,
                             const void *k, const void *g, const void *beta, void *ws,
                             hipStream_t s);

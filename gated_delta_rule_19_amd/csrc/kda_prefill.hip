@@ -516,11 +516,15 @@ __device__ __forceinline__ Frag<T> pack_acc_pair(const f32x4 &lo, const f32x4 &h
   return frag_from_f32<T>(x);
 }
 
-// LDS image of a chunk record: the same sections, each row padded by 16
-// bytes so that the 16 rows one wave reads per MFMA fragment start in
-// different LDS banks (a 256- or 128-byte row stride would put them all in
-// the same banks).
+// LDS image of a chunk record.  fp32 records: the same sections, each row
+// padded by 16 bytes so that the 16 rows one wave reads per MFMA fragment
+// start in different LDS banks (a 256- or 128-byte row stride would put
+// them all in the same banks).  bf16 records are stored as 1 KiB fragment
+// blocks (block (tile, k-step) holds the 16-byte fragment of lane l at
+// 16 l) and the image is the record itself: a fragment read is 64
+// consecutive 16-byte pieces.
 template <typename T> struct RecLds {
+  static constexpr bool pieces = false;
   static constexpr int es = sizeof(T);
   static constexpr int rowD = kD * es, rowC = kC * es;     // global row bytes
   static constexpr int padD = rowD + 16, padC = rowC + 16; // LDS row bytes
@@ -530,6 +534,17 @@ template <typename T> struct RecLds {
   static constexpr int invb = krt + kD * padC;
   static constexpr int mqk = invb + kC * padC;
   static constexpr int ac = mqk + kC * padC;
+  static constexpr int bytes = ac + kD * 4;
+  static constexpr int blocks = (bytes + 1023) / 1024;
+};
+template <> struct RecLds<bf16> {
+  static constexpr bool pieces = true;
+  static constexpr int qd = 0;
+  static constexpr int kd = qd + kC * kD * 2;
+  static constexpr int krt = kd + kC * kD * 2;
+  static constexpr int invb = krt + kD * kC * 2;
+  static constexpr int mqk = invb + kC * kC * 2;
+  static constexpr int ac = mqk + kC * kC * 2;
   static constexpr int bytes = ac + kD * 4;
   static constexpr int blocks = (bytes + 1023) / 1024;
 };
@@ -559,27 +574,36 @@ template <typename T, int NW> struct RecordCopy {
   // This lane's record byte offset for each of its wave's blocks; the same
   // for every chunk, so it is computed once per workgroup.
   __device__ __forceinline__ static void offsets(int (&goff)[kPerWave], int wv, int lane) {
-    constexpr RecOff off(sizeof(T));
+    constexpr int RB = (int)k1_record_bytes(sizeof(T));
+    if constexpr (L::pieces) { // the image is the record
 #pragma unroll
-    for (int j = 0; j < kPerWave; ++j) {
-      const int b = wv + j * NW; // wave-uniform
-      const int p = b * 1024 + lane * 16;
-      int g = 0;
-      if (b >= L::blocks)
-        g = 0;
-      else if (b * 1024 < L::kd)
-        g = section_src<L::padD, L::rowD>(p - L::qd, (int)off.qd);
-      else if (b * 1024 < L::krt)
-        g = section_src<L::padD, L::rowD>(p - L::kd, (int)off.kd);
-      else if (b * 1024 < L::invb)
-        g = section_src<L::padC, L::rowC>(p - L::krt, (int)off.krt);
-      else if (b * 1024 < L::mqk)
-        g = section_src<L::padC, L::rowC>(p - L::invb, (int)off.invb);
-      else if (b * 1024 < L::ac)
-        g = section_src<L::padC, L::rowC>(p - L::mqk, (int)off.mqk);
-      else
-        g = p - L::ac < kD * 4 ? (int)off.ac + (p - L::ac) : 0;
-      goff[j] = g;
+      for (int j = 0; j < kPerWave; ++j) {
+        const int p = (wv + j * NW) * 1024 + lane * 16;
+        goff[j] = p < RB ? p : 0;
+      }
+    } else {
+      constexpr RecOff off(sizeof(T));
+#pragma unroll
+      for (int j = 0; j < kPerWave; ++j) {
+        const int b = wv + j * NW; // wave-uniform
+        const int p = b * 1024 + lane * 16;
+        int g = 0;
+        if (b >= L::blocks)
+          g = 0;
+        else if (b * 1024 < L::kd)
+          g = section_src<L::padD, L::rowD>(p - L::qd, (int)off.qd);
+        else if (b * 1024 < L::krt)
+          g = section_src<L::padD, L::rowD>(p - L::kd, (int)off.kd);
+        else if (b * 1024 < L::invb)
+          g = section_src<L::padC, L::rowC>(p - L::krt, (int)off.krt);
+        else if (b * 1024 < L::mqk)
+          g = section_src<L::padC, L::rowC>(p - L::invb, (int)off.invb);
+        else if (b * 1024 < L::ac)
+          g = section_src<L::padC, L::rowC>(p - L::mqk, (int)off.mqk);
+        else
+          g = p - L::ac < kD * 4 ? (int)off.ac + (p - L::ac) : 0;
+        goff[j] = g;
+      }
     }
   }
   __device__ __forceinline__ static void issue(uint8_t *lds, const uint8_t *src,
@@ -608,8 +632,10 @@ __global__ __launch_bounds__(k2_threads(BV)) void k2_kernel(
   constexpr int RB = (int)k1_record_bytes(sizeof(T));
   constexpr int RBP = L::blocks * 1024; // LDS image, whole 1 KiB blocks
   constexpr int NBUF = 2 * RBP <= 160 * 1024 ? 2 : 1;
-  constexpr int LD = L::padD / (int)sizeof(T); // padded row length, 128-wide rows
-  constexpr int LC = L::padC / (int)sizeof(T); // padded row length, 64-wide rows
+  // fragment addressing: padded images take the row length (elements) of
+  // 128- and 64-wide rows, fragment-block images the k-steps per row
+  constexpr int LD = L::pieces ? kD / 32 : RecLds<float>::padD / 4;
+  constexpr int LC = L::pieces ? kC / 32 : RecLds<float>::padC / 4;
   __shared__ __attribute__((aligned(1024))) uint8_t srecA[RBP];
   __shared__ __attribute__((aligned(1024))) uint8_t srecB[NBUF == 2 ? RBP : 1];
   // bf16: each wave's own 64 x VW slice of the chunk's v also goes through
@@ -741,7 +767,10 @@ __global__ __launch_bounds__(k2_threads(BV)) void k2_kernel(
       // the next step (or phase) are read from LDS before the current step's
       // MFMAs are issued.
       auto frag = [&](const T *base, int ld, int tile, int s) {
-        return load_frag(base + (16 * tile + lr) * ld + 32 * s + 8 * lg);
+        if constexpr (L::pieces)
+          return load_frag(base + ((tile * ld + s) * 64 + lane) * 8);
+        else
+          return load_frag(base + (16 * tile + lr) * ld + 32 * s + 8 * lg);
       };
 
       // W = K_decay S, O = Q_decay S (K = channels, B operand = S)

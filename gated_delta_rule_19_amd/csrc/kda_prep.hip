@@ -12,33 +12,42 @@
 //   Q_decay = q e^{G},  K_decay = k e^{G},  K_restore = k e^{G_C - G},  a_last = e^{G_C}
 //   INV Diag(beta) with INV = (I + L)^-1.
 //
-// Record, row-major, bf16 unless stated:
+// Record, bf16 unless stated:
 //   Q_decay [C][D], K_decay [C][D]        columns = channels
 //   K_restore^T [D][C]                    row p = channel kperm(p), column kperm(token)
 //   INV Diag(beta) [C][C], M_qk [C][C]    column kperm(token)
 //   a_last [D] fp32                       entry p = channel kperm(p)
 // The state kernel keeps channel kperm(p) in row p of its state, so each of
-// these is an MFMA operand for it as stored.
+// these is an MFMA operand for it as stored.  The matrices are stored as
+// their MFMA A fragments: 16-byte piece g of row r (8 consecutive row
+// elements; G pieces per row, 16 or 8) sits at index
+//   ((r / 16) * (G / 4) + g / 4) * 64 + (g % 4) * 16 + r % 16,
+// so each 1 KiB block is the fragment of one 16-row tile and 32-column
+// k-step, lane l's 16 bytes at 16 l.  The prep writes, the state kernel's
+// copy into LDS and its fragment reads then all move 1 KiB of consecutive
+// bytes per instruction.
 //
 // One workgroup of 4 waves per (chunk, head) item, persistent: workgroup b
-// takes items b, b + grid, ..., three workgroups per compute unit.  Wave w
+// takes items b, b + grid, ..., two workgroups per compute unit.  Wave w
 // owns token tile w: lane (lr, lg) = (lane % 16, lane / 16) holds token
 // 16 w + lr and, for k-step s = 0..3, channels 32 s + 8 lg .. + 7 -- one
 // 16-byte load or store per k-step, and the MFMA fragment layout.  Three
 // stages per item, a barrier after the first two:
 //   A  tile scan of g; Q_loc, K_loc, K_st; diagonal L and M_qk tiles; then
 //      the loads of the item after next are issued
-//   B  decay factors; Q_decay, K_decay, K_restore^T, M_qk to the record;
+//   B  the previous item's INV Diag(beta) from LDS to its record; decay
+//      factors; Q_decay, K_decay, M_qk to the record; K_restore^T to LDS;
 //      off-diagonal L tiles to LDS; diagonal blocks of INV
-//   C  off-diagonal blocks of INV; INV Diag(beta) to the record
+//   C  K_restore^T to the record; off-diagonal blocks of INV, INV Diag(beta)
+//      to LDS
 // Stage A of the next item runs right after stage C, with no barrier between:
 // A writes no region that C reads (beta is double-buffered by item parity).
 //
-// Transposed products keep every store 8 or 16 bytes wide: an MFMA with its
-// two operands swapped returns the transposed tile, in which a lane holds 4
-// consecutive columns of one row instead of 4 rows of one column; and
-// K_restore^T is K_restore times a 0/1 selection matrix on the MFMA (exact:
-// one nonzero term per output).
+// Transposed products keep the fragments of every result row-contiguous: an
+// MFMA with its two operands swapped returns the transposed tile, in which a
+// lane holds 4 consecutive columns of one row instead of 4 rows of one
+// column; and K_restore^T is K_restore times a 0/1 selection matrix on the
+// MFMA (exact: one nonzero term per output).
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -49,6 +58,7 @@ namespace {
 constexpr int kPrepThreads = 256;
 constexpr int kLdOp = kD + 8; // bf16 rows of 128 channels (272 B: a fragment's 16 rows start in distinct banks)
 constexpr int kLdBk = 20;     // fp32 16 x 16 blocks (80-byte rows)
+constexpr int kLdRt = kC + 8; // bf16 rows of 64 (144 B)
 constexpr float kL2e = 1.4426950408889634f;
 
 // record sections, in elements of their type
@@ -79,7 +89,15 @@ struct PrepSmem {
   float Foff[6][kD];        // e^{p_I - p_J} of the off-diagonal pairs (wave-local)
   float Loff[6][16][kLdBk]; // off-diagonal blocks of L (stage B -> C)
   float Dinv[4][16][kLdBk]; // inverted diagonal blocks of I + L (stage B -> C)
+  bf16 KrT[kD][kLdRt];      // K_restore^T staged in record layout (stage B -> C)
+  bf16 Inv[kC][kLdRt];      // INV Diag(beta) staged (stage C -> next item's B)
 };
+
+// index of 16-byte piece g of row r in a piece-ordered section with G pieces
+// per row
+__host__ __device__ constexpr int piece_index(int r, int g, int G) {
+  return ((r >> 4) * (G >> 2) + (g >> 2)) * 64 + (g & 3) * 16 + (r & 15);
+}
 
 // Record stores go through one buffer resource per item (base address in
 // scalar registers), each lane adding a 32-bit offset: a 64-bit address per
@@ -98,18 +116,10 @@ __device__ __forceinline__ void rec_store8(__amdgpu_buffer_rsrc_t r, int e, cons
   }
   rec_store8(r, e, v);
 }
-__device__ __forceinline__ void rec_store4(__amdgpu_buffer_rsrc_t r, int e, const f32x4 &x) {
-  bf16x4 v;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    v[i] = static_cast<bf16>(x[i]);
-  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, 2 * e, 0, 0);
-}
 
 } // namespace
 
-__global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(3))) void prep_kernel(
+__global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2))) void prep_kernel(
     const ChunkDesc *__restrict__ chunks, int32_t H, const bf16 *__restrict__ q,
     const bf16 *__restrict__ k, const bf16 *__restrict__ g, const bf16 *__restrict__ beta,
     uint8_t *__restrict__ ws, int has_q, int32_t nitems) {
@@ -123,6 +133,15 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(3)
   // rows past the chunk end read 0 (no decay, no key, no query, beta 0).
   // beta stays raw until used: widening it at the load would make the wave
   // wait for every load in flight.
+  // the blocks of INV Diag(beta) above the diagonal are zero and the
+  // staging copy keeps them
+  for (int e = threadIdx.x; e < 6 * 256; e += kPrepThreads) {
+    const int t = e >> 8, rr = (e >> 4) & 15, c = e & 15;
+    const int bi = t < 3 ? 0 : (t < 5 ? 1 : 2);
+    const int bj = t < 3 ? t + 1 : (t < 5 ? t - 1 : 3);
+    sm.Inv[16 * bi + rr][kperm(16 * bj + c)] = static_cast<bf16>(0.f);
+  }
+
   u32x4 rg[4], rq[4], rk[4];
   unsigned short rbeta = 0;
   auto issue = [&](int item) {
@@ -230,10 +249,28 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(3)
     issue(item);
     stage_a(sm.Beta[0], item + gridDim.x);
   }
+  // INV Diag(beta) of the previous item leaves its staging copy at the start
+  // of the next item's stage B; before the first item the resource is empty,
+  // so those stores are dropped (and every iteration stores the same number
+  // of times)
+  __amdgpu_buffer_rsrc_t prev = buffer_rsrc(ws, 0u);
+  // piece u of a section with 8 pieces per row: row, first column
+  auto piece_row = [](int u) { return 16 * (u >> 7) + (u & 15); };
+  auto piece_col = [](int u) { return 8 * (4 * ((u >> 6) & 1) + ((u >> 4) & 3)); };
+  auto inv_out = [&](__amdgpu_buffer_rsrc_t dst) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int u = (int)threadIdx.x + kPrepThreads * n;
+      rec_store8(dst, kRecInvb + 8 * u,
+                 *reinterpret_cast<const bf16x8 *>(&sm.Inv[piece_row(u)][piece_col(u)]));
+    }
+  };
   for (; item < nitems; item += gridDim.x, par ^= 1) {
     const __amdgpu_buffer_rsrc_t rr = buffer_rsrc(ws + (int64_t)item * RB, (uint32_t)RB);
     float *Bt = sm.Beta[par];
     lds_barrier();
+    inv_out(prev);
+    prev = rr;
 
     // ---- stage B ------------------------------------------------------------
     f32x4 y;  // this tile's diagonal block of INV, column layout
@@ -281,14 +318,14 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(3)
         }
       }
       wave_lds_fence();
-      // Q_decay, K_decay and K_restore^T to the record:
+      // Q_decay and K_decay to the record, K_restore^T to its staging copy:
       //   Q_decay = Q_loc e^{p_I},  K_decay = K_loc e^{p_I},
       //   K_restore = (K_st e^{tot_I}) e^{G_C - p_{I+1}}
       // (K_st e^{tot_I} = k e^{p_{I+1} - G} <= |k|: every factor and partial
       // product is at most 1 in size, so a result underflows only where the
       // exact value is negligible).  K_restore^T comes from the selection
       // products: lane (n, lg) gets channel 32 s + 16 h + n of tokens
-      // 16 pw + 4 lg .. + 3, which are 4 consecutive record positions.
+      // 16 pw + 4 lg .. + 3, which are 4 consecutive positions of its row.
       {
         // selection matrices: B operand h picks channels 16 h .. 16 h + 15
         // of a 32-channel k-step (lane (n, lg), element j: 1 where
@@ -304,7 +341,7 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(3)
             w[d] = (kk >> 1) == d ? one : 0u;
           sel[h].v = __builtin_bit_cast(bf16x8, w);
         }
-        const int krt = kRecKrT + 32 * (pw >> 1) + 8 * lg + 4 * (pw & 1);
+        const int kcol = 32 * (pw >> 1) + 8 * lg + 4 * (pw & 1);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           float f0[8], fe[8], fc[8], xq[8], xk[8], xs[8], yq[8], yk[8], yr[8];
@@ -320,14 +357,19 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(3)
             yk[j] = xk[j] * f0[j];
             yr[j] = (xs[j] * fe[j]) * fc[j];
           }
-          rec_store8(rr, r * kD + 32 * s + 8 * lg, pack8(yq).v);
-          rec_store8(rr, kRecKd + r * kD + 32 * s + 8 * lg, pack8(yk).v);
+          const int pc = 8 * piece_index(r, 4 * s + lg, 16); // = 8 ((pw * 4 + s) * 64 + lane)
+          rec_store8(rr, pc, pack8(yq).v);
+          rec_store8(rr, kRecKd + pc, pack8(yk).v);
           const Frag<bf16> kr = pack8(yr);
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             f32x4 t = zero;
             mma(t, kr, sel[h]);
-            rec_store4(rr, krt + kperm_inv(32 * s + 16 * h + lr) * kC, t);
+            bf16x4 v4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              v4[i] = static_cast<bf16>(t[i]);
+            *reinterpret_cast<bf16x4 *>(&sm.KrT[kperm_inv(32 * s + 16 * h + lr)][kcol]) = v4;
           }
           // one k-step at a time: hoisting every step's LDS reads would
           // hold too many registers while the next item's loads are in flight
@@ -379,9 +421,8 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(3)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           md[i] = (4 * lg + i <= lr) ? accMr[i] : 0.f;
-        const int mo = kRecMqk + lr * kC + 8 * lg;
         auto put = [&](int I, int m, const f32x4 &lo, const f32x4 &hi) {
-          rec_store8(rr, mo + 16 * I * kC + 32 * m, lo, hi);
+          rec_store8(rr, kRecMqk + 8 * piece_index(16 * I + lr, 4 * m + lg, 8), lo, hi);
         };
         // two stores per wave on every path; the all-zero pieces take their
         // zeros from an opaque value, so that no zero vector is hoisted out
@@ -395,13 +436,13 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(3)
           put(0, 0, md, zero);
         } else if (pw == 1) {
           put(1, 0, accM[0], md);
-          rec_store8(rr, mo + 16 * kC + 32, zz);
+          rec_store8(rr, kRecMqk + 8 * piece_index(16 + lr, 4 + lg, 8), zz);
         } else if (pw == 2) {
           put(2, 0, accM[0], accM[1]);
           put(2, 1, md, zero);
         } else {
           put(3, 1, accM[0], md);
-          rec_store8(rr, mo + 32, zz);
+          rec_store8(rr, kRecMqk + 8 * piece_index(lr, 4 + lg, 8), zz);
         }
       }
 
@@ -436,24 +477,40 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(3)
     }
     lds_barrier();
 
-    // ---- stage C: INV Diag(beta) to the record ------------------------------
+    // ---- stage C: K_restore^T to the record; INV Diag(beta) to its staging
+    // copy ---------------------------------------------------------------------
     {
       const int lane = opaque_lane(), lr = lane & 15, lg = lane >> 4;
-      // column block j = pw, one 8-byte store per row block: zero above the
-      // diagonal, dv on it, and below it the block forward substitution
-      // X_ij = -D_i^-1 sum_{m=j}^{i-1} L_im X_mj, each X_ij also formed in
-      // the row layout for its store
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int u = 64 * pw + lane + kPrepThreads * n;
+        rec_store8(rr, kRecKrT + 8 * u,
+                   *reinterpret_cast<const bf16x8 *>(&sm.KrT[piece_row(u)][piece_col(u)]));
+      }
+      // column block j = pw: dv on the diagonal, and below it the block
+      // forward substitution X_ij = -D_i^-1 sum_{m=j}^{i-1} L_im X_mj, each
+      // X_ij also formed in the row layout for its 8-byte piece of the
+      // staging copy
       const int j = pw;
       f32x4 X[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         X[t] = (t == j) ? y : zero;
       const f32x4 bcj = *reinterpret_cast<const f32x4 *>(&Bt[16 * j + 4 * lg]);
-      const int vo = kRecInvb + lr * kC + 32 * (j >> 1) + 8 * lg + 4 * (j & 1);
+      const int vcol = 32 * (j >> 1) + 8 * lg + 4 * (j & 1);
+      auto put = [&](int i, const f32x4 &x) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v4[e] = static_cast<bf16>(x[e]);
+        *reinterpret_cast<bf16x4 *>(&sm.Inv[16 * i + lr][vcol]) = v4;
+      };
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        f32x4 o = (i == j) ? dv : zero;
+        if (i == j)
+          put(i, dv);
         if (i > j) {
+          f32x4 o = zero;
           f32x4 tsum = zero;
 #pragma unroll
           for (int m = 0; m < 3; ++m)
@@ -466,14 +523,16 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(3)
             X[i] = x;
           }
           mm16_rr(o, tsum, nd); // row layout
-          o *= bcj;
+          put(i, o * bcj);
         }
-        rec_store4(rr, vo + 16 * i * kC, o);
       }
     }
     if (item + (int)gridDim.x < nitems)
       stage_a(sm.Beta[par ^ 1], item + 2 * (int)gridDim.x);
   }
+  // the last item's INV Diag(beta)
+  lds_barrier();
+  inv_out(prev);
 }
 
 hipError_t launch_prep_bf16(const ChunkDesc *chunks, int32_t nchunks, int32_t H, const void *q,
@@ -481,9 +540,9 @@ hipError_t launch_prep_bf16(const ChunkDesc *chunks, int32_t nchunks, int32_t H,
                             hipStream_t s) {
   if (nchunks == 0)
     return hipSuccess;
-  // persistent grid: three workgroups per compute unit are resident
+  // persistent grid: two workgroups per compute unit are resident (LDS)
   const int64_t nitems = (int64_t)nchunks * H;
-  const int64_t resident = (int64_t)kComputeUnits * 3;
+  const int64_t resident = (int64_t)kComputeUnits * 2;
   dim3 grid((unsigned)std::min(nitems, resident)), block(kPrepThreads);
   // without q, k stands in as a readable buffer of the same shape
   const int has_q = q != nullptr;
