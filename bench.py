@@ -134,7 +134,7 @@ def traffic_from_counters(fetch_csv, write_csv, workload, command):
         scale = known / (copy_kib * 1024.0)
         last = {}
         for n, v in disp:
-            for tag in ("k1_kernel", "k2_kernel", "scan_kernel", "decode_kernel"):
+            for tag in ("prep_kernel", "k1_kernel", "k2_kernel", "scan_kernel", "decode_kernel"):
                 if tag in n:
                     last.setdefault(tag, []).append(v)
         out["counters"][counter] = {
@@ -142,7 +142,7 @@ def traffic_from_counters(fetch_csv, write_csv, workload, command):
             "kib_per_dispatch": {t: v[-1] for t, v in last.items()},
             "bytes_per_dispatch": {t: v[-1] * 1024.0 * scale for t, v in last.items()}}
     f, w = out["counters"]["FETCH_SIZE"], out["counters"]["WRITE_SIZE"]
-    prefill_tags = [t for t in ("k1_kernel", "k2_kernel", "scan_kernel")
+    prefill_tags = [t for t in ("prep_kernel", "k1_kernel", "k2_kernel", "scan_kernel")
                     if t in f["bytes_per_dispatch"]]
     out["hbm_bytes_per_launch"] = sum(f["bytes_per_dispatch"][t] + w["bytes_per_dispatch"].get(t, 0.0)
                                       for t in prefill_tags)

@@ -7,7 +7,8 @@ from the product path.
 
 Two independent formulations live here:
 
-* :func:`recurrence` / :func:`decode_step` / :func:`segment_transition` call
+* :func:`recurrence` / :func:`decode_step` / :func:`decode_replay` /
+  :func:`segment_transition` call
   the C file ``kda_oracle.c`` -- the per-token recurrence of
   "Kimi K3.1 Pro 架构完全拆解" §3.1, evaluated in the u-form of
   "Kimi K3 的架構" (hao.cnyes.com) §六, in fp64, threaded over
@@ -157,6 +158,66 @@ def decode_step(state, q, k, v, g, beta, threads: int = 0):
     N = k.shape[0]
     cu = np.arange(N + 1, dtype=np.int64)
     return recurrence(q, k, v, g, beta, cu_seqlens=cu, initial_state=state, threads=threads)
+
+
+def decode_replay(state, accepted, ck, cv, cg, cbeta, q, k, v, g, beta, threads: int = 0):
+    """Speculative-decode state replay ("Kimi K3.1 Pro 架构完全拆解" §3.4;
+    "部署 Kimi K3：从 KDA Kernel 到 Fleet 调度" §四): the state is rebuilt from
+    the cached projected inputs of the accepted draft tokens, not restored
+    from a snapshot.
+
+    Per sequence n, starting from ``state[n]`` (the state before the draft
+    window), the recurrence runs over the first m_n = clip(accepted[n], 0, W)
+    cached tokens (ck, cv, cg, cbeta: ``[N, W, H, d]`` / ``[N, W, H]``; their
+    outputs are not needed), then over the P new tokens (q, k, v, g, beta:
+    ``[N, P, H, d]`` / ``[N, P, H]``; the bonus token first, then the next
+    window's drafts).  Returns ``(o [N, P, H, dv], committed [N, H, dk, dv])``:
+    the outputs of the new tokens, and the state after the accepted tokens
+    and the bonus token (after the accepted tokens alone when P = 0).
+    """
+    S0 = _f64(state)
+    N, H, dk, dv = S0.shape
+    acc = np.asarray(accepted).reshape(-1)
+    if acc.size != N:
+        raise ValueError("accepted must hold one count per sequence")
+    ck = _f64(ck); cv = _f64(cv); cg = _f64(cg); cbeta = _f64(cbeta)
+    q = _f64(q); k = _f64(k); v = _f64(v); g = _f64(g); beta = _f64(beta)
+    W = ck.shape[1]
+    P = k.shape[1]
+    if (ck.shape != (N, W, H, dk) or cg.shape != ck.shape or cv.shape != (N, W, H, dv)
+            or cbeta.shape != (N, W, H)):
+        raise ValueError("cached window shapes")
+    if (k.shape != (N, P, H, dk) or q.shape != k.shape or g.shape != k.shape
+            or v.shape != (N, P, H, dv) or beta.shape != (N, P, H)):
+        raise ValueError("new window shapes")
+    m = np.clip(acc.astype(np.int64), 0, W)
+
+    def packed(n_new):
+        # per sequence: its accepted cached tokens, then its first n_new new tokens
+        parts = {"q": [], "k": [], "v": [], "g": [], "b": []}
+        lengths = []
+        for n in range(N):
+            mn = int(m[n])
+            parts["q"] += [np.zeros((mn, H, dk)), q[n, :n_new]]
+            parts["k"] += [ck[n, :mn], k[n, :n_new]]
+            parts["v"] += [cv[n, :mn], v[n, :n_new]]
+            parts["g"] += [cg[n, :mn], g[n, :n_new]]
+            parts["b"] += [cbeta[n, :mn], beta[n, :n_new]]
+            lengths.append(mn + n_new)
+        cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+        cat = {key: np.concatenate(val, axis=0) for key, val in parts.items()}
+        return cu, cat
+
+    cu, x = packed(P)
+    o_all, _ = recurrence(x["q"], x["k"], x["v"], x["g"], x["b"], cu_seqlens=cu,
+                          initial_state=S0, want_final=False, threads=threads)
+    o = np.zeros((N, P, H, dv), dtype=np.float64)
+    for n in range(N):
+        o[n] = o_all[cu[n] + int(m[n]):cu[n + 1]]
+    cu1, x1 = packed(min(P, 1))
+    _, committed = recurrence(x1["q"], x1["k"], x1["v"], x1["g"], x1["b"], cu_seqlens=cu1,
+                              initial_state=S0, want_o=False, threads=threads)
+    return o, committed
 
 
 def segment_transition(k, v, g, beta, cu_seglens=None, threads: int = 0):

@@ -218,3 +218,83 @@ def test_decay_lower_bound_range():
     assert 16 * wl.G_MIN == -80.0
     assert np.isfinite(np.float32(np.exp(80.0)))
     assert np.exp(80.0) < 3.38e38
+
+
+def _literal_step(S, q, k, v, g, b):
+    # one token of the recurrence in its product form ("Kimi K3.1 Pro 架构完全拆解"
+    # §3.1): S' = (I - b k k^T) Diag(exp g) S + b k v^T, o = S'^T q
+    kt = k[:, None]
+    S = (np.eye(k.size) - b * (kt @ kt.T)) @ np.diag(np.exp(g)) @ S + b * kt @ v[None, :]
+    return S, S.T @ q
+
+
+def _replay_case(N, W, P, H, dk, dv, seed):
+    cq, ck, cv, cg, cb = rand_inputs(N * W, H, dk, dv, seed, decay="mild")
+    q, k, v, g, b = rand_inputs(N * P, H, dk, dv, seed + 1, decay="mild")
+    cached = [x.reshape((N, W) + x.shape[1:]) for x in (ck, cv, cg, cb)]
+    new = [x.reshape((N, P) + x.shape[1:]) for x in (q, k, v, g, b)]
+    S0 = np.random.default_rng(seed + 2).standard_normal((N, H, dk, dv))
+    return S0, cached, new
+
+
+def test_replay_matches_snapshot_baseline():
+    # The rollback the pages compare against ("Kimi K3.1 Pro 架构完全拆解" §3.4;
+    # "部署 Kimi K3：从 KDA Kernel 到 Fleet 调度" §四): step the whole draft
+    # window keeping a state snapshot per position, restart from the snapshot
+    # after the accepted prefix, then run the new tokens; the state after the
+    # bonus token (the first new one) is the one committed.  Counts outside
+    # [0, W] are clamped.
+    N, W, P, H, dk, dv = 5, 4, 3, 2, 8, 6
+    S0, (ck, cv, cg, cb), (q, k, v, g, b) = _replay_case(N, W, P, H, dk, dv, 30)
+    accepted = np.array([0, 2, 4, 7, -1], dtype=np.int32)
+    o, committed = oracle.decode_replay(S0, accepted, ck, cv, cg, cb, q, k, v, g, b)
+    for n in range(N):
+        for h in range(H):
+            S = S0[n, h].copy()
+            snaps = [S]
+            for t in range(W):
+                S, _ = _literal_step(S, np.zeros(dk), ck[n, t, h], cv[n, t, h], cg[n, t, h],
+                                     cb[n, t, h])
+                snaps.append(S)
+            S = snaps[int(np.clip(accepted[n], 0, W))]
+            for j in range(P):
+                S, oj = _literal_step(S, q[n, j, h], k[n, j, h], v[n, j, h], g[n, j, h],
+                                      b[n, j, h])
+                np.testing.assert_allclose(o[n, j, h], oj, rtol=0, atol=1e-12)
+                if j == 0:
+                    np.testing.assert_allclose(committed[n, h], S, rtol=0, atol=1e-12)
+
+
+def test_replay_commit_depends_on_accepted_prefix_and_bonus_only():
+    N, W, P, H, dk, dv = 3, 3, 4, 2, 8, 8
+    S0, cached, new = _replay_case(N, W, P, H, dk, dv, 40)
+    accepted = np.array([1, 3, 0])
+    o, c = oracle.decode_replay(S0, accepted, *cached, *new)
+    # other drafts after the bonus: new outputs from the second token on, the
+    # same committed state
+    q, k, v, g, b = [x.copy() for x in new]
+    rng = np.random.default_rng(41)
+    k[:, 1:] = rng.standard_normal(k[:, 1:].shape) / np.sqrt(dk)
+    v[:, 1:] += 1.0
+    o2, c2 = oracle.decode_replay(S0, accepted, *cached, q, k, v, g, b)
+    assert np.array_equal(c2, c) and np.array_equal(o2[:, 0], o[:, 0])
+    assert rel(o2[:, 1:], o[:, 1:]) > 1e-3
+    # rejected cached tokens do not matter either
+    ck = cached[0].copy()
+    ck[0, 1:] += 1.0
+    ck[2, :] -= 1.0
+    o3, c3 = oracle.decode_replay(S0, accepted, ck, *cached[1:], *new)
+    assert np.array_equal(c3, c) and np.array_equal(o3, o)
+    # P = 0 commits the accepted prefix alone; m = 0, P = 1 is one decode step
+    z = [x[:, :0] for x in new]
+    _, c0 = oracle.decode_replay(S0, accepted, *cached, *z)
+    for n in range(N):
+        mn = int(accepted[n])
+        _, fn = oracle.recurrence(np.zeros((mn, H, dk)), cached[0][n, :mn], cached[1][n, :mn],
+                                  cached[2][n, :mn], cached[3][n, :mn],
+                                  initial_state=S0[n:n + 1])
+        assert rel(c0[n], fn[0]) < 1e-13
+    one = [x[:, :1] for x in new]
+    o1, c1 = oracle.decode_replay(S0, np.zeros(N, dtype=np.int32), *cached, *one)
+    od, sd = oracle.decode_step(S0, *[x[:, 0] for x in new])
+    assert np.array_equal(o1[:, 0], od) and np.array_equal(c1, sd)
