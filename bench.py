@@ -234,6 +234,58 @@ def time_decode(kda, wl, dev, steps_block=64, warmup_blocks=1):
             "model_bytes_per_step": DECODE_BYTES_PER_HEAD_TOKEN * N * H}
 
 
+def time_replay(kda, wl, dev, W=4, P=5, calls=16):
+    """Speculative-decode replay at the decode workload's shape (256 sequences
+    x 96 heads, fp32): W cached draft tokens, seeded accepted counts in
+    [0, W], P new tokens (the bonus token and P - 1 drafts).  Next to it, the
+    snapshot rollback it replaces: P single decode steps, each followed by a
+    copy of the state (one snapshot per position)."""
+    import numpy as np
+    import torch
+    w = wl.WORKLOADS["decode_f32_N256_H96_x64"]
+    N, H = w.lengths[0], w.H
+    c = wl.token_inputs(N * W, H, w.dtype, w.seed + 31, device=dev)
+    n = wl.token_inputs(N * P, H, w.dtype, w.seed + 32, device=dev)
+    cached = [c[x].reshape((N, W) + c[x].shape[1:]).contiguous() for x in ("k", "v", "g", "beta")]
+    new = [n[x].reshape((N, P) + n[x].shape[1:]).contiguous()
+           for x in ("q", "k", "v", "g", "beta")]
+    acc_np = np.random.default_rng(w.seed + 33).integers(0, W + 1, size=N).astype(np.int32)
+    acc = torch.from_numpy(acc_np).to(dev)
+    state = wl.states(N, H, w.seed + 34, device=dev)
+    o = torch.empty((N, P, H, D), dtype=w.dtype, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(calls):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) * 1e3 / calls
+
+    us = timed(lambda: kda.decode_replay(state, acc, *cached, *new, o=o))
+    toks = [[x[:, j].contiguous() for x in new] for j in range(P)]
+    snaps = [torch.empty_like(state) for _ in range(P)]
+    od = torch.empty((N, H, D), dtype=w.dtype, device=dev)
+
+    def snapshot_window():
+        for j in range(P):
+            kda.decode_step(state, *toks[j], o=od)
+            snaps[j].copy_(state)
+
+    us_snap = timed(snapshot_window)
+    gbs = DECODE_BYTES_PER_HEAD_TOKEN * N * H / (us * 1e-6) / 1e9
+    del c, n, cached, new, state, o, toks, snaps
+    torch.cuda.empty_cache()
+    return {"shape": "N=%d H=%d fp32, W=%d cached, P=%d new" % (N, H, W, P),
+            "accepted_mean": float(acc_np.mean()), "us_per_call": us,
+            "state_GB_per_s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
+            "snapshot_baseline_us": us_snap, "speedup_vs_snapshot": us_snap / us}
+
+
 def copy_reference(dev, reps=5):
     """Achievable HBM bandwidth: a plain elementwise copy of 1 GiB (read 1 GiB,
     write 1 GiB), best of `reps`, as the reference next to the nominal peak."""
@@ -354,6 +406,14 @@ def main():
         print("decode: %.1f us/step, %.0f GB/s state (%.1f%% of HBM peak)"
               % (dec["us_per_step"], dec["state_GB_per_s"], 100 * dec["hbm_frac"]),
               file=sys.stderr, flush=True)
+    rep = None
+    if not args.no_decode:
+        rep = time_replay(kda, wl, dev)
+        print("decode replay (%s, mean accepted %.2f): %.1f us/call, %.0f GB/s state (%.1f%% "
+              "of HBM peak); snapshot rollback %.1f us (x%.2f)"
+              % (rep["shape"], rep["accepted_mean"], rep["us_per_call"], rep["state_GB_per_s"],
+                 100 * rep["hbm_frac"], rep["snapshot_baseline_us"],
+                 rep["speedup_vs_snapshot"]), file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.workload)
@@ -389,6 +449,7 @@ def main():
         "cpu_baseline": cpu,
         "prefill": main_res,
         "decode": dec,
+        "decode_replay": rep,
         "extra": extra or None,
     }
     print(json.dumps(line), flush=True)

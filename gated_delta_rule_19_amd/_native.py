@@ -35,6 +35,7 @@ EXPORTED = (
     "kda_chunk_prefill_workspace_size",
     "kda_chunk_prefill",
     "kda_decode_step",
+    "kda_decode_replay",
     "kda_segment_transition_workspace_size",
     "kda_segment_transition",
 )
@@ -74,6 +75,9 @@ def load():
                                           vp, vp, i32, vp, sz, vp]
         lib.kda_decode_step.restype = i32
         lib.kda_decode_step.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.kda_decode_replay.restype = i32
+        lib.kda_decode_replay.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32,
+                                          vp, vp, vp, vp, vp, vp, vp, vp]
         lib.kda_segment_transition_workspace_size.restype = sz
         lib.kda_segment_transition_workspace_size.argtypes = [i32, lp, i32, i32, i32, i32]
         lib.kda_segment_transition.restype = i32
@@ -226,6 +230,41 @@ def decode_step(state, q, k, v, g, beta, o=None):
                              _ptr(g), _ptr(beta), _ptr(state), _ptr(o), _stream_ptr(dev))
     if st != KDA_OK:
         raise KdaError(st, "kda_decode_step")
+    return o
+
+
+def decode_replay(state, accepted, ck, cv, cg, cbeta, q, k, v, g, beta, o=None):
+    """Speculative-decode replay (``kda_decode_replay``), state updated in place.
+
+    ``accepted``: int32 ``[N]`` on the device; cached window ``ck, cg``
+    ``[N, W, H, 128]``, ``cv`` ``[N, W, H, 128]``, ``cbeta`` ``[N, W, H]``; new
+    window (bonus token first) ``q, k, g, v`` ``[N, P, H, 128]``, ``beta``
+    ``[N, P, H]``.  Returns o ``[N, P, H, 128]``."""
+    lib = load()
+    N, H, dk, dv = state.shape
+    if state.dtype != torch.float32:
+        raise ValueError("state must be fp32 [N, H, dk, dv]")
+    if accepted.dtype != torch.int32 or accepted.shape != (N,):
+        raise ValueError("accepted must be int32 [N]")
+    W, P = ck.shape[1], k.shape[1]
+    dt = k.dtype
+    if ck.shape != (N, W, H, dk) or cg.shape != ck.shape or cv.shape != (N, W, H, dv) \
+            or cbeta.shape != (N, W, H):
+        raise ValueError("cached window shapes")
+    if k.shape != (N, P, H, dk) or q.shape != k.shape or g.shape != k.shape \
+            or v.shape != (N, P, H, dv) or beta.shape != (N, P, H):
+        raise ValueError("new window shapes")
+    for x in (ck, cv, cg, cbeta, q, v, g, beta):
+        if x.dtype != dt:
+            raise TypeError("the cached and new inputs must share one dtype")
+    dev = _check_device(state, accepted, ck, cv, cg, cbeta, q, k, v, g, beta, o)
+    if o is None:
+        o = torch.empty((N, P, H, dv), dtype=dt, device=dev)
+    st = lib.kda_decode_replay(N, H, dk, dv, _dtype_code(dt), W, _ptr(accepted), _ptr(ck),
+                               _ptr(cv), _ptr(cg), _ptr(cbeta), P, _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(g), _ptr(beta), _ptr(state), _ptr(o), _stream_ptr(dev))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_decode_replay")
     return o
 
 

@@ -414,6 +414,34 @@ kda_status kda_decode_step(int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dty
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+kda_status kda_decode_replay(int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
+                             int32_t W, const int32_t *accepted, const void *ck, const void *cv,
+                             const void *cg, const void *cbeta, int32_t P, const void *q,
+                             const void *k, const void *v, const void *g, const void *beta,
+                             float *state, void *o, void *stream) {
+  if (dk != kD || dv != kD || (dt != KDA_F32 && dt != KDA_BF16))
+    return KDA_ERR_UNSUPPORTED;
+  if (N < 0 || H < 1 || W < 0 || W > KDA_REPLAY_MAX_TOKENS || P < 0 ||
+      P > KDA_REPLAY_MAX_TOKENS)
+    return KDA_ERR_INVALID_ARG;
+  // token-row indices ((n W + t) H + h) kD stay within int64; blocks within 2^31
+  if ((int64_t)N * H >= ((int64_t)1 << 31))
+    return KDA_ERR_INVALID_ARG;
+  if (N == 0)
+    return KDA_OK;
+  if (!accepted || !state || !aligned16(state) || ((uintptr_t)accepted & 3))
+    return KDA_ERR_INVALID_ARG;
+  if (W > 0 && (!ck || !cv || !cg || !cbeta || !aligned16(ck) || !aligned16(cv) ||
+                !aligned16(cg) || !aligned_elt(cbeta, dt)))
+    return KDA_ERR_INVALID_ARG;
+  if (P > 0 && (!q || !k || !v || !g || !beta || !o || !aligned16(q) || !aligned16(k) ||
+                !aligned16(v) || !aligned16(g) || !aligned_elt(beta, dt) || !aligned16(o)))
+    return KDA_ERR_INVALID_ARG;
+  const hipError_t e = launch_replay(dt == KDA_BF16 ? 1 : 0, N, H, W, accepted, ck, cv, cg,
+                                     cbeta, P, q, k, v, g, beta, state, o, (hipStream_t)stream);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 size_t kda_segment_transition_workspace_size(int32_t num_segs,
                                              const int64_t *cu_seglens_host, int32_t H,
                                              int32_t dk, int32_t dv, kda_dtype dt) {

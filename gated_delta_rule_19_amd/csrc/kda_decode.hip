@@ -97,6 +97,133 @@ __global__ __launch_bounds__(256) void decode_kernel(const T *__restrict__ q,
   }
 }
 
+// Speculative-decode replay ("Kimi K3.1 Pro 架构完全拆解" §3.4; "部署 Kimi K3：
+// 从 KDA Kernel 到 Fleet 调度" §四): instead of restoring a state snapshot,
+// the state before a draft window is advanced through the m accepted draft
+// tokens from their cached projected inputs, then through the P new tokens
+// (the bonus token first, then the next window's drafts), all on chip.  The
+// state after the bonus token is written back; the new tokens' outputs are
+// written; the later drafts' states are not kept.  The layout and the step
+// are the decode kernel's: the state is read once and written once however
+// many tokens the call runs.
+template <typename T>
+__global__ __launch_bounds__(256) void replay_kernel(
+    int32_t H, int32_t W, int32_t P, const int32_t *__restrict__ accepted,
+    const T *__restrict__ ck, const T *__restrict__ cv, const T *__restrict__ cg,
+    const T *__restrict__ cb, const T *__restrict__ q, const T *__restrict__ k,
+    const T *__restrict__ v, const T *__restrict__ g, const T *__restrict__ beta,
+    float *__restrict__ state, T *__restrict__ o) {
+  const int64_t nh = blockIdx.x;
+  const int n = (int)(nh / H), h = (int)(nh - (int64_t)n * H);
+  const int tid = threadIdx.x;
+  const int cg4 = tid & 31; // column group: columns 4*cg4 .. 4*cg4+3
+  const int rg = tid >> 5;  // row group: rows 16*rg .. 16*rg+15
+
+  __shared__ float s_k[kD], s_q[kD], s_a[kD], s_v[kD], s_u[kD];
+  __shared__ float s_w[8][kD], s_y[8][kD];
+  __shared__ float s_kq, s_beta;
+
+  float *S = state + nh * (int64_t)(kD * kD);
+  f32x4 s[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    s[i] = __builtin_nontemporal_load(
+        reinterpret_cast<const f32x4 *>(S + (16 * rg + i) * kD + 4 * cg4));
+
+  const int m = min(max(accepted[n], 0), W); // accepted draft tokens to replay
+  const int total = m + P;
+  const int commit = m + min(P, 1); // tokens whose state is kept
+  for (int t = 0; t < total; ++t) {
+    const bool out = t >= m; // a new token: its output is written
+    const int j = t - m;
+    // this token's row of each input (cached window or new window)
+    const int64_t tok = out ? ((int64_t)n * P + j) * H + h : ((int64_t)n * W + t) * H + h;
+    const T *kk = out ? k : ck;
+    const T *vv = out ? v : cv;
+    const T *gg = out ? g : cg;
+    const T *bb = out ? beta : cb;
+    if (tid < kD) {
+      s_k[tid] = to_f32(kk[tok * kD + tid]);
+      s_a[tid] = __expf(to_f32(gg[tok * kD + tid]));
+      s_v[tid] = to_f32(vv[tok * kD + tid]);
+      float qv = 0.f; // (q is only read for new tokens: it may be null when P = 0)
+      if (out)
+        qv = to_f32(q[tok * kD + tid]);
+      s_q[tid] = qv;
+    }
+    if (tid == 0)
+      s_beta = to_f32(bb[tok]);
+    __syncthreads();
+
+    if (tid < 64) { // k . q, inside wave 0
+      float p = s_k[tid] * s_q[tid] + s_k[tid + 64] * s_q[tid + 64];
+#pragma unroll
+      for (int mm = 32; mm >= 1; mm >>= 1)
+        p += __shfl_xor(p, mm);
+      if (tid == 0)
+        s_kq = p;
+    }
+    f32x4 w = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 16 * rg + i;
+      s[i] *= s_a[r];
+      w += s_k[r] * s[i];
+      y += s_q[r] * s[i];
+    }
+    *reinterpret_cast<f32x4 *>(&s_w[rg][4 * cg4]) = w;
+    *reinterpret_cast<f32x4 *>(&s_y[rg][4 * cg4]) = y;
+    __syncthreads();
+
+    if (tid < kD) {
+      float ws = 0.f, ys = 0.f;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        ws += s_w[r][tid];
+        ys += s_y[r][tid];
+      }
+      const float u = s_beta * (s_v[tid] - ws);
+      s_u[tid] = u;
+      if (out)
+        o[tok * kD + tid] = from_f32<T>(ys + s_kq * u);
+    }
+    __syncthreads();
+
+    const f32x4 u4 = *reinterpret_cast<const f32x4 *>(&s_u[4 * cg4]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      s[i] += s_k[16 * rg + i] * u4;
+    if (t + 1 == commit) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        __builtin_nontemporal_store(
+            s[i], reinterpret_cast<f32x4 *>(S + (16 * rg + i) * kD + 4 * cg4));
+    }
+    __syncthreads(); // the next token rewrites the shared inputs
+  }
+}
+
+hipError_t launch_replay(int elt, int32_t N, int32_t H, int32_t W, const int32_t *accepted,
+                         const void *ck, const void *cv, const void *cg, const void *cb,
+                         int32_t P, const void *q, const void *k, const void *v, const void *g,
+                         const void *beta, float *state, void *o, hipStream_t s) {
+  const int64_t nh = (int64_t)N * H;
+  if (nh == 0)
+    return hipSuccess;
+  dim3 grid((unsigned)nh), block(256);
+  if (elt == 1)
+    replay_kernel<bf16><<<grid, block, 0, s>>>(
+        H, W, P, accepted, (const bf16 *)ck, (const bf16 *)cv, (const bf16 *)cg,
+        (const bf16 *)cb, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (const bf16 *)g,
+        (const bf16 *)beta, state, (bf16 *)o);
+  else
+    replay_kernel<float><<<grid, block, 0, s>>>(
+        H, W, P, accepted, (const float *)ck, (const float *)cv, (const float *)cg,
+        (const float *)cb, (const float *)q, (const float *)k, (const float *)v,
+        (const float *)g, (const float *)beta, state, (float *)o);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(int elt, int32_t N, int32_t H, const void *q, const void *k,
                          const void *v, const void *g, const void *beta, float *state, void *o,
                          hipStream_t s) {

@@ -158,6 +158,39 @@ kda_status kda_decode_step(int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dty
                            const void *beta, float *state, void *o, void *stream);
 
 /*
+ * Speculative-decode replay for N sequences ("Kimi K3.1 Pro 架构完全拆解"
+ * §3.4; "部署 Kimi K3：从 KDA Kernel 到 Fleet 调度" §四): the state is not
+ * rolled back from a snapshot but rebuilt from the cached projected inputs
+ * of the accepted draft tokens.  Per sequence n, from `state` (the state
+ * before the draft window), the decode step above runs over the first
+ * m_n = clamp(accepted[n], 0, W) cached tokens (their outputs are not
+ * produced), then over the P new tokens: the bonus token first, then the
+ * next window's drafts.  The state after the accepted tokens and the bonus
+ * token is written back (after the accepted tokens alone when P = 0); the
+ * later drafts' states are not kept.
+ *
+ *   W        : cached window length, 0 <= W <= KDA_REPLAY_MAX_TOKENS.
+ *   accepted : DEVICE int32 [N], accepted draft tokens per sequence (values
+ *              outside [0, W] are clamped; read on the device, no sync).
+ *   ck, cg   : [N, W, H, dk] of type dt;  cv : [N, W, H, dv];  cbeta : [N, W, H].
+ *              May be NULL when W == 0.
+ *   P        : new tokens, 0 <= P <= KDA_REPLAY_MAX_TOKENS.
+ *   q, k, g  : [N, P, H, dk] of type dt;  v : [N, P, H, dv];  beta : [N, P, H].
+ *              May be NULL when P == 0.
+ *   state    : [N, H, dk, dv] fp32, read and overwritten.
+ *   o        : [N, P, H, dv] of type dt: the new tokens' outputs; must not
+ *              overlap any input or the state.  May be NULL when P == 0.
+ * The state is read once and written once whatever W and P are.  N = 0 is a
+ * no-op.  Validation failures return before anything is enqueued.
+ */
+#define KDA_REPLAY_MAX_TOKENS 64
+kda_status kda_decode_replay(int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
+                             int32_t W, const int32_t *accepted, const void *ck, const void *cv,
+                             const void *cg, const void *cbeta, int32_t P, const void *q,
+                             const void *k, const void *v, const void *g, const void *beta,
+                             float *state, void *o, void *stream);
+
+/*
  * Segment transition pairs ("部署 Kimi K3：从 KDA Kernel 到 Fleet 调度", §二,
  * the KCP decomposition): for each packed segment s (tokens
  * [cu[s], cu[s+1])) and head h,

@@ -153,6 +153,37 @@ def test_decode_argument_errors(lib):
     assert dec(N=0) == E.KDA_OK
 
 
+def test_replay_argument_errors(lib):
+    E = nat
+
+    def rep(N=4, H=2, dk=128, dv=128, dt=nat.KDA_BF16, W=4, acc=FAKE, ck=FAKE, cv=FAKE,
+            cg=FAKE, cb=FAKE, P=3, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state=FAKE,
+            o=FAKE):
+        return lib.kda_decode_replay(N, H, dk, dv, dt, W, acc, ck, cv, cg, cb, P, q, k, v, g,
+                                     beta, state, o, None)
+
+    assert rep(dv=64) == E.KDA_ERR_UNSUPPORTED
+    assert rep(dt=3) == E.KDA_ERR_UNSUPPORTED
+    assert rep(W=-1) == E.KDA_ERR_INVALID_ARG
+    assert rep(W=65) == E.KDA_ERR_INVALID_ARG
+    assert rep(P=-1) == E.KDA_ERR_INVALID_ARG
+    assert rep(P=65) == E.KDA_ERR_INVALID_ARG
+    assert rep(acc=None) == E.KDA_ERR_INVALID_ARG
+    assert rep(acc=ctypes.c_void_p(0x100002)) == E.KDA_ERR_INVALID_ARG
+    assert rep(state=None) == E.KDA_ERR_INVALID_ARG
+    assert rep(ck=None) == E.KDA_ERR_INVALID_ARG        # needed when W > 0
+    assert rep(cb=ctypes.c_void_p(0x100001)) == E.KDA_ERR_INVALID_ARG
+    assert rep(o=None) == E.KDA_ERR_INVALID_ARG         # needed when P > 0
+    assert rep(k=MISALIGNED) == E.KDA_ERR_INVALID_ARG
+    assert rep(N=1 << 30, H=4) == E.KDA_ERR_INVALID_ARG
+    assert rep(N=0) == E.KDA_OK
+    # the cached window may be absent when W = 0, the new window when P = 0,
+    # but the remaining checks still apply
+    assert rep(W=0, ck=None, cv=None, cg=None, cb=None, state=None) == E.KDA_ERR_INVALID_ARG
+    assert rep(P=0, q=None, k=None, v=None, g=None, beta=None, o=None,
+               ck=MISALIGNED) == E.KDA_ERR_INVALID_ARG
+
+
 def test_segment_transition_argument_errors(lib):
     E = nat
     a, p = cu(0, 64, 100)
