@@ -133,26 +133,41 @@ __global__ __launch_bounds__(256) void replay_kernel(
   const int m = min(max(accepted[n], 0), W); // accepted draft tokens to replay
   const int total = m + P;
   const int commit = m + min(P, 1); // tokens whose state is kept
-  for (int t = 0; t < total; ++t) {
-    const bool out = t >= m; // a new token: its output is written
-    const int j = t - m;
-    // this token's row of each input (cached window or new window)
-    const int64_t tok = out ? ((int64_t)n * P + j) * H + h : ((int64_t)n * W + t) * H + h;
-    const T *kk = out ? k : ck;
-    const T *vv = out ? v : cv;
-    const T *gg = out ? g : cg;
-    const T *bb = out ? beta : cb;
+  // one token's inputs for thread tid < 128 (element tid of k, g, v, q) and
+  // beta; the next token's are loaded while the current one is stepped
+  struct TokIn {
+    float k, g, v, q, b;
+  };
+  auto load_tok = [&](int t) {
+    TokIn x = {0.f, 0.f, 0.f, 0.f, 0.f};
+    if (t >= total)
+      return x;
+    const bool out = t >= m;
+    const int64_t tok = out ? ((int64_t)n * P + (t - m)) * H + h : ((int64_t)n * W + t) * H + h;
     if (tid < kD) {
-      s_k[tid] = to_f32(kk[tok * kD + tid]);
-      s_a[tid] = __expf(to_f32(gg[tok * kD + tid]));
-      s_v[tid] = to_f32(vv[tok * kD + tid]);
-      float qv = 0.f; // (q is only read for new tokens: it may be null when P = 0)
-      if (out)
-        qv = to_f32(q[tok * kD + tid]);
-      s_q[tid] = qv;
+      x.k = to_f32((out ? k : ck)[tok * kD + tid]);
+      x.g = to_f32((out ? g : cg)[tok * kD + tid]);
+      x.v = to_f32((out ? v : cv)[tok * kD + tid]);
+      if (out) // (q may be null when P = 0)
+        x.q = to_f32(q[tok * kD + tid]);
     }
     if (tid == 0)
-      s_beta = to_f32(bb[tok]);
+      x.b = to_f32((out ? beta : cb)[tok]);
+    return x;
+  };
+  TokIn cur = load_tok(0);
+  for (int t = 0; t < total; ++t) {
+    const bool out = t >= m; // a new token: its output is written
+    const int64_t tok = out ? ((int64_t)n * P + (t - m)) * H + h : 0;
+    if (tid < kD) {
+      s_k[tid] = cur.k;
+      s_a[tid] = __expf(cur.g);
+      s_v[tid] = cur.v;
+      s_q[tid] = cur.q;
+    }
+    if (tid == 0)
+      s_beta = cur.b;
+    const TokIn nxt = load_tok(t + 1);
     __syncthreads();
 
     if (tid < 64) { // k . q, inside wave 0
@@ -199,6 +214,7 @@ __global__ __launch_bounds__(256) void replay_kernel(
         __builtin_nontemporal_store(
             s[i], reinterpret_cast<f32x4 *>(S + (16 * rg + i) * kD + 4 * cg4));
     }
+    cur = nxt;
     __syncthreads(); // the next token rewrites the shared inputs
   }
 }
