@@ -34,6 +34,7 @@ EXPORTED = (
     "kda_plan_num_segments",
     "kda_chunk_prefill_workspace_size",
     "kda_chunk_prefill",
+    "kda_chunk_prefill_ckpt",
     "kda_decode_step",
     "kda_decode_replay",
     "kda_segment_transition_workspace_size",
@@ -73,6 +74,9 @@ def load():
         lib.kda_chunk_prefill.restype = i32
         lib.kda_chunk_prefill.argtypes = [i32, lp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                           vp, vp, i32, vp, sz, vp]
+        lib.kda_chunk_prefill_ckpt.restype = i32
+        lib.kda_chunk_prefill_ckpt.argtypes = [i32, lp, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                               vp, vp, vp, i32, lp, i32, vp, vp, sz, vp]
         lib.kda_decode_step.restype = i32
         lib.kda_decode_step.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.kda_decode_replay.restype = i32
@@ -167,6 +171,30 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None,
     Returns ``(o, final_state or None)``.  ``final_state`` may be passed in
     (it may be ``initial_state`` itself for an in-place resume).
     """
+    o, final_state, _, _ = _prefill(q, k, v, g, beta, cu_seqlens, initial_state,
+                                    output_final_state, split_hint, o, final_state, workspace)
+    return o, final_state
+
+
+def chunk_prefill_checkpoint(q, k, v, g, beta, cu_seqlens=None, initial_state=None,
+                             align: int = 512, pos0=None, checkpoint=None,
+                             output_final_state: bool = True, split_hint: int = 0, o=None,
+                             final_state=None, workspace=None):
+    """Prefill that also writes each sequence's state at its last
+    ``align``-aligned absolute position (``kda_chunk_prefill_ckpt``).
+
+    ``pos0``: the absolute position of each sequence's first token (host
+    integers, multiples of 64; None = 0).  Returns ``(o, final_state,
+    checkpoint [N, H, 128, 128], positions)``: positions[n] is the absolute
+    position whose state checkpoint[n] holds, or -1 when sequence n has no
+    aligned position past pos0[n] (checkpoint[n] is then not written).
+    """
+    return _prefill(q, k, v, g, beta, cu_seqlens, initial_state, output_final_state,
+                    split_hint, o, final_state, workspace, int(align), pos0, checkpoint)
+
+
+def _prefill(q, k, v, g, beta, cu_seqlens, initial_state, output_final_state, split_hint, o,
+             final_state, workspace, align=0, pos0=None, checkpoint=None):
     lib = load()
     if q.dim() == 4:
         if cu_seqlens is not None and q.shape[0] != 1:
@@ -202,13 +230,34 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None,
                                                       split_hint))
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    st = lib.kda_chunk_prefill(N, _cu_ptr(cu), H, dk, dv, code, _ptr(q), _ptr(k), _ptr(v),
-                               _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
-                               _ptr(final_state), int(split_hint), _ptr(workspace),
-                               workspace.numel(), _stream_ptr(dev))
+    if align == 0:
+        st = lib.kda_chunk_prefill(N, _cu_ptr(cu), H, dk, dv, code, _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
+                                   _ptr(final_state), int(split_hint), _ptr(workspace),
+                                   workspace.numel(), _stream_ptr(dev))
+        if st != KDA_OK:
+            raise KdaError(st, "kda_chunk_prefill")
+        return o, final_state, None, None
+    p0 = np.zeros(N, dtype=np.int64) if pos0 is None else \
+        np.ascontiguousarray(np.asarray(pos0, dtype=np.int64))
+    if p0.shape != (N,):
+        raise ValueError("pos0 must hold one position per sequence")
+    if checkpoint is None:
+        checkpoint = torch.zeros((N, H, dk, dv), dtype=torch.float32, device=dev)
+    elif checkpoint.dtype != torch.float32 or checkpoint.shape != (N, H, dk, dv):
+        raise ValueError("checkpoint must be fp32 [N, H, dk, dv]")
+    _check_device(checkpoint)
+    st = lib.kda_chunk_prefill_ckpt(N, _cu_ptr(cu), H, dk, dv, code, _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
+                                    _ptr(final_state), int(split_hint), _cu_ptr(p0),
+                                    int(align), _ptr(checkpoint), _ptr(workspace),
+                                    workspace.numel(), _stream_ptr(dev))
     if st != KDA_OK:
-        raise KdaError(st, "kda_chunk_prefill")
-    return o, final_state
+        raise KdaError(st, "kda_chunk_prefill_ckpt")
+    end = p0 + np.diff(cu)
+    pos = end // align * align
+    pos = np.where(pos > p0, pos, -1)
+    return o, final_state, checkpoint, pos
 
 
 def decode_step(state, q, k, v, g, beta, o=None):

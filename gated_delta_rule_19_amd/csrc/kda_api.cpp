@@ -75,7 +75,7 @@ ChainDesc chain(int64_t tok0, int64_t ntok, int64_t chunk0, int64_t init_idx,
   c.chunk0 = (int32_t)chunk0;
   c.init_idx = (int32_t)init_idx;
   c.final_idx = (int32_t)final_idx;
-  c.pad0 = c.pad1 = 0;
+  c.ckpt_chunk = c.ckpt_idx = -1;
   return c;
 }
 
@@ -118,8 +118,19 @@ void layout(Plan &p, int32_t H, size_t es) {
 }
 
 // Prefill schedule.  Returns false on bad cu_seqlens.
+// Chunk count, from the sequence start, of sequence n's state checkpoint: the
+// last position p with pos0 < p <= pos0 + len and p a multiple of align
+// (pos0 and align multiples of the chunk length); 0 when there is none.
+int64_t ckpt_chunks(int64_t pos0, int64_t len, int64_t align) {
+  if (align <= 0)
+    return 0;
+  const int64_t p = (pos0 + len) / align * align;
+  return p > pos0 ? (p - pos0) / kC : 0;
+}
+
 bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_hint,
-                        bool has_init, bool has_final, size_t es, Plan &p) {
+                        bool has_init, bool has_final, size_t es, Plan &p,
+                        const int64_t *pos0 = nullptr, int64_t align = 0) {
   if (!cu || cu[0] != 0)
     return false;
   for (int32_t n = 0; n < N; ++n)
@@ -136,9 +147,15 @@ bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_h
       d.seq = n;
       p.chunks.push_back(d);
     }
+    // the chunk after which the checkpoint state is taken, if any
+    const int64_t ck = ckpt_chunks(pos0 ? pos0[n] : 0, len, align) - 1;
     const int64_t nseg = plan_nseg(len, N, H, split_hint);
     if (nseg <= 1) {
       p.chains.push_back(chain(cu[n], len, c0, has_init ? n : -1, has_final ? n : -1));
+      if (ck >= 0) {
+        p.chains.back().ckpt_chunk = (int32_t)ck;
+        p.chains.back().ckpt_idx = n;
+      }
       continue;
     }
     const int64_t q = nch / nseg, r = nch % nseg;
@@ -152,6 +169,10 @@ bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_h
         p.segchains.push_back(chain(t0, nt, c0 + s0, -1, pair0 + j));
       const bool last = j + 1 == nseg;
       p.chains.push_back(chain(t0, nt, c0 + s0, -2 - (sin0 + j), (last && has_final) ? n : -1));
+      if (ck >= s0 && ck < s0 + cnt) {
+        p.chains.back().ckpt_chunk = (int32_t)(ck - s0);
+        p.chains.back().ckpt_idx = n;
+      }
     }
     p.scans.push_back(ScanDesc{(int32_t)pair0, (int32_t)nseg, (int32_t)sin0,
                                has_init ? n : -1});
@@ -290,6 +311,80 @@ hipError_t upload_tables(const Plan &p, void *ws, hipStream_t stream) {
 
 } // namespace
 
+namespace {
+
+// kda_chunk_prefill and kda_chunk_prefill_ckpt (ckpt_align = 0: no checkpoints)
+kda_status prefill_impl(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_t H, int32_t dk,
+                        int32_t dv, kda_dtype dt, const void *q, const void *k, const void *v,
+                        const void *g, const void *beta, const float *initial_state, void *o,
+                        float *final_state, int32_t split_hint, const int64_t *pos0,
+                        int32_t ckpt_align, float *ckpt, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+  if (dk != kD || dv != kD || (dt != KDA_F32 && dt != KDA_BF16))
+    return KDA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || H < 1 || split_hint < 0 || !cu_seqlens_host)
+    return KDA_ERR_INVALID_ARG;
+  if (ckpt_align != 0) {
+    if (ckpt_align < 0 || ckpt_align % kC != 0 || !ckpt || !aligned16(ckpt))
+      return KDA_ERR_INVALID_ARG;
+    for (int32_t n = 0; pos0 && n < num_seqs; ++n)
+      if (pos0[n] < 0 || pos0[n] % kC != 0 || pos0[n] > ((int64_t)1 << 62))
+        return KDA_ERR_INVALID_ARG;
+  }
+  Plan p;
+  if (!build_prefill_plan(num_seqs, cu_seqlens_host, H, split_hint, initial_state != nullptr,
+                          final_state != nullptr, elt_size(dt), p, pos0, ckpt_align))
+    return KDA_ERR_INVALID_ARG;
+  if (!plan_fits(p, H))
+    return KDA_ERR_INVALID_ARG;
+  const int64_t T = cu_seqlens_host[num_seqs];
+  if (T > 0) {
+    if (!q || !k || !v || !g || !beta || !o)
+      return KDA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) ||
+        !aligned_elt(beta, dt) || !aligned16(o))
+      return KDA_ERR_INVALID_ARG;
+  }
+  if (!aligned16(initial_state) || !aligned16(final_state))
+    return KDA_ERR_INVALID_ARG;
+  if (num_seqs == 0)
+    return KDA_OK;
+  if (p.total > 0) {
+    if (!workspace || workspace_bytes < p.total || ((uintptr_t)workspace % kAlign) != 0)
+      return KDA_ERR_WORKSPACE;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t *ws = (uint8_t *)workspace;
+  const int elt = dt == KDA_BF16 ? 1 : 0;
+  const ChunkDesc *d_chunks = (const ChunkDesc *)(ws + p.off_chunks);
+  hipError_t e = upload_tables(p, ws, s);
+  if (p.fused) {
+    if (e == hipSuccess)
+      e = launch_fused((const ChainDesc *)(ws + p.off_chains), (int32_t)p.chains.size(), H, q,
+                       k, v, g, beta, o, initial_state, nullptr, final_state,
+                       ckpt_align ? ckpt : nullptr, s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  }
+  if (e == hipSuccess)
+    e = launch_k1(elt, d_chunks, (int32_t)p.chunks.size(), H, q, k, g, beta, ws + p.off_rec, s);
+  if (e == hipSuccess && !p.segchains.empty()) {
+    e = launch_k2(elt, 1, (const ChainDesc *)(ws + p.off_seg), (int32_t)p.segchains.size(), H,
+                  ws + p.off_rec, v, nullptr, nullptr, nullptr, (float *)(ws + p.off_St),
+                  (float *)(ws + p.off_M), s);
+    if (e == hipSuccess)
+      e = launch_scan((const ScanDesc *)(ws + p.off_scan), (int32_t)p.scans.size(), H,
+                      (const float *)(ws + p.off_M), (const float *)(ws + p.off_St),
+                      initial_state, (float *)(ws + p.off_Sin), s);
+  }
+  if (e == hipSuccess)
+    e = launch_k2(elt, 0, (const ChainDesc *)(ws + p.off_chains), (int32_t)p.chains.size(), H,
+                  ws + p.off_rec, v, o, initial_state, (const float *)(ws + p.off_Sin),
+                  final_state, ckpt_align ? ckpt : nullptr, s);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+} // namespace
+
 extern "C" {
 
 const char *kda_status_string(kda_status s) {
@@ -332,65 +427,30 @@ size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, const int64_t *cu_seql
   return p.total;
 }
 
+
 kda_status kda_chunk_prefill(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_t H,
                              int32_t dk, int32_t dv, kda_dtype dt, const void *q, const void *k,
                              const void *v, const void *g, const void *beta,
                              const float *initial_state, void *o, float *final_state,
                              int32_t split_hint, void *workspace, size_t workspace_bytes,
                              void *stream) {
-  if (dk != kD || dv != kD || (dt != KDA_F32 && dt != KDA_BF16))
-    return KDA_ERR_UNSUPPORTED;
-  if (num_seqs < 0 || H < 1 || split_hint < 0 || !cu_seqlens_host)
+  return prefill_impl(num_seqs, cu_seqlens_host, H, dk, dv, dt, q, k, v, g, beta, initial_state,
+                      o, final_state, split_hint, nullptr, 0, nullptr, workspace,
+                      workspace_bytes, stream);
+}
+
+kda_status kda_chunk_prefill_ckpt(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_t H,
+                                  int32_t dk, int32_t dv, kda_dtype dt, const void *q,
+                                  const void *k, const void *v, const void *g, const void *beta,
+                                  const float *initial_state, void *o, float *final_state,
+                                  int32_t split_hint, const int64_t *pos0_host,
+                                  int32_t ckpt_align, float *ckpt_state, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+  if (ckpt_align <= 0)
     return KDA_ERR_INVALID_ARG;
-  Plan p;
-  if (!build_prefill_plan(num_seqs, cu_seqlens_host, H, split_hint, initial_state != nullptr,
-                          final_state != nullptr, elt_size(dt), p))
-    return KDA_ERR_INVALID_ARG;
-  if (!plan_fits(p, H))
-    return KDA_ERR_INVALID_ARG;
-  const int64_t T = cu_seqlens_host[num_seqs];
-  if (T > 0) {
-    if (!q || !k || !v || !g || !beta || !o)
-      return KDA_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) ||
-        !aligned_elt(beta, dt) || !aligned16(o))
-      return KDA_ERR_INVALID_ARG;
-  }
-  if (!aligned16(initial_state) || !aligned16(final_state))
-    return KDA_ERR_INVALID_ARG;
-  if (num_seqs == 0)
-    return KDA_OK;
-  if (p.total > 0) {
-    if (!workspace || workspace_bytes < p.total || ((uintptr_t)workspace % kAlign) != 0)
-      return KDA_ERR_WORKSPACE;
-  }
-  hipStream_t s = (hipStream_t)stream;
-  uint8_t *ws = (uint8_t *)workspace;
-  const int elt = dt == KDA_BF16 ? 1 : 0;
-  const ChunkDesc *d_chunks = (const ChunkDesc *)(ws + p.off_chunks);
-  hipError_t e = upload_tables(p, ws, s);
-  if (p.fused) {
-    if (e == hipSuccess)
-      e = launch_fused((const ChainDesc *)(ws + p.off_chains), (int32_t)p.chains.size(), H, q,
-                       k, v, g, beta, o, initial_state, nullptr, final_state, s);
-    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
-  }
-  if (e == hipSuccess)
-    e = launch_k1(elt, d_chunks, (int32_t)p.chunks.size(), H, q, k, g, beta, ws + p.off_rec, s);
-  if (e == hipSuccess && !p.segchains.empty()) {
-    e = launch_k2(elt, 1, (const ChainDesc *)(ws + p.off_seg), (int32_t)p.segchains.size(), H,
-                  ws + p.off_rec, v, nullptr, nullptr, nullptr, (float *)(ws + p.off_St),
-                  (float *)(ws + p.off_M), s);
-    if (e == hipSuccess)
-      e = launch_scan((const ScanDesc *)(ws + p.off_scan), (int32_t)p.scans.size(), H,
-                      (const float *)(ws + p.off_M), (const float *)(ws + p.off_St),
-                      initial_state, (float *)(ws + p.off_Sin), s);
-  }
-  if (e == hipSuccess)
-    e = launch_k2(elt, 0, (const ChainDesc *)(ws + p.off_chains), (int32_t)p.chains.size(), H,
-                  ws + p.off_rec, v, o, initial_state, (const float *)(ws + p.off_Sin),
-                  final_state, nullptr, s);
-  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  return prefill_impl(num_seqs, cu_seqlens_host, H, dk, dv, dt, q, k, v, g, beta, initial_state,
+                      o, final_state, split_hint, pos0_host, ckpt_align, ckpt_state, workspace,
+                      workspace_bytes, stream);
 }
 
 kda_status kda_decode_step(int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,

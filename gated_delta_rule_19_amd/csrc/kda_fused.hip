@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
     const ChainDesc *__restrict__ chains, int32_t H, const bf16 *__restrict__ q,
     const bf16 *__restrict__ k, const bf16 *__restrict__ v, const bf16 *__restrict__ g,
     const bf16 *__restrict__ beta, bf16 *__restrict__ o, const float *__restrict__ init,
-    const float *__restrict__ sin, float *__restrict__ final_state) {
+    const float *__restrict__ sin, float *__restrict__ final_state, float *__restrict__ ckpt) {
   using Sm = FusedSmem<NCT>;
   __shared__ __attribute__((aligned(16))) Sm sm;
   constexpr int VW = 16 * NCT; // state columns per state wave
@@ -326,6 +326,22 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
       }
     };
 
+    // the state after chunk ch, when it is the chain's checkpoint
+    auto ckpt_store = [&](int ch) {
+      if (ch == cd.ckpt_chunk && ckpt != nullptr) {
+        const int ln = opaque_lane(), lr = ln & 15, lg = ln >> 4;
+        const int wcol = col0 + VW * wv + lr;
+        float *cp = ckpt + ((int64_t)cd.ckpt_idx * H + h) * (kD * kD);
+#pragma unroll
+        for (int c = 0; c < NCT; ++c)
+#pragma unroll
+          for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              cp[kperm(16 * ct + 4 * lg + i) * kD + wcol + 16 * c] = S[c][ct][i];
+      }
+    };
+
     // D_b^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) for N = L_bb (N^16 = 0), b =
     // this wave's index: the diagonal blocks of INV = (I + L)^-1 of the chunk
     // being prepared, to LDS (for the prep's off-diagonal blocks) and to the
@@ -377,6 +393,7 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
         stage_u(ch);
         lds_barrier();
         stage_s();
+        ckpt_store(ch);
         lds_barrier();
         stage_inv();
         lds_barrier();
@@ -386,6 +403,7 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
       stage_u(nch - 1);
       lds_barrier();
       stage_s();
+      ckpt_store(nch - 1);
       lds_barrier();
       lds_barrier();
       lds_barrier();
@@ -672,7 +690,7 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
 
 hipError_t launch_fused(const ChainDesc *chains, int32_t nchains, int32_t H, const void *q,
                         const void *k, const void *v, const void *g, const void *beta, void *o,
-                        const float *init, const float *sin, float *final_state,
+                        const float *init, const float *sin, float *final_state, float *ckpt,
                         hipStream_t s) {
   if (nchains == 0)
     return hipSuccess;
@@ -681,7 +699,7 @@ hipError_t launch_fused(const ChainDesc *chains, int32_t nchains, int32_t H, con
   dim3 grid((unsigned)nchains, (unsigned)H, kD / (64 * NCT)), block(kFThreads);
   fused_kernel<NCT><<<grid, block, 0, s>>>(chains, H, (const bf16 *)q, (const bf16 *)k,
                                            (const bf16 *)v, (const bf16 *)g, (const bf16 *)beta,
-                                           (bf16 *)o, init, sin, final_state);
+                                           (bf16 *)o, init, sin, final_state, ckpt);
   return hipGetLastError();
 }
 

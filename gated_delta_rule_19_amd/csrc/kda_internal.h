@@ -25,13 +25,16 @@ static_assert(sizeof(ChunkDesc) == 16, "ChunkDesc layout");
 //   init_idx == -1 : entry state = 0 (segment pass: [0 | I])
 //   init_idx <= -2 : entry state = planner entry state Sin[-2 - init_idx]
 //   final_idx >= 0 : exit state written at index final_idx of the output base
+//   ckpt_chunk >= 0: the state after the chain's chunk ckpt_chunk (counted
+//                    from the chain's first chunk) is also written, at index
+//                    ckpt_idx of the checkpoint output
 struct ChainDesc {
   int64_t tok0;
   int32_t ntok;
   int32_t chunk0;
   int32_t init_idx;
   int32_t final_idx;
-  int32_t pad0, pad1;
+  int32_t ckpt_chunk, ckpt_idx;
 };
 static_assert(sizeof(ChainDesc) == 32, "ChainDesc layout");
 
@@ -95,16 +98,18 @@ hipError_t launch_prep_bf16(const ChunkDesc *chunks, int32_t nchunks, int32_t H,
                             const void *k, const void *g, const void *beta, void *ws,
                             hipStream_t s);
 
-// mode 0: prefill/replay (width dv, writes o and exit states);
+// mode 0: prefill/replay (width dv, writes o and exit states to final_a,
+//         and the chains' state checkpoints to final_b when it is not null);
 // mode 1: segment pass (width dk + dv: [S~ | M], no o).
 hipError_t launch_k2(int elt, int mode, const ChainDesc *chains, int32_t nchains, int32_t H,
                      const void *ws, const void *v, void *o, const float *init,
                      const float *sin, float *final_a, float *final_b, hipStream_t s);
 
-// Fused chunk prep + state chain (bf16, width dv): writes o and exit states.
+// Fused chunk prep + state chain (bf16, width dv): writes o, exit states and
+// (when ckpt is not null) the chains' state checkpoints.
 hipError_t launch_fused(const ChainDesc *chains, int32_t nchains, int32_t H, const void *q,
                         const void *k, const void *v, const void *g, const void *beta, void *o,
-                        const float *init, const float *sin, float *final_state,
+                        const float *init, const float *sin, float *final_state, float *ckpt,
                         hipStream_t s);
 
 hipError_t launch_scan(const ScanDesc *descs, int32_t ndesc, int32_t H, const float *Mseg,

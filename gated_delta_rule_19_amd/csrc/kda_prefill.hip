@@ -506,7 +506,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // kperm column order to match).  The chunk records are copied into LDS once
 // per workgroup (double-buffered: chunk i+1's record is in flight while
 // chunk i is computed), so the only barrier is one per chunk.
-//   MODE 0: prefill / replay, width dv; writes o and the exit state.
+//   MODE 0: prefill / replay, width dv; writes o and the exit state (out_a)
+//           and, for chains that hold one, the state checkpoint (out_b).
 //   MODE 1: segment pass, width dk + dv of [S~ | M] from [0 | I] with values
 //           [V | 0]; the exit state's S~ part goes to out_a, M part to out_b.
 // ---------------------------------------------------------------------------
@@ -950,6 +951,21 @@ __global__ __launch_bounds__(k2_threads(BV)) void k2_kernel(
             ar[1][ct] = nr[1][ct];
           }
         }
+      }
+      // prefill: the state after this chunk is also a checkpoint (out_b);
+      // its addresses come from an opaque lane index, so that they are
+      // formed here and not kept in registers across the chunk loop
+      if (MODE == 0 && ch == cd.ckpt_chunk && out_b != nullptr) {
+        const int ln = opaque_lane(), clg = ln >> 4;
+        float *cp = out_b + ((int64_t)cd.ckpt_idx * H + h) * (kD * kD) + vcol0 +
+                    16 * NCT * wv + (ln & 15);
+#pragma unroll
+        for (int c = 0; c < NCT; ++c)
+#pragma unroll
+          for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              cp[srow(16 * ct + 4 * clg + i) * kD + 16 * c] = S[c][ct][i];
       }
 
       if (more) {

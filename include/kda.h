@@ -142,6 +142,34 @@ kda_status kda_chunk_prefill(int32_t num_seqs, const int64_t *cu_seqlens_host, i
                              size_t workspace_bytes, void *stream);
 
 /*
+ * kda_chunk_prefill that also writes, per sequence, the state at its last
+ * hash-aligned position: the KDA checkpoint a prefix cache keeps after each
+ * forward pass ("部署 Kimi K3：从 KDA Kernel 到 Fleet 调度" §三 3.2, the KDA
+ * kernel persists the state at the last hash-aligned position it processed;
+ * "Kimi K3.1 Pro 架构完全拆解" §8.2, checkpoints only on hash-block ends).
+ *
+ *   pos0_host  : HOST [num_seqs], the absolute position of each sequence's
+ *                first token (a resumed prefill starts past 0), each a
+ *                non-negative multiple of 64; NULL means all 0.
+ *   ckpt_align : the hash-block length in tokens, a positive multiple of 64
+ *                (for example 512).
+ *   ckpt_state : [num_seqs, H, dk, dv] fp32.  For sequence n of length L the
+ *                checkpoint position is p = floor((pos0 + L) / ckpt_align)
+ *                * ckpt_align; when p > pos0, slice n receives the state after
+ *                the sequence's first p - pos0 tokens (its initial state
+ *                included; equal to its final state when p = pos0 + L).
+ *                Otherwise slice n is not written.
+ * Everything else, the workspace size included, is as for kda_chunk_prefill.
+ */
+kda_status kda_chunk_prefill_ckpt(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_t H,
+                                  int32_t dk, int32_t dv, kda_dtype dt, const void *q,
+                                  const void *k, const void *v, const void *g, const void *beta,
+                                  const float *initial_state, void *o, float *final_state,
+                                  int32_t split_hint, const int64_t *pos0_host,
+                                  int32_t ckpt_align, float *ckpt_state, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/*
  * One decode step for N independent sequences, updating the state IN PLACE
  * ("Kimi K3 的架構" (hao.cnyes.com), §六, the alternative form the decode
  * kernel follows; "Kimi K3.1 Pro 架构完全拆解" §3.4, state updated in place):

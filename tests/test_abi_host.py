@@ -153,6 +153,28 @@ def test_decode_argument_errors(lib):
     assert dec(N=0) == E.KDA_OK
 
 
+def test_checkpoint_prefill_argument_errors(lib):
+    E = nat
+    a, p = cu(0, 256, 700)
+    pos = np.array([0, 512], dtype=np.int64)
+
+    def run(align=512, pos0=pos, ckpt=FAKE, dk=128, n=2):
+        pp = None if pos0 is None else pos0.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        return lib.kda_chunk_prefill_ckpt(n, p, 2, dk, 128, nat.KDA_BF16, FAKE, FAKE, FAKE,
+                                          FAKE, FAKE, None, FAKE, None, 0, pp, align, ckpt,
+                                          FAKE, 1 << 30, None)
+
+    assert run(dk=64) == E.KDA_ERR_UNSUPPORTED
+    assert run(align=0) == E.KDA_ERR_INVALID_ARG      # this entry point needs an alignment
+    assert run(align=-512) == E.KDA_ERR_INVALID_ARG
+    assert run(align=500) == E.KDA_ERR_INVALID_ARG    # not a multiple of the chunk
+    assert run(ckpt=None) == E.KDA_ERR_INVALID_ARG
+    assert run(ckpt=MISALIGNED) == E.KDA_ERR_INVALID_ARG
+    assert run(pos0=np.array([0, 100], dtype=np.int64)) == E.KDA_ERR_INVALID_ARG
+    assert run(pos0=np.array([-64, 0], dtype=np.int64)) == E.KDA_ERR_INVALID_ARG
+    assert run(n=0, pos0=None) == E.KDA_OK
+
+
 def test_replay_argument_errors(lib):
     E = nat
 
