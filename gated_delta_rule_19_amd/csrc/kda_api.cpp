@@ -231,9 +231,12 @@ size_t elt_size(kda_dtype dt) { return dt == KDA_BF16 ? 2 : 4; }
 // Limits that keep every index inside the kernels' int32 / grid ranges.
 bool plan_fits(const Plan &p, int32_t H) {
   const int64_t lim = (int64_t)1 << 30;
+  // the state chain's 1-D grid: (chains x heads, rounded up to 8) x up to 4
+  // column blocks workgroups
+  const int64_t pairs = (int64_t)std::max(p.chains.size(), p.segchains.size()) * H;
   return (int64_t)p.chunks.size() < lim && (int64_t)p.chains.size() < lim &&
          (int64_t)p.segchains.size() < lim && (int64_t)p.scans.size() < lim &&
-         H <= 65535 && p.npairs < lim && p.nsin < lim;
+         H <= 65535 && p.npairs < lim && p.nsin < lim && (pairs + 8) * 4 < ((int64_t)1 << 31);
 }
 
 // ---- pinned staging for the schedule upload --------------------------------
@@ -370,7 +373,7 @@ kda_status prefill_impl(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_
   if (e == hipSuccess && !p.segchains.empty()) {
     e = launch_k2(elt, 1, (const ChainDesc *)(ws + p.off_seg), (int32_t)p.segchains.size(), H,
                   ws + p.off_rec, v, nullptr, nullptr, nullptr, (float *)(ws + p.off_St),
-                  (float *)(ws + p.off_M), s);
+                  (float *)(ws + p.off_M), /*m_scan_order=*/1, s);
     if (e == hipSuccess)
       e = launch_scan((const ScanDesc *)(ws + p.off_scan), (int32_t)p.scans.size(), H,
                       (const float *)(ws + p.off_M), (const float *)(ws + p.off_St),
@@ -379,7 +382,7 @@ kda_status prefill_impl(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_
   if (e == hipSuccess)
     e = launch_k2(elt, 0, (const ChainDesc *)(ws + p.off_chains), (int32_t)p.chains.size(), H,
                   ws + p.off_rec, v, o, initial_state, (const float *)(ws + p.off_Sin),
-                  final_state, ckpt_align ? ckpt : nullptr, s);
+                  final_state, ckpt_align ? ckpt : nullptr, 0, s);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -560,7 +563,7 @@ kda_status kda_segment_transition(int32_t num_segs, const int64_t *cu_seglens_ho
                   ws + p.off_rec, s);
   if (e == hipSuccess)
     e = launch_k2(elt, 1, (const ChainDesc *)(ws + p.off_seg), (int32_t)p.segchains.size(), H,
-                  ws + p.off_rec, v, nullptr, nullptr, nullptr, S_tilde, M, s);
+                  ws + p.off_rec, v, nullptr, nullptr, nullptr, S_tilde, M, 0, s);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -76,17 +76,33 @@ constexpr size_t k1_record_bytes(size_t es) {
 }
 
 // Column blocks of the state-carrying kernel (columns of S per workgroup;
-// each of its waves carries kK2ColTiles 16-column tiles).  The wide block
-// reads each chunk record once per head; the narrow one doubles the
-// workgroups (each record is then read twice) for launches with too few
-// chains to give every compute unit one workgroup.
+// each of its waves carries NCT 16-column tiles).  The wide block reads each
+// chunk record once per head; the narrow one doubles the workgroups (each
+// record is then read twice) for launches with too few chains to give every
+// compute unit one workgroup.  The planner's segment pass over many segments
+// is throughput-bound: there, 64-column blocks with one record buffer let two
+// workgroups share a compute unit, each hiding the other's record loads.
 constexpr int kBVWide = 128;
 constexpr int kBVNarrow = 64;
-constexpr int kK2ColTiles = 1;
-constexpr int k2_threads(int bv) { return bv / (16 * kK2ColTiles) * 64; }
+constexpr int kK2ThroughputGroups = 512; // wide workgroups from which the segment pass uses it
+constexpr int kK2ThroughputBV = 64;
+constexpr int kK2ThroughputNCT = 1;
+constexpr int k2_threads(int bv, int nct) { return bv / (16 * nct) * 64; }
 constexpr int kComputeUnits = 256;
 // Column block of the planner scan kernel.
-constexpr int kScanBV = 8;
+constexpr int kScanBV = 16;
+
+// Position of M[r][m] (r: output row, m: reduction index) in the scan order
+// the planner's segment pass writes its transition matrices in: 1 KiB blocks,
+// one per (wave w = r / 32, k-group i = m / 16, row tile t = r / 16 % 2) in
+// that order, each holding the 64 lanes' A operands of the scan kernel's
+// v_mfma_f32_16x16x4f32 products (lane 16 (m / 4 % 4) + r % 16, four
+// consecutive reduction indices per lane).  One scan load is then 1 KiB
+// contiguous.
+__host__ __device__ constexpr int scan_m_index(int r, int m) {
+  return ((((r >> 5) * 8 + (m >> 4)) * 2 + ((r >> 4) & 1)) * 64 + ((m >> 2) & 3) * 16 +
+          (r & 15)) * 4 + (m & 3);
+}
 
 // Launchers (enqueue only; return the hipGetLastError of the launch).
 hipError_t launch_k1(int elt, const ChunkDesc *chunks, int32_t nchunks, int32_t H,
@@ -100,10 +116,12 @@ hipError_t launch_prep_bf16(const ChunkDesc *chunks, int32_t nchunks, int32_t H,
 
 // mode 0: prefill/replay (width dv, writes o and exit states to final_a,
 //         and the chains' state checkpoints to final_b when it is not null);
-// mode 1: segment pass (width dk + dv: [S~ | M], no o).
+// mode 1: segment pass (width dk + dv: [S~ | M], no o; S~ to final_a, M to
+//         final_b, row-major or, with m_scan_order, at scan_m_index).
 hipError_t launch_k2(int elt, int mode, const ChainDesc *chains, int32_t nchains, int32_t H,
                      const void *ws, const void *v, void *o, const float *init,
-                     const float *sin, float *final_a, float *final_b, hipStream_t s);
+                     const float *sin, float *final_a, float *final_b, int m_scan_order,
+                     hipStream_t s);
 
 // Fused chunk prep + state chain (bf16, width dv): writes o, exit states and
 // (when ckpt is not null) the chains' state checkpoints.

@@ -495,8 +495,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
 // ---------------------------------------------------------------------------
 // K2: state-carrying chain.  One workgroup per (chain, head, column block of
-// BV = 128 or 64 state columns); wave w owns the kK2ColTiles 16-column tiles
-// starting at vcol0 + 16 kK2ColTiles w, so one workgroup reads each chunk
+// BV = 128 or 64 state columns); wave w owns the NCT 16-column tiles
+// starting at vcol0 + 16 NCT w, so one workgroup reads each chunk
 // record once for its BV columns, and each A fragment a wave reads from LDS
 // serves all of its column tiles.
 // The columns of V, U, O and S are independent, so each wave carries its own
@@ -622,17 +622,17 @@ template <typename T, int NW> struct RecordCopy {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <typename T, int MODE, int BV>
-__global__ __launch_bounds__(k2_threads(BV)) void k2_kernel(
-    const ChainDesc *__restrict__ chains, int32_t H, const uint8_t *__restrict__ ws,
-    const T *__restrict__ v, T *__restrict__ o, const float *__restrict__ init,
-    const float *__restrict__ sin, float *__restrict__ out_a, float *__restrict__ out_b) {
-  constexpr int NW = k2_threads(BV) / 64;
-  constexpr int NCT = kK2ColTiles;
+template <typename T, int MODE, int BV, int NCT, int NBUF>
+__global__ __launch_bounds__(k2_threads(BV, NCT)) void k2_kernel(
+    const ChainDesc *__restrict__ chains, int32_t npairs, int32_t H,
+    const uint8_t *__restrict__ ws, const T *__restrict__ v, T *__restrict__ o,
+    const float *__restrict__ init, const float *__restrict__ sin, float *__restrict__ out_a,
+    float *__restrict__ out_b, int32_t m_scan_order) {
+  constexpr int NW = k2_threads(BV, NCT) / 64;
   using L = RecLds<T>;
   constexpr int RB = (int)k1_record_bytes(sizeof(T));
   constexpr int RBP = L::blocks * 1024; // LDS image, whole 1 KiB blocks
-  constexpr int NBUF = 2 * RBP <= 160 * 1024 ? 2 : 1;
+  static_assert(NBUF == 1 || 2 * RBP <= 160 * 1024, "two record buffers must fit in LDS");
   // fragment addressing: padded images take the row length (elements) of
   // 128- and 64-wide rows, fragment-block images the k-steps per row
   constexpr int LD = L::pieces ? kD / 32 : RecLds<float>::padD / 4;
@@ -641,14 +641,23 @@ __global__ __launch_bounds__(k2_threads(BV)) void k2_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t srecB[NBUF == 2 ? RBP : 1];
   // bf16: each wave's own 64 x VW slice of the chunk's v also goes through
   // LDS (direct-to-LDS loads, 16 bytes per lane); fp32 keeps it in registers
-  // (its record is single-buffered and leaves no room).
-  constexpr bool VLDS = NBUF == 2;
+  // (its record leaves no room).
+  constexpr bool VLDS = sizeof(T) == 2;
   constexpr int VW = 16 * NCT;
   __shared__ __attribute__((aligned(16))) T sv[VLDS ? NW : 1][VLDS ? kC * VW : 1];
 
-  const ChainDesc cd = chains[blockIdx.x];
-  const int h = blockIdx.y;
-  const int col0 = blockIdx.z * BV;
+  // Workgroup -> (chain, head, column block): the column blocks of one
+  // (chain, head) pair are 8 workgroups apart, so they run on the same XCD
+  // (workgroups go to the 8 XCDs round-robin) at about the same time, and
+  // all but the first read each chunk record from that XCD's L2.
+  constexpr int NCB = (MODE == 1 ? 2 * kD : kD) / BV;
+  const int grp = blockIdx.x / (8 * NCB), rem = blockIdx.x - grp * 8 * NCB;
+  const int pair = 8 * grp + (rem & 7);
+  if (pair >= npairs)
+    return;
+  const int chain_i = pair / H, h = pair - chain_i * H;
+  const ChainDesc cd = chains[chain_i];
+  const int col0 = (rem >> 3) * BV;
   const bool mpart = (MODE == 1) && (col0 >= kD);
   const int vcol0 = mpart ? col0 - kD : col0;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
@@ -1004,13 +1013,16 @@ __global__ __launch_bounds__(k2_threads(BV)) void k2_kernel(
     fp = base + ((int64_t)cd.final_idx * H + h) * (kD * kD);
   }
   if (fp) {
+    const bool scan_order = MODE == 1 && mpart && m_scan_order;
 #pragma unroll
     for (int c = 0; c < NCT; ++c)
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          fp[srow(16 * ct + 4 * lg + i) * kD + wcol + 16 * c] = S[c][ct][i];
+        for (int i = 0; i < 4; ++i) {
+          const int r = srow(16 * ct + 4 * lg + i), col = wcol + 16 * c;
+          fp[scan_order ? scan_m_index(r, col) : r * kD + col] = S[c][ct][i];
+        }
   }
 }
 
@@ -1019,53 +1031,171 @@ __global__ __launch_bounds__(k2_threads(BV)) void k2_kernel(
 //   Sin[0] = S_0,   Sin[j+1] = S~_j + M_j Sin[j]
 // ("部署 Kimi K3：从 KDA Kernel 到 Fleet 调度", §二: S = S~ + M S_in, pairs
 // compose associatively).  Serial over segments, parallel over heads and
-// column blocks of kScanBV state columns.  fp32 throughout.
+// column blocks of kScanBV = 16 state columns, fp32 throughout.
+//
+// One workgroup of four waves per (sequence, head, column block).  Each step
+// is a 128 x 16 x 128 product on v_mfma_f32_16x16x4f32: wave w owns output
+// rows 32w .. 32w + 31 (two 16-row tiles) and all 128 reduction indices.  The
+// k-step (i, e) of a lane in lane group kq = lane / 16 reduces over state row
+//   m = 16 i + 4 kq + e     (i = 0..7, e = 0..3),
+// so the lane's A operand is four consecutive reduction indices of M_j per i
+// (M_j is stored in that order, scan_m_index: one 16-byte load per lane and
+// 1 KiB contiguous per wave) and its B operand four contiguous floats of the
+// transposed state in LDS.  The loads of M_{j+1} and S~_{j+1} are spread
+// over step j's products, and the state goes through LDS (double-buffered,
+// one barrier per step).
 // ---------------------------------------------------------------------------
+namespace {
+
+struct ScanIn {
+  f32x4 a[8][2]; // a[i][t][e] = M[32w + 16t + lane % 16][16 i + 4 kq + e]
+  float st[2][4]; // st[t][e] = S~[32w + 16t + 4 kq + e][col0 + lane % 16]
+  float warm[2];  // L2 warm-up loads of a later step (values unused)
+};
+
+constexpr int kScanLd = kD + 4; // LDS row stride (floats) of the transposed state
+
+} // namespace
+
 __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanDesc *__restrict__ descs,
-                                                        int32_t H,
+                                                        int32_t ndesc, int32_t H,
                                                         const float *__restrict__ Mseg,
                                                         const float *__restrict__ Stseg,
                                                         const float *__restrict__ init,
                                                         float *__restrict__ sin) {
-  static_assert(kScanBV == 8, "thread map assumes 8 columns");
-  __shared__ __attribute__((aligned(16))) float sS[kD][kScanBV];
-  const ScanDesc d = descs[blockIdx.x];
-  const int h = blockIdx.y;
-  const int col0 = blockIdx.z * kScanBV;
-  const int tid = threadIdx.x;
-  const int r = tid >> 1, cq = (tid & 1) * 4;
+  static_assert(kScanBV == 16 && kThreads == 256, "thread map assumes 16 columns, 4 waves");
+  constexpr int NCB = kD / kScanBV;
+  // Column blocks of one (sequence, head) sit 8 workgroup ids apart, so they
+  // run on one XCD and share its L2 copy of M_j and S~_j.
+  const int grp = blockIdx.x / (8 * NCB), rem = blockIdx.x - grp * 8 * NCB;
+  const int pair = 8 * grp + (rem & 7);
+  if (pair >= ndesc * H)
+    return;
+  const int di = pair / H, h = pair - di * H;
+  const ScanDesc d = descs[di];
+  const int col0 = (rem >> 3) * kScanBV;
+
+  __shared__ __attribute__((aligned(16))) float sT[2][kScanBV][kScanLd]; // [buf][col][row]
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = lane & 15, kq = lane >> 4;
   const int64_t mat = (int64_t)kD * kD;
 
-  f32x4 cur = {0.f, 0.f, 0.f, 0.f};
-  if (d.init_idx >= 0)
-    cur = *reinterpret_cast<const f32x4 *>(init + ((int64_t)d.init_idx * H + h) * mat +
-                                           r * kD + col0 + cq);
-  *reinterpret_cast<f32x4 *>(sin + ((int64_t)d.sin0 * H + h) * mat + r * kD + col0 + cq) = cur;
-  *reinterpret_cast<f32x4 *>(&sS[r][cq]) = cur;
-  __syncthreads();
-
-  for (int j = 0; j + 1 < d.nseg; ++j) {
-    const float *Mj = Mseg + ((int64_t)(d.pair0 + j) * H + h) * mat + r * kD;
-    const float *Sj = Stseg + ((int64_t)(d.pair0 + j) * H + h) * mat + r * kD;
-    f32x4 acc = *reinterpret_cast<const f32x4 *>(Sj + col0 + cq);
-#pragma unroll 4
-    for (int m = 0; m < kD; m += 4) {
-      const f32x4 mr = *reinterpret_cast<const f32x4 *>(Mj + m);
+  // entry state of segment 0: init (or zero) -> LDS and Sin[sin0]
+  {
+    const int m = tid >> 1, c0 = (tid & 1) * 8;
+    f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
+    if (d.init_idx >= 0) {
+      const float *src = init + ((int64_t)d.init_idx * H + h) * mat + m * kD + col0 + c0;
+      x0 = *reinterpret_cast<const f32x4 *>(src);
+      x1 = *reinterpret_cast<const f32x4 *>(src + 4);
+    }
+    float *dst = sin + ((int64_t)d.sin0 * H + h) * mat + m * kD + col0 + c0;
+    *reinterpret_cast<f32x4 *>(dst) = x0;
+    *reinterpret_cast<f32x4 *>(dst + 4) = x1;
 #pragma unroll
-      for (int mm = 0; mm < 4; ++mm)
-        acc += mr[mm] * *reinterpret_cast<const f32x4 *>(&sS[m + mm][cq]);
+    for (int c = 0; c < 4; ++c) {
+      sT[0][c0 + c][m] = x0[c];
+      sT[0][c0 + 4 + c][m] = x1[c];
+    }
+  }
+
+  const int nstep = d.nseg - 1;
+  const int cb = rem >> 3;
+  // Loads of step j in the order the products consume them.  The two warm-up
+  // loads touch step j + 1's lines of M (this column block's eighth) and of
+  // S~ (this block's columns), so that step's own loads, issued one step
+  // later, hit L2.
+  auto mat_at = [&](const float *base, int j) {
+    return base + ((int64_t)(d.pair0 + j) * H + h) * mat;
+  };
+  // the rest of step j's inputs: S~ and the two warm-up loads, which touch
+  // step j + 1's lines of M (this column block's eighth) and of S~ (this
+  // block's columns) so that its own loads, issued a step later, hit L2
+  auto load_rest = [&](ScanIn &in, int j) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float *sr = mat_at(Stseg, j) + (32 * w + 16 * t + 4 * kq) * kD + col0 + n;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        in.st[t][e] = sr[e * kD];
+    }
+    const int jw = min(j + 1, nstep - 1);
+    in.warm[0] = mat_at(Mseg, jw)[(cb * 64 + lane) * 32];
+    in.warm[1] = mat_at(Stseg, jw)[(tid & 127) * kD + col0];
+  };
+  // the A operands of k-group i, row tile t: 1 KiB block (8 w + i) * 2 + t
+  auto load_a = [&](ScanIn &in, const float *mj, int i) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      in.a[i][t] = *reinterpret_cast<const f32x4 *>(mj + ((8 * w + i) * 2 + t) * 256 + 4 * lane);
+  };
+  auto load = [&](ScanIn &in, int j) {
+    const float *mj = mat_at(Mseg, j);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      load_a(in, mj, i);
+    load_rest(in, j);
+  };
+  // step j: reads sT[j & 1], writes sT[(j + 1) & 1] and Sin[sin0 + j + 1];
+  // loads the inputs of step j + 1 (clamped: the last step reloads its own)
+  auto step = [&](const ScanIn &cur, ScanIn &nxt, int j) {
+    const int jn = min(j + 1, nstep - 1);
+    const float *mn = mat_at(Mseg, jn);
+    const float *src = &sT[j & 1][n][4 * kq];
+    f32x4 b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      b[i] = *reinterpret_cast<const f32x4 *>(src + 16 * i);
+    load_rest(nxt, jn);
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      load_a(nxt, mn, i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.a[i][t][e], b[i][e], acc[t], 0, 0, 0);
+    }
+    // issue order: the B reads, the S~ and warm-up loads of step j + 1, then
+    // two of its M loads per eight products
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 10, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
+    // the warm-up values are consumed (as nothing) only here, a step after
+    // their loads were issued
+    asm volatile("" ::"v"(cur.warm[0]), "v"(cur.warm[1]));
+    float *dst = sin + ((int64_t)(d.sin0 + j + 1) * H + h) * mat + col0 + n;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc[t][e] += cur.st[t][e];
+      const int r0 = 32 * w + 16 * t + 4 * kq;
+      *reinterpret_cast<f32x4 *>(&sT[(j + 1) & 1][n][r0]) = acc[t];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dst[(r0 + e) * kD] = acc[t][e];
     }
     __syncthreads();
-    *reinterpret_cast<f32x4 *>(&sS[r][cq]) = acc;
-    *reinterpret_cast<f32x4 *>(sin + ((int64_t)(d.sin0 + j + 1) * H + h) * mat + r * kD +
-                               col0 + cq) = acc;
-    __syncthreads();
+  };
+
+  ScanIn in0, in1;
+  load(in0, 0);
+  __syncthreads();
+  int j = 0;
+  for (; j + 2 <= nstep; j += 2) {
+    step(in0, in1, j);
+    step(in1, in0, j + 1);
   }
+  if (j < nstep)
+    step(in0, in1, j);
 }
 
-// ---------------------------------------------------------------------------
-// Launchers
-// ---------------------------------------------------------------------------
 hipError_t launch_k1(int elt, const ChunkDesc *chunks, int32_t nchunks, int32_t H,
                      const void *q, const void *k, const void *g, const void *beta, void *ws,
                      hipStream_t s) {
@@ -1087,44 +1217,52 @@ hipError_t launch_k1(int elt, const ChunkDesc *chunks, int32_t nchunks, int32_t 
   return hipGetLastError();
 }
 
-template <int BV>
+template <int BV, int NCT, int NB16>
 static void launch_k2_bv(int elt, int mode, const ChainDesc *chains, int32_t nchains,
                          int32_t H, const uint8_t *w, const void *v, void *o,
                          const float *init, const float *sin, float *final_a, float *final_b,
-                         hipStream_t s) {
-  const unsigned width = mode == 1 ? 2 * kD : kD;
-  dim3 grid((unsigned)nchains, (unsigned)H, width / BV), block(k2_threads(BV));
+                         int32_t mso, hipStream_t s) {
+  // bf16 records: NB16 LDS record buffers; fp32 records: one (two do not fit)
+  const int64_t npairs = (int64_t)nchains * H;
+  const int64_t ncb = (mode == 1 ? 2 * kD : kD) / BV;
+  dim3 grid((unsigned)((npairs + 7) / 8 * 8 * ncb)), block(k2_threads(BV, NCT));
+  const int32_t np = (int32_t)npairs;
   if (elt == 1) {
     if (mode == 1)
-      k2_kernel<bf16, 1, BV><<<grid, block, 0, s>>>(chains, H, w, (const bf16 *)v,
-                                                    (bf16 *)o, init, sin, final_a, final_b);
+      k2_kernel<bf16, 1, BV, NCT, NB16><<<grid, block, 0, s>>>(
+          chains, np, H, w, (const bf16 *)v, (bf16 *)o, init, sin, final_a, final_b, mso);
     else
-      k2_kernel<bf16, 0, BV><<<grid, block, 0, s>>>(chains, H, w, (const bf16 *)v,
-                                                    (bf16 *)o, init, sin, final_a, final_b);
+      k2_kernel<bf16, 0, BV, NCT, NB16><<<grid, block, 0, s>>>(
+          chains, np, H, w, (const bf16 *)v, (bf16 *)o, init, sin, final_a, final_b, mso);
   } else {
     if (mode == 1)
-      k2_kernel<float, 1, BV><<<grid, block, 0, s>>>(chains, H, w, (const float *)v,
-                                                     (float *)o, init, sin, final_a, final_b);
+      k2_kernel<float, 1, BV, NCT, 1><<<grid, block, 0, s>>>(
+          chains, np, H, w, (const float *)v, (float *)o, init, sin, final_a, final_b, mso);
     else
-      k2_kernel<float, 0, BV><<<grid, block, 0, s>>>(chains, H, w, (const float *)v,
-                                                     (float *)o, init, sin, final_a, final_b);
+      k2_kernel<float, 0, BV, NCT, 1><<<grid, block, 0, s>>>(
+          chains, np, H, w, (const float *)v, (float *)o, init, sin, final_a, final_b, mso);
   }
 }
 
 hipError_t launch_k2(int elt, int mode, const ChainDesc *chains, int32_t nchains, int32_t H,
                      const void *ws, const void *v, void *o, const float *init,
-                     const float *sin, float *final_a, float *final_b, hipStream_t s) {
+                     const float *sin, float *final_a, float *final_b, int m_scan_order,
+                     hipStream_t s) {
   if (nchains == 0)
     return hipSuccess;
+  const int32_t mso = mode == 1 && m_scan_order;
   const int64_t width = mode == 1 ? 2 * kD : kD;
   const int64_t wide_groups = (int64_t)nchains * H * (width / kBVWide);
   const uint8_t *w = (const uint8_t *)ws;
   if (wide_groups < kComputeUnits)
-    launch_k2_bv<kBVNarrow>(elt, mode, chains, nchains, H, w, v, o, init, sin, final_a,
-                            final_b, s);
-  else
-    launch_k2_bv<kBVWide>(elt, mode, chains, nchains, H, w, v, o, init, sin, final_a,
-                          final_b, s);
+    launch_k2_bv<kBVNarrow, 1, 2>(elt, mode, chains, nchains, H, w, v, o, init, sin, final_a,
+                                  final_b, mso, s);
+  else if (mode == 0 || wide_groups < kK2ThroughputGroups)
+    launch_k2_bv<kBVWide, 1, 2>(elt, mode, chains, nchains, H, w, v, o, init, sin, final_a,
+                                final_b, mso, s);
+  else // the segment pass of many segments: two single-buffered workgroups per CU
+    launch_k2_bv<kK2ThroughputBV, kK2ThroughputNCT, 1>(elt, mode, chains, nchains, H, w, v, o,
+                                                       init, sin, final_a, final_b, mso, s);
   return hipGetLastError();
 }
 
@@ -1132,8 +1270,9 @@ hipError_t launch_scan(const ScanDesc *descs, int32_t ndesc, int32_t H, const fl
                        const float *Stseg, const float *init, float *sin, hipStream_t s) {
   if (ndesc == 0)
     return hipSuccess;
-  dim3 grid((unsigned)ndesc, (unsigned)H, kD / kScanBV), block(kThreads);
-  scan_kernel<<<grid, block, 0, s>>>(descs, H, Mseg, Stseg, init, sin);
+  const int64_t pairs = (int64_t)ndesc * H;
+  const unsigned grid = (unsigned)((pairs + 7) / 8 * 8 * (kD / kScanBV));
+  scan_kernel<<<grid, kThreads, 0, s>>>(descs, ndesc, H, Mseg, Stseg, init, sin);
   return hipGetLastError();
 }
 

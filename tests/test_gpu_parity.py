@@ -86,6 +86,13 @@ def test_prefill_many_chains(dtype):
     prefill_vs_oracle([70, 130, 65], 96, dtype, 34, init=True)
 
 
+def test_prefill_fp32_many_chains_two_tiles_per_wave():
+    # 128 sequences x 4 heads: enough 128-column workgroups that each state
+    # wave carries two 16-column tiles
+    lengths = list(np.random.default_rng(77).integers(1, 140, size=128))
+    prefill_vs_oracle(lengths, 4, torch.float32, 78, init=True)
+
+
 @pytest.fixture(params=["fused", "two_kernel"])
 def bf16_path(request, monkeypatch):
     """Run a bf16 test through one prefill implementation (the library reads
