@@ -17,10 +17,17 @@ Two independent formulations live here:
   §六 written out in numpy fp64, used only to pin the recurrence (the two
   must agree to rounding).
 
+* :func:`gate_log_decay`, :func:`l2_normalize`, :func:`gated_rmsnorm` and
+  :func:`prefill_gated` -- the layer's steps on either side of the
+  recurrence (decay gate, q / k normalization, output norm and gate), plain
+  numpy fp64.
+
 Pins (tests marked ``not gpu``) tie the oracle to facts the pages and the
 mathematics fix: the literal product form, beta = 0 pure decay, linear
 attention, the delta rule's exact retrieval, the segment identity
-S = S~ + M S_in, and a hand-expanded dk = dv = 2 example.
+S = S~ + M S_in, and hand-expanded dk = dv = 2 examples (with and without
+the prologue and epilogue); the gate, norm and output-gate steps also
+against closed forms (sigmoid(0) = 1/2, sigmoid(ln 3) = 3/4, 3-4-5 rows).
 """
 from __future__ import annotations
 
@@ -236,3 +243,76 @@ def segment_transition(k, v, g, beta, cu_seglens=None, threads: int = 0):
     if rc != 0:
         raise RuntimeError("kda_oracle_segment failed (%d)" % rc)
     return M, St
+
+
+# ---------------------------------------------------------------------------
+# The layer's steps on either side of the recurrence: the decay gate and the
+# q / k normalization before it, the output norm and gate after it.  Plain
+# numpy fp64, elementwise or per (token, head) row.
+# ---------------------------------------------------------------------------
+
+G_MIN = -5.0
+
+
+def _sigmoid(x):
+    from scipy.special import expit
+    return expit(x)
+
+
+def gate_log_decay(z, A_log, g_min=G_MIN):
+    """Log decay from raw gate logits ("Kimi K3.1 Pro 架构完全拆解" §3.2):
+    ``g[t, h, c] = g_min * sigmoid(exp(A_log[h]) * z[t, h, c])``, which lies in
+    (g_min, 0); A_log is the per-head learned log scale, g_min = -5 fixed.
+    z ``[T, H, dk]``, A_log ``[H]``."""
+    z = _f64(z)
+    A = _f64(A_log).reshape(-1)
+    if z.ndim != 3 or A.size != z.shape[1]:
+        raise ValueError("z must be [T, H, dk] and A_log [H]")
+    return g_min * _sigmoid(np.exp(A)[None, :, None] * z)
+
+
+def l2_normalize(x, eps):
+    """L2 normalization of every (token, head) row of q or k over its dk
+    channels ("Kimi K3 的架構" §七: q and k are L2-normalized before KDA).
+    The pages give no epsilon; the reading here is x / sqrt(sum x^2 + eps)."""
+    x = _f64(x)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+def gated_rmsnorm(o, gate, weight=None, eps=1e-6):
+    """Output norm and gate ("Kimi K3.1 Pro 架构完全拆解" §3.3): a head-wise
+    RMSNorm of each (token, head) output row over its dv channels, then the
+    full-rank per-channel sigmoid gate (its logits W_g x are an input):
+    ``sigmoid(gate) * weight * o / sqrt(mean(o^2) + eps)``.  weight ``[dv]``
+    (None: ones) is the norm's per-channel scale."""
+    o = _f64(o)
+    gate = _f64(gate)
+    if gate.shape != o.shape:
+        raise ValueError("gate must have the shape of o")
+    w = np.ones(o.shape[-1]) if weight is None else _f64(weight).reshape(-1)
+    if w.size != o.shape[-1]:
+        raise ValueError("weight must have dv entries")
+    rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    return _sigmoid(gate) * w * (o / rms)
+
+
+def prefill_gated(q, k, v, beta, g=None, z=None, A_log=None, g_min=G_MIN, qk_norm_eps=None,
+                  out_gate=None, out_norm_weight=None, out_norm_eps=1e-6, cu_seqlens=None,
+                  initial_state=None, threads: int = 0):
+    """The recurrence with the layer's prologue and epilogue, in that order:
+    g from the gate logits z (when z is given, else g as passed), q and k
+    L2-normalized (when qk_norm_eps is not None), the recurrence, then the
+    output norm and gate (when out_gate is given).
+    Returns ``(o [T, H, dv], final [N, H, dk, dv])``."""
+    if (g is None) == (z is None):
+        raise ValueError("pass exactly one of g and z")
+    gg = gate_log_decay(z, A_log, g_min) if z is not None else g
+    qq, kk = q, k
+    if qk_norm_eps is not None:
+        qq = l2_normalize(q, qk_norm_eps)
+        kk = l2_normalize(k, qk_norm_eps)
+    o, fin = recurrence(qq, kk, v, gg, beta, cu_seqlens=cu_seqlens,
+                        initial_state=initial_state, threads=threads)
+    if out_gate is not None:
+        o = gated_rmsnorm(o, out_gate, out_norm_weight, out_norm_eps)
+    return o, fin

@@ -298,3 +298,121 @@ def test_replay_commit_depends_on_accepted_prefix_and_bonus_only():
     o1, c1 = oracle.decode_replay(S0, np.zeros(N, dtype=np.int32), *cached, *one)
     od, sd = oracle.decode_step(S0, *[x[:, 0] for x in new])
     assert np.array_equal(o1[:, 0], od) and np.array_equal(c1, sd)
+
+
+# --- prologue and epilogue --------------------------------------------------
+
+
+def test_gate_log_decay_closed_forms():
+    """g = g_min sigmoid(e^A z): sigmoid(0) = 1/2, sigmoid(ln 3) = 3/4,
+    sigmoid(-ln 3) = 1/4, and e^A scales z (A = ln 2 doubles it)."""
+    ln3 = np.log(3.0)
+    z = np.array([[[0.0, ln3, -ln3, ln3 / 2]], [[0.0, ln3, -ln3, ln3 / 2]]])  # [2, 1, 4]
+    g = oracle.gate_log_decay(z, [0.0])
+    np.testing.assert_allclose(g[0, 0], [-2.5, -3.75, -1.25, -5.0 / (1 + 3 ** -0.5)],
+                               rtol=0, atol=1e-14)
+    z2 = np.full((1, 2, 1), ln3 / 2)
+    g2 = oracle.gate_log_decay(z2, [np.log(2.0), 0.0])
+    np.testing.assert_allclose(g2[0, :, 0], [-3.75, -5.0 / (1 + 3 ** -0.5)], atol=1e-14)
+
+
+def test_gate_log_decay_range_and_limits():
+    """The log decay stays in (g_min, 0), so every retention factor is at
+    least e^-5 (the pages' bound), and tends to g_min / 0 at the ends.
+    (|e^A z| stays below ~30 here, where fp64 still resolves sigmoid < 1.)"""
+    rng = np.random.default_rng(7)
+    z = 2.0 * rng.standard_normal((64, 3, 16))
+    g = oracle.gate_log_decay(z, [0.3, -1.0, 1.2])
+    assert np.all(g < 0.0) and np.all(g > -5.0)
+    assert np.all(np.exp(g) > np.exp(-5.0))
+    ends = oracle.gate_log_decay(np.array([[[40.0, -40.0]]]), [0.0])
+    np.testing.assert_allclose(ends[0, 0], [-5.0, 0.0], atol=1e-15)
+    # a custom lower bound scales the whole gate
+    np.testing.assert_allclose(oracle.gate_log_decay(z, [0.3, -1.0, 1.2], g_min=-2.0),
+                               0.4 * g, rtol=1e-15)
+
+
+def test_l2_normalize_closed_forms():
+    x = np.zeros((1, 2, 4))
+    x[0, 0, :2] = [3.0, 4.0]
+    x[0, 1, :] = [1.0, 1.0, 1.0, 1.0]
+    y = oracle.l2_normalize(x, 0.0)
+    np.testing.assert_allclose(y[0, 0], [0.6, 0.8, 0.0, 0.0], atol=1e-16)
+    np.testing.assert_allclose(y[0, 1], [0.5] * 4, atol=1e-16)
+    # with eps the norm is sqrt(|x|^2 / (|x|^2 + eps)), along the same direction
+    ye = oracle.l2_normalize(x, 11.0)
+    np.testing.assert_allclose(np.linalg.norm(ye[0, 0]), np.sqrt(25.0 / 36.0), rtol=1e-15)
+    np.testing.assert_allclose(ye[0, 0], y[0, 0] * 5.0 / 6.0, atol=1e-16)
+    rng = np.random.default_rng(3)
+    z = rng.standard_normal((8, 3, 128))
+    np.testing.assert_allclose(np.linalg.norm(oracle.l2_normalize(z, 0.0), axis=-1), 1.0,
+                               rtol=1e-14)
+
+
+def test_gated_rmsnorm_closed_forms():
+    """RMSNorm over each row's channels (not across heads), then the gate."""
+    ln3 = np.log(3.0)
+    o = np.array([[[1.0, -1.0, 1.0, -1.0], [2.0, 2.0, 2.0, 2.0]]])  # [1, 2 heads, 4]
+    gate = np.array([[[0.0, ln3, -ln3, 0.0], [0.0, 0.0, 0.0, 0.0]]])
+    w = [1.0, 2.0, 3.0, 4.0]
+    y = oracle.gated_rmsnorm(o, gate, w, eps=0.0)
+    np.testing.assert_allclose(y[0, 0], [0.5, -1.5, 0.75, -2.0], atol=1e-15)
+    np.testing.assert_allclose(y[0, 1], [0.5, 1.0, 1.5, 2.0], atol=1e-15)
+    # eps enters under the root: mean(o^2) = 4, eps = 5 -> o / 3
+    ye = oracle.gated_rmsnorm(o, gate, None, eps=5.0)
+    np.testing.assert_allclose(ye[0, 1], [1.0 / 3.0] * 4, atol=1e-15)
+    # scale invariance of the norm (eps = 0) and RMS 1 under an open gate
+    rng = np.random.default_rng(5)
+    r = rng.standard_normal((6, 3, 128))
+    big = np.full_like(r, 40.0)
+    a = oracle.gated_rmsnorm(r, big, None, eps=0.0)
+    np.testing.assert_allclose(oracle.gated_rmsnorm(7.5 * r, big, None, eps=0.0), a, rtol=1e-13)
+    np.testing.assert_allclose(np.sqrt(np.mean(a * a, axis=-1)), 1.0, rtol=1e-13)
+
+
+def test_prefill_gated_hand_expanded():
+    """Two tokens, dk = dv = 2, written out by hand: q, k L2-normalized, g
+    from z (A = 0), the recurrence, then RMSNorm and the gate.  Head 1 runs
+    the same inputs scaled, so a norm taken across heads would fail."""
+    ln3 = np.log(3.0)
+    q = np.array([[[3.0, 4.0]], [[1.0, 1.0]]])
+    k = np.array([[[2.0, 0.0]], [[0.0, 5.0]]])
+    v = np.array([[[2.0, -2.0]], [[1.0, 1.0]]])
+    z = np.array([[[0.0, 0.0]], [[0.0, ln3]]])
+    beta = np.array([[0.5], [1.0]])
+    gate = np.array([[[ln3, 0.0]], [[0.0, -ln3]]])
+    w = np.array([2.0, 1.0])
+    # head 1: q, k scaled (normalization removes it), v scaled by 10
+    Q = np.concatenate([q, 3.0 * q], axis=1)
+    K = np.concatenate([k, 0.5 * k], axis=1)
+    V = np.concatenate([v, 10.0 * v], axis=1)
+    Z = np.concatenate([z, z], axis=1)
+    B = np.concatenate([beta, beta], axis=1)
+    G8 = np.concatenate([gate, gate], axis=1)
+    o, fin = oracle.prefill_gated(Q, K, V, B, z=Z, A_log=[0.0, 0.0], qk_norm_eps=0.0,
+                                  out_gate=G8, out_norm_weight=w, out_norm_eps=0.0)
+    # token 1: S = 0.5 [1,0]^T [2,-2];  o = S^T [.6,.8] = [0.6, -0.6] -> rms 0.6
+    np.testing.assert_allclose(o[0, 0], [0.75 * 2.0 * 1.0, 0.5 * 1.0 * -1.0], atol=1e-14)
+    # token 2: alpha = (e^-2.5, e^-3.75); S <- Diag(alpha) S = [[a, -a], [0, 0]];
+    # k = [0, 1]: w = 0, u = v; S += k u^T = [[a, -a], [1, 1]];
+    # o = S^T [1, 1] / sqrt 2 = [a + 1, 1 - a] / sqrt 2
+    a = np.exp(-2.5)
+    o2 = np.array([a + 1.0, 1.0 - a]) / np.sqrt(2.0)
+    rms = np.sqrt(np.mean(o2 * o2))
+    np.testing.assert_allclose(o[1, 0], [0.5 * 2.0 * o2[0] / rms, 0.25 * 1.0 * o2[1] / rms],
+                               atol=1e-14)
+    np.testing.assert_allclose(o[:, 1], o[:, 0], atol=1e-14)
+    np.testing.assert_allclose(fin[0, 0], [[a, -a], [1.0, 1.0]], atol=1e-14)
+    np.testing.assert_allclose(fin[0, 1], 10.0 * fin[0, 0], atol=1e-13)
+
+
+def test_prefill_gated_without_prologue_or_epilogue_is_the_recurrence():
+    q, k, v, g, beta = rand_inputs(40, 2, 8, 8, seed=9)
+    o0, f0 = oracle.recurrence(q, k, v, g, beta)
+    o1, f1 = oracle.prefill_gated(q, k, v, beta, g=g)
+    np.testing.assert_array_equal(o0, o1)
+    np.testing.assert_array_equal(f0, f1)
+    # unit-norm q, k: normalization with eps = 0 changes nothing but rounding
+    o2, f2 = oracle.prefill_gated(q, k, v, beta, g=g, qk_norm_eps=0.0)
+    np.testing.assert_allclose(o2, o0, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(f2, f0, rtol=1e-12, atol=1e-12)
