@@ -35,6 +35,7 @@ EXPORTED = (
     "kda_chunk_prefill_workspace_size",
     "kda_chunk_prefill",
     "kda_chunk_prefill_ckpt",
+    "kda_chunk_prefill_gated",
     "kda_decode_step",
     "kda_decode_replay",
     "kda_segment_transition_workspace_size",
@@ -77,6 +78,11 @@ def load():
         lib.kda_chunk_prefill_ckpt.restype = i32
         lib.kda_chunk_prefill_ckpt.argtypes = [i32, lp, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                                vp, vp, vp, i32, lp, i32, vp, vp, sz, vp]
+        lib.kda_chunk_prefill_gated.restype = i32
+        f32 = ctypes.c_float
+        lib.kda_chunk_prefill_gated.argtypes = [i32, lp, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                                vp, f32, f32, vp, vp, f32, vp, vp, vp, i32, vp,
+                                                sz, vp]
         lib.kda_decode_step.restype = i32
         lib.kda_decode_step.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.kda_decode_replay.restype = i32
@@ -193,8 +199,31 @@ def chunk_prefill_checkpoint(q, k, v, g, beta, cu_seqlens=None, initial_state=No
                     split_hint, o, final_state, workspace, int(align), pos0, checkpoint)
 
 
+def chunk_prefill_gated(q, k, v, g, beta, A_log=None, g_min: float = -5.0,
+                        qk_norm_eps: float = 0.0, out_gate=None, out_norm_weight=None,
+                        out_norm_eps: float = 1e-6, cu_seqlens=None, initial_state=None,
+                        output_final_state: bool = True, split_hint: int = 0, o=None,
+                        final_state=None, workspace=None):
+    """Prefill with the layer's prologue and epilogue fused in
+    (``kda_chunk_prefill_gated``).
+
+    ``A_log`` (fp32 ``[H]``): g holds raw gate logits and the log decay is
+    ``g_min * sigmoid(exp(A_log[h]) * g)``.  ``qk_norm_eps > 0``: q and k
+    rows are L2-normalized with that epsilon.  ``out_gate`` (``[T, H, 128]``,
+    q's dtype): o becomes ``sigmoid(out_gate) * w * o / sqrt(mean(o^2) +
+    out_norm_eps)`` with w = ``out_norm_weight`` (fp32 ``[128]``, None: ones).
+    Returns ``(o, final_state or None)``.
+    """
+    gated = (A_log, float(g_min), float(qk_norm_eps), out_gate, out_norm_weight,
+             float(out_norm_eps))
+    o, final_state, _, _ = _prefill(q, k, v, g, beta, cu_seqlens, initial_state,
+                                    output_final_state, split_hint, o, final_state, workspace,
+                                    gated=gated)
+    return o, final_state
+
+
 def _prefill(q, k, v, g, beta, cu_seqlens, initial_state, output_final_state, split_hint, o,
-             final_state, workspace, align=0, pos0=None, checkpoint=None):
+             final_state, workspace, align=0, pos0=None, checkpoint=None, gated=None):
     lib = load()
     if q.dim() == 4:
         if cu_seqlens is not None and q.shape[0] != 1:
@@ -202,6 +231,8 @@ def _prefill(q, k, v, g, beta, cu_seqlens, initial_state, output_final_state, sp
         B, T = q.shape[0], q.shape[1]
         q, k, v, g = (x.reshape(B * T, *x.shape[2:]) for x in (q, k, v, g))
         beta = beta.reshape(B * T, beta.shape[-1])
+        if gated is not None and gated[3] is not None:
+            gated = gated[:3] + (gated[3].reshape(B * T, *gated[3].shape[2:]),) + gated[4:]
         if cu_seqlens is None:
             cu_seqlens = np.arange(B + 1, dtype=np.int64) * T
     T, H, dk = k.shape
@@ -230,6 +261,24 @@ def _prefill(q, k, v, g, beta, cu_seqlens, initial_state, output_final_state, sp
                                                       split_hint))
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if gated is not None:
+        A_log, g_min, qk_eps, out_gate, nw, neps = gated
+        _check_device(A_log, out_gate, nw)
+        if A_log is not None and (A_log.dtype != torch.float32 or A_log.shape != (H,)):
+            raise ValueError("A_log must be fp32 [H]")
+        if out_gate is not None and (out_gate.dtype != dt or out_gate.shape != (T, H, dv)):
+            raise ValueError("out_gate must have o's dtype and shape")
+        if nw is not None and (nw.dtype != torch.float32 or nw.shape != (dv,)):
+            raise ValueError("out_norm_weight must be fp32 [dv]")
+        st = lib.kda_chunk_prefill_gated(N, _cu_ptr(cu), H, dk, dv, code, _ptr(q), _ptr(k),
+                                         _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log), g_min,
+                                         qk_eps, _ptr(out_gate), _ptr(nw), neps,
+                                         _ptr(initial_state), _ptr(o), _ptr(final_state),
+                                         int(split_hint), _ptr(workspace), workspace.numel(),
+                                         _stream_ptr(dev))
+        if st != KDA_OK:
+            raise KdaError(st, "kda_chunk_prefill_gated")
+        return o, final_state, None, None
     if align == 0:
         st = lib.kda_chunk_prefill(N, _cu_ptr(cu), H, dk, dv, code, _ptr(q), _ptr(k), _ptr(v),
                                    _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),

@@ -316,13 +316,15 @@ hipError_t upload_tables(const Plan &p, void *ws, hipStream_t stream) {
 
 namespace {
 
-// kda_chunk_prefill and kda_chunk_prefill_ckpt (ckpt_align = 0: no checkpoints)
+// kda_chunk_prefill, kda_chunk_prefill_ckpt (ckpt_align = 0: no checkpoints)
+// and kda_chunk_prefill_gated (prologue / epilogue on)
 kda_status prefill_impl(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_t H, int32_t dk,
                         int32_t dv, kda_dtype dt, const void *q, const void *k, const void *v,
                         const void *g, const void *beta, const float *initial_state, void *o,
                         float *final_state, int32_t split_hint, const int64_t *pos0,
                         int32_t ckpt_align, float *ckpt, void *workspace,
-                        size_t workspace_bytes, void *stream) {
+                        size_t workspace_bytes, void *stream, const Prologue &pro = Prologue(),
+                        const Epilogue &epi = Epilogue()) {
   if (dk != kD || dv != kD || (dt != KDA_F32 && dt != KDA_BF16))
     return KDA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || H < 1 || split_hint < 0 || !cu_seqlens_host)
@@ -350,6 +352,8 @@ kda_status prefill_impl(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_
   }
   if (!aligned16(initial_state) || !aligned16(final_state))
     return KDA_ERR_INVALID_ARG;
+  if (T > 0 && epi.on() && !aligned_elt(epi.gate, dt))
+    return KDA_ERR_INVALID_ARG;
   if (num_seqs == 0)
     return KDA_OK;
   if (p.total > 0) {
@@ -365,15 +369,16 @@ kda_status prefill_impl(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_
     if (e == hipSuccess)
       e = launch_fused((const ChainDesc *)(ws + p.off_chains), (int32_t)p.chains.size(), H, q,
                        k, v, g, beta, o, initial_state, nullptr, final_state,
-                       ckpt_align ? ckpt : nullptr, s);
+                       ckpt_align ? ckpt : nullptr, pro, epi, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
   }
   if (e == hipSuccess)
-    e = launch_k1(elt, d_chunks, (int32_t)p.chunks.size(), H, q, k, g, beta, ws + p.off_rec, s);
+    e = launch_k1(elt, d_chunks, (int32_t)p.chunks.size(), H, q, k, g, beta, ws + p.off_rec, pro,
+                  s);
   if (e == hipSuccess && !p.segchains.empty()) {
     e = launch_k2(elt, 1, (const ChainDesc *)(ws + p.off_seg), (int32_t)p.segchains.size(), H,
                   ws + p.off_rec, v, nullptr, nullptr, nullptr, (float *)(ws + p.off_St),
-                  (float *)(ws + p.off_M), /*m_scan_order=*/1, s);
+                  (float *)(ws + p.off_M), /*m_scan_order=*/1, Epilogue(), s);
     if (e == hipSuccess)
       e = launch_scan((const ScanDesc *)(ws + p.off_scan), (int32_t)p.scans.size(), H,
                       (const float *)(ws + p.off_M), (const float *)(ws + p.off_St),
@@ -382,7 +387,7 @@ kda_status prefill_impl(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_
   if (e == hipSuccess)
     e = launch_k2(elt, 0, (const ChainDesc *)(ws + p.off_chains), (int32_t)p.chains.size(), H,
                   ws + p.off_rec, v, o, initial_state, (const float *)(ws + p.off_Sin),
-                  final_state, ckpt_align ? ckpt : nullptr, 0, s);
+                  final_state, ckpt_align ? ckpt : nullptr, 0, epi, s);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -454,6 +459,39 @@ kda_status kda_chunk_prefill_ckpt(int32_t num_seqs, const int64_t *cu_seqlens_ho
   return prefill_impl(num_seqs, cu_seqlens_host, H, dk, dv, dt, q, k, v, g, beta, initial_state,
                       o, final_state, split_hint, pos0_host, ckpt_align, ckpt_state, workspace,
                       workspace_bytes, stream);
+}
+
+kda_status kda_chunk_prefill_gated(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_t H,
+                                   int32_t dk, int32_t dv, kda_dtype dt, const void *q,
+                                   const void *k, const void *v, const void *g, const void *beta,
+                                   const float *A_log, float g_min, float qk_norm_eps,
+                                   const void *out_gate, const float *out_norm_weight,
+                                   float out_norm_eps, const float *initial_state, void *o,
+                                   float *final_state, int32_t split_hint, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+  Prologue pro;
+  Epilogue epi;
+  if (A_log) {
+    // the chunk kernels' bound: every 16-token cumulative log decay >= -80
+    if (!(g_min >= -5.f && g_min < 0.f) || ((uintptr_t)A_log & 3u) != 0)
+      return KDA_ERR_INVALID_ARG;
+    pro.A_log = A_log;
+    pro.g_min = g_min;
+  }
+  if (!(qk_norm_eps >= 0.f) || qk_norm_eps > 3.0e38f)
+    return KDA_ERR_INVALID_ARG;
+  pro.qk_eps = qk_norm_eps;
+  if (out_gate) {
+    if (!(out_norm_eps > 0.f) || out_norm_eps > 3.0e38f ||
+        ((uintptr_t)out_norm_weight & 3u) != 0 || out_gate == o)
+      return KDA_ERR_INVALID_ARG;
+    epi.gate = out_gate;
+    epi.weight = out_norm_weight;
+    epi.eps = out_norm_eps;
+  }
+  return prefill_impl(num_seqs, cu_seqlens_host, H, dk, dv, dt, q, k, v, g, beta, initial_state,
+                      o, final_state, split_hint, nullptr, 0, nullptr, workspace,
+                      workspace_bytes, stream, pro, epi);
 }
 
 kda_status kda_decode_step(int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
@@ -560,10 +598,10 @@ kda_status kda_segment_transition(int32_t num_segs, const int64_t *cu_seglens_ho
   hipError_t e = upload_tables(p, ws, s);
   if (e == hipSuccess)
     e = launch_k1(elt, d_chunks, (int32_t)p.chunks.size(), H, nullptr, k, g, beta,
-                  ws + p.off_rec, s);
+                  ws + p.off_rec, Prologue(), s);
   if (e == hipSuccess)
     e = launch_k2(elt, 1, (const ChainDesc *)(ws + p.off_seg), (int32_t)p.segchains.size(), H,
-                  ws + p.off_rec, v, nullptr, nullptr, nullptr, S_tilde, M, 0, s);
+                  ws + p.off_rec, v, nullptr, nullptr, nullptr, S_tilde, M, 0, Epilogue(), s);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

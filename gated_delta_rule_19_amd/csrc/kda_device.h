@@ -229,6 +229,13 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// The bounded log decay from a raw gate logit z, g_min * sigmoid(ea z), with
+// ea = exp(A_h) the head's scale ("Kimi K3.1 Pro 架构完全拆解" §3.2).  Tends
+// to 0 as ea z -> -inf (exp overflows to inf, its reciprocal is 0).
+__device__ __forceinline__ float gate_log_decay(float z, float ea, float g_min) {
+  return g_min * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-(ea * z) * 1.4426950408889634f));
+}
+
 // Lane index as an opaque value: lane-dependent addresses built on it are
 // recomputed where they are used instead of being hoisted out of the chunk
 // loop and kept alive (or spilled) across all of its stages.

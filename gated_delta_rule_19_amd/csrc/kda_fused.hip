@@ -98,6 +98,9 @@ template <int NCT> struct FusedSmem {
   float L[kC][kLdL];       // L = StrictTril(Diag(beta) K_decay K_inv^T), fp32
   float Dinv[4][16][kLdB]; // inverted diagonal blocks of I + L
   float Beta[kC];
+  float Iq[kC], Ik[kC];    // prologue: 1 / |q|, 1 / |k| per token (stage A -> B)
+  float Red[4][kC];        // output norm: per state wave, partial sums of o^2 per token
+  float Scl[4][kC];        // output norm: each state wave's copy of the row scales
   float Fac[4][2][kD];     // per tile, log2 units: p_I, G_C - p_I
   float Foff[6][kD];       // e^{p_I - p_J} for the off-diagonal pairs
 };
@@ -109,12 +112,17 @@ __device__ __forceinline__ int off_pair(int I, int J) { return I * (I - 1) / 2 +
 
 } // namespace
 
-template <int NCT>
+// PRO: the prologue (gate logits -> log decay, q / k L2 norm) is compiled in;
+// which of its steps run is decided by A_log != null and qk_eps > 0.
+// EPI: o leaves through the output norm and gate.
+template <int NCT, bool PRO, bool EPI>
 __global__ __launch_bounds__(kFThreads) void fused_kernel(
     const ChainDesc *__restrict__ chains, int32_t H, const bf16 *__restrict__ q,
     const bf16 *__restrict__ k, const bf16 *__restrict__ v, const bf16 *__restrict__ g,
     const bf16 *__restrict__ beta, bf16 *__restrict__ o, const float *__restrict__ init,
-    const float *__restrict__ sin, float *__restrict__ final_state, float *__restrict__ ckpt) {
+    const float *__restrict__ sin, float *__restrict__ final_state, float *__restrict__ ckpt,
+    const float *__restrict__ A_log, float g_min, float qk_eps, const bf16 *__restrict__ ogate,
+    const float *__restrict__ onw, float oeps) {
   using Sm = FusedSmem<NCT>;
   __shared__ __attribute__((aligned(16))) Sm sm;
   constexpr int VW = 16 * NCT; // state columns per state wave
@@ -215,6 +223,62 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
     // U = INV Diag(beta) (V - W), O += M_qk U and store o, for chunk ch;
     // U is left packed in bu for the state update
     Frag<bf16> bu[NCT][2];
+    // O of chunk ch to o; with the output norm and gate ("Kimi K3.1 Pro 架构完全拆解"
+    // §3.3) once the state waves' partial sums are in LDS:
+    //   o = sigmoid(gate) w o / sqrt(mean(o^2) + eps) per token row
+    auto store_o = [&](int ch) {
+      const int ln = opaque_lane(), lr = ln & 15, lg = ln >> 4;
+      const int wcol = col0 + VW * wv + lr;
+      const int len = min(kC, cd.ntok - ch * kC);
+      const int64_t tok = cd.tok0 + (int64_t)ch * kC;
+      if constexpr (EPI) {
+        float tot = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          tot += sm.Red[w][ln];
+        sm.Scl[wv][ln] = __builtin_amdgcn_rsqf(tot * (1.f / kD) + oeps);
+        wave_lds_fence();
+        // one 16-column tile at a time (fewer live registers)
+        const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(
+            ogate + tok * rowstride + (int64_t)h * kD, (uint32_t)((len - 1) * rowstride + kD) * 2);
+        const int go = (int)((4 * lg * rowstride + wcol) * 2);
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) {
+          float gz[4][4];
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              gz[tt][i] = buffer_load1(rg, go + (int)((16 * tt + i) * rowstride * 2) + 32 * c,
+                                       (const bf16 *)nullptr);
+          const float wn = onw ? onw[wcol + 16 * c] : 1.f;
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            const f32x4 sc = *reinterpret_cast<const f32x4 *>(&sm.Scl[wv][16 * tt + 4 * lg]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float sg =
+                  __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-gz[tt][i] * kLog2e));
+              Oa[c][tt][i] *= sc[i] * wn * sg;
+            }
+          }
+        }
+      }
+      // rows past the chunk end fall outside the buffer and are dropped
+      const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(
+          o + tok * rowstride + (int64_t)h * kD, (uint32_t)((len - 1) * rowstride + kD) * 2);
+      const int vo = (int)((4 * lg * rowstride + wcol) * 2);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int so = (int)((16 * tt + i) * rowstride * 2); // wave-uniform
+#pragma unroll
+          for (int c = 0; c < NCT; ++c)
+            buffer_store(ro, static_cast<bf16>(Oa[c][tt][i]), vo + 32 * c, so);
+        }
+    };
+
     auto stage_u = [&](int ch) {
       const int ln = opaque_lane(), lr = ln & 15, lg = ln >> 4;
       const int wcol = col0 + VW * wv + lr;
@@ -280,19 +344,35 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
           for (int c = 0; c < NCT; ++c)
             mma(Oa[c][tt], am[tt], bu[c][s]);
       }
-      // rows past the chunk end fall outside the buffer and are dropped
-      const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(
-          o + tok * rowstride + (int64_t)h * kD, (uint32_t)((len - 1) * rowstride + kD) * 2);
-      const int vo = (int)((4 * lg * rowstride + wcol) * 2);
+      if constexpr (EPI) {
+        // output norm: this wave's sums of o^2 per token, reduce-scattered
+        // over the 16 lanes of a row group (lane lr ends with row tile
+        // lr / 4, row lr % 4), to LDS; o leaves after the next barrier
+        float x[16];
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+        for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int so = (int)((16 * tt + i) * rowstride * 2); // wave-uniform
+          for (int i = 0; i < 4; ++i) {
+            float a = 0.f;
 #pragma unroll
-          for (int c = 0; c < NCT; ++c)
-            buffer_store(ro, static_cast<bf16>(Oa[c][tt][i]), vo + 32 * c, so);
+            for (int c = 0; c < NCT; ++c)
+              a += Oa[c][tt][i] * Oa[c][tt][i];
+            x[4 * tt + i] = a;
+          }
+#pragma unroll
+        for (int st = 8; st >= 1; st >>= 1) {
+          const bool up = (lr & st) != 0;
+#pragma unroll
+          for (int m = 0; m < st; ++m) {
+            const float send = up ? x[m] : x[m + st];
+            const float keep = up ? x[m + st] : x[m];
+            x[m] = keep + __shfl_xor(send, st);
+          }
         }
+        sm.Red[wv][16 * (lr >> 2) + 4 * lg + (lr & 3)] = x[0];
+      } else {
+        store_o(ch);
+      }
     };
 
     // S = Diag(a_last) S + K_restore^T U (K = tokens), for the chunk whose
@@ -392,6 +472,8 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
       for (int ch = 0; ch + 1 < nch; ++ch) {
         stage_u(ch);
         lds_barrier();
+        if constexpr (EPI)
+          store_o(ch);
         stage_s();
         ckpt_store(ch);
         lds_barrier();
@@ -402,6 +484,8 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
       }
       stage_u(nch - 1);
       lds_barrier();
+      if constexpr (EPI)
+        store_o(nch - 1);
       stage_s();
       ckpt_store(nch - 1);
       lds_barrier();
@@ -451,6 +535,9 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
     };
     if (nch > 0)
       issue(0);
+    // prologue: the head's gate scale e^{A_h}
+    const bool gate_on = PRO && A_log != nullptr, qk_on = PRO && qk_eps > 0.f;
+    const float ea = gate_on ? __expf(A_log[h]) : 1.f;
 
     float xg[4][8];            // G_loc log2(e) per record channel
     Frag<bf16> fq[4], fk[4];   // Q_loc, K_loc fragments
@@ -465,14 +552,50 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
         const int lane = opaque_lane(), lr = lane & 15, lg = lane >> 4, r = 16 * pw + lr;
         // inclusive cumulative sum over the tile's tokens, then the tile
         // totals (lane 15 of each row) to LDS
+        float iq = 1.f, ik = 1.f; // 1 / |q|, 1 / |k| of this lane's token
+        if (qk_on) {
+          // the token's 128 channels sit in lanes lr, lr + 16, lr + 32, lr + 48
+          float sq = 0.f, sk = 0.f;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            float a[8], b[8];
+            widen8(rq[s], a);
+            widen8(rk[s], b);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              sq += a[j] * a[j];
+              sk += b[j] * b[j];
+            }
+          }
+          sq += __shfl_xor(sq, 16);
+          sk += __shfl_xor(sk, 16);
+          sq += __shfl_xor(sq, 32);
+          sk += __shfl_xor(sk, 32);
+          iq = __builtin_amdgcn_rsqf(sq + qk_eps);
+          ik = __builtin_amdgcn_rsqf(sk + qk_eps);
+          if (lg == 0) {
+            sm.Iq[r] = iq;
+            sm.Ik[r] = ik;
+          }
+        }
         float G[4][8];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < 4; ++s)
           widen8(rg[s], G[s]);
+        if (gate_on) {
+          // rows past the chunk end decay by nothing
+          const bool valid = r < min(kC, cd.ntok - it * kC);
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              G[s][j] = valid ? gate_log_decay(G[s][j], ea, g_min) : 0.f;
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
           for (int j = 0; j < 8; ++j)
             G[s][j] = row_scan16(G[s][j]);
-        }
         if (lr == 15) {
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
@@ -491,6 +614,13 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
           float qv[8], kv[8], xq[8], xk[8], xs[8];
           widen8(rq[s], qv);
           widen8(rk[s], kv);
+          if (qk_on) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              qv[j] *= iq;
+              kv[j] *= ik;
+            }
+          }
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const float x = G[s][j] * kLog2e;
@@ -568,6 +698,14 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
           load8f(&sm.Fac[pw][1][32 * s + 8 * lg], xc);
           widen8(rq[s], qv);
           widen8(rk[s], kv);
+          if (qk_on) {
+            const float iq = sm.Iq[r], ik = sm.Ik[r];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              qv[j] *= iq;
+              kv[j] *= ik;
+            }
+          }
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const float a = __builtin_amdgcn_exp2f(xg[s][j] + xp[j]); // e^{G}
@@ -691,15 +829,24 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
 hipError_t launch_fused(const ChainDesc *chains, int32_t nchains, int32_t H, const void *q,
                         const void *k, const void *v, const void *g, const void *beta, void *o,
                         const float *init, const float *sin, float *final_state, float *ckpt,
-                        hipStream_t s) {
+                        const Prologue &pro, const Epilogue &epi, hipStream_t s) {
   if (nchains == 0)
     return hipSuccess;
   // one workgroup per (chain, head) carries all 128 state columns
   constexpr int NCT = 2;
   dim3 grid((unsigned)nchains, (unsigned)H, kD / (64 * NCT)), block(kFThreads);
-  fused_kernel<NCT><<<grid, block, 0, s>>>(chains, H, (const bf16 *)q, (const bf16 *)k,
-                                           (const bf16 *)v, (const bf16 *)g, (const bf16 *)beta,
-                                           (bf16 *)o, init, sin, final_state, ckpt);
+  auto launch = [&](auto kern) {
+    kern<<<grid, block, 0, s>>>(chains, H, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v,
+                                (const bf16 *)g, (const bf16 *)beta, (bf16 *)o, init, sin,
+                                final_state, ckpt, pro.A_log, pro.g_min, pro.qk_eps,
+                                (const bf16 *)epi.gate, epi.weight, epi.eps);
+  };
+  if (epi.on())
+    launch(fused_kernel<NCT, true, true>);
+  else if (pro.on())
+    launch(fused_kernel<NCT, true, false>);
+  else
+    launch(fused_kernel<NCT, false, false>);
   return hipGetLastError();
 }
 

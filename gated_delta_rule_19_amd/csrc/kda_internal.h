@@ -104,31 +104,58 @@ __host__ __device__ constexpr int scan_m_index(int r, int m) {
           (r & 15)) * 4 + (m & 3);
 }
 
+// Steps of the layer fused into the chunk prep ("Kimi K3.1 Pro 架构完全拆解"
+// §3.2; "Kimi K3 的架構" §七):
+//   A_log != null : the g input holds raw gate logits z, and the log decay is
+//                   g_min * sigmoid(exp(A_log[h]) * z) (rows past a chunk's
+//                   end decay by nothing);
+//   qk_eps > 0    : q and k rows are L2-normalized, x / sqrt(sum x^2 + qk_eps).
+struct Prologue {
+  const float *A_log = nullptr;
+  float g_min = -5.f;
+  float qk_eps = 0.f;
+  bool on() const { return A_log != nullptr || qk_eps > 0.f; }
+};
+
+// Output norm and gate fused into the store of o ("Kimi K3.1 Pro 架构完全拆解"
+// §3.3): o <- sigmoid(gate) * weight * o / sqrt(mean(o^2) + eps) per
+// (token, head) row over its dv channels.  gate: [T, H, dv] of o's element
+// type; weight: [dv] fp32 or null (ones).
+struct Epilogue {
+  const void *gate = nullptr;
+  const float *weight = nullptr;
+  float eps = 1e-6f;
+  bool on() const { return gate != nullptr; }
+};
+
 // Launchers (enqueue only; return the hipGetLastError of the launch).
 hipError_t launch_k1(int elt, const ChunkDesc *chunks, int32_t nchunks, int32_t H,
                      const void *q, const void *k, const void *g, const void *beta, void *ws,
-                     hipStream_t s);
+                     const Prologue &pro, hipStream_t s);
 
 // Chunk prep for bf16 inputs (the records launch_k1 writes for elt == 1).
 hipError_t launch_prep_bf16(const ChunkDesc *chunks, int32_t nchunks, int32_t H, const void *q,
                             const void *k, const void *g, const void *beta, void *ws,
-                            hipStream_t s);
+                            const Prologue &pro, hipStream_t s);
 
 // mode 0: prefill/replay (width dv, writes o and exit states to final_a,
-//         and the chains' state checkpoints to final_b when it is not null);
+//         and the chains' state checkpoints to final_b when it is not null;
+//         with the epilogue on, o leaves normalized and gated and the whole
+//         dv-wide row is one workgroup's);
 // mode 1: segment pass (width dk + dv: [S~ | M], no o; S~ to final_a, M to
 //         final_b, row-major or, with m_scan_order, at scan_m_index).
 hipError_t launch_k2(int elt, int mode, const ChainDesc *chains, int32_t nchains, int32_t H,
                      const void *ws, const void *v, void *o, const float *init,
                      const float *sin, float *final_a, float *final_b, int m_scan_order,
-                     hipStream_t s);
+                     const Epilogue &epi, hipStream_t s);
 
 // Fused chunk prep + state chain (bf16, width dv): writes o, exit states and
-// (when ckpt is not null) the chains' state checkpoints.
+// (when ckpt is not null) the chains' state checkpoints; with the prologue
+// and the output epilogue.
 hipError_t launch_fused(const ChainDesc *chains, int32_t nchains, int32_t H, const void *q,
                         const void *k, const void *v, const void *g, const void *beta, void *o,
                         const float *init, const float *sin, float *final_state, float *ckpt,
-                        hipStream_t s);
+                        const Prologue &pro, const Epilogue &epi, hipStream_t s);
 
 hipError_t launch_scan(const ScanDesc *descs, int32_t ndesc, int32_t H, const float *Mseg,
                        const float *Stseg, const float *init, float *sin, hipStream_t s);

@@ -104,14 +104,14 @@ template <> struct Raw4<float> {
 // the L / M_qk products keep the same (permuted) channel order on both
 // sides, which leaves the sums over channels unchanged.
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k1_kernel(const ChunkDesc *__restrict__ chunks,
-                                                      int32_t H, const T *__restrict__ q,
-                                                      const T *__restrict__ k,
-                                                      const T *__restrict__ g,
-                                                      const T *__restrict__ beta,
-                                                      uint8_t *__restrict__ ws, int has_q,
-                                                      int32_t nitems) {
+// PRO: the prologue (gate logits -> log decay, q / k L2 norm) is compiled in;
+// which of its steps run is decided by A_log != null and qk_eps > 0.
+template <typename T, bool PRO>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k1_kernel(
+    const ChunkDesc *__restrict__ chunks, int32_t H, const T *__restrict__ q,
+    const T *__restrict__ k, const T *__restrict__ g, const T *__restrict__ beta,
+    uint8_t *__restrict__ ws, int has_q, int32_t nitems, const float *__restrict__ A_log,
+    float g_min, float qk_eps) {
   constexpr int LD = kD + 16 / (int)sizeof(T); // operand row stride: rows 16 B apart in banks
   constexpr size_t OPB = (size_t)kC * LD * sizeof(T);
   constexpr RecOff off(sizeof(T));
@@ -204,6 +204,47 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       Raw4<T>::widen(rwg[j][u], &gv[j][4 * u]);
   if (tid < kC)
     sBeta[tid] = rbeta;
+  // prologue: the log decay from the gate logits (rows past the chunk end
+  // decay by nothing), and 1 / |q|, 1 / |k| per row (a row's 128 channels
+  // are spread over 16 consecutive lanes, channel group t % 16)
+  float iq[4] = {1.f, 1.f, 1.f, 1.f}, ik[4] = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (PRO) {
+    if (A_log != nullptr) {
+      const float ea = __expf(A_log[h]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          gv[j][e] = row0 + j < len ? g_min / (1.f + __expf(-ea * gv[j][e])) : 0.f;
+    }
+    if (qk_eps > 0.f) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          float a[4], b[4];
+          Raw4<T>::widen(rwk[j][u], b);
+          if (has_q)
+            Raw4<T>::widen(rwq[j][u], a);
+          else
+            a[0] = a[1] = a[2] = a[3] = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sq += a[e] * a[e];
+            sk += b[e] * b[e];
+          }
+        }
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) {
+          sq += __shfl_xor(sq, m);
+          sk += __shfl_xor(sk, m);
+        }
+        iq[j] = 1.f / __builtin_sqrtf(sq + qk_eps);
+        ik[j] = 1.f / __builtin_sqrtf(sk + qk_eps);
+      }
+    }
+  }
 
   // ---- phase 1: inclusive cumulative log-decay per channel -------------
   // own rows, then the 4 row groups of the wave (lanes 16 apart), then the
@@ -317,6 +358,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         Raw4<T>::widen(rwq[j][u], qv);
       else
         qv[0] = qv[1] = qv[2] = qv[3] = 0.f;
+      if constexpr (PRO) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qv[e] *= iq[j];
+          kv[e] *= ik[j];
+        }
+      }
       float xq[4], xk[4], xs[4], xQ[4], xK[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -622,12 +670,16 @@ template <typename T, int NW> struct RecordCopy {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <typename T, int MODE, int BV, int NCT, int NBUF>
+// EPI: o leaves through the output norm and gate (mode 0, whole rows: the
+// workgroup carries all dv columns).
+template <typename T, int MODE, int BV, int NCT, int NBUF, bool EPI>
 __global__ __launch_bounds__(k2_threads(BV, NCT)) void k2_kernel(
     const ChainDesc *__restrict__ chains, int32_t npairs, int32_t H,
     const uint8_t *__restrict__ ws, const T *__restrict__ v, T *__restrict__ o,
     const float *__restrict__ init, const float *__restrict__ sin, float *__restrict__ out_a,
-    float *__restrict__ out_b, int32_t m_scan_order) {
+    float *__restrict__ out_b, int32_t m_scan_order, const T *__restrict__ ogate,
+    const float *__restrict__ onw, float oeps) {
+  static_assert(!EPI || (MODE == 0 && BV == kD), "the output norm needs whole rows");
   constexpr int NW = k2_threads(BV, NCT) / 64;
   using L = RecLds<T>;
   constexpr int RB = (int)k1_record_bytes(sizeof(T));
@@ -645,6 +697,10 @@ __global__ __launch_bounds__(k2_threads(BV, NCT)) void k2_kernel(
   constexpr bool VLDS = sizeof(T) == 2;
   constexpr int VW = 16 * NCT;
   __shared__ __attribute__((aligned(16))) T sv[VLDS ? NW : 1][VLDS ? kC * VW : 1];
+  // output norm: per-wave partial sums of squares of each token row, and each
+  // wave's own copy of the rows' scale factors
+  __shared__ __attribute__((aligned(16))) float sRed[EPI ? NW : 1][EPI ? kC : 1];
+  __shared__ __attribute__((aligned(16))) float sScl[EPI ? NW : 1][EPI ? kC : 1];
 
   // Workgroup -> (chain, head, column block): the column blocks of one
   // (chain, head) pair are 8 workgroups apart, so they run on the same XCD
@@ -742,6 +798,76 @@ __global__ __launch_bounds__(k2_threads(BV, NCT)) void k2_kernel(
     wait_vmem();
     __syncthreads();
 
+    // Output norm and gate of one chunk's O tile ("Kimi K3.1 Pro 架构完全拆解"
+    // §3.3): O[r][c] <- sigmoid(gate) w[c] O[r][c] / sqrt(mean_c O[r][c]^2 + eps).
+    // Lane (lr, lg) holds rows 16 tt + 4 lg + i of columns wcol + 16 c.  The
+    // sums of squares are reduce-scattered over the 16 lanes of a row group
+    // (lane lr ends with row tt = lr / 4, i = lr % 4), summed over the waves
+    // through LDS (one barrier), and every wave keeps its own copy of the 64
+    // scale factors.
+    [[maybe_unused]] float wnorm[NCT];
+    if constexpr (EPI) {
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+        wnorm[c] = onw ? onw[wcol + 16 * c] : 1.f;
+    }
+    [[maybe_unused]] auto norm_gate = [&](f32x4 (&Oa)[NCT][4], T (&gt)[EPI ? NCT : 1][4][4],
+                                          int64_t tok, int len) {
+      if constexpr (!VLDS) {
+        const T *gb = ogate + tok * rowstride + (int64_t)h * kD + wcol;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const T *gr = gb + (int64_t)min(16 * tt + 4 * lg + i, len - 1) * rowstride;
+#pragma unroll
+            for (int c = 0; c < NCT; ++c)
+              gt[c][tt][i] = gr[16 * c];
+          }
+      }
+      float x[16];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float a = 0.f;
+#pragma unroll
+          for (int c = 0; c < NCT; ++c)
+            a += Oa[c][tt][i] * Oa[c][tt][i];
+          x[4 * tt + i] = a;
+        }
+#pragma unroll
+      for (int st = 8; st >= 1; st >>= 1) {
+        const bool up = (lr & st) != 0;
+#pragma unroll
+        for (int m = 0; m < st; ++m) {
+          const float send = up ? x[m] : x[m + st];
+          const float keep = up ? x[m + st] : x[m];
+          x[m] = keep + __shfl_xor(send, st);
+        }
+      }
+      sRed[wv][16 * (lr >> 2) + 4 * lg + (lr & 3)] = x[0];
+      __syncthreads();
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+        tot += sRed[w][lane];
+      sScl[wv][lane] = __builtin_amdgcn_rsqf(tot * (1.f / kD) + oeps);
+      wave_lds_fence();
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const f32x4 sc = *reinterpret_cast<const f32x4 *>(&sScl[wv][16 * tt + 4 * lg]);
+#pragma unroll
+        for (int c = 0; c < NCT; ++c)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float z = to_f32(gt[c][tt][i]);
+            const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+            Oa[c][tt][i] *= sc[i] * wnorm[c] * sg;
+          }
+      }
+    };
+
     // One chunk: computes from the record image in `cur` while chunk ch+1's
     // record goes into `nxt`.  The buffers are distinct LDS objects and the
     // loop is unrolled by two, so every access names its buffer statically
@@ -754,6 +880,22 @@ __global__ __launch_bounds__(k2_threads(BV, NCT)) void k2_kernel(
       // chunk ch+1: its record straight into the other LDS buffer (fp32:
       // its v into registers); in flight while chunk ch is computed
       T vnxt[VLDS ? 1 : NCT][4][4];
+      // bf16: output gate logits of this chunk, first of all: the wait for
+      // them at the store of o then covers none of the loads below (fp32
+      // loads them at the store: its registers are full)
+      T gt[EPI ? NCT : 1][4][4];
+      if constexpr (EPI && VLDS) {
+        const T *gb = ogate + tok * rowstride + (int64_t)h * kD + wcol;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const T *gr = gb + (int64_t)min(16 * tt + 4 * lg + i, len - 1) * rowstride;
+#pragma unroll
+            for (int c = 0; c < NCT; ++c)
+              gt[c][tt][i] = gr[16 * c];
+          }
+      }
       // (v first: a wait the compiler places before these register loads
       // must not cover the record copy)
       if (more) {
@@ -913,6 +1055,8 @@ __global__ __launch_bounds__(k2_threads(BV, NCT)) void k2_kernel(
 #pragma unroll
             for (int c = 0; c < NCT; ++c)
               mma(Oa[c][tt], am[s][tt], bu[c][s]);
+        if constexpr (EPI)
+          norm_gate(Oa, gt, tok, len);
         // rows past the chunk end fall outside the buffer and are dropped
         const __amdgpu_buffer_rsrc_t ro =
             buffer_rsrc(o + tok * rowstride + (int64_t)h * kD,
@@ -1198,11 +1342,11 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanDesc *__restri
 
 hipError_t launch_k1(int elt, const ChunkDesc *chunks, int32_t nchunks, int32_t H,
                      const void *q, const void *k, const void *g, const void *beta, void *ws,
-                     hipStream_t s) {
+                     const Prologue &pro, hipStream_t s) {
   if (nchunks == 0)
     return hipSuccess;
   if (elt == 1)
-    return launch_prep_bf16(chunks, nchunks, H, q, k, g, beta, ws, s);
+    return launch_prep_bf16(chunks, nchunks, H, q, k, g, beta, ws, pro, s);
   // persistent grid: as many workgroups as are resident at once (LDS
   // limits fp32 to 1 per compute unit), each walking its items
   const int64_t nitems = (int64_t)nchunks * H;
@@ -1211,58 +1355,81 @@ hipError_t launch_k1(int elt, const ChunkDesc *chunks, int32_t nchunks, int32_t 
   // without q, k stands in as a readable buffer of the same shape
   const int has_q = q != nullptr;
   const void *qq = has_q ? q : k;
-  k1_kernel<float><<<grid, block, 0, s>>>(chunks, H, (const float *)qq, (const float *)k,
-                                            (const float *)g, (const float *)beta,
-                                            (uint8_t *)ws, has_q, (int32_t)nitems);
+  auto launch = [&](auto kern) {
+    kern<<<grid, block, 0, s>>>(chunks, H, (const float *)qq, (const float *)k,
+                                (const float *)g, (const float *)beta, (uint8_t *)ws, has_q,
+                                (int32_t)nitems, pro.A_log, pro.g_min, pro.qk_eps);
+  };
+  if (pro.on())
+    launch(k1_kernel<float, true>);
+  else
+    launch(k1_kernel<float, false>);
   return hipGetLastError();
 }
 
-template <int BV, int NCT, int NB16>
+template <int BV, int NCT, int NB16, bool EPI>
 static void launch_k2_bv(int elt, int mode, const ChainDesc *chains, int32_t nchains,
                          int32_t H, const uint8_t *w, const void *v, void *o,
                          const float *init, const float *sin, float *final_a, float *final_b,
-                         int32_t mso, hipStream_t s) {
+                         int32_t mso, const Epilogue &epi, hipStream_t s) {
   // bf16 records: NB16 LDS record buffers; fp32 records: one (two do not fit)
   const int64_t npairs = (int64_t)nchains * H;
   const int64_t ncb = (mode == 1 ? 2 * kD : kD) / BV;
   dim3 grid((unsigned)((npairs + 7) / 8 * 8 * ncb)), block(k2_threads(BV, NCT));
   const int32_t np = (int32_t)npairs;
+  // with the output epilogue, bf16 runs one tile per wave (8 waves) and fp32
+  // two (4 waves: a wave per SIMD, whose registers its fp32 fragments need)
+  constexpr bool kBf16 = !EPI || NCT == 1, kF32 = !EPI || NCT == 2;
   if (elt == 1) {
+    if constexpr (kBf16) {
     if (mode == 1)
-      k2_kernel<bf16, 1, BV, NCT, NB16><<<grid, block, 0, s>>>(
-          chains, np, H, w, (const bf16 *)v, (bf16 *)o, init, sin, final_a, final_b, mso);
+      k2_kernel<bf16, 1, BV, NCT, NB16, false><<<grid, block, 0, s>>>(
+          chains, np, H, w, (const bf16 *)v, (bf16 *)o, init, sin, final_a, final_b, mso,
+          nullptr, nullptr, 0.f);
     else
-      k2_kernel<bf16, 0, BV, NCT, NB16><<<grid, block, 0, s>>>(
-          chains, np, H, w, (const bf16 *)v, (bf16 *)o, init, sin, final_a, final_b, mso);
-  } else {
+      k2_kernel<bf16, 0, BV, NCT, NB16, EPI><<<grid, block, 0, s>>>(
+          chains, np, H, w, (const bf16 *)v, (bf16 *)o, init, sin, final_a, final_b, mso,
+          (const bf16 *)epi.gate, epi.weight, epi.eps);
+    }
+  } else if constexpr (kF32) {
     if (mode == 1)
-      k2_kernel<float, 1, BV, NCT, 1><<<grid, block, 0, s>>>(
-          chains, np, H, w, (const float *)v, (float *)o, init, sin, final_a, final_b, mso);
+      k2_kernel<float, 1, BV, NCT, 1, false><<<grid, block, 0, s>>>(
+          chains, np, H, w, (const float *)v, (float *)o, init, sin, final_a, final_b, mso,
+          nullptr, nullptr, 0.f);
     else
-      k2_kernel<float, 0, BV, NCT, 1><<<grid, block, 0, s>>>(
-          chains, np, H, w, (const float *)v, (float *)o, init, sin, final_a, final_b, mso);
+      k2_kernel<float, 0, BV, NCT, 1, EPI><<<grid, block, 0, s>>>(
+          chains, np, H, w, (const float *)v, (float *)o, init, sin, final_a, final_b, mso,
+          (const float *)epi.gate, epi.weight, epi.eps);
   }
 }
 
 hipError_t launch_k2(int elt, int mode, const ChainDesc *chains, int32_t nchains, int32_t H,
                      const void *ws, const void *v, void *o, const float *init,
                      const float *sin, float *final_a, float *final_b, int m_scan_order,
-                     hipStream_t s) {
+                     const Epilogue &epi, hipStream_t s) {
   if (nchains == 0)
     return hipSuccess;
   const int32_t mso = mode == 1 && m_scan_order;
   const int64_t width = mode == 1 ? 2 * kD : kD;
   const int64_t wide_groups = (int64_t)nchains * H * (width / kBVWide);
   const uint8_t *w = (const uint8_t *)ws;
-  if (wide_groups < kComputeUnits)
-    launch_k2_bv<kBVNarrow, 1, 2>(elt, mode, chains, nchains, H, w, v, o, init, sin, final_a,
-                                  final_b, mso, s);
+  if (mode == 0 && epi.on()) { // the output norm needs whole rows: the wide block
+    if (elt == 1)
+      launch_k2_bv<kBVWide, 1, 2, true>(elt, mode, chains, nchains, H, w, v, o, init, sin,
+                                        final_a, final_b, mso, epi, s);
+    else
+      launch_k2_bv<kBVWide, 2, 1, true>(elt, mode, chains, nchains, H, w, v, o, init, sin,
+                                        final_a, final_b, mso, epi, s);
+  }
+  else if (wide_groups < kComputeUnits)
+    launch_k2_bv<kBVNarrow, 1, 2, false>(elt, mode, chains, nchains, H, w, v, o, init, sin,
+                                         final_a, final_b, mso, epi, s);
   else if (mode == 0 || wide_groups < kK2ThroughputGroups)
-    launch_k2_bv<kBVWide, 1, 2>(elt, mode, chains, nchains, H, w, v, o, init, sin, final_a,
-                                final_b, mso, s);
+    launch_k2_bv<kBVWide, 1, 2, false>(elt, mode, chains, nchains, H, w, v, o, init, sin,
+                                       final_a, final_b, mso, epi, s);
   else // the segment pass of many segments: two single-buffered workgroups per CU
-    launch_k2_bv<kK2ThroughputBV, kK2ThroughputNCT, 1>(elt, mode, chains, nchains, H, w, v, o,
-                                                       init, sin, final_a, final_b, mso, s);
+    launch_k2_bv<kK2ThroughputBV, kK2ThroughputNCT, 1, false>(
+        elt, mode, chains, nchains, H, w, v, o, init, sin, final_a, final_b, mso, epi, s);
   return hipGetLastError();
 }
 

@@ -119,10 +119,14 @@ __device__ __forceinline__ void rec_store8(__amdgpu_buffer_rsrc_t r, int e, cons
 
 } // namespace
 
+// PRO: the prologue (gate logits -> log decay, q / k L2 norm) is compiled in;
+// which of its steps run is decided by A_log != null and qk_eps > 0.
+template <bool PRO>
 __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2))) void prep_kernel(
     const ChunkDesc *__restrict__ chunks, int32_t H, const bf16 *__restrict__ q,
     const bf16 *__restrict__ k, const bf16 *__restrict__ g, const bf16 *__restrict__ beta,
-    uint8_t *__restrict__ ws, int has_q, int32_t nitems) {
+    uint8_t *__restrict__ ws, int has_q, int32_t nitems, const float *__restrict__ A_log,
+    float g_min, float qk_eps) {
   __shared__ __attribute__((aligned(16))) PrepSmem sm;
   const int pw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // token tile
   const int64_t rowstride = (int64_t)H * kD;
@@ -144,10 +148,19 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2)
 
   u32x4 rg[4], rq[4], rk[4];
   unsigned short rbeta = 0;
+  // prologue: the head's gate log scale, and whether this lane's token is
+  // inside the chunk (rows past its end must not decay)
+  const bool gate_on = PRO && A_log != nullptr, qk_on = PRO && qk_eps > 0.f;
+  float rA = 0.f;
+  bool rvalid = true;
   auto issue = [&](int item) {
     const int ln = opaque_lane(), lr = ln & 15, lg = ln >> 4, r = 16 * pw + lr;
     const int ci = item / H, h = item - ci * H;
     const ChunkDesc cd = chunks[ci];
+    if (gate_on) {
+      rA = A_log[h];
+      rvalid = r < cd.len;
+    }
     const int64_t base = cd.tok0 * rowstride + (int64_t)h * kD;
     const uint32_t nbytes = (uint32_t)(((cd.len - 1) * rowstride + kD) * 2);
     const __amdgpu_buffer_rsrc_t bg = buffer_rsrc(g + base, nbytes);
@@ -188,11 +201,43 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2)
     // the tile totals (lane 15 of each row) to LDS
     float G[4][8];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < 4; ++s)
       widen8(rg[s], G[s]);
+    if (gate_on) {
+      const float ea = __builtin_amdgcn_exp2f(rA * kL2e);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          G[s][j] = rvalid ? gate_log_decay(G[s][j], ea, g_min) : 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         G[s][j] = row_scan16(G[s][j]);
+    // prologue: 1 / |q|, 1 / |k| of this lane's token (its 128 channels are
+    // spread over the four lanes lr, lr + 16, lr + 32, lr + 48)
+    float iq = 1.f, ik = 1.f;
+    if (qk_on) {
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float a[8], b[8];
+        widen8(rq[s], a);
+        widen8(rk[s], b);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          sq += a[j] * a[j];
+          sk += b[j] * b[j];
+        }
+      }
+      sq += __shfl_xor(sq, 16);
+      sk += __shfl_xor(sk, 16);
+      sq += __shfl_xor(sq, 32);
+      sk += __shfl_xor(sk, 32);
+      iq = __builtin_amdgcn_rsqf(sq + qk_eps);
+      ik = __builtin_amdgcn_rsqf(sk + qk_eps);
     }
     if (lr == 15) {
 #pragma unroll
@@ -213,6 +258,13 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2)
       float qv[8], kv[8], xq[8], xk[8], xs[8];
       widen8(rq[s], qv);
       widen8(rk[s], kv);
+      if (qk_on) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          qv[j] *= iq;
+          kv[j] *= ik;
+        }
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float x = G[s][j] * kL2e;
@@ -537,7 +589,7 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2)
 
 hipError_t launch_prep_bf16(const ChunkDesc *chunks, int32_t nchunks, int32_t H, const void *q,
                             const void *k, const void *g, const void *beta, void *ws,
-                            hipStream_t s) {
+                            const Prologue &pro, hipStream_t s) {
   if (nchunks == 0)
     return hipSuccess;
   // persistent grid: two workgroups per compute unit are resident (LDS)
@@ -546,9 +598,15 @@ hipError_t launch_prep_bf16(const ChunkDesc *chunks, int32_t nchunks, int32_t H,
   dim3 grid((unsigned)std::min(nitems, resident)), block(kPrepThreads);
   // without q, k stands in as a readable buffer of the same shape
   const int has_q = q != nullptr;
-  prep_kernel<<<grid, block, 0, s>>>(chunks, H, (const bf16 *)(has_q ? q : k), (const bf16 *)k,
-                                     (const bf16 *)g, (const bf16 *)beta, (uint8_t *)ws, has_q,
-                                     (int32_t)nitems);
+  auto launch = [&](auto kern) {
+    kern<<<grid, block, 0, s>>>(chunks, H, (const bf16 *)(has_q ? q : k), (const bf16 *)k,
+                                (const bf16 *)g, (const bf16 *)beta, (uint8_t *)ws, has_q,
+                                (int32_t)nitems, pro.A_log, pro.g_min, pro.qk_eps);
+  };
+  if (pro.on())
+    launch(prep_kernel<true>);
+  else
+    launch(prep_kernel<false>);
   return hipGetLastError();
 }
 

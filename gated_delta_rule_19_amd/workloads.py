@@ -99,6 +99,24 @@ def token_inputs(T: int, H: int, dtype: torch.dtype, seed: int, device="cpu",
     return out
 
 
+def raw_layer_inputs(T: int, H: int, dtype: torch.dtype, seed: int, device="cpu"):
+    """Raw inputs of the KDA layer around the recurrence, all drawn at random
+    (none of the layer's own arithmetic): q, k ``[T, H, 128]`` ~ N(0, 1), not
+    normalized; v ~ N(0, 1); z, the decay gate's logits, ~ N(0, 1); beta =
+    sigmoid(N(0, 1)); the output gate's logits ``[T, H, 128]`` ~ N(0, 1);
+    A_log fp32 ``[H]`` ~ U(-1, 1) (per-head log scale); norm_weight fp32
+    ``[128]`` ~ 1 + 0.1 N(0, 1)."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    f = dict(dtype=torch.float32, device=device, generator=gen)
+    out = {n: torch.randn((T, H, D), **f).to(dtype) for n in ("q", "k", "v", "z", "out_gate")}
+    out["beta"] = torch.sigmoid(torch.randn((T, H), **f)).to(dtype)
+    out["A_log"] = torch.rand((H,), **f) * 2.0 - 1.0
+    out["norm_weight"] = 1.0 + 0.1 * torch.randn((D,), **f)
+    return out
+
+
 def states(N: int, H: int, seed: int, device="cpu", std: float = 0.1) -> torch.Tensor:
     """fp32 states ``[N, H, 128, 128]`` ~ N(0, std^2)."""
     device = torch.device(device)

@@ -170,6 +170,44 @@ kda_status kda_chunk_prefill_ckpt(int32_t num_seqs, const int64_t *cu_seqlens_ho
                                   size_t workspace_bytes, void *stream);
 
 /*
+ * kda_chunk_prefill with the layer's steps on either side of the recurrence
+ * fused into its kernels, so that none of them costs a pass over [T, H, d]:
+ *
+ *   before ("Kimi K3.1 Pro 架构完全拆解" §3.2; "Kimi K3 的架構" §七)
+ *     A_log != NULL : g holds the raw gate logits z, and the log decay is
+ *                     g_min * sigmoid(exp(A_log[h]) * z), in (g_min, 0).
+ *                     A_log: DEVICE [H] fp32, the per-head log scale;
+ *                     g_min: -5 <= g_min < 0 (the pages fix -5).
+ *                     A_log == NULL: g is the log decay, g_min is ignored.
+ *     qk_norm_eps > 0 : each (token, head) row of q and of k is divided by
+ *                     sqrt(sum of its squares + qk_norm_eps) first;
+ *                     qk_norm_eps == 0: q and k are used as given.
+ *   after ("Kimi K3.1 Pro 架构完全拆解" §3.3)
+ *     out_gate != NULL : each (token, head) row of the output over its dv
+ *                     channels is replaced by
+ *                       sigmoid(out_gate) * w * o / sqrt(mean(o^2) + out_norm_eps)
+ *                     out_gate: [T_total, H, dv] of type dt, the logits of
+ *                     the full-rank output gate (its projection is not
+ *                     done here), must not overlap o; out_norm_weight: DEVICE
+ *                     [dv] fp32 (w), or NULL for ones; out_norm_eps > 0.
+ *                     out_gate == NULL: o is the recurrence output.
+ *
+ * final_state is the state of the recurrence (it is not normalized).
+ * Everything else, the workspace size included, is as for kda_chunk_prefill.
+ * Invalid values (g_min outside [-5, 0), a negative or non-finite
+ * qk_norm_eps, out_norm_eps <= 0 with a gate, misaligned pointers) return
+ * KDA_ERR_INVALID_ARG before anything is enqueued.
+ */
+kda_status kda_chunk_prefill_gated(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_t H,
+                                   int32_t dk, int32_t dv, kda_dtype dt, const void *q,
+                                   const void *k, const void *v, const void *g, const void *beta,
+                                   const float *A_log, float g_min, float qk_norm_eps,
+                                   const void *out_gate, const float *out_norm_weight,
+                                   float out_norm_eps, const float *initial_state, void *o,
+                                   float *final_state, int32_t split_hint, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
+/*
  * One decode step for N independent sequences, updating the state IN PLACE
  * ("Kimi K3 的架構" (hao.cnyes.com), §六, the alternative form the decode
  * kernel follows; "Kimi K3.1 Pro 架构完全拆解" §3.4, state updated in place):

@@ -233,3 +233,30 @@ def test_binding_rejects_cpu_tensors(lib):
     x = torch.zeros(4, 2, 128)
     with pytest.raises(ValueError):
         nat.chunk_prefill(x, x, x, x, torch.zeros(4, 2))
+
+
+def test_gated_prefill_argument_errors(lib):
+    E = nat
+    a, p = cu(0, 256, 700)
+    GATE = ctypes.c_void_p(0x200000)
+    nan, inf = float("nan"), float("inf")
+
+    def run(A=FAKE, gmin=-5.0, qe=1e-6, og=GATE, w=None, oe=1e-6, o=FAKE, n=2, dk=128):
+        return lib.kda_chunk_prefill_gated(n, p, 2, dk, 128, nat.KDA_BF16, FAKE, FAKE, FAKE,
+                                           FAKE, FAKE, A, gmin, qe, og, w, oe, None, o, None, 0,
+                                           FAKE, 1 << 30, None)
+
+    assert run(dk=64) == E.KDA_ERR_UNSUPPORTED
+    for gmin in (-5.5, 0.0, 1.0, nan, -inf):           # the log decay must stay in [-5, 0)
+        assert run(gmin=gmin) == E.KDA_ERR_INVALID_ARG
+    assert run(A=ctypes.c_void_p(0x100002)) == E.KDA_ERR_INVALID_ARG   # fp32 alignment
+    for qe in (-1e-6, nan, inf):
+        assert run(qe=qe) == E.KDA_ERR_INVALID_ARG
+    for oe in (0.0, -1.0, nan, inf):                   # the output norm needs eps > 0
+        assert run(oe=oe) == E.KDA_ERR_INVALID_ARG
+    assert run(w=ctypes.c_void_p(0x100002)) == E.KDA_ERR_INVALID_ARG
+    assert run(og=ctypes.c_void_p(0x200001)) == E.KDA_ERR_INVALID_ARG  # bf16 alignment
+    assert run(og=FAKE) == E.KDA_ERR_INVALID_ARG       # the gate may not be o itself
+    assert run(n=0) == E.KDA_OK
+    # with a step off, its parameters are not looked at
+    assert run(A=None, gmin=nan, og=None, oe=nan, n=0) == E.KDA_OK

@@ -1,0 +1,180 @@
+"""GPU parity of the gated prefill (kda_chunk_prefill_gated): the decay gate
+and the q / k L2 norm fused into the chunk prep, the output RMSNorm and
+sigmoid gate fused into the store of o, against the fp64 oracle's
+prefill_gated on the same seeded raw inputs.
+
+Bar: the final states, and o without the output gate, meet the plain
+prefill's bar max|x - x_ref| <= tol * max|x_ref| (tol = 1e-2 for bf16 inputs,
+1e-4 for fp32).  o through the output norm and gate, y = s o~ / r with
+s = w sigmoid(gate) and r = sqrt(mean(o~^2) + eps) per row, meets that bar
+too for fp32; for bf16 it meets the bound the plain bar implies through the
+norm: with E = tol * max|o~_ref| the recurrence output's error,
+    |y - y_ref| <= |s| E (1 + |o~_ref| / r_ref) / r_ref + 2^-8 |y_ref|
+(|r - r_ref| <= rms of the error <= E; the last term is y's bf16 rounding).
+A row whose output is small against the sequence's largest one is scaled up
+by the norm, and with it its share of the recurrence's bf16 error.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import gated_delta_rule_19_amd as kda
+from gated_delta_rule_19_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = {torch.float32: 1e-4, torch.bfloat16: 1e-2}
+DTYPES = [torch.float32, torch.bfloat16]
+QK_EPS = 1e-6
+OUT_EPS = 1e-6
+
+
+def rel_err(x, ref):
+    x = x.detach().cpu().double().numpy() if isinstance(x, torch.Tensor) else x
+    assert x.shape == ref.shape
+    assert np.all(np.isfinite(x))
+    return float(np.max(np.abs(x - ref)) / max(float(np.max(np.abs(ref))), 1e-30))
+
+
+def gated_vs_oracle(lengths, H, dtype, seed, gate=True, qk=True, epi=True, weight=True,
+                    init=False, split=0):
+    print("gated case", dict(lengths=lengths, H=H, dtype=str(dtype), seed=seed, gate=gate,
+                             qk=qk, epi=epi, init=init, split=split), flush=True)
+    cu = wl.cu_from_lengths(lengths)
+    T = int(cu[-1])
+    d = wl.raw_layer_inputs(T, H, dtype, seed, device=DEV)
+    if not gate:  # a plain log decay in place of the logits
+        d["z"] = wl.token_inputs(T, H, dtype, seed + 5, device=DEV)["g"]
+    if not qk:    # unit rows, as the plain prefill takes them
+        u = wl.token_inputs(T, H, dtype, seed + 6, device=DEV)
+        d["q"], d["k"] = u["q"], u["k"]
+    S0 = wl.states(len(lengths), H, seed + 1, device=DEV) if init else None
+    nw = d["norm_weight"] if weight else None
+    o, fin = kda.chunk_prefill_gated(
+        d["q"], d["k"], d["v"], d["z"], d["beta"], A_log=d["A_log"] if gate else None,
+        qk_norm_eps=QK_EPS if qk else 0.0, out_gate=d["out_gate"] if epi else None,
+        out_norm_weight=nw, out_norm_eps=OUT_EPS, cu_seqlens=cu, initial_state=S0,
+        split_hint=split)
+    torch.cuda.synchronize()
+    kw = dict(g=None, z=d["z"], A_log=d["A_log"]) if gate else dict(g=d["z"])
+    o_ref, f_ref = oracle.prefill_gated(
+        d["q"], d["k"], d["v"], d["beta"], qk_norm_eps=QK_EPS if qk else None,
+        out_gate=d["out_gate"] if epi else None, out_norm_weight=nw, out_norm_eps=OUT_EPS,
+        cu_seqlens=cu, initial_state=S0, **kw)
+    if T > 0:
+        if epi and dtype == torch.bfloat16:
+            check_gated_bound(o, o_ref, d, nw, kw, qk, cu, S0, dtype)
+        else:
+            eo = rel_err(o, o_ref)
+            assert eo <= TOL[dtype], ("o", eo)
+    ef = rel_err(fin, f_ref)
+    assert ef <= TOL[dtype], ("final", ef)
+    return o, fin
+
+
+def check_gated_bound(o, y_ref, d, nw, kw, qk, cu, S0, dtype):
+    """The bf16 bound above, element by element."""
+    ot_ref, _ = oracle.prefill_gated(d["q"], d["k"], d["v"], d["beta"],
+                                     qk_norm_eps=QK_EPS if qk else None, cu_seqlens=cu,
+                                     initial_state=S0, **kw)
+    E = TOL[dtype] * float(np.max(np.abs(ot_ref)))
+    r = np.sqrt(np.mean(ot_ref * ot_ref, axis=-1, keepdims=True) + OUT_EPS)
+    gate = d["out_gate"].detach().cpu().double().numpy()
+    w = np.ones(ot_ref.shape[-1]) if nw is None else nw.detach().cpu().double().numpy()
+    s = np.abs(w / (1.0 + np.exp(-gate)))
+    bound = s * E * (1.0 + np.abs(ot_ref) / r) / r + 2.0 ** -8 * np.abs(y_ref)
+    y = o.detach().cpu().double().numpy()
+    assert np.all(np.isfinite(y))
+    excess = np.abs(y - y_ref) / bound
+    assert float(np.max(excess)) <= 1.0, ("o vs its bound", float(np.max(excess)))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("T", [1, 17, 64, 200, 1000])
+def test_gated_lengths(T, dtype):
+    # (one token without an initial state has a single dot product for its
+    # output: give it a state, as a resumed prefill has)
+    gated_vs_oracle([T], 2, dtype, 500 + T, init=(T % 2 == 0 or T == 1))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_gated_packed_varlen_with_states(dtype):
+    gated_vs_oracle([0, 1, 64, 130, 0, 77, 255], 3, dtype, 541, init=True)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("steps", ["gate", "qk", "epi", "epi_no_weight"])
+def test_gated_each_step_alone(steps, dtype):
+    """One step on at a time, so that a mistake in one is not hidden by the
+    others (a norm over the wrong axis, a wrong sign in a sigmoid)."""
+    gated_vs_oracle([150, 90], 2, dtype, 560, gate=steps == "gate", qk=steps == "qk",
+                    epi=steps.startswith("epi"), weight=steps == "epi")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_gated_planner_split(dtype):
+    """A long sequence split into segments: the prologue feeds the segment
+    pass and the replay alike, the epilogue is in the replay."""
+    gated_vs_oracle([1000], 2, dtype, 570, init=True, split=4)
+
+
+@pytest.mark.parametrize("fused", ["1", "0"])
+@pytest.mark.parametrize("epi", [True, False])
+def test_gated_fused_and_two_kernel_paths(fused, epi, monkeypatch):
+    """bf16 with enough (sequence, head) chains for the fused kernel, forced
+    on and off; with and without the output epilogue."""
+    monkeypatch.setenv("KDA_FUSED_PREFILL", fused)
+    gated_vs_oracle([70, 1, 128, 129, 0, 64], 4, torch.bfloat16, 580, epi=epi, init=True)
+
+
+def test_gated_large_gate_logits_saturate():
+    """Gate logits of +-40: the log decay reaches its bounds (g_min and 0)
+    and the output gate its ends (0 and 1) without overflow."""
+    T, H = 130, 2
+    cu = wl.cu_from_lengths([T])
+    d = wl.raw_layer_inputs(T, H, torch.float32, 590, device=DEV)
+    d["z"] = (torch.sign(d["z"]) * 40.0).contiguous()
+    d["out_gate"] = (torch.sign(d["out_gate"]) * 40.0).contiguous()
+    o, fin = kda.chunk_prefill_gated(d["q"], d["k"], d["v"], d["z"], d["beta"], A_log=d["A_log"],
+                                     qk_norm_eps=QK_EPS, out_gate=d["out_gate"],
+                                     out_norm_weight=d["norm_weight"], cu_seqlens=cu)
+    torch.cuda.synchronize()
+    o_ref, f_ref = oracle.prefill_gated(d["q"], d["k"], d["v"], d["beta"], z=d["z"],
+                                        A_log=d["A_log"], qk_norm_eps=QK_EPS,
+                                        out_gate=d["out_gate"], out_norm_weight=d["norm_weight"],
+                                        cu_seqlens=cu)
+    assert rel_err(o, o_ref) <= TOL[torch.float32]
+    assert rel_err(fin, f_ref) <= TOL[torch.float32]
+
+
+@pytest.mark.parametrize("fused", ["1", "0"])
+def test_gated_epilogue_exact_recurrence_bf16(fused, monkeypatch):
+    """bf16 inputs on which the recurrence is exact (beta = 0, g = 0, q in
+    {-1, 0, 1}, integer initial states: o~ = S0^T q, every product and sum an
+    exact integer), so the output norm and gate are checked to y's own bf16
+    rounding, on the fused kernel and on the two kernels."""
+    monkeypatch.setenv("KDA_FUSED_PREFILL", fused)
+    lengths, H = [70, 64, 1, 130], 3
+    cu = wl.cu_from_lengths(lengths)
+    T, N = int(cu[-1]), len(lengths)
+    d = wl.raw_layer_inputs(T, H, torch.bfloat16, 600, device=DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(601)
+    q = torch.randint(-1, 2, (T, H, 128), generator=gen, device=DEV).to(torch.bfloat16)
+    S0 = torch.randint(-8, 9, (N, H, 128, 128), generator=gen, device=DEV).to(torch.float32)
+    zero_g = torch.zeros_like(q)
+    zero_b = torch.zeros((T, H), dtype=torch.bfloat16, device=DEV)
+    o, fin = kda.chunk_prefill_gated(q, d["k"], d["v"], zero_g, zero_b,
+                                     out_gate=d["out_gate"], out_norm_weight=d["norm_weight"],
+                                     out_norm_eps=OUT_EPS, cu_seqlens=cu, initial_state=S0)
+    torch.cuda.synchronize()
+    y_ref, f_ref = oracle.prefill_gated(q, d["k"], d["v"], zero_b, g=zero_g,
+                                        out_gate=d["out_gate"],
+                                        out_norm_weight=d["norm_weight"], out_norm_eps=OUT_EPS,
+                                        cu_seqlens=cu, initial_state=S0)
+    y = o.detach().cpu().double().numpy()
+    assert np.all(np.isfinite(y))
+    bound = 2.0 ** -8 * np.abs(y_ref) + 1e-6 * float(np.max(np.abs(y_ref)))
+    assert float(np.max(np.abs(y - y_ref) / bound)) <= 1.0
+    np.testing.assert_array_equal(fin.cpu().numpy(), f_ref)
