@@ -156,7 +156,10 @@ def traffic_from_counters(fetch_csv, write_csv, workload, command):
     print(json.dumps(out, indent=1))
 
 
-def time_prefill(kda, wl, name, steps, warmup, split_hint, dev):
+def time_prefill(kda, wl, name, steps, warmup, split_hint, dev, gated=False):
+    """Event-timed prefill calls.  gated: kda_chunk_prefill_gated with every
+    step on (decay gate from logits, q / k L2 norm, output norm and gate) on
+    the same inputs (g serves as the gate logits, v as the output gate's)."""
     import torch
     w = wl.WORKLOADS[name]
     d = wl.prefill_case(w, device=dev)
@@ -168,10 +171,19 @@ def time_prefill(kda, wl, name, steps, warmup, split_hint, dev):
     nbytes = kda.prefill_workspace_size(cu, H, w.dtype, split_hint)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
 
+    A_log = torch.zeros((H,), dtype=torch.float32, device=dev)
+    nw = torch.ones((D,), dtype=torch.float32, device=dev)
+
     def step():
-        kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu,
-                          initial_state=d["init"], split_hint=split_hint, o=o,
-                          final_state=fin, workspace=ws)
+        if gated:
+            kda.chunk_prefill_gated(d["q"], d["k"], d["v"], d["g"], d["beta"], A_log=A_log,
+                                    qk_norm_eps=1e-6, out_gate=d["v"], out_norm_weight=nw,
+                                    cu_seqlens=cu, initial_state=d["init"],
+                                    split_hint=split_hint, o=o, final_state=fin, workspace=ws)
+        else:
+            kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu,
+                              initial_state=d["init"], split_hint=split_hint, o=o,
+                              final_state=fin, workspace=ws)
 
     for _ in range(warmup):
         step()
@@ -385,6 +397,11 @@ def main():
     print("prefill %s: %.3f ms/step, %.3g tokens/s, %.1f TFLOP/s (%.1f%% of bf16 MFMA peak)"
           % (args.workload, main_res["ms_per_step"], main_res["tokens_per_s"],
              main_res["tflops"], 100 * main_res["mfma_frac"]), file=sys.stderr, flush=True)
+    gated = time_prefill(kda, wl, args.workload, args.steps, 2, args.split, dev, gated=True)
+    gated["vs_plain"] = gated["ms_per_step"] / main_res["ms_per_step"]
+    print("prefill %s gated (decay gate, q/k norm, output norm and gate fused): %.3f ms/step "
+          "(x%.3f of the plain call)" % (args.workload, gated["ms_per_step"], gated["vs_plain"]),
+          file=sys.stderr, flush=True)
     extra = {}
     if args.all:
         for name in ("prefill_bf16_T131072_H12", "prefill_bf16_varlen64_H96_resume",
@@ -395,6 +412,12 @@ def main():
             extra[name] = r
             print("prefill %s: %.3f ms/step, %.3g tokens/s, %.1f%% MFMA"
                   % (name, r["ms_per_step"], r["tokens_per_s"], 100 * r["mfma_frac"]),
+                  file=sys.stderr, flush=True)
+            rg = time_prefill(kda, wl, name, max(3, args.steps // 2), 1, 0, dev, gated=True)
+            rg["vs_plain"] = rg["ms_per_step"] / r["ms_per_step"]
+            extra[name + "_gated"] = rg
+            print("prefill %s gated: %.3f ms/step (x%.3f)" % (name, rg["ms_per_step"],
+                                                               rg["vs_plain"]),
                   file=sys.stderr, flush=True)
     copy_ref = copy_reference(dev)
     print("plain copy: %.0f GB/s achievable (%.1f%% of the %.0f GB/s HBM peak)"
@@ -448,6 +471,7 @@ def main():
         "hbm_reference": {"peak_GB_per_s": PEAK_HBM_GBS, "copy": copy_ref},
         "cpu_baseline": cpu,
         "prefill": main_res,
+        "prefill_gated": gated,
         "decode": dec,
         "decode_replay": rep,
         "extra": extra or None,

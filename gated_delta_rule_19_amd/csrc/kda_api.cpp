@@ -384,10 +384,16 @@ kda_status prefill_impl(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_
                       (const float *)(ws + p.off_M), (const float *)(ws + p.off_St),
                       initial_state, (float *)(ws + p.off_Sin), s);
   }
+  // the output epilogue: in the replay pass's stores when it runs whole
+  // rows, else as a pass of its own after it
+  const bool epi_in_k2 = epi.on() && k2_fuses_epilogue((int32_t)p.chains.size(), H);
   if (e == hipSuccess)
     e = launch_k2(elt, 0, (const ChainDesc *)(ws + p.off_chains), (int32_t)p.chains.size(), H,
                   ws + p.off_rec, v, o, initial_state, (const float *)(ws + p.off_Sin),
-                  final_state, ckpt_align ? ckpt : nullptr, 0, epi, s);
+                  final_state, ckpt_align ? ckpt : nullptr, 0, epi_in_k2 ? epi : Epilogue(),
+                  s);
+  if (e == hipSuccess && epi.on() && !epi_in_k2)
+    e = launch_out_norm_gate(elt, T * H, o, epi, s);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -254,6 +254,24 @@ __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// Sum of squares of 8 bf16 values held as 4 raw dwords, added to acc
+// (v_dot2c_f32_bf16: the products are exact in fp32).  The pairs come out of
+// a whole-vector bit-cast: a bit-cast of a single element r[j] would read
+// element 0 whatever j.
+__device__ __forceinline__ float sumsq8_bf16(const u32x4 &r, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x8 v = __builtin_bit_cast(bf16x8, r);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1),
+                                        __builtin_shufflevector(v, v, 0, 1), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3),
+                                        __builtin_shufflevector(v, v, 2, 3), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5),
+                                        __builtin_shufflevector(v, v, 4, 5), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7),
+                                        __builtin_shufflevector(v, v, 6, 7), acc, false);
+  return acc;
+}
+
 // 8 bf16 (raw dwords) -> fp32
 __device__ __forceinline__ void widen8(u32x4 w, float *x) {
 #pragma unroll

@@ -558,14 +558,8 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
           float sq = 0.f, sk = 0.f;
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            float a[8], b[8];
-            widen8(rq[s], a);
-            widen8(rk[s], b);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              sq += a[j] * a[j];
-              sk += b[j] * b[j];
-            }
+            sq = sumsq8_bf16(rq[s], sq);
+            sk = sumsq8_bf16(rk[s], sk);
           }
           sq += __shfl_xor(sq, 16);
           sk += __shfl_xor(sk, 16);

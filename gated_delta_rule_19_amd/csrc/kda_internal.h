@@ -157,6 +157,16 @@ hipError_t launch_fused(const ChainDesc *chains, int32_t nchains, int32_t H, con
                         const float *init, const float *sin, float *final_state, float *ckpt,
                         const Prologue &pro, const Epilogue &epi, hipStream_t s);
 
+// Whether the state chain's replay pass takes the output epilogue itself:
+// when its plain launch runs 128-column blocks anyway (at least one wide
+// workgroup per compute unit).  Otherwise it runs the 64-column blocks
+// without it and launch_out_norm_gate follows.
+bool k2_fuses_epilogue(int32_t nchains, int32_t H);
+
+// The output norm and gate as a pass of its own over o ([rows, dv], in place).
+hipError_t launch_out_norm_gate(int elt, int64_t rows, void *o, const Epilogue &epi,
+                                hipStream_t s);
+
 hipError_t launch_scan(const ScanDesc *descs, int32_t ndesc, int32_t H, const float *Mseg,
                        const float *Stseg, const float *init, float *sin, hipStream_t s);
 

@@ -1340,6 +1340,67 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanDesc *__restri
     step(in0, in1, j);
 }
 
+// ---------------------------------------------------------------------------
+// Output norm and gate as a pass of its own over o, in place ("Kimi K3.1 Pro
+// 架构完全拆解" §3.3): o <- sigmoid(gate) w o / sqrt(mean(o^2) + eps) per
+// (token, head) row.  For calls whose state chain runs 64-column blocks
+// (few chains), where a whole row is no single workgroup's.  16 threads per
+// row, 8 channels each (16-byte bf16 loads); HBM-bound.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void out_norm_gate_kernel(T *__restrict__ o,
+                                                                 const T *__restrict__ gate,
+                                                                 const float *__restrict__ w,
+                                                                 float eps, int64_t rows) {
+  const int part = threadIdx.x & 15;
+  float wn[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    wn[j] = w ? w[8 * part + j] : 1.f;
+  // the 16 threads of a row stay together (same r), so the row reduction
+  // below only ever reads active lanes
+  for (int64_t r = (int64_t)blockIdx.x * (kThreads / 16) + (threadIdx.x >> 4); r < rows;
+       r += (int64_t)gridDim.x * (kThreads / 16)) {
+    T *op = o + r * kD + 8 * part;
+    float x[8], z[8];
+    frag_to_f32(load_frag(op), x);
+    frag_to_f32(load_frag(gate + r * kD + 8 * part), z);
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      ss += x[j] * x[j];
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1)
+      ss += __shfl_xor(ss, m);
+    const float sc = __builtin_amdgcn_rsqf(ss * (1.f / kD) + eps);
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      y[j] = x[j] * sc * wn[j] *
+             __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z[j] * 1.4426950408889634f));
+    store8(op, y);
+  }
+}
+
+hipError_t launch_out_norm_gate(int elt, int64_t rows, void *o, const Epilogue &epi,
+                                hipStream_t s) {
+  if (rows == 0)
+    return hipSuccess;
+  const int64_t groups = (rows + kThreads / 16 - 1) / (kThreads / 16);
+  const unsigned grid = (unsigned)std::min<int64_t>(groups, (int64_t)kComputeUnits * 8);
+  if (elt == 1)
+    out_norm_gate_kernel<bf16><<<grid, kThreads, 0, s>>>((bf16 *)o, (const bf16 *)epi.gate,
+                                                          epi.weight, epi.eps, rows);
+  else
+    out_norm_gate_kernel<float><<<grid, kThreads, 0, s>>>((float *)o, (const float *)epi.gate,
+                                                           epi.weight, epi.eps, rows);
+  return hipGetLastError();
+}
+
+bool k2_fuses_epilogue(int32_t nchains, int32_t H) {
+  return (int64_t)nchains * H * (kD / kBVWide) >= kComputeUnits;
+}
+
 hipError_t launch_k1(int elt, const ChunkDesc *chunks, int32_t nchunks, int32_t H,
                      const void *q, const void *k, const void *g, const void *beta, void *ws,
                      const Prologue &pro, hipStream_t s) {

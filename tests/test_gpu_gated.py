@@ -8,9 +8,10 @@ prefill's bar max|x - x_ref| <= tol * max|x_ref| (tol = 1e-2 for bf16 inputs,
 1e-4 for fp32).  o through the output norm and gate, y = s o~ / r with
 s = w sigmoid(gate) and r = sqrt(mean(o~^2) + eps) per row, meets that bar
 too for fp32; for bf16 it meets the bound the plain bar implies through the
-norm: with E = tol * max|o~_ref| the recurrence output's error,
-    |y - y_ref| <= |s| E (1 + |o~_ref| / r_ref) / r_ref + 2^-8 |y_ref|
-(|r - r_ref| <= rms of the error <= E; the last term is y's bf16 rounding).
+norm: with E = tol * max|o~_ref| the recurrence output's error (o~ as stored
+included), |r - r_ref| <= rms of the error <= E, so r >= r_ref - E and
+    |y - y_ref| <= |s| E (1 + |o~_ref| / r_ref) / (r_ref - E) + 2^-8 |y_ref|
+(the last term is y's own bf16 rounding; rows with r_ref <= E are not bounded).
 A row whose output is small against the sequence's largest one is scaled up
 by the norm, and with it its share of the recurrence's bf16 error.
 """
@@ -83,7 +84,9 @@ def check_gated_bound(o, y_ref, d, nw, kw, qk, cu, S0, dtype):
     gate = d["out_gate"].detach().cpu().double().numpy()
     w = np.ones(ot_ref.shape[-1]) if nw is None else nw.detach().cpu().double().numpy()
     s = np.abs(w / (1.0 + np.exp(-gate)))
-    bound = s * E * (1.0 + np.abs(ot_ref) / r) / r + 2.0 ** -8 * np.abs(y_ref)
+    with np.errstate(divide="ignore"):
+        lo = np.where(r > E, r - E, 0.0)
+        bound = s * E * (1.0 + np.abs(ot_ref) / r) / lo + 2.0 ** -8 * np.abs(y_ref)
     y = o.detach().cpu().double().numpy()
     assert np.all(np.isfinite(y))
     excess = np.abs(y - y_ref) / bound
@@ -122,10 +125,22 @@ def test_gated_planner_split(dtype):
 @pytest.mark.parametrize("fused", ["1", "0"])
 @pytest.mark.parametrize("epi", [True, False])
 def test_gated_fused_and_two_kernel_paths(fused, epi, monkeypatch):
-    """bf16 with enough (sequence, head) chains for the fused kernel, forced
-    on and off; with and without the output epilogue."""
+    """bf16 with the fused kernel forced on and off; with and without the
+    output epilogue (few chains: on the two-kernel path it is a pass of its
+    own after the state chain)."""
     monkeypatch.setenv("KDA_FUSED_PREFILL", fused)
     gated_vs_oracle([70, 1, 128, 129, 0, 64], 4, torch.bfloat16, 580, epi=epi, init=True)
+
+
+# 64 sequences x 4 heads = 256 (sequence, head) chains: the two-kernel state
+# chain runs 128-column blocks and takes the output epilogue in its stores
+MANY = [1 + (37 * i) % 140 for i in range(64)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_gated_many_chains_epilogue_in_state_chain(dtype, monkeypatch):
+    monkeypatch.setenv("KDA_FUSED_PREFILL", "0")
+    gated_vs_oracle(MANY, 4, dtype, 585, init=True)
 
 
 def test_gated_large_gate_logits_saturate():
@@ -148,14 +163,15 @@ def test_gated_large_gate_logits_saturate():
     assert rel_err(fin, f_ref) <= TOL[torch.float32]
 
 
-@pytest.mark.parametrize("fused", ["1", "0"])
-def test_gated_epilogue_exact_recurrence_bf16(fused, monkeypatch):
+@pytest.mark.parametrize("path", ["fused", "state_chain", "own_pass"])
+def test_gated_epilogue_exact_recurrence_bf16(path, monkeypatch):
     """bf16 inputs on which the recurrence is exact (beta = 0, g = 0, q in
     {-1, 0, 1}, integer initial states: o~ = S0^T q, every product and sum an
     exact integer), so the output norm and gate are checked to y's own bf16
-    rounding, on the fused kernel and on the two kernels."""
-    monkeypatch.setenv("KDA_FUSED_PREFILL", fused)
-    lengths, H = [70, 64, 1, 130], 3
+    rounding on each of the three places the epilogue runs: the fused kernel,
+    the state chain's stores (many chains) and its own pass (few chains)."""
+    monkeypatch.setenv("KDA_FUSED_PREFILL", "1" if path == "fused" else "0")
+    lengths, H = ([70, 64, 1, 130], 3) if path != "state_chain" else (MANY, 4)
     cu = wl.cu_from_lengths(lengths)
     T, N = int(cu[-1]), len(lengths)
     d = wl.raw_layer_inputs(T, H, torch.bfloat16, 600, device=DEV)
