@@ -35,6 +35,8 @@ EXPORTED = (
     "kda_chunk_prefill_workspace_size",
     "kda_chunk_prefill",
     "kda_chunk_prefill_ckpt",
+    "kda_chunk_prefill_ckpt_all",
+    "kda_prefill_num_checkpoints",
     "kda_chunk_prefill_gated",
     "kda_decode_step",
     "kda_decode_replay",
@@ -78,6 +80,10 @@ def load():
         lib.kda_chunk_prefill_ckpt.restype = i32
         lib.kda_chunk_prefill_ckpt.argtypes = [i32, lp, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                                vp, vp, vp, i32, lp, i32, vp, vp, sz, vp]
+        lib.kda_chunk_prefill_ckpt_all.restype = i32
+        lib.kda_chunk_prefill_ckpt_all.argtypes = lib.kda_chunk_prefill_ckpt.argtypes
+        lib.kda_prefill_num_checkpoints.restype = i64
+        lib.kda_prefill_num_checkpoints.argtypes = [i32, lp, lp, i32]
         lib.kda_chunk_prefill_gated.restype = i32
         f32 = ctypes.c_float
         lib.kda_chunk_prefill_gated.argtypes = [i32, lp, i32, i32, i32, i32, vp, vp, vp, vp, vp,
@@ -199,6 +205,22 @@ def chunk_prefill_checkpoint(q, k, v, g, beta, cu_seqlens=None, initial_state=No
                     split_hint, o, final_state, workspace, int(align), pos0, checkpoint)
 
 
+def chunk_prefill_checkpoints(q, k, v, g, beta, cu_seqlens=None, initial_state=None,
+                              align: int = 512, pos0=None, checkpoints=None,
+                              output_final_state: bool = True, split_hint: int = 0, o=None,
+                              final_state=None, workspace=None):
+    """Prefill that writes the state at every ``align``-aligned absolute
+    position of every sequence (``kda_chunk_prefill_ckpt_all``).
+
+    Returns ``(o, final_state, checkpoints [M, H, 128, 128], seq, positions)``:
+    checkpoint i belongs to sequence ``seq[i]`` and holds the state at
+    absolute position ``positions[i]`` (sequence-major, increasing).
+    """
+    return _prefill(q, k, v, g, beta, cu_seqlens, initial_state, output_final_state,
+                    split_hint, o, final_state, workspace, int(align), pos0, checkpoints,
+                    all_ckpts=True)
+
+
 def chunk_prefill_gated(q, k, v, g, beta, A_log=None, g_min: float = -5.0,
                         qk_norm_eps: float = 0.0, out_gate=None, out_norm_weight=None,
                         out_norm_eps: float = 1e-6, cu_seqlens=None, initial_state=None,
@@ -223,7 +245,8 @@ def chunk_prefill_gated(q, k, v, g, beta, A_log=None, g_min: float = -5.0,
 
 
 def _prefill(q, k, v, g, beta, cu_seqlens, initial_state, output_final_state, split_hint, o,
-             final_state, workspace, align=0, pos0=None, checkpoint=None, gated=None):
+             final_state, workspace, align=0, pos0=None, checkpoint=None, gated=None,
+             all_ckpts=False):
     lib = load()
     if q.dim() == 4:
         if cu_seqlens is not None and q.shape[0] != 1:
@@ -291,18 +314,35 @@ def _prefill(q, k, v, g, beta, cu_seqlens, initial_state, output_final_state, sp
         np.ascontiguousarray(np.asarray(pos0, dtype=np.int64))
     if p0.shape != (N,):
         raise ValueError("pos0 must hold one position per sequence")
+    if all_ckpts:
+        M = int(lib.kda_prefill_num_checkpoints(N, _cu_ptr(cu), _cu_ptr(p0), int(align)))
+        if M < 0:
+            raise ValueError("invalid cu_seqlens / pos0 / align for checkpoints")
+        shape = (M, H, dk, dv)
+    else:
+        shape = (N, H, dk, dv)
     if checkpoint is None:
-        checkpoint = torch.zeros((N, H, dk, dv), dtype=torch.float32, device=dev)
-    elif checkpoint.dtype != torch.float32 or checkpoint.shape != (N, H, dk, dv):
-        raise ValueError("checkpoint must be fp32 [N, H, dk, dv]")
+        checkpoint = torch.zeros(shape, dtype=torch.float32, device=dev)
+    elif checkpoint.dtype != torch.float32 or checkpoint.shape != shape:
+        raise ValueError("checkpoint buffer must be fp32 %s" % (shape,))
     _check_device(checkpoint)
-    st = lib.kda_chunk_prefill_ckpt(N, _cu_ptr(cu), H, dk, dv, code, _ptr(q), _ptr(k), _ptr(v),
-                                    _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
-                                    _ptr(final_state), int(split_hint), _cu_ptr(p0),
-                                    int(align), _ptr(checkpoint), _ptr(workspace),
-                                    workspace.numel(), _stream_ptr(dev))
+    fn = lib.kda_chunk_prefill_ckpt_all if all_ckpts else lib.kda_chunk_prefill_ckpt
+    st = fn(N, _cu_ptr(cu), H, dk, dv, code, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+            _ptr(initial_state), _ptr(o), _ptr(final_state), int(split_hint), _cu_ptr(p0),
+            int(align), _ptr(checkpoint) if checkpoint.numel() else None, _ptr(workspace),
+            workspace.numel(), _stream_ptr(dev))
     if st != KDA_OK:
-        raise KdaError(st, "kda_chunk_prefill_ckpt")
+        raise KdaError(st, "kda_chunk_prefill_ckpt_all" if all_ckpts
+                       else "kda_chunk_prefill_ckpt")
+    if all_ckpts:
+        seq, pos = [], []
+        for n in range(N):
+            end = int(p0[n]) + int(cu[n + 1] - cu[n])
+            for m in range(int(p0[n]) // align + 1, end // align + 1):
+                seq.append(n)
+                pos.append(m * align)
+        return o, final_state, checkpoint, np.array(seq, dtype=np.int64), \
+            np.array(pos, dtype=np.int64)
     end = p0 + np.diff(cu)
     pos = end // align * align
     pos = np.where(pos > p0, pos, -1)

@@ -76,6 +76,8 @@ ChainDesc chain(int64_t tok0, int64_t ntok, int64_t chunk0, int64_t init_idx,
   c.init_idx = (int32_t)init_idx;
   c.final_idx = (int32_t)final_idx;
   c.ckpt_chunk = c.ckpt_idx = -1;
+  c.ckpt_last = -2;
+  c.ckpt_every = 1;
   return c;
 }
 
@@ -128,9 +130,55 @@ int64_t ckpt_chunks(int64_t pos0, int64_t len, int64_t align) {
   return p > pos0 ? (p - pos0) / kC : 0;
 }
 
+// Hash-aligned positions p with pos0 < p <= pos0 + len.
+int64_t ckpt_count(int64_t pos0, int64_t len, int64_t align) {
+  return align <= 0 ? 0 : (pos0 + len) / align - pos0 / align;
+}
+
+// The checkpoints of one sequence, as chunks counted from its first: chunk
+// `first` (the one ending at the first checkpoint), then every `every`
+// chunks, `count` of them.  all = false: only the last one.
+struct SeqCkpts {
+  int64_t first = -1, every = 1, count = 0;
+};
+SeqCkpts seq_ckpts(int64_t pos0, int64_t len, int64_t align, bool all) {
+  SeqCkpts c;
+  const int64_t n = ckpt_count(pos0, len, align);
+  if (n <= 0)
+    return c;
+  if (!all) {
+    c.first = ckpt_chunks(pos0, len, align) - 1;
+    c.count = 1;
+    return c;
+  }
+  c.first = ((pos0 / align + 1) * align - pos0) / kC - 1;
+  c.every = align / kC;
+  c.count = n;
+  return c;
+}
+
+// Gives chain `c` (chunks [s0, s0 + cnt) of its sequence) the sequence's
+// checkpoints that fall in it; idx0: the sequence's first checkpoint index.
+void assign_ckpts(ChainDesc &c, const SeqCkpts &k, int64_t s0, int64_t cnt, int64_t idx0) {
+  if (k.count <= 0)
+    return;
+  const int64_t last = k.first + (k.count - 1) * k.every;
+  const int64_t j0 = s0 <= k.first ? 0 : (s0 - k.first + k.every - 1) / k.every;
+  const int64_t c0 = k.first + j0 * k.every;
+  const int64_t c1 = std::min(last, s0 + cnt - 1);
+  if (c0 > c1)
+    return;
+  c.ckpt_chunk = (int32_t)(c0 - s0);
+  c.ckpt_last = (int32_t)(c1 - s0);
+  c.ckpt_every = (int32_t)k.every;
+  c.ckpt_idx = (int32_t)(idx0 + j0);
+}
+
 bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_hint,
                         bool has_init, bool has_final, size_t es, Plan &p,
-                        const int64_t *pos0 = nullptr, int64_t align = 0) {
+                        const int64_t *pos0 = nullptr, int64_t align = 0,
+                        bool all_ckpts = false) {
+  int64_t ckpt_base = 0; // first checkpoint index of the current sequence
   if (!cu || cu[0] != 0)
     return false;
   for (int32_t n = 0; n < N; ++n)
@@ -147,15 +195,15 @@ bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_h
       d.seq = n;
       p.chunks.push_back(d);
     }
-    // the chunk after which the checkpoint state is taken, if any
-    const int64_t ck = ckpt_chunks(pos0 ? pos0[n] : 0, len, align) - 1;
+    // the chunks after which checkpoint states are taken (last-only mode:
+    // one per sequence, at index n; all: the sequence's run of indices)
+    const SeqCkpts ck = seq_ckpts(pos0 ? pos0[n] : 0, len, align, all_ckpts);
+    const int64_t idx0 = all_ckpts ? ckpt_base : n;
+    ckpt_base += ck.count;
     const int64_t nseg = plan_nseg(len, N, H, split_hint);
     if (nseg <= 1) {
       p.chains.push_back(chain(cu[n], len, c0, has_init ? n : -1, has_final ? n : -1));
-      if (ck >= 0) {
-        p.chains.back().ckpt_chunk = (int32_t)ck;
-        p.chains.back().ckpt_idx = n;
-      }
+      assign_ckpts(p.chains.back(), ck, 0, nch, idx0);
       continue;
     }
     const int64_t q = nch / nseg, r = nch % nseg;
@@ -169,10 +217,7 @@ bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_h
         p.segchains.push_back(chain(t0, nt, c0 + s0, -1, pair0 + j));
       const bool last = j + 1 == nseg;
       p.chains.push_back(chain(t0, nt, c0 + s0, -2 - (sin0 + j), (last && has_final) ? n : -1));
-      if (ck >= s0 && ck < s0 + cnt) {
-        p.chains.back().ckpt_chunk = (int32_t)(ck - s0);
-        p.chains.back().ckpt_idx = n;
-      }
+      assign_ckpts(p.chains.back(), ck, s0, cnt, idx0);
     }
     p.scans.push_back(ScanDesc{(int32_t)pair0, (int32_t)nseg, (int32_t)sin0,
                                has_init ? n : -1});
@@ -324,7 +369,7 @@ kda_status prefill_impl(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_
                         float *final_state, int32_t split_hint, const int64_t *pos0,
                         int32_t ckpt_align, float *ckpt, void *workspace,
                         size_t workspace_bytes, void *stream, const Prologue &pro = Prologue(),
-                        const Epilogue &epi = Epilogue()) {
+                        const Epilogue &epi = Epilogue(), bool all_ckpts = false) {
   if (dk != kD || dv != kD || (dt != KDA_F32 && dt != KDA_BF16))
     return KDA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || H < 1 || split_hint < 0 || !cu_seqlens_host)
@@ -338,7 +383,8 @@ kda_status prefill_impl(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_
   }
   Plan p;
   if (!build_prefill_plan(num_seqs, cu_seqlens_host, H, split_hint, initial_state != nullptr,
-                          final_state != nullptr, elt_size(dt), p, pos0, ckpt_align))
+                          final_state != nullptr, elt_size(dt), p, pos0, ckpt_align,
+                          all_ckpts))
     return KDA_ERR_INVALID_ARG;
   if (!plan_fits(p, H))
     return KDA_ERR_INVALID_ARG;
@@ -465,6 +511,45 @@ kda_status kda_chunk_prefill_ckpt(int32_t num_seqs, const int64_t *cu_seqlens_ho
   return prefill_impl(num_seqs, cu_seqlens_host, H, dk, dv, dt, q, k, v, g, beta, initial_state,
                       o, final_state, split_hint, pos0_host, ckpt_align, ckpt_state, workspace,
                       workspace_bytes, stream);
+}
+
+int64_t kda_prefill_num_checkpoints(int32_t num_seqs, const int64_t *cu_seqlens_host,
+                                    const int64_t *pos0_host, int32_t ckpt_align) {
+  if (num_seqs < 0 || !cu_seqlens_host || cu_seqlens_host[0] != 0 || ckpt_align <= 0 ||
+      ckpt_align % kC != 0)
+    return -1;
+  int64_t total = 0;
+  for (int32_t n = 0; n < num_seqs; ++n) {
+    const int64_t len = cu_seqlens_host[n + 1] - cu_seqlens_host[n];
+    const int64_t p0 = pos0_host ? pos0_host[n] : 0;
+    if (len < 0 || p0 < 0 || p0 % kC != 0 || p0 > ((int64_t)1 << 62))
+      return -1;
+    total += ckpt_count(p0, len, ckpt_align);
+  }
+  return total;
+}
+
+kda_status kda_chunk_prefill_ckpt_all(int32_t num_seqs, const int64_t *cu_seqlens_host,
+                                      int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
+                                      const void *q, const void *k, const void *v,
+                                      const void *g, const void *beta,
+                                      const float *initial_state, void *o, float *final_state,
+                                      int32_t split_hint, const int64_t *pos0_host,
+                                      int32_t ckpt_align, float *ckpt_states, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+  if (ckpt_align <= 0)
+    return KDA_ERR_INVALID_ARG;
+  const int64_t n = kda_prefill_num_checkpoints(num_seqs, cu_seqlens_host, pos0_host,
+                                                ckpt_align);
+  if (n < 0 || n > INT32_MAX / 2)
+    return KDA_ERR_INVALID_ARG;
+  if (n == 0) // nothing to write: the states need no buffer
+    return prefill_impl(num_seqs, cu_seqlens_host, H, dk, dv, dt, q, k, v, g, beta,
+                        initial_state, o, final_state, split_hint, nullptr, 0, nullptr,
+                        workspace, workspace_bytes, stream);
+  return prefill_impl(num_seqs, cu_seqlens_host, H, dk, dv, dt, q, k, v, g, beta, initial_state,
+                      o, final_state, split_hint, pos0_host, ckpt_align, ckpt_states, workspace,
+                      workspace_bytes, stream, Prologue(), Epilogue(), /*all_ckpts=*/true);
 }
 
 kda_status kda_chunk_prefill_gated(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_t H,

@@ -406,12 +406,16 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
       }
     };
 
-    // the state after chunk ch, when it is the chain's checkpoint
+    // the state after chunk ch, when it is one of the chain's checkpoints
+    // (the next one is chunk ck_next, at index ck_idx)
+    int ck_next = cd.ckpt_chunk, ck_idx = cd.ckpt_idx;
     auto ckpt_store = [&](int ch) {
-      if (ch == cd.ckpt_chunk && ckpt != nullptr) {
+      if (ckpt != nullptr && ch == ck_next && ch <= cd.ckpt_last) {
         const int ln = opaque_lane(), lr = ln & 15, lg = ln >> 4;
         const int wcol = col0 + VW * wv + lr;
-        float *cp = ckpt + ((int64_t)cd.ckpt_idx * H + h) * (kD * kD);
+        float *cp = ckpt + ((int64_t)ck_idx * H + h) * (kD * kD);
+        ck_next += cd.ckpt_every;
+        ++ck_idx;
 #pragma unroll
         for (int c = 0; c < NCT; ++c)
 #pragma unroll

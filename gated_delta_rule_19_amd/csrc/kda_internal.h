@@ -25,18 +25,20 @@ static_assert(sizeof(ChunkDesc) == 16, "ChunkDesc layout");
 //   init_idx == -1 : entry state = 0 (segment pass: [0 | I])
 //   init_idx <= -2 : entry state = planner entry state Sin[-2 - init_idx]
 //   final_idx >= 0 : exit state written at index final_idx of the output base
-//   ckpt_chunk >= 0: the state after the chain's chunk ckpt_chunk (counted
-//                    from the chain's first chunk) is also written, at index
-//                    ckpt_idx of the checkpoint output
+//   checkpoints    : the states after the chain's chunks ckpt_chunk,
+//                    ckpt_chunk + ckpt_every, ... up to ckpt_last (counted
+//                    from the chain's first chunk) are also written, at
+//                    indices ckpt_idx, ckpt_idx + 1, ... of the checkpoint
+//                    output; none when ckpt_last < ckpt_chunk
 struct ChainDesc {
   int64_t tok0;
   int32_t ntok;
   int32_t chunk0;
   int32_t init_idx;
   int32_t final_idx;
-  int32_t ckpt_chunk, ckpt_idx;
+  int32_t ckpt_chunk, ckpt_last, ckpt_every, ckpt_idx;
 };
-static_assert(sizeof(ChainDesc) == 32, "ChainDesc layout");
+static_assert(sizeof(ChainDesc) == 40, "ChainDesc layout");
 
 // One split sequence for the planner's prefix scan.
 struct ScanDesc {

@@ -868,6 +868,9 @@ __global__ __launch_bounds__(k2_threads(BV, NCT)) void k2_kernel(
       }
     };
 
+    // the chain's next checkpoint chunk and its index (wave-uniform)
+    [[maybe_unused]] int ck_next = cd.ckpt_chunk, ck_idx = cd.ckpt_idx;
+
     // One chunk: computes from the record image in `cur` while chunk ch+1's
     // record goes into `nxt`.  The buffers are distinct LDS objects and the
     // loop is unrolled by two, so every access names its buffer statically
@@ -1108,10 +1111,12 @@ __global__ __launch_bounds__(k2_threads(BV, NCT)) void k2_kernel(
       // prefill: the state after this chunk is also a checkpoint (out_b);
       // its addresses come from an opaque lane index, so that they are
       // formed here and not kept in registers across the chunk loop
-      if (MODE == 0 && ch == cd.ckpt_chunk && out_b != nullptr) {
+      if (MODE == 0 && out_b != nullptr && ch == ck_next && ch <= cd.ckpt_last) {
         const int ln = opaque_lane(), clg = ln >> 4;
-        float *cp = out_b + ((int64_t)cd.ckpt_idx * H + h) * (kD * kD) + vcol0 +
+        float *cp = out_b + ((int64_t)ck_idx * H + h) * (kD * kD) + vcol0 +
                     16 * NCT * wv + (ln & 15);
+        ck_next += cd.ckpt_every;
+        ++ck_idx;
 #pragma unroll
         for (int c = 0; c < NCT; ++c)
 #pragma unroll

@@ -170,6 +170,40 @@ kda_status kda_chunk_prefill_ckpt(int32_t num_seqs, const int64_t *cu_seqlens_ho
                                   size_t workspace_bytes, void *stream);
 
 /*
+ * kda_chunk_prefill_ckpt, but with a checkpoint at every hash-aligned
+ * position rather than the last one only: the optional form of the KDA
+ * kernel's state persistence ("部署 Kimi K3：从 KDA Kernel 到 Fleet 调度"
+ * §三 3.2, a state per hash block boundary; "Kimi K3.1 Pro 架构完全拆解"
+ * §8.2).  For sequence n the positions are p = m * ckpt_align with
+ * pos0[n] < p <= pos0[n] + L_n, in increasing order; the k-th of them gets
+ * the state after the sequence's first p - pos0[n] tokens.
+ *
+ *   ckpt_states : [kda_prefill_num_checkpoints(...), H, dk, dv] fp32, the
+ *                 sequences' checkpoints one after another (sequence 0's
+ *                 first); may be NULL when there are none.
+ * pos0_host and ckpt_align as for kda_chunk_prefill_ckpt; everything else,
+ * the workspace size included, as for kda_chunk_prefill.
+ */
+kda_status kda_chunk_prefill_ckpt_all(int32_t num_seqs, const int64_t *cu_seqlens_host,
+                                      int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
+                                      const void *q, const void *k, const void *v,
+                                      const void *g, const void *beta,
+                                      const float *initial_state, void *o, float *final_state,
+                                      int32_t split_hint, const int64_t *pos0_host,
+                                      int32_t ckpt_align, float *ckpt_states, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
+/*
+ * The number of checkpoints kda_chunk_prefill_ckpt_all writes: the
+ * ckpt_align-aligned positions p with pos0[n] < p <= pos0[n] + L_n, summed
+ * over the sequences (host only).  -1 for invalid arguments (cu_seqlens not
+ * starting at 0 or decreasing, pos0 negative or not a multiple of 64,
+ * ckpt_align not a positive multiple of 64).
+ */
+int64_t kda_prefill_num_checkpoints(int32_t num_seqs, const int64_t *cu_seqlens_host,
+                                    const int64_t *pos0_host, int32_t ckpt_align);
+
+/*
  * kda_chunk_prefill with the layer's steps on either side of the recurrence
  * fused into its kernels, so that none of them costs a pass over [T, H, d]:
  *

@@ -260,3 +260,21 @@ def test_gated_prefill_argument_errors(lib):
     assert run(n=0) == E.KDA_OK
     # with a step off, its parameters are not looked at
     assert run(A=None, gmin=nan, og=None, oe=nan, n=0) == E.KDA_OK
+
+
+def test_num_checkpoints(lib):
+    a, p = cu(0, 1000, 1500, 1564, 1564)
+    pos = np.array([0, 448, 512, 64], dtype=np.int64)
+    pp = pos.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    # 512 | 512 | none (576 < 1024) | none (empty)
+    assert lib.kda_prefill_num_checkpoints(4, p, pp, 512) == 2
+    # every 64 tokens: 15 + 7 + 1 + 0
+    assert lib.kda_prefill_num_checkpoints(4, p, pp, 64) == 15 + 7 + 1
+    assert lib.kda_prefill_num_checkpoints(4, p, None, 512) == 1 + 0 + 0 + 0
+    assert lib.kda_prefill_num_checkpoints(4, p, pp, 500) == -1       # not a multiple of 64
+    assert lib.kda_prefill_num_checkpoints(4, p, pp, 0) == -1
+    bad = np.array([0, 100, 512, 64], dtype=np.int64)
+    assert lib.kda_prefill_num_checkpoints(
+        4, p, bad.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), 512) == -1
+    a2, p2 = cu(0, 100, 50)                                            # decreasing
+    assert lib.kda_prefill_num_checkpoints(2, p2, None, 64) == -1

@@ -90,3 +90,61 @@ def bf16_path(request, monkeypatch):
 
 def test_checkpoint_bf16_paths(bf16_path):
     check([700, 1000, 40, 1536], [0, 448, 960, 0], 512, 2, torch.bfloat16, 730)
+
+
+# --- every hash-aligned position (kda_chunk_prefill_ckpt_all) ----------------
+
+
+def check_all(lengths, pos0, align, H, dtype, seed, split=0, fused=None, monkeypatch=None):
+    print("all-checkpoints case", dict(lengths=lengths, pos0=pos0, align=align, H=H,
+                                       dtype=str(dtype), split=split, fused=fused), flush=True)
+    if fused is not None:
+        monkeypatch.setenv("KDA_FUSED_PREFILL", fused)
+    cu = wl.cu_from_lengths(lengths)
+    N, T = len(lengths), int(cu[-1])
+    d = wl.token_inputs(T, H, dtype, seed, device=DEV, decay="mild")
+    S0 = wl.states(N, H, seed + 1, device=DEV)
+    o, fin, ck, seq, pos = kda.chunk_prefill_checkpoints(
+        d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu, initial_state=S0,
+        align=align, pos0=pos0, split_hint=split)
+    torch.cuda.synchronize()
+    o2, fin2 = kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu,
+                                 initial_state=S0, split_hint=split)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(fin, fin2)
+    p0 = np.zeros(N, dtype=np.int64) if pos0 is None else np.asarray(pos0)
+    # the positions, independently: every multiple of align in (p0, p0 + L]
+    want = [(n, m * align) for n in range(N)
+            for m in range(1, (int(p0[n]) + lengths[n]) // align + 1) if m * align > p0[n]]
+    assert [(int(a), int(b)) for a, b in zip(seq, pos)] == want
+    assert ck.shape[0] == len(want)
+    for i, (n, p) in enumerate(want):
+        a, b = int(cu[n]), int(cu[n]) + int(p - p0[n])
+        _, ref = oracle.recurrence(d["q"][a:b], d["k"][a:b], d["v"][a:b], d["g"][a:b],
+                                   d["beta"][a:b], initial_state=S0[n:n + 1], want_o=False)
+        assert rel_err(ck[i], ref[0]) <= TOL[dtype], (i, n, p)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_all_checkpoints_positions(dtype):
+    # several boundaries per sequence, resumed sequences (pos0 > 0), one
+    # ending exactly on a boundary, ones with none, an empty one
+    check_all([1300, 512, 1000, 40, 0, 1536, 130], [0, 512, 448, 960, 64, 0, 384], 256, 3,
+              dtype, 720)
+
+
+@pytest.mark.parametrize("split", [3, 7])
+def test_all_checkpoints_with_planner_split(split):
+    # segments of a split sequence each hold some of its boundaries
+    check_all([1500, 300], [128, 0], 128, 2, torch.float32, 730, split=split)
+
+
+@pytest.mark.parametrize("fused", ["1", "0"])
+def test_all_checkpoints_fused_and_two_kernel(fused, monkeypatch):
+    check_all([700, 65, 1024, 256], [64, 0, 512, 192], 128, 4, torch.bfloat16, 740,
+              fused=fused, monkeypatch=monkeypatch)
+
+
+def test_all_checkpoints_none():
+    # no sequence reaches a boundary: nothing is written, no buffer needed
+    check_all([100, 30], [0, 64], 512, 2, torch.float32, 750)
