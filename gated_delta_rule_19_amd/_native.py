@@ -39,7 +39,9 @@ EXPORTED = (
     "kda_prefill_num_checkpoints",
     "kda_chunk_prefill_gated",
     "kda_decode_step",
+    "kda_decode_step_gated",
     "kda_decode_replay",
+    "kda_decode_replay_gated",
     "kda_segment_transition_workspace_size",
     "kda_segment_transition",
 )
@@ -91,6 +93,13 @@ def load():
                                                 sz, vp]
         lib.kda_decode_step.restype = i32
         lib.kda_decode_step.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.kda_decode_step_gated.restype = i32
+        lib.kda_decode_step_gated.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                              f32, f32, vp, vp, f32, vp, vp, vp]
+        lib.kda_decode_replay_gated.restype = i32
+        lib.kda_decode_replay_gated.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                                i32, vp, vp, vp, vp, vp, vp, f32, f32, vp, vp,
+                                                f32, vp, vp, vp]
         lib.kda_decode_replay.restype = i32
         lib.kda_decode_replay.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32,
                                           vp, vp, vp, vp, vp, vp, vp, vp]
@@ -371,7 +380,44 @@ def decode_step(state, q, k, v, g, beta, o=None):
     return o
 
 
-def decode_replay(state, accepted, ck, cv, cg, cbeta, q, k, v, g, beta, o=None):
+def _layer_check(H, dv, dt, A_log, out_gate, out_shape, nw):
+    _check_device(A_log, out_gate, nw)
+    if A_log is not None and (A_log.dtype != torch.float32 or A_log.shape != (H,)):
+        raise ValueError("A_log must be fp32 [H]")
+    if out_gate is not None and (out_gate.dtype != dt or out_gate.shape != out_shape):
+        raise ValueError("out_gate must have o's dtype and shape")
+    if nw is not None and (nw.dtype != torch.float32 or nw.shape != (dv,)):
+        raise ValueError("out_norm_weight must be fp32 [dv]")
+
+
+def decode_step_gated(state, q, k, v, g, beta, A_log=None, g_min: float = -5.0,
+                      qk_norm_eps: float = 0.0, out_gate=None, out_norm_weight=None,
+                      out_norm_eps: float = 1e-6, o=None):
+    """``decode_step`` with the layer's steps fused in (``kda_decode_step_gated``);
+    the arguments mean what they mean for ``chunk_prefill_gated``."""
+    lib = load()
+    N, H, dk = k.shape
+    dv = v.shape[-1]
+    if state.dtype != torch.float32 or state.shape != (N, H, dk, dv):
+        raise ValueError("state must be fp32 [N, H, dk, dv]")
+    dt = q.dtype
+    for x in (k, v, g, beta):
+        if x.dtype != dt:
+            raise TypeError("q, k, v, g and beta must share one dtype")
+    dev = _check_device(state, q, k, v, g, beta, o)
+    _layer_check(H, dv, dt, A_log, out_gate, (N, H, dv), out_norm_weight)
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=dt, device=dev)
+    st = lib.kda_decode_step_gated(N, H, dk, dv, _dtype_code(dt), _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(g), _ptr(beta), _ptr(A_log), float(g_min),
+                                   float(qk_norm_eps), _ptr(out_gate), _ptr(out_norm_weight),
+                                   float(out_norm_eps), _ptr(state), _ptr(o), _stream_ptr(dev))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_decode_step_gated")
+    return o
+
+
+def decode_replay(state, accepted, ck, cv, cg, cbeta, q, k, v, g, beta, o=None, _gated=None):
     """Speculative-decode replay (``kda_decode_replay``), state updated in place.
 
     ``accepted``: int32 ``[N]`` on the device; cached window ``ck, cg``
@@ -398,12 +444,35 @@ def decode_replay(state, accepted, ck, cv, cg, cbeta, q, k, v, g, beta, o=None):
     dev = _check_device(state, accepted, ck, cv, cg, cbeta, q, k, v, g, beta, o)
     if o is None:
         o = torch.empty((N, P, H, dv), dtype=dt, device=dev)
+    if _gated is not None:
+        A_log, g_min, qk_eps, out_gate, nw, neps = _gated
+        _layer_check(H, dv, dt, A_log, out_gate, (N, P, H, dv), nw)
+        st = lib.kda_decode_replay_gated(N, H, dk, dv, _dtype_code(dt), W, _ptr(accepted),
+                                         _ptr(ck), _ptr(cv), _ptr(cg), _ptr(cbeta), P, _ptr(q),
+                                         _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log),
+                                         float(g_min), float(qk_eps), _ptr(out_gate), _ptr(nw),
+                                         float(neps), _ptr(state), _ptr(o), _stream_ptr(dev))
+        if st != KDA_OK:
+            raise KdaError(st, "kda_decode_replay_gated")
+        return o
     st = lib.kda_decode_replay(N, H, dk, dv, _dtype_code(dt), W, _ptr(accepted), _ptr(ck),
                                _ptr(cv), _ptr(cg), _ptr(cbeta), P, _ptr(q), _ptr(k), _ptr(v),
                                _ptr(g), _ptr(beta), _ptr(state), _ptr(o), _stream_ptr(dev))
     if st != KDA_OK:
         raise KdaError(st, "kda_decode_replay")
     return o
+
+
+def decode_replay_gated(state, accepted, ck, cv, cg, cbeta, q, k, v, g, beta, A_log=None,
+                        g_min: float = -5.0, qk_norm_eps: float = 0.0, out_gate=None,
+                        out_norm_weight=None, out_norm_eps: float = 1e-6, o=None):
+    """``decode_replay`` with the layer's steps fused in
+    (``kda_decode_replay_gated``): the gate and q / k norms apply to cached and
+    new tokens (the cache holds raw inputs), the output norm and gate
+    (out_gate ``[N, P, H, 128]``) to the new tokens' outputs."""
+    return decode_replay(state, accepted, ck, cv, cg, cbeta, q, k, v, g, beta, o=o,
+                         _gated=(A_log, g_min, qk_norm_eps, out_gate, out_norm_weight,
+                                 out_norm_eps))
 
 
 def segment_transition(k, v, g, beta, cu_seglens=None, M=None, S_tilde=None, workspace=None):

@@ -361,6 +361,32 @@ hipError_t upload_tables(const Plan &p, void *ws, hipStream_t stream) {
 
 namespace {
 
+// The gated entry points' layer arguments, validated (KDA_OK or
+// KDA_ERR_INVALID_ARG); `o` is the output the gate may not alias.
+kda_status layer_steps(const float *A_log, float g_min, float qk_norm_eps, const void *out_gate,
+                       const float *out_norm_weight, float out_norm_eps, const void *o,
+                       Prologue &pro, Epilogue &epi) {
+  if (A_log) {
+    // the chunk kernels' bound: every 16-token cumulative log decay >= -80
+    if (!(g_min >= -5.f && g_min < 0.f) || ((uintptr_t)A_log & 3u) != 0)
+      return KDA_ERR_INVALID_ARG;
+    pro.A_log = A_log;
+    pro.g_min = g_min;
+  }
+  if (!(qk_norm_eps >= 0.f) || qk_norm_eps > 3.0e38f)
+    return KDA_ERR_INVALID_ARG;
+  pro.qk_eps = qk_norm_eps;
+  if (out_gate) {
+    if (!(out_norm_eps > 0.f) || out_norm_eps > 3.0e38f ||
+        ((uintptr_t)out_norm_weight & 3u) != 0 || (o != nullptr && out_gate == o))
+      return KDA_ERR_INVALID_ARG;
+    epi.gate = out_gate;
+    epi.weight = out_norm_weight;
+    epi.eps = out_norm_eps;
+  }
+  return KDA_OK;
+}
+
 // kda_chunk_prefill, kda_chunk_prefill_ckpt (ckpt_align = 0: no checkpoints)
 // and kda_chunk_prefill_gated (prologue / epilogue on)
 kda_status prefill_impl(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_t H, int32_t dk,
@@ -440,6 +466,65 @@ kda_status prefill_impl(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_
                   s);
   if (e == hipSuccess && epi.on() && !epi_in_k2)
     e = launch_out_norm_gate(elt, T * H, o, epi, s);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+} // namespace
+
+namespace {
+
+kda_status decode_impl(int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
+                       const void *q, const void *k, const void *v, const void *g,
+                       const void *beta, float *state, void *o, void *stream,
+                       const Prologue &pro, const Epilogue &epi) {
+  if (dk != kD || dv != kD || (dt != KDA_F32 && dt != KDA_BF16))
+    return KDA_ERR_UNSUPPORTED;
+  if (N < 0 || H < 1)
+    return KDA_ERR_INVALID_ARG;
+  if ((int64_t)N * H >= ((int64_t)1 << 31))
+    return KDA_ERR_INVALID_ARG;
+  if (N == 0)
+    return KDA_OK;
+  if (!q || !k || !v || !g || !beta || !state || !o)
+    return KDA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) ||
+      !aligned_elt(beta, dt) || !aligned16(state) || !aligned16(o))
+    return KDA_ERR_INVALID_ARG;
+  if (epi.on() && !aligned_elt(epi.gate, dt))
+    return KDA_ERR_INVALID_ARG;
+  const hipError_t e = launch_decode(dt == KDA_BF16 ? 1 : 0, N, H, q, k, v, g, beta, state, o,
+                                     pro, epi, (hipStream_t)stream);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status replay_impl(int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype dt, int32_t W,
+                       const int32_t *accepted, const void *ck, const void *cv, const void *cg,
+                       const void *cbeta, int32_t P, const void *q, const void *k,
+                       const void *v, const void *g, const void *beta, float *state, void *o,
+                       void *stream, const Prologue &pro, const Epilogue &epi) {
+  if (dk != kD || dv != kD || (dt != KDA_F32 && dt != KDA_BF16))
+    return KDA_ERR_UNSUPPORTED;
+  if (N < 0 || H < 1 || W < 0 || W > KDA_REPLAY_MAX_TOKENS || P < 0 ||
+      P > KDA_REPLAY_MAX_TOKENS)
+    return KDA_ERR_INVALID_ARG;
+  // token-row indices ((n W + t) H + h) kD stay within int64; blocks within 2^31
+  if ((int64_t)N * H >= ((int64_t)1 << 31))
+    return KDA_ERR_INVALID_ARG;
+  if (N == 0)
+    return KDA_OK;
+  if (!accepted || !state || !aligned16(state) || ((uintptr_t)accepted & 3))
+    return KDA_ERR_INVALID_ARG;
+  if (W > 0 && (!ck || !cv || !cg || !cbeta || !aligned16(ck) || !aligned16(cv) ||
+                !aligned16(cg) || !aligned_elt(cbeta, dt)))
+    return KDA_ERR_INVALID_ARG;
+  if (P > 0 && (!q || !k || !v || !g || !beta || !o || !aligned16(q) || !aligned16(k) ||
+                !aligned16(v) || !aligned16(g) || !aligned_elt(beta, dt) || !aligned16(o)))
+    return KDA_ERR_INVALID_ARG;
+  if (P > 0 && epi.on() && !aligned_elt(epi.gate, dt))
+    return KDA_ERR_INVALID_ARG;
+  const hipError_t e = launch_replay(dt == KDA_BF16 ? 1 : 0, N, H, W, accepted, ck, cv, cg,
+                                     cbeta, P, q, k, v, g, beta, state, o, pro, epi,
+                                     (hipStream_t)stream);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -562,24 +647,10 @@ kda_status kda_chunk_prefill_gated(int32_t num_seqs, const int64_t *cu_seqlens_h
                                    size_t workspace_bytes, void *stream) {
   Prologue pro;
   Epilogue epi;
-  if (A_log) {
-    // the chunk kernels' bound: every 16-token cumulative log decay >= -80
-    if (!(g_min >= -5.f && g_min < 0.f) || ((uintptr_t)A_log & 3u) != 0)
-      return KDA_ERR_INVALID_ARG;
-    pro.A_log = A_log;
-    pro.g_min = g_min;
-  }
-  if (!(qk_norm_eps >= 0.f) || qk_norm_eps > 3.0e38f)
-    return KDA_ERR_INVALID_ARG;
-  pro.qk_eps = qk_norm_eps;
-  if (out_gate) {
-    if (!(out_norm_eps > 0.f) || out_norm_eps > 3.0e38f ||
-        ((uintptr_t)out_norm_weight & 3u) != 0 || out_gate == o)
-      return KDA_ERR_INVALID_ARG;
-    epi.gate = out_gate;
-    epi.weight = out_norm_weight;
-    epi.eps = out_norm_eps;
-  }
+  const kda_status st = layer_steps(A_log, g_min, qk_norm_eps, out_gate, out_norm_weight,
+                                    out_norm_eps, o, pro, epi);
+  if (st != KDA_OK)
+    return st;
   return prefill_impl(num_seqs, cu_seqlens_host, H, dk, dv, dt, q, k, v, g, beta, initial_state,
                       o, final_state, split_hint, nullptr, 0, nullptr, workspace,
                       workspace_bytes, stream, pro, epi);
@@ -588,22 +659,23 @@ kda_status kda_chunk_prefill_gated(int32_t num_seqs, const int64_t *cu_seqlens_h
 kda_status kda_decode_step(int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
                            const void *q, const void *k, const void *v, const void *g,
                            const void *beta, float *state, void *o, void *stream) {
-  if (dk != kD || dv != kD || (dt != KDA_F32 && dt != KDA_BF16))
-    return KDA_ERR_UNSUPPORTED;
-  if (N < 0 || H < 1)
-    return KDA_ERR_INVALID_ARG;
-  if ((int64_t)N * H >= ((int64_t)1 << 31))
-    return KDA_ERR_INVALID_ARG;
-  if (N == 0)
-    return KDA_OK;
-  if (!q || !k || !v || !g || !beta || !state || !o)
-    return KDA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) ||
-      !aligned_elt(beta, dt) || !aligned16(state) || !aligned16(o))
-    return KDA_ERR_INVALID_ARG;
-  const hipError_t e = launch_decode(dt == KDA_BF16 ? 1 : 0, N, H, q, k, v, g, beta, state, o,
-                                     (hipStream_t)stream);
-  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  return decode_impl(N, H, dk, dv, dt, q, k, v, g, beta, state, o, stream, Prologue(),
+                     Epilogue());
+}
+
+kda_status kda_decode_step_gated(int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
+                                 const void *q, const void *k, const void *v, const void *g,
+                                 const void *beta, const float *A_log, float g_min,
+                                 float qk_norm_eps, const void *out_gate,
+                                 const float *out_norm_weight, float out_norm_eps,
+                                 float *state, void *o, void *stream) {
+  Prologue pro;
+  Epilogue epi;
+  const kda_status st = layer_steps(A_log, g_min, qk_norm_eps, out_gate, out_norm_weight,
+                                    out_norm_eps, o, pro, epi);
+  if (st != KDA_OK)
+    return st;
+  return decode_impl(N, H, dk, dv, dt, q, k, v, g, beta, state, o, stream, pro, epi);
 }
 
 kda_status kda_decode_replay(int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
@@ -611,27 +683,26 @@ kda_status kda_decode_replay(int32_t N, int32_t H, int32_t dk, int32_t dv, kda_d
                              const void *cg, const void *cbeta, int32_t P, const void *q,
                              const void *k, const void *v, const void *g, const void *beta,
                              float *state, void *o, void *stream) {
-  if (dk != kD || dv != kD || (dt != KDA_F32 && dt != KDA_BF16))
-    return KDA_ERR_UNSUPPORTED;
-  if (N < 0 || H < 1 || W < 0 || W > KDA_REPLAY_MAX_TOKENS || P < 0 ||
-      P > KDA_REPLAY_MAX_TOKENS)
-    return KDA_ERR_INVALID_ARG;
-  // token-row indices ((n W + t) H + h) kD stay within int64; blocks within 2^31
-  if ((int64_t)N * H >= ((int64_t)1 << 31))
-    return KDA_ERR_INVALID_ARG;
-  if (N == 0)
-    return KDA_OK;
-  if (!accepted || !state || !aligned16(state) || ((uintptr_t)accepted & 3))
-    return KDA_ERR_INVALID_ARG;
-  if (W > 0 && (!ck || !cv || !cg || !cbeta || !aligned16(ck) || !aligned16(cv) ||
-                !aligned16(cg) || !aligned_elt(cbeta, dt)))
-    return KDA_ERR_INVALID_ARG;
-  if (P > 0 && (!q || !k || !v || !g || !beta || !o || !aligned16(q) || !aligned16(k) ||
-                !aligned16(v) || !aligned16(g) || !aligned_elt(beta, dt) || !aligned16(o)))
-    return KDA_ERR_INVALID_ARG;
-  const hipError_t e = launch_replay(dt == KDA_BF16 ? 1 : 0, N, H, W, accepted, ck, cv, cg,
-                                     cbeta, P, q, k, v, g, beta, state, o, (hipStream_t)stream);
-  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  return replay_impl(N, H, dk, dv, dt, W, accepted, ck, cv, cg, cbeta, P, q, k, v, g, beta,
+                     state, o, stream, Prologue(), Epilogue());
+}
+
+kda_status kda_decode_replay_gated(int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
+                                   int32_t W, const int32_t *accepted, const void *ck,
+                                   const void *cv, const void *cg, const void *cbeta, int32_t P,
+                                   const void *q, const void *k, const void *v, const void *g,
+                                   const void *beta, const float *A_log, float g_min,
+                                   float qk_norm_eps, const void *out_gate,
+                                   const float *out_norm_weight, float out_norm_eps,
+                                   float *state, void *o, void *stream) {
+  Prologue pro;
+  Epilogue epi;
+  const kda_status st = layer_steps(A_log, g_min, qk_norm_eps, out_gate, out_norm_weight,
+                                    out_norm_eps, o, pro, epi);
+  if (st != KDA_OK)
+    return st;
+  return replay_impl(N, H, dk, dv, dt, W, accepted, ck, cv, cg, cbeta, P, q, k, v, g, beta,
+                     state, o, stream, pro, epi);
 }
 
 size_t kda_segment_transition_workspace_size(int32_t num_segs,

@@ -18,14 +18,81 @@
 
 namespace kda {
 
-template <typename T>
+// The layer's steps around the recurrence, for the LAYER variants of the
+// kernels below ("Kimi K3.1 Pro 架构完全拆解" §3.2, §3.3, §3.4: the decode /
+// replay kernel also does the input normalization, the gating and the output
+// norm).  The norms act as scalars: with ik = 1/|k| and iq = 1/|q|,
+//   w = ik (DS^T k),  y = iq (DS^T q),  k.q -> ik iq (k.q),  S' = DS + k (ik u)^T,
+// so the raw k and q stay in LDS.  The output norm takes the 128 outputs of
+// a (sequence, head) row, which are this workgroup's.
+template <typename T> struct LayerArgs {
+  const float *A_log;  // [H] or null: g holds the log decay itself
+  float g_min;
+  float qk_eps;        // > 0: q, k normalized
+  const T *ogate;      // output gate logits (laid out like o), or null
+  const float *onw;    // [dv] or null
+  float oeps;
+};
+
+// Wave 0: k.q, and (LAYER) the inverse norms; results to LDS.
+template <bool LAYER, typename T>
+__device__ __forceinline__ void kq_norms(int tid, const float *s_k, const float *s_q,
+                                         const LayerArgs<T> &la, float *s_kq, float *s_ik,
+                                         float *s_iq) {
+  if (tid < 64) {
+    float p = s_k[tid] * s_q[tid] + s_k[tid + 64] * s_q[tid + 64];
+    float pk = 0.f, pq = 0.f;
+    const bool qk = LAYER && la.qk_eps > 0.f;
+    if (qk) {
+      pk = s_k[tid] * s_k[tid] + s_k[tid + 64] * s_k[tid + 64];
+      pq = s_q[tid] * s_q[tid] + s_q[tid + 64] * s_q[tid + 64];
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      p += __shfl_xor(p, m);
+      if (qk) {
+        pk += __shfl_xor(pk, m);
+        pq += __shfl_xor(pq, m);
+      }
+    }
+    if (tid == 0) {
+      const float ik = qk ? __builtin_amdgcn_rsqf(pk + la.qk_eps) : 1.f;
+      const float iq = qk ? __builtin_amdgcn_rsqf(pq + la.qk_eps) : 1.f;
+      *s_kq = p * ik * iq;
+      *s_ik = ik;
+      *s_iq = iq;
+    }
+  }
+}
+
+// Threads 0..127 (two whole waves) hold one output each: its RMS norm over
+// the 128 and the gate.  Call once with `store` false before a barrier (the
+// per-wave sums of squares go to s_ss), then with `store` true after it.
+__device__ __forceinline__ float out_norm_sum(int tid, float x, float *s_ss) {
+  float p = x * x;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1)
+    p += __shfl_xor(p, m);
+  if ((tid & 63) == 0)
+    s_ss[tid >> 6] = p;
+  return x;
+}
+__device__ __forceinline__ float out_norm_apply(int tid, float x, float z, const float *s_ss,
+                                                const float *onw, float eps) {
+  const float sc = __builtin_amdgcn_rsqf((s_ss[0] + s_ss[1]) * (1.f / kD) + eps);
+  const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+  return x * sc * (onw ? onw[tid] : 1.f) * sg;
+}
+
+template <typename T, bool LAYER>
 __global__ __launch_bounds__(256) void decode_kernel(const T *__restrict__ q,
                                                      const T *__restrict__ k,
                                                      const T *__restrict__ v,
                                                      const T *__restrict__ g,
                                                      const T *__restrict__ beta,
                                                      float *__restrict__ state,
-                                                     T *__restrict__ o) {
+                                                     T *__restrict__ o, int32_t H,
+                                                     LayerArgs<T> la) {
   const int64_t nh = blockIdx.x;
   const int tid = threadIdx.x;
   const int cg = tid & 31; // column group: columns 4*cg .. 4*cg+3
@@ -33,7 +100,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const T *__restrict__ q,
 
   __shared__ float s_k[kD], s_q[kD], s_a[kD], s_v[kD], s_u[kD];
   __shared__ float s_w[8][kD], s_y[8][kD];
-  __shared__ float s_kq, s_beta;
+  __shared__ float s_kq, s_beta, s_ik, s_iq, s_ss[2];
 
   float *S = state + nh * (int64_t)(kD * kD);
   f32x4 s[16];
@@ -42,26 +109,26 @@ __global__ __launch_bounds__(256) void decode_kernel(const T *__restrict__ q,
     s[i] = __builtin_nontemporal_load(
         reinterpret_cast<const f32x4 *>(S + (16 * rg + i) * kD + 4 * cg));
 
+  const bool epi = LAYER && la.ogate != nullptr;
+  float zo = 0.f; // this thread's output gate logit (tid < 128)
   if (tid < kD) {
     const int64_t off = nh * kD + tid;
     s_k[tid] = to_f32(k[off]);
     s_q[tid] = to_f32(q[off]);
-    s_a[tid] = __expf(to_f32(g[off]));
+    float gg = to_f32(g[off]);
+    if (LAYER && la.A_log)
+      gg = gate_log_decay(gg, __expf(la.A_log[nh % H]), la.g_min);
+    s_a[tid] = __expf(gg);
     s_v[tid] = to_f32(v[off]);
+    if (epi)
+      zo = to_f32(la.ogate[off]);
   }
   if (tid == 0)
     s_beta = to_f32(beta[nh]);
   __syncthreads();
 
-  // k . q, reduced inside wave 0
-  if (tid < 64) {
-    float p = s_k[tid] * s_q[tid] + s_k[tid + 64] * s_q[tid + 64];
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-      p += __shfl_xor(p, m);
-    if (tid == 0)
-      s_kq = p;
-  }
+  // k . q (and the inverse norms), reduced inside wave 0
+  kq_norms<LAYER>(tid, s_k, s_q, la, &s_kq, &s_ik, &s_iq);
 
   f32x4 w = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -75,6 +142,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const T *__restrict__ q,
   *reinterpret_cast<f32x4 *>(&s_y[rg][4 * cg]) = y;
   __syncthreads();
 
+  float ov = 0.f;
   if (tid < kD) {
     float ws = 0.f, ys = 0.f;
 #pragma unroll
@@ -82,11 +150,18 @@ __global__ __launch_bounds__(256) void decode_kernel(const T *__restrict__ q,
       ws += s_w[r][tid];
       ys += s_y[r][tid];
     }
-    const float u = s_beta * (s_v[tid] - ws);
-    s_u[tid] = u;
-    o[nh * kD + tid] = from_f32<T>(ys + s_kq * u);
+    const float ik = LAYER ? s_ik : 1.f, iq = LAYER ? s_iq : 1.f;
+    const float u = s_beta * (s_v[tid] - ik * ws);
+    s_u[tid] = ik * u;
+    ov = iq * ys + s_kq * u;
+    if (epi)
+      out_norm_sum(tid, ov, s_ss);
+    else
+      o[nh * kD + tid] = from_f32<T>(ov);
   }
   __syncthreads();
+  if (epi && tid < kD)
+    o[nh * kD + tid] = from_f32<T>(out_norm_apply(tid, ov, zo, s_ss, la.onw, la.oeps));
 
   const f32x4 u4 = *reinterpret_cast<const f32x4 *>(&s_u[4 * cg]);
 #pragma unroll
@@ -106,13 +181,13 @@ __global__ __launch_bounds__(256) void decode_kernel(const T *__restrict__ q,
 // written; the later drafts' states are not kept.  The layout and the step
 // are the decode kernel's: the state is read once and written once however
 // many tokens the call runs.
-template <typename T>
+template <typename T, bool LAYER>
 __global__ __launch_bounds__(256) void replay_kernel(
     int32_t H, int32_t W, int32_t P, const int32_t *__restrict__ accepted,
     const T *__restrict__ ck, const T *__restrict__ cv, const T *__restrict__ cg,
     const T *__restrict__ cb, const T *__restrict__ q, const T *__restrict__ k,
     const T *__restrict__ v, const T *__restrict__ g, const T *__restrict__ beta,
-    float *__restrict__ state, T *__restrict__ o) {
+    float *__restrict__ state, T *__restrict__ o, LayerArgs<T> la) {
   const int64_t nh = blockIdx.x;
   const int n = (int)(nh / H), h = (int)(nh - (int64_t)n * H);
   const int tid = threadIdx.x;
@@ -121,7 +196,7 @@ __global__ __launch_bounds__(256) void replay_kernel(
 
   __shared__ float s_k[kD], s_q[kD], s_a[kD], s_v[kD], s_u[kD];
   __shared__ float s_w[8][kD], s_y[8][kD];
-  __shared__ float s_kq, s_beta;
+  __shared__ float s_kq, s_beta, s_ik, s_iq, s_ss[2];
 
   float *S = state + nh * (int64_t)(kD * kD);
   f32x4 s[16];
@@ -129,6 +204,10 @@ __global__ __launch_bounds__(256) void replay_kernel(
   for (int i = 0; i < 16; ++i)
     s[i] = __builtin_nontemporal_load(
         reinterpret_cast<const f32x4 *>(S + (16 * rg + i) * kD + 4 * cg4));
+  // the layer's steps apply to cached and new tokens alike (per token,
+  // elementwise or per row), so the cache may hold the raw inputs
+  const bool epi = LAYER && la.ogate != nullptr;
+  const float ea = (LAYER && la.A_log) ? __expf(la.A_log[h]) : 1.f;
 
   const int m = min(max(accepted[n], 0), W); // accepted draft tokens to replay
   const int total = m + P;
@@ -136,10 +215,10 @@ __global__ __launch_bounds__(256) void replay_kernel(
   // one token's inputs for thread tid < 128 (element tid of k, g, v, q) and
   // beta; the next token's are loaded while the current one is stepped
   struct TokIn {
-    float k, g, v, q, b;
+    float k, g, v, q, b, z;
   };
   auto load_tok = [&](int t) {
-    TokIn x = {0.f, 0.f, 0.f, 0.f, 0.f};
+    TokIn x = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (t >= total)
       return x;
     const bool out = t >= m;
@@ -150,6 +229,8 @@ __global__ __launch_bounds__(256) void replay_kernel(
       x.v = to_f32((out ? v : cv)[tok * kD + tid]);
       if (out) // (q may be null when P = 0)
         x.q = to_f32(q[tok * kD + tid]);
+      if (out && epi)
+        x.z = to_f32(la.ogate[tok * kD + tid]);
     }
     if (tid == 0)
       x.b = to_f32((out ? beta : cb)[tok]);
@@ -161,7 +242,7 @@ __global__ __launch_bounds__(256) void replay_kernel(
     const int64_t tok = out ? ((int64_t)n * P + (t - m)) * H + h : 0;
     if (tid < kD) {
       s_k[tid] = cur.k;
-      s_a[tid] = __expf(cur.g);
+      s_a[tid] = __expf((LAYER && la.A_log) ? gate_log_decay(cur.g, ea, la.g_min) : cur.g);
       s_v[tid] = cur.v;
       s_q[tid] = cur.q;
     }
@@ -170,14 +251,8 @@ __global__ __launch_bounds__(256) void replay_kernel(
     const TokIn nxt = load_tok(t + 1);
     __syncthreads();
 
-    if (tid < 64) { // k . q, inside wave 0
-      float p = s_k[tid] * s_q[tid] + s_k[tid + 64] * s_q[tid + 64];
-#pragma unroll
-      for (int mm = 32; mm >= 1; mm >>= 1)
-        p += __shfl_xor(p, mm);
-      if (tid == 0)
-        s_kq = p;
-    }
+    // k . q (and the inverse norms), inside wave 0
+    kq_norms<LAYER>(tid, s_k, s_q, la, &s_kq, &s_ik, &s_iq);
     f32x4 w = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -190,6 +265,7 @@ __global__ __launch_bounds__(256) void replay_kernel(
     *reinterpret_cast<f32x4 *>(&s_y[rg][4 * cg4]) = y;
     __syncthreads();
 
+    float ov = 0.f;
     if (tid < kD) {
       float ws = 0.f, ys = 0.f;
 #pragma unroll
@@ -197,12 +273,18 @@ __global__ __launch_bounds__(256) void replay_kernel(
         ws += s_w[r][tid];
         ys += s_y[r][tid];
       }
-      const float u = s_beta * (s_v[tid] - ws);
-      s_u[tid] = u;
-      if (out)
-        o[tok * kD + tid] = from_f32<T>(ys + s_kq * u);
+      const float ik = LAYER ? s_ik : 1.f, iq = LAYER ? s_iq : 1.f;
+      const float u = s_beta * (s_v[tid] - ik * ws);
+      s_u[tid] = ik * u;
+      ov = iq * ys + s_kq * u;
+      if (out && epi)
+        out_norm_sum(tid, ov, s_ss);
+      else if (out)
+        o[tok * kD + tid] = from_f32<T>(ov);
     }
     __syncthreads();
+    if (out && epi && tid < kD)
+      o[tok * kD + tid] = from_f32<T>(out_norm_apply(tid, ov, cur.z, s_ss, la.onw, la.oeps));
 
     const f32x4 u4 = *reinterpret_cast<const f32x4 *>(&s_u[4 * cg4]);
 #pragma unroll
@@ -219,42 +301,51 @@ __global__ __launch_bounds__(256) void replay_kernel(
   }
 }
 
+template <typename T> static LayerArgs<T> layer_args(const Epilogue &epi, const Prologue &pro) {
+  return LayerArgs<T>{pro.A_log, pro.g_min, pro.qk_eps, (const T *)epi.gate, epi.weight, epi.eps};
+}
+
 hipError_t launch_replay(int elt, int32_t N, int32_t H, int32_t W, const int32_t *accepted,
                          const void *ck, const void *cv, const void *cg, const void *cb,
                          int32_t P, const void *q, const void *k, const void *v, const void *g,
-                         const void *beta, float *state, void *o, hipStream_t s) {
+                         const void *beta, float *state, void *o, const Prologue &pro,
+                         const Epilogue &epi, hipStream_t s) {
   const int64_t nh = (int64_t)N * H;
   if (nh == 0)
     return hipSuccess;
   dim3 grid((unsigned)nh), block(256);
+  const bool layer = pro.on() || epi.on();
+  auto run = [&](auto kern, auto tag) {
+    using T = decltype(tag);
+    kern<<<grid, block, 0, s>>>(H, W, P, accepted, (const T *)ck, (const T *)cv, (const T *)cg,
+                                (const T *)cb, (const T *)q, (const T *)k, (const T *)v,
+                                (const T *)g, (const T *)beta, state, (T *)o,
+                                layer_args<T>(epi, pro));
+  };
   if (elt == 1)
-    replay_kernel<bf16><<<grid, block, 0, s>>>(
-        H, W, P, accepted, (const bf16 *)ck, (const bf16 *)cv, (const bf16 *)cg,
-        (const bf16 *)cb, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (const bf16 *)g,
-        (const bf16 *)beta, state, (bf16 *)o);
+    layer ? run(replay_kernel<bf16, true>, bf16()) : run(replay_kernel<bf16, false>, bf16());
   else
-    replay_kernel<float><<<grid, block, 0, s>>>(
-        H, W, P, accepted, (const float *)ck, (const float *)cv, (const float *)cg,
-        (const float *)cb, (const float *)q, (const float *)k, (const float *)v,
-        (const float *)g, (const float *)beta, state, (float *)o);
+    layer ? run(replay_kernel<float, true>, 0.f) : run(replay_kernel<float, false>, 0.f);
   return hipGetLastError();
 }
 
 hipError_t launch_decode(int elt, int32_t N, int32_t H, const void *q, const void *k,
                          const void *v, const void *g, const void *beta, float *state, void *o,
-                         hipStream_t s) {
+                         const Prologue &pro, const Epilogue &epi, hipStream_t s) {
   const int64_t nh = (int64_t)N * H;
   if (nh == 0)
     return hipSuccess;
   dim3 grid((unsigned)nh), block(256);
+  const bool layer = pro.on() || epi.on();
+  auto run = [&](auto kern, auto tag) {
+    using T = decltype(tag);
+    kern<<<grid, block, 0, s>>>((const T *)q, (const T *)k, (const T *)v, (const T *)g,
+                                (const T *)beta, state, (T *)o, H, layer_args<T>(epi, pro));
+  };
   if (elt == 1)
-    decode_kernel<bf16><<<grid, block, 0, s>>>(
-        (const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (const bf16 *)g,
-        (const bf16 *)beta, state, (bf16 *)o);
+    layer ? run(decode_kernel<bf16, true>, bf16()) : run(decode_kernel<bf16, false>, bf16());
   else
-    decode_kernel<float><<<grid, block, 0, s>>>(
-        (const float *)q, (const float *)k, (const float *)v, (const float *)g,
-        (const float *)beta, state, (float *)o);
+    layer ? run(decode_kernel<float, true>, 0.f) : run(decode_kernel<float, false>, 0.f);
   return hipGetLastError();
 }
 

@@ -173,13 +173,16 @@ hipError_t launch_scan(const ScanDesc *descs, int32_t ndesc, int32_t H, const fl
                        const float *Stseg, const float *init, float *sin, hipStream_t s);
 
 // Speculative-decode replay: m accepted cached tokens, then P new tokens.
+// The prologue applies to cached and new tokens, the epilogue to the new
+// tokens' outputs.
 hipError_t launch_replay(int elt, int32_t N, int32_t H, int32_t W, const int32_t *accepted,
                          const void *ck, const void *cv, const void *cg, const void *cb,
                          int32_t P, const void *q, const void *k, const void *v, const void *g,
-                         const void *beta, float *state, void *o, hipStream_t s);
+                         const void *beta, float *state, void *o, const Prologue &pro,
+                         const Epilogue &epi, hipStream_t s);
 
 hipError_t launch_decode(int elt, int32_t N, int32_t H, const void *q, const void *k,
                          const void *v, const void *g, const void *beta, float *state, void *o,
-                         hipStream_t s);
+                         const Prologue &pro, const Epilogue &epi, hipStream_t s);
 
 } // namespace kda

@@ -258,6 +258,21 @@ kda_status kda_decode_step(int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dty
                            const void *beta, float *state, void *o, void *stream);
 
 /*
+ * kda_decode_step with the layer's steps fused in ("Kimi K3.1 Pro 架构完全拆解"
+ * §3.4: the decode kernel also does the input normalization, the gating and
+ * the output norm; §3.2, §3.3 for the steps): A_log, g_min, qk_norm_eps,
+ * out_gate ([N, H, dv] of type dt), out_norm_weight and out_norm_eps mean
+ * what they mean for kda_chunk_prefill_gated.  The state stays the
+ * recurrence's.
+ */
+kda_status kda_decode_step_gated(int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
+                                 const void *q, const void *k, const void *v, const void *g,
+                                 const void *beta, const float *A_log, float g_min,
+                                 float qk_norm_eps, const void *out_gate,
+                                 const float *out_norm_weight, float out_norm_eps,
+                                 float *state, void *o, void *stream);
+
+/*
  * Speculative-decode replay for N sequences ("Kimi K3.1 Pro 架构完全拆解"
  * §3.4; "部署 Kimi K3：从 KDA Kernel 到 Fleet 调度" §四): the state is not
  * rolled back from a snapshot but rebuilt from the cached projected inputs
@@ -289,6 +304,22 @@ kda_status kda_decode_replay(int32_t N, int32_t H, int32_t dk, int32_t dv, kda_d
                              const void *cg, const void *cbeta, int32_t P, const void *q,
                              const void *k, const void *v, const void *g, const void *beta,
                              float *state, void *o, void *stream);
+
+/*
+ * kda_decode_replay with the layer's steps fused in (as
+ * kda_decode_step_gated).  The gate and the q / k norms apply to the cached
+ * tokens as to the new ones, so the window cache holds the raw inputs (with
+ * A_log, cg holds gate logits like g); out_gate is [N, P, H, dv] of type dt,
+ * the new tokens' output gate logits.
+ */
+kda_status kda_decode_replay_gated(int32_t N, int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
+                                   int32_t W, const int32_t *accepted, const void *ck,
+                                   const void *cv, const void *cg, const void *cbeta, int32_t P,
+                                   const void *q, const void *k, const void *v, const void *g,
+                                   const void *beta, const float *A_log, float g_min,
+                                   float qk_norm_eps, const void *out_gate,
+                                   const float *out_norm_weight, float out_norm_eps,
+                                   float *state, void *o, void *stream);
 
 /*
  * Segment transition pairs ("部署 Kimi K3：从 KDA Kernel 到 Fleet 调度", §二,

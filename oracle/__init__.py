@@ -316,3 +316,28 @@ def prefill_gated(q, k, v, beta, g=None, z=None, A_log=None, g_min=G_MIN, qk_nor
     if out_gate is not None:
         o = gated_rmsnorm(o, out_gate, out_norm_weight, out_norm_eps)
     return o, fin
+
+
+def decode_replay_gated(state, accepted, ck, cv, cz, cbeta, q, k, v, z, beta, A_log=None,
+                        g_min=G_MIN, qk_norm_eps=None, out_gate=None, out_norm_weight=None,
+                        out_norm_eps=1e-6, threads: int = 0):
+    """Speculative-decode replay with the layer's steps ("Kimi K3.1 Pro 架构完全拆解"
+    §3.4): every token, cached or new, has its decay gate (from the logits
+    cz / z when A_log is given, else they are the log decay) and its q / k
+    norm applied before the recurrence; the new tokens' outputs then get the
+    output norm and gate.  Shapes as for :func:`decode_replay`; out_gate
+    ``[N, P, H, dv]``."""
+    def gate(x):
+        if A_log is None:
+            return _f64(x)
+        x = _f64(x)
+        return gate_log_decay(x.reshape(-1, *x.shape[2:]), A_log, g_min).reshape(x.shape)
+
+    def norm(x):
+        return _f64(x) if qk_norm_eps is None else l2_normalize(x, qk_norm_eps)
+
+    o, committed = decode_replay(state, accepted, norm(ck), cv, gate(cz), cbeta, norm(q),
+                                 norm(k), v, gate(z), beta, threads=threads)
+    if out_gate is not None:
+        o = gated_rmsnorm(o, out_gate, out_norm_weight, out_norm_eps)
+    return o, committed

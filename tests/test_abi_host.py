@@ -278,3 +278,25 @@ def test_num_checkpoints(lib):
         4, p, bad.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), 512) == -1
     a2, p2 = cu(0, 100, 50)                                            # decreasing
     assert lib.kda_prefill_num_checkpoints(2, p2, None, 64) == -1
+
+
+def test_gated_decode_argument_errors(lib):
+    E = nat
+    GATE = ctypes.c_void_p(0x200000)
+
+    def step(gmin=-5.0, qe=1e-6, og=GATE, oe=1e-6, o=FAKE, N=2):
+        return lib.kda_decode_step_gated(N, 2, 128, 128, nat.KDA_BF16, FAKE, FAKE, FAKE, FAKE,
+                                         FAKE, FAKE, gmin, qe, og, None, oe, FAKE, o, None)
+
+    def rep(gmin=-5.0, qe=1e-6, og=GATE, oe=1e-6, o=FAKE, N=2):
+        return lib.kda_decode_replay_gated(N, 2, 128, 128, nat.KDA_BF16, 4, FAKE, FAKE, FAKE,
+                                           FAKE, FAKE, 3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                           gmin, qe, og, None, oe, FAKE, o, None)
+
+    for fn in (step, rep):
+        assert fn(gmin=-6.0) == E.KDA_ERR_INVALID_ARG
+        assert fn(qe=-1.0) == E.KDA_ERR_INVALID_ARG
+        assert fn(oe=0.0) == E.KDA_ERR_INVALID_ARG
+        assert fn(og=FAKE) == E.KDA_ERR_INVALID_ARG       # the gate may not be o
+        assert fn(og=ctypes.c_void_p(0x200001)) == E.KDA_ERR_INVALID_ARG
+        assert fn(N=0) == E.KDA_OK

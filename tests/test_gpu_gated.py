@@ -194,3 +194,82 @@ def test_gated_epilogue_exact_recurrence_bf16(path, monkeypatch):
     bound = 2.0 ** -8 * np.abs(y_ref) + 1e-6 * float(np.max(np.abs(y_ref)))
     assert float(np.max(np.abs(y - y_ref) / bound)) <= 1.0
     np.testing.assert_array_equal(fin.cpu().numpy(), f_ref)
+
+
+# --- decode and replay with the layer's steps -------------------------------
+
+
+def check_norm_bound(y, y_ref, ot_ref, gate, nw, dtype):
+    """The output-norm bar of this file's docstring, for any output layout
+    (rows over the last axis)."""
+    if dtype == torch.float32:
+        assert rel_err(y, y_ref) <= TOL[dtype]
+        return
+    E = TOL[dtype] * float(np.max(np.abs(ot_ref)))
+    r = np.sqrt(np.mean(ot_ref * ot_ref, axis=-1, keepdims=True) + OUT_EPS)
+    g = gate.detach().cpu().double().numpy()
+    w = np.ones(ot_ref.shape[-1]) if nw is None else nw.detach().cpu().double().numpy()
+    s = np.abs(w / (1.0 + np.exp(-g)))
+    with np.errstate(divide="ignore"):
+        lo = np.where(r > E, r - E, 0.0)
+        bound = s * E * (1.0 + np.abs(ot_ref) / r) / lo + 2.0 ** -8 * np.abs(y_ref)
+    yy = y.detach().cpu().double().numpy()
+    assert np.all(np.isfinite(yy))
+    assert float(np.max(np.abs(yy - y_ref) / bound)) <= 1.0
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_decode_step_gated(dtype):
+    N, H, steps = 5, 3, 4
+    print("gated decode", N, H, steps, dtype, flush=True)
+    d = wl.raw_layer_inputs(N * steps, H, dtype, 610, device=DEV)
+    state = wl.states(N, H, 611, device=DEV)
+    ref = state.detach().cpu().double().numpy()
+    cu = np.arange(N + 1, dtype=np.int64)
+    for s_ in range(steps):
+        sl = slice(s_ * N, (s_ + 1) * N)
+        o = kda.decode_step_gated(state, d["q"][sl], d["k"][sl], d["v"][sl], d["z"][sl],
+                                  d["beta"][sl], A_log=d["A_log"], qk_norm_eps=QK_EPS,
+                                  out_gate=d["out_gate"][sl], out_norm_weight=d["norm_weight"],
+                                  out_norm_eps=OUT_EPS)
+        torch.cuda.synchronize()
+        kw = dict(z=d["z"][sl], A_log=d["A_log"], qk_norm_eps=QK_EPS, cu_seqlens=cu,
+                  initial_state=ref)
+        ot_ref, _ = oracle.prefill_gated(d["q"][sl], d["k"][sl], d["v"][sl], d["beta"][sl],
+                                         **kw)
+        y_ref, ref = oracle.prefill_gated(d["q"][sl], d["k"][sl], d["v"][sl], d["beta"][sl],
+                                          out_gate=d["out_gate"][sl],
+                                          out_norm_weight=d["norm_weight"],
+                                          out_norm_eps=OUT_EPS, **kw)
+        check_norm_bound(o, y_ref, ot_ref, d["out_gate"][sl], d["norm_weight"], dtype)
+    assert rel_err(state, ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("epi", [True, False])
+def test_decode_replay_gated(dtype, epi):
+    N, H, W, P = 6, 2, 4, 5
+    print("gated replay", N, H, W, P, dtype, epi, flush=True)
+    c = wl.raw_layer_inputs(N * W, H, dtype, 620, device=DEV)
+    x = wl.raw_layer_inputs(N * P, H, dtype, 621, device=DEV)
+    shp = lambda t, L: t.reshape(N, L, *t.shape[1:]).contiguous()
+    ck, cv, cz, cb = (shp(c[n], W) for n in ("k", "v", "z", "beta"))
+    q, k, v, z, b, og = (shp(x[n], P) for n in ("q", "k", "v", "z", "beta", "out_gate"))
+    acc = torch.tensor([0, 1, 4, 2, 7, -1], dtype=torch.int32, device=DEV)
+    state = wl.states(N, H, 622, device=DEV)
+    S0 = state.detach().cpu().double().numpy()
+    o = kda.decode_replay_gated(state, acc, ck, cv, cz, cb, q, k, v, z, b, A_log=x["A_log"],
+                                qk_norm_eps=QK_EPS, out_gate=og if epi else None,
+                                out_norm_weight=x["norm_weight"], out_norm_eps=OUT_EPS)
+    torch.cuda.synchronize()
+    kw = dict(A_log=x["A_log"], qk_norm_eps=QK_EPS)
+    ot_ref, committed = oracle.decode_replay_gated(S0, acc.cpu().numpy(), ck, cv, cz, cb, q, k,
+                                                   v, z, b, **kw)
+    if epi:
+        y_ref, _ = oracle.decode_replay_gated(S0, acc.cpu().numpy(), ck, cv, cz, cb, q, k, v, z,
+                                              b, out_gate=og, out_norm_weight=x["norm_weight"],
+                                              out_norm_eps=OUT_EPS, **kw)
+        check_norm_bound(o, y_ref, ot_ref, og, x["norm_weight"], dtype)
+    else:
+        assert rel_err(o, ot_ref) <= TOL[dtype]
+    assert rel_err(state, committed) <= TOL[dtype]
