@@ -101,3 +101,64 @@ def test_decode_f32_N256_H96_64_steps_sampled():
                                          initial_state=init[n, h][None, None])
         assert rel_err(outs[:, n, h], o_ref[:, 0]) <= 1e-4
         assert rel_err(state[n, h], f_ref[0, 0]) <= 1e-4
+
+
+# --- the gated call (kda_chunk_prefill_gated) at full size -------------------
+# As the benchmark times it: the workload's g serves as the decay gate's
+# logits and its v as the output gate's; A_log and the norm weight are fixed
+# per head / channel.  o is held to the output-norm bound of
+# tests/test_gpu_gated.py (derived from the plain bar), the states to the
+# plain bar.
+
+
+def run_gated(name):
+    w = wl.WORKLOADS[name]
+    say("gated workload", name)
+    d = wl.prefill_case(w, device=DEV)
+    A = torch.linspace(-1.0, 1.0, w.H, device=DEV, dtype=torch.float32)
+    nw = 1.0 + 0.1 * torch.cos(torch.arange(128, device=DEV, dtype=torch.float32))
+    o, fin = kda.chunk_prefill_gated(d["q"], d["k"], d["v"], d["g"], d["beta"], A_log=A,
+                                     qk_norm_eps=1e-6, out_gate=d["v"], out_norm_weight=nw,
+                                     out_norm_eps=1e-6, cu_seqlens=d["cu"],
+                                     initial_state=d["init"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(fin).all()
+    return w, d, A, nw, o, fin
+
+
+def check_heads_gated(w, d, A, nw, o, fin, seqs, heads):
+    cu = d["cu"]
+    tol = TOL[w.dtype]
+    wn = nw.cpu().double().numpy()
+    for n in seqs:
+        a, b = int(cu[n]), int(cu[n + 1])
+        sl = {x: d[x][a:b, heads] for x in ("q", "k", "v", "g", "beta")}
+        init = None if d["init"] is None else d["init"][n:n + 1, heads]
+        kw = dict(z=sl["g"], A_log=A[heads], qk_norm_eps=1e-6, initial_state=init)
+        ot, f_ref = oracle.prefill_gated(sl["q"], sl["k"], sl["v"], sl["beta"], **kw)
+        y_ref, _ = oracle.prefill_gated(sl["q"], sl["k"], sl["v"], sl["beta"], out_gate=sl["v"],
+                                        out_norm_weight=nw, out_norm_eps=1e-6, **kw)
+        y = o[a:b, heads].detach().cpu().double().numpy()
+        assert np.all(np.isfinite(y))
+        E = tol * float(np.max(np.abs(ot)))
+        r = np.sqrt(np.mean(ot * ot, axis=-1, keepdims=True) + 1e-6)
+        s = np.abs(wn / (1.0 + np.exp(-sl["v"].detach().cpu().double().numpy())))
+        with np.errstate(divide="ignore"):
+            lo = np.where(r > E, r - E, 0.0)
+            bound = s * E * (1.0 + np.abs(ot) / r) / lo + 2.0 ** -8 * np.abs(y_ref)
+        ex = float(np.max(np.abs(y - y_ref) / bound))
+        ef = rel_err(fin[n:n + 1, heads], f_ref)
+        say("  seq %d len %d heads %s: o vs bound %.3g, err_S %.3g" % (n, b - a, heads, ex, ef))
+        assert ex <= 1.0 and ef <= tol
+
+
+def test_gated_prefill_bf16_T8192_H96_sampled_heads():
+    w, d, A, nw, o, fin = run_gated("prefill_bf16_T8192_H96")
+    check_heads_gated(w, d, A, nw, o, fin, [0], list(range(0, 96, 16)))
+
+
+def test_gated_prefill_bf16_varlen64_H96_resume_sampled():
+    w, d, A, nw, o, fin = run_gated("prefill_bf16_varlen64_H96_resume")
+    lens = np.diff(d["cu"])
+    seqs = sorted({int(np.argmin(lens)), 17})
+    check_heads_gated(w, d, A, nw, o, fin, seqs, [0, 95])
