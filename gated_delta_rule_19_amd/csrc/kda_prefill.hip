@@ -657,9 +657,17 @@ template <typename T, int NW> struct RecordCopy {
   }
   __device__ __forceinline__ static void issue(uint8_t *lds, const uint8_t *src,
                                                const int (&goff)[kPerWave], int wv) {
+    issue_part<0, 1>(lds, src, goff, wv);
+  }
+  // Part P of NP of this wave's blocks (the copy spread over a phase's
+  // products, so that the wave's instruction issue never waits behind a
+  // burst of copies)
+  template <int P, int NP>
+  __device__ __forceinline__ static void issue_part(uint8_t *lds, const uint8_t *src,
+                                                    const int (&goff)[kPerWave], int wv) {
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc(src, (uint32_t)k1_record_bytes(sizeof(T)));
 #pragma unroll
-    for (int j = 0; j < kPerWave; ++j) {
+    for (int j = P * kPerWave / NP; j < (P + 1) * kPerWave / NP; ++j) {
       const int b = wv + j * NW; // wave-uniform
       if (b >= L::blocks)
         break;
@@ -697,6 +705,17 @@ __global__ __launch_bounds__(k2_threads(BV, NCT)) void k2_kernel(
   constexpr bool VLDS = sizeof(T) == 2;
   constexpr int VW = 16 * NCT;
   __shared__ __attribute__((aligned(16))) T sv[VLDS ? NW : 1][VLDS ? kC * VW : 1];
+  // bf16 o of up to 4 waves leaves through a per-wave LDS tile: the
+  // accumulator layout holds 4 rows of one column per lane, so direct stores
+  // are 16 two-byte stores per lane; the tile read back row-wise is two
+  // 16-byte stores (the 8-wave block has no LDS left for it).  The tile of
+  // chunk ch is written to LDS in chunk ch and leaves at the start of chunk
+  // ch + 1, after the barrier that waited for the next record's copy: any
+  // memory operation of this wave while that copy is in flight waits for it
+  // (a store behind the copy's instructions, an LDS read for its possible
+  // aliasing), which cost a sixth of the chunk step.
+  constexpr bool OT = VLDS && MODE == 0 && NW <= 4 && NCT == 1 && !EPI;
+  __shared__ __attribute__((aligned(16))) T sot[OT ? NW : 1][OT ? kC * VW : 1];
   // output norm: per-wave partial sums of squares of each token row, and each
   // wave's own copy of the rows' scale factors
   __shared__ __attribute__((aligned(16))) float sRed[EPI ? NW : 1][EPI ? kC : 1];
@@ -871,12 +890,39 @@ __global__ __launch_bounds__(k2_threads(BV, NCT)) void k2_kernel(
     // the chain's next checkpoint chunk and its index (wave-uniform)
     [[maybe_unused]] int ck_next = cd.ckpt_chunk, ck_idx = cd.ckpt_idx;
 
+    // o of chunk ch from this wave's LDS tile (OT): row lane / 2 (+ 32),
+    // columns 8 (lane % 2) .. + 7; rows past the chunk end fall outside the
+    // buffer and are dropped
+    [[maybe_unused]] auto flush_o = [&](int ch) {
+      if constexpr (OT) {
+        const int len = min(kC, cd.ntok - ch * kC);
+        const int64_t tok = cd.tok0 + (int64_t)ch * kC;
+        const __amdgpu_buffer_rsrc_t ro =
+            buffer_rsrc(o + tok * rowstride + (int64_t)h * kD,
+                        (uint32_t)((len - 1) * rowstride + kD) * sizeof(T));
+        const T *ot = &sot[wv][0];
+        const int ln = opaque_lane();
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int r = 32 * j + (ln >> 1), c8 = 8 * (ln & 1);
+          const bf16x8 x = *reinterpret_cast<const bf16x8 *>(&ot[r * VW + c8]);
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(u32x4, x), ro,
+              (int)((r * rowstride + vcol0 + VW * wv + c8) * sizeof(T)), 0, 0);
+        }
+      }
+    };
+
     // One chunk: computes from the record image in `cur` while chunk ch+1's
     // record goes into `nxt`.  The buffers are distinct LDS objects and the
     // loop is unrolled by two, so every access names its buffer statically
     // and the compiler does not make reads of `cur` wait for the copy.
     auto chunk_step = [&](const int ch, uint8_t *cur, uint8_t *nxt)
                           __attribute__((always_inline)) {
+      if constexpr (OT) {
+        if (ch > 0)
+          flush_o(ch - 1);
+      }
       const int len = min(kC, cd.ntok - ch * kC);
       const int64_t tok = cd.tok0 + (int64_t)ch * kC;
       const bool more = ch + 1 < nch;
@@ -904,10 +950,11 @@ __global__ __launch_bounds__(k2_threads(BV, NCT)) void k2_kernel(
       if (more) {
         if constexpr (!VLDS)
           load_v(vnxt, ch + 1);
-        if (NBUF == 2)
-          RCopy::issue(nxt, rec0 + (int64_t)(ch + 1) * rec_step, goff, wv);
       }
       __builtin_amdgcn_sched_barrier(0); // keep the loads issued here, ahead of the math
+      // (the record copy of chunk ch+1 is issued in four parts over the
+      // first phase's k-steps below)
+      const uint8_t *rec_nxt = rec0 + (int64_t)(ch + 1) * rec_step;
 
       const uint8_t *R = cur;
       const T *Qd = reinterpret_cast<const T *>(R + L::qd);
@@ -953,6 +1000,16 @@ __global__ __launch_bounds__(k2_threads(BV, NCT)) void k2_kernel(
       Frag<T> ai[2][4]; // INV Diag(beta) fragments, read during the last step
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
+        if (NBUF == 2 && more) {
+          if (s == 0)
+            RCopy::template issue_part<0, 4>(nxt, rec_nxt, goff, wv);
+          else if (s == 1)
+            RCopy::template issue_part<1, 4>(nxt, rec_nxt, goff, wv);
+          else if (s == 2)
+            RCopy::template issue_part<2, 4>(nxt, rec_nxt, goff, wv);
+          else
+            RCopy::template issue_part<3, 4>(nxt, rec_nxt, goff, wv);
+        }
         Frag<T> nk[4], nq[4];
         if (s < 3) {
 #pragma unroll
@@ -1064,16 +1121,27 @@ __global__ __launch_bounds__(k2_threads(BV, NCT)) void k2_kernel(
         const __amdgpu_buffer_rsrc_t ro =
             buffer_rsrc(o + tok * rowstride + (int64_t)h * kD,
                         (uint32_t)((len - 1) * rowstride + kD) * sizeof(T));
-        const int vo = (int)((4 * lg * rowstride + wcol) * sizeof(T));
+        if constexpr (OT) {
+          // tile row 16 tt + 4 lg + i, column lr (flush_o at the start of
+          // the next chunk, or after the last)
+          T *ot = &sot[wv][0];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+          for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int so = (int)((16 * tt + i) * rowstride * sizeof(T)); // wave-uniform
+            for (int i = 0; i < 4; ++i)
+              ot[(16 * tt + 4 * lg + i) * VW + lr] = from_f32<T>(Oa[0][tt][i]);
+        } else {
+          const int vo = (int)((4 * lg * rowstride + wcol) * sizeof(T));
 #pragma unroll
-            for (int c = 0; c < NCT; ++c)
-              buffer_store(ro, from_f32<T>(Oa[c][tt][i]), vo + 16 * c * (int)sizeof(T), so);
-          }
+          for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int so = (int)((16 * tt + i) * rowstride * sizeof(T)); // wave-uniform
+#pragma unroll
+              for (int c = 0; c < NCT; ++c)
+                buffer_store(ro, from_f32<T>(Oa[c][tt][i]), vo + 16 * c * (int)sizeof(T), so);
+            }
+        }
       }
       // S = Diag(a_last) S + K_restore^T U, in two halves of 4 row tiles
 #pragma unroll
@@ -1154,6 +1222,8 @@ __global__ __launch_bounds__(k2_threads(BV, NCT)) void k2_kernel(
       for (int ch = 0; ch < nch; ++ch)
         chunk_step(ch, srecA, srecA);
     }
+    if constexpr (OT)
+      flush_o(nch - 1);
   }
 
   float *fp = nullptr;
