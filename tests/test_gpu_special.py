@@ -1,0 +1,152 @@
+"""GPU prefill and decode on the method's degenerate gates, checked against
+closed forms of the recurrence S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1}
++ beta_t k_t v_t^T, o_t = S_t^T q_t ("Kimi K3.1 Pro 架构完全拆解" §3.1) as well
+as against the oracle:
+
+- beta = 0, g = 0: nothing is written and nothing decays, so every final
+  state is its initial state bit for bit (the write term is an exact zero and
+  the decay an exact one) and o_t = S_0^T q_t;
+- beta = 0: pure per-channel decay, S_t = Diag(exp(G_t)) S_0 with G_t the
+  running sum of g over the sequence;
+- beta = 1, g = 0, orthonormal keys: each write overwrites its own key's
+  direction only, so S_T^T k_t = v_t for every token t (fp32).
+
+Each case runs through the bf16 kernels (fused and two-kernel), the fp32
+kernels and the sequence-split planner.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import gated_delta_rule_19_amd as kda
+from gated_delta_rule_19_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = {torch.float32: 1e-4, torch.bfloat16: 1e-2}
+LENGTHS = [70, 130, 1]
+H = 3
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def rel_err(x, ref):
+    x = x.detach().cpu().double().numpy() if isinstance(x, torch.Tensor) else np.asarray(x)
+    ref = ref.detach().cpu().double().numpy() if isinstance(ref, torch.Tensor) else ref
+    assert x.shape == ref.shape
+    assert np.all(np.isfinite(x))
+    return float(np.max(np.abs(x - ref)) / max(float(np.max(np.abs(ref))), 1e-30))
+
+
+@pytest.fixture(params=["fp32", "bf16_fused", "bf16_two_kernel", "fp32_split", "bf16_split"])
+def path(request, monkeypatch):
+    """(dtype, split_hint) of one prefill implementation; the library reads
+    KDA_FUSED_PREFILL at every call."""
+    name = request.param
+    dtype = torch.float32 if name.startswith("fp32") else torch.bfloat16
+    split = 2 if name.endswith("split") else 0
+    if name.startswith("bf16"):
+        monkeypatch.setenv("KDA_FUSED_PREFILL", "1" if name == "bf16_fused" else "0")
+    say("special-gate path:", name)
+    return dtype, split
+
+
+def decayed_reference(q, g, S0, lengths):
+    """o_t = (Diag(exp(G_t)) S_0)^T q_t and the final Diag(exp(G_T)) S_0 per
+    sequence, in fp64 (the beta = 0 closed form)."""
+    q = q.detach().cpu().double()
+    g = g.detach().cpu().double()
+    S0 = S0.detach().cpu().double()
+    o = torch.zeros(q.shape, dtype=torch.float64)
+    fin = S0.clone()
+    t0 = 0
+    for n, L in enumerate(lengths):
+        if L:
+            G = torch.cumsum(g[t0:t0 + L], dim=0)               # [L, H, dk]
+            St = torch.exp(G)[..., None] * S0[n][None]          # [L, H, dk, dv]
+            o[t0:t0 + L] = torch.einsum("thkv,thk->thv", St, q[t0:t0 + L])
+            fin[n] = St[-1]
+        t0 += L
+    return o, fin
+
+
+def test_no_write_no_decay_keeps_state(path):
+    dtype, split = path
+    cu = wl.cu_from_lengths(LENGTHS)
+    d = wl.token_inputs(int(cu[-1]), H, dtype, 901, device=DEV)
+    d["g"].zero_()
+    d["beta"].zero_()
+    S0 = wl.states(len(LENGTHS), H, 902, device=DEV)
+    o, fin = kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu,
+                               initial_state=S0, split_hint=split)
+    torch.cuda.synchronize()
+    # the state is carried through unchanged: an exact zero write, an exact one decay
+    assert torch.equal(fin, S0), float((fin - S0).abs().max())
+    o_ref, _ = decayed_reference(d["q"], d["g"], S0, LENGTHS)
+    assert rel_err(o, o_ref) <= TOL[dtype]
+
+
+def test_no_write_is_pure_decay(path):
+    dtype, split = path
+    cu = wl.cu_from_lengths(LENGTHS)
+    d = wl.token_inputs(int(cu[-1]), H, dtype, 903, device=DEV, decay="mild")
+    d["beta"].zero_()
+    S0 = wl.states(len(LENGTHS), H, 904, device=DEV)
+    o, fin = kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu,
+                               initial_state=S0, split_hint=split)
+    torch.cuda.synchronize()
+    o_ref, f_ref = decayed_reference(d["q"], d["g"], S0, LENGTHS)
+    assert rel_err(o, o_ref) <= TOL[dtype]
+    assert rel_err(fin, f_ref) <= TOL[dtype]
+    # and the oracle agrees with the closed form
+    o_or, f_or = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu,
+                                   initial_state=S0)
+    assert rel_err(o_or, o_ref.numpy()) <= 1e-12
+    assert rel_err(f_or, f_ref.numpy()) <= 1e-12
+
+
+@pytest.mark.parametrize("split", [0, 2])
+@pytest.mark.parametrize("T", [64, 100, 128])
+def test_orthonormal_keys_recall_values(T, split):
+    # beta = 1, no decay, keys orthonormal within each head: after the last
+    # token, S^T k_t = v_t for every t, whatever the initial state
+    say("orthonormal recall", dict(T=T, split=split))
+    gen = torch.Generator().manual_seed(905 + T)
+    d = wl.token_inputs(T, H, torch.float32, 906 + T, device=DEV)
+    K = torch.empty((T, H, 128), dtype=torch.float64)
+    for h in range(H):
+        Qm, _ = torch.linalg.qr(torch.randn((128, 128), dtype=torch.float64, generator=gen))
+        K[:, h] = Qm[:T]
+    d["k"] = K.float().to(DEV)
+    d["g"].zero_()
+    d["beta"].fill_(1.0)
+    S0 = wl.states(1, H, 907, device=DEV)
+    o, fin = kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=S0,
+                               split_hint=split)
+    torch.cuda.synchronize()
+    recall = torch.einsum("hkv,thk->thv", fin[0].double().cpu(), d["k"].double().cpu())
+    V = d["v"].double().cpu()
+    assert float((recall - V).abs().max()) <= 1e-4 * float(V.abs().max())
+    o_ref, f_ref = oracle.recurrence(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                     initial_state=S0)
+    assert rel_err(o, o_ref) <= TOL[torch.float32]
+    assert rel_err(fin, f_ref) <= TOL[torch.float32]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_decode_no_write_no_decay_keeps_state(dtype):
+    say("decode special gates", dtype)
+    N = 4
+    d = wl.token_inputs(N, H, dtype, 908, device=DEV)
+    d["g"].zero_()
+    d["beta"].zero_()
+    S = wl.states(N, H, 909, device=DEV)
+    S0 = S.clone()
+    o = kda.decode_step(S, d["q"], d["k"], d["v"], d["g"], d["beta"])
+    torch.cuda.synchronize()
+    assert torch.equal(S, S0)
+    o_ref = torch.einsum("nhkv,nhk->nhv", S0.double().cpu(), d["q"].double().cpu())
+    assert rel_err(o, o_ref) <= TOL[dtype]
