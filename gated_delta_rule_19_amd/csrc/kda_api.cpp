@@ -329,6 +329,17 @@ void staging_release(Staging *s) {
   s->in_use = false;
 }
 
+// The schedule tables are copied from a pinned host buffer that later calls
+// reuse, so a captured copy would read whatever a later call left there at
+// each replay: calls that upload tables refuse a capturing stream (before
+// anything is enqueued).
+kda_status refuse_capture(hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess)
+    return KDA_ERR_HIP;
+  return cs == hipStreamCaptureStatusNone ? KDA_OK : KDA_ERR_UNSUPPORTED;
+}
+
 // Copy the plan's tables into the workspace on `stream`.
 hipError_t upload_tables(const Plan &p, void *ws, hipStream_t stream) {
   if (p.table_bytes == 0)
@@ -433,6 +444,8 @@ kda_status prefill_impl(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_
       return KDA_ERR_WORKSPACE;
   }
   hipStream_t s = (hipStream_t)stream;
+  if (const kda_status cs = refuse_capture(s); cs != KDA_OK)
+    return cs;
   uint8_t *ws = (uint8_t *)workspace;
   const int elt = dt == KDA_BF16 ? 1 : 0;
   const ChunkDesc *d_chunks = (const ChunkDesc *)(ws + p.off_chunks);
@@ -754,6 +767,8 @@ kda_status kda_segment_transition(int32_t num_segs, const int64_t *cu_seglens_ho
       return KDA_ERR_WORKSPACE;
   }
   hipStream_t s = (hipStream_t)stream;
+  if (const kda_status cs = refuse_capture(s); cs != KDA_OK)
+    return cs;
   uint8_t *ws = (uint8_t *)workspace;
   const int elt = dt == KDA_BF16 ? 1 : 0;
   const ChunkDesc *d_chunks = (const ChunkDesc *)(ws + p.off_chunks);

@@ -20,6 +20,12 @@
  *   Every call validates its arguments on the host first; on failure it
  *   returns a negative status and enqueues nothing.  On success the work is
  *   enqueued asynchronously on `stream`; no call synchronises.
+ * - HIP graph capture: the prefill calls and kda_segment_transition upload
+ *   their schedule from a pinned host buffer that later calls reuse, so a
+ *   captured copy would read stale tables on replay; on a stream that is
+ *   capturing they return KDA_ERR_UNSUPPORTED and enqueue nothing.  The
+ *   decode calls (step and replay, plain and gated) upload nothing and
+ *   launch one kernel each; they may be captured.
  * - dk = dv = 128 and the chunk length C = 64 are fixed in this build.
  * - Element type of q, k, v, g, beta and o is `dt`: KDA_F32 (fp32) or
  *   KDA_BF16 (bfloat16).  States, M and S~ are always fp32.  All arithmetic
@@ -54,7 +60,7 @@ typedef int32_t kda_status;
 
 #define KDA_OK 0
 #define KDA_ERR_INVALID_ARG (-1) /* NULL required pointer, bad size, bad cu_seqlens, misaligned */
-#define KDA_ERR_UNSUPPORTED (-2) /* dk/dv other than 128, unknown dtype */
+#define KDA_ERR_UNSUPPORTED (-2) /* dk/dv other than 128, unknown dtype, capturing stream */
 #define KDA_ERR_WORKSPACE (-3)   /* workspace NULL or smaller than the size query returned */
 #define KDA_ERR_HIP (-4)         /* a HIP runtime call or launch failed; outputs undefined */
 
