@@ -17,6 +17,8 @@ Two independent formulations live here:
   §六 written out in numpy fp64, used only to pin the recurrence (the two
   must agree to rounding).
 
+* :func:`segment_scan` -- the fold of segment pairs into entry states,
+  one numpy fp64 matrix product per segment.
 * :func:`gate_log_decay`, :func:`l2_normalize`, :func:`gated_rmsnorm` and
   :func:`prefill_gated` -- the layer's steps on either side of the
   recurrence (decay gate, q / k normalization, output norm and gate), plain
@@ -25,7 +27,8 @@ Two independent formulations live here:
 Pins (tests marked ``not gpu``) tie the oracle to facts the pages and the
 mathematics fix: the literal product form, beta = 0 pure decay, linear
 attention, the delta rule's exact retrieval, the segment identity
-S = S~ + M S_in, and hand-expanded dk = dv = 2 examples (with and without
+S = S~ + M S_in, the fold of a sequence's segment pairs against the
+recurrence's states at the cuts, and hand-expanded dk = dv = 2 examples (with and without
 the prologue and epilogue); the gate, norm and output-gate steps also
 against closed forms (sigmoid(0) = 1/2, sigmoid(ln 3) = 3/4, 3-4-5 rows).
 """
@@ -243,6 +246,24 @@ def segment_transition(k, v, g, beta, cu_seglens=None, threads: int = 0):
     if rc != 0:
         raise RuntimeError("kda_oracle_segment failed (%d)" % rc)
     return M, St
+
+
+def segment_scan(M, S_tilde, initial_state=None):
+    """Entry states of a chain of segments from their pairs
+    ("部署 Kimi K3：从 KDA Kernel 到 Fleet 调度" §二: the state after a segment
+    is S~ + M S_in, and the pairs of the shards before a device fold into its
+    entry state): S_in[0] = initial_state (or zero), S_in[j + 1] = S~_j +
+    M_j S_in[j], one matrix product per step, fp64.  Returns
+    ``[S + 1, H, dk, dv]``."""
+    M = _f64(M); St = _f64(S_tilde)
+    S, H, dk, _ = M.shape
+    dv = St.shape[3]
+    out = np.zeros((S + 1, H, dk, dv), dtype=np.float64)
+    if initial_state is not None:
+        out[0] = _f64(initial_state)
+    for j in range(S):
+        out[j + 1] = St[j] + np.matmul(M[j], out[j])
+    return out
 
 
 # ---------------------------------------------------------------------------

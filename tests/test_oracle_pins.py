@@ -6,7 +6,8 @@ Each test ties the oracle to something other than itself:
   * an independent chunkwise formulation (oracle/chunk_form.py);
   * closed forms: beta = 0 pure decay, plain causal linear attention,
     delta-rule exact retrieval;
-  * the segment identity S = S~ + M S_in and its associativity;
+  * the segment identity S = S~ + M S_in and its associativity, and the
+    fold of a sequence's pairs against its states at the cuts;
   * boundary semantics: resume, packing, decode == prefill.
 A plausible mistake (a dropped decay, a wrong sign, decay on columns instead
 of rows, the pre- instead of post-update state in o, exp2 for exp, an
@@ -174,6 +175,29 @@ def test_segment_identity_and_associativity(decay):
         np.testing.assert_allclose(Mw[0, h], M[2, h] @ M[0, h], rtol=1e-11, atol=1e-14)
         np.testing.assert_allclose(Sw[0, h], St[2, h] + M[2, h] @ St[0, h], rtol=1e-11,
                                    atol=1e-13)
+
+
+@pytest.mark.parametrize("with_init", [True, False])
+def test_segment_scan_equals_states_at_the_cuts(with_init):
+    # folding a sequence's segment pairs gives the recurrence's own state at
+    # every cut (a transposed M, a reversed product or a dropped S~ fails)
+    T, H, dk, dv = 50, 2, 16, 12
+    q, k, v, g, beta = rand_inputs(T, H, dk, dv, 16, decay="mild")
+    cu = np.array([0, 9, 9, 30, 50])
+    M, St = oracle.segment_transition(k, v, g, beta, cu_seglens=cu)
+    S0 = np.random.default_rng(17).standard_normal((H, dk, dv)) if with_init else None
+    S_in = oracle.segment_scan(M, St, S0)
+    assert S_in.shape == (5, H, dk, dv)
+    np.testing.assert_array_equal(S_in[0], S0 if with_init else np.zeros((H, dk, dv)))
+    for j in range(1, 5):
+        e = cu[j]
+        _, fin = oracle.recurrence(q[:e], k[:e], v[:e], g[:e], beta[:e],
+                                   initial_state=None if S0 is None else S0[None],
+                                   want_o=False)
+        np.testing.assert_allclose(S_in[j], fin[0], rtol=1e-10, atol=1e-12)
+    # no pairs: the entry state only
+    S_e = oracle.segment_scan(M[:0], St[:0], S0)
+    assert S_e.shape == (1, H, dk, dv)
 
 
 def test_resume_packing_and_decode_equivalence():
