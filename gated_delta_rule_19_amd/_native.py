@@ -44,6 +44,7 @@ EXPORTED = (
     "kda_decode_replay_gated",
     "kda_segment_transition_workspace_size",
     "kda_segment_transition",
+    "kda_segment_scan",
 )
 
 _lib = None
@@ -108,6 +109,8 @@ def load():
         lib.kda_segment_transition.restype = i32
         lib.kda_segment_transition.argtypes = [i32, lp, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                                vp, vp, sz, vp]
+        lib.kda_segment_scan.restype = i32
+        lib.kda_segment_scan.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
         _lib = lib
         return lib
 
@@ -503,3 +506,31 @@ def segment_transition(k, v, g, beta, cu_seglens=None, M=None, S_tilde=None, wor
     if st != KDA_OK:
         raise KdaError(st, "kda_segment_transition")
     return M, S_tilde
+
+
+def segment_scan(M, S_tilde, initial_state=None, S_in=None):
+    """Entry states of a chain of segments from their (M, S~) pairs
+    (``kda_segment_scan``): M ``[num_segs, H, dk, dk]``, S~ ``[num_segs, H,
+    dk, dv]``, initial_state ``[H, dk, dv]`` or None (zero), all fp32.
+    Returns S_in ``[num_segs + 1, H, dk, dv]``: S_in[0] = initial_state,
+    S_in[j + 1] = S~_j + M_j S_in[j]."""
+    lib = load()
+    S, H, dk, _ = M.shape
+    dv = S_tilde.shape[-1]
+    for x in (M, S_tilde, initial_state, S_in):
+        if x is not None and (x.dtype != torch.float32 or not x.is_contiguous()):
+            raise TypeError("M, S_tilde, initial_state and S_in must be contiguous fp32")
+    if S_tilde.shape != (S, H, dk, dv):
+        raise ValueError("S_tilde must be [num_segs, H, dk, dv]")
+    if initial_state is not None and initial_state.shape != (H, dk, dv):
+        raise ValueError("initial_state must be [H, dk, dv]")
+    dev = _check_device(M, S_tilde, initial_state, S_in)
+    if S_in is None:
+        S_in = torch.empty((S + 1, H, dk, dv), dtype=torch.float32, device=dev)
+    elif S_in.shape != (S + 1, H, dk, dv):
+        raise ValueError("S_in must be [num_segs + 1, H, dk, dv]")
+    st = lib.kda_segment_scan(S, H, dk, dv, _ptr(M), _ptr(S_tilde), _ptr(initial_state),
+                              _ptr(S_in), _stream_ptr(dev))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_segment_scan")
+    return S_in

@@ -782,4 +782,32 @@ kda_status kda_segment_transition(int32_t num_segs, const int64_t *cu_seglens_ho
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+kda_status kda_segment_scan(int32_t num_segs, int32_t H, int32_t dk, int32_t dv, const float *M,
+                            const float *S_tilde, const float *initial_state, float *S_in,
+                            void *stream) {
+  if (dk != kD || dv != kD)
+    return KDA_ERR_UNSUPPORTED;
+  if (num_segs < 0 || H < 1 || H > (1 << 24) || !S_in || !aligned16(S_in) ||
+      !aligned16(initial_state))
+    return KDA_ERR_INVALID_ARG;
+  if (num_segs > 0 && (!M || !S_tilde || !aligned16(M) || !aligned16(S_tilde)))
+    return KDA_ERR_INVALID_ARG;
+  const int64_t mat = (int64_t)H * kD * kD * (int64_t)sizeof(float);
+  if ((int64_t)num_segs + 1 > INT64_MAX / 2 / mat)
+    return KDA_ERR_INVALID_ARG;
+  // S_in is written while the pairs and the initial state are read
+  const uint8_t *out = (const uint8_t *)S_in;
+  const int64_t out_bytes = ((int64_t)num_segs + 1) * mat;
+  auto overlaps = [&](const float *in, int64_t bytes) {
+    const uint8_t *a = (const uint8_t *)in;
+    return in && bytes > 0 && a < out + out_bytes && out < a + bytes;
+  };
+  if (overlaps(M, num_segs * mat) || overlaps(S_tilde, num_segs * mat) ||
+      overlaps(initial_state, mat))
+    return KDA_ERR_INVALID_ARG;
+  const hipError_t e = launch_scan_rows(num_segs, H, M, S_tilde, initial_state, S_in,
+                                        (hipStream_t)stream);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 } // extern "C"

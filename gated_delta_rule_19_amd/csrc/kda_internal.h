@@ -172,6 +172,12 @@ hipError_t launch_out_norm_gate(int elt, int64_t rows, void *o, const Epilogue &
 hipError_t launch_scan(const ScanDesc *descs, int32_t ndesc, int32_t H, const float *Mseg,
                        const float *Stseg, const float *init, float *sin, hipStream_t s);
 
+// The scan of one chain of nsteps row-major pairs (M [nsteps, H, dk, dk],
+// S~ [nsteps, H, dk, dv]) from init ([H, dk, dv] or null: zero): writes the
+// nsteps + 1 states sin[0] = init, sin[j + 1] = S~_j + M_j sin[j].
+hipError_t launch_scan_rows(int32_t nsteps, int32_t H, const float *M, const float *St,
+                            const float *init, float *sin, hipStream_t s);
+
 // Speculative-decode replay: m accepted cached tokens, then P new tokens.
 // The prologue applies to cached and new tokens, the epilogue to the new
 // tokens' outputs.

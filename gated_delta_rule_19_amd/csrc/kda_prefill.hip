@@ -1276,8 +1276,13 @@ constexpr int kScanLd = kD + 4; // LDS row stride (floats) of the transposed sta
 
 } // namespace
 
+//
+// ROWS: M_j is row-major (M[r][m] at r * dk + m), as kda_segment_transition
+// writes it; the lane's four consecutive reduction indices are then one
+// 16-byte load from its own row.  descs == null: the one sequence `one`.
+template <bool ROWS>
 __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanDesc *__restrict__ descs,
-                                                        int32_t ndesc, int32_t H,
+                                                        ScanDesc one, int32_t ndesc, int32_t H,
                                                         const float *__restrict__ Mseg,
                                                         const float *__restrict__ Stseg,
                                                         const float *__restrict__ init,
@@ -1291,7 +1296,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanDesc *__restri
   if (pair >= ndesc * H)
     return;
   const int di = pair / H, h = pair - di * H;
-  const ScanDesc d = descs[di];
+  const ScanDesc d = descs ? descs[di] : one;
   const int col0 = (rem >> 3) * kScanBV;
 
   __shared__ __attribute__((aligned(16))) float sT[2][kScanBV][kScanLd]; // [buf][col][row]
@@ -1343,10 +1348,13 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanDesc *__restri
     in.warm[1] = mat_at(Stseg, jw)[(tid & 127) * kD + col0];
   };
   // the A operands of k-group i, row tile t: 1 KiB block (8 w + i) * 2 + t
+  // in scan order, else M[32 w + 16 t + n][16 i + 4 kq .. + 3]
   auto load_a = [&](ScanIn &in, const float *mj, int i) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
-      in.a[i][t] = *reinterpret_cast<const f32x4 *>(mj + ((8 * w + i) * 2 + t) * 256 + 4 * lane);
+      in.a[i][t] = *reinterpret_cast<const f32x4 *>(
+          ROWS ? mj + (32 * w + 16 * t + n) * kD + 16 * i + 4 * kq
+               : mj + ((8 * w + i) * 2 + t) * 256 + 4 * lane);
   };
   auto load = [&](ScanIn &in, int j) {
     const float *mj = mat_at(Mseg, j);
@@ -1404,7 +1412,8 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanDesc *__restri
   };
 
   ScanIn in0, in1;
-  load(in0, 0);
+  if (nstep > 0) // (no pairs: only the entry state is written)
+    load(in0, 0);
   __syncthreads();
   int j = 0;
   for (; j + 2 <= nstep; j += 2) {
@@ -1575,7 +1584,16 @@ hipError_t launch_scan(const ScanDesc *descs, int32_t ndesc, int32_t H, const fl
     return hipSuccess;
   const int64_t pairs = (int64_t)ndesc * H;
   const unsigned grid = (unsigned)((pairs + 7) / 8 * 8 * (kD / kScanBV));
-  scan_kernel<<<grid, kThreads, 0, s>>>(descs, ndesc, H, Mseg, Stseg, init, sin);
+  scan_kernel<false><<<grid, kThreads, 0, s>>>(descs, ScanDesc{}, ndesc, H, Mseg, Stseg, init,
+                                               sin);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_rows(int32_t nsteps, int32_t H, const float *M, const float *St,
+                            const float *init, float *sin, hipStream_t s) {
+  const ScanDesc one{0, nsteps + 1, 0, init ? 0 : -1};
+  const unsigned grid = (unsigned)(((int64_t)H + 7) / 8 * 8 * (kD / kScanBV));
+  scan_kernel<true><<<grid, kThreads, 0, s>>>(nullptr, one, 1, H, M, St, init, sin);
   return hipGetLastError();
 }
 

@@ -24,8 +24,8 @@
  *   their schedule from a pinned host buffer that later calls reuse, so a
  *   captured copy would read stale tables on replay; on a stream that is
  *   capturing they return KDA_ERR_UNSUPPORTED and enqueue nothing.  The
- *   decode calls (step and replay, plain and gated) upload nothing and
- *   launch one kernel each; they may be captured.
+ *   decode calls (step and replay, plain and gated) and kda_segment_scan
+ *   upload nothing and launch one kernel each; they may be captured.
  * - dk = dv = 128 and the chunk length C = 64 are fixed in this build.
  * - Element type of q, k, v, g, beta and o is `dt`: KDA_F32 (fp32) or
  *   KDA_BF16 (bfloat16).  States, M and S~ are always fp32.  All arithmetic
@@ -352,6 +352,33 @@ kda_status kda_segment_transition(int32_t num_segs, const int64_t *cu_seglens_ho
                                   int32_t H, int32_t dk, int32_t dv, kda_dtype dt, const void *k, const void *v,
                                   const void *g, const void *beta, float *M, float *S_tilde,
                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Prefix scan of segment transition pairs ("部署 Kimi K3：从 KDA Kernel 到
+ * Fleet 调度", §二: pairs compose associatively; in the cross-device KCP each
+ * device folds the pairs of the shards before its own into its entry state).
+ * For pairs (M_j, S_tilde_j), j = 0 .. num_segs-1, per head h:
+ *     S_in[0] = initial_state (or zero),
+ *     S_in[j+1] = S_tilde_j + M_j S_in[j],
+ * so S_in[j] is the state entering segment j and S_in[num_segs] the state
+ * after the last one.  With kda_segment_transition on each shard of a
+ * sequence, this call, then kda_chunk_prefill of shard j from S_in[j], the
+ * shards' outputs and states equal those of one prefill over the sequence.
+ *
+ *   M        : [num_segs, H, dk, dk] fp32, row-major, as kda_segment_transition
+ *              writes it.
+ *   S_tilde  : [num_segs, H, dk, dv] fp32.
+ *   initial_state : [H, dk, dv] fp32, or NULL for zero.
+ *   S_in     : [num_segs + 1, H, dk, dv] fp32 output; must not overlap M,
+ *              S_tilde or initial_state (KDA_ERR_INVALID_ARG).
+ * num_segs = 0 writes S_in[0] only.  Serial over the pairs, parallel over
+ * heads and 16-column blocks, fp32 throughout (fp32 matrix cores).  No
+ * workspace and no schedule upload: the call launches one kernel and may be
+ * captured into a HIP graph.  H <= 2^24.
+ */
+kda_status kda_segment_scan(int32_t num_segs, int32_t H, int32_t dk, int32_t dv, const float *M,
+                            const float *S_tilde, const float *initial_state, float *S_in,
+                            void *stream);
 
 #ifdef __cplusplus
 }

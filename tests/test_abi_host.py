@@ -228,6 +228,33 @@ def test_segment_transition_argument_errors(lib):
     assert seg(n=0, pp=pb) == E.KDA_OK
 
 
+def test_segment_scan_argument_errors(lib):
+    E = nat
+    mat = 128 * 128 * 4  # bytes of one head's fp32 state
+    M = ctypes.c_void_p(0x10000000)
+    S = ctypes.c_void_p(0x20000000)
+    out = ctypes.c_void_p(0x30000000)
+
+    def scan(n=2, H=1, dk=128, M=M, S=S, init=None, out=out):
+        return lib.kda_segment_scan(n, H, dk, 128, M, S, init, out, None)
+
+    assert scan(dk=64) == E.KDA_ERR_UNSUPPORTED
+    assert scan(n=-1) == E.KDA_ERR_INVALID_ARG
+    assert scan(H=0) == E.KDA_ERR_INVALID_ARG
+    assert scan(H=(1 << 24) + 1) == E.KDA_ERR_INVALID_ARG
+    assert scan(out=None) == E.KDA_ERR_INVALID_ARG
+    assert scan(out=ctypes.c_void_p(0x30000000 + 4)) == E.KDA_ERR_INVALID_ARG   # misaligned
+    assert scan(M=None) == E.KDA_ERR_INVALID_ARG
+    assert scan(S=None) == E.KDA_ERR_INVALID_ARG
+    assert scan(init=ctypes.c_void_p(0x40000008)) == E.KDA_ERR_INVALID_ARG     # misaligned
+    # S_in ([3, 1, 128, 128]) overlapping the last pair's M, S~ or the initial state
+    assert scan(out=ctypes.c_void_p(0x10000000 + mat)) == E.KDA_ERR_INVALID_ARG
+    assert scan(out=ctypes.c_void_p(0x20000000 - 2 * mat)) == E.KDA_ERR_INVALID_ARG
+    assert scan(init=ctypes.c_void_p(0x30000000 + 2 * mat)) == E.KDA_ERR_INVALID_ARG
+    # without pairs M and S~ may be null (the call then only writes S_in[0]);
+    # its validation passes, which the GPU tests exercise
+
+
 def test_binding_rejects_cpu_tensors(lib):
     import torch
     x = torch.zeros(4, 2, 128)

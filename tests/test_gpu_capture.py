@@ -65,3 +65,26 @@ def test_captured_decode_step_replays_equal_eager(dtype):
         say("replay", step)
         assert torch.equal(o_graph, o_eager)
         assert torch.equal(S_graph, S_eager)
+
+
+def test_captured_segment_scan_replays_equal_eager():
+    say("captured segment scan")
+    nseg, H = 4, 3
+    M = torch.empty((nseg, H, 128, 128), dtype=torch.float32, device=DEV)
+    St = torch.empty((nseg, H, 128, 128), dtype=torch.float32, device=DEV)
+    S0 = wl.states(1, H, 970, device=DEV)[0]
+    S_graph = torch.empty((nseg + 1, H, 128, 128), dtype=torch.float32, device=DEV)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        kda.segment_scan(M, St, S0, S_in=S_graph)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        gen = torch.Generator(device=DEV).manual_seed(971 + rep)
+        M.copy_(torch.randn(M.shape, device=DEV, generator=gen) / 128 ** 0.5)
+        St.copy_(torch.randn(St.shape, device=DEV, generator=gen))
+        graph.replay()
+        S_eager = kda.segment_scan(M, St, S0)
+        torch.cuda.synchronize()
+        say("replay", rep)
+        assert torch.equal(S_graph, S_eager)
