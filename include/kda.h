@@ -26,7 +26,7 @@
  *   capturing they return KDA_ERR_UNSUPPORTED and enqueue nothing.  The
  *   decode calls (step and replay, plain and gated) and kda_segment_scan
  *   upload nothing and launch one kernel each; they may be captured.
- * - dk = dv = 128 and the chunk length C = 64 are fixed in this build.
+ * - dk = dv = 128 and the chunk length C = 64 are fixed in this version of the library.
  * - Element type of q, k, v, g, beta and o is `dt`: KDA_F32 (fp32) or
  *   KDA_BF16 (bfloat16).  States, M and S~ are always fp32.  All arithmetic
  *   accumulates in fp32; with KDA_BF16 the matrix products take bf16

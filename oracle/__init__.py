@@ -110,7 +110,7 @@ def _cu(cu_seqlens, T):
 
 def default_threads() -> int:
     """Threads the oracle uses by default: the CPUs this process may run on,
-    capped at 16 (a one-GPU machine's CPU share)."""
+    capped at 16 (the CPU share of a host that serves one GPU)."""
     try:
         n = len(os.sched_getaffinity(0))
     except (AttributeError, OSError):
