@@ -357,8 +357,10 @@ def cpu_baseline(wl, name, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    # 20 untimed steps bring the device to its steady clock: with 3, a fresh
+    # process times the prefill call 4-6% slower than it runs sustained
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill_bf16_T8192_H96")
     ap.add_argument("--split", type=int, default=0, help="split_hint (0 = automatic)")
     ap.add_argument("--no-decode", action="store_true")
@@ -397,7 +399,8 @@ def main():
     print("prefill %s: %.3f ms/step, %.3g tokens/s, %.1f TFLOP/s (%.1f%% of bf16 MFMA peak)"
           % (args.workload, main_res["ms_per_step"], main_res["tokens_per_s"],
              main_res["tflops"], 100 * main_res["mfma_frac"]), file=sys.stderr, flush=True)
-    gated = time_prefill(kda, wl, args.workload, args.steps, 2, args.split, dev, gated=True)
+    gated = time_prefill(kda, wl, args.workload, args.steps, args.warmup, args.split, dev,
+                         gated=True)
     gated["vs_plain"] = gated["ms_per_step"] / main_res["ms_per_step"]
     print("prefill %s gated (decay gate, q/k norm, output norm and gate fused): %.3f ms/step "
           "(x%.3f of the plain call)" % (args.workload, gated["ms_per_step"], gated["vs_plain"]),
