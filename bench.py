@@ -407,16 +407,17 @@ def main():
           file=sys.stderr, flush=True)
     extra = {}
     if args.all:
+        warm = max(2, args.warmup // 2)
         for name in ("prefill_bf16_T131072_H12", "prefill_bf16_varlen64_H96_resume",
                      "prefill_f32_T256_H2"):
             if name == args.workload:
                 continue
-            r = time_prefill(kda, wl, name, max(3, args.steps // 2), 1, 0, dev)
+            r = time_prefill(kda, wl, name, max(3, args.steps // 2), warm, 0, dev)
             extra[name] = r
             print("prefill %s: %.3f ms/step, %.3g tokens/s, %.1f%% MFMA"
                   % (name, r["ms_per_step"], r["tokens_per_s"], 100 * r["mfma_frac"]),
                   file=sys.stderr, flush=True)
-            rg = time_prefill(kda, wl, name, max(3, args.steps // 2), 1, 0, dev, gated=True)
+            rg = time_prefill(kda, wl, name, max(3, args.steps // 2), warm, 0, dev, gated=True)
             rg["vs_plain"] = rg["ms_per_step"] / r["ms_per_step"]
             extra[name + "_gated"] = rg
             print("prefill %s gated: %.3f ms/step (x%.3f)" % (name, rg["ms_per_step"],
