@@ -787,8 +787,9 @@ kda_status kda_segment_scan(int32_t num_segs, int32_t H, int32_t dk, int32_t dv,
                             void *stream) {
   if (dk != kD || dv != kD)
     return KDA_ERR_UNSUPPORTED;
-  if (num_segs < 0 || H < 1 || H > (1 << 24) || !S_in || !aligned16(S_in) ||
-      !aligned16(initial_state))
+  // (the scan's descriptor counts num_segs + 1 states in an int32)
+  if (num_segs < 0 || num_segs > INT32_MAX - 1 || H < 1 || H > (1 << 24) || !S_in ||
+      !aligned16(S_in) || !aligned16(initial_state))
     return KDA_ERR_INVALID_ARG;
   if (num_segs > 0 && (!M || !S_tilde || !aligned16(M) || !aligned16(S_tilde)))
     return KDA_ERR_INVALID_ARG;

@@ -240,6 +240,7 @@ def test_segment_scan_argument_errors(lib):
 
     assert scan(dk=64) == E.KDA_ERR_UNSUPPORTED
     assert scan(n=-1) == E.KDA_ERR_INVALID_ARG
+    assert scan(n=2 ** 31 - 1) == E.KDA_ERR_INVALID_ARG
     assert scan(H=0) == E.KDA_ERR_INVALID_ARG
     assert scan(H=(1 << 24) + 1) == E.KDA_ERR_INVALID_ARG
     assert scan(out=None) == E.KDA_ERR_INVALID_ARG
