@@ -2,7 +2,7 @@
 
 - Against the oracle's fold of the same fp32 pairs (the pairs are the
   oracle's own transitions of seeded inputs, rounded to fp32): S_in[0] =
-  init, S_in[j + 1] = S~_j + M_j S_in[j], for 0 .. 17 pairs and 1 .. 12 heads.
+  init, S_in[j + 1] = S~_j + M_j S_in[j], for 0 .. 63 pairs and 1 .. 12 heads.
 - The cross-device KCP decomposition ("部署 Kimi K3：从 KDA Kernel 到 Fleet
   调度" §二) on one GPU: a sequence cut into shards, each shard's (M, S~)
   from kda_segment_transition, the pairs folded into the shards' entry
@@ -45,7 +45,8 @@ def oracle_pairs(nseg, H, seed):
 
 
 @pytest.mark.parametrize("nseg,H,init", [(1, 1, True), (2, 3, False), (5, 12, True),
-                                         (17, 4, True), (17, 1, False)])
+                                         (17, 4, True), (17, 1, False),
+                                         (63, 12, True)])  # the long-context planner's shape
 def test_segment_scan_vs_oracle(nseg, H, init):
     say("segment scan case", dict(nseg=nseg, H=H, init=init))
     M, St = oracle_pairs(nseg, H, 1200 + nseg + H)
