@@ -1,0 +1,55 @@
+"""The bf16 bar for outputs that leave through the output norm and gate.
+
+The output step ("Kimi K3.1 Pro 架构完全拆解" §3.3) maps each (token, head) row
+of the recurrence output o~ to y = s o~ / r, with s = w sigmoid(gate) and
+r = sqrt(mean(o~^2) + eps).  The plain bar holds the recurrence output to
+max|o~ - o~_ref| <= E = tol * max|o~_ref|.  Through the norm that implies,
+row by row: |r - r_ref| <= rms of the error <= E, so r >= r_ref - E and
+
+    |y - y_ref| <= |s| E (1 + |o~_ref| / r_ref) / (r_ref - E) + 2^-8 |y_ref|
+
+(the last term is y's own bf16 rounding).  A row whose output is small
+against the largest one is scaled up by the norm, and with it its share of
+the recurrence's error.
+
+Rows with r_ref <= E get no finite bound from this: their recurrence output
+is within the error of zero.  They are counted, the count is printed, and
+their fraction of all rows is held to MAX_EXEMPT_FRACTION.  They are held to
+what the norm guarantees for any input, |y| <= |s| sqrt(dv) (a row's largest
+element is at most sqrt(dv) times its rms), with the bf16 rounding of y on
+top.
+"""
+import numpy as np
+
+# the largest fraction of rows allowed below the bar (r_ref <= E)
+MAX_EXEMPT_FRACTION = 0.02
+
+
+def check_norm_bound(y, y_ref, ot_ref, s, tol, eps, label=""):
+    """y, y_ref, ot_ref, s: fp64 arrays with rows over the last axis (s may
+    broadcast); eps: the norm's epsilon (inside r and r_ref).  Returns
+    (largest error / bound over the bounded rows, count of rows below the
+    bar)."""
+    y = np.asarray(y, dtype=np.float64)
+    assert y.shape == y_ref.shape == ot_ref.shape
+    assert np.all(np.isfinite(y))
+    s = np.abs(np.broadcast_to(s, y.shape))
+    E = tol * float(np.max(np.abs(ot_ref)))
+    r = np.sqrt(np.mean(ot_ref * ot_ref, axis=-1, keepdims=True) + eps)
+    bounded = (r > E)[..., 0]
+    rows = int(np.prod(y.shape[:-1]))
+    exempt = rows - int(np.count_nonzero(bounded))
+    print("%s output-norm rows below the bar (r_ref <= E = %.3g): %d of %d (%.3g%%)"
+          % (label, E, exempt, rows, 100.0 * exempt / max(rows, 1)), flush=True)
+    assert exempt <= MAX_EXEMPT_FRACTION * rows, (exempt, rows)
+    excess = 0.0
+    if np.any(bounded):
+        rb, ob, sb = r[bounded], ot_ref[bounded], s[bounded]
+        bound = sb * E * (1.0 + np.abs(ob) / rb) / (rb - E) + 2.0 ** -8 * np.abs(y_ref[bounded])
+        excess = float(np.max(np.abs(y[bounded] - y_ref[bounded]) / bound))
+        assert excess <= 1.0, ("o vs its bound", excess)
+    if exempt:
+        dv = y.shape[-1]
+        cap = s[~bounded] * np.sqrt(dv) * (1.0 + 2.0 ** -7)
+        assert np.all(np.abs(y[~bounded]) <= cap), "a row below the bar exceeds the norm's cap"
+    return excess, exempt

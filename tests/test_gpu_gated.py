@@ -11,9 +11,10 @@ too for fp32; for bf16 it meets the bound the plain bar implies through the
 norm: with E = tol * max|o~_ref| the recurrence output's error (o~ as stored
 included), |r - r_ref| <= rms of the error <= E, so r >= r_ref - E and
     |y - y_ref| <= |s| E (1 + |o~_ref| / r_ref) / (r_ref - E) + 2^-8 |y_ref|
-(the last term is y's own bf16 rounding; rows with r_ref <= E are not bounded).
-A row whose output is small against the sequence's largest one is scaled up
-by the norm, and with it its share of the recurrence's bf16 error.
+(the last term is y's own bf16 rounding).  A row whose output is small
+against the sequence's largest one is scaled up by the norm, and with it its
+share of the recurrence's bf16 error.  Rows with r_ref <= E are counted and
+held to a stated small fraction and to the norm's own cap (tests/gated_bound.py).
 """
 import numpy as np
 import pytest
@@ -21,6 +22,7 @@ import torch
 
 import oracle
 import gated_delta_rule_19_amd as kda
+from gated_bound import check_norm_bound as norm_bar
 from gated_delta_rule_19_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -79,18 +81,11 @@ def check_gated_bound(o, y_ref, d, nw, kw, qk, cu, S0, dtype):
     ot_ref, _ = oracle.prefill_gated(d["q"], d["k"], d["v"], d["beta"],
                                      qk_norm_eps=QK_EPS if qk else None, cu_seqlens=cu,
                                      initial_state=S0, **kw)
-    E = TOL[dtype] * float(np.max(np.abs(ot_ref)))
-    r = np.sqrt(np.mean(ot_ref * ot_ref, axis=-1, keepdims=True) + OUT_EPS)
     gate = d["out_gate"].detach().cpu().double().numpy()
     w = np.ones(ot_ref.shape[-1]) if nw is None else nw.detach().cpu().double().numpy()
-    s = np.abs(w / (1.0 + np.exp(-gate)))
-    with np.errstate(divide="ignore"):
-        lo = np.where(r > E, r - E, 0.0)
-        bound = s * E * (1.0 + np.abs(ot_ref) / r) / lo + 2.0 ** -8 * np.abs(y_ref)
-    y = o.detach().cpu().double().numpy()
-    assert np.all(np.isfinite(y))
-    excess = np.abs(y - y_ref) / bound
-    assert float(np.max(excess)) <= 1.0, ("o vs its bound", float(np.max(excess)))
+    s = w / (1.0 + np.exp(-gate))
+    norm_bar(o.detach().cpu().double().numpy(), y_ref, ot_ref, s, TOL[dtype], OUT_EPS,
+             "prefill")
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -122,13 +117,13 @@ def test_gated_planner_split(dtype):
     gated_vs_oracle([1000], 2, dtype, 570, init=True, split=4)
 
 
-@pytest.mark.parametrize("fused", ["1", "0"])
+@pytest.mark.parametrize("fused", ["fused", "two_kernel"])
 @pytest.mark.parametrize("epi", [True, False])
 def test_gated_fused_and_two_kernel_paths(fused, epi, monkeypatch):
     """bf16 with the fused kernel forced on and off; with and without the
     output epilogue (few chains: on the two-kernel path it is a pass of its
     own after the state chain)."""
-    monkeypatch.setenv("KDA_FUSED_PREFILL", fused)
+    monkeypatch.setattr(kda._native, "DEFAULT_PREFILL_PATH", fused)
     gated_vs_oracle([70, 1, 128, 129, 0, 64], 4, torch.bfloat16, 580, epi=epi, init=True)
 
 
@@ -139,7 +134,7 @@ MANY = [1 + (37 * i) % 140 for i in range(64)]
 
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_gated_many_chains_epilogue_in_state_chain(dtype, monkeypatch):
-    monkeypatch.setenv("KDA_FUSED_PREFILL", "0")
+    monkeypatch.setattr(kda._native, "DEFAULT_PREFILL_PATH", "two_kernel")
     gated_vs_oracle(MANY, 4, dtype, 585, init=True)
 
 
@@ -170,7 +165,8 @@ def test_gated_epilogue_exact_recurrence_bf16(path, monkeypatch):
     exact integer), so the output norm and gate are checked to y's own bf16
     rounding on each of the three places the epilogue runs: the fused kernel,
     the state chain's stores (many chains) and its own pass (few chains)."""
-    monkeypatch.setenv("KDA_FUSED_PREFILL", "1" if path == "fused" else "0")
+    monkeypatch.setattr(kda._native, "DEFAULT_PREFILL_PATH",
+                        "fused" if path == "fused" else "two_kernel")
     lengths, H = ([70, 64, 1, 130], 3) if path != "state_chain" else (MANY, 4)
     cu = wl.cu_from_lengths(lengths)
     T, N = int(cu[-1]), len(lengths)
@@ -205,17 +201,10 @@ def check_norm_bound(y, y_ref, ot_ref, gate, nw, dtype):
     if dtype == torch.float32:
         assert rel_err(y, y_ref) <= TOL[dtype]
         return
-    E = TOL[dtype] * float(np.max(np.abs(ot_ref)))
-    r = np.sqrt(np.mean(ot_ref * ot_ref, axis=-1, keepdims=True) + OUT_EPS)
     g = gate.detach().cpu().double().numpy()
     w = np.ones(ot_ref.shape[-1]) if nw is None else nw.detach().cpu().double().numpy()
-    s = np.abs(w / (1.0 + np.exp(-g)))
-    with np.errstate(divide="ignore"):
-        lo = np.where(r > E, r - E, 0.0)
-        bound = s * E * (1.0 + np.abs(ot_ref) / r) / lo + 2.0 ** -8 * np.abs(y_ref)
-    yy = y.detach().cpu().double().numpy()
-    assert np.all(np.isfinite(yy))
-    assert float(np.max(np.abs(yy - y_ref) / bound)) <= 1.0
+    norm_bar(y.detach().cpu().double().numpy(), y_ref, ot_ref, w / (1.0 + np.exp(-g)),
+             TOL[dtype], OUT_EPS, "decode")
 
 
 @pytest.mark.parametrize("dtype", DTYPES)

@@ -440,3 +440,87 @@ def test_prefill_gated_without_prologue_or_epilogue_is_the_recurrence():
     o2, f2 = oracle.prefill_gated(q, k, v, beta, g=g, qk_norm_eps=0.0)
     np.testing.assert_allclose(o2, o0, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(f2, f0, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_replay_gated_hand_built_window():
+    """The gated speculative-decode replay ("Kimi K3.1 Pro 架构完全拆解" §3.4:
+    the decode kernel also normalizes, gates and applies the output norm;
+    "部署 Kimi K3：从 KDA Kernel 到 Fleet 调度" §四: the state is rebuilt from the
+    cached projected inputs of the accepted tokens) against a window built
+    token by token here: every token, cached or new, gets its decay from its
+    gate logits, g = g_min sigmoid(e^{A_h} z), and its q / k rows
+    L2-normalized; the literal product step runs over the accepted cached
+    tokens, then the new ones; only the new tokens' outputs get the RMSNorm
+    and the sigmoid output gate; the state committed is the one after the
+    bonus (first new) token.  The same window with one of those steps moved
+    to the wrong token set is then shown to differ, so each would be caught."""
+    N, W, P, H, dk, dv = 4, 3, 3, 2, 8, 6
+    rng = np.random.default_rng(77)
+    ck = 2.5 * rng.standard_normal((N, W, H, dk))   # raw (unnormalized) keys
+    cv = rng.standard_normal((N, W, H, dv))
+    cz = rng.standard_normal((N, W, H, dk))         # raw gate logits
+    cb = 1.0 / (1.0 + np.exp(-rng.standard_normal((N, W, H))))
+    q = 0.7 * rng.standard_normal((N, P, H, dk))
+    k = 3.0 * rng.standard_normal((N, P, H, dk))
+    v = rng.standard_normal((N, P, H, dv))
+    z = rng.standard_normal((N, P, H, dk))
+    b = 1.0 / (1.0 + np.exp(-rng.standard_normal((N, P, H))))
+    og = rng.standard_normal((N, P, H, dv))         # output gate logits
+    wn = 0.5 + rng.random(dv)                        # RMSNorm weight
+    S0 = 0.3 * rng.standard_normal((N, H, dk, dv))
+    A_log = np.array([0.4, -0.7])
+    g_min, qk_eps, o_eps = -0.2, 1e-3, 1e-5          # mild decay: the cached tokens matter
+    accepted = np.array([0, 2, 3, 9], dtype=np.int32)
+
+    def gate(x, h):
+        return g_min / (1.0 + np.exp(-np.exp(A_log[h]) * x))
+
+    def unit(x):
+        return x / np.sqrt(np.dot(x, x) + qk_eps)
+
+    def window(gate_cached=True, norm_cached=True, gate_new=True, norm_new=True):
+        o_ref = np.zeros((N, P, H, dv))
+        com = np.zeros((N, H, dk, dv))
+        for n in range(N):
+            m = int(np.clip(accepted[n], 0, W))
+            for h in range(H):
+                S = S0[n, h].copy()
+                for t in range(m):
+                    kk = unit(ck[n, t, h]) if norm_cached else ck[n, t, h]
+                    gg = gate(cz[n, t, h], h) if gate_cached else cz[n, t, h]
+                    S, _ = _literal_step(S, np.zeros(dk), kk, cv[n, t, h], gg, cb[n, t, h])
+                for j in range(P):
+                    kk = unit(k[n, j, h]) if norm_new else k[n, j, h]
+                    qq = unit(q[n, j, h]) if norm_new else q[n, j, h]
+                    gg = gate(z[n, j, h], h) if gate_new else z[n, j, h]
+                    S, oj = _literal_step(S, qq, kk, v[n, j, h], gg, b[n, j, h])
+                    rms = np.sqrt(np.mean(oj * oj) + o_eps)
+                    o_ref[n, j, h] = wn * oj / rms / (1.0 + np.exp(-og[n, j, h]))
+                    if j == 0:
+                        com[n, h] = S
+        return o_ref, com
+
+    o, committed = oracle.decode_replay_gated(
+        S0, accepted, ck, cv, cz, cb, q, k, v, z, b, A_log=A_log, g_min=g_min,
+        qk_norm_eps=qk_eps, out_gate=og, out_norm_weight=wn, out_norm_eps=o_eps)
+    o_ref, c_ref = window()
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(committed, c_ref, rtol=0, atol=1e-12)
+    # each step on the wrong token set (or skipped) changes the result well
+    # beyond rounding, so none of those mistakes could pass the check above
+    for wrong in ({"gate_cached": False}, {"norm_cached": False}, {"gate_new": False},
+                  {"norm_new": False}):
+        ow, cw = window(**wrong)
+        assert max(rel(ow, o_ref), rel(cw, c_ref)) > 1e-3, wrong
+    # the output norm and gate belong to the new tokens' outputs alone: the
+    # plain replay of the same normalized, gated inputs gives the raw
+    # outputs, which the epilogue maps onto o exactly
+    o_raw, c_raw = oracle.decode_replay(
+        S0, accepted, ck / np.sqrt(np.sum(ck * ck, -1, keepdims=True) + qk_eps), cv,
+        g_min / (1.0 + np.exp(-np.exp(A_log)[None, None, :, None] * cz)), cb,
+        q / np.sqrt(np.sum(q * q, -1, keepdims=True) + qk_eps),
+        k / np.sqrt(np.sum(k * k, -1, keepdims=True) + qk_eps), v,
+        g_min / (1.0 + np.exp(-np.exp(A_log)[None, None, :, None] * z)), b)
+    rms = np.sqrt(np.mean(o_raw * o_raw, -1, keepdims=True) + o_eps)
+    np.testing.assert_allclose(wn * o_raw / rms / (1.0 + np.exp(-og)), o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(c_raw, committed, rtol=0, atol=1e-12)
