@@ -156,7 +156,7 @@ def traffic_from_counters(fetch_csv, write_csv, workload, command):
     print(json.dumps(out, indent=1))
 
 
-def time_prefill(kda, wl, name, steps, warmup, split_hint, dev, gated=False):
+def time_prefill(kda, wl, name, steps, warmup, split_hint, dev, gated=False, path="auto"):
     """Event-timed prefill calls.  gated: kda_chunk_prefill_gated with every
     step on (decay gate from logits, q / k L2 norm, output norm and gate) on
     the same inputs (g serves as the gate logits, v as the output gate's)."""
@@ -168,7 +168,7 @@ def time_prefill(kda, wl, name, steps, warmup, split_hint, dev, gated=False):
     T = int(cu[-1])
     o = torch.empty((T, H, D), dtype=w.dtype, device=dev)
     fin = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
-    nbytes = kda.prefill_workspace_size(cu, H, w.dtype, split_hint)
+    nbytes = kda.prefill_workspace_size(cu, H, w.dtype, split_hint, path=path)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
 
     A_log = torch.zeros((H,), dtype=torch.float32, device=dev)
@@ -179,11 +179,12 @@ def time_prefill(kda, wl, name, steps, warmup, split_hint, dev, gated=False):
             kda.chunk_prefill_gated(d["q"], d["k"], d["v"], d["g"], d["beta"], A_log=A_log,
                                     qk_norm_eps=1e-6, out_gate=d["v"], out_norm_weight=nw,
                                     cu_seqlens=cu, initial_state=d["init"],
-                                    split_hint=split_hint, o=o, final_state=fin, workspace=ws)
+                                    split_hint=split_hint, o=o, final_state=fin, workspace=ws,
+                                    path=path)
         else:
             kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu,
                               initial_state=d["init"], split_hint=split_hint, o=o,
-                              final_state=fin, workspace=ws)
+                              final_state=fin, workspace=ws, path=path)
 
     for _ in range(warmup):
         step()
@@ -208,6 +209,7 @@ def time_prefill(kda, wl, name, steps, warmup, split_hint, dev, gated=False):
         "tokens_per_s": T / (ms * 1e-3), "chunk_heads": chunk_heads, "model_flops": flops,
         "tflops": tflops, "mfma_frac": tflops / PEAK_BF16_TFLOPS,
         "segments_auto": [kda.plan_num_segments(L, N, H, split_hint) for L in w.lengths[:1]],
+        "path": path,
     }
     del d, o, fin, ws
     torch.cuda.empty_cache()
@@ -351,7 +353,21 @@ def cpu_baseline(wl, name, budget_s=10.0):
         heads_done += h1 - h0
     del d
     tok_s = T * heads_done / H / compute_s
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = os.cpu_count()
     return {"value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "nproc": os.cpu_count(), "cpus_allowed": allowed, "cpu_model": model,
             "sample": "%s: %d head passes (%.1f times the %d heads), all %d tokens each, fp64 "
                       "per-token recurrence; compute %.1f s (host copies %.1f s, not counted)"
                       % (name, heads_done, heads_done / H, H, T, compute_s, copy_s)}
@@ -369,7 +385,11 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true",
-                    help="also time the long-context and packed-resume prefill workloads")
+                    help="also time the gated call on the other workloads, and the fp32 one")
+    ap.add_argument("--path", default="auto", choices=["auto", "two_kernel", "fused"],
+                    help="prefill implementation (kda_prefill_options.path)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the long-context and packed-resume prefill workloads")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run one calibration copy, one prefill call and one decode step "
                          "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs) and exit")
@@ -398,29 +418,37 @@ def main():
     if args.traffic_probe:
         traffic_probe(kda, wl, args.workload, dev)
         return
-    main_res = time_prefill(kda, wl, args.workload, args.steps, args.warmup, args.split, dev)
+    main_res = time_prefill(kda, wl, args.workload, args.steps, args.warmup, args.split, dev,
+                            path=args.path)
     print("prefill %s: %.3f ms/step, %.3g tokens/s, %.1f TFLOP/s (%.1f%% of bf16 MFMA peak)"
           % (args.workload, main_res["ms_per_step"], main_res["tokens_per_s"],
              main_res["tflops"], 100 * main_res["mfma_frac"]), file=sys.stderr, flush=True)
     gated = time_prefill(kda, wl, args.workload, args.steps, args.warmup, args.split, dev,
-                         gated=True)
+                         gated=True, path=args.path)
     gated["vs_plain"] = gated["ms_per_step"] / main_res["ms_per_step"]
     print("prefill %s gated (decay gate, q/k norm, output norm and gate fused): %.3f ms/step "
           "(x%.3f of the plain call)" % (args.workload, gated["ms_per_step"], gated["vs_plain"]),
           file=sys.stderr, flush=True)
+    # the other prefill workloads: the long-context planner and the packed
+    # resume in every default run (few steps each), the gated call on them and
+    # the fp32 workload with --all
     extra = {}
+    names = [] if args.no_extra else ["prefill_bf16_T131072_H12",
+                                      "prefill_bf16_varlen64_H96_resume"]
     if args.all:
-        warm = max(2, args.warmup // 2)
-        for name in ("prefill_bf16_T131072_H12", "prefill_bf16_varlen64_H96_resume",
-                     "prefill_f32_T256_H2"):
-            if name == args.workload:
-                continue
-            r = time_prefill(kda, wl, name, max(3, args.steps // 2), warm, 0, dev)
-            extra[name] = r
-            print("prefill %s: %.3f ms/step, %.3g tokens/s, %.1f%% MFMA"
-                  % (name, r["ms_per_step"], r["tokens_per_s"], 100 * r["mfma_frac"]),
-                  file=sys.stderr, flush=True)
-            rg = time_prefill(kda, wl, name, max(3, args.steps // 2), warm, 0, dev, gated=True)
+        names.append("prefill_f32_T256_H2")
+    warm = max(2, args.warmup // 4)
+    for name in names:
+        if name == args.workload:
+            continue
+        steps = 5 if "varlen" in name else max(5, args.steps // 2)
+        r = time_prefill(kda, wl, name, steps, warm, 0, dev)
+        extra[name] = r
+        print("prefill %s: %.3f ms/step, %.3g tokens/s, %.1f%% MFMA"
+              % (name, r["ms_per_step"], r["tokens_per_s"], 100 * r["mfma_frac"]),
+              file=sys.stderr, flush=True)
+        if args.all:
+            rg = time_prefill(kda, wl, name, steps, warm, 0, dev, gated=True)
             rg["vs_plain"] = rg["ms_per_step"] / r["ms_per_step"]
             extra[name + "_gated"] = rg
             print("prefill %s gated: %.3f ms/step (x%.3f)" % (name, rg["ms_per_step"],

@@ -26,6 +26,21 @@ KDA_F32 = 0
 KDA_BF16 = 1
 CHUNK = 64
 HEAD_DIM = 128
+# prefill implementations (kda_prefill_options.path); the prefill wrappers
+# pass DEFAULT_PREFILL_PATH when no path is given (tests set it to run one
+# implementation through helpers that do not take a path)
+PATHS = {"auto": 0, "two_kernel": 1, "fused": 2}
+DEFAULT_PREFILL_PATH = "auto"
+
+
+class PrefillOptions(ctypes.Structure):
+    """``kda_prefill_options`` of include/kda.h, field for field."""
+    _fields_ = [("path", ctypes.c_int32), ("ckpt_align", ctypes.c_int32),
+                ("ckpt_all", ctypes.c_int32), ("g_min", ctypes.c_float),
+                ("qk_norm_eps", ctypes.c_float), ("out_norm_eps", ctypes.c_float),
+                ("pos0_host", ctypes.POINTER(ctypes.c_int64)), ("ckpt_state", ctypes.c_void_p),
+                ("A_log", ctypes.c_void_p), ("out_gate", ctypes.c_void_p),
+                ("out_norm_weight", ctypes.c_void_p)]
 
 # Every symbol include/kda.h declares.
 EXPORTED = (
@@ -34,6 +49,8 @@ EXPORTED = (
     "kda_plan_num_segments",
     "kda_chunk_prefill_workspace_size",
     "kda_chunk_prefill",
+    "kda_chunk_prefill_ex_workspace_size",
+    "kda_chunk_prefill_ex",
     "kda_chunk_prefill_ckpt",
     "kda_chunk_prefill_ckpt_all",
     "kda_prefill_num_checkpoints",
@@ -80,6 +97,12 @@ def load():
         lib.kda_chunk_prefill.restype = i32
         lib.kda_chunk_prefill.argtypes = [i32, lp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                           vp, vp, i32, vp, sz, vp]
+        op = ctypes.POINTER(PrefillOptions)
+        lib.kda_chunk_prefill_ex_workspace_size.restype = sz
+        lib.kda_chunk_prefill_ex_workspace_size.argtypes = [i32, lp, i32, i32, i32, i32, i32, op]
+        lib.kda_chunk_prefill_ex.restype = i32
+        lib.kda_chunk_prefill_ex.argtypes = [i32, lp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                             vp, vp, i32, op, vp, sz, vp]
         lib.kda_chunk_prefill_ckpt.restype = i32
         lib.kda_chunk_prefill_ckpt.argtypes = [i32, lp, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                                vp, vp, vp, i32, lp, i32, vp, vp, sz, vp]
@@ -135,6 +158,10 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _addr(t):
+    return None if t is None else t.data_ptr()
+
+
 def _stream_ptr(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
@@ -152,6 +179,17 @@ def _host_cu(cu, T: int) -> np.ndarray:
 
 def _cu_ptr(cu: np.ndarray):
     return cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def _expect(t, shape, dtype, name):
+    """Reject a tensor whose shape or dtype is not what the kernels will
+    index: an undersized buffer would be read or written out of bounds."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s (got %s)" % (name, dtype, t.dtype))
 
 
 def _check_device(*ts):
@@ -177,33 +215,44 @@ def plan_num_segments(seq_len: int, num_seqs: int, H: int, split_hint: int = 0) 
     return r
 
 
-def prefill_workspace_size(cu_seqlens, H: int, dtype: torch.dtype, split_hint: int = 0) -> int:
+def _path_code(path: str) -> int:
+    path = path or DEFAULT_PREFILL_PATH
+    if path not in PATHS:
+        raise ValueError("path must be one of %s" % sorted(PATHS))
+    return PATHS[path]
+
+
+def prefill_workspace_size(cu_seqlens, H: int, dtype: torch.dtype, split_hint: int = 0,
+                           path: str = None) -> int:
     cu = _host_cu(cu_seqlens, 0)
-    return int(load().kda_chunk_prefill_workspace_size(cu.size - 1, _cu_ptr(cu), H, HEAD_DIM,
-                                                       HEAD_DIM, _dtype_code(dtype),
-                                                       split_hint))
+    opts = PrefillOptions(path=_path_code(path))
+    return int(load().kda_chunk_prefill_ex_workspace_size(cu.size - 1, _cu_ptr(cu), H, HEAD_DIM,
+                                                          HEAD_DIM, _dtype_code(dtype),
+                                                          split_hint, ctypes.byref(opts)))
 
 
 def chunk_prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None,
                   output_final_state: bool = True, split_hint: int = 0, o=None,
-                  final_state=None, workspace=None):
+                  final_state=None, workspace=None, path: str = None):
     """Chunked KDA prefill (``kda_chunk_prefill``).
 
     q, k, g: ``[T, H, 128]`` (or ``[B, T, H, 128]`` for B fixed-length
     sequences when ``cu_seqlens`` is None); v likewise; beta ``[T, H]`` or
     ``[B, T, H]``.  initial_state ``[N, H, 128, 128]`` fp32 or None.
     Returns ``(o, final_state or None)``.  ``final_state`` may be passed in
-    (it may be ``initial_state`` itself for an in-place resume).
+    (it may be ``initial_state`` itself for an in-place resume).  ``path``:
+    "auto", "two_kernel" or "fused" (``kda_prefill_options.path``).
     """
     o, final_state, _, _ = _prefill(q, k, v, g, beta, cu_seqlens, initial_state,
-                                    output_final_state, split_hint, o, final_state, workspace)
+                                    output_final_state, split_hint, o, final_state, workspace,
+                                    path=path)
     return o, final_state
 
 
 def chunk_prefill_checkpoint(q, k, v, g, beta, cu_seqlens=None, initial_state=None,
                              align: int = 512, pos0=None, checkpoint=None,
                              output_final_state: bool = True, split_hint: int = 0, o=None,
-                             final_state=None, workspace=None):
+                             final_state=None, workspace=None, path: str = None):
     """Prefill that also writes each sequence's state at its last
     ``align``-aligned absolute position (``kda_chunk_prefill_ckpt``).
 
@@ -214,13 +263,14 @@ def chunk_prefill_checkpoint(q, k, v, g, beta, cu_seqlens=None, initial_state=No
     aligned position past pos0[n] (checkpoint[n] is then not written).
     """
     return _prefill(q, k, v, g, beta, cu_seqlens, initial_state, output_final_state,
-                    split_hint, o, final_state, workspace, int(align), pos0, checkpoint)
+                    split_hint, o, final_state, workspace, int(align), pos0, checkpoint,
+                    path=path)
 
 
 def chunk_prefill_checkpoints(q, k, v, g, beta, cu_seqlens=None, initial_state=None,
                               align: int = 512, pos0=None, checkpoints=None,
                               output_final_state: bool = True, split_hint: int = 0, o=None,
-                              final_state=None, workspace=None):
+                              final_state=None, workspace=None, path: str = None):
     """Prefill that writes the state at every ``align``-aligned absolute
     position of every sequence (``kda_chunk_prefill_ckpt_all``).
 
@@ -230,14 +280,14 @@ def chunk_prefill_checkpoints(q, k, v, g, beta, cu_seqlens=None, initial_state=N
     """
     return _prefill(q, k, v, g, beta, cu_seqlens, initial_state, output_final_state,
                     split_hint, o, final_state, workspace, int(align), pos0, checkpoints,
-                    all_ckpts=True)
+                    all_ckpts=True, path=path)
 
 
 def chunk_prefill_gated(q, k, v, g, beta, A_log=None, g_min: float = -5.0,
                         qk_norm_eps: float = 0.0, out_gate=None, out_norm_weight=None,
                         out_norm_eps: float = 1e-6, cu_seqlens=None, initial_state=None,
                         output_final_state: bool = True, split_hint: int = 0, o=None,
-                        final_state=None, workspace=None):
+                        final_state=None, workspace=None, path: str = None):
     """Prefill with the layer's prologue and epilogue fused in
     (``kda_chunk_prefill_gated``).
 
@@ -252,14 +302,15 @@ def chunk_prefill_gated(q, k, v, g, beta, A_log=None, g_min: float = -5.0,
              float(out_norm_eps))
     o, final_state, _, _ = _prefill(q, k, v, g, beta, cu_seqlens, initial_state,
                                     output_final_state, split_hint, o, final_state, workspace,
-                                    gated=gated)
+                                    gated=gated, path=path)
     return o, final_state
 
 
 def _prefill(q, k, v, g, beta, cu_seqlens, initial_state, output_final_state, split_hint, o,
              final_state, workspace, align=0, pos0=None, checkpoint=None, gated=None,
-             all_ckpts=False):
+             all_ckpts=False, path=None):
     lib = load()
+    path = path or DEFAULT_PREFILL_PATH
     if q.dim() == 4:
         if cu_seqlens is not None and q.shape[0] != 1:
             raise ValueError("cu_seqlens requires B == 1")
@@ -283,69 +334,55 @@ def _prefill(q, k, v, g, beta, cu_seqlens, initial_state, output_final_state, sp
     N = cu.size - 1
     if cu[-1] != T:
         raise ValueError("cu_seqlens[-1] must equal the number of tokens")
+    _expect(initial_state, (N, H, dk, dv), torch.float32, "initial_state")
+    _expect(final_state, (N, H, dk, dv), torch.float32, "final_state")
+    _expect(o, (T, H, dv), dt, "o")
+    if gated is not None:
+        _layer_check(H, dv, dt, gated[0], gated[3], (T, H, dv), gated[4])
+    if align != 0:
+        p0 = np.zeros(N, dtype=np.int64) if pos0 is None else \
+            np.ascontiguousarray(np.asarray(pos0, dtype=np.int64))
+        if p0.shape != (N,):
+            raise ValueError("pos0 must hold one position per sequence")
+        if all_ckpts:
+            M = int(lib.kda_prefill_num_checkpoints(N, _cu_ptr(cu), _cu_ptr(p0), int(align)))
+            if M < 0:
+                raise ValueError("invalid cu_seqlens / pos0 / align for checkpoints")
+            shape = (M, H, dk, dv)
+        else:
+            shape = (N, H, dk, dv)
+        _expect(checkpoint, shape, torch.float32, "checkpoint buffer")
     dev = _check_device(q, k, v, g, beta, initial_state, final_state, o)
-    if initial_state is not None and (initial_state.dtype != torch.float32
-                                      or initial_state.shape != (N, H, dk, dv)):
-        raise ValueError("initial_state must be fp32 [N, H, dk, dv]")
     if o is None:
         o = torch.empty((T, H, dv), dtype=dt, device=dev)
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     code = _dtype_code(dt)
-    nbytes = int(lib.kda_chunk_prefill_workspace_size(N, _cu_ptr(cu), H, dk, dv, code,
-                                                      split_hint))
-    if workspace is None or workspace.numel() < nbytes:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    opts = PrefillOptions(path=_path_code(path), g_min=-5.0, out_norm_eps=1e-6)
     if gated is not None:
         A_log, g_min, qk_eps, out_gate, nw, neps = gated
-        _check_device(A_log, out_gate, nw)
-        if A_log is not None and (A_log.dtype != torch.float32 or A_log.shape != (H,)):
-            raise ValueError("A_log must be fp32 [H]")
-        if out_gate is not None and (out_gate.dtype != dt or out_gate.shape != (T, H, dv)):
-            raise ValueError("out_gate must have o's dtype and shape")
-        if nw is not None and (nw.dtype != torch.float32 or nw.shape != (dv,)):
-            raise ValueError("out_norm_weight must be fp32 [dv]")
-        st = lib.kda_chunk_prefill_gated(N, _cu_ptr(cu), H, dk, dv, code, _ptr(q), _ptr(k),
-                                         _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log), g_min,
-                                         qk_eps, _ptr(out_gate), _ptr(nw), neps,
-                                         _ptr(initial_state), _ptr(o), _ptr(final_state),
-                                         int(split_hint), _ptr(workspace), workspace.numel(),
-                                         _stream_ptr(dev))
-        if st != KDA_OK:
-            raise KdaError(st, "kda_chunk_prefill_gated")
-        return o, final_state, None, None
-    if align == 0:
-        st = lib.kda_chunk_prefill(N, _cu_ptr(cu), H, dk, dv, code, _ptr(q), _ptr(k), _ptr(v),
-                                   _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
-                                   _ptr(final_state), int(split_hint), _ptr(workspace),
-                                   workspace.numel(), _stream_ptr(dev))
-        if st != KDA_OK:
-            raise KdaError(st, "kda_chunk_prefill")
-        return o, final_state, None, None
-    p0 = np.zeros(N, dtype=np.int64) if pos0 is None else \
-        np.ascontiguousarray(np.asarray(pos0, dtype=np.int64))
-    if p0.shape != (N,):
-        raise ValueError("pos0 must hold one position per sequence")
-    if all_ckpts:
-        M = int(lib.kda_prefill_num_checkpoints(N, _cu_ptr(cu), _cu_ptr(p0), int(align)))
-        if M < 0:
-            raise ValueError("invalid cu_seqlens / pos0 / align for checkpoints")
-        shape = (M, H, dk, dv)
-    else:
-        shape = (N, H, dk, dv)
-    if checkpoint is None:
-        checkpoint = torch.zeros(shape, dtype=torch.float32, device=dev)
-    elif checkpoint.dtype != torch.float32 or checkpoint.shape != shape:
-        raise ValueError("checkpoint buffer must be fp32 %s" % (shape,))
-    _check_device(checkpoint)
-    fn = lib.kda_chunk_prefill_ckpt_all if all_ckpts else lib.kda_chunk_prefill_ckpt
-    st = fn(N, _cu_ptr(cu), H, dk, dv, code, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-            _ptr(initial_state), _ptr(o), _ptr(final_state), int(split_hint), _cu_ptr(p0),
-            int(align), _ptr(checkpoint) if checkpoint.numel() else None, _ptr(workspace),
-            workspace.numel(), _stream_ptr(dev))
+        opts.A_log, opts.g_min, opts.qk_norm_eps = _addr(A_log), g_min, qk_eps
+        opts.out_gate, opts.out_norm_weight, opts.out_norm_eps = _addr(out_gate), _addr(nw), neps
+    if align != 0:
+        if checkpoint is None:
+            checkpoint = torch.zeros(shape, dtype=torch.float32, device=dev)
+        _check_device(checkpoint)
+        opts.ckpt_align, opts.ckpt_all = int(align), int(bool(all_ckpts))
+        opts.pos0_host = _cu_ptr(p0)
+        opts.ckpt_state = _addr(checkpoint) if checkpoint.numel() else None
+    nbytes = int(lib.kda_chunk_prefill_ex_workspace_size(N, _cu_ptr(cu), H, dk, dv, code,
+                                                         split_hint, ctypes.byref(opts)))
+    # (0 for a request the call will refuse: it then returns its status)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    st = lib.kda_chunk_prefill_ex(N, _cu_ptr(cu), H, dk, dv, code, _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(o),
+                                  _ptr(final_state), int(split_hint), ctypes.byref(opts),
+                                  _ptr(workspace), workspace.numel(), _stream_ptr(dev))
     if st != KDA_OK:
-        raise KdaError(st, "kda_chunk_prefill_ckpt_all" if all_ckpts
-                       else "kda_chunk_prefill_ckpt")
+        raise KdaError(st, "kda_chunk_prefill_ex")
+    if align == 0:
+        return o, final_state, None, None
     if all_ckpts:
         seq, pos = [], []
         for n in range(N):
@@ -361,18 +398,27 @@ def _prefill(q, k, v, g, beta, cu_seqlens, initial_state, output_final_state, sp
     return o, final_state, checkpoint, pos
 
 
+def _decode_check(state, q, k, v, g, beta, o):
+    N, H, dk = k.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    _expect(state, (N, H, dk, dv), torch.float32, "state")
+    _expect(q, (N, H, dk), dt, "q")
+    _expect(g, (N, H, dk), dt, "g")
+    _expect(v, (N, H, dv), dt, "v")
+    _expect(k, (N, H, dk), dt, "k")
+    _expect(beta, (N, H), dt, "beta")
+    _expect(o, (N, H, dv), dt, "o")
+
+
 def decode_step(state, q, k, v, g, beta, o=None):
     """One in-place decode step (``kda_decode_step``): inputs ``[N, H, 128]``,
     beta ``[N, H]``, state ``[N, H, 128, 128]`` fp32 (updated).  Returns o."""
     lib = load()
     N, H, dk = k.shape
     dv = v.shape[-1]
-    if state.dtype != torch.float32 or state.shape != (N, H, dk, dv):
-        raise ValueError("state must be fp32 [N, H, dk, dv]")
+    _decode_check(state, q, k, v, g, beta, o)
     dt = q.dtype
-    for x in (k, v, g, beta):
-        if x.dtype != dt:
-            raise TypeError("q, k, v, g and beta must share one dtype")
     dev = _check_device(state, q, k, v, g, beta, o)
     if o is None:
         o = torch.empty((N, H, dv), dtype=dt, device=dev)
@@ -384,13 +430,10 @@ def decode_step(state, q, k, v, g, beta, o=None):
 
 
 def _layer_check(H, dv, dt, A_log, out_gate, out_shape, nw):
+    _expect(A_log, (H,), torch.float32, "A_log")
+    _expect(out_gate, out_shape, dt, "out_gate")
+    _expect(nw, (dv,), torch.float32, "out_norm_weight")
     _check_device(A_log, out_gate, nw)
-    if A_log is not None and (A_log.dtype != torch.float32 or A_log.shape != (H,)):
-        raise ValueError("A_log must be fp32 [H]")
-    if out_gate is not None and (out_gate.dtype != dt or out_gate.shape != out_shape):
-        raise ValueError("out_gate must have o's dtype and shape")
-    if nw is not None and (nw.dtype != torch.float32 or nw.shape != (dv,)):
-        raise ValueError("out_norm_weight must be fp32 [dv]")
 
 
 def decode_step_gated(state, q, k, v, g, beta, A_log=None, g_min: float = -5.0,
@@ -401,12 +444,8 @@ def decode_step_gated(state, q, k, v, g, beta, A_log=None, g_min: float = -5.0,
     lib = load()
     N, H, dk = k.shape
     dv = v.shape[-1]
-    if state.dtype != torch.float32 or state.shape != (N, H, dk, dv):
-        raise ValueError("state must be fp32 [N, H, dk, dv]")
+    _decode_check(state, q, k, v, g, beta, o)
     dt = q.dtype
-    for x in (k, v, g, beta):
-        if x.dtype != dt:
-            raise TypeError("q, k, v, g and beta must share one dtype")
     dev = _check_device(state, q, k, v, g, beta, o)
     _layer_check(H, dv, dt, A_log, out_gate, (N, H, dv), out_norm_weight)
     if o is None:
@@ -444,6 +483,7 @@ def decode_replay(state, accepted, ck, cv, cg, cbeta, q, k, v, g, beta, o=None, 
     for x in (ck, cv, cg, cbeta, q, v, g, beta):
         if x.dtype != dt:
             raise TypeError("the cached and new inputs must share one dtype")
+    _expect(o, (N, P, H, dv), dt, "o")
     dev = _check_device(state, accepted, ck, cv, cg, cbeta, q, k, v, g, beta, o)
     if o is None:
         o = torch.empty((N, P, H, dv), dtype=dt, device=dev)
@@ -491,6 +531,11 @@ def segment_transition(k, v, g, beta, cu_seglens=None, M=None, S_tilde=None, wor
     S = cu.size - 1
     if cu[-1] != T:
         raise ValueError("cu_seglens[-1] must equal the number of tokens")
+    _expect(g, (T, H, dk), dt, "g")
+    _expect(v, (T, H, dv), dt, "v")
+    _expect(beta, (T, H), dt, "beta")
+    _expect(M, (S, H, dk, dk), torch.float32, "M")
+    _expect(S_tilde, (S, H, dk, dv), torch.float32, "S_tilde")
     dev = _check_device(k, v, g, beta, M, S_tilde)
     if M is None:
         M = torch.empty((S, H, dk, dk), dtype=torch.float32, device=dev)
@@ -520,15 +565,13 @@ def segment_scan(M, S_tilde, initial_state=None, S_in=None):
     for x in (M, S_tilde, initial_state, S_in):
         if x is not None and (x.dtype != torch.float32 or not x.is_contiguous()):
             raise TypeError("M, S_tilde, initial_state and S_in must be contiguous fp32")
-    if S_tilde.shape != (S, H, dk, dv):
-        raise ValueError("S_tilde must be [num_segs, H, dk, dv]")
-    if initial_state is not None and initial_state.shape != (H, dk, dv):
-        raise ValueError("initial_state must be [H, dk, dv]")
+    _expect(M, (S, H, HEAD_DIM, HEAD_DIM), torch.float32, "M")
+    _expect(S_tilde, (S, H, HEAD_DIM, HEAD_DIM), torch.float32, "S_tilde")
+    _expect(initial_state, (H, dk, dv), torch.float32, "initial_state")
+    _expect(S_in, (S + 1, H, dk, dv), torch.float32, "S_in")
     dev = _check_device(M, S_tilde, initial_state, S_in)
     if S_in is None:
         S_in = torch.empty((S + 1, H, dk, dv), dtype=torch.float32, device=dev)
-    elif S_in.shape != (S + 1, H, dk, dv):
-        raise ValueError("S_in must be [num_segs + 1, H, dk, dv]")
     st = lib.kda_segment_scan(S, H, dk, dv, _ptr(M), _ptr(S_tilde), _ptr(initial_state),
                               _ptr(S_in), _stream_ptr(dev))
     if st != KDA_OK:

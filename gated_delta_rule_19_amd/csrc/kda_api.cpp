@@ -44,15 +44,6 @@ bool aligned_elt(const void *p, kda_dtype dt) {
   return ((uintptr_t)p & (dt == KDA_BF16 ? 1u : 3u)) == 0;
 }
 
-// KDA_FUSED_PREFILL=1 forces the fused bf16 prefill kernel, =0 the two-kernel
-// path (unsplit bf16 calls only); unset or any other value: automatic.
-int fused_override() {
-  const char *e = std::getenv("KDA_FUSED_PREFILL");
-  if (!e || !e[0] || e[1])
-    return -1;
-  return e[0] == '1' ? 1 : (e[0] == '0' ? 0 : -1);
-}
-
 int64_t plan_nseg(int64_t len, int32_t num_seqs, int32_t H, int32_t split_hint) {
   if (len <= 0)
     return 1;
@@ -90,6 +81,8 @@ struct Plan {
   int64_t npairs = 0, nsin = 0;
   // bf16 without a planner split runs the fused kernel: no chunk-prep records
   bool fused = false;
+  // the fused path was asked for a call it cannot run (fp32, or split)
+  bool path_unsupported = false;
   // workspace layout
   size_t off_chunks = 0, off_chains = 0, off_seg = 0, off_scan = 0, table_bytes = 0;
   size_t off_rec = 0, off_M = 0, off_St = 0, off_Sin = 0, total = 0;
@@ -174,10 +167,12 @@ void assign_ckpts(ChainDesc &c, const SeqCkpts &k, int64_t s0, int64_t cnt, int6
   c.ckpt_idx = (int32_t)(idx0 + j0);
 }
 
+// path: KDA_PATH_AUTO, KDA_PATH_TWO_KERNEL or KDA_PATH_FUSED (the caller has
+// checked that a fused request is bf16 and unsplit)
 bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_hint,
                         bool has_init, bool has_final, size_t es, Plan &p,
                         const int64_t *pos0 = nullptr, int64_t align = 0,
-                        bool all_ckpts = false) {
+                        bool all_ckpts = false, int32_t path = KDA_PATH_AUTO) {
   int64_t ckpt_base = 0; // first checkpoint index of the current sequence
   if (!cu || cu[0] != 0)
     return false;
@@ -233,12 +228,12 @@ bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_h
   // run fused in one kernel and no chunk-prep records go through memory.
   // With fewer chains the chunk-parallel prep kernel keeps the whole chip
   // busy and the two-kernel path is faster.
-  p.fused = es == 2 && p.segchains.empty() &&
-            (int64_t)p.chains.size() * H >= kFusedMinChainHeads;
-  if (es == 2 && p.segchains.empty()) {
-    const int force = fused_override();
-    if (force >= 0)
-      p.fused = force == 1;
+  const bool can_fuse = es == 2 && p.segchains.empty();
+  if (path == KDA_PATH_FUSED) {
+    p.fused = can_fuse;
+    p.path_unsupported = !can_fuse;
+  } else if (path == KDA_PATH_AUTO) {
+    p.fused = can_fuse && (int64_t)p.chains.size() * H >= kFusedMinChainHeads;
   }
   layout(p, H, es);
   return true;
@@ -406,9 +401,12 @@ kda_status prefill_impl(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_
                         float *final_state, int32_t split_hint, const int64_t *pos0,
                         int32_t ckpt_align, float *ckpt, void *workspace,
                         size_t workspace_bytes, void *stream, const Prologue &pro = Prologue(),
-                        const Epilogue &epi = Epilogue(), bool all_ckpts = false) {
+                        const Epilogue &epi = Epilogue(), bool all_ckpts = false,
+                        int32_t path = KDA_PATH_AUTO) {
   if (dk != kD || dv != kD || (dt != KDA_F32 && dt != KDA_BF16))
     return KDA_ERR_UNSUPPORTED;
+  if (path != KDA_PATH_AUTO && path != KDA_PATH_TWO_KERNEL && path != KDA_PATH_FUSED)
+    return KDA_ERR_INVALID_ARG;
   if (num_seqs < 0 || H < 1 || split_hint < 0 || !cu_seqlens_host)
     return KDA_ERR_INVALID_ARG;
   if (ckpt_align != 0) {
@@ -421,8 +419,10 @@ kda_status prefill_impl(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_
   Plan p;
   if (!build_prefill_plan(num_seqs, cu_seqlens_host, H, split_hint, initial_state != nullptr,
                           final_state != nullptr, elt_size(dt), p, pos0, ckpt_align,
-                          all_ckpts))
+                          all_ckpts, path))
     return KDA_ERR_INVALID_ARG;
+  if (p.path_unsupported)
+    return KDA_ERR_UNSUPPORTED;
   if (!plan_fits(p, H))
     return KDA_ERR_INVALID_ARG;
   const int64_t T = cu_seqlens_host[num_seqs];
@@ -571,18 +571,65 @@ int32_t kda_plan_num_segments(int64_t seq_len, int32_t num_seqs, int32_t H, int3
   return (int32_t)std::min<int64_t>(n, INT32_MAX);
 }
 
+size_t kda_chunk_prefill_ex_workspace_size(int32_t num_seqs, const int64_t *cu_seqlens_host,
+                                           int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
+                                           int32_t split_hint, const kda_prefill_options *opts) {
+  const int32_t path = opts ? opts->path : KDA_PATH_AUTO;
+  if (num_seqs < 0 || H < 1 || dk != kD || dv != kD || (dt != KDA_F32 && dt != KDA_BF16) ||
+      split_hint < 0 || (path != KDA_PATH_AUTO && path != KDA_PATH_TWO_KERNEL &&
+                         path != KDA_PATH_FUSED))
+    return 0;
+  Plan p;
+  // has_init / has_final and the checkpoint and layer options do not change
+  // the layout
+  if (!build_prefill_plan(num_seqs, cu_seqlens_host, H, split_hint, false, true, elt_size(dt),
+                          p, nullptr, 0, false, path) ||
+      p.path_unsupported)
+    return 0;
+  return p.total;
+}
+
 size_t kda_chunk_prefill_workspace_size(int32_t num_seqs, const int64_t *cu_seqlens_host,
                                         int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
                                         int32_t split_hint) {
-  if (num_seqs < 0 || H < 1 || dk != kD || dv != kD || (dt != KDA_F32 && dt != KDA_BF16) ||
-      split_hint < 0)
-    return 0;
-  Plan p;
-  // has_init / has_final do not change the layout
-  if (!build_prefill_plan(num_seqs, cu_seqlens_host, H, split_hint, false, true, elt_size(dt),
-                          p))
-    return 0;
-  return p.total;
+  return kda_chunk_prefill_ex_workspace_size(num_seqs, cu_seqlens_host, H, dk, dv, dt,
+                                             split_hint, nullptr);
+}
+
+kda_status kda_chunk_prefill_ex(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_t H,
+                                int32_t dk, int32_t dv, kda_dtype dt, const void *q,
+                                const void *k, const void *v, const void *g, const void *beta,
+                                const float *initial_state, void *o, float *final_state,
+                                int32_t split_hint, const kda_prefill_options *opts,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+  kda_prefill_options d;
+  std::memset(&d, 0, sizeof(d));
+  d.g_min = -5.f;
+  d.out_norm_eps = 1e-6f;
+  const kda_prefill_options &op = opts ? *opts : d;
+  Prologue pro;
+  Epilogue epi;
+  const kda_status st = layer_steps(op.A_log, op.g_min, op.qk_norm_eps, op.out_gate,
+                                    op.out_norm_weight, op.out_norm_eps, o, pro, epi);
+  if (st != KDA_OK)
+    return st;
+  if (op.ckpt_align < 0 || (op.ckpt_all != 0 && op.ckpt_all != 1))
+    return KDA_ERR_INVALID_ARG;
+  float *ckpt = op.ckpt_align > 0 ? op.ckpt_state : nullptr;
+  int32_t align = op.ckpt_align;
+  if (align > 0 && op.ckpt_all) {
+    const int64_t n = kda_prefill_num_checkpoints(num_seqs, cu_seqlens_host, op.pos0_host,
+                                                  align);
+    if (n < 0 || n > INT32_MAX / 2)
+      return KDA_ERR_INVALID_ARG;
+    if (n == 0) { // nothing to write: the states need no buffer
+      align = 0;
+      ckpt = nullptr;
+    }
+  }
+  return prefill_impl(num_seqs, cu_seqlens_host, H, dk, dv, dt, q, k, v, g, beta, initial_state,
+                      o, final_state, split_hint, align ? op.pos0_host : nullptr, align, ckpt,
+                      workspace, workspace_bytes, stream, pro, epi, op.ckpt_all != 0, op.path);
 }
 
 

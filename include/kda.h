@@ -114,10 +114,8 @@ int32_t kda_plan_num_segments(int64_t seq_len, int32_t num_seqs, int32_t H, int3
  * at least 512 (sequence, head) pairs, one fused kernel builds each chunk's
  * operands on chip while it carries the state (the workspace then holds only
  * the schedule); otherwise a chunk-parallel prep kernel writes the per-chunk
- * operands to the workspace and a state-carrying kernel reads them.  The
- * environment variable KDA_FUSED_PREFILL=1 (or 0) forces the fused (or the
- * two-kernel) path for unsplit bf16 calls; it must not change between the
- * workspace-size query and the call.
+ * operands to the workspace and a state-carrying kernel reads them.
+ * kda_chunk_prefill_ex chooses between them explicitly.
  *
  *   num_seqs         : N >= 0 sequences.
  *   cu_seqlens_host  : HOST, N+1 int64, cu[0] = 0, nondecreasing.  The
@@ -146,6 +144,61 @@ kda_status kda_chunk_prefill(int32_t num_seqs, const int64_t *cu_seqlens_host, i
                              const void *g, const void *beta, const float *initial_state,
                              void *o, float *final_state, int32_t split_hint, void *workspace,
                              size_t workspace_bytes, void *stream);
+
+/*
+ * The prefill with every option in one call: which implementation runs, the
+ * state checkpoints of kda_chunk_prefill_ckpt / kda_chunk_prefill_ckpt_all
+ * and the layer steps of kda_chunk_prefill_gated (the paragraphs of those
+ * calls define them; any combination is allowed).  The calls above are this
+ * one with some options fixed.
+ *
+ *   path          : KDA_PATH_AUTO (the library chooses as described for
+ *                   kda_chunk_prefill), KDA_PATH_TWO_KERNEL (chunk-prep
+ *                   kernel, then the state-carrying kernel; any dtype and
+ *                   split), or KDA_PATH_FUSED (the fused kernel; KDA_BF16
+ *                   and no planner split only, else KDA_ERR_UNSUPPORTED).
+ *   ckpt_align    : 0 for no checkpoints; else the hash-block length, a
+ *                   positive multiple of 64, with pos0_host and ckpt_state
+ *                   as for kda_chunk_prefill_ckpt; ckpt_all = 1 writes every
+ *                   aligned position (ckpt_state then as ckpt_states of
+ *                   kda_chunk_prefill_ckpt_all), 0 the last one only.
+ *   A_log, g_min, qk_norm_eps, out_gate, out_norm_weight, out_norm_eps :
+ *                   as for kda_chunk_prefill_gated (A_log NULL: g is the log
+ *                   decay; qk_norm_eps 0: q and k as given; out_gate NULL: o
+ *                   as the recurrence gives it).
+ * opts == NULL means path AUTO with no checkpoints and no layer steps.  The
+ * workspace size depends on the path: query it with
+ * kda_chunk_prefill_ex_workspace_size and the same options (it returns 0 for
+ * an invalid or unsupported request).
+ */
+#define KDA_PATH_AUTO 0
+#define KDA_PATH_TWO_KERNEL 1
+#define KDA_PATH_FUSED 2
+
+typedef struct kda_prefill_options {
+  int32_t path;
+  int32_t ckpt_align;
+  int32_t ckpt_all;
+  float g_min;
+  float qk_norm_eps;
+  float out_norm_eps;
+  const int64_t *pos0_host;
+  float *ckpt_state;
+  const float *A_log;
+  const void *out_gate;
+  const float *out_norm_weight;
+} kda_prefill_options;
+
+size_t kda_chunk_prefill_ex_workspace_size(int32_t num_seqs, const int64_t *cu_seqlens_host,
+                                           int32_t H, int32_t dk, int32_t dv, kda_dtype dt,
+                                           int32_t split_hint, const kda_prefill_options *opts);
+
+kda_status kda_chunk_prefill_ex(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_t H,
+                                int32_t dk, int32_t dv, kda_dtype dt, const void *q,
+                                const void *k, const void *v, const void *g, const void *beta,
+                                const float *initial_state, void *o, float *final_state,
+                                int32_t split_hint, const kda_prefill_options *opts,
+                                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * kda_chunk_prefill that also writes, per sequence, the state at its last

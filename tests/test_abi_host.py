@@ -328,3 +328,46 @@ def test_gated_decode_argument_errors(lib):
         assert fn(og=FAKE) == E.KDA_ERR_INVALID_ARG       # the gate may not be o
         assert fn(og=ctypes.c_void_p(0x200001)) == E.KDA_ERR_INVALID_ARG
         assert fn(N=0) == E.KDA_OK
+
+
+def test_options_struct_layout():
+    # kda_prefill_options: three int32, three float, five pointers
+    O = nat.PrefillOptions
+    assert ctypes.sizeof(O) == 64
+    assert [O.path.offset, O.ckpt_align.offset, O.ckpt_all.offset, O.g_min.offset,
+            O.qk_norm_eps.offset, O.out_norm_eps.offset, O.pos0_host.offset,
+            O.ckpt_state.offset, O.A_log.offset, O.out_gate.offset,
+            O.out_norm_weight.offset] == [0, 4, 8, 12, 16, 20, 24, 32, 40, 48, 56]
+
+
+def test_prefill_path_selection(lib):
+    """The implementation is an explicit argument of the size query and the
+    call; a fused request the fused kernel cannot run is refused by both."""
+    def size(cuv, H, dt, split, path):
+        a, p = cu(*cuv)
+        o = nat.PrefillOptions(path=path)
+        return lib.kda_chunk_prefill_ex_workspace_size(len(cuv) - 1, p, H, 128, 128, dt, split,
+                                                       ctypes.byref(o))
+    one = (0, 256)
+    auto = size(one, 2, nat.KDA_BF16, 0, 0)
+    two = size(one, 2, nat.KDA_BF16, 0, 1)
+    fused = size(one, 2, nat.KDA_BF16, 0, 2)
+    assert auto == two > 4 * 2 * 64 * 1024          # few chains: the two kernels, with records
+    assert 0 < fused < 64 * 1024                    # the fused kernel: schedule tables only
+    a, p = cu(*one)
+    assert auto == lib.kda_chunk_prefill_ex_workspace_size(1, p, 2, 128, 128, nat.KDA_BF16, 0,
+                                                           None)
+    assert size(one, 2, nat.KDA_F32, 0, 2) == 0     # fused is bf16 only
+    assert size((0, 64 * 64), 1, nat.KDA_BF16, 8, 2) == 0   # and takes no planner split
+    assert size(one, 2, nat.KDA_BF16, 0, 3) == 0    # unknown path
+    # the call refuses the same requests before touching the device
+    def call(dt, split, path, cuv=one):
+        a, p = cu(*cuv)
+        o = nat.PrefillOptions(path=path, g_min=-5.0, out_norm_eps=1e-6)
+        return lib.kda_chunk_prefill_ex(len(cuv) - 1, p, 2, 128, 128, dt, FAKE, FAKE, FAKE, FAKE,
+                                        FAKE, None, FAKE, FAKE, split, ctypes.byref(o), None, 0,
+                                        None)
+    assert call(nat.KDA_F32, 0, 2) == nat.KDA_ERR_UNSUPPORTED
+    assert call(nat.KDA_BF16, 8, 2, cuv=(0, 64 * 64)) == nat.KDA_ERR_UNSUPPORTED
+    assert call(nat.KDA_BF16, 0, 9) == nat.KDA_ERR_INVALID_ARG
+    assert call(nat.KDA_BF16, 0, 2) == nat.KDA_ERR_WORKSPACE   # valid request, no workspace

@@ -84,7 +84,8 @@ def test_checkpoint_with_planner_split(split):
 
 @pytest.fixture(params=["fused", "two_kernel"])
 def bf16_path(request, monkeypatch):
-    monkeypatch.setenv("KDA_FUSED_PREFILL", "1" if request.param == "fused" else "0")
+    monkeypatch.setattr(kda._native, "DEFAULT_PREFILL_PATH",
+                        "fused" if request.param == "fused" else "two_kernel")
     return request.param
 
 
@@ -99,7 +100,7 @@ def check_all(lengths, pos0, align, H, dtype, seed, split=0, fused=None, monkeyp
     print("all-checkpoints case", dict(lengths=lengths, pos0=pos0, align=align, H=H,
                                        dtype=str(dtype), split=split, fused=fused), flush=True)
     if fused is not None:
-        monkeypatch.setenv("KDA_FUSED_PREFILL", fused)
+        monkeypatch.setattr(kda._native, "DEFAULT_PREFILL_PATH", fused)
     cu = wl.cu_from_lengths(lengths)
     N, T = len(lengths), int(cu[-1])
     d = wl.token_inputs(T, H, dtype, seed, device=DEV, decay="mild")
@@ -139,7 +140,7 @@ def test_all_checkpoints_with_planner_split(split):
     check_all([1500, 300], [128, 0], 128, 2, torch.float32, 730, split=split)
 
 
-@pytest.mark.parametrize("fused", ["1", "0"])
+@pytest.mark.parametrize("fused", ["fused", "two_kernel"])
 def test_all_checkpoints_fused_and_two_kernel(fused, monkeypatch):
     check_all([700, 65, 1024, 256], [64, 0, 512, 192], 128, 4, torch.bfloat16, 740,
               fused=fused, monkeypatch=monkeypatch)

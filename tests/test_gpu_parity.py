@@ -96,8 +96,9 @@ def test_prefill_fp32_many_chains_two_tiles_per_wave():
 @pytest.fixture(params=["fused", "two_kernel"])
 def bf16_path(request, monkeypatch):
     """Run a bf16 test through one prefill implementation (the library reads
-    KDA_FUSED_PREFILL at every call)."""
-    monkeypatch.setenv("KDA_FUSED_PREFILL", "1" if request.param == "fused" else "0")
+    the path given to every prefill call)."""
+    monkeypatch.setattr(kda._native, "DEFAULT_PREFILL_PATH",
+                        "fused" if request.param == "fused" else "two_kernel")
     say("bf16 prefill path:", request.param)
     return request.param
 

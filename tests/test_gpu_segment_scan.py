@@ -61,6 +61,23 @@ def test_segment_scan_vs_oracle(nseg, H, init):
     assert rel_err(S_in, ref) <= 1e-4
 
 
+def test_segment_scan_more_than_255_pairs():
+    """300 pairs: more steps than any 8-bit count could hold.  The fold does
+    not depend on the pairs being transitions of real tokens, so random
+    contracting M (spectral radius about 0.5) and random S~ serve."""
+    S, H = 300, 2
+    say("segment scan case", dict(nseg=S, H=H, init=True))
+    rng = np.random.default_rng(1250)
+    M = torch.from_numpy(rng.standard_normal((S, H, 128, 128)) * (0.5 / np.sqrt(128)))
+    St = torch.from_numpy(rng.standard_normal((S, H, 128, 128)))
+    M, St = M.float().to(DEV), St.float().to(DEV)
+    S0 = wl.states(1, H, 1251, device=DEV)[0]
+    S_in = kda.segment_scan(M, St, S0)
+    torch.cuda.synchronize()
+    ref = oracle.segment_scan(M, St, S0)
+    assert rel_err(S_in, ref) <= 1e-4
+
+
 def test_segment_scan_without_pairs():
     say("segment scan, no pairs")
     H = 3

@@ -44,12 +44,13 @@ def rel_err(x, ref):
 @pytest.fixture(params=["fp32", "bf16_fused", "bf16_two_kernel", "fp32_split", "bf16_split"])
 def path(request, monkeypatch):
     """(dtype, split_hint) of one prefill implementation; the library reads
-    KDA_FUSED_PREFILL at every call."""
+    the path given to every prefill call."""
     name = request.param
     dtype = torch.float32 if name.startswith("fp32") else torch.bfloat16
     split = 2 if name.endswith("split") else 0
     if name.startswith("bf16"):
-        monkeypatch.setenv("KDA_FUSED_PREFILL", "1" if name == "bf16_fused" else "0")
+        monkeypatch.setattr(kda._native, "DEFAULT_PREFILL_PATH",
+                            "fused" if name == "bf16_fused" else "two_kernel")
     say("special-gate path:", name)
     return dtype, split
 
