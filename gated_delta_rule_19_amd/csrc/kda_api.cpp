@@ -176,6 +176,10 @@ bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_h
   int64_t ckpt_base = 0; // first checkpoint index of the current sequence
   if (!cu || cu[0] != 0)
     return false;
+  // the fused kernel takes whole sequences: asking for it turns the
+  // automatic split off (an explicit split is refused below)
+  if (path == KDA_PATH_FUSED && split_hint == 0)
+    split_hint = 1;
   for (int32_t n = 0; n < N; ++n)
     if (cu[n + 1] < cu[n] || cu[n + 1] - cu[n] > INT32_MAX)
       return false;

@@ -156,7 +156,9 @@ kda_status kda_chunk_prefill(int32_t num_seqs, const int64_t *cu_seqlens_host, i
  *                   kda_chunk_prefill), KDA_PATH_TWO_KERNEL (chunk-prep
  *                   kernel, then the state-carrying kernel; any dtype and
  *                   split), or KDA_PATH_FUSED (the fused kernel; KDA_BF16
- *                   and no planner split only, else KDA_ERR_UNSUPPORTED).
+ *                   only; it takes whole sequences, so split_hint = 0 then
+ *                   means no split, and split_hint > 1 on a sequence of more
+ *                   than one chunk is KDA_ERR_UNSUPPORTED).
  *   ckpt_align    : 0 for no checkpoints; else the hash-block length, a
  *                   positive multiple of 64, with pos0_host and ckpt_state
  *                   as for kda_chunk_prefill_ckpt; ckpt_all = 1 writes every

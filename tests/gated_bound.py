@@ -13,26 +13,34 @@ against the largest one is scaled up by the norm, and with it its share of
 the recurrence's error.
 
 Rows with r_ref <= E get no finite bound from this: their recurrence output
-is within the error of zero.  They are counted, the count is printed, and
-their fraction of all rows is held to MAX_EXEMPT_FRACTION.  They are held to
-what the norm guarantees for any input, |y| <= |s| sqrt(dv) (a row's largest
-element is at most sqrt(dv) times its rms), with the bf16 rounding of y on
-top.
+is within the error of zero.  They are checked against the GPU's own
+recurrence output instead: the test also runs the same call without the
+output gate, which gives o~_gpu (held to the plain bar itself), and on those
+rows y must equal s o~_gpu / r(o~_gpu) up to the roundings between the two
+(o~ to bf16, r from it, y to bf16: 2^-6 of each element, plus 2^-12 of the
+row's largest).  That checks the output step's arithmetic exactly where the
+derived bound says nothing.  Their count is printed and held to
+MAX_EXEMPT_FRACTION (a sanity limit: 0 to 18% of the rows in these tests,
+about 3% at the full-size workloads).
 """
 import numpy as np
 
 # the largest fraction of rows allowed below the bar (r_ref <= E)
-MAX_EXEMPT_FRACTION = 0.02
+MAX_EXEMPT_FRACTION = 0.25
 
 
-def check_norm_bound(y, y_ref, ot_ref, s, tol, eps, label=""):
-    """y, y_ref, ot_ref, s: fp64 arrays with rows over the last axis (s may
-    broadcast); eps: the norm's epsilon (inside r and r_ref).  Returns
+def check_norm_bound(y, y_ref, ot_ref, s, tol, eps, ot_gpu, label=""):
+    """y, y_ref, ot_ref, ot_gpu, s: fp64 arrays with rows over the last axis
+    (s may broadcast); eps: the norm's epsilon (inside r and r_ref).  Returns
     (largest error / bound over the bounded rows, count of rows below the
     bar)."""
     y = np.asarray(y, dtype=np.float64)
-    assert y.shape == y_ref.shape == ot_ref.shape
-    assert np.all(np.isfinite(y))
+    ot_gpu = np.asarray(ot_gpu, dtype=np.float64)
+    assert y.shape == y_ref.shape == ot_ref.shape == ot_gpu.shape
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(ot_gpu))
+    # the recurrence output itself meets the plain bar
+    e_plain = float(np.max(np.abs(ot_gpu - ot_ref))) / max(float(np.max(np.abs(ot_ref))), 1e-30)
+    assert e_plain <= tol, ("o without the output gate", e_plain)
     s = np.abs(np.broadcast_to(s, y.shape))
     E = tol * float(np.max(np.abs(ot_ref)))
     r = np.sqrt(np.mean(ot_ref * ot_ref, axis=-1, keepdims=True) + eps)
@@ -49,7 +57,11 @@ def check_norm_bound(y, y_ref, ot_ref, s, tol, eps, label=""):
         excess = float(np.max(np.abs(y[bounded] - y_ref[bounded]) / bound))
         assert excess <= 1.0, ("o vs its bound", excess)
     if exempt:
-        dv = y.shape[-1]
-        cap = s[~bounded] * np.sqrt(dv) * (1.0 + 2.0 ** -7)
-        assert np.all(np.abs(y[~bounded]) <= cap), "a row below the bar exceeds the norm's cap"
+        og = ot_gpu[~bounded]
+        rg = np.sqrt(np.mean(og * og, axis=-1, keepdims=True) + eps)
+        y_exp = s[~bounded] * og / rg
+        lim = 2.0 ** -6 * np.abs(y_exp) + 2.0 ** -12 * np.max(np.abs(y_exp), axis=-1,
+                                                               keepdims=True)
+        worst = float(np.max(np.abs(y[~bounded] - y_exp) - lim))
+        assert worst <= 0.0, ("a row below the bar differs from its own output step", worst)
     return excess, exempt

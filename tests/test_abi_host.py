@@ -359,6 +359,8 @@ def test_prefill_path_selection(lib):
                                                            None)
     assert size(one, 2, nat.KDA_F32, 0, 2) == 0     # fused is bf16 only
     assert size((0, 64 * 64), 1, nat.KDA_BF16, 8, 2) == 0   # and takes no planner split
+    # (asking for it turns the automatic split off: few heads of one long sequence)
+    assert 0 < size((0, 64 * 64), 1, nat.KDA_BF16, 0, 2) < 64 * 1024
     assert size(one, 2, nat.KDA_BF16, 0, 3) == 0    # unknown path
     # the call refuses the same requests before touching the device
     def call(dt, split, path, cuv=one):

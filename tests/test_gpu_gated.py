@@ -67,7 +67,13 @@ def gated_vs_oracle(lengths, H, dtype, seed, gate=True, qk=True, epi=True, weigh
         cu_seqlens=cu, initial_state=S0, **kw)
     if T > 0:
         if epi and dtype == torch.bfloat16:
-            check_gated_bound(o, o_ref, d, nw, kw, qk, cu, S0, dtype)
+            # the same call without the output gate: the GPU's own o~
+            ot_gpu, _ = kda.chunk_prefill_gated(
+                d["q"], d["k"], d["v"], d["z"], d["beta"], A_log=d["A_log"] if gate else None,
+                qk_norm_eps=QK_EPS if qk else 0.0, cu_seqlens=cu, initial_state=S0,
+                split_hint=split)
+            torch.cuda.synchronize()
+            check_gated_bound(o, o_ref, d, nw, kw, qk, cu, S0, dtype, ot_gpu)
         else:
             eo = rel_err(o, o_ref)
             assert eo <= TOL[dtype], ("o", eo)
@@ -76,8 +82,9 @@ def gated_vs_oracle(lengths, H, dtype, seed, gate=True, qk=True, epi=True, weigh
     return o, fin
 
 
-def check_gated_bound(o, y_ref, d, nw, kw, qk, cu, S0, dtype):
-    """The bf16 bound above, element by element."""
+def check_gated_bound(o, y_ref, d, nw, kw, qk, cu, S0, dtype, ot_gpu):
+    """The bf16 bound above, element by element (ot_gpu: the GPU's o~ from
+    the same call without the output gate)."""
     ot_ref, _ = oracle.prefill_gated(d["q"], d["k"], d["v"], d["beta"],
                                      qk_norm_eps=QK_EPS if qk else None, cu_seqlens=cu,
                                      initial_state=S0, **kw)
@@ -85,7 +92,7 @@ def check_gated_bound(o, y_ref, d, nw, kw, qk, cu, S0, dtype):
     w = np.ones(ot_ref.shape[-1]) if nw is None else nw.detach().cpu().double().numpy()
     s = w / (1.0 + np.exp(-gate))
     norm_bar(o.detach().cpu().double().numpy(), y_ref, ot_ref, s, TOL[dtype], OUT_EPS,
-             "prefill")
+             ot_gpu.detach().cpu().double().numpy(), "prefill")
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -195,16 +202,17 @@ def test_gated_epilogue_exact_recurrence_bf16(path, monkeypatch):
 # --- decode and replay with the layer's steps -------------------------------
 
 
-def check_norm_bound(y, y_ref, ot_ref, gate, nw, dtype):
+def check_norm_bound(y, y_ref, ot_ref, gate, nw, dtype, ot_gpu):
     """The output-norm bar of this file's docstring, for any output layout
-    (rows over the last axis)."""
+    (rows over the last axis); ot_gpu: the GPU's o~ from the same call
+    without the output gate."""
     if dtype == torch.float32:
         assert rel_err(y, y_ref) <= TOL[dtype]
         return
     g = gate.detach().cpu().double().numpy()
     w = np.ones(ot_ref.shape[-1]) if nw is None else nw.detach().cpu().double().numpy()
     norm_bar(y.detach().cpu().double().numpy(), y_ref, ot_ref, w / (1.0 + np.exp(-g)),
-             TOL[dtype], OUT_EPS, "decode")
+             TOL[dtype], OUT_EPS, ot_gpu.detach().cpu().double().numpy(), "decode")
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -217,6 +225,10 @@ def test_decode_step_gated(dtype):
     cu = np.arange(N + 1, dtype=np.int64)
     for s_ in range(steps):
         sl = slice(s_ * N, (s_ + 1) * N)
+        # the same step without the output gate, on a copy of the state
+        ot_gpu = kda.decode_step_gated(state.clone(), d["q"][sl], d["k"][sl], d["v"][sl],
+                                       d["z"][sl], d["beta"][sl], A_log=d["A_log"],
+                                       qk_norm_eps=QK_EPS)
         o = kda.decode_step_gated(state, d["q"][sl], d["k"][sl], d["v"][sl], d["z"][sl],
                                   d["beta"][sl], A_log=d["A_log"], qk_norm_eps=QK_EPS,
                                   out_gate=d["out_gate"][sl], out_norm_weight=d["norm_weight"],
@@ -230,7 +242,7 @@ def test_decode_step_gated(dtype):
                                           out_gate=d["out_gate"][sl],
                                           out_norm_weight=d["norm_weight"],
                                           out_norm_eps=OUT_EPS, **kw)
-        check_norm_bound(o, y_ref, ot_ref, d["out_gate"][sl], d["norm_weight"], dtype)
+        check_norm_bound(o, y_ref, ot_ref, d["out_gate"][sl], d["norm_weight"], dtype, ot_gpu)
     assert rel_err(state, ref) <= TOL[dtype]
 
 
@@ -247,6 +259,9 @@ def test_decode_replay_gated(dtype, epi):
     acc = torch.tensor([0, 1, 4, 2, 7, -1], dtype=torch.int32, device=DEV)
     state = wl.states(N, H, 622, device=DEV)
     S0 = state.detach().cpu().double().numpy()
+    # the same replay without the output gate, on a copy of the state
+    ot_gpu = kda.decode_replay_gated(state.clone(), acc, ck, cv, cz, cb, q, k, v, z, b,
+                                     A_log=x["A_log"], qk_norm_eps=QK_EPS)
     o = kda.decode_replay_gated(state, acc, ck, cv, cz, cb, q, k, v, z, b, A_log=x["A_log"],
                                 qk_norm_eps=QK_EPS, out_gate=og if epi else None,
                                 out_norm_weight=x["norm_weight"], out_norm_eps=OUT_EPS)
@@ -258,7 +273,7 @@ def test_decode_replay_gated(dtype, epi):
         y_ref, _ = oracle.decode_replay_gated(S0, acc.cpu().numpy(), ck, cv, cz, cb, q, k, v, z,
                                               b, out_gate=og, out_norm_weight=x["norm_weight"],
                                               out_norm_eps=OUT_EPS, **kw)
-        check_norm_bound(o, y_ref, ot_ref, og, x["norm_weight"], dtype)
+        check_norm_bound(o, y_ref, ot_ref, og, x["norm_weight"], dtype, ot_gpu)
     else:
         assert rel_err(o, ot_ref) <= TOL[dtype]
     assert rel_err(state, committed) <= TOL[dtype]

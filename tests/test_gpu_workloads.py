@@ -134,12 +134,16 @@ def run_gated(name):
                                      qk_norm_eps=1e-6, out_gate=d["v"], out_norm_weight=nw,
                                      out_norm_eps=1e-6, cu_seqlens=d["cu"],
                                      initial_state=d["init"])
+    # the same call without the output gate: the GPU's own o~
+    ot_gpu, _ = kda.chunk_prefill_gated(d["q"], d["k"], d["v"], d["g"], d["beta"], A_log=A,
+                                        qk_norm_eps=1e-6, cu_seqlens=d["cu"],
+                                        initial_state=d["init"], output_final_state=False)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all() and torch.isfinite(fin).all()
-    return w, d, A, nw, o, fin
+    return w, d, A, nw, o, fin, ot_gpu
 
 
-def check_heads_gated(w, d, A, nw, o, fin, seqs, heads):
+def check_heads_gated(w, d, A, nw, o, fin, ot_gpu, seqs, heads):
     cu = d["cu"]
     tol = TOL[w.dtype]
     wn = nw.cpu().double().numpy()
@@ -154,7 +158,8 @@ def check_heads_gated(w, d, A, nw, o, fin, seqs, heads):
         y = o[a:b, heads].detach().cpu().double().numpy()
         assert np.all(np.isfinite(y))
         s = wn / (1.0 + np.exp(-sl["v"].detach().cpu().double().numpy()))
-        ex, nex = norm_bar(y, y_ref, ot, s, tol, 1e-6, "seq %d" % n)
+        ex, nex = norm_bar(y, y_ref, ot, s, tol, 1e-6,
+                           ot_gpu[a:b, heads].detach().cpu().double().numpy(), "seq %d" % n)
         ef = rel_err(fin[n:n + 1, heads], f_ref)
         say("  seq %d len %d heads %s: o vs bound %.3g (%d rows below the bar), err_S %.3g"
             % (n, b - a, heads, ex, nex, ef))
@@ -162,12 +167,12 @@ def check_heads_gated(w, d, A, nw, o, fin, seqs, heads):
 
 
 def test_gated_prefill_bf16_T8192_H96_sampled_heads():
-    w, d, A, nw, o, fin = run_gated("prefill_bf16_T8192_H96")
-    check_heads_gated(w, d, A, nw, o, fin, [0], list(range(0, 96, 16)))
+    w, d, A, nw, o, fin, ot = run_gated("prefill_bf16_T8192_H96")
+    check_heads_gated(w, d, A, nw, o, fin, ot, [0], list(range(0, 96, 16)))
 
 
 def test_gated_prefill_bf16_varlen64_H96_resume_sampled():
-    w, d, A, nw, o, fin = run_gated("prefill_bf16_varlen64_H96_resume")
+    w, d, A, nw, o, fin, ot = run_gated("prefill_bf16_varlen64_H96_resume")
     lens = np.diff(d["cu"])
     seqs = sorted({int(np.argmin(lens)), 17})
-    check_heads_gated(w, d, A, nw, o, fin, seqs, [0, 95])
+    check_heads_gated(w, d, A, nw, o, fin, ot, seqs, [0, 95])
