@@ -51,6 +51,7 @@ EXPORTED = (
     "kda_chunk_prefill",
     "kda_chunk_prefill_ex_workspace_size",
     "kda_chunk_prefill_ex",
+    "kda_chunk_prefill_noalloc",
     "kda_chunk_prefill_ckpt",
     "kda_chunk_prefill_ckpt_all",
     "kda_prefill_num_checkpoints",
@@ -103,6 +104,9 @@ def load():
         lib.kda_chunk_prefill_ex.restype = i32
         lib.kda_chunk_prefill_ex.argtypes = [i32, lp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                              vp, vp, i32, op, vp, sz, vp]
+        lib.kda_chunk_prefill_noalloc.restype = i32
+        lib.kda_chunk_prefill_noalloc.argtypes = [i32, lp, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                                  vp, vp, vp, vp]
         lib.kda_chunk_prefill_ckpt.restype = i32
         lib.kda_chunk_prefill_ckpt.argtypes = [i32, lp, i32, i32, i32, i32, vp, vp, vp, vp, vp,
                                                vp, vp, vp, i32, lp, i32, vp, vp, sz, vp]

@@ -25,6 +25,10 @@
 
 using namespace kda;
 
+static_assert(kNoAllocScratchBytes == (size_t)KDA_NOALLOC_SCRATCH_BYTES,
+              "the header's scratch size is the library's");
+static_assert(sizeof(kda_prefill_options) == 64, "kda_prefill_options layout");
+
 namespace {
 
 // Automatic split policy: split only when the unsplit state-carrying work
@@ -660,6 +664,60 @@ kda_status kda_chunk_prefill_ckpt(int32_t num_seqs, const int64_t *cu_seqlens_ho
   return prefill_impl(num_seqs, cu_seqlens_host, H, dk, dv, dt, q, k, v, g, beta, initial_state,
                       o, final_state, split_hint, pos0_host, ckpt_align, ckpt_state, workspace,
                       workspace_bytes, stream);
+}
+
+kda_status kda_chunk_prefill_noalloc(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_t H,
+                                     int32_t dk, int32_t dv, kda_dtype dt, const void *q,
+                                     const void *k, const void *v, const void *g,
+                                     const void *beta, const float *initial_state, void *o,
+                                     float *final_state, void *stream) {
+  if (dk != kD || dv != kD || dt != KDA_BF16)
+    return KDA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || H < 1 || !cu_seqlens_host)
+    return KDA_ERR_INVALID_ARG;
+  Plan p;
+  if (!build_prefill_plan(num_seqs, cu_seqlens_host, H, 0, initial_state != nullptr,
+                          final_state != nullptr, 2, p, nullptr, 0, false, KDA_PATH_FUSED))
+    return KDA_ERR_INVALID_ARG;
+  if (p.path_unsupported || !p.fused || !plan_fits(p, H))
+    return KDA_ERR_INVALID_ARG;
+  const int64_t T = cu_seqlens_host[num_seqs];
+  if (T > 0) {
+    if (!q || !k || !v || !g || !beta || !o)
+      return KDA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) ||
+        !aligned_elt(beta, dt) || !aligned16(o))
+      return KDA_ERR_INVALID_ARG;
+  }
+  if (!aligned16(initial_state) || !aligned16(final_state))
+    return KDA_ERR_INVALID_ARG;
+  // the schedule must fit the fixed scratch (no workspace argument)
+  if (p.total > kNoAllocScratchBytes)
+    return KDA_ERR_WORKSPACE;
+  if (num_seqs == 0)
+    return KDA_OK;
+  void *scr = nullptr;
+  hipError_t e = noalloc_scratch(&scr);
+  if (e != hipSuccess)
+    return KDA_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  {
+    // The tables go up from a fixed host buffer.  A copy from pageable host
+    // memory has read its source when hipMemcpyAsync returns, so the buffer
+    // is free again for the next call (the lock orders host threads).
+    static std::mutex mu;
+    static uint8_t host[kNoAllocScratchBytes];
+    std::lock_guard<std::mutex> lk(mu);
+    std::memset(host, 0, p.table_bytes);
+    if (!p.chains.empty())
+      std::memcpy(host + p.off_chains, p.chains.data(), p.chains.size() * sizeof(ChainDesc));
+    e = hipMemcpyAsync(scr, host, p.table_bytes, hipMemcpyHostToDevice, s);
+  }
+  if (e == hipSuccess)
+    e = launch_fused((const ChainDesc *)((uint8_t *)scr + p.off_chains),
+                     (int32_t)p.chains.size(), H, q, k, v, g, beta, o, initial_state, nullptr,
+                     final_state, nullptr, Prologue(), Epilogue(), s);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 int64_t kda_prefill_num_checkpoints(int32_t num_seqs, const int64_t *cu_seqlens_host,

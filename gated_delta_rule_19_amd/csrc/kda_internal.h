@@ -130,6 +130,14 @@ struct Epilogue {
   bool on() const { return gate != nullptr; }
 };
 
+// Size of the fixed device scratch of the allocation-free prefill
+// (kda_chunk_prefill_noalloc): its schedule tables, one per device.
+constexpr size_t kNoAllocScratchBytes = 1u << 20;
+
+// The device address of this device's fixed scratch (kda_scratch.hip):
+// hipGetSymbolAddress on the first call per device, cached afterwards.
+hipError_t noalloc_scratch(void **out);
+
 // Launchers (enqueue only; return the hipGetLastError of the launch).
 hipError_t launch_k1(int elt, const ChunkDesc *chunks, int32_t nchunks, int32_t H,
                      const void *q, const void *k, const void *g, const void *beta, void *ws,

@@ -203,6 +203,30 @@ kda_status kda_chunk_prefill_ex(int32_t num_seqs, const int64_t *cu_seqlens_host
                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kda_chunk_prefill for callers that cannot allocate device memory (code in
+ * tight serving loops, or harnesses that forbid hipMalloc): it takes no
+ * workspace and allocates nothing.  It runs the fused kernel (KDA_BF16 only,
+ * no planner split) with its schedule tables in a fixed device array of
+ * KDA_NOALLOC_SCRATCH_BYTES that each device the library runs on holds until
+ * the process ends; the tables are uploaded with a host-to-device copy from
+ * a fixed host buffer.
+ *   Returns KDA_ERR_UNSUPPORTED for dt != KDA_BF16 or dk, dv != 128, and
+ *   KDA_ERR_WORKSPACE when the schedule exceeds the array (40 bytes per
+ *   sequence plus alignment: about 26,000 sequences).
+ * Every call on one device uses that device's array, which keeps the last
+ * call's contents: calls that overlap on one GPU (on different streams, or
+ * from different host threads without ordering) race.  Arguments and results
+ * are otherwise those of kda_chunk_prefill with split_hint = 0.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (1 << 20)
+
+kda_status kda_chunk_prefill_noalloc(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_t H,
+                                     int32_t dk, int32_t dv, kda_dtype dt, const void *q,
+                                     const void *k, const void *v, const void *g,
+                                     const void *beta, const float *initial_state, void *o,
+                                     float *final_state, void *stream);
+
+/*
  * kda_chunk_prefill that also writes, per sequence, the state at its last
  * hash-aligned position: the KDA checkpoint a prefix cache keeps after each
  * forward pass ("部署 Kimi K3：从 KDA Kernel 到 Fleet 调度" §三 3.2, the KDA
