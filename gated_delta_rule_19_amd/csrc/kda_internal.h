@@ -167,6 +167,15 @@ hipError_t launch_fused(const ChainDesc *chains, int32_t nchains, int32_t H, con
                         const float *init, const float *sin, float *final_state, float *ckpt,
                         const Prologue &pro, const Epilogue &epi, hipStream_t s);
 
+// Fused chunk prep + state chain, one workgroup per (chain, head) with all
+// dv columns (bf16, no prologue or epilogue; entry states from `init` or
+// zero): writes o, exit states and (when ckpt is not null) the chains' state
+// checkpoints.
+hipError_t launch_fused2(const ChainDesc *chains, int32_t nchains, int32_t H, const void *q,
+                         const void *k, const void *v, const void *g, const void *beta,
+                         void *o, const float *init, float *final_state, float *ckpt,
+                         hipStream_t s);
+
 // Whether the state chain's replay pass takes the output epilogue itself:
 // when its plain launch runs 128-column blocks anyway (at least one wide
 // workgroup per compute unit).  Otherwise it runs the 64-column blocks
