@@ -61,7 +61,7 @@ def stored_traffic(workload: str):
 COPY_PROBE_FLOATS = 256 << 20   # 1 GiB fp32 read + 1 GiB written by the calibration copy
 
 
-def traffic_probe(kda, wl, name, dev):
+def traffic_probe(kda, wl, name, dev, path="auto"):
     """One prefill call and one decode step bracketed by a plain elementwise
     copy of known size, for rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE):
     the copy's counter reading calibrates the counters to bytes."""
@@ -73,12 +73,12 @@ def traffic_probe(kda, wl, name, dev):
     T = int(cu[-1])
     o = torch.empty((T, H, D), dtype=w.dtype, device=dev)
     fin = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(kda.prefill_workspace_size(cu, H, w.dtype, 0), 1), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(max(kda.prefill_workspace_size(cu, H, w.dtype, 0, path=path), 1),
+                     dtype=torch.uint8, device=dev)
 
     def step():
         kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu,
-                          initial_state=d["init"], o=o, final_state=fin, workspace=ws)
+                          initial_state=d["init"], o=o, final_state=fin, workspace=ws, path=path)
 
     step()                                   # warm (first-touch, schedule upload)
     torch.cuda.synchronize(dev)
@@ -416,7 +416,7 @@ def main():
     kda.load()
     dev = torch.device("cuda:0")
     if args.traffic_probe:
-        traffic_probe(kda, wl, args.workload, dev)
+        traffic_probe(kda, wl, args.workload, dev, path=args.path)
         return
     main_res = time_prefill(kda, wl, args.workload, args.steps, args.warmup, args.split, dev,
                             path=args.path)

@@ -27,22 +27,36 @@
 //
 // Workgroup of 8 waves, two per SIMD:
 //   waves 0-3, state: wave w carries state columns 32 w .. 32 w + 31 (two
-//     16-column MFMA tiles) through the chunks, S in MFMA accumulators;
+//     16-column MFMA tiles) through the chunks, S in MFMA accumulators.
+//     After its chunk step it also inverts D_w of the chunk being prepared:
+//     a chain of dependent MFMAs that would otherwise sit on the prep waves'
+//     path, which is the longer one;
 //   waves 4-7, prep: wave 4 + I owns token tile I of the chunk being
 //     prepared.  Lane (lr, lg) = (lane % 16, lane / 16) holds token 16 I + lr
 //     and, for k-step s, channels 32 s + 8 lg .. + 7: one 16-byte load per
 //     input and k-step, and the MFMA A-fragment layout.
-// Step k: the prep waves build chunk k's record into LDS buffer k % 2 while
-// the state waves consume chunk k - 1 from the other buffer; one workgroup
-// barrier ends each step.  Inside a step the prep waves meet twice more on
-// an LDS counter (the state waves are not held): after the tile scan (tile
-// totals), and after their K_rs tiles are written (off-diagonal pairs).
+// Step k: the prep waves build chunk k's operands while the state waves
+// consume chunk k - 1's; one workgroup barrier ends each step.  The prep
+// waves also scan chunk k + 1's decay and turn the tile totals into their
+// per-channel factors within step k, so chunk k + 1's elementwise work
+// starts as soon as step k + 1 does.  Q_decay, K_decay, M_qk and the L and
+// D^-1 blocks, which the state waves read early in a step, have one LDS
+// copy: the prep waves overwrite them only after every state wave has
+// counted itself done with the previous chunk's (LDS counters, bounded
+// waits).  K_restore^T, beta and a_last, read late, have two copies by
+// chunk parity.  The prep waves meet once per step, before the off-
+// diagonal tile pairs (every tile's K_rs and tile totals written).  A
+// wave on the same SIMD as MFMA work loses VALU issue to it, so the work
+// is spread to keep each SIMD's share even rather than to keep MFMA away
+// from the VALU-bound prep.
 //
 // State row order: accumulator row p holds channel kperm(p) (kda_internal.h),
 // so two stacked accumulator tiles packed together are the B operand of the
 // channel-contracting products with channels in natural order.  Token
-// columns of the record's token-contracting operands (M_qk, K_restore^T) are
-// in kperm order to match U packed the same way.
+// columns of the token-contracting operands (M_qk, K_restore^T) are in kperm
+// order to match U packed the same way.  o is computed transposed (the same
+// fragments with the operand roles swapped), so that a lane holds four
+// adjacent output columns of one token and stores them as one 8-byte piece.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -52,8 +66,10 @@ namespace {
 
 constexpr int kF2Threads = 512;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kLdN = 20; // fp32 row stride of the N blocks
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 // acc(16x16) += A(16x16) B(16x16) on v_mfma_f32_16x16x16_bf16: lane (lr, lg)
 // gives A[lr][4 lg .. + 3] and B[4 lg .. + 3][lr], the accumulator layout of B.
@@ -70,54 +86,6 @@ __device__ __forceinline__ bf16x4 pack4(const f32x4 &x) {
   return v;
 }
 
-// One chunk's operands in LDS.  The bf16 MFMA A operands of the state step
-// are stored as fragment blocks: 1 KiB per (16-row tile, 32-wide k-step),
-// lane l's 16 bytes at 16 l, so a fragment read is 64 consecutive 16-byte
-// pieces.  The 16 x 16 operands of the substitution are 512-byte blocks,
-// lane l's 8 bytes at 8 l.
-struct Rec {
-  bf16 qd[16][512];  // Q_decay, block 4 tt + s
-  bf16 kd[16][512];  // K_decay, block 4 tt + s
-  bf16 krt[16][512]; // K_restore^T, block 2 ct + s' (rows: state rows)
-  bf16 mqk[8][512];  // M_qk, block 2 tt + s'
-  bf16 lo[6][256];   // L_IJ, J < I, at off_pair(I, J)
-  bf16 dn[4][256];   // -(I + L_II)^-1
-  float beta[kC];
-  float al[kD];      // a_last by state row
-};
-
-struct PrepScratch {
-  float tot[4][kD];      // tile totals of g (log2 units) per channel
-  float fac[4][5][kD];   // per prep wave: its per-channel factors
-  bf16 krs[4][4][512];   // K_rs of token tiles 0..3 (tile 3's is not read), fragment blocks per k-step
-  int ctr;               // the prep waves' meeting counter
-};
-
-struct F2Smem {
-  Rec rec[2];
-  PrepScratch ps;
-};
-static_assert(sizeof(F2Smem) <= 160 * 1024, "fused prefill LDS");
-
-__device__ __forceinline__ int off_pair(int I, int J) { return I * (I - 1) / 2 + J; }
-
-// The four prep waves meet: each publishes its LDS writes and waits until
-// all four have arrived `target / 4` times.  Only LDS is ordered (global
-// loads stay in flight).  The wait is bounded so that every wave exits
-// even if a meeting were never completed.
-__device__ __forceinline__ void prep_meet(int *ctr, int target) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  if ((threadIdx.x & 63) == 0)
-    __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  for (int it = 0; it < (1 << 18); ++it) {
-    const int v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    if (__builtin_amdgcn_readfirstlane(v) >= target)
-      break;
-    __builtin_amdgcn_s_sleep(1);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // A B in the column layout for 16 x 16 fp32 blocks (a: A in the row layout,
 // b: B in the column layout, as mm16_rr), with the four K = 4 steps in two
 // independent accumulators so that the chain of dependent MFMAs is half as
@@ -129,6 +97,93 @@ __device__ __forceinline__ f32x4 mm16_split(const f32x4 c, const f32x4 a, const 
   x = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], x, 0, 0, 0);
   y = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], y, 0, 0, 0);
   return x + y;
+}
+
+// One chunk's operands in LDS.  The bf16 MFMA A operands of the state step
+// are stored as fragment blocks: 1 KiB per (16-row tile, 32-wide k-step),
+// lane l's 16 bytes at 16 l, so a fragment read is 64 consecutive 16-byte
+// pieces.  The 16 x 16 operands of the substitution are 512-byte blocks,
+// lane l's 8 bytes at 8 l.
+struct RecOnce {     // one copy (read early in a step)
+  bf16 qd[16][512];  // Q_decay, block 4 tt + s
+  bf16 kd[16][512];  // K_decay, block 4 tt + s
+  bf16 mqk[8][512];  // M_qk, block 2 tt + s'
+  bf16 lo[6][256];   // L_IJ, J < I, at off_pair(I, J)
+  bf16 dn[4][256];   // -(I + L_II)^-1
+};
+struct RecTwice {    // two copies by chunk parity (read late in a step)
+  bf16 krt[16][512]; // K_restore^T, block 2 ct + s' (rows: state rows)
+  float beta[kC];
+  float al[kD];      // a_last by state row
+};
+
+struct PrepScratch {
+  float tot[4][kD];        // tile totals of g (log2 units) per channel
+  float fac[4][5][kD];     // per prep wave: its per-channel factors
+  bf16 krs[3][4][512];     // K_rs of token tiles 0..2, fragment blocks per k-step
+  bf16 bsc[3][4][512];     // B_20, B_30, B_31 (K_rs,J scaled to tile I's reference point)
+  bf16 t3k[4][512];        // K_loc of token tile 3, fragment blocks per k-step
+  bf16 t3q[4][512];        // Q_loc of token tile 3
+  float nmat[4][16][kLdN]; // N of each token tile, fp32, row-major
+};
+
+struct F2Smem {
+  RecOnce a;
+  RecTwice b[2];
+  PrepScratch ps;
+  bf16 vst[4][kC * 32]; // each state wave's 64 x 32 slice of v (vst_off)
+  int meet;             // prep waves' arrivals at their meetings
+  int q_done;           // state waves done reading Q_decay, K_decay
+  int m_done;           // state waves done reading M_qk, L, D^-1
+  int n_ready;          // prep waves' N blocks written
+};
+static_assert(sizeof(F2Smem) <= 160 * 1024, "fused prefill LDS");
+
+__device__ __forceinline__ int off_pair(int I, int J) { return I * (I - 1) / 2 + J; }
+
+// LDS synchronisation, written out: the compiler's own fences and barriers
+// would also wait for the LDS DMA of the next chunk's v that each state wave
+// keeps in flight (tracked by vmcnt), and with it for the whole load.  Only
+// LDS is ordered here; LDS operations of a wave complete in order.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// Finish this wave's LDS reads and writes, then count one arrival on ctr.
+__device__ __forceinline__ void lds_signal(int *ctr) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if ((threadIdx.x & 63) == 0)
+    asm volatile("ds_add_u32 %0, %1" ::"v"(lds_addr(ctr)), "v"(1) : "memory");
+}
+
+// Wait until ctr reaches target.  The wait is bounded so that every wave
+// exits even if a count were never reached.
+__device__ __forceinline__ void lds_wait(const int *ctr, int target) {
+  const uint32_t a = lds_addr(ctr);
+  for (int it = 0; it < (1 << 18); ++it) {
+    int v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+    if (__builtin_amdgcn_readfirstlane(v) >= target)
+      break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Workgroup barrier after this wave's LDS operations have completed.
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Byte offset of v[row][col] (row < 64 tokens, col < 32 of a state wave's
+// columns) in its LDS copy.  The copy is 64-byte slots, one row each, whose
+// four 16-byte pieces are permuted: row 16 t + 4 a + b sits in slot
+// 16 t + 4 b + a, and its piece p at position p ^ (a & 2).  The reads of the
+// substitution's right-hand side (the 16 columns of a tile, rows 4 a + b for
+// the four lane groups a) then fall in 32 different banks.
+__device__ __forceinline__ int vst_off(int row, int col) {
+  const int a = (row >> 2) & 3;
+  const int slot = (row & ~15) | ((row & 3) << 2) | a;
+  return slot * 64 + 16 * ((col >> 3) ^ (a & 2)) + 2 * (col & 7);
 }
 
 } // namespace
@@ -149,16 +204,17 @@ __global__ __launch_bounds__(kF2Threads) void fused2_kernel(
   const int nch = (cd.ntok + kC - 1) / kC;
 
   // M_qk blocks (and halves) above the diagonal are zero and never written
-  // again; the meeting counter starts at 0
+  // again; the counters start at 0
   {
-    uint32_t *z = reinterpret_cast<uint32_t *>(&sm.rec[0].mqk[0][0]);
-    uint32_t *z1 = reinterpret_cast<uint32_t *>(&sm.rec[1].mqk[0][0]);
-    for (int e = tid; e < 8 * 512 / 2; e += kF2Threads) {
+    uint32_t *z = reinterpret_cast<uint32_t *>(&sm.a.mqk[0][0]);
+    for (int e = tid; e < 8 * 512 / 2; e += kF2Threads)
       z[e] = 0u;
-      z1[e] = 0u;
+    if (tid == 0) {
+      sm.meet = 0;
+      sm.q_done = 0;
+      sm.m_done = 0;
+      sm.n_ready = 0;
     }
-    if (tid == 0)
-      sm.ps.ctr = 0;
   }
   __syncthreads();
 
@@ -178,25 +234,24 @@ __global__ __launch_bounds__(kF2Threads) void fused2_kernel(
           for (int i = 0; i < 4; ++i)
             S[c][ct][i] = ip ? ip[kperm(16 * ct + 4 * lg + i) * kD + col0 + 16 * c + lr] : 0.f;
     }
-    // v of one chunk: rows 16 tt + 4 lg + i, columns col0 + 16 c + lr (rows
-    // past the chunk end read 0)
-    unsigned short vr[2][4][4];
+    uint8_t *vs = reinterpret_cast<uint8_t *>(&sm.vst[wv][0]);
+    // this wave's columns of v for chunk ch, straight into its LDS copy:
+    // instruction j, lane l fills slot 16 j + l / 4, position l % 4 (vst_off
+    // inverted); rows past the chunk end read 0
     auto load_v = [&](int ch) {
-      const int ln = opaque_lane(), llr = ln & 15, llg = ln >> 4;
+      const int ln = opaque_lane();
       const bool in = ch < nch;
       const int len = in ? min(kC, cd.ntok - ch * kC) : 0;
-      const bf16 *vb = v + (cd.tok0 + (int64_t)(in ? ch : 0) * kC) * rowstride + (int64_t)h * kD;
+      const bf16 *vb =
+          v + (cd.tok0 + (int64_t)(in ? ch : 0) * kC) * rowstride + (int64_t)h * kD + col0;
       const __amdgpu_buffer_rsrc_t rv =
-          buffer_rsrc(vb, in ? (uint32_t)(((len - 1) * rowstride + kD) * 2) : 0u);
+          buffer_rsrc(vb, in ? (uint32_t)(((len - 1) * rowstride + 32) * 2) : 0u);
+      const int piece = (ln & 3) ^ ((ln >> 2) & 2);
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int c = 0; c < 2; ++c)
-            vr[c][tt][i] = __builtin_amdgcn_raw_buffer_load_b16(
-                rv, (int)(((16 * tt + 4 * llg + i) * rowstride + col0 + 16 * c + llr) * 2), 0,
-                0);
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * j + 4 * ((ln >> 2) & 3) + (ln >> 4);
+        lds_load16(rv, (int)((row * rowstride + 8 * piece) * 2), vs + 1024 * j);
+      }
     };
     load_v(0);
     int ck_next = cd.ckpt_chunk, ck_idx = cd.ckpt_idx;
@@ -204,116 +259,122 @@ __global__ __launch_bounds__(kF2Threads) void fused2_kernel(
     for (int step = 0; step <= nch; ++step) {
       if (step > 0) {
         const int ch = step - 1;
-        const Rec &R = sm.rec[ch & 1];
+        const RecOnce &A = sm.a;
+        const RecTwice &B = sm.b[ch & 1];
         const int ln = opaque_lane(), llr = ln & 15, llg = ln >> 4;
         auto frag = [&](const bf16 *blk) { return load_frag(blk + ln * 8); };
-        // W = K_decay S and O = Q_decay S (K = channels, B operand = S)
+        // W = K_decay S and O^T = S^T Q_decay^T (K = channels; the packed
+        // state is the B operand of the first and the A operand of the second)
         Frag<bf16> bs[2][4];
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int s = 0; s < 4; ++s)
             bs[c][s] = pack_acc2(S[c][2 * s], S[c][2 * s + 1]);
-        f32x4 W[2][4], Oa[2][4];
+        f32x4 W[2][4], Ot[2][4];
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) {
             W[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            Oa[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            Ot[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           Frag<bf16> ak[4], aq[4];
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) {
-            ak[tt] = frag(&R.kd[4 * tt + s][0]);
-            aq[tt] = frag(&R.qd[4 * tt + s][0]);
+            ak[tt] = frag(&A.kd[4 * tt + s][0]);
+            aq[tt] = frag(&A.qd[4 * tt + s][0]);
           }
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
               mma(W[c][tt], ak[tt], bs[c][s]);
-              mma(Oa[c][tt], aq[tt], bs[c][s]);
+              mma(Ot[c][tt], bs[c][s], aq[tt]);
             }
         }
-        // Diag(beta) (W - V), the right-hand side of the substitution
+        lds_signal(&sm.q_done);
+        // Diag(beta) (W - V), the right-hand side of the substitution; then
+        // the next chunk's v into the copy just read
+        wait_vmem_all(); // this chunk's v is in LDS
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-          const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&R.beta[16 * tt + 4 * llg]);
+          const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&B.beta[16 * tt + 4 * llg]);
 #pragma unroll
           for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              W[c][tt][i] =
-                  b4[i] * (W[c][tt][i] - __builtin_bit_cast(float, (unsigned)vr[c][tt][i] << 16));
+            for (int i = 0; i < 4; ++i) {
+              const float vv = static_cast<float>(*reinterpret_cast<const bf16 *>(
+                  vs + vst_off(16 * tt + 4 * llg + i, 16 * c + llr)));
+              W[c][tt][i] = b4[i] * (W[c][tt][i] - vv);
+            }
         }
+        wave_lds_fence();
         load_v(ch + 1);
         // U_I = -D_I^-1 (Diag(beta_I)(W_I - V_I) + sum_{J<I} L_IJ U_J), tile by tile
         bf16x4 ub[2][4];
-        f32x4 U[2][4];
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-          const bf16x4 dn = *reinterpret_cast<const bf16x4 *>(&R.dn[I][ln * 4]);
+          const bf16x4 dn = *reinterpret_cast<const bf16x4 *>(&A.dn[I][ln * 4]);
           bf16x4 lo[3];
 #pragma unroll
           for (int J = 0; J < I; ++J)
-            lo[J] = *reinterpret_cast<const bf16x4 *>(&R.lo[off_pair(I, J)][ln * 4]);
+            lo[J] = *reinterpret_cast<const bf16x4 *>(&A.lo[off_pair(I, J)][ln * 4]);
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             f32x4 a = W[c][I];
 #pragma unroll
             for (int J = 0; J < I; ++J)
               a = mma16(a, lo[J], ub[c][J]);
-            U[c][I] = mma16(zero, dn, pack4(a));
-            ub[c][I] = pack4(U[c][I]);
+            ub[c][I] = pack4(mma16(zero, dn, pack4(a)));
           }
         }
-        // O += M_qk U (K = tokens, kperm order: two stacked U tiles)
+        // O^T += U^T M_qk^T (K = tokens, kperm order: two stacked U tiles)
         Frag<bf16> bu[2][2];
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
+          for (int s = 0; s < 2; ++s)
             bu[c][s].v = __builtin_shufflevector(ub[c][2 * s], ub[c][2 * s + 1], 0, 1, 2, 3, 4,
                                                  5, 6, 7);
-          }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           Frag<bf16> am[4];
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt)
-            am[tt] = frag(&R.mqk[2 * tt + s][0]);
+            am[tt] = frag(&A.mqk[2 * tt + s][0]);
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
             for (int c = 0; c < 2; ++c)
-              mma(Oa[c][tt], am[tt], bu[c][s]);
+              mma(Ot[c][tt], bu[c][s], am[tt]);
         }
+        lds_signal(&sm.m_done);
         {
-          // o, rows past the chunk end dropped by the buffer range
+          // o: lane (lr, lg) holds columns col0 + 16 c + 4 lg .. + 3 of token
+          // 16 tt + lr; rows past the chunk end are dropped by the buffer range
           const int len = min(kC, cd.ntok - ch * kC);
           const int64_t tok = cd.tok0 + (int64_t)ch * kC;
           const __amdgpu_buffer_rsrc_t ro =
               buffer_rsrc(o + tok * rowstride + (int64_t)h * kD,
                           (uint32_t)(((len - 1) * rowstride + kD) * 2));
-          const int vo = (int)((4 * llg * rowstride + col0 + llr) * 2);
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int so = (int)((16 * tt + i) * rowstride * 2); // wave-uniform
-#pragma unroll
-              for (int c = 0; c < 2; ++c)
-                buffer_store(ro, static_cast<bf16>(Oa[c][tt][i]), vo + 32 * c, so);
+            for (int c = 0; c < 2; ++c) {
+              const int off =
+                  (int)(((16 * tt + llr) * rowstride + col0 + 16 * c + 4 * llg) * 2);
+              __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pack4(Ot[c][tt])),
+                                                    ro, off, 0, 0);
             }
         }
         // S = Diag(a_last) S + K_restore^T U
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
-          const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&R.al[16 * ct + 4 * llg]);
+          const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&B.al[16 * ct + 4 * llg]);
 #pragma unroll
           for (int c = 0; c < 2; ++c)
             S[c][ct] *= a4;
@@ -325,7 +386,7 @@ __global__ __launch_bounds__(kF2Threads) void fused2_kernel(
             Frag<bf16> ar[4];
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
-              ar[ct] = frag(&R.krt[2 * (4 * hf + ct) + s][0]);
+              ar[ct] = frag(&B.krt[2 * (4 * hf + ct) + s][0]);
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
@@ -348,7 +409,39 @@ __global__ __launch_bounds__(kF2Threads) void fused2_kernel(
           }
         }
       }
-      __syncthreads();
+      if (step < nch) {
+        // -D_w^-1 of the chunk being prepared, in the row layout: the column
+        // layout of (I + N^T)^-1 = (I - M)(I + M^2)(I + M^4)(I + M^8) with
+        // M = N^T (M_col = N_row, M_row = N_col; mm16_split(c, a_row, b_col)
+        // = c + A B in the column layout)
+        const int ln = opaque_lane(), llr = ln & 15, llg = ln >> 4;
+        lds_wait(&sm.n_ready, 4 * (step + 1));
+        const float *N = &sm.ps.nmat[wv][0][0];
+        f32x4 Nc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          Nc[i] = N[(4 * llg + i) * kLdN + llr]; // row 4 lg + i, column lr
+        const f32x4 Nr = *reinterpret_cast<const f32x4 *>(&N[llr * kLdN + 4 * llg]);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 M2c = mm16_split(z, Nc, Nr); // M M
+        const f32x4 M2r = mm16_split(z, Nr, Nc); // (M^2)^T = N N
+        const f32x4 M4c = mm16_split(z, M2r, M2c);
+        const f32x4 M4r = mm16_split(z, M2c, M2r);
+        f32x4 eye;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          eye[i] = (4 * llg + i == llr) ? 1.f : 0.f;
+        f32x4 Y = mm16_split(eye, M4r, M4c); // I + M^8
+        Y = mm16_split(Y, M4r, Y);           // (I + M^4) Y
+        Y = mm16_split(Y, M2r, Y);           // (I + M^2) Y
+        Y = mm16_split(Y, -Nc, Y);           // (I - M) Y
+        // -D_w^-1 as the substitution's A operand (lane (lr, lg): row lr,
+        // columns 4 lg .. + 3), once every state wave is done with the
+        // previous chunk's
+        lds_wait(&sm.m_done, 4 * step);
+        *reinterpret_cast<bf16x4 *>(&sm.a.dn[wv][ln * 4]) = pack4(-Y);
+      }
+      lds_sync();
     }
     if (cd.final_idx >= 0) {
       float *fp = final_state + ((int64_t)cd.final_idx * H + h) * (kD * kD) + col0 + lr;
@@ -362,9 +455,12 @@ __global__ __launch_bounds__(kF2Threads) void fused2_kernel(
     }
   } else {
     // ============================ prep waves ============================
+    // Wave 4 + I, step k: chunk k's decayed operands and tile products, and
+    // the tile scan and per-channel factors of chunk k + 1 (so that no
+    // exchange of tile totals sits between the start of a step and its
+    // elementwise work).
     const int I = wv - 4; // token tile
     u32x4 rg[4], rq[4], rk[4];
-    unsigned short rb = 0;
     // inputs of chunk ch (an empty range past the last chunk: every load
     // reads 0, and every step issues the same loads)
     auto rsrc_of = [&](const bf16 *base, int ch) {
@@ -374,10 +470,9 @@ __global__ __launch_bounds__(kF2Threads) void fused2_kernel(
       return buffer_rsrc(base + tok * rowstride + (int64_t)h * kD,
                          in ? (uint32_t)(((len - 1) * rowstride + kD) * 2) : 0u);
     };
-    // g and beta are used by the tile scan, q and k later: each group is
-    // loaded right after its previous values are consumed, g and beta first,
-    // so that waiting for them never waits for the q / k loads behind them
-    auto issue_gb = [&](int ch) {
+    // g feeds the tile scan, q and k the elementwise work: each group is
+    // loaded right after its previous values are consumed
+    auto issue_g = [&](int ch) {
       const int ln = opaque_lane(), llr = ln & 15, llg = ln >> 4;
       const __amdgpu_buffer_rsrc_t r = rsrc_of(g, ch);
 #pragma unroll
@@ -385,12 +480,23 @@ __global__ __launch_bounds__(kF2Threads) void fused2_kernel(
         rg[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                               r, (int)(((16 * I + llr) * rowstride + 32 * s +
                                                         8 * llg) * 2), 0, 0));
+    };
+    // beta of token 16 I + lr of chunk ch, raw bf16 (loaded and stored within
+    // one step: a load whose register lives across the step boundary would be
+    // waited for there)
+    auto load_beta = [&](int ch) -> unsigned short {
+      const int ln = opaque_lane(), llr = ln & 15;
       const bool in = ch < nch;
       const int len = in ? min(kC, cd.ntok - ch * kC) : 0;
       const int64_t tok = cd.tok0 + (int64_t)(in ? ch : 0) * kC;
       const __amdgpu_buffer_rsrc_t rbb = buffer_rsrc(
           beta + tok * H + h, in ? (uint32_t)(((len - 1) * (int64_t)H + 1) * 2) : 0u);
-      rb = __builtin_amdgcn_raw_buffer_load_b16(rbb, (int)((16 * I + llr) * H * 2), 0, 0);
+      return __builtin_amdgcn_raw_buffer_load_b16(rbb, (int)((16 * I + llr) * H * 2), 0, 0);
+    };
+    auto store_beta = [&](int ch, unsigned short raw) {
+      const int ln = opaque_lane();
+      if ((ln >> 4) == 0)
+        sm.b[ch & 1].beta[16 * I + (ln & 15)] = __builtin_bit_cast(float, (unsigned)raw << 16);
     };
     auto issue_qk = [&](int ch) {
       const int ln = opaque_lane(), llr = ln & 15, llg = ln >> 4;
@@ -402,9 +508,64 @@ __global__ __launch_bounds__(kF2Threads) void fused2_kernel(
         rq[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r2, vo, 0, 0));
       }
     };
-    issue_gb(0);
-    issue_qk(0);
-    int meet = 0;
+    // tile scan of the loaded g (log2 units, inclusive over the 16 tokens of
+    // the tile, level by level over all 32 values so that no DPP step waits
+    // on the one just issued); lane 15 of each row writes the tile totals
+    float G[4][8];
+    auto scan = [&]() {
+      const int ln = opaque_lane(), llr = ln & 15, llg = ln >> 4;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        widen8(rg[s], G[s]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          G[s][j] *= kLog2e;
+      }
+#pragma unroll
+      for (int d = 1; d < 16; d *= 2)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            G[s][j] += dpp_shr(G[s][j], d);
+      if (llr == 15) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          *reinterpret_cast<f32x4 *>(&sm.ps.tot[I][32 * s + 8 * llg]) =
+              f32x4{G[s][0], G[s][1], G[s][2], G[s][3]};
+          *reinterpret_cast<f32x4 *>(&sm.ps.tot[I][32 * s + 8 * llg + 4]) =
+              f32x4{G[s][4], G[s][5], G[s][6], G[s][7]};
+        }
+      }
+    };
+    // this wave's factor rows from the four tile totals (two channels per
+    // lane): 0 e^{p_I}, 1 e^{tot_I}, 2 e^{G_C - p_{I+1}}, and the scales of
+    // the non-adjacent pair operands it writes (tile 0: 3 e^{tot_1} for
+    // B_20, 4 e^{tot_1 + tot_2} for B_30; tile 1: 3 e^{tot_2} for B_31);
+    // tile 0 also keeps a_last of its two channels
+    float alr[2] = {1.f, 1.f};
+    auto factors = [&]() {
+      const int c0 = 2 * opaque_lane();
+      PrepScratch &P = sm.ps;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int c = c0 + e;
+        const float t0 = P.tot[0][c], t1 = P.tot[1][c], t2 = P.tot[2][c], t3 = P.tot[3][c];
+        const float pI = I == 0 ? 0.f : (I == 1 ? t0 : (I == 2 ? t0 + t1 : t0 + t1 + t2));
+        const float tI = I == 0 ? t0 : (I == 1 ? t1 : (I == 2 ? t2 : t3));
+        const float gC = t0 + t1 + t2 + t3;
+        P.fac[I][0][c] = __builtin_amdgcn_exp2f(pI);           // e^{p_I} <= 1
+        P.fac[I][1][c] = __builtin_amdgcn_exp2f(tI);           // e^{tot_I} in [e^-80, 1]
+        P.fac[I][2][c] = __builtin_amdgcn_exp2f(gC - pI - tI); // e^{G_C - p_{I+1}} <= 1
+        if (I == 0) {
+          P.fac[0][3][c] = __builtin_amdgcn_exp2f(t1);
+          P.fac[0][4][c] = __builtin_amdgcn_exp2f(t1 + t2);
+          alr[e] = __builtin_amdgcn_exp2f(gC);
+        }
+        if (I == 1)
+          P.fac[1][3][c] = __builtin_amdgcn_exp2f(t2);
+      }
+    };
     // selection matrices for K_restore^T: B operand h picks channels
     // 16 h .. 16 h + 15 of a 32-channel k-step (lane (n, lg), element j: 1
     // where 8 lg + j == 16 h + n; bf16 1.0 = 0x3f80)
@@ -420,117 +581,134 @@ __global__ __launch_bounds__(kF2Threads) void fused2_kernel(
       f.v = __builtin_bit_cast(bf16x8, w);
       return f;
     };
+    // the off-diagonal pair (Ip, J): L_IJ = Diag(beta_I) K_loc,I B_IJ^T and
+    // M_IJ = Q_loc,I B_IJ^T from the B_IJ fragment blocks and tile Ip's
+    // K_loc / Q_loc fragments (lane (lr, lg): row 16 Ip + lr, token
+    // 16 J + 4 lg + i)
+    auto pair = [&](int Ip, int J, const bf16 *bsrc, const Frag<bf16> (&ak)[4],
+                    const Frag<bf16> (&aq)[4], float brow) {
+      const int ln = opaque_lane();
+      f32x4 accL = {0.f, 0.f, 0.f, 0.f}, accM = accL;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const Frag<bf16> b = load_frag(bsrc + s * 512 + ln * 8);
+        mma(accL, b, ak[s]);
+        mma(accM, b, aq[s]);
+      }
+      *reinterpret_cast<bf16x4 *>(&sm.a.lo[off_pair(Ip, J)][ln * 4]) = pack4(accL * brow);
+      *reinterpret_cast<bf16x4 *>(&sm.a.mqk[2 * Ip + (J >> 1)][ln * 8 + 4 * (J & 1)]) =
+          pack4(accM);
+    };
+
+    // chunk 0's beta, tile scan and factors
+    issue_g(0);
+    issue_qk(0);
+    store_beta(0, load_beta(0));
+    int meet = 0;
+    scan();
+    issue_g(1);
+    meet += 4;
+    lds_signal(&sm.meet);
+    lds_wait(&sm.meet, meet);
+    factors();
 
     for (int step = 0; step <= nch; ++step) {
       if (step < nch) {
-        Rec &R = sm.rec[step & 1];
+        RecOnce &A = sm.a;
+        RecTwice &B = sm.b[step & 1];
         PrepScratch &P = sm.ps;
         const int lane = opaque_lane(), lr = lane & 15, lg = lane >> 4;
-        // ---- phase 1: tile scan of g (log2 units), tile totals, beta ----
-        // (level by level over all 32 values, so that no DPP step waits on
-        // the one just issued)
-        float G[4][8];
+        const unsigned short rb_next = load_beta(step + 1);
+        if (I == 0) {
+          B.al[kperm_inv(2 * lane)] = alr[0];
+          B.al[kperm_inv(2 * lane + 1)] = alr[1];
+        }
+        // ---- elementwise: Q_loc, K_loc, K_st (tile products), Q_decay,
+        // K_decay (record, written once the state waves are done with the
+        // previous chunk's), K_rs and the scaled pair operands, K_restore
+        // (transposed into the record); the diagonal tile's products ----
+        Frag<bf16> fq[4], fk[4], fs[4], fre[4];
+        bf16x8 pq[4], pk[4];
+        f32x4 accLc = {0.f, 0.f, 0.f, 0.f}, accMr = accLc;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          widen8(rg[s], G[s]);
+          float el[8], es[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            G[s][j] *= kLog2e;
-        }
+          for (int j = 0; j < 8; ++j) {
+            el[j] = __builtin_amdgcn_exp2f(G[s][j]);
+            es[j] = __builtin_amdgcn_exp2f(-G[s][j]);
+          }
+          float fp[8], ft[8], fr[8], qv[8], kv[8];
+          load8f(&P.fac[I][0][32 * s + 8 * lg], fp);
+          load8f(&P.fac[I][1][32 * s + 8 * lg], ft);
+          load8f(&P.fac[I][2][32 * s + 8 * lg], fr);
+          widen8(rq[s], qv);
+          widen8(rk[s], kv);
+          float xq[8], xk[8], xs[8], yq[8], yk[8], yr[8], yre[8];
 #pragma unroll
-        for (int d = 1; d < 16; d *= 2)
+          for (int j = 0; j < 8; ++j) {
+            xq[j] = qv[j] * el[j];  // Q_loc
+            xk[j] = kv[j] * el[j];  // K_loc
+            xs[j] = kv[j] * es[j];  // K_st
+            yq[j] = xq[j] * fp[j];  // Q_decay
+            yk[j] = xk[j] * fp[j];  // K_decay
+            yr[j] = xs[j] * ft[j];  // K_rs
+            yre[j] = yr[j] * fr[j]; // K_restore
+          }
+          fq[s] = pack8(xq);
+          fk[s] = pack8(xk);
+          fs[s] = pack8(xs);
+          fre[s] = pack8(yre);
+          pq[s] = pack8(yq).v;
+          pk[s] = pack8(yk).v;
+          // diagonal tile: L_II in the column layout; M_II swapped, in the
+          // row layout (row r = lr)
+          mma(accLc, fk[s], fs[s]);
+          mma(accMr, fs[s], fq[s]);
+          if (I < 3)
+            *reinterpret_cast<bf16x8 *>(&P.krs[I][s][lane * 8]) = pack8(yr).v;
+          if (I == 0) {
+            float f3[8], f4[8], b3[8], b4[8];
+            load8f(&P.fac[0][3][32 * s + 8 * lg], f3);
+            load8f(&P.fac[0][4][32 * s + 8 * lg], f4);
 #pragma unroll
-          for (int s = 0; s < 4; ++s)
+            for (int j = 0; j < 8; ++j) {
+              b3[j] = yr[j] * f3[j];
+              b4[j] = yr[j] * f4[j];
+            }
+            *reinterpret_cast<bf16x8 *>(&P.bsc[0][s][lane * 8]) = pack8(b3).v; // B_20
+            *reinterpret_cast<bf16x8 *>(&P.bsc[1][s][lane * 8]) = pack8(b4).v; // B_30
+          } else if (I == 1) {
+            float f3[8], b3[8];
+            load8f(&P.fac[1][3][32 * s + 8 * lg], f3);
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-              G[s][j] += dpp_shr(G[s][j], d);
-        const float bt = __builtin_bit_cast(float, (unsigned)rb << 16); // beta of token 16 I + lr
-        issue_gb(step + 1);
-        if (lr == 15) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            *reinterpret_cast<f32x4 *>(&P.tot[I][32 * s + 8 * lg]) =
-                f32x4{G[s][0], G[s][1], G[s][2], G[s][3]};
-            *reinterpret_cast<f32x4 *>(&P.tot[I][32 * s + 8 * lg + 4]) =
-                f32x4{G[s][4], G[s][5], G[s][6], G[s][7]};
+              b3[j] = yr[j] * f3[j];
+            *reinterpret_cast<bf16x8 *>(&P.bsc[2][s][lane * 8]) = pack8(b3).v; // B_31
+          } else if (I == 3) {
+            // tile 3's K_loc and Q_loc for the pair (3, 0), which tile 0's wave computes
+            *reinterpret_cast<bf16x8 *>(&P.t3k[s][lane * 8]) = fk[s].v;
+            *reinterpret_cast<bf16x8 *>(&P.t3q[s][lane * 8]) = fq[s].v;
           }
         }
-        if (lg == 0)
-          R.beta[16 * I + lr] = bt;
-        meet += 4;
-        prep_meet(&P.ctr, meet);
-
-        // ---- phase 2: per-channel factors, decayed operands, diagonal tile ----
+        // N = strictly lower part of Diag(beta) L_II (lane (lr, lg): row
+        // 4 lg + i, column lr), for the state wave that inverts I + N
         {
-          // two channels per lane; each prep wave has its own factor table
-          const int c0 = 2 * lane;
+          const f32x4 bcol = *reinterpret_cast<const f32x4 *>(&B.beta[16 * I + 4 * lg]);
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int c = c0 + e;
-            const float t0 = P.tot[0][c], t1 = P.tot[1][c], t2 = P.tot[2][c], t3 = P.tot[3][c];
-            const float pI = I == 0 ? 0.f : (I == 1 ? t0 : (I == 2 ? t0 + t1 : t0 + t1 + t2));
-            const float tI = I == 0 ? t0 : (I == 1 ? t1 : (I == 2 ? t2 : t3));
-            const float gC = t0 + t1 + t2 + t3;
-            P.fac[I][0][c] = __builtin_amdgcn_exp2f(pI);            // e^{p_I} <= 1
-            P.fac[I][1][c] = __builtin_amdgcn_exp2f(tI);            // e^{tot_I} in [e^-80, 1]
-            P.fac[I][2][c] = __builtin_amdgcn_exp2f(gC - pI - tI);  // e^{G_C - p_{I+1}} <= 1
-            if (I == 2)
-              P.fac[2][3][c] = __builtin_amdgcn_exp2f(t1);          // pair (2, 0)
-            if (I == 3) {
-              P.fac[3][3][c] = __builtin_amdgcn_exp2f(t2);          // pair (3, 1)
-              P.fac[3][4][c] = __builtin_amdgcn_exp2f(t1 + t2);     // pair (3, 0)
-            }
-            if (I == 0)
-              R.al[kperm_inv(c)] = __builtin_amdgcn_exp2f(gC);      // a_last
-          }
+          for (int i = 0; i < 4; ++i)
+            P.nmat[I][4 * lg + i][lr] = (4 * lg + i > lr) ? bcol[i] * accLc[i] : 0.f;
         }
-        wave_lds_fence();
-        Frag<bf16> fq[4], fk[4], fs[4], fre[4];
-        f32x4 accLc = {0.f, 0.f, 0.f, 0.f}, accLr = accLc, accMr = accLc;
+        lds_signal(&sm.n_ready);
+        // (every state wave is done reading the previous chunk's Q_decay, K_decay)
+        lds_wait(&sm.q_done, 4 * step);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          *reinterpret_cast<bf16x8 *>(&A.qd[4 * I + s][lane * 8]) = pq[s];
+          *reinterpret_cast<bf16x8 *>(&A.kd[4 * I + s][lane * 8]) = pk[s];
+        }
+        issue_qk(step + 1);
         {
-          // elementwise: Q_loc, K_loc, K_st (tile products), Q_decay, K_decay
-          // (record), K_rs (exchange), K_restore (transposed into the record)
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            float el[8], es[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              el[j] = __builtin_amdgcn_exp2f(G[s][j]);
-              es[j] = __builtin_amdgcn_exp2f(-G[s][j]);
-            }
-            float fp[8], ft[8], fr[8], qv[8], kv[8];
-            load8f(&P.fac[I][0][32 * s + 8 * lg], fp);
-            load8f(&P.fac[I][1][32 * s + 8 * lg], ft);
-            load8f(&P.fac[I][2][32 * s + 8 * lg], fr);
-            widen8(rq[s], qv);
-            widen8(rk[s], kv);
-            float xq[8], xk[8], xs[8], yq[8], yk[8], yr[8], yre[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              xq[j] = qv[j] * el[j];  // Q_loc
-              xk[j] = kv[j] * el[j];  // K_loc
-              xs[j] = kv[j] * es[j];  // K_st
-              yq[j] = xq[j] * fp[j];  // Q_decay
-              yk[j] = xk[j] * fp[j];  // K_decay
-              yr[j] = xs[j] * ft[j];  // K_rs
-              yre[j] = yr[j] * fr[j]; // K_restore
-            }
-            fq[s] = pack8(xq);
-            fk[s] = pack8(xk);
-            fs[s] = pack8(xs);
-            fre[s] = pack8(yre);
-            *reinterpret_cast<bf16x8 *>(&R.qd[4 * I + s][lane * 8]) = pack8(yq).v;
-            *reinterpret_cast<bf16x8 *>(&R.kd[4 * I + s][lane * 8]) = pack8(yk).v;
-            *reinterpret_cast<bf16x8 *>(&P.krs[I][s][lane * 8]) = pack8(yr).v;
-          }
-          // diagonal tile: L_II in the column layout and, swapped, in the row
-          // layout; M_II swapped (row r = lr)
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            mma(accLc, fk[s], fs[s]);
-            mma(accLr, fs[s], fk[s]);
-            mma(accMr, fs[s], fq[s]);
-          }
           // K_restore^T: the selection products give lane (n, lg) channel
           // 32 s + 16 hs + n of tokens 16 I + 4 lg .. + 3, which go to state
           // row p = kperm_inv(channel), k-step I / 2, positions 4 (I % 2) ..
@@ -549,83 +727,56 @@ __global__ __launch_bounds__(kF2Threads) void fused2_kernel(
             for (int hs = 0; hs < 2; ++hs) {
               const int p = kperm_inv(32 * s + 16 * hs + lr);
               *reinterpret_cast<bf16x4 *>(
-                  &R.krt[2 * (p >> 4) + (I >> 1)][((lg << 4) + (p & 15)) * 8 + 4 * (I & 1)]) =
+                  &B.krt[2 * (p >> 4) + (I >> 1)][((lg << 4) + (p & 15)) * 8 + 4 * (I & 1)]) =
                   pack4(tr[s][hs]);
             }
         }
-        issue_qk(step + 1);
-        // N = strictly lower part of Diag(beta) L_II, both layouts
-        f32x4 Nc, Nr;
+        // next chunk's tile scan (its g was loaded a step ago)
+        scan();
+        issue_g(step + 2);
+        // (every state wave is done reading the previous chunk's M_qk, L and,
+        // from the other copy, beta)
+        lds_wait(&sm.m_done, 4 * step);
+        store_beta(step + 1, rb_next);
         {
-          const f32x4 bcol = *reinterpret_cast<const f32x4 *>(&R.beta[16 * I + 4 * lg]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            Nc[i] = (4 * lg + i > lr) ? bcol[i] * accLc[i] : 0.f; // row 4 lg + i, col lr
-            Nr[i] = (lr > 4 * lg + i) ? bt * accLr[i] : 0.f;      // row lr, col 4 lg + i
-          }
-        }
-        // D_I^-1 in the row layout: the column layout of (I + N^T)^-1 =
-        // (I - M)(I + M^2)(I + M^4)(I + M^8) with M = N^T (M_col = N_row,
-        // M_row = N_col; mm16_rr(acc, a_row, b_col) += A B in the column layout)
-        {
-          const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-          const f32x4 M2c = mm16_split(z, Nc, Nr);   // M M
-          const f32x4 M2r = mm16_split(z, Nr, Nc);   // (M^2)^T = N N
-          const f32x4 M4c = mm16_split(z, M2r, M2c);
-          const f32x4 M4r = mm16_split(z, M2c, M2r);
-          f32x4 eye;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            eye[i] = (4 * lg + i == lr) ? 1.f : 0.f;
-          f32x4 Y = mm16_split(eye, M4r, M4c);       // I + M^8
-          Y = mm16_split(Y, M4r, Y);                 // (I + M^4) Y
-          Y = mm16_split(Y, M2r, Y);                 // (I + M^2) Y
-          Y = mm16_split(Y, -Nc, Y);                 // (I - M) Y
-          // -D_I^-1 as the substitution's A operand: lane (lr, lg) row lr,
-          // columns 4 lg .. + 3
-          *reinterpret_cast<bf16x4 *>(&R.dn[I][lane * 4]) = pack4(-Y);
-        }
-        // M_II with its diagonal: rows 16 I + lr, tokens 16 I + 4 lg + i
-        {
+          // M_II with its diagonal: rows 16 I + lr, tokens 16 I + 4 lg + i
           f32x4 m = accMr;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             m[i] = (4 * lg + i <= lr) ? m[i] : 0.f;
-          *reinterpret_cast<bf16x4 *>(
-              &R.mqk[2 * I + (I >> 1)][lane * 8 + 4 * (I & 1)]) = pack4(m);
+          *reinterpret_cast<bf16x4 *>(&A.mqk[2 * I + (I >> 1)][lane * 8 + 4 * (I & 1)]) =
+              pack4(m);
         }
         meet += 4;
-        prep_meet(&P.ctr, meet);
+        lds_signal(&sm.meet);
+        lds_wait(&sm.meet, meet);
 
-        // ---- phase 3: off-diagonal tile pairs (I, J), J < I ----
-#pragma unroll
-        for (int J = 0; J < 3; ++J) {
-          if (J >= I)
-            break;
-          f32x4 accL = {0.f, 0.f, 0.f, 0.f}, accM = accL;
-          // B_IJ = K_rs,J e^{p_I - p_{J+1}}: the factor is 1 for J = I - 1
-          const int fidx = (I == 2 && J == 0) ? 3 : ((I == 3 && J == 1) ? 3 : 4);
+        // ---- off-diagonal tile pairs (B_IJ: K_rs,J itself for J = I - 1,
+        // else its scaled copy), two per wave at most ----
+        if (I == 0) {
+          Frag<bf16> t3k[4], t3q[4];
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            Frag<bf16> b = load_frag(&P.krs[J][s][lane * 8]);
-            if (J + 1 < I) {
-              float x[8], f[8];
-              frag_to_f32(b, x);
-              load8f(&P.fac[I][fidx][32 * s + 8 * lg], f);
-#pragma unroll
-              for (int j = 0; j < 8; ++j)
-                x[j] *= f[j];
-              b = pack8(x);
-            }
-            mma(accL, b, fk[s]); // lane (lr, lg): row r = 16 I + lr, token 16 J + 4 lg + i
-            mma(accM, b, fq[s]);
+            t3k[s] = load_frag(&P.t3k[s][lane * 8]);
+            t3q[s] = load_frag(&P.t3q[s][lane * 8]);
           }
-          *reinterpret_cast<bf16x4 *>(&R.lo[off_pair(I, J)][lane * 4]) = pack4(accL * bt);
-          *reinterpret_cast<bf16x4 *>(
-              &R.mqk[2 * I + (J >> 1)][lane * 8 + 4 * (J & 1)]) = pack4(accM);
+          pair(3, 0, &P.bsc[1][0][0], t3k, t3q, B.beta[48 + lr]);
+        } else {
+          const float brow = B.beta[16 * I + lr];
+          if (I == 1) {
+            pair(1, 0, &P.krs[0][0][0], fk, fq, brow);
+          } else if (I == 2) {
+            pair(2, 0, &P.bsc[0][0][0], fk, fq, brow);
+            pair(2, 1, &P.krs[1][0][0], fk, fq, brow);
+          } else {
+            pair(3, 1, &P.bsc[2][0][0], fk, fq, brow);
+            pair(3, 2, &P.krs[2][0][0], fk, fq, brow);
+          }
         }
+        // next chunk's factors (every tile total is in after the meeting)
+        factors();
       }
-      __syncthreads();
+      lds_sync();
     }
   }
 }
