@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libkda.so")
 SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_prep.hip", "kda_fused.hip",
-           "kda_fused2.hip", "kda_scratch.hip"]
+           "kda_scratch.hip"]
 ARCH = "gfx950"
 
 

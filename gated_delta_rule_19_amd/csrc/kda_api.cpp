@@ -459,16 +459,10 @@ kda_status prefill_impl(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_
   const ChunkDesc *d_chunks = (const ChunkDesc *)(ws + p.off_chunks);
   hipError_t e = upload_tables(p, ws, s);
   if (p.fused) {
-    if (e == hipSuccess) {
-      if (!pro.on() && !epi.on())
-        e = launch_fused2((const ChainDesc *)(ws + p.off_chains), (int32_t)p.chains.size(), H,
-                          q, k, v, g, beta, o, initial_state, final_state,
-                          ckpt_align ? ckpt : nullptr, s);
-      else
-        e = launch_fused((const ChainDesc *)(ws + p.off_chains), (int32_t)p.chains.size(), H,
-                         q, k, v, g, beta, o, initial_state, nullptr, final_state,
-                         ckpt_align ? ckpt : nullptr, pro, epi, s);
-    }
+    if (e == hipSuccess)
+      e = launch_fused((const ChainDesc *)(ws + p.off_chains), (int32_t)p.chains.size(), H, q,
+                        k, v, g, beta, o, initial_state, final_state,
+                        ckpt_align ? ckpt : nullptr, s, pro, epi);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
   }
   if (e == hipSuccess)
@@ -720,7 +714,7 @@ kda_status kda_chunk_prefill_noalloc(int32_t num_seqs, const int64_t *cu_seqlens
     e = hipMemcpyAsync(scr, host, p.table_bytes, hipMemcpyHostToDevice, s);
   }
   if (e == hipSuccess)
-    e = launch_fused2((const ChainDesc *)((uint8_t *)scr + p.off_chains),
+    e = launch_fused((const ChainDesc *)((uint8_t *)scr + p.off_chains),
                       (int32_t)p.chains.size(), H, q, k, v, g, beta, o, initial_state,
                       final_state, nullptr, s);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;

@@ -1,53 +1,62 @@
 // KDA chunked prefill with chunk prep and state carry fused in one kernel
-// (bf16 inputs, fp32 state and accumulation).
+// (bf16 inputs, fp32 state and accumulation): one workgroup per (sequence,
+// head) carries all 128 state columns, and each chunk's operands are built
+// in LDS by the same workgroup while it carries the state through the
+// previous chunk.  Only the layer's own inputs and outputs touch HBM.
 //
-// The mathematics is the two-kernel path's (kda_prefill.hip): the FlashKDA
-// chunk form of "Kimi K3 的架構" (hao.cnyes.com) §六, with the 16-token
-// reference points that the decay's lower bound allows ("Kimi K3.1 Pro
-// 架构完全拆解" §3.2).  What changes is where the chunk-prep results live:
-// here they never leave the compute unit, so the only HBM traffic is the
-// layer's own inputs and outputs (q, k, v, g, beta in; o and states out).
+// The mathematics is the FlashKDA chunk form of "Kimi K3 的架構"
+// (hao.cnyes.com) §六, with the 16-token reference points that the decay's
+// lower bound allows ("Kimi K3.1 Pro 架构完全拆解" §3.2).  With G the
+// inclusive cumulative log-decay from the chunk start, p_I = G before token
+// tile I, G_loc = G - p_I, tot_I = the tile's total and G_C the chunk total:
+//   Q_loc = q e^{G_loc},  K_loc = k e^{G_loc},  K_st = k e^{-G_loc}   (<= e^80 |k|)
+//   K_rs  = K_st e^{tot_I} = k e^{p_{I+1} - G}                        (<= |k|)
+//   Q_decay = Q_loc e^{p_I},  K_decay = K_loc e^{p_I},  K_restore = K_rs e^{G_C - p_{I+1}}
+//   L_IJ = Diag(beta) K_loc,I B_IJ^T,  M_IJ = Q_loc,I B_IJ^T   (J <= I)
+//   with B_II = K_st,I and, for J < I, B_IJ = K_rs,J e^{p_I - p_{J+1}} = k_t e^{p_I - G_t}
+// (every factor and partial product is at most 1 in size except K_st's, so
+// a result underflows only where the exact value is negligible).
 //
-// One workgroup of 8 waves owns one (chain, head, column block of 64 NCT
-// state columns).  The waves have two roles that run side by side, two waves
-// per SIMD:
-//   waves 0-3, state: wave w carries columns 16 NCT w .. 16 NCT w + 16 NCT - 1
-//     of the column block through the chunks, S in MFMA accumulators:
-//       W = K_decay S,  O = Q_decay S,  U = INV Diag(beta) (V - W),
-//       O += M_qk U,  S = Diag(a_last) S + K_restore^T U;
-//   waves 4-7, prep: wave p owns token tile p (16 tokens) of chunk c and
-//     builds its part of that chunk's record: cumulative log-decay, decayed
-//     q / k, K_restore, L and M_qk on MFMA, INV = (I + L)^-1.
-// A chunk step is four stages separated by workgroup barriers.  Every record
-// region is rewritten by the prep only in a stage after the one in which the
-// state waves read it, so one record buffer serves both roles:
-//   stage | state waves                            | prep waves (chunk c)
-//   A     | -                                      | tile scan, Q_loc/K_loc/K_start, diagonal L, M_qk tiles
-//   B     | U, O += M_qk U, store o, S update      | factors, K_decay/Q_decay -> record, off-diagonal tiles
-//         |   (chunk c - 1)                        |
-//   C     | -                                      | L, M_qk, K_restore^T, a_last -> record; diagonal INV blocks
-//   D     | W = K_decay S, O = Q_decay S (chunk c) | off-diagonal blocks of INV -> record
+// The state step per chunk is the pages' U = INV Diag(beta)(V - K_decay S),
+// O = Q_decay S + M_qk U, S = Diag(a_last) S + K_restore^T U, with INV =
+// (I + L)^-1 applied by block forward substitution over the four 16-token
+// tiles (any exact method gives the same unique result):
+//   U_I = D_I^-1 (Diag(beta_I)(V_I - W_I) - sum_{J<I} L_IJ U_J),  D_I = I + L_II,
+// where D_I^-1 comes from the Neumann product (I - N)(I + N^2)(I + N^4)(I + N^8)
+// of the strictly lower N = L_II (N^16 = 0).
 //
-// Prep lane layout: prep wave p, lane (lr, lg) = (lane % 16, lane / 16) holds
-// token 16 p + lr and, for k-step s = 0..3, channels 32 s + 8 lg .. + 7: one
-// 16-byte load per input and k-step, the MFMA A-fragment layout of the L /
-// M_qk products, and one 16-byte row piece of Q_decay / K_decay.  The tile's
-// cumulative sum of g runs across the 16 lanes of a DPP row.
+// Workgroup of 8 waves, two per SIMD:
+//   waves 0-3, state: wave w carries state columns 32 w .. 32 w + 31 (two
+//     16-column MFMA tiles) through the chunks, S in MFMA accumulators.
+//     After its chunk step it also inverts D_w of the chunk being prepared:
+//     a chain of dependent MFMAs that would otherwise sit on the prep waves'
+//     path, which is the longer one;
+//   waves 4-7, prep: wave 4 + I owns token tile I of the chunk being
+//     prepared.  Lane (lr, lg) = (lane % 16, lane / 16) holds token 16 I + lr
+//     and, for k-step s, channels 32 s + 8 lg .. + 7: one 16-byte load per
+//     input and k-step, and the MFMA A-fragment layout.
+// Step k: the prep waves build chunk k's operands while the state waves
+// consume chunk k - 1's; one workgroup barrier ends each step.  The prep
+// waves also scan chunk k + 1's decay and turn the tile totals into their
+// per-channel factors within step k, so chunk k + 1's elementwise work
+// starts as soon as step k + 1 does.  Q_decay, K_decay, M_qk and the L and
+// D^-1 blocks, which the state waves read early in a step, have one LDS
+// copy: the prep waves overwrite them only after every state wave has
+// counted itself done with the previous chunk's (LDS counters, bounded
+// waits).  K_restore^T, beta and a_last, read late, have two copies by
+// chunk parity.  The prep waves meet once per step, before the off-
+// diagonal tile pairs (every tile's K_rs and tile totals written).  A
+// wave on the same SIMD as MFMA work loses VALU issue to it, so the work
+// is spread to keep each SIMD's share even rather than to keep MFMA away
+// from the VALU-bound prep.
 //
-// State row order: the state waves keep channel kperm(p) in accumulator row
-// p (p = 16 ct + 4 lg + i).  Packing two stacked accumulator tiles then gives
-// exactly channels 32 s + 8 lg .. + 7 in lane (., lg), the B operand of the
-// K = channels products, so the state feeds W and O without moving data
-// between lanes.  K_restore^T and a_last are stored in the same row order.
-//
-// Numerics, with G the inclusive cumulative log-decay from the chunk start,
-// p_I = G before token tile I, G_loc = G - p_I and G_C the chunk total:
-//   Q_loc = q e^{G_loc},  K_loc = k e^{G_loc}            (<= |q|, |k|)
-//   K_st  = k e^{-G_loc}                                 (<= e^80 |k|)
-//   L_IJ  = K_loc,I (K_st,J e^{p_I - p_J})^T  for J < I;  K_loc,I K_st,I^T on the diagonal
-//   Q_decay = q e^{G_loc + p_I},  K_decay = k e^{G_loc + p_I},  K_restore = k e^{G_C - p_I - G_loc}
-// Every exponent is <= 0 except K_st's (< 80); a factor that underflows does
-// so only where the exact product is below e^-20 of its neighbours.
+// State row order: accumulator row p holds channel kperm(p) (kda_internal.h),
+// so two stacked accumulator tiles packed together are the B operand of the
+// channel-contracting products with channels in natural order.  Token
+// columns of the token-contracting operands (M_qk, K_restore^T) are in kperm
+// order to match U packed the same way.  o is computed transposed (the same
+// fragments with the operand roles swapped), so that a lane holds four
+// adjacent output columns of one token and stores them as one 8-byte piece.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -55,507 +64,655 @@ namespace kda {
 
 namespace {
 
-constexpr int kFWaves = 8;
-constexpr int kFThreads = 64 * kFWaves;
-constexpr int kLdD = kD + 8; // bf16 rows of 128 (272 B: 16 rows of a fragment read hit distinct banks)
-constexpr int kLdC = kC + 8; // bf16 rows of 64 (144 B)
-constexpr int kLdL = kC + 4; // fp32 rows of 64
-constexpr int kLdB = 20;     // fp32 16 x 16 blocks
+constexpr int kFusedThreads = 512;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kLdN = 20; // fp32 row stride of the N blocks
 
-// The 6 off-diagonal tile pairs (I, J), I > J, and the prep wave that
-// computes each (two waves take two pairs, two take one).  A pair's A
-// operand (K_loc / Q_loc rows of tile I) is in registers when the wave owns
-// tile I, else it comes from the copy tile 3 leaves in LDS.
-//   wave 0: (3,0)   wave 1: (1,0) (3,1)   wave 2: (2,0) (2,1)   wave 3: (3,2)
-__host__ __device__ constexpr int pair_count(int w) { return (w == 1 || w == 2) ? 2 : 1; }
-__host__ __device__ constexpr int pair_I(int w, int n) {
-  return w == 0 ? 3 : (w == 1 ? (n == 0 ? 1 : 3) : (w == 2 ? 2 : 3));
-}
-__host__ __device__ constexpr int pair_J(int w, int n) {
-  return w == 0 ? 0 : (w == 1 ? (n == 0 ? 0 : 1) : (w == 2 ? (n == 0 ? 0 : 1) : 2));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// acc(16x16) += A(16x16) B(16x16) on v_mfma_f32_16x16x16_bf16: lane (lr, lg)
+// gives A[lr][4 lg .. + 3] and B[4 lg .. + 3][lr], the accumulator layout of B.
+__device__ __forceinline__ f32x4 mma16(f32x4 acc, bf16x4 a, bf16x4 b) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), acc, 0, 0, 0);
 }
 
-template <int NCT> struct FusedSmem {
-  // the chunk record (state waves read it, prep waves rewrite it)
-  bf16 Qd[kC][kLdD];   // Q_decay, rows = tokens, columns = channels
-  bf16 Kd[kC][kLdD];   // K_decay
-  bf16 KrT[kD][kLdC];  // K_restore^T, row p = channel kperm(p), columns kperm(token)
-  bf16 INVb[kC][kLdC]; // INV Diag(beta), columns kperm(token)
-  bf16 Mqk[kC][kLdC];  // M_qk, columns kperm(token)
-  float aL[kD];        // a_last, entry p = channel kperm(p)
-  // v of each state wave's columns: 64 rows x 16 NCT columns
-  bf16 sv[4][kC * 16 * NCT];
-  // prep scratch
-  float Tot[4][kD]; // per-tile totals of g
-  union {
-    struct {
-      bf16 Kst[4][16][kLdD]; // K_start per tile (stage A -> B)
-      bf16 Aq3[2][16][kLdD]; // K_loc, Q_loc of tile 3 (stage A -> B)
-    } ab;
-    float Pow[4][2][16][kLdB]; // per prep wave: N^2, N^4 of its diagonal block (stage C)
-  } x;
-  float L[kC][kLdL];       // L = StrictTril(Diag(beta) K_decay K_inv^T), fp32
-  float Dinv[4][16][kLdB]; // inverted diagonal blocks of I + L
-  float Beta[kC];
-  float Iq[kC], Ik[kC];    // prologue: 1 / |q|, 1 / |k| per token (stage A -> B)
-  float Red[4][kC];        // output norm: per state wave, partial sums of o^2 per token
-  float Scl[4][kC];        // output norm: each state wave's copy of the row scales
-  float Fac[4][2][kD];     // per tile, log2 units: p_I, G_C - p_I
-  float Foff[6][kD];       // e^{p_I - p_J} for the off-diagonal pairs
+__device__ __forceinline__ bf16x4 pack4(const f32x4 &x) {
+  bf16x4 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    v[i] = static_cast<bf16>(x[i]);
+  return v;
+}
+
+// A B in the column layout for 16 x 16 fp32 blocks (a: A in the row layout,
+// b: B in the column layout, as mm16_rr), with the four K = 4 steps in two
+// independent accumulators so that the chain of dependent MFMAs is half as
+// long; c is added.
+__device__ __forceinline__ f32x4 mm16_split(const f32x4 c, const f32x4 a, const f32x4 b) {
+  f32x4 x = c, y = {0.f, 0.f, 0.f, 0.f};
+  x = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], x, 0, 0, 0);
+  y = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], y, 0, 0, 0);
+  x = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], x, 0, 0, 0);
+  y = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], y, 0, 0, 0);
+  return x + y;
+}
+
+// One chunk's operands in LDS.  The bf16 MFMA A operands of the state step
+// are stored as fragment blocks: 1 KiB per (16-row tile, 32-wide k-step),
+// lane l's 16 bytes at 16 l, so a fragment read is 64 consecutive 16-byte
+// pieces.  The 16 x 16 operands of the substitution are 512-byte blocks,
+// lane l's 8 bytes at 8 l.
+struct RecOnce {     // one copy (read early in a step)
+  bf16 qd[16][512];  // Q_decay, block 4 tt + s
+  bf16 kd[16][512];  // K_decay, block 4 tt + s
+  bf16 mqk[8][512];  // M_qk, block 2 tt + s'
+  bf16 lo[6][256];   // L_IJ, J < I, at off_pair(I, J)
+  bf16 dn[4][256];   // -(I + L_II)^-1
+};
+struct RecTwice {    // two copies by chunk parity (read late in a step)
+  bf16 krt[16][512]; // K_restore^T, block 2 ct + s' (rows: state rows)
+  float beta[kC];
+  float al[kD];      // a_last by state row
 };
 
-// index of the tile pair (I, J), I > J, among the 6 off-diagonal pairs
+struct PrepScratch {
+  float tot[4][kD];        // tile totals of g (log2 units) per channel
+  float fac[4][5][kD];     // per prep wave: its per-channel factors
+  bf16 krs[3][4][512];     // K_rs of token tiles 0..2, fragment blocks per k-step
+  bf16 bsc[3][4][512];     // B_20, B_30, B_31 (K_rs,J scaled to tile I's reference point)
+  bf16 t3k[4][512];        // K_loc of token tile 3, fragment blocks per k-step
+  bf16 t3q[4][512];        // Q_loc of token tile 3
+  float nmat[4][16][kLdN]; // N of each token tile, fp32, row-major
+};
+
+struct FusedSmem {
+  RecOnce a;
+  RecTwice b[2];
+  PrepScratch ps;
+  bf16 vst[4][kC * 32]; // each state wave's 64 x 32 slice of v (vst_off)
+  float ored[4][kC];    // output norm: each state wave's sums of o^2 per token
+  int meet;             // prep waves' arrivals at their meetings
+  int q_done;           // state waves done reading Q_decay, K_decay
+  int m_done;           // state waves done reading M_qk, L, D^-1
+  int n_ready;          // prep waves' N blocks written
+  int o_red;            // state waves' output-norm sums written
+};
+static_assert(sizeof(FusedSmem) <= 160 * 1024, "fused prefill LDS");
+
 __device__ __forceinline__ int off_pair(int I, int J) { return I * (I - 1) / 2 + J; }
 
+// LDS synchronisation, written out: the compiler's own fences and barriers
+// would also wait for the LDS DMA of the next chunk's v that each state wave
+// keeps in flight (tracked by vmcnt), and with it for the whole load.  Only
+// LDS is ordered here; LDS operations of a wave complete in order.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
 
+// Finish this wave's LDS reads and writes, then count one arrival on ctr.
+__device__ __forceinline__ void lds_signal(int *ctr) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if ((threadIdx.x & 63) == 0)
+    asm volatile("ds_add_u32 %0, %1" ::"v"(lds_addr(ctr)), "v"(1) : "memory");
+}
+
+// Wait until ctr reaches target.  The wait is bounded so that every wave
+// exits even if a count were never reached.
+__device__ __forceinline__ void lds_wait(const int *ctr, int target) {
+  const uint32_t a = lds_addr(ctr);
+  for (int it = 0; it < (1 << 18); ++it) {
+    int v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+    if (__builtin_amdgcn_readfirstlane(v) >= target)
+      break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Workgroup barrier after this wave's LDS operations have completed.
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Byte offset of v[row][col] (row < 64 tokens, col < 32 of a state wave's
+// columns) in its LDS copy.  The copy is 64-byte slots, one row each, whose
+// four 16-byte pieces are permuted: row 16 t + 4 a + b sits in slot
+// 16 t + 4 b + a, and its piece p at position p ^ (a & 2).  The reads of the
+// substitution's right-hand side (the 16 columns of a tile, rows 4 a + b for
+// the four lane groups a) then fall in 32 different banks.
+__device__ __forceinline__ int vst_off(int row, int col) {
+  const int a = (row >> 2) & 3;
+  const int slot = (row & ~15) | ((row & 3) << 2) | a;
+  return slot * 64 + 16 * ((col >> 3) ^ (a & 2)) + 2 * (col & 7);
+}
 
 } // namespace
 
-// PRO: the prologue (gate logits -> log decay, q / k L2 norm) is compiled in;
-// which of its steps run is decided by A_log != null and qk_eps > 0.
-// EPI: o leaves through the output norm and gate.
-template <int NCT, bool PRO, bool EPI>
-__global__ __launch_bounds__(kFThreads) void fused_kernel(
+// PRO: the decay gate from logits and the q / k L2 norm run in the prep
+// (which of them is decided by A_log != null and qk_eps > 0); EPI: o leaves
+// through the output norm and gate.
+template <bool PRO, bool EPI>
+__global__ __launch_bounds__(kFusedThreads) void fused_kernel(
     const ChainDesc *__restrict__ chains, int32_t H, const bf16 *__restrict__ q,
     const bf16 *__restrict__ k, const bf16 *__restrict__ v, const bf16 *__restrict__ g,
     const bf16 *__restrict__ beta, bf16 *__restrict__ o, const float *__restrict__ init,
-    const float *__restrict__ sin, float *__restrict__ final_state, float *__restrict__ ckpt,
-    const float *__restrict__ A_log, float g_min, float qk_eps, const bf16 *__restrict__ ogate,
-    const float *__restrict__ onw, float oeps) {
-  using Sm = FusedSmem<NCT>;
-  __shared__ __attribute__((aligned(16))) Sm sm;
-  constexpr int VW = 16 * NCT; // state columns per state wave
+    float *__restrict__ final_state, float *__restrict__ ckpt, const float *__restrict__ A_log,
+    float g_min, float qk_eps, const bf16 *__restrict__ ogate, const float *__restrict__ onw,
+    float oeps) {
+  __shared__ __attribute__((aligned(1024))) FusedSmem sm;
 
-  const ChainDesc cd = chains[blockIdx.x];
-  const int h = blockIdx.y;
-  const int col0 = blockIdx.z * (4 * VW);
+  const int chain_i = blockIdx.x / H, h = blockIdx.x - chain_i * H;
+  const ChainDesc cd = chains[chain_i];
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t rowstride = (int64_t)H * kD;
   const int nch = (cd.ntok + kC - 1) / kC;
 
-  // The upper 16 x 16 tiles of M_qk and INV Diag(beta) are zero and are
-  // never written again.
-  for (int e = tid; e < 6 * 256; e += kFThreads) {
-    const int t = e >> 8, r = (e >> 4) & 15, c = e & 15;
-    const int bi = t < 3 ? 0 : (t < 5 ? 1 : 2);
-    const int bj = t < 3 ? t + 1 : (t < 5 ? t - 1 : 3);
-    sm.INVb[16 * bi + r][kperm(16 * bj + c)] = static_cast<bf16>(0.f);
-    sm.Mqk[16 * bi + r][kperm(16 * bj + c)] = static_cast<bf16>(0.f);
+  // M_qk blocks (and halves) above the diagonal are zero and never written
+  // again; the counters start at 0
+  {
+    uint32_t *z = reinterpret_cast<uint32_t *>(&sm.a.mqk[0][0]);
+    for (int e = tid; e < 8 * 512 / 2; e += kFusedThreads)
+      z[e] = 0u;
+    if (tid == 0) {
+      sm.meet = 0;
+      sm.q_done = 0;
+      sm.m_done = 0;
+      sm.n_ready = 0;
+      sm.o_red = 0;
+    }
   }
-  lds_barrier();
+  __syncthreads();
 
   if (wv < 4) {
     // =========================== state waves ===========================
     const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-    const int wcol = col0 + VW * wv + lr; // this lane's column in tile c: wcol + 16 c
-    f32x4 S[NCT][8];                      // rows p = 16 ct + 4 lg + i: channel kperm(p)
+    const int col0 = 32 * wv; // columns col0 + 16 c + lr, c = 0, 1
+    f32x4 S[2][8];            // rows p = 16 ct + 4 lg + i: channel kperm(p)
     {
-      const float *ip = nullptr;
-      if (cd.init_idx >= 0)
-        ip = init + ((int64_t)cd.init_idx * H + h) * (kD * kD);
-      else if (cd.init_idx <= -2)
-        ip = sin + ((int64_t)(-2 - cd.init_idx) * H + h) * (kD * kD);
+      const float *ip = cd.init_idx >= 0 ? init + ((int64_t)cd.init_idx * H + h) * (kD * kD)
+                                         : nullptr;
 #pragma unroll
-      for (int c = 0; c < NCT; ++c)
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            S[c][ct][i] = ip ? ip[kperm(16 * ct + 4 * lg + i) * kD + wcol + 16 * c] : 0.f;
+            S[c][ct][i] = ip ? ip[kperm(16 * ct + 4 * lg + i) * kD + col0 + 16 * c + lr] : 0.f;
     }
-    uint8_t *svw = reinterpret_cast<uint8_t *>(&sm.sv[wv][0]);
-    // rows 0..63 of this wave's VW columns of one chunk into its LDS slice:
-    // lane l of instruction j moves 16 bytes (8 columns) of row
-    // (64 j + l) / (2 NCT); rows past the chunk end read as 0
-    auto v_to_lds = [&](int chunk) {
-      const int clen = min(kC, cd.ntok - chunk * kC);
+    uint8_t *vs = reinterpret_cast<uint8_t *>(&sm.vst[wv][0]);
+    // this wave's columns of v for chunk ch, straight into its LDS copy:
+    // instruction j, lane l fills slot 16 j + l / 4, position l % 4 (vst_off
+    // inverted); rows past the chunk end read 0
+    auto load_v = [&](int ch) {
+      const int ln = opaque_lane();
+      const bool in = ch < nch;
+      const int len = in ? min(kC, cd.ntok - ch * kC) : 0;
       const bf16 *vb =
-          v + (cd.tok0 + (int64_t)chunk * kC) * rowstride + (int64_t)h * kD + col0 + VW * wv;
+          v + (cd.tok0 + (int64_t)(in ? ch : 0) * kC) * rowstride + (int64_t)h * kD + col0;
       const __amdgpu_buffer_rsrc_t rv =
-          buffer_rsrc(vb, (uint32_t)(((clen - 1) * rowstride + VW) * sizeof(bf16)));
+          buffer_rsrc(vb, in ? (uint32_t)(((len - 1) * rowstride + 32) * 2) : 0u);
+      const int piece = (ln & 3) ^ ((ln >> 2) & 2);
 #pragma unroll
-      for (int j = 0; j < 2 * NCT; ++j) {
-        const int u = 64 * j + lane, r = u / (2 * NCT), qq = u % (2 * NCT);
-        lds_load16(rv, (int)((r * rowstride + 8 * qq) * sizeof(bf16)), svw + 1024 * j);
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * j + 4 * ((ln >> 2) & 3) + (ln >> 4);
+        lds_load16(rv, (int)((row * rowstride + 8 * piece) * 2), vs + 1024 * j);
       }
     };
-    f32x4 W[NCT][4], Oa[NCT][4]; // of the chunk whose record is current
+    load_v(0);
+    int ck_next = cd.ckpt_chunk, ck_idx = cd.ckpt_idx;
 
-    // W = K_decay S and O = Q_decay S (K = channels)
-    auto stage_wo = [&]() {
-      const int ln = opaque_lane(), lr = ln & 15, lg = ln >> 4;
-      auto frag = [&](const bf16 *base, int ld, int tile, int s) {
-        return load_frag(base + (16 * tile + lr) * ld + 32 * s + 8 * lg);
-      };
-      Frag<bf16> bs[NCT][4];
+    for (int step = 0; step <= nch; ++step) {
+      if (step > 0) {
+        const int ch = step - 1;
+        const RecOnce &A = sm.a;
+        const RecTwice &B = sm.b[ch & 1];
+        const int ln = opaque_lane(), llr = ln & 15, llg = ln >> 4;
+        auto frag = [&](const bf16 *blk) { return load_frag(blk + ln * 8); };
+        // W = K_decay S and O^T = S^T Q_decay^T (K = channels; the packed
+        // state is the B operand of the first and the A operand of the second)
+        Frag<bf16> bs[2][4];
 #pragma unroll
-      for (int c = 0; c < NCT; ++c)
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          bs[c][s] = pack_acc2(S[c][2 * s], S[c][2 * s + 1]);
+          for (int s = 0; s < 4; ++s)
+            bs[c][s] = pack_acc2(S[c][2 * s], S[c][2 * s + 1]);
+        f32x4 W[2][4], Ot[2][4];
 #pragma unroll
-      for (int c = 0; c < NCT; ++c)
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          W[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          Oa[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        Frag<bf16> ak[4], aq[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          ak[tt] = frag(&sm.Kd[0][0], kLdD, tt, s);
-          aq[tt] = frag(&sm.Qd[0][0], kLdD, tt, s);
-        }
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-          for (int c = 0; c < NCT; ++c) {
-            mma(W[c][tt], ak[tt], bs[c][s]);
-            mma(Oa[c][tt], aq[tt], bs[c][s]);
+          for (int tt = 0; tt < 4; ++tt) {
+            W[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            Ot[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
-      }
-    };
-
-    // U = INV Diag(beta) (V - W), O += M_qk U and store o, for chunk ch;
-    // U is left packed in bu for the state update
-    Frag<bf16> bu[NCT][2];
-    // O of chunk ch to o; with the output norm and gate ("Kimi K3.1 Pro 架构完全拆解"
-    // §3.3) once the state waves' partial sums are in LDS:
-    //   o = sigmoid(gate) w o / sqrt(mean(o^2) + eps) per token row
-    auto store_o = [&](int ch) {
-      const int ln = opaque_lane(), lr = ln & 15, lg = ln >> 4;
-      const int wcol = col0 + VW * wv + lr;
-      const int len = min(kC, cd.ntok - ch * kC);
-      const int64_t tok = cd.tok0 + (int64_t)ch * kC;
-      if constexpr (EPI) {
-        float tot = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
-          tot += sm.Red[w][ln];
-        sm.Scl[wv][ln] = __builtin_amdgcn_rsqf(tot * (1.f / kD) + oeps);
-        wave_lds_fence();
-        // one 16-column tile at a time (fewer live registers)
-        const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(
-            ogate + tok * rowstride + (int64_t)h * kD, (uint32_t)((len - 1) * rowstride + kD) * 2);
-        const int go = (int)((4 * lg * rowstride + wcol) * 2);
+        for (int s = 0; s < 4; ++s) {
+          Frag<bf16> ak[4], aq[4];
 #pragma unroll
-        for (int c = 0; c < NCT; ++c) {
-          float gz[4][4];
+          for (int tt = 0; tt < 4; ++tt) {
+            ak[tt] = frag(&A.kd[4 * tt + s][0]);
+            aq[tt] = frag(&A.qd[4 * tt + s][0]);
+          }
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              gz[tt][i] = buffer_load1(rg, go + (int)((16 * tt + i) * rowstride * 2) + 32 * c,
-                                       (const bf16 *)nullptr);
-          const float wn = onw ? onw[wcol + 16 * c] : 1.f;
+            for (int c = 0; c < 2; ++c) {
+              mma(W[c][tt], ak[tt], bs[c][s]);
+              mma(Ot[c][tt], bs[c][s], aq[tt]);
+            }
+        }
+        lds_signal(&sm.q_done);
+        // Diag(beta) (W - V), the right-hand side of the substitution; then
+        // the next chunk's v into the copy just read
+        wait_vmem_all(); // this chunk's v is in LDS
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {
-            const f32x4 sc = *reinterpret_cast<const f32x4 *>(&sm.Scl[wv][16 * tt + 4 * lg]);
+        for (int tt = 0; tt < 4; ++tt) {
+          const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&B.beta[16 * tt + 4 * llg]);
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float sg =
-                  __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-gz[tt][i] * kLog2e));
-              Oa[c][tt][i] *= sc[i] * wn * sg;
+              const float vv = static_cast<float>(*reinterpret_cast<const bf16 *>(
+                  vs + vst_off(16 * tt + 4 * llg + i, 16 * c + llr)));
+              W[c][tt][i] = b4[i] * (W[c][tt][i] - vv);
+            }
+        }
+        wave_lds_fence();
+        load_v(ch + 1);
+        // U_I = -D_I^-1 (Diag(beta_I)(W_I - V_I) + sum_{J<I} L_IJ U_J), tile by tile
+        bf16x4 ub[2][4];
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+          const bf16x4 dn = *reinterpret_cast<const bf16x4 *>(&A.dn[I][ln * 4]);
+          bf16x4 lo[3];
+#pragma unroll
+          for (int J = 0; J < I; ++J)
+            lo[J] = *reinterpret_cast<const bf16x4 *>(&A.lo[off_pair(I, J)][ln * 4]);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            f32x4 a = W[c][I];
+#pragma unroll
+            for (int J = 0; J < I; ++J)
+              a = mma16(a, lo[J], ub[c][J]);
+            ub[c][I] = pack4(mma16(zero, dn, pack4(a)));
+          }
+        }
+        // O^T += U^T M_qk^T (K = tokens, kperm order: two stacked U tiles)
+        Frag<bf16> bu[2][2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            bu[c][s].v = __builtin_shufflevector(ub[c][2 * s], ub[c][2 * s + 1], 0, 1, 2, 3, 4,
+                                                 5, 6, 7);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          Frag<bf16> am[4];
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+            am[tt] = frag(&A.mqk[2 * tt + s][0]);
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+              mma(Ot[c][tt], bu[c][s], am[tt]);
+        }
+        lds_signal(&sm.m_done);
+        {
+          // o: lane (lr, lg) holds columns col0 + 16 c + 4 lg .. + 3 of token
+          // 16 tt + lr; rows past the chunk end are dropped by the buffer range
+          const int len = min(kC, cd.ntok - ch * kC);
+          const int64_t tok = cd.tok0 + (int64_t)ch * kC;
+          const __amdgpu_buffer_rsrc_t ro =
+              buffer_rsrc(o + tok * rowstride + (int64_t)h * kD,
+                          (uint32_t)(((len - 1) * rowstride + kD) * 2));
+          if constexpr (EPI) {
+            // output norm and gate ("Kimi K3.1 Pro 架构完全拆解" §3.3): per
+            // token row, o <- sigmoid(gate) w o / sqrt(mean(o^2) + eps); the
+            // row's sum of squares is this wave's 32 columns (lane groups
+            // combined) plus the other state waves', through LDS
+            const __amdgpu_buffer_rsrc_t rgt =
+                buffer_rsrc(ogate + tok * rowstride + (int64_t)h * kD,
+                            (uint32_t)(((len - 1) * rowstride + kD) * 2));
+            u32x2 gz[2][4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+              for (int c = 0; c < 2; ++c)
+                gz[c][tt] = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                               rgt, (int)(((16 * tt + llr) * rowstride + col0 + 16 * c + 4 * llg) * 2),
+                               0, 0));
+            float ss[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+              float a = 0.f;
+#pragma unroll
+              for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  a += Ot[c][tt][i] * Ot[c][tt][i];
+              a += __shfl_xor(a, 16);
+              a += __shfl_xor(a, 32);
+              ss[tt] = a;
+            }
+            if (llg == 0) {
+#pragma unroll
+              for (int tt = 0; tt < 4; ++tt)
+                sm.ored[wv][16 * tt + llr] = ss[tt];
+            }
+            lds_signal(&sm.o_red);
+            lds_wait(&sm.o_red, 4 * step);
+            f32x4 wn[2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+              wn[c] = onw ? *reinterpret_cast<const f32x4 *>(&onw[col0 + 16 * c + 4 * llg])
+                          : f32x4{1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+              const int t = 16 * tt + llr;
+              const float rs = __builtin_amdgcn_rsqf(
+                  (sm.ored[0][t] + sm.ored[1][t] + sm.ored[2][t] + sm.ored[3][t]) * (1.f / kD) +
+                  oeps);
+#pragma unroll
+              for (int c = 0; c < 2; ++c) {
+                float z[4];
+                z[0] = __builtin_bit_cast(float, gz[c][tt][0] << 16);
+                z[1] = __builtin_bit_cast(float, gz[c][tt][0] & 0xffff0000u);
+                z[2] = __builtin_bit_cast(float, gz[c][tt][1] << 16);
+                z[3] = __builtin_bit_cast(float, gz[c][tt][1] & 0xffff0000u);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  Ot[c][tt][i] *= rs * wn[c][i] *
+                                  __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z[i] * kLog2e));
+              }
             }
           }
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              const int off =
+                  (int)(((16 * tt + llr) * rowstride + col0 + 16 * c + 4 * llg) * 2);
+              __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pack4(Ot[c][tt])),
+                                                    ro, off, 0, 0);
+            }
         }
-      }
-      // rows past the chunk end fall outside the buffer and are dropped
-      const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(
-          o + tok * rowstride + (int64_t)h * kD, (uint32_t)((len - 1) * rowstride + kD) * 2);
-      const int vo = (int)((4 * lg * rowstride + wcol) * 2);
+        // S = Diag(a_last) S + K_restore^T U
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+        for (int ct = 0; ct < 8; ++ct) {
+          const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&B.al[16 * ct + 4 * llg]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int so = (int)((16 * tt + i) * rowstride * 2); // wave-uniform
-#pragma unroll
-          for (int c = 0; c < NCT; ++c)
-            buffer_store(ro, static_cast<bf16>(Oa[c][tt][i]), vo + 32 * c, so);
+          for (int c = 0; c < 2; ++c)
+            S[c][ct] *= a4;
         }
-    };
-
-    auto stage_u = [&](int ch) {
-      const int ln = opaque_lane(), lr = ln & 15, lg = ln >> 4;
-      const int wcol = col0 + VW * wv + lr;
-      auto frag = [&](const bf16 *base, int ld, int tile, int s) {
-        return load_frag(base + (16 * tile + lr) * ld + 32 * s + 8 * lg);
-      };
-      const int len = min(kC, cd.ntok - ch * kC);
-      const int64_t tok = cd.tok0 + (int64_t)ch * kC;
-      wait_vmem_all(); // this chunk's v is in the wave's LDS slice
-      const bf16 *svb = &sm.sv[wv][0];
 #pragma unroll
-      for (int c = 0; c < NCT; ++c)
+        for (int s = 0; s < 2; ++s) {
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+          for (int hf = 0; hf < 2; ++hf) {
+            Frag<bf16> ar[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = 16 * tt + 4 * lg + i;
-            W[c][tt][i] = static_cast<float>(svb[row * VW + 16 * c + lr]) - W[c][tt][i];
-          }
-      if (ch + 1 < nch) {
-        __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0): the slice reads have returned
-        v_to_lds(ch + 1);
-      }
-      Frag<bf16> bw[NCT][2];
+            for (int ct = 0; ct < 4; ++ct)
+              ar[ct] = frag(&B.krt[2 * (4 * hf + ct) + s][0]);
 #pragma unroll
-      for (int c = 0; c < NCT; ++c)
+            for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-          bw[c][s] = pack_acc2(W[c][2 * s], W[c][2 * s + 1]);
-      f32x4 U[NCT][4];
-#pragma unroll
-      for (int c = 0; c < NCT; ++c)
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-          U[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        Frag<bf16> ai[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-          ai[tt] = frag(&sm.INVb[0][0], kLdC, tt, s);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-          for (int c = 0; c < NCT; ++c)
-            mma(U[c][tt], ai[tt], bw[c][s]);
-      }
-#pragma unroll
-      for (int c = 0; c < NCT; ++c)
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-          bu[c][s] = pack_acc2(U[c][2 * s], U[c][2 * s + 1]);
-      // O += M_qk U
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        Frag<bf16> am[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-          am[tt] = frag(&sm.Mqk[0][0], kLdC, tt, s);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-          for (int c = 0; c < NCT; ++c)
-            mma(Oa[c][tt], am[tt], bu[c][s]);
-      }
-      if constexpr (EPI) {
-        // output norm: this wave's sums of o^2 per token, reduce-scattered
-        // over the 16 lanes of a row group (lane lr ends with row tile
-        // lr / 4, row lr % 4), to LDS; o leaves after the next barrier
-        float x[16];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float a = 0.f;
-#pragma unroll
-            for (int c = 0; c < NCT; ++c)
-              a += Oa[c][tt][i] * Oa[c][tt][i];
-            x[4 * tt + i] = a;
-          }
-#pragma unroll
-        for (int st = 8; st >= 1; st >>= 1) {
-          const bool up = (lr & st) != 0;
-#pragma unroll
-          for (int m = 0; m < st; ++m) {
-            const float send = up ? x[m] : x[m + st];
-            const float keep = up ? x[m + st] : x[m];
-            x[m] = keep + __shfl_xor(send, st);
+              for (int c = 0; c < 2; ++c)
+                mma(S[c][4 * hf + ct], ar[ct], bu[c][s]);
           }
         }
-        sm.Red[wv][16 * (lr >> 2) + 4 * lg + (lr & 3)] = x[0];
-      } else {
-        store_o(ch);
-      }
-    };
-
-    // S = Diag(a_last) S + K_restore^T U (K = tokens), for the chunk whose
-    // U was packed into bu by stage_u
-    auto stage_s = [&]() {
-      const int ln = opaque_lane(), lr = ln & 15, lg = ln >> 4;
-      auto frag = [&](const bf16 *base, int ld, int tile, int s) {
-        return load_frag(base + (16 * tile + lr) * ld + 32 * s + 8 * lg);
-      };
+        if (ckpt != nullptr) {
+          if (ch == ck_next && ch <= cd.ckpt_last) {
+            float *cp = ckpt + ((int64_t)ck_idx * H + h) * (kD * kD) + col0 + llr;
+            ck_next += cd.ckpt_every;
+            ++ck_idx;
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&sm.aL[16 * ct + 4 * lg]);
+            for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int c = 0; c < NCT; ++c)
-          S[c][ct] *= a4;
-      }
+              for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          Frag<bf16> ar[4];
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
-            ar[ct] = frag(&sm.KrT[0][0], kLdC, 4 * hf + ct, s);
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-            for (int c = 0; c < NCT; ++c)
-              mma(S[c][4 * hf + ct], ar[ct], bu[c][s]);
+                for (int i = 0; i < 4; ++i)
+                  cp[kperm(16 * ct + 4 * llg + i) * kD + 16 * c] = S[c][ct][i];
+          }
         }
       }
-    };
-
-    // the state after chunk ch, when it is one of the chain's checkpoints
-    // (the next one is chunk ck_next, at index ck_idx)
-    int ck_next = cd.ckpt_chunk, ck_idx = cd.ckpt_idx;
-    auto ckpt_store = [&](int ch) {
-      if (ckpt != nullptr && ch == ck_next && ch <= cd.ckpt_last) {
-        const int ln = opaque_lane(), lr = ln & 15, lg = ln >> 4;
-        const int wcol = col0 + VW * wv + lr;
-        float *cp = ckpt + ((int64_t)ck_idx * H + h) * (kD * kD);
-        ck_next += cd.ckpt_every;
-        ++ck_idx;
+      if (step < nch) {
+        // -D_w^-1 of the chunk being prepared, in the row layout: the column
+        // layout of (I + N^T)^-1 = (I - M)(I + M^2)(I + M^4)(I + M^8) with
+        // M = N^T (M_col = N_row, M_row = N_col; mm16_split(c, a_row, b_col)
+        // = c + A B in the column layout)
+        const int ln = opaque_lane(), llr = ln & 15, llg = ln >> 4;
+        lds_wait(&sm.n_ready, 4 * (step + 1));
+        const float *N = &sm.ps.nmat[wv][0][0];
+        f32x4 Nc;
 #pragma unroll
-        for (int c = 0; c < NCT; ++c)
+        for (int i = 0; i < 4; ++i)
+          Nc[i] = N[(4 * llg + i) * kLdN + llr]; // row 4 lg + i, column lr
+        const f32x4 Nr = *reinterpret_cast<const f32x4 *>(&N[llr * kLdN + 4 * llg]);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 M2c = mm16_split(z, Nc, Nr); // M M
+        const f32x4 M2r = mm16_split(z, Nr, Nc); // (M^2)^T = N N
+        const f32x4 M4c = mm16_split(z, M2r, M2c);
+        const f32x4 M4r = mm16_split(z, M2c, M2r);
+        f32x4 eye;
 #pragma unroll
-          for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              cp[kperm(16 * ct + 4 * lg + i) * kD + wcol + 16 * c] = S[c][ct][i];
+        for (int i = 0; i < 4; ++i)
+          eye[i] = (4 * llg + i == llr) ? 1.f : 0.f;
+        f32x4 Y = mm16_split(eye, M4r, M4c); // I + M^8
+        Y = mm16_split(Y, M4r, Y);           // (I + M^4) Y
+        Y = mm16_split(Y, M2r, Y);           // (I + M^2) Y
+        Y = mm16_split(Y, -Nc, Y);           // (I - M) Y
+        // -D_w^-1 as the substitution's A operand (lane (lr, lg): row lr,
+        // columns 4 lg .. + 3), once every state wave is done with the
+        // previous chunk's
+        lds_wait(&sm.m_done, 4 * step);
+        *reinterpret_cast<bf16x4 *>(&sm.a.dn[wv][ln * 4]) = pack4(-Y);
       }
-    };
-
-    // D_b^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) for N = L_bb (N^16 = 0), b =
-    // this wave's index: the diagonal blocks of INV = (I + L)^-1 of the chunk
-    // being prepared, to LDS (for the prep's off-diagonal blocks) and to the
-    // record as INV Diag(beta)
-    auto stage_inv = [&]() {
-      const int ln = opaque_lane(), lr = ln & 15, lg = ln >> 4;
-      const int b = wv;
-      const float *N = &sm.L[16 * b][16 * b];
-      float *P2 = &sm.x.Pow[b][0][0][0];
-      float *P4 = &sm.x.Pow[b][1][0][0];
-      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-      const f32x4 n1 = acc_load(N, kLdL, lr, lg);
-      f32x4 n2 = zero, n4 = zero, y = zero;
-      mm16_lds_acc(n2, N, kLdL, n1, lr, lg); // N^2
-      acc_store(P2, kLdB, n2, lr, lg);
-      wave_lds_fence();
-      mm16_lds_acc(n4, P2, kLdB, n2, lr, lg); // N^4
-      acc_store(P4, kLdB, n4, lr, lg);
-      wave_lds_fence();
-      mm16_lds_acc(y, P4, kLdB, n4, lr, lg); // N^8
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        y[i] += (4 * lg + i == lr) ? 1.f : 0.f; // I + N^8
-      mm16_lds_acc(y, P4, kLdB, y, lr, lg);      // (I + N^4) Y
-      mm16_lds_acc(y, P2, kLdB, y, lr, lg);      // (I + N^2) Y
-      mm16_lds_acc(y, N, kLdL, y, lr, lg, -1.f); // (I - N) Y
-      acc_store(&sm.Dinv[b][0][0], kLdB, y, lr, lg);
-      const float bcol = sm.Beta[16 * b + lr];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sm.INVb[16 * b + 4 * lg + i][kperm(16 * b + lr)] = static_cast<bf16>(y[i] * bcol);
-    };
-
-    // chunk steps 0 .. nch, four barriers each (the ends of stages A-D):
-    // step it finishes chunk it - 1 in stages A and B, inverts the diagonal
-    // blocks of chunk it in stage C and starts chunk it in stage D
-    if (nch == 0) {
-      for (int b = 0; b < 4; ++b)
-        lds_barrier();
-    } else {
-      v_to_lds(0);
-      lds_barrier();
-      lds_barrier();
-      stage_inv();
-      lds_barrier();
-      stage_wo();
-      lds_barrier();
-      for (int ch = 0; ch + 1 < nch; ++ch) {
-        stage_u(ch);
-        lds_barrier();
-        if constexpr (EPI)
-          store_o(ch);
-        stage_s();
-        ckpt_store(ch);
-        lds_barrier();
-        stage_inv();
-        lds_barrier();
-        stage_wo();
-        lds_barrier();
-      }
-      stage_u(nch - 1);
-      lds_barrier();
-      if constexpr (EPI)
-        store_o(nch - 1);
-      stage_s();
-      ckpt_store(nch - 1);
-      lds_barrier();
-      lds_barrier();
-      lds_barrier();
+      lds_sync();
     }
     if (cd.final_idx >= 0) {
-      float *fp = final_state + ((int64_t)cd.final_idx * H + h) * (kD * kD);
+      float *fp = final_state + ((int64_t)cd.final_idx * H + h) * (kD * kD) + col0 + lr;
 #pragma unroll
-      for (int c = 0; c < NCT; ++c)
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            fp[kperm(16 * ct + 4 * lg + i) * kD + wcol + 16 * c] = S[c][ct][i];
+            fp[kperm(16 * ct + 4 * lg + i) * kD + 16 * c] = S[c][ct][i];
     }
   } else {
     // ============================ prep waves ============================
-    const int pw = wv - 4; // token tile
-    // raw inputs of the chunk being prepared: channels 32 s + 8 lg .. + 7 of
-    // this lane's token, per k-step s
+    // Wave 4 + I, step k: chunk k's decayed operands and tile products, and
+    // the tile scan and per-channel factors of chunk k + 1 (so that no
+    // exchange of tile totals sits between the start of a step and its
+    // elementwise work).
+    const int I = wv - 4; // token tile
     u32x4 rg[4], rq[4], rk[4];
-    // beta stays raw until it is used: widening it where it is loaded would
-    // make the wave wait for every load in flight
-    unsigned short rbeta = 0;
-    auto issue = [&](int chunk) {
-      const int ln = opaque_lane(), lr = ln & 15, lg = ln >> 4, r = 16 * pw + lr;
-      const int len = min(kC, cd.ntok - chunk * kC);
-      const int64_t tok = cd.tok0 + (int64_t)chunk * kC;
-      const int64_t base = tok * rowstride + (int64_t)h * kD;
-      const uint32_t nbytes = (uint32_t)(((len - 1) * rowstride + kD) * 2);
-      const __amdgpu_buffer_rsrc_t bg = buffer_rsrc(g + base, nbytes);
-      const __amdgpu_buffer_rsrc_t bk = buffer_rsrc(k + base, nbytes);
-      const __amdgpu_buffer_rsrc_t bq = buffer_rsrc(q + base, nbytes);
+    // inputs of chunk ch (an empty range past the last chunk: every load
+    // reads 0, and every step issues the same loads)
+    auto rsrc_of = [&](const bf16 *base, int ch) {
+      const bool in = ch < nch;
+      const int len = in ? min(kC, cd.ntok - ch * kC) : 0;
+      const int64_t tok = cd.tok0 + (int64_t)(in ? ch : 0) * kC;
+      return buffer_rsrc(base + tok * rowstride + (int64_t)h * kD,
+                         in ? (uint32_t)(((len - 1) * rowstride + kD) * 2) : 0u);
+    };
+    // g feeds the tile scan, q and k the elementwise work: each group is
+    // loaded right after its previous values are consumed
+    auto issue_g = [&](int ch) {
+      const int ln = opaque_lane(), llr = ln & 15, llg = ln >> 4;
+      const __amdgpu_buffer_rsrc_t r = rsrc_of(g, ch);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        rg[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              r, (int)(((16 * I + llr) * rowstride + 32 * s +
+                                                        8 * llg) * 2), 0, 0));
+    };
+    // beta of token 16 I + lr of chunk ch, raw bf16 (loaded and stored within
+    // one step: a load whose register lives across the step boundary would be
+    // waited for there)
+    auto load_beta = [&](int ch) -> unsigned short {
+      const int ln = opaque_lane(), llr = ln & 15;
+      const bool in = ch < nch;
+      const int len = in ? min(kC, cd.ntok - ch * kC) : 0;
+      const int64_t tok = cd.tok0 + (int64_t)(in ? ch : 0) * kC;
+      const __amdgpu_buffer_rsrc_t rbb = buffer_rsrc(
+          beta + tok * H + h, in ? (uint32_t)(((len - 1) * (int64_t)H + 1) * 2) : 0u);
+      return __builtin_amdgcn_raw_buffer_load_b16(rbb, (int)((16 * I + llr) * H * 2), 0, 0);
+    };
+    auto store_beta = [&](int ch, unsigned short raw) {
+      const int ln = opaque_lane();
+      if ((ln >> 4) == 0)
+        sm.b[ch & 1].beta[16 * I + (ln & 15)] = __builtin_bit_cast(float, (unsigned)raw << 16);
+    };
+    auto issue_qk = [&](int ch) {
+      const int ln = opaque_lane(), llr = ln & 15, llg = ln >> 4;
+      const __amdgpu_buffer_rsrc_t r1 = rsrc_of(k, ch), r2 = rsrc_of(q, ch);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int vo = (int)((r * rowstride + 32 * s + 8 * lg) * 2);
-        rg[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(bg, vo, 0, 0));
-        rk[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(bk, vo, 0, 0));
-        rq[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(bq, vo, 0, 0));
-      }
-      if (lg == 0) {
-        const __amdgpu_buffer_rsrc_t bb =
-            buffer_rsrc(beta + tok * H + h, (uint32_t)(((len - 1) * (int64_t)H + 1) * 2));
-        rbeta = __builtin_amdgcn_raw_buffer_load_b16(bb, (int)(r * H * 2), 0, 0);
+        const int vo = (int)(((16 * I + llr) * rowstride + 32 * s + 8 * llg) * 2);
+        rk[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r1, vo, 0, 0));
+        rq[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r2, vo, 0, 0));
       }
     };
-    if (nch > 0)
-      issue(0);
-    // prologue: the head's gate scale e^{A_h}
+    // tile scan of the loaded g (log2 units, inclusive over the 16 tokens of
+    // the tile, level by level over all 32 values so that no DPP step waits
+    // on the one just issued); lane 15 of each row writes the tile totals
+    float G[4][8];
     const bool gate_on = PRO && A_log != nullptr, qk_on = PRO && qk_eps > 0.f;
-    const float ea = gate_on ? __expf(A_log[h]) : 1.f;
+    const float ea = gate_on ? __expf(A_log[h]) : 1.f; // the head's gate scale e^{A_h}
+    auto scan = [&](int ch) {
+      const int ln = opaque_lane(), llr = ln & 15, llg = ln >> 4;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        widen8(rg[s], G[s]);
+      if (gate_on) {
+        // the log decay from the gate logits; rows past the chunk end decay
+        // by nothing
+        const bool valid = 16 * I + llr < min(kC, cd.ntok - ch * kC);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            G[s][j] = valid ? gate_log_decay(G[s][j], ea, g_min) : 0.f;
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          G[s][j] *= kLog2e;
+#pragma unroll
+      for (int d = 1; d < 16; d *= 2)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            G[s][j] += dpp_shr(G[s][j], d);
+      if (llr == 15) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          *reinterpret_cast<f32x4 *>(&sm.ps.tot[I][32 * s + 8 * llg]) =
+              f32x4{G[s][0], G[s][1], G[s][2], G[s][3]};
+          *reinterpret_cast<f32x4 *>(&sm.ps.tot[I][32 * s + 8 * llg + 4]) =
+              f32x4{G[s][4], G[s][5], G[s][6], G[s][7]};
+        }
+      }
+    };
+    // this wave's factor rows from the four tile totals (two channels per
+    // lane): 0 e^{p_I}, 1 e^{tot_I}, 2 e^{G_C - p_{I+1}}, and the scales of
+    // the non-adjacent pair operands it writes (tile 0: 3 e^{tot_1} for
+    // B_20, 4 e^{tot_1 + tot_2} for B_30; tile 1: 3 e^{tot_2} for B_31);
+    // tile 0 also keeps a_last of its two channels
+    float alr[2] = {1.f, 1.f};
+    auto factors = [&]() {
+      const int c0 = 2 * opaque_lane();
+      PrepScratch &P = sm.ps;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int c = c0 + e;
+        const float t0 = P.tot[0][c], t1 = P.tot[1][c], t2 = P.tot[2][c], t3 = P.tot[3][c];
+        const float pI = I == 0 ? 0.f : (I == 1 ? t0 : (I == 2 ? t0 + t1 : t0 + t1 + t2));
+        const float tI = I == 0 ? t0 : (I == 1 ? t1 : (I == 2 ? t2 : t3));
+        const float gC = t0 + t1 + t2 + t3;
+        P.fac[I][0][c] = __builtin_amdgcn_exp2f(pI);           // e^{p_I} <= 1
+        P.fac[I][1][c] = __builtin_amdgcn_exp2f(tI);           // e^{tot_I} in [e^-80, 1]
+        P.fac[I][2][c] = __builtin_amdgcn_exp2f(gC - pI - tI); // e^{G_C - p_{I+1}} <= 1
+        if (I == 0) {
+          P.fac[0][3][c] = __builtin_amdgcn_exp2f(t1);
+          P.fac[0][4][c] = __builtin_amdgcn_exp2f(t1 + t2);
+          alr[e] = __builtin_amdgcn_exp2f(gC);
+        }
+        if (I == 1)
+          P.fac[1][3][c] = __builtin_amdgcn_exp2f(t2);
+      }
+    };
+    // selection matrices for K_restore^T: B operand h picks channels
+    // 16 h .. 16 h + 15 of a 32-channel k-step (lane (n, lg), element j: 1
+    // where 8 lg + j == 16 h + n; bf16 1.0 = 0x3f80)
+    auto selection = [&](int hsel) {
+      const int ln = opaque_lane(), llr = ln & 15, llg = ln >> 4;
+      const int kk = 16 * hsel + llr - 8 * llg;
+      const unsigned one = 0x3f80u << (16 * (kk & 1));
+      u32x4 w;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        w[d] = (kk >= 0 && kk < 8 && (kk >> 1) == d) ? one : 0u;
+      Frag<bf16> f;
+      f.v = __builtin_bit_cast(bf16x8, w);
+      return f;
+    };
+    // the off-diagonal pair (Ip, J): L_IJ = Diag(beta_I) K_loc,I B_IJ^T and
+    // M_IJ = Q_loc,I B_IJ^T from the B_IJ fragment blocks and tile Ip's
+    // K_loc / Q_loc fragments (lane (lr, lg): row 16 Ip + lr, token
+    // 16 J + 4 lg + i)
+    auto pair = [&](int Ip, int J, const bf16 *bsrc, const Frag<bf16> (&ak)[4],
+                    const Frag<bf16> (&aq)[4], float brow) {
+      const int ln = opaque_lane();
+      f32x4 accL = {0.f, 0.f, 0.f, 0.f}, accM = accL;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const Frag<bf16> b = load_frag(bsrc + s * 512 + ln * 8);
+        mma(accL, b, ak[s]);
+        mma(accM, b, aq[s]);
+      }
+      *reinterpret_cast<bf16x4 *>(&sm.a.lo[off_pair(Ip, J)][ln * 4]) = pack4(accL * brow);
+      *reinterpret_cast<bf16x4 *>(&sm.a.mqk[2 * Ip + (J >> 1)][ln * 8 + 4 * (J & 1)]) =
+          pack4(accM);
+    };
 
-    float xg[4][8];            // G_loc log2(e) per record channel
-    Frag<bf16> fq[4], fk[4];   // Q_loc, K_loc fragments
-    f32x4 accLd, accMd;        // diagonal tile pair (L, M_qk)
-    f32x4 accLp[2], accMp[2];  // this wave's off-diagonal pairs
-    Frag<bf16> kr[4];          // K_restore of this lane's token, record order
-    float aLr[2] = {0.f, 0.f}; // a_last of two channels (wave 0)
+    // chunk 0's beta, tile scan and factors
+    issue_g(0);
+    issue_qk(0);
+    store_beta(0, load_beta(0));
+    int meet = 0;
+    scan(0);
+    issue_g(1);
+    meet += 4;
+    lds_signal(&sm.meet);
+    lds_wait(&sm.meet, meet);
+    factors();
 
-    for (int it = 0; it < nch; ++it) {
-      // ---- stage A: tile scan, Q_loc / K_loc / K_start, diagonal tile pair ----
-      {
-        const int lane = opaque_lane(), lr = lane & 15, lg = lane >> 4, r = 16 * pw + lr;
-        // inclusive cumulative sum over the tile's tokens, then the tile
-        // totals (lane 15 of each row) to LDS
+    for (int step = 0; step <= nch; ++step) {
+      if (step < nch) {
+        RecOnce &A = sm.a;
+        RecTwice &B = sm.b[step & 1];
+        PrepScratch &P = sm.ps;
+        const int lane = opaque_lane(), lr = lane & 15, lg = lane >> 4;
+        const unsigned short rb_next = load_beta(step + 1);
+        if (I == 0) {
+          B.al[kperm_inv(2 * lane)] = alr[0];
+          B.al[kperm_inv(2 * lane + 1)] = alr[1];
+        }
+        // ---- elementwise: Q_loc, K_loc, K_st (tile products), Q_decay,
+        // K_decay (record, written once the state waves are done with the
+        // previous chunk's), K_rs and the scaled pair operands, K_restore
+        // (transposed into the record); the diagonal tile's products ----
+        Frag<bf16> fq[4], fk[4], fs[4], fre[4];
+        bf16x8 pq[4], pk[4];
+        f32x4 accLc = {0.f, 0.f, 0.f, 0.f}, accMr = accLc;
         float iq = 1.f, ik = 1.f; // 1 / |q|, 1 / |k| of this lane's token
         if (qk_on) {
           // the token's 128 channels sit in lanes lr, lr + 16, lr + 32, lr + 48
@@ -571,45 +728,19 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
           sk += __shfl_xor(sk, 32);
           iq = __builtin_amdgcn_rsqf(sq + qk_eps);
           ik = __builtin_amdgcn_rsqf(sk + qk_eps);
-          if (lg == 0) {
-            sm.Iq[r] = iq;
-            sm.Ik[r] = ik;
-          }
         }
-        float G[4][8];
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          widen8(rg[s], G[s]);
-        if (gate_on) {
-          // rows past the chunk end decay by nothing
-          const bool valid = r < min(kC, cd.ntok - it * kC);
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              G[s][j] = valid ? gate_log_decay(G[s][j], ea, g_min) : 0.f;
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            G[s][j] = row_scan16(G[s][j]);
-        if (lr == 15) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            *reinterpret_cast<f32x4 *>(&sm.Tot[pw][32 * s + 8 * lg]) =
-                f32x4{G[s][0], G[s][1], G[s][2], G[s][3]};
-            *reinterpret_cast<f32x4 *>(&sm.Tot[pw][32 * s + 8 * lg + 4]) =
-                f32x4{G[s][4], G[s][5], G[s][6], G[s][7]};
-          }
-        }
-        if (lg == 0)
-          sm.Beta[r] = __builtin_bit_cast(float, (unsigned)rbeta << 16);
-        accLd = f32x4{0.f, 0.f, 0.f, 0.f};
-        accMd = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          float qv[8], kv[8], xq[8], xk[8], xs[8];
+          float el[8], es[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            el[j] = __builtin_amdgcn_exp2f(G[s][j]);
+            es[j] = __builtin_amdgcn_exp2f(-G[s][j]);
+          }
+          float fp[8], ft[8], fr[8], qv[8], kv[8];
+          load8f(&P.fac[I][0][32 * s + 8 * lg], fp);
+          load8f(&P.fac[I][1][32 * s + 8 * lg], ft);
+          load8f(&P.fac[I][2][32 * s + 8 * lg], fr);
           widen8(rq[s], qv);
           widen8(rk[s], kv);
           if (qk_on) {
@@ -619,232 +750,162 @@ __global__ __launch_bounds__(kFThreads) void fused_kernel(
               kv[j] *= ik;
             }
           }
+          float xq[8], xk[8], xs[8], yq[8], yk[8], yr[8], yre[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const float x = G[s][j] * kLog2e;
-            xg[s][j] = x;
-            const float e1 = __builtin_amdgcn_exp2f(x);
-            xq[j] = qv[j] * e1;
-            xk[j] = kv[j] * e1;
-            xs[j] = kv[j] * __builtin_amdgcn_exp2f(-x);
+            xq[j] = qv[j] * el[j];  // Q_loc
+            xk[j] = kv[j] * el[j];  // K_loc
+            xs[j] = kv[j] * es[j];  // K_st
+            yq[j] = xq[j] * fp[j];  // Q_decay
+            yk[j] = xk[j] * fp[j];  // K_decay
+            yr[j] = xs[j] * ft[j];  // K_rs
+            yre[j] = yr[j] * fr[j]; // K_restore
           }
           fq[s] = pack8(xq);
           fk[s] = pack8(xk);
-          const Frag<bf16> fs = pack8(xs);
-          *reinterpret_cast<bf16x8 *>(&sm.x.ab.Kst[pw][lr][32 * s + 8 * lg]) = fs.v;
-          if (pw == 3) {
-            *reinterpret_cast<bf16x8 *>(&sm.x.ab.Aq3[0][lr][32 * s + 8 * lg]) = fk[s].v;
-            *reinterpret_cast<bf16x8 *>(&sm.x.ab.Aq3[1][lr][32 * s + 8 * lg]) = fq[s].v;
-          }
-          mma(accLd, fk[s], fs);
-          mma(accMd, fq[s], fs);
-        }
-        // the diagonal L tile (beta-scaled rows, strictly lower) for the
-        // state waves' inversion of the diagonal blocks in stage C
-        wave_lds_fence(); // this wave's beta entries are in LDS
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * pw + 4 * lg + i, col = 16 * pw + lr;
-          sm.L[row][col] = col < row ? sm.Beta[row] * accLd[i] : 0.f;
-        }
-      }
-      lds_barrier();
-      // ---- stage B: factors, Q_decay / K_decay / K_restore, off-diagonal pairs ----
-      {
-        const int lane = opaque_lane(), lr = lane & 15, lg = lane >> 4, r = 16 * pw + lr;
-        {
-          // this tile's factors for two record-order channels per lane
-          const int c0 = 2 * lane;
-          float t[4][2];
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const float2 x = *reinterpret_cast<const float2 *>(&sm.Tot[w][c0]);
-            t[w][0] = x.x;
-            t[w][1] = x.y;
-          }
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            float pI = 0.f, gc = 0.f;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              pI += w < pw ? t[w][e] : 0.f;
-              gc += t[w][e];
-            }
-            sm.Fac[pw][0][c0 + e] = pI * kLog2e;
-            sm.Fac[pw][1][c0 + e] = (gc - pI) * kLog2e;
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-              if (n < pair_count(pw)) {
-                const int I = pair_I(pw, n), J = pair_J(pw, n);
-                float sum = 0.f; // p_I - p_J = t_J + ... + t_{I-1} <= 0
-#pragma unroll
-                for (int w = 0; w < 3; ++w)
-                  sum += (w >= J && w < I) ? t[w][e] : 0.f;
-                sm.Foff[off_pair(I, J)][c0 + e] = __builtin_amdgcn_exp2f(sum * kLog2e);
-              }
-            }
-            if (pw == 0)
-              aLr[e] = __builtin_amdgcn_exp2f(gc * kLog2e);
-          }
-        }
-        wave_lds_fence();
-        // Q_decay and K_decay rows to the record, K_restore to registers
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          float xp[8], xc[8], qv[8], kv[8], yq[8], yk[8], yr[8];
-          load8f(&sm.Fac[pw][0][32 * s + 8 * lg], xp);
-          load8f(&sm.Fac[pw][1][32 * s + 8 * lg], xc);
-          widen8(rq[s], qv);
-          widen8(rk[s], kv);
-          if (qk_on) {
-            const float iq = sm.Iq[r], ik = sm.Ik[r];
+          fs[s] = pack8(xs);
+          fre[s] = pack8(yre);
+          pq[s] = pack8(yq).v;
+          pk[s] = pack8(yk).v;
+          // diagonal tile: L_II in the column layout; M_II swapped, in the
+          // row layout (row r = lr)
+          mma(accLc, fk[s], fs[s]);
+          mma(accMr, fs[s], fq[s]);
+          if (I < 3)
+            *reinterpret_cast<bf16x8 *>(&P.krs[I][s][lane * 8]) = pack8(yr).v;
+          if (I == 0) {
+            float f3[8], f4[8], b3[8], b4[8];
+            load8f(&P.fac[0][3][32 * s + 8 * lg], f3);
+            load8f(&P.fac[0][4][32 * s + 8 * lg], f4);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-              qv[j] *= iq;
-              kv[j] *= ik;
+              b3[j] = yr[j] * f3[j];
+              b4[j] = yr[j] * f4[j];
             }
-          }
+            *reinterpret_cast<bf16x8 *>(&P.bsc[0][s][lane * 8]) = pack8(b3).v; // B_20
+            *reinterpret_cast<bf16x8 *>(&P.bsc[1][s][lane * 8]) = pack8(b4).v; // B_30
+          } else if (I == 1) {
+            float f3[8], b3[8];
+            load8f(&P.fac[1][3][32 * s + 8 * lg], f3);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float a = __builtin_amdgcn_exp2f(xg[s][j] + xp[j]); // e^{G}
-            const float b = __builtin_amdgcn_exp2f(xc[j] - xg[s][j]); // e^{G_C - G}
-            yq[j] = qv[j] * a;
-            yk[j] = kv[j] * a;
-            yr[j] = kv[j] * b;
-          }
-          *reinterpret_cast<bf16x8 *>(&sm.Qd[r][32 * s + 8 * lg]) = pack8(yq).v;
-          *reinterpret_cast<bf16x8 *>(&sm.Kd[r][32 * s + 8 * lg]) = pack8(yk).v;
-          kr[s] = pack8(yr);
-        }
-        // off-diagonal pairs (I, J): B = K_start of tile J times e^{p_I - p_J}
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-          accLp[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-          accMp[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (n < pair_count(pw)) {
-            const int I = pair_I(pw, n), J = pair_J(pw, n);
-            const int pi = off_pair(I, J);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              const Frag<bf16> e = load_frag(&sm.x.ab.Kst[J][lr][32 * s + 8 * lg]);
-              float xs[8], fo[8];
-              frag_to_f32(e, xs);
-              load8f(&sm.Foff[pi][32 * s + 8 * lg], fo);
-#pragma unroll
-              for (int j = 0; j < 8; ++j)
-                xs[j] *= fo[j];
-              const Frag<bf16> b = pack8(xs);
-              Frag<bf16> ak, aq;
-              if (I == pw) {
-                ak = fk[s];
-                aq = fq[s];
-              } else {
-                ak = load_frag(&sm.x.ab.Aq3[0][lr][32 * s + 8 * lg]);
-                aq = load_frag(&sm.x.ab.Aq3[1][lr][32 * s + 8 * lg]);
-              }
-              mma(accLp[n], ak, b);
-              mma(accMp[n], aq, b);
-            }
+            for (int j = 0; j < 8; ++j)
+              b3[j] = yr[j] * f3[j];
+            *reinterpret_cast<bf16x8 *>(&P.bsc[2][s][lane * 8]) = pack8(b3).v; // B_31
+          } else if (I == 3) {
+            // tile 3's K_loc and Q_loc for the pair (3, 0), which tile 0's wave computes
+            *reinterpret_cast<bf16x8 *>(&P.t3k[s][lane * 8]) = fk[s].v;
+            *reinterpret_cast<bf16x8 *>(&P.t3q[s][lane * 8]) = fq[s].v;
           }
         }
-        // the next chunk's inputs are in flight from here on
-        if (it + 1 < nch)
-          issue(it + 1);
-      }
-      lds_barrier();
-      // ---- stage C: L / M_qk tiles, K_restore^T, a_last -------------------------
-      {
-        const int lane = opaque_lane(), lr = lane & 15, lg = lane >> 4, r = 16 * pw + lr;
-        // off-diagonal tiles (I > J: no mask) and the diagonal M_qk tile
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-          if (n < pair_count(pw)) {
-            const int I = pair_I(pw, n), J = pair_J(pw, n), col = 16 * J + lr;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int row = 16 * I + 4 * lg + i;
-              sm.L[row][col] = sm.Beta[row] * accLp[n][i];
-              sm.Mqk[row][kperm(col)] = static_cast<bf16>(accMp[n][i]);
-            }
-          }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * pw + 4 * lg + i, col = 16 * pw + lr;
-          sm.Mqk[row][kperm(col)] = static_cast<bf16>(col <= row ? accMd[i] : 0.f);
-        }
-        // K_restore^T: row kperm_inv(channel), column kperm(token)
+        // N = strictly lower part of Diag(beta) L_II (lane (lr, lg): row
+        // 4 lg + i, column lr), for the state wave that inverts I + N
         {
-          const int kc = kperm(r);
+          const f32x4 bcol = *reinterpret_cast<const f32x4 *>(&B.beta[16 * I + 4 * lg]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            P.nmat[I][4 * lg + i][lr] = (4 * lg + i > lr) ? bcol[i] * accLc[i] : 0.f;
+        }
+        lds_signal(&sm.n_ready);
+        // (every state wave is done reading the previous chunk's Q_decay, K_decay)
+        lds_wait(&sm.q_done, 4 * step);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          *reinterpret_cast<bf16x8 *>(&A.qd[4 * I + s][lane * 8]) = pq[s];
+          *reinterpret_cast<bf16x8 *>(&A.kd[4 * I + s][lane * 8]) = pk[s];
+        }
+        issue_qk(step + 1);
+        {
+          // K_restore^T: the selection products give lane (n, lg) channel
+          // 32 s + 16 hs + n of tokens 16 I + 4 lg .. + 3, which go to state
+          // row p = kperm_inv(channel), k-step I / 2, positions 4 (I % 2) ..
+          const Frag<bf16> sel0 = selection(0), sel1 = selection(1);
+          f32x4 tr[4][2];
 #pragma unroll
           for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              sm.KrT[kperm_inv(32 * s + 8 * lg + e)][kc] = kr[s].v[e];
+            for (int hs = 0; hs < 2; ++hs) {
+              tr[s][hs] = f32x4{0.f, 0.f, 0.f, 0.f};
+              mma(tr[s][hs], fre[s], hs ? sel1 : sel0);
+            }
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int hs = 0; hs < 2; ++hs) {
+              const int p = kperm_inv(32 * s + 16 * hs + lr);
+              *reinterpret_cast<bf16x4 *>(
+                  &B.krt[2 * (p >> 4) + (I >> 1)][((lg << 4) + (p & 15)) * 8 + 4 * (I & 1)]) =
+                  pack4(tr[s][hs]);
+            }
         }
-        if (pw == 0) {
-          sm.aL[kperm_inv(2 * lane)] = aLr[0];
-          sm.aL[kperm_inv(2 * lane + 1)] = aLr[1];
+        // next chunk's tile scan (its g was loaded a step ago)
+        scan(step + 1);
+        issue_g(step + 2);
+        // (every state wave is done reading the previous chunk's M_qk, L and,
+        // from the other copy, beta)
+        lds_wait(&sm.m_done, 4 * step);
+        store_beta(step + 1, rb_next);
+        {
+          // M_II with its diagonal: rows 16 I + lr, tokens 16 I + 4 lg + i
+          f32x4 m = accMr;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            m[i] = (4 * lg + i <= lr) ? m[i] : 0.f;
+          *reinterpret_cast<bf16x4 *>(&A.mqk[2 * I + (I >> 1)][lane * 8 + 4 * (I & 1)]) =
+              pack4(m);
         }
-      }
-      lds_barrier();
-      // ---- stage D: off-diagonal blocks of INV ---------------------------------
-      {
-        const int lane = opaque_lane(), lr = lane & 15, lg = lane >> 4;
-        // column block j = pw: X_ij = -D_i^-1 sum_{m=j}^{i-1} L_im X_mj
-        const int j = pw;
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        f32x4 X[4];
-        const f32x4 dj = acc_load(&sm.Dinv[j][0][0], kLdB, lr, lg);
+        meet += 4;
+        lds_signal(&sm.meet);
+        lds_wait(&sm.meet, meet);
+
+        // ---- off-diagonal tile pairs (B_IJ: K_rs,J itself for J = I - 1,
+        // else its scaled copy), two per wave at most ----
+        if (I == 0) {
+          Frag<bf16> t3k[4], t3q[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          X[t] = (t == j) ? dj : zero;
-        const float bcol = sm.Beta[16 * j + lr];
-#pragma unroll
-        for (int i = 1; i < 4; ++i) {
-          if (i > j) {
-            f32x4 t = zero;
-#pragma unroll
-            for (int m = 0; m < 3; ++m)
-              if (m >= j && m < i)
-                mm16_lds_acc(t, &sm.L[16 * i][16 * m], kLdL, X[m], lr, lg);
-            f32x4 x = zero;
-            mm16_lds_acc(x, &sm.Dinv[i][0][0], kLdB, t, lr, lg, -1.f);
-            X[i] = x;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              sm.INVb[16 * i + 4 * lg + e][kperm(16 * j + lr)] = static_cast<bf16>(x[e] * bcol);
+          for (int s = 0; s < 4; ++s) {
+            t3k[s] = load_frag(&P.t3k[s][lane * 8]);
+            t3q[s] = load_frag(&P.t3q[s][lane * 8]);
+          }
+          pair(3, 0, &P.bsc[1][0][0], t3k, t3q, B.beta[48 + lr]);
+        } else {
+          const float brow = B.beta[16 * I + lr];
+          if (I == 1) {
+            pair(1, 0, &P.krs[0][0][0], fk, fq, brow);
+          } else if (I == 2) {
+            pair(2, 0, &P.bsc[0][0][0], fk, fq, brow);
+            pair(2, 1, &P.krs[1][0][0], fk, fq, brow);
+          } else {
+            pair(3, 1, &P.bsc[2][0][0], fk, fq, brow);
+            pair(3, 2, &P.krs[2][0][0], fk, fq, brow);
           }
         }
+        // next chunk's factors (every tile total is in after the meeting)
+        factors();
       }
-      lds_barrier();
+      lds_sync();
     }
-    // the last chunk step only consumes the last record
-    for (int b = 0; b < 4; ++b)
-      lds_barrier();
   }
 }
 
 hipError_t launch_fused(const ChainDesc *chains, int32_t nchains, int32_t H, const void *q,
-                        const void *k, const void *v, const void *g, const void *beta, void *o,
-                        const float *init, const float *sin, float *final_state, float *ckpt,
-                        const Prologue &pro, const Epilogue &epi, hipStream_t s) {
+                         const void *k, const void *v, const void *g, const void *beta,
+                         void *o, const float *init, float *final_state, float *ckpt,
+                         hipStream_t s, const Prologue &pro, const Epilogue &epi) {
   if (nchains == 0)
     return hipSuccess;
-  // one workgroup per (chain, head) carries all 128 state columns
-  constexpr int NCT = 2;
-  dim3 grid((unsigned)nchains, (unsigned)H, kD / (64 * NCT)), block(kFThreads);
+  dim3 grid((unsigned)((int64_t)nchains * H)), block(kFusedThreads);
   auto launch = [&](auto kern) {
     kern<<<grid, block, 0, s>>>(chains, H, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v,
-                                (const bf16 *)g, (const bf16 *)beta, (bf16 *)o, init, sin,
+                                (const bf16 *)g, (const bf16 *)beta, (bf16 *)o, init,
                                 final_state, ckpt, pro.A_log, pro.g_min, pro.qk_eps,
                                 (const bf16 *)epi.gate, epi.weight, epi.eps);
   };
   if (epi.on())
-    launch(fused_kernel<NCT, true, true>);
+    launch(fused_kernel<true, true>);
   else if (pro.on())
-    launch(fused_kernel<NCT, true, false>);
+    launch(fused_kernel<true, false>);
   else
-    launch(fused_kernel<NCT, false, false>);
+    launch(fused_kernel<false, false>);
   return hipGetLastError();
 }
 

@@ -159,22 +159,15 @@ hipError_t launch_k2(int elt, int mode, const ChainDesc *chains, int32_t nchains
                      const float *sin, float *final_a, float *final_b, int m_scan_order,
                      const Epilogue &epi, hipStream_t s);
 
-// Fused chunk prep + state chain (bf16, width dv): writes o, exit states and
-// (when ckpt is not null) the chains' state checkpoints; with the prologue
-// and the output epilogue.
-hipError_t launch_fused(const ChainDesc *chains, int32_t nchains, int32_t H, const void *q,
-                        const void *k, const void *v, const void *g, const void *beta, void *o,
-                        const float *init, const float *sin, float *final_state, float *ckpt,
-                        const Prologue &pro, const Epilogue &epi, hipStream_t s);
-
 // Fused chunk prep + state chain, one workgroup per (chain, head) with all
-// dv columns (bf16, no prologue or epilogue; entry states from `init` or
-// zero): writes o, exit states and (when ckpt is not null) the chains' state
-// checkpoints.
-hipError_t launch_fused2(const ChainDesc *chains, int32_t nchains, int32_t H, const void *q,
+// dv columns (bf16; entry states from `init` or zero): writes o, exit states
+// and (when ckpt is not null) the chains' state checkpoints; with the
+// prologue and the output epilogue.
+hipError_t launch_fused(const ChainDesc *chains, int32_t nchains, int32_t H, const void *q,
                          const void *k, const void *v, const void *g, const void *beta,
                          void *o, const float *init, float *final_state, float *ckpt,
-                         hipStream_t s);
+                         hipStream_t s, const Prologue &pro = Prologue(),
+                         const Epilogue &epi = Epilogue());
 
 // Whether the state chain's replay pass takes the output epilogue itself:
 // when its plain launch runs 128-column blocks anyway (at least one wide
