@@ -58,98 +58,145 @@ def stored_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def stored_counters(workload: str):
+    """SQ counter summary of the prefill call (profiles/counters_<workload>.json)
+    from committed rocprofv3 runs, if they were taken on the current kernel
+    sources; else None."""
+    path = os.path.join(ROOT, "profiles", "counters_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("call")
+
+
 COPY_PROBE_FLOATS = 256 << 20   # 1 GiB fp32 read + 1 GiB written by the calibration copy
+# kernels of this library, by the part of their names that identifies them
+LIB_KERNELS = ("prep_kernel", "k1_kernel", "k2_kernel", "scan_kernel", "fused_kernel",
+               "out_norm_gate_kernel", "decode_kernel")
 
 
-def traffic_probe(kda, wl, name, dev, path="auto"):
-    """One prefill call and one decode step bracketed by a plain elementwise
-    copy of known size, for rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE):
-    the copy's counter reading calibrates the counters to bytes."""
-    import torch
-    w = wl.WORKLOADS[name]
-    d = wl.prefill_case(w, device=dev)
-    cu = d["cu"]
-    N, H = len(w.lengths), w.H
-    T = int(cu[-1])
-    o = torch.empty((T, H, D), dtype=w.dtype, device=dev)
-    fin = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(kda.prefill_workspace_size(cu, H, w.dtype, 0, path=path), 1),
-                     dtype=torch.uint8, device=dev)
+def probe_dispatches(path, counters):
+    """Per dispatch of a --traffic-probe counter run: (name, {counter: value})
+    in dispatch order, each counter summed over its instances."""
+    import csv
+    rows = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] not in counters:
+                continue
+            key = int(r["Dispatch_Id"])
+            ent = rows.setdefault(key, [r["Kernel_Name"], {}])
+            ent[1][r["Counter_Name"]] = ent[1].get(r["Counter_Name"], 0.0) + float(
+                r["Counter_Value"])
+    return [tuple(rows[k]) for k in sorted(rows)]
 
-    def step():
-        kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu,
-                          initial_state=d["init"], o=o, final_state=fin, workspace=ws, path=path)
 
-    step()                                   # warm (first-touch, schedule upload)
-    torch.cuda.synchronize(dev)
-    src = torch.ones(COPY_PROBE_FLOATS, dtype=torch.float32, device=dev)
-    dst = torch.empty_like(src)
-    torch.cuda.synchronize(dev)
-    torch.mul(src, 1.0, out=dst)             # the calibration copy
-    torch.cuda.synchronize(dev)
-    del src, dst
-    step()                                   # the measured prefill call
-    torch.cuda.synchronize(dev)
-    del d, o, fin, ws
-    torch.cuda.empty_cache()
-    wd = wl.WORKLOADS["decode_f32_N256_H96_x64"]
-    dd = wl.decode_case(wd, device=dev)
-    od = torch.empty((wd.lengths[0], wd.H, D), dtype=wd.dtype, device=dev)
-    for _ in range(2):                       # warm, then the measured step
-        kda.decode_step(dd["state"], dd["q"][0], dd["k"][0], dd["v"][0], dd["g"][0],
-                        dd["beta"][0], o=od)
-        torch.cuda.synchronize(dev)
-    chunk_heads = sum((L + C - 1) // C for L in w.lengths) * H
-    print(json.dumps({"probe": name, "copy_bytes_read": 4 * COPY_PROBE_FLOATS,
-                      "copy_bytes_written": 4 * COPY_PROBE_FLOATS,
-                      "chunk_heads": chunk_heads}), flush=True)
+def probe_window(disp):
+    """The measured prefill call of a --traffic-probe run: the library's
+    dispatches (and the schedule uploads among them) that follow the
+    calibration copy, the last call before the decode steps; and that
+    copy's index."""
+    first_dec = next(i for i, (n, _) in enumerate(disp) if "decode_kernel" in n)
+    lib = [i for i in range(first_dec)
+           if any(t in disp[i][0] for t in LIB_KERNELS)]
+    i = lib[-1]
+    while i >= 0 and (any(t in disp[i][0] for t in LIB_KERNELS) or "copyBuffer" in disp[i][0]):
+        i -= 1
+    assert i >= 0 and "elementwise" in disp[i][0].lower(), "no calibration copy before the call"
+    call = [(next(t for t in LIB_KERNELS if t in n), c) for n, c in disp[i + 1:lib[-1] + 1]
+            if any(t in n for t in LIB_KERNELS)]
+    return i, call
 
 
 def traffic_from_counters(fetch_csv, write_csv, workload, command):
-    """Per-dispatch HBM bytes of the prefill kernels and the decode kernel
-    from two rocprofv3 counter files (FETCH_SIZE and WRITE_SIZE, KiB per
-    dispatch), each scaled so that the calibration copy reads/writes exactly
-    its known size.  The last dispatch of each kernel is the measured one."""
-    import csv
-
-    def per_dispatch(path, counter):
-        rows = {}
-        with open(path) as f:
-            for r in csv.DictReader(f):
-                if r["Counter_Name"] != counter:
-                    continue
-                key = int(r["Dispatch_Id"])
-                name = r["Kernel_Name"]
-                rows.setdefault(key, [name, 0.0])
-                rows[key][1] += float(r["Counter_Value"])
-        return [rows[k] for k in sorted(rows)]
-
+    """HBM bytes of the measured prefill call and of the decode step from two
+    rocprofv3 counter files of --traffic-probe runs (FETCH_SIZE and
+    WRITE_SIZE, KiB per dispatch), each scaled so that the calibration copy
+    reads / writes exactly its known size."""
     out = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
            "command": command, "counters": {}}
     for counter, path, known in (("FETCH_SIZE", fetch_csv, 4 * COPY_PROBE_FLOATS),
                                  ("WRITE_SIZE", write_csv, 4 * COPY_PROBE_FLOATS)):
-        disp = per_dispatch(path, counter)
-        copies = [v for n, v in disp if "elementwise" in n.lower()]
-        copy_kib = max(copies)
+        disp = probe_dispatches(path, (counter,))
+        icopy, call = probe_window(disp)
+        copy_kib = disp[icopy][1][counter]
         scale = known / (copy_kib * 1024.0)
-        last = {}
-        for n, v in disp:
-            for tag in ("prep_kernel", "k1_kernel", "k2_kernel", "scan_kernel", "decode_kernel"):
-                if tag in n:
-                    last.setdefault(tag, []).append(v)
+        dec = [c[counter] for n, c in disp if "decode_kernel" in n]
         out["counters"][counter] = {
             "copy_kib": copy_kib, "scale": scale,
-            "kib_per_dispatch": {t: v[-1] for t, v in last.items()},
-            "bytes_per_dispatch": {t: v[-1] * 1024.0 * scale for t, v in last.items()}}
+            "call_dispatches": [[t, c[counter] * 1024.0 * scale] for t, c in call],
+            "call_bytes": sum(c[counter] for _, c in call) * 1024.0 * scale,
+            "decode_bytes": dec[-1] * 1024.0 * scale if dec else None}
     f, w = out["counters"]["FETCH_SIZE"], out["counters"]["WRITE_SIZE"]
-    prefill_tags = [t for t in ("prep_kernel", "k1_kernel", "k2_kernel", "scan_kernel")
-                    if t in f["bytes_per_dispatch"]]
-    out["hbm_bytes_per_launch"] = sum(f["bytes_per_dispatch"][t] + w["bytes_per_dispatch"].get(t, 0.0)
-                                      for t in prefill_tags)
-    if "decode_kernel" in f["bytes_per_dispatch"]:
-        out["decode_hbm_bytes_per_step"] = (f["bytes_per_dispatch"]["decode_kernel"] +
-                                            w["bytes_per_dispatch"].get("decode_kernel", 0.0))
+    out["hbm_bytes_per_launch"] = f["call_bytes"] + w["call_bytes"]
+    if f["decode_bytes"] is not None:
+        out["decode_hbm_bytes_per_step"] = f["decode_bytes"] + w["decode_bytes"]
     path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    with open(path, "w") as fo:
+        json.dump(out, fo, indent=1)
+        fo.write("\n")
+    print(json.dumps(out, indent=1))
+
+
+# SIMDs of one XCD: GRBM_GUI_ACTIVE counts each XCD's busy cycles, so the
+# SIMD-cycles of a dispatch are this times its summed GRBM_GUI_ACTIVE
+SIMDS_PER_XCD = 32 * 4
+
+
+def counters_from(csv_paths, workload, command):
+    """SQ activity of the measured prefill call from --traffic-probe counter
+    runs (rocprofv3 --pmc, one file per pass): per dispatch and for the call,
+    the fraction of SIMD cycles the MFMA unit was busy, VALU instructions per
+    SIMD cycle (times 4: a wave64 VALU op holds the SIMD 4 cycles), LDS
+    instructions and bank-conflict cycles per LDS-active cycle."""
+    merged = None
+    for path in csv_paths:
+        disp = probe_dispatches(path, ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU",
+                                       "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_WAVES",
+                                       "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS",
+                                       "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                                       "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_WAIT_INST_LDS",
+                                       "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"))
+        _, call = probe_window(disp)
+        if merged is None:
+            merged = [[t, dict(c)] for t, c in call]
+        else:
+            assert [t for t, _ in merged] == [t for t, _ in call], "passes differ"
+            for m, (_, c) in zip(merged, call):
+                for k, v in c.items():
+                    if k == "GRBM_GUI_ACTIVE":
+                        m[1][k] = max(m[1].get(k, 0.0), v)
+                    else:
+                        m[1][k] = v
+
+    def derive(c):
+        simd = SIMDS_PER_XCD * c["GRBM_GUI_ACTIVE"]
+        d = {"grbm_gui_active": c["GRBM_GUI_ACTIVE"]}
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+            d["mfma_busy_frac"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / simd
+        if "SQ_INSTS_VALU" in c:
+            d["valu_issue_frac"] = 4.0 * c["SQ_INSTS_VALU"] / simd
+        for k in ("SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                  "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_WAVES"):
+            if k in c:
+                d[k.lower()] = c[k]
+        if c.get("SQ_ACTIVE_INST_LDS"):
+            d["lds_bank_conflict_per_active"] = (c.get("SQ_LDS_BANK_CONFLICT", 0.0) /
+                                                 c["SQ_ACTIVE_INST_LDS"])
+        return d
+
+    out = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
+           "command": command, "dispatches": [[t, derive(c)] for t, c in merged]}
+    tot = {}
+    for _, c in merged:
+        for k, v in c.items():
+            tot[k] = tot.get(k, 0.0) + v
+    out["call"] = derive(tot)
+    out["call"]["kernels"] = [t for t, _ in merged]
+    path = os.path.join(ROOT, "profiles", "counters_%s.json" % workload)
     with open(path, "w") as fo:
         json.dump(out, fo, indent=1)
         fo.write("\n")
@@ -396,12 +443,18 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two counter_collection.csv files of --traffic-probe runs into "
                          "profiles/traffic_<workload>.json (no GPU needed)")
+    ap.add_argument("--counters-from", nargs="+", metavar="CSV",
+                    help="turn counter_collection.csv files of --traffic-probe SQ counter runs "
+                         "into profiles/counters_<workload>.json (no GPU needed)")
     ap.add_argument("--traffic-command", default="",
                     help="the command line that produced the counter files (recorded)")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from_counters(args.traffic_from[0], args.traffic_from[1], args.workload,
                               args.traffic_command)
+        return
+    if args.counters_from:
+        counters_from(args.counters_from, args.workload, args.traffic_command)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -443,6 +496,8 @@ def main():
             continue
         steps = 5 if "varlen" in name else max(5, args.steps // 2)
         r = time_prefill(kda, wl, name, steps, warm, 0, dev)
+        r["traffic"] = stored_traffic(name)
+        r["counters"] = stored_counters(name)
         extra[name] = r
         print("prefill %s: %.3f ms/step, %.3g tokens/s, %.1f%% MFMA"
               % (name, r["ms_per_step"], r["tokens_per_s"], 100 * r["mfma_frac"]),
@@ -480,6 +535,7 @@ def main():
 
     w = wl.WORKLOADS[args.workload]
     traffic = stored_traffic(args.workload)
+    counters = stored_counters(args.workload)
     line = {
         "metric": METRIC,
         "value": main_res["tokens_per_s"],
@@ -499,8 +555,12 @@ def main():
         "roofline": {"bound": "mfma", "achieved": main_res["tflops"],
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": main_res["mfma_frac"], "traffic": traffic,
-                     "kernel": "kda_chunk_prefill launch sequence (chunk prep K1 + state "
-                               "chain K2), model FLOPs per call / event-timed call duration",
+                     "kernel": "kda_chunk_prefill call, %s implementation (%s), model "
+                               "FLOPs per call / event-timed call duration"
+                               % (args.path, "+".join(counters["kernels"]) if counters else
+                                  "kernels per the committed counter runs"),
+                     "mfma_busy_frac": counters["mfma_busy_frac"] if counters else None,
+                     "valu_issue_frac": counters["valu_issue_frac"] if counters else None,
                      "hbm_GB_per_s": (traffic / (main_res["ms_per_step"] * 1e-3) / 1e9
                                       if traffic else None)},
         "hbm_reference": {"peak_GB_per_s": PEAK_HBM_GBS, "copy": copy_ref},
