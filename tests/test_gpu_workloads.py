@@ -31,13 +31,13 @@ def rel_err(x, ref):
     return float(np.max(np.abs(x - ref)) / max(float(np.max(np.abs(ref))), 1e-30))
 
 
-def run_prefill(name, split=0):
+def run_prefill(name, split=0, path=None):
     w = wl.WORKLOADS[name]
-    say("workload", name, "split_hint", split, "segments =",
+    say("workload", name, "split_hint", split, "path", path, "segments =",
         kda.plan_num_segments(max(w.lengths), len(w.lengths), w.H, split))
     d = wl.prefill_case(w, device=DEV)
     o, fin = kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu"],
-                               initial_state=d["init"], split_hint=split)
+                               initial_state=d["init"], split_hint=split, path=path)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all() and torch.isfinite(fin).all()
     return w, d, o, fin
@@ -71,8 +71,12 @@ def test_prefill_f32_T256_H2_full():
     check_heads(w, d, o, fin, [0], [0, 1])
 
 
-def test_prefill_bf16_T8192_H96_sampled_heads():
-    w, d, o, fin = run_prefill("prefill_bf16_T8192_H96")
+@pytest.mark.parametrize("path", [None, "fused"])
+def test_prefill_bf16_T8192_H96_sampled_heads(path):
+    """The automatic choice (chunk prep, then the state chain) and the fused
+    kernel, whose one workgroup per head carries the state through all 128
+    chunks of the sequence."""
+    w, d, o, fin = run_prefill("prefill_bf16_T8192_H96", path=path)
     check_heads(w, d, o, fin, [0], list(range(0, 96, 8)))
 
 
