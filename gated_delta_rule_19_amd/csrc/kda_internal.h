@@ -72,9 +72,22 @@ __host__ __device__ constexpr int kperm_inv(int p) {
 //   a_last [D] fp32; 256-aligned.  fp32 records keep Q_decay / K_decay
 //   columns in kperm order and the state rows in channel order; bf16 records
 //   the reverse, and store Q_decay, K_decay and M_qk in 16-byte pieces in
-//   the order the bf16 prep writes them (kda_prep.hip).
+//   the order the bf16 prep writes them (kda_prep.hip).  bf16 records hold
+//   the two lower-triangular C x C matrices as their nonzero 1 KiB fragment
+//   blocks only (tri_block).
+constexpr int kTriBlocks = 6; // nonzero (16-row, 32-token) blocks of a lower-triangular C x C
 constexpr size_t k1_record_bytes(size_t es) {
-  return ((3 * 64 * 128 + 2 * 64 * 64) * es + 128 * 4 + 255) / 256 * 256;
+  return es == 2 ? ((3 * 64 * 128 + 2 * kTriBlocks * 512) * es + 128 * 4 + 255) / 256 * 256
+                 : ((3 * 64 * 128 + 2 * 64 * 64) * es + 128 * 4 + 255) / 256 * 256;
+}
+
+// A lower-triangular C x C matrix (INV Diag(beta), M_qk) in a bf16 record:
+// its 16-row by 32-token fragment blocks b = 2 (row tile) + (token half),
+// of which blocks 1 and 3 (row tiles 0 and 1 against tokens 32..63) lie
+// wholly above the diagonal and are not stored.  The stored block index of
+// block b, or -1 for those two.
+__host__ __device__ constexpr int tri_block(int b) {
+  return b == 0 ? 0 : (b == 2 ? 1 : (b >= 4 ? b - 2 : -1));
 }
 
 // Column blocks of the state-carrying kernel (columns of S per workgroup;

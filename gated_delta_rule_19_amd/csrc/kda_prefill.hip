@@ -592,8 +592,8 @@ template <> struct RecLds<bf16> {
   static constexpr int kd = qd + kC * kD * 2;
   static constexpr int krt = kd + kC * kD * 2;
   static constexpr int invb = krt + kD * kC * 2;
-  static constexpr int mqk = invb + kC * kC * 2;
-  static constexpr int ac = mqk + kC * kC * 2;
+  static constexpr int mqk = invb + kTriBlocks * 1024; // stored blocks only (tri_block)
+  static constexpr int ac = mqk + kTriBlocks * 1024;
   static constexpr int bytes = ac + kD * 4;
   static constexpr int blocks = (bytes + 1023) / 1024;
 };
@@ -974,6 +974,15 @@ __global__ __launch_bounds__(k2_threads(BV, NCT)) void k2_kernel(
         else
           return load_frag(base + (16 * tile + lr) * ld + 32 * s + 8 * lg);
       };
+      // INV Diag(beta) and M_qk are lower triangular: their blocks (row
+      // tile 0 or 1, tokens 32..63) are zero, not stored in bf16 records and
+      // not multiplied
+      auto frag_tri = [&](const T *base, int tile, int s) {
+        if constexpr (L::pieces)
+          return load_frag(base + (tri_block(2 * tile + s) * 64 + lane) * 8);
+        else
+          return frag(base, LC, tile, s);
+      };
 
       // W = K_decay S, O = Q_decay S (K = channels, B operand = S)
       Frag<T> bs[NCT][4];
@@ -1021,8 +1030,9 @@ __global__ __launch_bounds__(k2_threads(BV, NCT)) void k2_kernel(
         } else {
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) {
-            ai[0][tt] = frag(INVb, LC, tt, 0);
-            ai[1][tt] = frag(INVb, LC, tt, 1);
+            ai[0][tt] = frag_tri(INVb, tt, 0);
+            if (tt >= 2)
+              ai[1][tt] = frag_tri(INVb, tt, 1);
           }
         }
 #pragma unroll
@@ -1075,8 +1085,9 @@ __global__ __launch_bounds__(k2_threads(BV, NCT)) void k2_kernel(
       if (MODE == 0) {
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-          am[0][tt] = frag(Mqk, LC, tt, 0);
-          am[1][tt] = frag(Mqk, LC, tt, 1);
+          am[0][tt] = frag_tri(Mqk, tt, 0);
+          if (tt >= 2)
+            am[1][tt] = frag_tri(Mqk, tt, 1);
         }
       }
       f32x4 U[NCT][4];
@@ -1088,7 +1099,7 @@ __global__ __launch_bounds__(k2_threads(BV, NCT)) void k2_kernel(
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+        for (int tt = s == 1 ? 2 : 0; tt < 4; ++tt)
 #pragma unroll
           for (int c = 0; c < NCT; ++c)
             mma(U[c][tt], ai[s][tt], bw[c][s]);
@@ -1111,7 +1122,7 @@ __global__ __launch_bounds__(k2_threads(BV, NCT)) void k2_kernel(
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt)
+          for (int tt = s == 1 ? 2 : 0; tt < 4; ++tt)
 #pragma unroll
             for (int c = 0; c < NCT; ++c)
               mma(Oa[c][tt], am[s][tt], bu[c][s]);

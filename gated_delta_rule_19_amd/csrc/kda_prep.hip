@@ -64,9 +64,14 @@ constexpr float kL2e = 1.4426950408889634f;
 // record sections, in elements of their type
 constexpr int kRecKd = kC * kD;          // bf16
 constexpr int kRecKrT = 2 * kC * kD;     // bf16
-constexpr int kRecInvb = 3 * kC * kD;    // bf16
-constexpr int kRecMqk = kRecInvb + kC * kC;
-constexpr int kRecAl = (kRecMqk + kC * kC) / 2; // fp32
+constexpr int kRecInvb = 3 * kC * kD;    // bf16, the stored blocks of a triangular C x C
+constexpr int kRecMqk = kRecInvb + kTriBlocks * 512; // bf16, likewise
+constexpr int kRecAl = (kRecMqk + kTriBlocks * 512) / 2; // fp32
+// An element offset past the end of every record: a store there falls
+// outside the item's buffer resource and is dropped.  The pieces of a
+// triangular section's unstored blocks go there, so that every path issues
+// the same number of record stores.
+constexpr int kRecDrop = 1 << 28;
 
 // The 6 off-diagonal tile pairs (I, J), I > J, by wave: (3,0) (3,1) | (1,0) |
 // (2,0) (2,1) | (3,2).  Each M_qk row piece that spans the tile pair
@@ -97,6 +102,14 @@ struct PrepSmem {
 // per row
 __host__ __device__ constexpr int piece_index(int r, int g, int G) {
   return ((r >> 4) * (G >> 2) + (g >> 2)) * 64 + (g & 3) * 16 + (r & 15);
+}
+
+// record element offset of the 16-byte piece g of row r (8 pieces per row)
+// of the triangular section at `base`, or kRecDrop for a piece of one of its
+// unstored blocks
+__host__ __device__ constexpr int tri_piece(int base, int r, int g) {
+  const int tb = tri_block(2 * (r >> 4) + (g >> 2));
+  return tb < 0 ? kRecDrop : base + 8 * (tb * 64 + (g & 3) * 16 + (r & 15));
 }
 
 // Record stores go through one buffer resource per item (base address in
@@ -307,7 +320,8 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       const int u = (int)threadIdx.x + kPrepThreads * n;
-      rec_store8(dst, kRecInvb + 8 * u,
+      const int tb = tri_block(u >> 6);
+      rec_store8(dst, tb < 0 ? kRecDrop : kRecInvb + 8 * (tb * 64 + (u & 63)),
                  *reinterpret_cast<const bf16x8 *>(&sm.Inv[piece_row(u)][piece_col(u)]));
     }
   };
@@ -468,11 +482,12 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2)
         for (int i = 0; i < 4; ++i)
           md[i] = (4 * lg + i <= lr) ? accMr[i] : 0.f;
         auto put = [&](int I, int m, const f32x4 &lo, const f32x4 &hi) {
-          rec_store8(rr, kRecMqk + 8 * piece_index(16 * I + lr, 4 * m + lg, 8), lo, hi);
+          rec_store8(rr, tri_piece(kRecMqk, 16 * I + lr, 4 * m + lg), lo, hi);
         };
-        // two stores per wave on every path; the all-zero pieces take their
-        // zeros from an opaque value, so that no zero vector is hoisted out
-        // of the item loop and kept in registers across it
+        // two stores per wave on every path; the pieces of the unstored
+        // all-zero blocks are dropped, and take their zeros from an opaque
+        // value, so that no zero vector is hoisted out of the item loop and
+        // kept in registers across it
         u32x4 zw;
         asm volatile("v_mov_b32 %0, 0\n\tv_mov_b32 %1, 0\n\tv_mov_b32 %2, 0\n\tv_mov_b32 %3, 0"
                      : "=v"(zw[0]), "=v"(zw[1]), "=v"(zw[2]), "=v"(zw[3]));
@@ -482,13 +497,13 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2)
           put(0, 0, md, zero);
         } else if (pw == 1) {
           put(1, 0, accM[0], md);
-          rec_store8(rr, kRecMqk + 8 * piece_index(16 + lr, 4 + lg, 8), zz);
+          rec_store8(rr, tri_piece(kRecMqk, 16 + lr, 4 + lg), zz); // unstored block: dropped
         } else if (pw == 2) {
           put(2, 0, accM[0], accM[1]);
           put(2, 1, md, zero);
         } else {
           put(3, 1, accM[0], md);
-          rec_store8(rr, kRecMqk + 8 * piece_index(lr, 4 + lg, 8), zz);
+          rec_store8(rr, tri_piece(kRecMqk, lr, 4 + lg), zz); // unstored block: dropped
         }
       }
 

@@ -70,9 +70,10 @@ def test_workspace_sizes(lib):
     a, p = cu(0, 256)
     ws32 = lib.kda_chunk_prefill_workspace_size(1, p, 2, 128, 128, nat.KDA_F32, 0)
     ws16 = lib.kda_chunk_prefill_workspace_size(1, p, 2, 128, 128, nat.KDA_BF16, 0)
-    # 4 chunks x 2 heads of chunk-prep records (128.5 KiB fp32, 64.5 KiB bf16)
+    # 4 chunks x 2 heads of chunk-prep records: 128.5 KiB fp32; 60.5 KiB bf16,
+    # whose two triangular 64 x 64 sections keep 6 of their 8 1 KiB blocks
     assert ws32 > 4 * 2 * 128 * 1024
-    assert ws32 > ws16 > 4 * 2 * 64 * 1024
+    assert 4 * 2 * 61952 <= ws16 < 4 * 2 * 61952 + 4096
     # bf16 with at least 512 (sequence, head) chains runs the fused kernel,
     # which keeps its records on chip and needs only the schedule tables
     a4, p4 = cu(*[256 * i for i in range(65)])
@@ -352,7 +353,7 @@ def test_prefill_path_selection(lib):
     auto = size(one, 2, nat.KDA_BF16, 0, 0)
     two = size(one, 2, nat.KDA_BF16, 0, 1)
     fused = size(one, 2, nat.KDA_BF16, 0, 2)
-    assert auto == two > 4 * 2 * 64 * 1024          # few chains: the two kernels, with records
+    assert auto == two >= 4 * 2 * 61952         # few chains: the two kernels, with records
     assert 0 < fused < 64 * 1024                    # the fused kernel: schedule tables only
     a, p = cu(*one)
     assert auto == lib.kda_chunk_prefill_ex_workspace_size(1, p, 2, 128, 128, nat.KDA_BF16, 0,
