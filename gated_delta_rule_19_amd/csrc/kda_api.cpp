@@ -471,9 +471,9 @@ kda_status prefill_impl(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_
   if (e == hipSuccess && !p.segchains.empty()) {
     e = launch_k2(elt, 1, (const ChainDesc *)(ws + p.off_seg), (int32_t)p.segchains.size(), H,
                   ws + p.off_rec, v, nullptr, nullptr, nullptr, (float *)(ws + p.off_St),
-                  (float *)(ws + p.off_M), /*m_scan_order=*/1, Epilogue(), s);
+                  (float *)(ws + p.off_M), /*m_scan_order=*/elt == 1 ? 2 : 1, Epilogue(), s);
     if (e == hipSuccess)
-      e = launch_scan((const ScanDesc *)(ws + p.off_scan), (int32_t)p.scans.size(), H,
+      e = launch_scan(elt, (const ScanDesc *)(ws + p.off_scan), (int32_t)p.scans.size(), H,
                       (const float *)(ws + p.off_M), (const float *)(ws + p.off_St),
                       initial_state, (float *)(ws + p.off_Sin), s);
   }

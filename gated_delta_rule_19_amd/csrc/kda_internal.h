@@ -119,6 +119,18 @@ __host__ __device__ constexpr int scan_m_index(int r, int m) {
           (r & 15)) * 4 + (m & 3);
 }
 
+// bf16 planners hold M_j as two bf16 matrices, hi = bf16(M) and lo =
+// bf16(M - hi), hi at elements [0, dk^2) and lo at [dk^2, 2 dk^2) of the
+// same 64 KiB slot, each in the order of the bf16 scan kernel's
+// v_mfma_f32_16x16x32_bf16 A operands: 1 KiB blocks per (wave w = r / 32,
+// k-step s = m / 32, row tile t = r / 16 % 2) in that order, lane
+// 16 (m / 8 % 4) + r % 16 holding the eight reduction indices
+// m / 8 * 8 .. + 7.
+__host__ __device__ constexpr int scan_m_bf16_index(int r, int m) {
+  return ((((r >> 5) * 4 + (m >> 5)) * 2 + ((r >> 4) & 1)) * 64 + ((m >> 3) & 3) * 16 +
+          (r & 15)) * 8 + (m & 7);
+}
+
 // Steps of the layer fused into the chunk prep ("Kimi K3.1 Pro 架构完全拆解"
 // §3.2; "Kimi K3 的架構" §七):
 //   A_log != null : the g input holds raw gate logits z, and the log decay is
@@ -166,7 +178,8 @@ hipError_t launch_prep_bf16(const ChunkDesc *chunks, int32_t nchunks, int32_t H,
 //         with the epilogue on, o leaves normalized and gated and the whole
 //         dv-wide row is one workgroup's);
 // mode 1: segment pass (width dk + dv: [S~ | M], no o; S~ to final_a, M to
-//         final_b, row-major or, with m_scan_order, at scan_m_index).
+//         final_b: m_scan_order 0 row-major, 1 at scan_m_index, 2 (bf16
+//         records) as hi / lo bf16 at scan_m_bf16_index).
 hipError_t launch_k2(int elt, int mode, const ChainDesc *chains, int32_t nchains, int32_t H,
                      const void *ws, const void *v, void *o, const float *init,
                      const float *sin, float *final_a, float *final_b, int m_scan_order,
@@ -192,7 +205,9 @@ bool k2_fuses_epilogue(int32_t nchains, int32_t H);
 hipError_t launch_out_norm_gate(int elt, int64_t rows, void *o, const Epilogue &epi,
                                 hipStream_t s);
 
-hipError_t launch_scan(const ScanDesc *descs, int32_t ndesc, int32_t H, const float *Mseg,
+// elt 1 (bf16 planners): Mseg holds the hi / lo bf16 M of scan_m_bf16_index
+// and the products run as three bf16 MFMAs; elt 0: fp32 M at scan_m_index.
+hipError_t launch_scan(int elt, const ScanDesc *descs, int32_t ndesc, int32_t H, const float *Mseg,
                        const float *Stseg, const float *init, float *sin, hipStream_t s);
 
 // The scan of one chain of nsteps row-major pairs (M [nsteps, H, dk, dk],

@@ -1243,16 +1243,32 @@ __global__ __launch_bounds__(k2_threads(BV, NCT)) void k2_kernel(
     fp = base + ((int64_t)cd.final_idx * H + h) * (kD * kD);
   }
   if (fp) {
-    const bool scan_order = MODE == 1 && mpart && m_scan_order;
+    const int order = (MODE == 1 && mpart) ? m_scan_order : 0;
+    if (order == 2) { // hi / lo bf16 for the bf16 scan
+      bf16 *fb = reinterpret_cast<bf16 *>(fp);
 #pragma unroll
-    for (int c = 0; c < NCT; ++c)
+      for (int c = 0; c < NCT; ++c)
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct)
+        for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = srow(16 * ct + 4 * lg + i), col = wcol + 16 * c;
-          fp[scan_order ? scan_m_index(r, col) : r * kD + col] = S[c][ct][i];
-        }
+          for (int i = 0; i < 4; ++i) {
+            const int r = srow(16 * ct + 4 * lg + i), col = wcol + 16 * c;
+            const int x = scan_m_bf16_index(r, col);
+            const bf16 hi = static_cast<bf16>(S[c][ct][i]);
+            fb[x] = hi;
+            fb[kD * kD + x] = static_cast<bf16>(S[c][ct][i] - static_cast<float>(hi));
+          }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = srow(16 * ct + 4 * lg + i), col = wcol + 16 * c;
+            fp[order == 1 ? scan_m_index(r, col) : r * kD + col] = S[c][ct][i];
+          }
+    }
   }
 }
 
@@ -1436,6 +1452,169 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanDesc *__restri
 }
 
 // ---------------------------------------------------------------------------
+// The planner scan of bf16 calls.  Same recurrence, grid and state handling
+// as scan_kernel; the product M_j Sin[j] runs on v_mfma_f32_16x16x32_bf16.
+// M = M_hi + M_lo as the segment pass writes it (scan_m_bf16_index), and the
+// state is split into three bf16 parts x = x_hi + x_mid + x_lo, exactly (each
+// part takes the next 8 significant bits).  Then
+//   M S ~= M_hi (S_hi + S_mid + S_lo) + M_lo S_hi,
+// four bf16 MFMAs (16 cycles each) per 32-wide k-step in place of eight fp32
+// ones (32 cycles each).  The terms left out, M_lo (S_mid + S_lo) and the
+// remainder of M below M_lo, are of relative size 2^-16 of the product, far
+// below the bf16 rounding of the chain's own products; M = I (no decay, no
+// writes) carries the state exactly.  Sums and the state stay fp32: the
+// thread that forms an entry of the next state splits it once into its
+// LDS copy, where the B operands are read.  With the products this cheap a
+// step is bound by the latency of its M loads, so the workgroup has 8 waves
+// (16 state rows each, 32 VGPRs of M per lane and step) and keeps three
+// steps' inputs in registers, each loaded two steps before its use (no L2
+// warm-up loads: with the loads that far ahead they only lengthened the
+// in-order wait for them, 101 against 72 us for 63 steps of 12 heads).
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kScanBf16Threads = 512; // 8 waves: wave w owns state rows 16 w .. + 15
+constexpr int kScanBf16Ahead = 2;     // steps between a load of M_j and its use
+
+struct ScanInBf16 {
+  bf16x8 a[4][2]; // a[s][p]: part p (hi, lo) of M[16w + lane % 16][32 s + 8 kq .. + 7]
+  float st[4];    // st[e] = S~[16w + 4 kq + e][col0 + lane % 16]
+};
+
+constexpr int kScanLdB = kD + 8; // LDS row stride (bf16) of a transposed state part
+
+// x = hi + mid + lo exactly, each part bf16 (round to nearest)
+__device__ __forceinline__ void split3(float x, bf16 &hi, bf16 &mid, bf16 &lo) {
+  hi = static_cast<bf16>(x);
+  const float r = x - static_cast<float>(hi);
+  mid = static_cast<bf16>(r);
+  lo = static_cast<bf16>(r - static_cast<float>(mid));
+}
+
+} // namespace
+
+__global__ __launch_bounds__(kScanBf16Threads) void scan_bf16_kernel(
+    const ScanDesc *__restrict__ descs, int32_t ndesc, int32_t H, const bf16 *__restrict__ Mseg,
+    const float *__restrict__ Stseg, const float *__restrict__ init, float *__restrict__ sin) {
+  static_assert(kScanBV == 16, "thread map assumes 16 columns");
+  constexpr int NCB = kD / kScanBV;
+  // column blocks of one (sequence, head) 8 workgroup ids apart: one XCD
+  const int grp = blockIdx.x / (8 * NCB), rem = blockIdx.x - grp * 8 * NCB;
+  const int pair = 8 * grp + (rem & 7);
+  if (pair >= ndesc * H)
+    return;
+  const int di = pair / H, h = pair - di * H;
+  const ScanDesc d = descs[di];
+  const int col0 = (rem >> 3) * kScanBV;
+
+  // the state's three parts, transposed: [buf][part][col][row]
+  __shared__ __attribute__((aligned(16))) bf16 sB[2][3][kScanBV][kScanLdB];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = lane & 15, kq = lane >> 4;
+  const int64_t mat = (int64_t)kD * kD;
+
+  // entry state of segment 0: init (or zero) -> LDS and Sin[sin0]
+  {
+    const int m = tid >> 2, c0 = (tid & 3) * 4;
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if (d.init_idx >= 0)
+      x = *reinterpret_cast<const f32x4 *>(init + ((int64_t)d.init_idx * H + h) * mat +
+                                           m * kD + col0 + c0);
+    *reinterpret_cast<f32x4 *>(sin + ((int64_t)d.sin0 * H + h) * mat + m * kD + col0 + c0) = x;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      bf16 hi, mid, lo;
+      split3(x[c], hi, mid, lo);
+      sB[0][0][c0 + c][m] = hi;
+      sB[0][1][c0 + c][m] = mid;
+      sB[0][2][c0 + c][m] = lo;
+    }
+  }
+
+  const int nstep = d.nseg - 1;
+  // pair j's slot: the hi / lo bf16 M (2 dk^2 elements, the 64 KiB of one
+  // fp32 matrix) and S~
+  auto m_at = [&](int j) { return Mseg + ((int64_t)(d.pair0 + j) * H + h) * (2 * mat); };
+  auto st_at = [&](int j) { return Stseg + ((int64_t)(d.pair0 + j) * H + h) * mat; };
+  // the inputs of step j (clamped to the last)
+  auto load = [&](ScanInBf16 &in, int j) {
+    j = min(j, nstep - 1);
+    const bf16 *mj = m_at(j);
+    // block ((w / 2) * 4 + s) * 2 + w % 2 of each part (scan_m_bf16_index)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        in.a[s][p] = *reinterpret_cast<const bf16x8 *>(
+            mj + p * mat + ((((w >> 1) * 4 + s) * 2 + (w & 1)) * 64 + lane) * 8);
+    const float *sr = st_at(j) + (16 * w + 4 * kq) * kD + col0 + n;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      in.st[e] = sr[e * kD];
+  };
+  // step j: reads sB[j & 1] and the inputs in `cur`, writes sB[(j + 1) & 1]
+  // and Sin[sin0 + j + 1]; `ahead` takes the inputs of step j + kScanBf16Ahead
+  auto step = [&](const ScanInBf16 &cur, ScanInBf16 &ahead, int j) {
+    // B operands: rows 32 s + 8 kq .. + 7 of column n, each part
+    Frag<bf16> b[4][3];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+        b[s][p].v = *reinterpret_cast<const bf16x8 *>(&sB[j & 1][p][n][32 * s + 8 * kq]);
+    load(ahead, j + kScanBf16Ahead);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      Frag<bf16> ah, al;
+      ah.v = cur.a[s][0];
+      al.v = cur.a[s][1];
+      mma(acc, ah, b[s][0]);
+      mma(acc, ah, b[s][1]);
+      mma(acc, ah, b[s][2]);
+      mma(acc, al, b[s][0]);
+    }
+    float *dst = sin + ((int64_t)(d.sin0 + j + 1) * H + h) * mat + col0 + n;
+    const int r0 = 16 * w + 4 * kq;
+    bf16x4 ph, pm, pl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += cur.st[e];
+      bf16 hi, mid, lo;
+      split3(acc[e], hi, mid, lo);
+      ph[e] = hi;
+      pm[e] = mid;
+      pl[e] = lo;
+      dst[(r0 + e) * kD] = acc[e];
+    }
+    *reinterpret_cast<bf16x4 *>(&sB[(j + 1) & 1][0][n][r0]) = ph;
+    *reinterpret_cast<bf16x4 *>(&sB[(j + 1) & 1][1][n][r0]) = pm;
+    *reinterpret_cast<bf16x4 *>(&sB[(j + 1) & 1][2][n][r0]) = pl;
+    __syncthreads();
+  };
+
+  // a ring of three input sets: step j reads set j % 3 and fills set
+  // (j + 2) % 3, the one step j - 1 read
+  static_assert(kScanBf16Ahead == 2, "the ring below holds three input sets");
+  ScanInBf16 in0, in1, in2;
+  if (nstep > 0) { // (no pairs: only the entry state is written)
+    load(in0, 0);
+    load(in1, 1);
+  }
+  __syncthreads();
+  int j = 0;
+  for (; j + 3 <= nstep; j += 3) {
+    step(in0, in2, j);
+    step(in1, in0, j + 1);
+    step(in2, in1, j + 2);
+  }
+  if (j < nstep)
+    step(in0, in2, j);
+  if (j + 1 < nstep)
+    step(in1, in0, j + 1);
+}
+
+// ---------------------------------------------------------------------------
 // Output norm and gate as a pass of its own over o, in place ("Kimi K3.1 Pro
 // 架构完全拆解" §3.3): o <- sigmoid(gate) w o / sqrt(mean(o^2) + eps) per
 // (token, head) row.  For calls whose state chain runs 64-column blocks
@@ -1565,7 +1744,7 @@ hipError_t launch_k2(int elt, int mode, const ChainDesc *chains, int32_t nchains
                      const Epilogue &epi, hipStream_t s) {
   if (nchains == 0)
     return hipSuccess;
-  const int32_t mso = mode == 1 && m_scan_order;
+  const int32_t mso = mode == 1 ? m_scan_order : 0;
   const int64_t width = mode == 1 ? 2 * kD : kD;
   const int64_t wide_groups = (int64_t)nchains * H * (width / kBVWide);
   const uint8_t *w = (const uint8_t *)ws;
@@ -1589,14 +1768,19 @@ hipError_t launch_k2(int elt, int mode, const ChainDesc *chains, int32_t nchains
   return hipGetLastError();
 }
 
-hipError_t launch_scan(const ScanDesc *descs, int32_t ndesc, int32_t H, const float *Mseg,
-                       const float *Stseg, const float *init, float *sin, hipStream_t s) {
+hipError_t launch_scan(int elt, const ScanDesc *descs, int32_t ndesc, int32_t H,
+                       const float *Mseg, const float *Stseg, const float *init, float *sin,
+                       hipStream_t s) {
   if (ndesc == 0)
     return hipSuccess;
   const int64_t pairs = (int64_t)ndesc * H;
   const unsigned grid = (unsigned)((pairs + 7) / 8 * 8 * (kD / kScanBV));
-  scan_kernel<false><<<grid, kThreads, 0, s>>>(descs, ScanDesc{}, ndesc, H, Mseg, Stseg, init,
-                                               sin);
+  if (elt == 1)
+    scan_bf16_kernel<<<grid, kScanBf16Threads, 0, s>>>(descs, ndesc, H, (const bf16 *)Mseg,
+                                                        Stseg, init, sin);
+  else
+    scan_kernel<false><<<grid, kThreads, 0, s>>>(descs, ScanDesc{}, ndesc, H, Mseg, Stseg, init,
+                                                 sin);
   return hipGetLastError();
 }
 
