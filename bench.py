@@ -74,8 +74,8 @@ def stored_counters(workload: str):
 
 COPY_PROBE_FLOATS = 256 << 20   # 1 GiB fp32 read + 1 GiB written by the calibration copy
 # kernels of this library, by the part of their names that identifies them
-LIB_KERNELS = ("prep_kernel", "k1_kernel", "k2_kernel", "scan_kernel", "fused_kernel",
-               "out_norm_gate_kernel", "decode_kernel")
+LIB_KERNELS = ("prep_kernel", "k1_kernel", "k2_kernel", "scan_kernel", "scan_bf16_kernel",
+               "fused_kernel", "out_norm_gate_kernel", "decode_kernel")
 
 
 def probe_dispatches(path, counters):
@@ -109,6 +109,50 @@ def probe_window(disp):
     call = [(next(t for t in LIB_KERNELS if t in n), c) for n, c in disp[i + 1:lib[-1] + 1]
             if any(t in n for t in LIB_KERNELS)]
     return i, call
+
+
+def traffic_probe(kda, wl, name, dev, path="auto"):
+    """One prefill call and one decode step bracketed by a plain elementwise
+    copy of known size, for rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE):
+    the copy's counter reading calibrates the counters to bytes."""
+    import torch
+    w = wl.WORKLOADS[name]
+    d = wl.prefill_case(w, device=dev)
+    cu = d["cu"]
+    N, H = len(w.lengths), w.H
+    T = int(cu[-1])
+    o = torch.empty((T, H, D), dtype=w.dtype, device=dev)
+    fin = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(kda.prefill_workspace_size(cu, H, w.dtype, 0, path=path), 1),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu,
+                          initial_state=d["init"], o=o, final_state=fin, workspace=ws, path=path)
+
+    step()                                   # warm (first-touch, schedule upload)
+    torch.cuda.synchronize(dev)
+    src = torch.ones(COPY_PROBE_FLOATS, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize(dev)
+    torch.mul(src, 1.0, out=dst)             # the calibration copy
+    torch.cuda.synchronize(dev)
+    del src, dst
+    step()                                   # the measured prefill call
+    torch.cuda.synchronize(dev)
+    del d, o, fin, ws
+    torch.cuda.empty_cache()
+    wd = wl.WORKLOADS["decode_f32_N256_H96_x64"]
+    dd = wl.decode_case(wd, device=dev)
+    od = torch.empty((wd.lengths[0], wd.H, D), dtype=wd.dtype, device=dev)
+    for _ in range(2):                       # warm, then the measured step
+        kda.decode_step(dd["state"], dd["q"][0], dd["k"][0], dd["v"][0], dd["g"][0],
+                        dd["beta"][0], o=od)
+        torch.cuda.synchronize(dev)
+    chunk_heads = sum((L + C - 1) // C for L in w.lengths) * H
+    print(json.dumps({"probe": name, "copy_bytes_read": 4 * COPY_PROBE_FLOATS,
+                      "copy_bytes_written": 4 * COPY_PROBE_FLOATS,
+                      "chunk_heads": chunk_heads}), flush=True)
 
 
 def traffic_from_counters(fetch_csv, write_csv, workload, command):

@@ -69,3 +69,21 @@ def test_probe_window_refuses_a_run_without_the_copy(tmp_path):
     _write(p, [(n, {"FETCH_SIZE": v}) for n, v in rows], ["FETCH_SIZE"])
     with pytest.raises((AssertionError, StopIteration, IndexError)):
         bench.probe_window(bench.probe_dispatches(p, ("FETCH_SIZE",)))
+
+
+def test_probe_window_counts_the_bf16_planner_scan(tmp_path):
+    # the bf16 planner's scan kernel has a name of its own
+    rows = PROBE[:5] + [("void kda::prep_kernel<false>(...)", 1.0),
+                        ("void kda::k2_kernel<bf16, 1, 64, 1, 1, false>(...)", 2.0),
+                        ("kda::scan_bf16_kernel(kda::ScanDesc const*, ...)", 3.0),
+                        ("void kda::k2_kernel<bf16, 0, 128, 1, 2, false>(...)", 4.0)] + PROBE[7:]
+    p = str(tmp_path / "c.csv")
+    _write(p, [(n, {"FETCH_SIZE": v}) for n, v in rows], ["FETCH_SIZE"])
+    _, call = bench.probe_window(bench.probe_dispatches(p, ("FETCH_SIZE",)))
+    assert [t for t, _ in call] == ["prep_kernel", "k2_kernel", "scan_bf16_kernel", "k2_kernel"]
+    assert sum(c["FETCH_SIZE"] for _, c in call) == pytest.approx(10.0)
+
+
+def test_traffic_probe_entry_exists():
+    # --traffic-probe is the command every committed counter summary cites
+    assert callable(bench.traffic_probe)
