@@ -35,13 +35,40 @@ FLOP_PER_CHUNK_HEAD = 12 * C ** 3 + 8 * C ** 2 * D + 6 * C * D ** 2  # 13,631,48
 DECODE_BYTES_PER_HEAD_TOKEN = 8 * D * D                              # fp32 state read + write
 
 
+def strip_c_comments(text: str) -> str:
+    """C / C++ source without its comments and with runs of blank space
+    collapsed (string and character literals kept as they are)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code: a counter summary taken on other
+    code is not reported, one taken before a comment-only edit still is."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_delta_rule_19_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
             h.update(name.encode())
-            h.update(f.read())
+            h.update(strip_c_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

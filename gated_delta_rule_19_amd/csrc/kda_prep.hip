@@ -15,7 +15,8 @@
 // Record, bf16 unless stated:
 //   Q_decay [C][D], K_decay [C][D]        columns = channels
 //   K_restore^T [D][C]                    row p = channel kperm(p), column kperm(token)
-//   INV Diag(beta) [C][C], M_qk [C][C]    column kperm(token)
+//   INV Diag(beta) [C][C], M_qk [C][C]    column kperm(token); lower triangular, so
+//                                         only 6 of their 8 fragment blocks are stored
 //   a_last [D] fp32                       entry p = channel kperm(p)
 // The state kernel keeps channel kperm(p) in row p of its state, so each of
 // these is an MFMA operand for it as stored.  The matrices are stored as

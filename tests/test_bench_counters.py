@@ -87,3 +87,11 @@ def test_probe_window_counts_the_bf16_planner_scan(tmp_path):
 def test_traffic_probe_entry_exists():
     # --traffic-probe is the command every committed counter summary cites
     assert callable(bench.traffic_probe)
+
+
+def test_source_hash_ignores_comments_only():
+    code = "int a = 1;\nchar c = '\\\\'; // note\n/* block */ const char *s = \"// kept\";\n"
+    assert bench.strip_c_comments(code) == \
+        "int a = 1; char c = '\\\\'; const char *s = \"// kept\";"
+    assert bench.strip_c_comments("x = 1; // a\n") == bench.strip_c_comments("x  =  1;\n// b")
+    assert bench.strip_c_comments("x = 1;") != bench.strip_c_comments("x = 2;")
