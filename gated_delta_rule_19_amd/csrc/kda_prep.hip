@@ -116,9 +116,11 @@ __host__ __device__ constexpr int tri_piece(int base, int r, int g) {
 // Record stores go through one buffer resource per item (base address in
 // scalar registers), each lane adding a 32-bit offset: a 64-bit address per
 // lane and store would take two vector registers.  Offsets are in bf16
-// elements.
+// elements.  The records are read only by the next kernel, so they are
+// stored non-temporal (the whole 8192 x 96 call measured 0.605 -> 0.595 ms).
+constexpr int kNt = 2; // cache-policy bits of a buffer access: nt
 __device__ __forceinline__ void rec_store8(__amdgpu_buffer_rsrc_t r, int e, bf16x8 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, 2 * e, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, 2 * e, 0, kNt);
 }
 __device__ __forceinline__ void rec_store8(__amdgpu_buffer_rsrc_t r, int e, const f32x4 &lo,
                                            const f32x4 &hi) {
