@@ -1465,16 +1465,19 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(const ScanDesc *__restri
 // writes) carries the state exactly.  Sums and the state stay fp32: the
 // thread that forms an entry of the next state splits it once into its
 // LDS copy, where the B operands are read.  With the products this cheap a
-// step is bound by the latency of its M loads, so the workgroup has 8 waves
-// (16 state rows each, 32 VGPRs of M per lane and step) and keeps three
-// steps' inputs in registers, each loaded two steps before its use (no L2
-// warm-up loads: with the loads that far ahead they only lengthened the
-// in-order wait for them, 101 against 72 us for 63 steps of 12 heads).
+// step is bound by the latency of its M loads, so the workgroup has 8
+// compute waves (16 state rows each, 32 VGPRs of M per lane and step) that
+// keep three steps' inputs in registers, each loaded two steps before its
+// use, and a ninth wave that warms L2 with the lines of later steps.  Its
+// loads sit in its own in-order memory counter: warm-up loads issued by the
+// compute waves themselves lengthened their waits (101 against 72 us for 63
+// steps of 12 heads).
 // ---------------------------------------------------------------------------
 namespace {
 
-constexpr int kScanBf16Threads = 512; // 8 waves: wave w owns state rows 16 w .. + 15
+constexpr int kScanBf16Threads = 576; // 8 waves: wave w owns state rows 16 w .. + 15; wave 8 warms L2
 constexpr int kScanBf16Ahead = 2;     // steps between a load of M_j and its use
+constexpr int kScanBf16Warm = 3;      // steps between wave 8's L2 warm-up of a step and its use
 
 struct ScanInBf16 {
   bf16x8 a[4][2]; // a[s][p]: part p (hi, lo) of M[16w + lane % 16][32 s + 8 kq .. + 7]
@@ -1509,12 +1512,13 @@ __global__ __launch_bounds__(kScanBf16Threads) void scan_bf16_kernel(
 
   // the state's three parts, transposed: [buf][part][col][row]
   __shared__ __attribute__((aligned(16))) bf16 sB[2][3][kScanBV][kScanLdB];
+  __shared__ __attribute__((aligned(16))) float sWarm[64]; // wave 8's loads land here, unread
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 15, kq = lane >> 4;
   const int64_t mat = (int64_t)kD * kD;
 
   // entry state of segment 0: init (or zero) -> LDS and Sin[sin0]
-  {
+  if (w < 8) {
     const int m = tid >> 2, c0 = (tid & 3) * 4;
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
     if (d.init_idx >= 0)
@@ -1597,11 +1601,40 @@ __global__ __launch_bounds__(kScanBf16Threads) void scan_bf16_kernel(
   // (j + 2) % 3, the one step j - 1 read
   static_assert(kScanBf16Ahead == 2, "the ring below holds three input sets");
   ScanInBf16 in0, in1, in2;
-  if (nstep > 0) { // (no pairs: only the entry state is written)
+  if (w < 8 && nstep > 0) { // (no pairs: only the entry state is written)
     load(in0, 0);
     load(in1, 1);
   }
   __syncthreads();
+  if (w == 8) {
+    // L2 warm-up, kScanBf16Warm steps ahead of use: this column block's
+    // eighth of the M slot (one 128-byte line per lane) and its 16 columns
+    // of S~ (64 bytes of each row), as loads into an LDS area nobody reads,
+    // so that they sit in this wave's memory counter only.  One barrier per
+    // step, as the compute waves; the loads are waited for before the wave
+    // ends (they write this workgroup's LDS).
+    const int cb = rem >> 3;
+    auto warm = [&](int jw) {
+      const __amdgpu_buffer_rsrc_t rm = buffer_rsrc(m_at(jw), (uint32_t)(4 * mat));
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(st_at(jw), (uint32_t)(4 * mat));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rm, (__attribute__((address_space(3))) void *)sWarm, 4, (cb * 64 + lane) * 128, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void *)sWarm, 4,
+            ((64 * r + lane) * kD + col0) * 4, 0, 0, 0);
+    };
+    for (int jw = 2; jw < min(kScanBf16Warm, nstep); ++jw)
+      warm(jw);
+    for (int jj = 0; jj < nstep; ++jj) {
+      if (jj + kScanBf16Warm < nstep)
+        warm(jj + kScanBf16Warm);
+      asm volatile("s_barrier" ::: "memory");
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    return;
+  }
   int j = 0;
   for (; j + 3 <= nstep; j += 3) {
     step(in0, in2, j);
