@@ -410,11 +410,19 @@ def time_replay(kda, wl, dev, W=4, P=5, calls=16):
 
     us_snap = timed(snapshot_window)
     gbs = DECODE_BYTES_PER_HEAD_TOKEN * N * H / (us * 1e-6) / 1e9
+    # every byte the call must move: the state read and written, the accepted
+    # cached tokens' k, v, g and beta, the new tokens' q, k, v, g and beta,
+    # and the new tokens' outputs
+    es = torch.tensor([], dtype=w.dtype).element_size()
+    token_bytes = H * es * (int(acc_np.sum()) * (3 * D + 1) + N * P * (4 * D + 1) + N * P * D)
+    all_bytes = DECODE_BYTES_PER_HEAD_TOKEN * N * H + token_bytes
     del c, n, cached, new, state, o, toks, snaps
     torch.cuda.empty_cache()
     return {"shape": "N=%d H=%d fp32, W=%d cached, P=%d new" % (N, H, W, P),
             "accepted_mean": float(acc_np.mean()), "us_per_call": us,
             "state_GB_per_s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
+            "bytes_per_call": all_bytes,
+            "hbm_frac_all_bytes": all_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
             "snapshot_baseline_us": us_snap, "speedup_vs_snapshot": us_snap / us}
 
 
@@ -594,10 +602,12 @@ def main():
     if not args.no_decode:
         rep = time_replay(kda, wl, dev)
         print("decode replay (%s, mean accepted %.2f): %.1f us/call, %.0f GB/s state (%.1f%% "
-              "of HBM peak); snapshot rollback %.1f us (x%.2f)"
+              "of HBM peak; %.1f%% with the token inputs and outputs); snapshot rollback "
+              "%.1f us (x%.2f)"
               % (rep["shape"], rep["accepted_mean"], rep["us_per_call"], rep["state_GB_per_s"],
-                 100 * rep["hbm_frac"], rep["snapshot_baseline_us"],
-                 rep["speedup_vs_snapshot"]), file=sys.stderr, flush=True)
+                 100 * rep["hbm_frac"], 100 * rep["hbm_frac_all_bytes"],
+                 rep["snapshot_baseline_us"], rep["speedup_vs_snapshot"]),
+              file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.workload)
