@@ -104,13 +104,14 @@ constexpr int kK2ThroughputBV = 64;
 constexpr int kK2ThroughputNCT = 1;
 constexpr int k2_threads(int bv, int nct) { return bv / (16 * nct) * 64; }
 constexpr int kComputeUnits = 256;
-// Column block of the planner scan kernel.
+// Column block of the planner scan kernels.
 constexpr int kScanBV = 16;
 
 // Position of M[r][m] (r: output row, m: reduction index) in the scan order
-// the planner's segment pass writes its transition matrices in: 1 KiB blocks,
-// one per (wave w = r / 32, k-group i = m / 16, row tile t = r / 16 % 2) in
-// that order, each holding the 64 lanes' A operands of the scan kernel's
+// the planner's segment pass writes its transition matrices in for fp32
+// calls: 1 KiB blocks, one per (wave w = r / 32, k-group i = m / 16, row
+// tile t = r / 16 % 2) in that order, each holding the 64 lanes' A operands
+// of the fp32 scan kernel's
 // v_mfma_f32_16x16x4f32 products (lane 16 (m / 4 % 4) + r % 16, four
 // consecutive reduction indices per lane).  One scan load is then 1 KiB
 // contiguous.

@@ -1277,7 +1277,8 @@ __global__ __launch_bounds__(k2_threads(BV, NCT)) void k2_kernel(
 //   Sin[0] = S_0,   Sin[j+1] = S~_j + M_j Sin[j]
 // ("部署 Kimi K3：从 KDA Kernel 到 Fleet 调度", §二: S = S~ + M S_in, pairs
 // compose associatively).  Serial over segments, parallel over heads and
-// column blocks of kScanBV = 16 state columns, fp32 throughout.
+// column blocks of kScanBV = 16 state columns, fp32 throughout (fp32 calls
+// and kda_segment_scan; bf16 calls use scan_bf16_kernel below).
 //
 // One workgroup of four waves per (sequence, head, column block).  Each step
 // is a 128 x 16 x 128 product on v_mfma_f32_16x16x4f32: wave w owns output
