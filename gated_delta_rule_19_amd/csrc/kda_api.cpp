@@ -37,8 +37,11 @@ namespace {
 constexpr int64_t kAutoMinChains = 64;
 constexpr int64_t kAutoSegments = 64;
 constexpr int64_t kAutoMinSegChunks = 4;
-// Fewest (sequence, head) chains for the fused prefill kernel.
+// Fewest (sequence, head) chains for the fused prefill kernel, and fewest
+// (segment, head) chains of a planner split for its segment pass and replay
+// to run on the fused kernel too.
 constexpr int64_t kFusedMinChainHeads = 512;
+constexpr int64_t kFusedSplitMinChainHeads = 256;
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -85,7 +88,10 @@ struct Plan {
   int64_t npairs = 0, nsin = 0;
   // bf16 without a planner split runs the fused kernel: no chunk-prep records
   bool fused = false;
-  // the fused path was asked for a call it cannot run (fp32, or split)
+  // bf16 with a planner split whose segment pass and replay run on the fused
+  // kernel: no chunk-prep records either
+  bool fused_split = false;
+  // the fused path was asked for a call it cannot run (fp32)
   bool path_unsupported = false;
   // workspace layout
   size_t off_chunks = 0, off_chains = 0, off_seg = 0, off_scan = 0, table_bytes = 0;
@@ -104,7 +110,7 @@ void layout(Plan &p, int32_t H, size_t es) {
   o = align_up(o + p.scans.size() * sizeof(ScanDesc));
   p.table_bytes = o;
   p.off_rec = o;
-  if (!p.fused)
+  if (!p.fused && !p.fused_split)
     o = align_up(o + p.chunks.size() * (size_t)H * k1_record_bytes(es));
   const size_t mat = (size_t)kD * kD * sizeof(float);
   p.off_M = o;
@@ -171,8 +177,7 @@ void assign_ckpts(ChainDesc &c, const SeqCkpts &k, int64_t s0, int64_t cnt, int6
   c.ckpt_idx = (int32_t)(idx0 + j0);
 }
 
-// path: KDA_PATH_AUTO, KDA_PATH_TWO_KERNEL or KDA_PATH_FUSED (the caller has
-// checked that a fused request is bf16 and unsplit)
+// path: KDA_PATH_AUTO, KDA_PATH_TWO_KERNEL or KDA_PATH_FUSED
 bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_hint,
                         bool has_init, bool has_final, size_t es, Plan &p,
                         const int64_t *pos0 = nullptr, int64_t align = 0,
@@ -180,8 +185,8 @@ bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_h
   int64_t ckpt_base = 0; // first checkpoint index of the current sequence
   if (!cu || cu[0] != 0)
     return false;
-  // the fused kernel takes whole sequences: asking for it turns the
-  // automatic split off (an explicit split is refused below)
+  // asking for the fused kernel turns the automatic split off (an explicit
+  // split runs the planner on it)
   if (path == KDA_PATH_FUSED && split_hint == 0)
     split_hint = 1;
   for (int32_t n = 0; n < N; ++n)
@@ -231,17 +236,20 @@ bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_h
   auto longer = [](const ChainDesc &a, const ChainDesc &b) { return a.ntok > b.ntok; };
   std::stable_sort(p.chains.begin(), p.chains.end(), longer);
   std::stable_sort(p.segchains.begin(), p.segchains.end(), longer);
-  // bf16 without a planner split and with enough chains to give every
-  // compute unit a few (sequence, head) pairs: chunk prep and state carry
-  // run fused in one kernel and no chunk-prep records go through memory.
-  // With fewer chains the chunk-parallel prep kernel keeps the whole chip
-  // busy and the two-kernel path is faster.
-  const bool can_fuse = es == 2 && p.segchains.empty();
+  // bf16 with enough chains to give every compute unit a few (sequence or
+  // segment, head) pairs: chunk prep and state carry run fused in one kernel
+  // and no chunk-prep records go through memory (with a split, in the
+  // segment pass and in the replay).  With fewer chains the chunk-parallel
+  // prep kernel keeps the whole chip busy and the two-kernel path is faster.
+  const bool split = !p.segchains.empty();
   if (path == KDA_PATH_FUSED) {
-    p.fused = can_fuse;
-    p.path_unsupported = !can_fuse;
+    p.fused = es == 2 && !split;
+    p.fused_split = es == 2 && split;
+    p.path_unsupported = es != 2;
   } else if (path == KDA_PATH_AUTO) {
-    p.fused = can_fuse && (int64_t)p.chains.size() * H >= kFusedMinChainHeads;
+    p.fused = es == 2 && !split && (int64_t)p.chains.size() * H >= kFusedMinChainHeads;
+    p.fused_split =
+        es == 2 && split && (int64_t)p.segchains.size() * H >= kFusedSplitMinChainHeads;
   }
   layout(p, H, es);
   return true;
@@ -461,8 +469,25 @@ kda_status prefill_impl(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_
   if (p.fused) {
     if (e == hipSuccess)
       e = launch_fused((const ChainDesc *)(ws + p.off_chains), (int32_t)p.chains.size(), H, q,
-                        k, v, g, beta, o, initial_state, final_state,
+                        k, v, g, beta, o, initial_state, nullptr, final_state,
                         ckpt_align ? ckpt : nullptr, s, pro, epi);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  }
+  if (p.fused_split) {
+    // segment pass, scan and replay, the passes that carry a state on the
+    // fused kernel
+    if (e == hipSuccess)
+      e = launch_fused_seg((const ChainDesc *)(ws + p.off_seg), (int32_t)p.segchains.size(), H,
+                           k, v, g, beta, (float *)(ws + p.off_St), (float *)(ws + p.off_M), s,
+                           pro);
+    if (e == hipSuccess)
+      e = launch_scan(elt, (const ScanDesc *)(ws + p.off_scan), (int32_t)p.scans.size(), H,
+                      (const float *)(ws + p.off_M), (const float *)(ws + p.off_St),
+                      initial_state, (float *)(ws + p.off_Sin), s);
+    if (e == hipSuccess)
+      e = launch_fused((const ChainDesc *)(ws + p.off_chains), (int32_t)p.chains.size(), H, q,
+                        k, v, g, beta, o, initial_state, (const float *)(ws + p.off_Sin),
+                        final_state, ckpt_align ? ckpt : nullptr, s, pro, epi);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
   }
   if (e == hipSuccess)
@@ -716,7 +741,7 @@ kda_status kda_chunk_prefill_noalloc(int32_t num_seqs, const int64_t *cu_seqlens
   if (e == hipSuccess)
     e = launch_fused((const ChainDesc *)((uint8_t *)scr + p.off_chains),
                       (int32_t)p.chains.size(), H, q, k, v, g, beta, o, initial_state,
-                      final_state, nullptr, s);
+                      nullptr, final_state, nullptr, s);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -190,17 +190,28 @@ __device__ __forceinline__ int vst_off(int row, int col) {
 
 } // namespace
 
+// MODE 0: prefill / replay: o, exit states to final_state, checkpoints.
+//   Entry states: init[init_idx] (init_idx >= 0), sin[-2 - init_idx]
+//   (init_idx <= -2: the planner's scanned entry states), else zero.
+// MODE 1: the planner's segment pass: each state wave carries its 32
+//   columns of S~ (from 0, values V) and the same 32 columns of M (from the
+//   identity, values 0): four column tiles, no o.  S~ leaves to final_state
+//   (row-major), M to m_out as hi / lo bf16 at scan_m_bf16_index.  The prep
+//   waves build no query operands.
 // PRO: the decay gate from logits and the q / k L2 norm run in the prep
 // (which of them is decided by A_log != null and qk_eps > 0); EPI: o leaves
 // through the output norm and gate.
-template <bool PRO, bool EPI>
+template <int MODE, bool PRO, bool EPI>
 __global__ __launch_bounds__(kFusedThreads) void fused_kernel(
     const ChainDesc *__restrict__ chains, int32_t H, const bf16 *__restrict__ q,
     const bf16 *__restrict__ k, const bf16 *__restrict__ v, const bf16 *__restrict__ g,
     const bf16 *__restrict__ beta, bf16 *__restrict__ o, const float *__restrict__ init,
-    float *__restrict__ final_state, float *__restrict__ ckpt, const float *__restrict__ A_log,
-    float g_min, float qk_eps, const bf16 *__restrict__ ogate, const float *__restrict__ onw,
-    float oeps) {
+    const float *__restrict__ sin, float *__restrict__ final_state, float *__restrict__ m_out,
+    float *__restrict__ ckpt, const float *__restrict__ A_log, float g_min, float qk_eps,
+    const bf16 *__restrict__ ogate, const float *__restrict__ onw, float oeps) {
+  static_assert(MODE == 0 || !EPI, "the segment pass writes no o");
+  constexpr bool kQ = MODE == 0; // query operands (Q_decay, M_qk) and o
+  constexpr int NC = MODE == 0 ? 2 : 4; // 16-column state tiles per state wave
   __shared__ __attribute__((aligned(1024))) FusedSmem sm;
 
   const int chain_i = blockIdx.x / H, h = blockIdx.x - chain_i * H;
@@ -229,18 +240,25 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(
   if (wv < 4) {
     // =========================== state waves ===========================
     const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-    const int col0 = 32 * wv; // columns col0 + 16 c + lr, c = 0, 1
-    f32x4 S[2][8];            // rows p = 16 ct + 4 lg + i: channel kperm(p)
+    // columns col0 + 16 (c % 2) + lr of S (MODE 0) or of S~ (c < 2) and M
+    // (c >= 2, MODE 1)
+    const int col0 = 32 * wv;
+    f32x4 S[NC][8]; // rows p = 16 ct + 4 lg + i: channel kperm(p)
     {
-      const float *ip = cd.init_idx >= 0 ? init + ((int64_t)cd.init_idx * H + h) * (kD * kD)
-                                         : nullptr;
+      const float *ip = nullptr;
+      if (MODE == 0 && cd.init_idx >= 0)
+        ip = init + ((int64_t)cd.init_idx * H + h) * (kD * kD);
+      else if (MODE == 0 && cd.init_idx <= -2)
+        ip = sin + ((int64_t)(-2 - cd.init_idx) * H + h) * (kD * kD);
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            S[c][ct][i] = ip ? ip[kperm(16 * ct + 4 * lg + i) * kD + col0 + 16 * c + lr] : 0.f;
+          for (int i = 0; i < 4; ++i) {
+            const int ch = kperm(16 * ct + 4 * lg + i), col = col0 + 16 * (c & 1) + lr;
+            S[c][ct][i] = c >= 2 ? (ch == col ? 1.f : 0.f) : (ip ? ip[ch * kD + col] : 0.f);
+          }
     }
     uint8_t *vs = reinterpret_cast<uint8_t *>(&sm.vst[wv][0]);
     // this wave's columns of v for chunk ch, straight into its LDS copy:
@@ -272,82 +290,120 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(
         const int ln = opaque_lane(), llr = ln & 15, llg = ln >> 4;
         auto frag = [&](const bf16 *blk) { return load_frag(blk + ln * 8); };
         // W = K_decay S and O^T = S^T Q_decay^T (K = channels; the packed
-        // state is the B operand of the first and the A operand of the second)
-        Frag<bf16> bs[2][4];
+        // state is the B operand of the first and the A operand of the second),
+        // then U by substitution.  MODE 1 runs W, the right-hand side and the
+        // substitution for its S~ tiles and then for its M tiles (holding the
+        // W of all four at once would exceed the registers).
+        [[maybe_unused]] f32x4 Ot[2][4];
+        bf16x4 ub[NC][4];
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            bs[c][s] = pack_acc2(S[c][2 * s], S[c][2 * s + 1]);
-        f32x4 W[2][4], Ot[2][4];
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {
-            W[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            Ot[c][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          Frag<bf16> ak[4], aq[4];
-#pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {
-            ak[tt] = frag(&A.kd[4 * tt + s][0]);
-            aq[tt] = frag(&A.qd[4 * tt + s][0]);
-          }
-#pragma unroll
-          for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-              mma(W[c][tt], ak[tt], bs[c][s]);
-              mma(Ot[c][tt], bs[c][s], aq[tt]);
-            }
-        }
-        lds_signal(&sm.q_done);
-        // Diag(beta) (W - V), the right-hand side of the substitution; then
-        // the next chunk's v into the copy just read
-        wait_vmem_all(); // this chunk's v is in LDS
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&B.beta[16 * tt + 4 * llg]);
+        for (int hv = 0; hv < NC / 2; ++hv) {
+          f32x4 W[2][4];
 #pragma unroll
           for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float vv = static_cast<float>(*reinterpret_cast<const bf16 *>(
-                  vs + vst_off(16 * tt + 4 * llg + i, 16 * c + llr)));
-              W[c][tt][i] = b4[i] * (W[c][tt][i] - vv);
+            for (int tt = 0; tt < 4; ++tt)
+              W[c][tt] = zero;
+          if constexpr (kQ) {
+            Frag<bf16> bs[2][4];
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+              for (int s = 0; s < 4; ++s)
+                bs[c][s] = pack_acc2(S[c][2 * s], S[c][2 * s + 1]);
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+              for (int tt = 0; tt < 4; ++tt)
+                Ot[c][tt] = zero;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              Frag<bf16> ak[4], aq[4];
+#pragma unroll
+              for (int tt = 0; tt < 4; ++tt) {
+                ak[tt] = frag(&A.kd[4 * tt + s][0]);
+                aq[tt] = frag(&A.qd[4 * tt + s][0]);
+              }
+#pragma unroll
+              for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                  mma(W[c][tt], ak[tt], bs[c][s]);
+                  mma(Ot[c][tt], bs[c][s], aq[tt]);
+                }
             }
-        }
-        wave_lds_fence();
-        load_v(ch + 1);
-        // U_I = -D_I^-1 (Diag(beta_I)(W_I - V_I) + sum_{J<I} L_IJ U_J), tile by tile
-        bf16x4 ub[2][4];
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+          } else {
+            // the state packed one k-step at a time
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          const bf16x4 dn = *reinterpret_cast<const bf16x4 *>(&A.dn[I][ln * 4]);
-          bf16x4 lo[3];
+            for (int s = 0; s < 4; ++s) {
+              Frag<bf16> ak[4], bs[2];
 #pragma unroll
-          for (int J = 0; J < I; ++J)
-            lo[J] = *reinterpret_cast<const bf16x4 *>(&A.lo[off_pair(I, J)][ln * 4]);
+              for (int tt = 0; tt < 4; ++tt)
+                ak[tt] = frag(&A.kd[4 * tt + s][0]);
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            f32x4 a = W[c][I];
+              for (int c = 0; c < 2; ++c)
+                bs[c] = pack_acc2(S[2 * hv + c][2 * s], S[2 * hv + c][2 * s + 1]);
+#pragma unroll
+              for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+                  mma(W[c][tt], ak[tt], bs[c]);
+            }
+          }
+          if (hv == NC / 2 - 1)
+            lds_signal(&sm.q_done);
+          // Diag(beta) (W - V), the right-hand side of the substitution (M's
+          // columns: V = 0); then the next chunk's v into the copy just read
+          if (hv == 0)
+            wait_vmem_all(); // this chunk's v is in LDS
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&B.beta[16 * tt + 4 * llg]);
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float vv =
+                    hv == 1 ? 0.f
+                            : static_cast<float>(*reinterpret_cast<const bf16 *>(
+                                  vs + vst_off(16 * tt + 4 * llg + i, 16 * c + llr)));
+                W[c][tt][i] = b4[i] * (W[c][tt][i] - vv);
+              }
+          }
+          if (hv == 0) {
+            wave_lds_fence();
+            load_v(ch + 1);
+          }
+          // U_I = -D_I^-1 (Diag(beta_I)(W_I - V_I) + sum_{J<I} L_IJ U_J), tile by tile
+#pragma unroll
+          for (int I = 0; I < 4; ++I) {
+            const bf16x4 dn = *reinterpret_cast<const bf16x4 *>(&A.dn[I][ln * 4]);
+            bf16x4 lo[3];
 #pragma unroll
             for (int J = 0; J < I; ++J)
-              a = mma16(a, lo[J], ub[c][J]);
-            ub[c][I] = pack4(mma16(zero, dn, pack4(a)));
+              lo[J] = *reinterpret_cast<const bf16x4 *>(&A.lo[off_pair(I, J)][ln * 4]);
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              f32x4 a = W[c][I];
+#pragma unroll
+              for (int J = 0; J < I; ++J)
+                a = mma16(a, lo[J], ub[2 * hv + c][J]);
+              ub[2 * hv + c][I] = pack4(mma16(zero, dn, pack4(a)));
+            }
           }
         }
         // O^T += U^T M_qk^T (K = tokens, kperm order: two stacked U tiles)
-        Frag<bf16> bu[2][2];
+        Frag<bf16> bu[NC][2];
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < NC; ++c)
 #pragma unroll
           for (int s = 0; s < 2; ++s)
             bu[c][s].v = __builtin_shufflevector(ub[c][2 * s], ub[c][2 * s + 1], 0, 1, 2, 3, 4,
                                                  5, 6, 7);
+        if constexpr (!kQ)
+          lds_signal(&sm.m_done);
+        if constexpr (kQ) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           Frag<bf16> am[4];
@@ -441,12 +497,13 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(
                                                     ro, off, 0, 0);
             }
         }
+        } // kQ
         // S = Diag(a_last) S + K_restore^T U
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
           const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&B.al[16 * ct + 4 * llg]);
 #pragma unroll
-          for (int c = 0; c < 2; ++c)
+          for (int c = 0; c < NC; ++c)
             S[c][ct] *= a4;
         }
 #pragma unroll
@@ -460,11 +517,11 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-              for (int c = 0; c < 2; ++c)
+              for (int c = 0; c < NC; ++c)
                 mma(S[c][4 * hf + ct], ar[ct], bu[c][s]);
           }
         }
-        if (ckpt != nullptr) {
+        if (kQ && ckpt != nullptr) {
           if (ch == ck_next && ch <= cd.ckpt_last) {
             float *cp = ckpt + ((int64_t)ck_idx * H + h) * (kD * kD) + col0 + llr;
             ck_next += cd.ckpt_every;
@@ -522,6 +579,21 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             fp[kperm(16 * ct + 4 * lg + i) * kD + 16 * c] = S[c][ct][i];
+      if constexpr (MODE == 1) {
+        // M as hi / lo bf16 in the planner scan's operand order
+        bf16 *fb = reinterpret_cast<bf16 *>(m_out + ((int64_t)cd.final_idx * H + h) * (kD * kD));
+#pragma unroll
+        for (int c = 2; c < NC; ++c)
+#pragma unroll
+          for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int x = scan_m_bf16_index(kperm(16 * ct + 4 * lg + i), col0 + 16 * (c & 1) + lr);
+              const bf16 hi = static_cast<bf16>(S[c][ct][i]);
+              fb[x] = hi;
+              fb[kD * kD + x] = static_cast<bf16>(S[c][ct][i] - static_cast<float>(hi));
+            }
+      }
     }
   } else {
     // ============================ prep waves ============================
@@ -575,7 +647,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(
       for (int s = 0; s < 4; ++s) {
         const int vo = (int)(((16 * I + llr) * rowstride + 32 * s + 8 * llg) * 2);
         rk[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r1, vo, 0, 0));
-        rq[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r2, vo, 0, 0));
+        if constexpr (kQ)
+          rq[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r2, vo, 0, 0));
       }
     };
     // tile scan of the loaded g (log2 units, inclusive over the 16 tokens of
@@ -676,11 +749,13 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(
       for (int s = 0; s < 4; ++s) {
         const Frag<bf16> b = load_frag(bsrc + s * 512 + ln * 8);
         mma(accL, b, ak[s]);
-        mma(accM, b, aq[s]);
+        if constexpr (kQ)
+          mma(accM, b, aq[s]);
       }
       *reinterpret_cast<bf16x4 *>(&sm.a.lo[off_pair(Ip, J)][ln * 4]) = pack4(accL * brow);
-      *reinterpret_cast<bf16x4 *>(&sm.a.mqk[2 * Ip + (J >> 1)][ln * 8 + 4 * (J & 1)]) =
-          pack4(accM);
+      if constexpr (kQ)
+        *reinterpret_cast<bf16x4 *>(&sm.a.mqk[2 * Ip + (J >> 1)][ln * 8 + 4 * (J & 1)]) =
+            pack4(accM);
     };
 
     // chunk 0's beta, tile scan and factors
@@ -719,15 +794,18 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(
           float sq = 0.f, sk = 0.f;
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            sq = sumsq8_bf16(rq[s], sq);
+            if constexpr (kQ)
+              sq = sumsq8_bf16(rq[s], sq);
             sk = sumsq8_bf16(rk[s], sk);
           }
-          sq += __shfl_xor(sq, 16);
           sk += __shfl_xor(sk, 16);
-          sq += __shfl_xor(sq, 32);
           sk += __shfl_xor(sk, 32);
-          iq = __builtin_amdgcn_rsqf(sq + qk_eps);
           ik = __builtin_amdgcn_rsqf(sk + qk_eps);
+          if constexpr (kQ) {
+            sq += __shfl_xor(sq, 16);
+            sq += __shfl_xor(sq, 32);
+            iq = __builtin_amdgcn_rsqf(sq + qk_eps);
+          }
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -741,7 +819,13 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(
           load8f(&P.fac[I][0][32 * s + 8 * lg], fp);
           load8f(&P.fac[I][1][32 * s + 8 * lg], ft);
           load8f(&P.fac[I][2][32 * s + 8 * lg], fr);
-          widen8(rq[s], qv);
+          if constexpr (kQ) {
+            widen8(rq[s], qv);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              qv[j] = 0.f;
+          }
           widen8(rk[s], kv);
           if (qk_on) {
 #pragma unroll
@@ -761,16 +845,19 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(
             yr[j] = xs[j] * ft[j];  // K_rs
             yre[j] = yr[j] * fr[j]; // K_restore
           }
-          fq[s] = pack8(xq);
+          if constexpr (kQ) {
+            fq[s] = pack8(xq);
+            pq[s] = pack8(yq).v;
+          }
           fk[s] = pack8(xk);
           fs[s] = pack8(xs);
           fre[s] = pack8(yre);
-          pq[s] = pack8(yq).v;
           pk[s] = pack8(yk).v;
           // diagonal tile: L_II in the column layout; M_II swapped, in the
           // row layout (row r = lr)
           mma(accLc, fk[s], fs[s]);
-          mma(accMr, fs[s], fq[s]);
+          if constexpr (kQ)
+            mma(accMr, fs[s], fq[s]);
           if (I < 3)
             *reinterpret_cast<bf16x8 *>(&P.krs[I][s][lane * 8]) = pack8(yr).v;
           if (I == 0) {
@@ -794,7 +881,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(
           } else if (I == 3) {
             // tile 3's K_loc and Q_loc for the pair (3, 0), which tile 0's wave computes
             *reinterpret_cast<bf16x8 *>(&P.t3k[s][lane * 8]) = fk[s].v;
-            *reinterpret_cast<bf16x8 *>(&P.t3q[s][lane * 8]) = fq[s].v;
+            if constexpr (kQ)
+              *reinterpret_cast<bf16x8 *>(&P.t3q[s][lane * 8]) = fq[s].v;
           }
         }
         // N = strictly lower part of Diag(beta) L_II (lane (lr, lg): row
@@ -810,7 +898,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(
         lds_wait(&sm.q_done, 4 * step);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          *reinterpret_cast<bf16x8 *>(&A.qd[4 * I + s][lane * 8]) = pq[s];
+          if constexpr (kQ)
+            *reinterpret_cast<bf16x8 *>(&A.qd[4 * I + s][lane * 8]) = pq[s];
           *reinterpret_cast<bf16x8 *>(&A.kd[4 * I + s][lane * 8]) = pk[s];
         }
         issue_qk(step + 1);
@@ -844,7 +933,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(
         // from the other copy, beta)
         lds_wait(&sm.m_done, 4 * step);
         store_beta(step + 1, rb_next);
-        {
+        if constexpr (kQ) {
           // M_II with its diagonal: rows 16 I + lr, tokens 16 I + 4 lg + i
           f32x4 m = accMr;
 #pragma unroll
@@ -864,7 +953,8 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
             t3k[s] = load_frag(&P.t3k[s][lane * 8]);
-            t3q[s] = load_frag(&P.t3q[s][lane * 8]);
+            if constexpr (kQ)
+              t3q[s] = load_frag(&P.t3q[s][lane * 8]);
           }
           pair(3, 0, &P.bsc[1][0][0], t3k, t3q, B.beta[48 + lr]);
         } else {
@@ -889,23 +979,43 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(
 
 hipError_t launch_fused(const ChainDesc *chains, int32_t nchains, int32_t H, const void *q,
                          const void *k, const void *v, const void *g, const void *beta,
-                         void *o, const float *init, float *final_state, float *ckpt,
-                         hipStream_t s, const Prologue &pro, const Epilogue &epi) {
+                         void *o, const float *init, const float *sin, float *final_state,
+                         float *ckpt, hipStream_t s, const Prologue &pro, const Epilogue &epi) {
   if (nchains == 0)
     return hipSuccess;
   dim3 grid((unsigned)((int64_t)nchains * H)), block(kFusedThreads);
   auto launch = [&](auto kern) {
     kern<<<grid, block, 0, s>>>(chains, H, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v,
-                                (const bf16 *)g, (const bf16 *)beta, (bf16 *)o, init,
-                                final_state, ckpt, pro.A_log, pro.g_min, pro.qk_eps,
+                                (const bf16 *)g, (const bf16 *)beta, (bf16 *)o, init, sin,
+                                final_state, nullptr, ckpt, pro.A_log, pro.g_min, pro.qk_eps,
                                 (const bf16 *)epi.gate, epi.weight, epi.eps);
   };
   if (epi.on())
-    launch(fused_kernel<true, true>);
+    launch(fused_kernel<0, true, true>);
   else if (pro.on())
-    launch(fused_kernel<true, false>);
+    launch(fused_kernel<0, true, false>);
   else
-    launch(fused_kernel<false, false>);
+    launch(fused_kernel<0, false, false>);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_seg(const ChainDesc *chains, int32_t nchains, int32_t H, const void *k,
+                            const void *v, const void *g, const void *beta, float *st_out,
+                            float *m_out, hipStream_t s, const Prologue &pro) {
+  if (nchains == 0)
+    return hipSuccess;
+  dim3 grid((unsigned)((int64_t)nchains * H)), block(kFusedThreads);
+  auto launch = [&](auto kern) {
+    // (q is never read: k stands in for it)
+    kern<<<grid, block, 0, s>>>(chains, H, (const bf16 *)k, (const bf16 *)k, (const bf16 *)v,
+                                (const bf16 *)g, (const bf16 *)beta, nullptr, nullptr, nullptr,
+                                st_out, m_out, nullptr, pro.A_log, pro.g_min, pro.qk_eps,
+                                nullptr, nullptr, 0.f);
+  };
+  if (pro.on())
+    launch(fused_kernel<1, true, false>);
+  else
+    launch(fused_kernel<1, false, false>);
   return hipGetLastError();
 }
 

@@ -187,14 +187,23 @@ hipError_t launch_k2(int elt, int mode, const ChainDesc *chains, int32_t nchains
                      const Epilogue &epi, hipStream_t s);
 
 // Fused chunk prep + state chain, one workgroup per (chain, head) with all
-// dv columns (bf16; entry states from `init` or zero): writes o, exit states
-// and (when ckpt is not null) the chains' state checkpoints; with the
-// prologue and the output epilogue.
+// dv columns (bf16; entry states from `init` (init_idx >= 0), from the
+// planner's `sin` (init_idx <= -2) or zero): writes o, exit states and (when
+// ckpt is not null) the chains' state checkpoints; with the prologue and the
+// output epilogue.
 hipError_t launch_fused(const ChainDesc *chains, int32_t nchains, int32_t H, const void *q,
                          const void *k, const void *v, const void *g, const void *beta,
-                         void *o, const float *init, float *final_state, float *ckpt,
-                         hipStream_t s, const Prologue &pro = Prologue(),
+                         void *o, const float *init, const float *sin, float *final_state,
+                         float *ckpt, hipStream_t s, const Prologue &pro = Prologue(),
                          const Epilogue &epi = Epilogue());
+
+// The planner's segment pass on the fused kernel (bf16): for every chain,
+// its exit pair from [0 | I] with values [V | 0]: S~ to st_out[final_idx]
+// (row-major) and M to m_out[final_idx] as hi / lo bf16 at
+// scan_m_bf16_index; with the prologue (its query half unused).
+hipError_t launch_fused_seg(const ChainDesc *chains, int32_t nchains, int32_t H, const void *k,
+                            const void *v, const void *g, const void *beta, float *st_out,
+                            float *m_out, hipStream_t s, const Prologue &pro = Prologue());
 
 // Whether the state chain's replay pass takes the output epilogue itself:
 // when its plain launch runs 128-column blocks anyway (at least one wide

@@ -110,12 +110,14 @@ int32_t kda_plan_num_segments(int64_t seq_len, int32_t num_seqs, int32_t H, int3
  * transition pairs are combined by a prefix scan and then replayed (see
  * kda_plan_num_segments and kda_segment_transition); the result is the same
  * up to fp32 rounding.
- * Two implementations compute the same result.  With KDA_BF16, no split and
- * at least 512 (sequence, head) pairs, one fused kernel builds each chunk's
- * operands on chip while it carries the state (the workspace then holds only
- * the schedule); otherwise a chunk-parallel prep kernel writes the per-chunk
- * operands to the workspace and a state-carrying kernel reads them.
- * kda_chunk_prefill_ex chooses between them explicitly.
+ * Two implementations compute the same result.  With KDA_BF16 and at least
+ * 512 (sequence, head) pairs without a split, or at least 256 (segment,
+ * head) pairs with one, a fused kernel builds each chunk's operands on chip
+ * while it carries the state (with a split, in the segment pass and in the
+ * replay; the workspace then holds no per-chunk operands); otherwise a
+ * chunk-parallel prep kernel writes the per-chunk operands to the workspace
+ * and a state-carrying kernel reads them.  kda_chunk_prefill_ex chooses
+ * between them explicitly.
  *
  *   num_seqs         : N >= 0 sequences.
  *   cu_seqlens_host  : HOST, N+1 int64, cu[0] = 0, nondecreasing.  The
@@ -156,9 +158,9 @@ kda_status kda_chunk_prefill(int32_t num_seqs, const int64_t *cu_seqlens_host, i
  *                   kda_chunk_prefill), KDA_PATH_TWO_KERNEL (chunk-prep
  *                   kernel, then the state-carrying kernel; any dtype and
  *                   split), or KDA_PATH_FUSED (the fused kernel; KDA_BF16
- *                   only; it takes whole sequences, so split_hint = 0 then
- *                   means no split, and split_hint > 1 on a sequence of more
- *                   than one chunk is KDA_ERR_UNSUPPORTED).
+ *                   only; split_hint = 0 then means no split, and a split
+ *                   (split_hint > 1) runs the planner's segment pass and
+ *                   replay on it).
  *   ckpt_align    : 0 for no checkpoints; else the hash-block length, a
  *                   positive multiple of 64, with pos0_host and ckpt_state
  *                   as for kda_chunk_prefill_ckpt; ckpt_all = 1 writes every

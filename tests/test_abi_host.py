@@ -359,9 +359,22 @@ def test_prefill_path_selection(lib):
     assert auto == lib.kda_chunk_prefill_ex_workspace_size(1, p, 2, 128, 128, nat.KDA_BF16, 0,
                                                            None)
     assert size(one, 2, nat.KDA_F32, 0, 2) == 0     # fused is bf16 only
-    assert size((0, 64 * 64), 1, nat.KDA_BF16, 8, 2) == 0   # and takes no planner split
-    # (asking for it turns the automatic split off: few heads of one long sequence)
+    # asking for it turns the automatic split off (few heads of one long
+    # sequence); an explicit split runs the planner's segment pass and
+    # replay on it: its state buffers, still no records
+    mat = 128 * 128 * 4
     assert 0 < size((0, 64 * 64), 1, nat.KDA_BF16, 0, 2) < 64 * 1024
+    fsplit = size((0, 64 * 64), 1, nat.KDA_BF16, 8, 2)
+    assert (7 * 2 + 8) * mat <= fsplit < (7 * 2 + 8) * mat + 64 * 1024
+    assert size((0, 64 * 64), 1, nat.KDA_BF16, 8, 1) >= fsplit + 64 * 61952
+    # the automatic choice: a split into at least 256 (segment, head) chains
+    # runs on the fused kernel (131072 tokens x 12 heads: 64 segments), fewer
+    # on the two kernels
+    long12 = (0, 131072)
+    assert size(long12, 12, nat.KDA_BF16, 0, 0) == size(long12, 12, nat.KDA_BF16, 64, 2) < \
+        (63 * 2 + 64) * 12 * mat + 1024 * 1024
+    assert size((0, 64 * 64), 1, nat.KDA_BF16, 8, 0) == \
+        size((0, 64 * 64), 1, nat.KDA_BF16, 8, 1)
     assert size(one, 2, nat.KDA_BF16, 0, 3) == 0    # unknown path
     # the call refuses the same requests before touching the device
     def call(dt, split, path, cuv=one):
@@ -371,6 +384,6 @@ def test_prefill_path_selection(lib):
                                         FAKE, None, FAKE, FAKE, split, ctypes.byref(o), None, 0,
                                         None)
     assert call(nat.KDA_F32, 0, 2) == nat.KDA_ERR_UNSUPPORTED
-    assert call(nat.KDA_BF16, 8, 2, cuv=(0, 64 * 64)) == nat.KDA_ERR_UNSUPPORTED
+    assert call(nat.KDA_BF16, 8, 2, cuv=(0, 64 * 64)) == nat.KDA_ERR_WORKSPACE
     assert call(nat.KDA_BF16, 0, 9) == nat.KDA_ERR_INVALID_ARG
     assert call(nat.KDA_BF16, 0, 2) == nat.KDA_ERR_WORKSPACE   # valid request, no workspace

@@ -93,6 +93,13 @@ def test_checkpoint_bf16_paths(bf16_path):
     check([700, 1000, 40, 1536], [0, 448, 960, 0], 512, 2, torch.bfloat16, 730)
 
 
+@pytest.mark.parametrize("split", [2, 5])
+def test_checkpoint_bf16_planner_split_paths(split, bf16_path):
+    # the planner on either implementation: the checkpoints land in the
+    # replay chains
+    check([64 * 40, 300], [128, 0], 256, 2, torch.bfloat16, 731, split=split)
+
+
 # --- every hash-aligned position (kda_chunk_prefill_ckpt_all) ----------------
 
 
@@ -138,6 +145,12 @@ def test_all_checkpoints_positions(dtype):
 def test_all_checkpoints_with_planner_split(split):
     # segments of a split sequence each hold some of its boundaries
     check_all([1500, 300], [128, 0], 128, 2, torch.float32, 730, split=split)
+
+
+@pytest.mark.parametrize("fused", ["fused", "two_kernel"])
+def test_all_checkpoints_bf16_planner_split(fused, monkeypatch):
+    check_all([1500, 300], [128, 0], 128, 2, torch.bfloat16, 732, split=3, fused=fused,
+              monkeypatch=monkeypatch)
 
 
 @pytest.mark.parametrize("fused", ["fused", "two_kernel"])

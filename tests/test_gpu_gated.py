@@ -125,6 +125,14 @@ def test_gated_planner_split(dtype):
 
 
 @pytest.mark.parametrize("fused", ["fused", "two_kernel"])
+def test_gated_planner_split_bf16_paths(fused, monkeypatch):
+    """The planner on either implementation with every layer step: the gate
+    and the k norm in the segment pass, all of them in the replay."""
+    monkeypatch.setattr(kda._native, "DEFAULT_PREFILL_PATH", fused)
+    gated_vs_oracle([1000, 90], 2, torch.bfloat16, 575, init=True, split=4)
+
+
+@pytest.mark.parametrize("fused", ["fused", "two_kernel"])
 @pytest.mark.parametrize("epi", [True, False])
 def test_gated_fused_and_two_kernel_paths(fused, epi, monkeypatch):
     """bf16 with the fused kernel forced on and off; with and without the

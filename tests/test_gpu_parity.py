@@ -182,6 +182,24 @@ def test_split_matches_oracle(split, dtype):
                       split=split)
 
 
+@pytest.mark.parametrize("split", [2, 3, 8, 41])
+def test_bf16_fused_planner_matches_oracle(split, monkeypatch):
+    # the planner's segment pass ([S~ | M] from [0 | I]) and replay on the
+    # fused kernel, then the bf16 scan between them
+    monkeypatch.setattr(kda._native, "DEFAULT_PREFILL_PATH", "fused")
+    prefill_vs_oracle([64 * 40 + 13, 200], 2, torch.bfloat16, 40 + split, decay="mild",
+                      init=True, split=split)
+
+
+def test_bf16_fused_planner_packed_varlen(monkeypatch):
+    # sequences cut into min(5, chunks) segments, ragged last chunks, empty
+    # and one-chunk sequences unsplit, zero and given initial states
+    monkeypatch.setattr(kda._native, "DEFAULT_PREFILL_PATH", "fused")
+    prefill_vs_oracle([0, 1, 64, 130, 0, 77, 2000, 320], 3, torch.bfloat16, 45, init=True,
+                      split=5)
+    prefill_vs_oracle([129, 1000], 2, torch.bfloat16, 46, split=3)
+
+
 def test_split_invariance_fp32():
     say("split invariance")
     cu = wl.cu_from_lengths([64 * 64])

@@ -41,7 +41,8 @@ def rel_err(x, ref):
     return float(np.max(np.abs(x - ref)) / max(float(np.max(np.abs(ref))), 1e-30))
 
 
-@pytest.fixture(params=["fp32", "bf16_fused", "bf16_two_kernel", "fp32_split", "bf16_split"])
+@pytest.fixture(params=["fp32", "bf16_fused", "bf16_two_kernel", "fp32_split", "bf16_split",
+                        "bf16_fused_split"])
 def path(request, monkeypatch):
     """(dtype, split_hint) of one prefill implementation; the library reads
     the path given to every prefill call."""
@@ -50,7 +51,7 @@ def path(request, monkeypatch):
     split = 2 if name.endswith("split") else 0
     if name.startswith("bf16"):
         monkeypatch.setattr(kda._native, "DEFAULT_PREFILL_PATH",
-                            "fused" if name == "bf16_fused" else "two_kernel")
+                            "fused" if name.startswith("bf16_fused") else "two_kernel")
     say("special-gate path:", name)
     return dtype, split
 

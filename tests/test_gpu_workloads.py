@@ -80,12 +80,13 @@ def test_prefill_bf16_T8192_H96_sampled_heads(path):
     check_heads(w, d, o, fin, [0], list(range(0, 96, 8)))
 
 
-@pytest.mark.parametrize("split", [0, 128, 256])
-def test_prefill_bf16_T131072_H12_planner_all_heads(split):
+@pytest.mark.parametrize("split,path", [(0, None), (128, None), (256, None), (0, "two_kernel")])
+def test_prefill_bf16_T131072_H12_planner_all_heads(split, path):
     """The long-context workload through the planner: the automatic cut
-    (64 segments) and the 128- and 256-segment cuts the workload allows,
-    every head against the oracle."""
-    w, d, o, fin = run_prefill("prefill_bf16_T131072_H12", split)
+    (64 segments) and the 128- and 256-segment cuts the workload allows, on
+    the fused kernel (the automatic choice) and with the chunk records of
+    the two-kernel path, every head against the oracle."""
+    w, d, o, fin = run_prefill("prefill_bf16_T131072_H12", split, path=path)
     assert kda.plan_num_segments(131072, 1, 12, split) == {0: 64, 128: 128, 256: 256}[split]
     check_heads(w, d, o, fin, [0], list(range(12)))
 
