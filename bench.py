@@ -102,7 +102,7 @@ def stored_counters(workload: str):
 COPY_PROBE_FLOATS = 256 << 20   # 1 GiB fp32 read + 1 GiB written by the calibration copy
 # kernels of this library, by the part of their names that identifies them
 LIB_KERNELS = ("prep_kernel", "k1_kernel", "k2_kernel", "scan_kernel", "scan_bf16_kernel",
-               "fused_kernel", "out_norm_gate_kernel", "decode_kernel")
+               "fused_kernel", "fused_pass1_kernel", "out_norm_gate_kernel", "decode_kernel")
 
 
 def probe_dispatches(path, counters):
@@ -326,7 +326,12 @@ def time_prefill(kda, wl, name, steps, warmup, split_hint, dev, gated=False, pat
         "ms_per_step": ms, "ms_min": min(per), "wall_ms_per_step": wall / steps * 1e3,
         "tokens_per_s": T / (ms * 1e-3), "chunk_heads": chunk_heads, "model_flops": flops,
         "tflops": tflops, "mfma_frac": tflops / PEAK_BF16_TFLOPS,
-        "segments_auto": [kda.plan_num_segments(L, N, H, split_hint) for L in w.lengths[:1]],
+        # segments of the first sequence under this call's path (the fused
+        # path takes no automatic cut; the two-kernel one the fp32 cut)
+        "segments": [1 if path == "fused" and split_hint == 0 else
+                     kda.plan_num_segments(L, N, H, split_hint,
+                                           dtype=w.dtype if path == "auto" else None)
+                     for L in w.lengths[:1]],
         "path": path,
     }
     del d, o, fin, ws

@@ -47,6 +47,7 @@ EXPORTED = (
     "kda_status_string",
     "kda_version",
     "kda_plan_num_segments",
+    "kda_plan_num_segments_dt",
     "kda_chunk_prefill_workspace_size",
     "kda_chunk_prefill",
     "kda_chunk_prefill_ex_workspace_size",
@@ -93,6 +94,8 @@ def load():
         lib.kda_version.argtypes = []
         lib.kda_plan_num_segments.restype = i32
         lib.kda_plan_num_segments.argtypes = [i64, i32, i32, i32]
+        lib.kda_plan_num_segments_dt.restype = i32
+        lib.kda_plan_num_segments_dt.argtypes = [i64, i32, i32, i32, i32]
         lib.kda_chunk_prefill_workspace_size.restype = sz
         lib.kda_chunk_prefill_workspace_size.argtypes = [i32, lp, i32, i32, i32, i32, i32]
         lib.kda_chunk_prefill.restype = i32
@@ -212,10 +215,16 @@ def _check_device(*ts):
     return dev
 
 
-def plan_num_segments(seq_len: int, num_seqs: int, H: int, split_hint: int = 0) -> int:
-    r = int(load().kda_plan_num_segments(int(seq_len), int(num_seqs), int(H), int(split_hint)))
+def plan_num_segments(seq_len: int, num_seqs: int, H: int, split_hint: int = 0,
+                      dtype=None) -> int:
+    """Segments the automatic prefill path cuts a sequence into
+    (kda_plan_num_segments_dt; dtype None or torch.float32: the fp32 cut,
+    torch.bfloat16: the bf16 one)."""
+    dt = KDA_BF16 if dtype is not None and dtype == torch.bfloat16 else KDA_F32
+    r = int(load().kda_plan_num_segments_dt(int(seq_len), int(num_seqs), int(H),
+                                            int(split_hint), dt))
     if r < 0:
-        raise KdaError(r, "kda_plan_num_segments")
+        raise KdaError(r, "kda_plan_num_segments_dt")
     return r
 
 

@@ -51,7 +51,22 @@ bool aligned_elt(const void *p, kda_dtype dt) {
   return ((uintptr_t)p & (dt == KDA_BF16 ? 1u : 3u)) == 0;
 }
 
-int64_t plan_nseg(int64_t len, int32_t num_seqs, int32_t H, int32_t split_hint) {
+// Whether the automatic cut is the fused planner's: bf16 calls with a
+// chain count in [kFusedAutoMinChains, kFusedAutoMaxChains] on the automatic
+// path.  It cuts a sequence into as many segments as keep each of the fused
+// planner's two passes within one workgroup per compute unit (the first
+// pass runs (segments - 1) x chains workgroups), at least kAutoMinSegChunks
+// chunks each, and only when that gives 3 or more (two segments run one
+// after the other, which the unsplit call already does).
+constexpr int64_t kFusedAutoMinChains = 8, kFusedAutoMaxChains = 128;
+bool fused_auto_cut(int32_t num_seqs, int32_t H, size_t es, int32_t path, int32_t split_hint) {
+  const int64_t chains = (int64_t)num_seqs * H;
+  return es == 2 && path == KDA_PATH_AUTO && split_hint == 0 &&
+         chains >= kFusedAutoMinChains && chains <= kFusedAutoMaxChains;
+}
+
+int64_t plan_nseg(int64_t len, int32_t num_seqs, int32_t H, int32_t split_hint,
+                  bool fused_cut = false) {
   if (len <= 0)
     return 1;
   const int64_t nch = (len + kC - 1) / kC;
@@ -60,6 +75,10 @@ int64_t plan_nseg(int64_t len, int32_t num_seqs, int32_t H, int32_t split_hint) 
   if (split_hint > 1)
     return std::min<int64_t>(split_hint, nch);
   const int64_t chains = (int64_t)num_seqs * H;
+  if (fused_cut) {
+    const int64_t n = std::min<int64_t>(1 + kComputeUnits / chains, nch / kAutoMinSegChunks);
+    return n >= 3 ? n : 1;
+  }
   if (chains >= kAutoMinChains)
     return 1;
   return std::max<int64_t>(1, std::min<int64_t>(kAutoSegments, nch / kAutoMinSegChunks));
@@ -84,6 +103,7 @@ struct Plan {
   std::vector<ChunkDesc> chunks;
   std::vector<ChainDesc> chains;    // prefill / replay (width dv, writes o)
   std::vector<ChainDesc> segchains; // segment pass (width dk + dv)
+  std::vector<ChainDesc> headchains; // fused planner: first segments, run beside the segment pass
   std::vector<ScanDesc> scans;
   int64_t npairs = 0, nsin = 0;
   // bf16 without a planner split runs the fused kernel: no chunk-prep records
@@ -94,7 +114,8 @@ struct Plan {
   // the fused path was asked for a call it cannot run (fp32)
   bool path_unsupported = false;
   // workspace layout
-  size_t off_chunks = 0, off_chains = 0, off_seg = 0, off_scan = 0, table_bytes = 0;
+  size_t off_chunks = 0, off_chains = 0, off_seg = 0, off_head = 0, off_scan = 0,
+         table_bytes = 0;
   size_t off_rec = 0, off_M = 0, off_St = 0, off_Sin = 0, total = 0;
 };
 
@@ -106,6 +127,8 @@ void layout(Plan &p, int32_t H, size_t es) {
   o = align_up(o + p.chains.size() * sizeof(ChainDesc));
   p.off_seg = o;
   o = align_up(o + p.segchains.size() * sizeof(ChainDesc));
+  p.off_head = o;
+  o = align_up(o + p.headchains.size() * sizeof(ChainDesc));
   p.off_scan = o;
   o = align_up(o + p.scans.size() * sizeof(ScanDesc));
   p.table_bytes = o;
@@ -192,6 +215,31 @@ bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_h
   for (int32_t n = 0; n < N; ++n)
     if (cu[n + 1] < cu[n] || cu[n + 1] - cu[n] > INT32_MAX)
       return false;
+  // The implementation.  bf16 with enough chains to give every compute unit
+  // a few (sequence or segment, head) pairs: chunk prep and state carry run
+  // fused in one kernel and no chunk-prep records go through memory.  With
+  // fewer chains the chunk-parallel prep kernel keeps the whole chip busy
+  // and the two-kernel path is faster.  A split on the fused kernel (the
+  // fused planner) runs each split sequence's first segment from its known
+  // entry state beside the segment pass of its middle segments, then the
+  // scan, then the replay of all but the first segment.
+  const bool fcut = fused_auto_cut(N, H, es, path, split_hint);
+  std::vector<int64_t> nsegs(N);
+  int64_t split_pairs = 0; // (segment, head) chains of the first pass / H
+  for (int32_t n = 0; n < N; ++n) {
+    nsegs[n] = plan_nseg(cu[n + 1] - cu[n], N, H, split_hint, fcut);
+    split_pairs += nsegs[n] > 1 ? nsegs[n] - 1 : 0;
+  }
+  const bool split = split_pairs > 0;
+  if (path == KDA_PATH_FUSED) {
+    p.fused = es == 2 && !split;
+    p.fused_split = es == 2 && split;
+    p.path_unsupported = es != 2;
+  } else if (path == KDA_PATH_AUTO) {
+    p.fused = es == 2 && !split && (int64_t)N * H >= kFusedMinChainHeads;
+    p.fused_split =
+        es == 2 && split && (fcut || split_pairs * H >= kFusedSplitMinChainHeads);
+  }
   for (int32_t n = 0; n < N; ++n) {
     const int64_t len = cu[n + 1] - cu[n];
     const int64_t nch = (len + kC - 1) / kC;
@@ -208,49 +256,74 @@ bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_h
     const SeqCkpts ck = seq_ckpts(pos0 ? pos0[n] : 0, len, align, all_ckpts);
     const int64_t idx0 = all_ckpts ? ckpt_base : n;
     ckpt_base += ck.count;
-    const int64_t nseg = plan_nseg(len, N, H, split_hint);
+    const int64_t nseg = nsegs[n];
     if (nseg <= 1) {
       p.chains.push_back(chain(cu[n], len, c0, has_init ? n : -1, has_final ? n : -1));
       assign_ckpts(p.chains.back(), ck, 0, nch, idx0);
       continue;
     }
-    const int64_t q = nch / nseg, r = nch % nseg;
+    // chunk-aligned segments of near-equal length; on the fused planner the
+    // first one is about 7/8 of the others (its workgroups carry the state
+    // and o, the slower of the first pass's two kinds)
+    const int64_t first = p.fused_split ? std::max<int64_t>(1, nch * 7 / (7 + 8 * (nseg - 1)))
+                                        : -1;
+    const int64_t rest = p.fused_split ? nch - first : nch, nrest = p.fused_split ? nseg - 1 : nseg;
+    const int64_t q = rest / nrest, r = rest % nrest;
     const int64_t pair0 = p.npairs, sin0 = p.nsin;
     for (int64_t j = 0; j < nseg; ++j) {
-      const int64_t s0 = j * q + std::min(j, r);  // first chunk, relative to the sequence
-      const int64_t cnt = q + (j < r ? 1 : 0);
+      // first chunk (relative to the sequence) and chunk count of segment j
+      int64_t s0, cnt;
+      if (p.fused_split) {
+        const int64_t jj = j - 1;
+        s0 = j == 0 ? 0 : first + jj * q + std::min(jj, r);
+        cnt = j == 0 ? first : q + (jj < r ? 1 : 0);
+      } else {
+        s0 = j * q + std::min(j, r);
+        cnt = q + (j < r ? 1 : 0);
+      }
       const int64_t t0 = cu[n] + s0 * kC;
       const int64_t nt = std::min<int64_t>(cnt * kC, cu[n + 1] - t0);
-      if (j + 1 < nseg)
-        p.segchains.push_back(chain(t0, nt, c0 + s0, -1, pair0 + j));
       const bool last = j + 1 == nseg;
+      if (p.fused_split) {
+        // segment 0 from the known entry state, its exit state to Sin[sin0];
+        // segments 1 .. nseg - 2 through the segment pass (pairs from pair0);
+        // segments 1 .. nseg - 1 replayed from Sin[sin0 + j - 1]
+        if (j == 0) {
+          p.headchains.push_back(chain(t0, nt, c0 + s0, has_init ? n : -1, sin0));
+          assign_ckpts(p.headchains.back(), ck, s0, cnt, idx0);
+          continue;
+        }
+        if (!last)
+          p.segchains.push_back(chain(t0, nt, c0 + s0, -1, pair0 + j - 1));
+        p.chains.push_back(
+            chain(t0, nt, c0 + s0, -2 - (sin0 + j - 1), (last && has_final) ? n : -1));
+        assign_ckpts(p.chains.back(), ck, s0, cnt, idx0);
+        continue;
+      }
+      if (!last)
+        p.segchains.push_back(chain(t0, nt, c0 + s0, -1, pair0 + j));
       p.chains.push_back(chain(t0, nt, c0 + s0, -2 - (sin0 + j), (last && has_final) ? n : -1));
       assign_ckpts(p.chains.back(), ck, s0, cnt, idx0);
     }
-    p.scans.push_back(ScanDesc{(int32_t)pair0, (int32_t)nseg, (int32_t)sin0,
-                               has_init ? n : -1});
-    p.npairs += nseg - 1;
-    p.nsin += nseg;
+    if (p.fused_split) {
+      // entry states of segments 1 .. nseg - 1, from segment 1's in Sin[sin0]
+      if (nseg > 2)
+        p.scans.push_back(ScanDesc{(int32_t)pair0, (int32_t)(nseg - 1), (int32_t)sin0,
+                                   kScanEntryInSin});
+      p.npairs += nseg - 2;
+      p.nsin += nseg - 1;
+    } else {
+      p.scans.push_back(ScanDesc{(int32_t)pair0, (int32_t)nseg, (int32_t)sin0,
+                                 has_init ? n : -1});
+      p.npairs += nseg - 1;
+      p.nsin += nseg;
+    }
   }
   // longest chains first, so the tail of the launch is short work
   auto longer = [](const ChainDesc &a, const ChainDesc &b) { return a.ntok > b.ntok; };
   std::stable_sort(p.chains.begin(), p.chains.end(), longer);
   std::stable_sort(p.segchains.begin(), p.segchains.end(), longer);
-  // bf16 with enough chains to give every compute unit a few (sequence or
-  // segment, head) pairs: chunk prep and state carry run fused in one kernel
-  // and no chunk-prep records go through memory (with a split, in the
-  // segment pass and in the replay).  With fewer chains the chunk-parallel
-  // prep kernel keeps the whole chip busy and the two-kernel path is faster.
-  const bool split = !p.segchains.empty();
-  if (path == KDA_PATH_FUSED) {
-    p.fused = es == 2 && !split;
-    p.fused_split = es == 2 && split;
-    p.path_unsupported = es != 2;
-  } else if (path == KDA_PATH_AUTO) {
-    p.fused = es == 2 && !split && (int64_t)p.chains.size() * H >= kFusedMinChainHeads;
-    p.fused_split =
-        es == 2 && split && (int64_t)p.segchains.size() * H >= kFusedSplitMinChainHeads;
-  }
+  std::stable_sort(p.headchains.begin(), p.headchains.end(), longer);
   layout(p, H, es);
   return true;
 }
@@ -289,7 +362,8 @@ bool plan_fits(const Plan &p, int32_t H) {
   const int64_t lim = (int64_t)1 << 30;
   // the state chain's 1-D grid: (chains x heads, rounded up to 8) x up to 4
   // column blocks workgroups
-  const int64_t pairs = (int64_t)std::max(p.chains.size(), p.segchains.size()) * H;
+  const int64_t pairs =
+      (int64_t)std::max(p.chains.size(), p.segchains.size() + p.headchains.size()) * H;
   return (int64_t)p.chunks.size() < lim && (int64_t)p.chains.size() < lim &&
          (int64_t)p.segchains.size() < lim && (int64_t)p.scans.size() < lim &&
          H <= 65535 && p.npairs < lim && p.nsin < lim && (pairs + 8) * 4 < ((int64_t)1 << 31);
@@ -370,6 +444,8 @@ hipError_t upload_tables(const Plan &p, void *ws, hipStream_t stream) {
     std::memcpy(h + p.off_chains, p.chains.data(), p.chains.size() * sizeof(ChainDesc));
   if (!p.segchains.empty())
     std::memcpy(h + p.off_seg, p.segchains.data(), p.segchains.size() * sizeof(ChainDesc));
+  if (!p.headchains.empty())
+    std::memcpy(h + p.off_head, p.headchains.data(), p.headchains.size() * sizeof(ChainDesc));
   if (!p.scans.empty())
     std::memcpy(h + p.off_scan, p.scans.data(), p.scans.size() * sizeof(ScanDesc));
   e = hipMemcpyAsync(ws, h, p.table_bytes, hipMemcpyHostToDevice, stream);
@@ -474,16 +550,19 @@ kda_status prefill_impl(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
   }
   if (p.fused_split) {
-    // segment pass, scan and replay, the passes that carry a state on the
-    // fused kernel
+    // first segments beside the segment pass, scan, replay: every pass that
+    // carries a state on the fused kernel
+    float *Sin = (float *)(ws + p.off_Sin);
     if (e == hipSuccess)
-      e = launch_fused_seg((const ChainDesc *)(ws + p.off_seg), (int32_t)p.segchains.size(), H,
-                           k, v, g, beta, (float *)(ws + p.off_St), (float *)(ws + p.off_M), s,
-                           pro);
+      e = launch_fused_pass1((const ChainDesc *)(ws + p.off_head), (int32_t)p.headchains.size(),
+                             (const ChainDesc *)(ws + p.off_seg), (int32_t)p.segchains.size(),
+                             H, q, k, v, g, beta, o, initial_state, Sin,
+                             ckpt_align ? ckpt : nullptr, (float *)(ws + p.off_St),
+                             (float *)(ws + p.off_M), s, pro, epi);
     if (e == hipSuccess)
       e = launch_scan(elt, (const ScanDesc *)(ws + p.off_scan), (int32_t)p.scans.size(), H,
-                      (const float *)(ws + p.off_M), (const float *)(ws + p.off_St),
-                      initial_state, (float *)(ws + p.off_Sin), s);
+                      (const float *)(ws + p.off_M), (const float *)(ws + p.off_St), nullptr,
+                      Sin, s);
     if (e == hipSuccess)
       e = launch_fused((const ChainDesc *)(ws + p.off_chains), (int32_t)p.chains.size(), H, q,
                         k, v, g, beta, o, initial_state, (const float *)(ws + p.off_Sin),
@@ -598,9 +677,16 @@ const char *kda_status_string(kda_status s) {
 int32_t kda_version(void) { return 100; }
 
 int32_t kda_plan_num_segments(int64_t seq_len, int32_t num_seqs, int32_t H, int32_t split_hint) {
-  if (num_seqs < 0 || H < 1 || split_hint < 0)
+  return kda_plan_num_segments_dt(seq_len, num_seqs, H, split_hint, KDA_F32);
+}
+
+int32_t kda_plan_num_segments_dt(int64_t seq_len, int32_t num_seqs, int32_t H,
+                                 int32_t split_hint, kda_dtype dt) {
+  if (num_seqs < 0 || H < 1 || split_hint < 0 || (dt != KDA_F32 && dt != KDA_BF16))
     return KDA_ERR_INVALID_ARG;
-  const int64_t n = plan_nseg(seq_len, num_seqs, H, split_hint);
+  const int64_t n = plan_nseg(seq_len, num_seqs, H, split_hint,
+                              fused_auto_cut(num_seqs, H, elt_size(dt), KDA_PATH_AUTO,
+                                             split_hint));
   return (int32_t)std::min<int64_t>(n, INT32_MAX);
 }
 

@@ -201,20 +201,21 @@ __device__ __forceinline__ int vst_off(int row, int col) {
 // PRO: the decay gate from logits and the q / k L2 norm run in the prep
 // (which of them is decided by A_log != null and qk_eps > 0); EPI: o leaves
 // through the output norm and gate.
+// One workgroup's work: (chain, head) pair blk of `chains`.
 template <int MODE, bool PRO, bool EPI>
-__global__ __launch_bounds__(kFusedThreads) void fused_kernel(
-    const ChainDesc *__restrict__ chains, int32_t H, const bf16 *__restrict__ q,
-    const bf16 *__restrict__ k, const bf16 *__restrict__ v, const bf16 *__restrict__ g,
-    const bf16 *__restrict__ beta, bf16 *__restrict__ o, const float *__restrict__ init,
-    const float *__restrict__ sin, float *__restrict__ final_state, float *__restrict__ m_out,
-    float *__restrict__ ckpt, const float *__restrict__ A_log, float g_min, float qk_eps,
-    const bf16 *__restrict__ ogate, const float *__restrict__ onw, float oeps) {
+__device__ __forceinline__ void fused_body(
+    FusedSmem &sm, int blk, const ChainDesc *__restrict__ chains, int32_t H,
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const bf16 *__restrict__ g, const bf16 *__restrict__ beta, bf16 *__restrict__ o,
+    const float *__restrict__ init, const float *__restrict__ sin,
+    float *__restrict__ final_state, float *__restrict__ m_out, float *__restrict__ ckpt,
+    const float *__restrict__ A_log, float g_min, float qk_eps, const bf16 *__restrict__ ogate,
+    const float *__restrict__ onw, float oeps) {
   static_assert(MODE == 0 || !EPI, "the segment pass writes no o");
   constexpr bool kQ = MODE == 0; // query operands (Q_decay, M_qk) and o
   constexpr int NC = MODE == 0 ? 2 : 4; // 16-column state tiles per state wave
-  __shared__ __attribute__((aligned(1024))) FusedSmem sm;
 
-  const int chain_i = blockIdx.x / H, h = blockIdx.x - chain_i * H;
+  const int chain_i = blk / H, h = blk - chain_i * H;
   const ChainDesc cd = chains[chain_i];
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -245,20 +246,32 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(
     const int col0 = 32 * wv;
     f32x4 S[NC][8]; // rows p = 16 ct + 4 lg + i: channel kperm(p)
     {
-      const float *ip = nullptr;
-      if (MODE == 0 && cd.init_idx >= 0)
-        ip = init + ((int64_t)cd.init_idx * H + h) * (kD * kD);
-      else if (MODE == 0 && cd.init_idx <= -2)
-        ip = sin + ((int64_t)(-2 - cd.init_idx) * H + h) * (kD * kD);
+      // (each source pointer in a branch of its own: with a select between
+      // the two, a kernel holding two inlined bodies crashes the compiler)
+      auto load_state = [&](const float *ip) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
+          for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int ch = kperm(16 * ct + 4 * lg + i), col = col0 + 16 * (c & 1) + lr;
-            S[c][ct][i] = c >= 2 ? (ch == col ? 1.f : 0.f) : (ip ? ip[ch * kD + col] : 0.f);
-          }
+            for (int i = 0; i < 4; ++i)
+              S[c][ct][i] = ip[kperm(16 * ct + 4 * lg + i) * kD + col0 + 16 * c + lr];
+      };
+      if (MODE == 0 && cd.init_idx >= 0) {
+        load_state(init + ((int64_t)cd.init_idx * H + h) * (kD * kD));
+      } else if (MODE == 0 && cd.init_idx <= -2) {
+        load_state(sin + ((int64_t)(-2 - cd.init_idx) * H + h) * (kD * kD));
+      } else {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int ch = kperm(16 * ct + 4 * lg + i), col = col0 + 16 * (c & 1) + lr;
+              S[c][ct][i] = (c >= 2 && ch == col) ? 1.f : 0.f;
+            }
+      }
     }
     uint8_t *vs = reinterpret_cast<uint8_t *>(&sm.vst[wv][0]);
     // this wave's columns of v for chunk ch, straight into its LDS copy:
@@ -977,6 +990,69 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(
   }
 }
 
+template <int MODE, bool PRO, bool EPI>
+__global__ __launch_bounds__(kFusedThreads) void fused_kernel(
+    const ChainDesc *__restrict__ chains, int32_t H, const bf16 *__restrict__ q,
+    const bf16 *__restrict__ k, const bf16 *__restrict__ v, const bf16 *__restrict__ g,
+    const bf16 *__restrict__ beta, bf16 *__restrict__ o, const float *__restrict__ init,
+    const float *__restrict__ sin, float *__restrict__ final_state, float *__restrict__ m_out,
+    float *__restrict__ ckpt, const float *__restrict__ A_log, float g_min, float qk_eps,
+    const bf16 *__restrict__ ogate, const float *__restrict__ onw, float oeps) {
+  __shared__ __attribute__((aligned(1024))) FusedSmem sm;
+  fused_body<MODE, PRO, EPI>(sm, blockIdx.x, chains, H, q, k, v, g, beta, o, init, sin,
+                             final_state, m_out, ckpt, A_log, g_min, qk_eps, ogate, onw, oeps);
+}
+
+// The planner's first pass in one launch: the first segment of every split
+// sequence from its known entry state (MODE 0: o, and the exit state to
+// head_final) in workgroups [0, nhead), the segment pass of the segments
+// between its first and last (MODE 1) in the rest.
+template <bool PRO, bool EPI>
+__global__ __launch_bounds__(kFusedThreads) void fused_pass1_kernel(
+    const ChainDesc *__restrict__ heads, int32_t nhead, const ChainDesc *__restrict__ segs,
+    int32_t H, const bf16 *__restrict__ q, const bf16 *__restrict__ k,
+    const bf16 *__restrict__ v, const bf16 *__restrict__ g, const bf16 *__restrict__ beta,
+    bf16 *__restrict__ o, const float *__restrict__ init, float *__restrict__ head_final,
+    float *__restrict__ ckpt, float *__restrict__ st_out, float *__restrict__ m_out,
+    const float *__restrict__ A_log, float g_min, float qk_eps, const bf16 *__restrict__ ogate,
+    const float *__restrict__ onw, float oeps) {
+  __shared__ __attribute__((aligned(1024))) FusedSmem sm;
+  const int b = blockIdx.x;
+  if (b < nhead)
+    fused_body<0, PRO, EPI>(sm, b, heads, H, q, k, v, g, beta, o, init, nullptr, head_final,
+                            nullptr, ckpt, A_log, g_min, qk_eps, ogate, onw, oeps);
+  else
+    fused_body<1, PRO, false>(sm, b - nhead, segs, H, q, k, v, g, beta, nullptr, nullptr,
+                              nullptr, st_out, m_out, nullptr, A_log, g_min, qk_eps, nullptr,
+                              nullptr, 0.f);
+}
+
+hipError_t launch_fused_pass1(const ChainDesc *heads, int32_t nheads, const ChainDesc *segs,
+                              int32_t nsegs, int32_t H, const void *q, const void *k,
+                              const void *v, const void *g, const void *beta, void *o,
+                              const float *init, float *head_final, float *ckpt, float *st_out,
+                              float *m_out, hipStream_t s, const Prologue &pro,
+                              const Epilogue &epi) {
+  const int64_t nb = ((int64_t)nheads + nsegs) * H;
+  if (nb == 0)
+    return hipSuccess;
+  dim3 grid((unsigned)nb), block(kFusedThreads);
+  const int32_t nhead = nheads * H;
+  auto launch = [&](auto kern) {
+    kern<<<grid, block, 0, s>>>(heads, nhead, segs, H, (const bf16 *)q, (const bf16 *)k,
+                                (const bf16 *)v, (const bf16 *)g, (const bf16 *)beta, (bf16 *)o,
+                                init, head_final, ckpt, st_out, m_out, pro.A_log, pro.g_min,
+                                pro.qk_eps, (const bf16 *)epi.gate, epi.weight, epi.eps);
+  };
+  if (epi.on())
+    launch(fused_pass1_kernel<true, true>);
+  else if (pro.on())
+    launch(fused_pass1_kernel<true, false>);
+  else
+    launch(fused_pass1_kernel<false, false>);
+  return hipGetLastError();
+}
+
 hipError_t launch_fused(const ChainDesc *chains, int32_t nchains, int32_t H, const void *q,
                          const void *k, const void *v, const void *g, const void *beta,
                          void *o, const float *init, const float *sin, float *final_state,
@@ -996,26 +1072,6 @@ hipError_t launch_fused(const ChainDesc *chains, int32_t nchains, int32_t H, con
     launch(fused_kernel<0, true, false>);
   else
     launch(fused_kernel<0, false, false>);
-  return hipGetLastError();
-}
-
-hipError_t launch_fused_seg(const ChainDesc *chains, int32_t nchains, int32_t H, const void *k,
-                            const void *v, const void *g, const void *beta, float *st_out,
-                            float *m_out, hipStream_t s, const Prologue &pro) {
-  if (nchains == 0)
-    return hipSuccess;
-  dim3 grid((unsigned)((int64_t)nchains * H)), block(kFusedThreads);
-  auto launch = [&](auto kern) {
-    // (q is never read: k stands in for it)
-    kern<<<grid, block, 0, s>>>(chains, H, (const bf16 *)k, (const bf16 *)k, (const bf16 *)v,
-                                (const bf16 *)g, (const bf16 *)beta, nullptr, nullptr, nullptr,
-                                st_out, m_out, nullptr, pro.A_log, pro.g_min, pro.qk_eps,
-                                nullptr, nullptr, 0.f);
-  };
-  if (pro.on())
-    launch(fused_kernel<1, true, false>);
-  else
-    launch(fused_kernel<1, false, false>);
   return hipGetLastError();
 }
 

@@ -45,8 +45,11 @@ struct ScanDesc {
   int32_t pair0;    // index of segment 0's (M, S~) pair
   int32_t nseg;     // segments of this sequence (>= 2)
   int32_t sin0;     // index of segment 0's entry state in Sin
-  int32_t init_idx; // user initial_state index, or -1 for zero
+  int32_t init_idx; // user initial_state index, -1 for zero, or kScanEntryInSin
 };
+// ScanDesc::init_idx of a scan whose first entry state is already in
+// Sin[sin0] (bf16 scan only)
+constexpr int32_t kScanEntryInSin = -3;
 static_assert(sizeof(ScanDesc) == 16, "ScanDesc layout");
 
 // Column order of the chunk-prep record's MFMA A operands.  Inside each group
@@ -197,13 +200,18 @@ hipError_t launch_fused(const ChainDesc *chains, int32_t nchains, int32_t H, con
                          float *ckpt, hipStream_t s, const Prologue &pro = Prologue(),
                          const Epilogue &epi = Epilogue());
 
-// The planner's segment pass on the fused kernel (bf16): for every chain,
-// its exit pair from [0 | I] with values [V | 0]: S~ to st_out[final_idx]
-// (row-major) and M to m_out[final_idx] as hi / lo bf16 at
-// scan_m_bf16_index; with the prologue (its query half unused).
-hipError_t launch_fused_seg(const ChainDesc *chains, int32_t nchains, int32_t H, const void *k,
-                            const void *v, const void *g, const void *beta, float *st_out,
-                            float *m_out, hipStream_t s, const Prologue &pro = Prologue());
+// The planner's first pass on the fused kernel (bf16), one launch: the
+// first segment of every split sequence from its entry state (heads: o,
+// checkpoints, exit state to head_final[final_idx]) beside the segment pass
+// of its middle segments (segs: exit pair from [0 | I] with values [V | 0],
+// S~ to st_out[final_idx] row-major and M to m_out[final_idx] as hi / lo
+// bf16 at scan_m_bf16_index).
+hipError_t launch_fused_pass1(const ChainDesc *heads, int32_t nheads, const ChainDesc *segs,
+                              int32_t nsegs, int32_t H, const void *q, const void *k,
+                              const void *v, const void *g, const void *beta, void *o,
+                              const float *init, float *head_final, float *ckpt, float *st_out,
+                              float *m_out, hipStream_t s, const Prologue &pro = Prologue(),
+                              const Epilogue &epi = Epilogue());
 
 // Whether the state chain's replay pass takes the output epilogue itself:
 // when its plain launch runs 128-column blocks anyway (at least one wide

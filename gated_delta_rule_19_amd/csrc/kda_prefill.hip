@@ -1518,14 +1518,20 @@ __global__ __launch_bounds__(kScanBf16Threads) void scan_bf16_kernel(
   const int n = lane & 15, kq = lane >> 4;
   const int64_t mat = (int64_t)kD * kD;
 
-  // entry state of segment 0: init (or zero) -> LDS and Sin[sin0]
+  // entry state of segment 0: init (or zero) -> LDS and Sin[sin0], or
+  // Sin[sin0] as it stands -> LDS
   if (w < 8) {
     const int m = tid >> 2, c0 = (tid & 3) * 4;
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    if (d.init_idx >= 0)
-      x = *reinterpret_cast<const f32x4 *>(init + ((int64_t)d.init_idx * H + h) * mat +
-                                           m * kD + col0 + c0);
-    *reinterpret_cast<f32x4 *>(sin + ((int64_t)d.sin0 * H + h) * mat + m * kD + col0 + c0) = x;
+    float *s0 = sin + ((int64_t)d.sin0 * H + h) * mat + m * kD + col0 + c0;
+    if (d.init_idx == kScanEntryInSin)
+      x = *reinterpret_cast<const f32x4 *>(s0);
+    else {
+      if (d.init_idx >= 0)
+        x = *reinterpret_cast<const f32x4 *>(init + ((int64_t)d.init_idx * H + h) * mat +
+                                             m * kD + col0 + c0);
+      *reinterpret_cast<f32x4 *>(s0) = x;
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       bf16 hi, mid, lo;

@@ -79,17 +79,27 @@ int32_t kda_version(void);
 
 /*
  * Planner query (host only, no HIP calls): how many segments the chunked
- * prefill will cut sequence `seq_len` into, for a batch whose total
- * (sequence, head) count is `num_seqs * H`.
- *   split_hint = 0 : automatic (split long sequences only when the
- *                    unsplit work would leave most compute units idle);
+ * prefill of element type dt on the automatic path will cut sequence
+ * `seq_len` into, for a batch whose total (sequence, head) count is
+ * C = num_seqs * H.
+ *   split_hint = 0 : automatic: split long sequences only when the unsplit
+ *                    work would leave most compute units idle.  KDA_F32
+ *                    (and KDA_BF16 outside the next case): C < 64 cuts into
+ *                    min(64, chunks / 4) segments.  KDA_BF16 with
+ *                    8 <= C <= 128: min(1 + 256 / C, chunks / 4) segments
+ *                    when that is at least 3, else none (the fused
+ *                    planner, each of its passes one workgroup per compute
+ *                    unit);
  *   split_hint = 1 : never split;
  *   split_hint = n > 1 : cut every sequence longer than one chunk into
  *                    min(n, number of its chunks) chunk-aligned segments.
  * Returns >= 1 (or 1 for seq_len <= 0), or a negative status for bad input.
- * The sequence-split planner follows "部署 Kimi K3：从 KDA Kernel 到 Fleet
- * 调度", §1.2 (intra-device, SM-level context parallelism).
+ * kda_plan_num_segments is the KDA_F32 answer.  The sequence-split planner
+ * follows "部署 Kimi K3：从 KDA Kernel 到 Fleet 调度", §1.2 (intra-device,
+ * SM-level context parallelism).
  */
+int32_t kda_plan_num_segments_dt(int64_t seq_len, int32_t num_seqs, int32_t H,
+                                 int32_t split_hint, kda_dtype dt);
 int32_t kda_plan_num_segments(int64_t seq_len, int32_t num_seqs, int32_t H, int32_t split_hint);
 
 /*

@@ -7,6 +7,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 from gated_delta_rule_19_amd import _native as nat
 
@@ -53,6 +54,18 @@ def test_planner_policy(lib):
     assert nat.plan_num_segments(0, 1, 12, 64) == 1
     # automatic: few heads of one long sequence -> split; a full layer -> not
     assert nat.plan_num_segments(131072, 1, 12, 0) == 64
+    # bf16: the fused planner's cut for 8 .. 128 (sequence, head) chains,
+    # (segments - 1) x chains <= 256 workgroups per pass, >= 3 segments of
+    # >= 4 chunks
+    bf = torch.bfloat16
+    assert nat.plan_num_segments(131072, 1, 12, 0, bf) == 22
+    assert nat.plan_num_segments(8192, 1, 96, 0, bf) == 3
+    assert nat.plan_num_segments(8192, 1, 64, 0, bf) == 5
+    assert nat.plan_num_segments(8192, 2, 64, 0, bf) == 3      # 128 chains: 256 per pass
+    assert nat.plan_num_segments(8192, 1, 129, 0, bf) == 1     # above 128: 2 would be all
+    assert nat.plan_num_segments(640, 1, 96, 0, bf) == 1       # 10 chunks: 2 segments
+    assert nat.plan_num_segments(64 * 200, 1, 4, 0, bf) == 50  # below 8 chains: as fp32
+    assert nat.plan_num_segments(131072, 1, 12, 5, bf) == 5    # an explicit hint rules
     assert nat.plan_num_segments(8192, 1, 96, 0) == 1
     assert nat.plan_num_segments(256, 1, 2, 0) == 1
     with pytest.raises(nat.KdaError):
@@ -360,19 +373,20 @@ def test_prefill_path_selection(lib):
                                                            None)
     assert size(one, 2, nat.KDA_F32, 0, 2) == 0     # fused is bf16 only
     # asking for it turns the automatic split off (few heads of one long
-    # sequence); an explicit split runs the planner's segment pass and
-    # replay on it: its state buffers, still no records
+    # sequence); an explicit split runs the planner on it: the first segment
+    # from the entry state, the 6 middle segments' pairs, the 7 later
+    # segments' entry states, still no records
     mat = 128 * 128 * 4
     assert 0 < size((0, 64 * 64), 1, nat.KDA_BF16, 0, 2) < 64 * 1024
     fsplit = size((0, 64 * 64), 1, nat.KDA_BF16, 8, 2)
-    assert (7 * 2 + 8) * mat <= fsplit < (7 * 2 + 8) * mat + 64 * 1024
+    assert (6 * 2 + 7) * mat <= fsplit < (6 * 2 + 7) * mat + 64 * 1024
     assert size((0, 64 * 64), 1, nat.KDA_BF16, 8, 1) >= fsplit + 64 * 61952
     # the automatic choice: a split into at least 256 (segment, head) chains
     # runs on the fused kernel (131072 tokens x 12 heads: 64 segments), fewer
     # on the two kernels
     long12 = (0, 131072)
-    assert size(long12, 12, nat.KDA_BF16, 0, 0) == size(long12, 12, nat.KDA_BF16, 64, 2) < \
-        (63 * 2 + 64) * 12 * mat + 1024 * 1024
+    assert size(long12, 12, nat.KDA_BF16, 0, 0) == size(long12, 12, nat.KDA_BF16, 22, 2) < \
+        (20 * 2 + 21) * 12 * mat + 1024 * 1024
     assert size((0, 64 * 64), 1, nat.KDA_BF16, 8, 0) == \
         size((0, 64 * 64), 1, nat.KDA_BF16, 8, 1)
     assert size(one, 2, nat.KDA_BF16, 0, 3) == 0    # unknown path

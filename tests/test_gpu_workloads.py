@@ -71,11 +71,13 @@ def test_prefill_f32_T256_H2_full():
     check_heads(w, d, o, fin, [0], [0, 1])
 
 
-@pytest.mark.parametrize("path", [None, "fused"])
+@pytest.mark.parametrize("path", [None, "fused", "two_kernel"])
 def test_prefill_bf16_T8192_H96_sampled_heads(path):
-    """The automatic choice (chunk prep, then the state chain) and the fused
-    kernel, whose one workgroup per head carries the state through all 128
-    chunks of the sequence."""
+    """The automatic choice (the fused planner: 3 segments), the fused kernel
+    unsplit, whose one workgroup per head carries the state through all 128
+    chunks of the sequence, and chunk prep followed by the state chain."""
+    if path is None:
+        assert kda.plan_num_segments(8192, 1, 96, 0, dtype=torch.bfloat16) == 3
     w, d, o, fin = run_prefill("prefill_bf16_T8192_H96", path=path)
     check_heads(w, d, o, fin, [0], list(range(0, 96, 8)))
 
@@ -83,11 +85,15 @@ def test_prefill_bf16_T8192_H96_sampled_heads(path):
 @pytest.mark.parametrize("split,path", [(0, None), (128, None), (256, None), (0, "two_kernel")])
 def test_prefill_bf16_T131072_H12_planner_all_heads(split, path):
     """The long-context workload through the planner: the automatic cut
-    (64 segments) and the 128- and 256-segment cuts the workload allows, on
-    the fused kernel (the automatic choice) and with the chunk records of
-    the two-kernel path, every head against the oracle."""
+    (22 segments on the fused planner; 64 with the chunk records of the
+    two-kernel path) and the 128- and 256-segment cuts the workload allows,
+    every head against the oracle."""
     w, d, o, fin = run_prefill("prefill_bf16_T131072_H12", split, path=path)
-    assert kda.plan_num_segments(131072, 1, 12, split) == {0: 64, 128: 128, 256: 256}[split]
+    if path is None:
+        assert kda.plan_num_segments(131072, 1, 12, split, dtype=torch.bfloat16) == \
+            {0: 22, 128: 128, 256: 256}[split]
+    else:
+        assert kda.plan_num_segments(131072, 1, 12, split) == 64
     check_heads(w, d, o, fin, [0], list(range(12)))
 
 
