@@ -37,9 +37,11 @@
 //     input and k-step, and the MFMA A-fragment layout.
 // Step k: the prep waves build chunk k's operands while the state waves
 // consume chunk k - 1's; one workgroup barrier ends each step.  The prep
-// waves also scan chunk k + 1's decay and turn the tile totals into their
-// per-channel factors within step k, so chunk k + 1's elementwise work
-// starts as soon as step k + 1 does.  Q_decay, K_decay, M_qk and the L and
+// waves also scan chunk k + 1's decay within step k, and once they have met
+// (every tile total written) the state waves, whose path is the shorter,
+// turn the totals into the per-channel factors, state wave w those of token
+// tile w: chunk k + 1's elementwise work starts as soon as step k + 1 does.
+// Q_decay, K_decay, M_qk and the L and
 // D^-1 blocks, which the state waves read early in a step, have one LDS
 // copy: the prep waves overwrite them only after every state wave has
 // counted itself done with the previous chunk's (LDS counters, bounded
@@ -125,6 +127,7 @@ struct PrepScratch {
   bf16 t3k[4][512];        // K_loc of token tile 3, fragment blocks per k-step
   bf16 t3q[4][512];        // Q_loc of token tile 3
   float nmat[4][16][kLdN]; // N of each token tile, fp32, row-major
+  float alast[kD];         // a_last of the chunk being prepared, by channel
 };
 
 struct FusedSmem {
@@ -142,6 +145,33 @@ struct FusedSmem {
 static_assert(sizeof(FusedSmem) <= 160 * 1024, "fused prefill LDS");
 
 __device__ __forceinline__ int off_pair(int I, int J) { return I * (I - 1) / 2 + J; }
+
+// Token tile I's factor rows from the four tile totals (two channels per
+// lane): 0 e^{p_I}, 1 e^{tot_I}, 2 e^{G_C - p_{I+1}}, and the scales of the
+// non-adjacent pair operands built from that tile (tile 0: 3 e^{tot_1} for
+// B_20, 4 e^{tot_1 + tot_2} for B_30; tile 1: 3 e^{tot_2} for B_31); with
+// tile 0 also a_last by channel.  I is wave-uniform.
+__device__ __forceinline__ void tile_factors(PrepScratch &P, int I, int lane) {
+  const int c0 = 2 * lane;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int c = c0 + e;
+    const float t0 = P.tot[0][c], t1 = P.tot[1][c], t2 = P.tot[2][c], t3 = P.tot[3][c];
+    const float pI = I == 0 ? 0.f : (I == 1 ? t0 : (I == 2 ? t0 + t1 : t0 + t1 + t2));
+    const float tI = I == 0 ? t0 : (I == 1 ? t1 : (I == 2 ? t2 : t3));
+    const float gC = t0 + t1 + t2 + t3;
+    P.fac[I][0][c] = __builtin_amdgcn_exp2f(pI);           // e^{p_I} <= 1
+    P.fac[I][1][c] = __builtin_amdgcn_exp2f(tI);           // e^{tot_I} in [e^-80, 1]
+    P.fac[I][2][c] = __builtin_amdgcn_exp2f(gC - pI - tI); // e^{G_C - p_{I+1}} <= 1
+    if (I == 0) {
+      P.fac[0][3][c] = __builtin_amdgcn_exp2f(t1);
+      P.fac[0][4][c] = __builtin_amdgcn_exp2f(t1 + t2);
+      P.alast[c] = __builtin_amdgcn_exp2f(gC);
+    }
+    if (I == 1)
+      P.fac[1][3][c] = __builtin_amdgcn_exp2f(t2);
+  }
+}
 
 // LDS synchronisation, written out: the compiler's own fences and barriers
 // would also wait for the LDS DMA of the next chunk's v that each state wave
@@ -580,6 +610,11 @@ __device__ __forceinline__ void fused_body(
         // previous chunk's
         lds_wait(&sm.m_done, 4 * step);
         *reinterpret_cast<bf16x4 *>(&sm.a.dn[wv][ln * 4]) = pack4(-Y);
+        // the next chunk's factor rows of token tile wv, once every tile
+        // total is in (the prep waves' meeting): work the prep waves' path,
+        // the longer one, would otherwise end with
+        lds_wait(&sm.meet, 4 * (step + 2));
+        tile_factors(sm.ps, wv, ln);
       }
       lds_sync();
     }
@@ -707,34 +742,6 @@ __device__ __forceinline__ void fused_body(
         }
       }
     };
-    // this wave's factor rows from the four tile totals (two channels per
-    // lane): 0 e^{p_I}, 1 e^{tot_I}, 2 e^{G_C - p_{I+1}}, and the scales of
-    // the non-adjacent pair operands it writes (tile 0: 3 e^{tot_1} for
-    // B_20, 4 e^{tot_1 + tot_2} for B_30; tile 1: 3 e^{tot_2} for B_31);
-    // tile 0 also keeps a_last of its two channels
-    float alr[2] = {1.f, 1.f};
-    auto factors = [&]() {
-      const int c0 = 2 * opaque_lane();
-      PrepScratch &P = sm.ps;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int c = c0 + e;
-        const float t0 = P.tot[0][c], t1 = P.tot[1][c], t2 = P.tot[2][c], t3 = P.tot[3][c];
-        const float pI = I == 0 ? 0.f : (I == 1 ? t0 : (I == 2 ? t0 + t1 : t0 + t1 + t2));
-        const float tI = I == 0 ? t0 : (I == 1 ? t1 : (I == 2 ? t2 : t3));
-        const float gC = t0 + t1 + t2 + t3;
-        P.fac[I][0][c] = __builtin_amdgcn_exp2f(pI);           // e^{p_I} <= 1
-        P.fac[I][1][c] = __builtin_amdgcn_exp2f(tI);           // e^{tot_I} in [e^-80, 1]
-        P.fac[I][2][c] = __builtin_amdgcn_exp2f(gC - pI - tI); // e^{G_C - p_{I+1}} <= 1
-        if (I == 0) {
-          P.fac[0][3][c] = __builtin_amdgcn_exp2f(t1);
-          P.fac[0][4][c] = __builtin_amdgcn_exp2f(t1 + t2);
-          alr[e] = __builtin_amdgcn_exp2f(gC);
-        }
-        if (I == 1)
-          P.fac[1][3][c] = __builtin_amdgcn_exp2f(t2);
-      }
-    };
     // selection matrices for K_restore^T: B operand h picks channels
     // 16 h .. 16 h + 15 of a 32-channel k-step (lane (n, lg), element j: 1
     // where 8 lg + j == 16 h + n; bf16 1.0 = 0x3f80)
@@ -781,7 +788,7 @@ __device__ __forceinline__ void fused_body(
     meet += 4;
     lds_signal(&sm.meet);
     lds_wait(&sm.meet, meet);
-    factors();
+    tile_factors(sm.ps, I, opaque_lane());
 
     for (int step = 0; step <= nch; ++step) {
       if (step < nch) {
@@ -791,8 +798,8 @@ __device__ __forceinline__ void fused_body(
         const int lane = opaque_lane(), lr = lane & 15, lg = lane >> 4;
         const unsigned short rb_next = load_beta(step + 1);
         if (I == 0) {
-          B.al[kperm_inv(2 * lane)] = alr[0];
-          B.al[kperm_inv(2 * lane + 1)] = alr[1];
+          B.al[kperm_inv(2 * lane)] = P.alast[2 * lane];
+          B.al[kperm_inv(2 * lane + 1)] = P.alast[2 * lane + 1];
         }
         // ---- elementwise: Q_loc, K_loc, K_st (tile products), Q_decay,
         // K_decay (record, written once the state waves are done with the
@@ -982,8 +989,6 @@ __device__ __forceinline__ void fused_body(
             pair(3, 2, &P.krs[2][0][0], fk, fq, brow);
           }
         }
-        // next chunk's factors (every tile total is in after the meeting)
-        factors();
       }
       lds_sync();
     }
