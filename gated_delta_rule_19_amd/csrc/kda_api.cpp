@@ -37,10 +37,11 @@ namespace {
 constexpr int64_t kAutoMinChains = 64;
 constexpr int64_t kAutoSegments = 64;
 constexpr int64_t kAutoMinSegChunks = 4;
-// Fewest (sequence, head) chains for the fused prefill kernel, and fewest
-// (segment, head) chains of a planner split for its segment pass and replay
-// to run on the fused kernel too.
-constexpr int64_t kFusedMinChainHeads = 512;
+// Fewest (sequence, head) chains for the fused prefill kernel without a
+// split (below that the fused planner or the two kernels fill the chip
+// better), and fewest (segment, head) chains of an explicit planner split
+// for its segment pass and replay to run on the fused kernel too.
+constexpr int64_t kFusedMinChainHeads = 129;
 constexpr int64_t kFusedSplitMinChainHeads = 256;
 
 constexpr size_t kAlign = 256;
@@ -55,10 +56,12 @@ bool aligned_elt(const void *p, kda_dtype dt) {
 // chain count in [kFusedAutoMinChains, kFusedAutoMaxChains] on the automatic
 // path.  It cuts a sequence into as many segments as keep each of the fused
 // planner's two passes within one workgroup per compute unit (the first
-// pass runs (segments - 1) x chains workgroups), at least kAutoMinSegChunks
-// chunks each, and only when that gives 3 or more (two segments run one
+// pass runs (segments - 1) x chains workgroups), at least
+// kFusedMinSegChunks chunks each (shorter ones measured slower than the
+// two kernels), and only when that gives 3 or more (two segments run one
 // after the other, which the unsplit call already does).
 constexpr int64_t kFusedAutoMinChains = 8, kFusedAutoMaxChains = 128;
+constexpr int64_t kFusedMinSegChunks = 12;
 bool fused_auto_cut(int32_t num_seqs, int32_t H, size_t es, int32_t path, int32_t split_hint) {
   const int64_t chains = (int64_t)num_seqs * H;
   return es == 2 && path == KDA_PATH_AUTO && split_hint == 0 &&
@@ -76,7 +79,7 @@ int64_t plan_nseg(int64_t len, int32_t num_seqs, int32_t H, int32_t split_hint,
     return std::min<int64_t>(split_hint, nch);
   const int64_t chains = (int64_t)num_seqs * H;
   if (fused_cut) {
-    const int64_t n = std::min<int64_t>(1 + kComputeUnits / chains, nch / kAutoMinSegChunks);
+    const int64_t n = std::min<int64_t>(1 + kComputeUnits / chains, nch / kFusedMinSegChunks);
     return n >= 3 ? n : 1;
   }
   if (chains >= kAutoMinChains)

@@ -704,27 +704,33 @@ __device__ __forceinline__ void fused_body(
     // on the one just issued); lane 15 of each row writes the tile totals
     float G[4][8];
     const bool gate_on = PRO && A_log != nullptr, qk_on = PRO && qk_eps > 0.f;
-    const float ea = gate_on ? __expf(A_log[h]) : 1.f; // the head's gate scale e^{A_h}
+    // the head's gate scale e^{A_h}, with log2(e) folded into the exponent's
+    // scale and into g_min: the gated scan yields log2-unit decays directly
+    const float ea = gate_on ? __expf(A_log[h]) : 1.f;
+    const float nea2 = -ea * kLog2e, gmin2 = g_min * kLog2e;
     auto scan = [&](int ch) {
       const int ln = opaque_lane(), llr = ln & 15, llg = ln >> 4;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         widen8(rg[s], G[s]);
       if (gate_on) {
-        // the log decay from the gate logits; rows past the chunk end decay
-        // by nothing
+        // the log decay from the gate logits, g_min sigmoid(e^{A_h} z), in
+        // log2 units; rows past the chunk end decay by nothing
         const bool valid = 16 * I + llr < min(kC, cd.ntok - ch * kC);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
           for (int j = 0; j < 8; ++j)
-            G[s][j] = valid ? gate_log_decay(G[s][j], ea, g_min) : 0.f;
+            G[s][j] = valid ? gmin2 * __builtin_amdgcn_rcpf(
+                                          1.f + __builtin_amdgcn_exp2f(G[s][j] * nea2))
+                            : 0.f;
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            G[s][j] *= kLog2e;
       }
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          G[s][j] *= kLog2e;
 #pragma unroll
       for (int d = 1; d < 16; d *= 2)
 #pragma unroll

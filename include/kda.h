@@ -86,7 +86,7 @@ int32_t kda_version(void);
  *                    work would leave most compute units idle.  KDA_F32
  *                    (and KDA_BF16 outside the next case): C < 64 cuts into
  *                    min(64, chunks / 4) segments.  KDA_BF16 with
- *                    8 <= C <= 128: min(1 + 256 / C, chunks / 4) segments
+ *                    8 <= C <= 128: min(1 + 256 / C, chunks / 12) segments
  *                    when that is at least 3, else none (the fused
  *                    planner, each of its passes one workgroup per compute
  *                    unit);
@@ -120,14 +120,15 @@ int32_t kda_plan_num_segments(int64_t seq_len, int32_t num_seqs, int32_t H, int3
  * transition pairs are combined by a prefix scan and then replayed (see
  * kda_plan_num_segments and kda_segment_transition); the result is the same
  * up to fp32 rounding.
- * Two implementations compute the same result.  With KDA_BF16 and at least
- * 512 (sequence, head) pairs without a split, or at least 256 (segment,
- * head) pairs with one, a fused kernel builds each chunk's operands on chip
- * while it carries the state (with a split, in the segment pass and in the
- * replay; the workspace then holds no per-chunk operands); otherwise a
- * chunk-parallel prep kernel writes the per-chunk operands to the workspace
- * and a state-carrying kernel reads them.  kda_chunk_prefill_ex chooses
- * between them explicitly.
+ * Two implementations compute the same result.  With KDA_BF16, a fused
+ * kernel builds each chunk's operands on chip while it carries the state
+ * (the workspace then holds no per-chunk operands): without a split for at
+ * least 129 (sequence, head) pairs; with the bf16 automatic cut (8 to 128
+ * pairs, kda_plan_num_segments_dt) or an explicit split into at least 256
+ * (segment, head) pairs, in the planner's segment pass and replay.
+ * Otherwise a chunk-parallel prep kernel writes the per-chunk operands to
+ * the workspace and a state-carrying kernel reads them.
+ * kda_chunk_prefill_ex chooses between them explicitly.
  *
  *   num_seqs         : N >= 0 sequences.
  *   cu_seqlens_host  : HOST, N+1 int64, cu[0] = 0, nondecreasing.  The

@@ -56,7 +56,7 @@ def test_planner_policy(lib):
     assert nat.plan_num_segments(131072, 1, 12, 0) == 64
     # bf16: the fused planner's cut for 8 .. 128 (sequence, head) chains,
     # (segments - 1) x chains <= 256 workgroups per pass, >= 3 segments of
-    # >= 4 chunks
+    # >= 12 chunks
     bf = torch.bfloat16
     assert nat.plan_num_segments(131072, 1, 12, 0, bf) == 22
     assert nat.plan_num_segments(8192, 1, 96, 0, bf) == 3
@@ -64,6 +64,9 @@ def test_planner_policy(lib):
     assert nat.plan_num_segments(8192, 2, 64, 0, bf) == 3      # 128 chains: 256 per pass
     assert nat.plan_num_segments(8192, 1, 129, 0, bf) == 1     # above 128: 2 would be all
     assert nat.plan_num_segments(640, 1, 96, 0, bf) == 1       # 10 chunks: 2 segments
+    assert nat.plan_num_segments(64 * 35, 1, 96, 0, bf) == 1   # 35 chunks: 2 of 12
+    assert nat.plan_num_segments(64 * 36, 1, 96, 0, bf) == 3
+    assert nat.plan_num_segments(8192, 1, 16, 0, bf) == 10     # 128 chunks / 12
     assert nat.plan_num_segments(64 * 200, 1, 4, 0, bf) == 50  # below 8 chains: as fp32
     assert nat.plan_num_segments(131072, 1, 12, 5, bf) == 5    # an explicit hint rules
     assert nat.plan_num_segments(8192, 1, 96, 0) == 1
