@@ -47,8 +47,13 @@ __device__ __forceinline__ void kq_norms(int tid, const float *s_k, const float 
       pk = s_k[tid] * s_k[tid] + s_k[tid + 64] * s_k[tid + 64];
       pq = s_q[tid] * s_q[tid] + s_q[tid + 64] * s_q[tid + 64];
     }
+    p = add_xor16(add_xor32(p));
+    if (qk) {
+      pk = add_xor16(add_xor32(pk));
+      pq = add_xor16(add_xor32(pq));
+    }
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
+    for (int m = 8; m >= 1; m >>= 1) {
       p += __shfl_xor(p, m);
       if (qk) {
         pk += __shfl_xor(pk, m);
@@ -69,9 +74,9 @@ __device__ __forceinline__ void kq_norms(int tid, const float *s_k, const float 
 // the 128 and the gate.  Call once with `store` false before a barrier (the
 // per-wave sums of squares go to s_ss), then with `store` true after it.
 __device__ __forceinline__ float out_norm_sum(int tid, float x, float *s_ss) {
-  float p = x * x;
+  float p = add_xor16(add_xor32(x * x));
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1)
+  for (int m = 8; m >= 1; m >>= 1)
     p += __shfl_xor(p, m);
   if ((tid & 63) == 0)
     s_ss[tid >> 6] = p;

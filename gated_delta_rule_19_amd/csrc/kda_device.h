@@ -245,6 +245,24 @@ __device__ __forceinline__ int opaque_lane() {
   return l;
 }
 
+// x plus its value in lane ^ 32, and in lane ^ 16: the gfx950 lane swaps
+// (VALU, no LDS round trip) hand each lane its own value and its partner's,
+// and the sum is the same in both lanes (fp32 addition commutes).
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float add_xor32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const f32x2_t r = __builtin_bit_cast(
+      f32x2_t, (u32x2_t)__builtin_amdgcn_permlane32_swap(u, u, false, false));
+  return r.x + r.y;
+}
+__device__ __forceinline__ float add_xor16(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const f32x2_t r = __builtin_bit_cast(
+      f32x2_t, (u32x2_t)__builtin_amdgcn_permlane16_swap(u, u, false, false));
+  return r.x + r.y;
+}
+
 // LDS writes of this wave are complete and visible to its own later reads.
 __device__ __forceinline__ void wave_lds_fence() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");

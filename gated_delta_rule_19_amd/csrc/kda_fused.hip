@@ -494,8 +494,7 @@ __device__ __forceinline__ void fused_body(
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                   a += Ot[c][tt][i] * Ot[c][tt][i];
-              a += __shfl_xor(a, 16);
-              a += __shfl_xor(a, 32);
+              a = add_xor32(add_xor16(a));
               ss[tt] = a;
             }
             if (llg == 0) {
@@ -824,12 +823,10 @@ __device__ __forceinline__ void fused_body(
               sq = sumsq8_bf16(rq[s], sq);
             sk = sumsq8_bf16(rk[s], sk);
           }
-          sk += __shfl_xor(sk, 16);
-          sk += __shfl_xor(sk, 32);
+          sk = add_xor32(add_xor16(sk));
           ik = __builtin_amdgcn_rsqf(sk + qk_eps);
           if constexpr (kQ) {
-            sq += __shfl_xor(sq, 16);
-            sq += __shfl_xor(sq, 32);
+            sq = add_xor32(add_xor16(sq));
             iq = __builtin_amdgcn_rsqf(sq + qk_eps);
           }
         }

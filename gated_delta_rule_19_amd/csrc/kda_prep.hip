@@ -242,10 +242,8 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2)
         sq = sumsq8_bf16(rq[s], sq);
         sk = sumsq8_bf16(rk[s], sk);
       }
-      sq += __shfl_xor(sq, 16);
-      sk += __shfl_xor(sk, 16);
-      sq += __shfl_xor(sq, 32);
-      sk += __shfl_xor(sk, 32);
+      sq = add_xor32(add_xor16(sq));
+      sk = add_xor32(add_xor16(sk));
       iq = __builtin_amdgcn_rsqf(sq + qk_eps);
       ik = __builtin_amdgcn_rsqf(sk + qk_eps);
     }
