@@ -45,8 +45,9 @@
 // D^-1 blocks, which the state waves read early in a step, have one LDS
 // copy: the prep waves overwrite them only after every state wave has
 // counted itself done with the previous chunk's (LDS counters, bounded
-// waits).  K_restore^T, beta and a_last, read late, have two copies by
-// chunk parity.  The prep waves meet once per step, before the off-
+// waits).  K_restore (token-major; the state waves read it transposed with
+// gfx950's transposing LDS reads), beta and a_last, read late, have two
+// copies by chunk parity.  The prep waves meet once per step, before the off-
 // diagonal tile pairs (every tile's K_rs and tile totals written).  A
 // wave on the same SIMD as MFMA work loses VALU issue to it, so the work
 // is spread to keep each SIMD's share even rather than to keep MFMA away
@@ -113,8 +114,11 @@ struct RecOnce {     // one copy (read early in a step)
   bf16 lo[6][256];   // L_IJ, J < I, at off_pair(I, J)
   bf16 dn[4][256];   // -(I + L_II)^-1
 };
-struct RecTwice {    // two copies by chunk parity (read late in a step)
-  bf16 krt[16][512]; // K_restore^T, block 2 ct + s' (rows: state rows)
+// K_restore's row stride in LDS, in elements: 32 elements of padding put the
+// four token rows of one transposed read in different banks
+constexpr int kKrLd = kD + 32;
+struct RecTwice {      // two copies by chunk parity (read late in a step)
+  bf16 kr[kC][kKrLd];  // K_restore, token-major (channels in order)
   float beta[kC];
   float al[kD];      // a_last by state row
 };
@@ -332,6 +336,23 @@ __device__ __forceinline__ void fused_body(
         const RecTwice &B = sm.b[ch & 1];
         const int ln = opaque_lane(), llr = ln & 15, llg = ln >> 4;
         auto frag = [&](const bf16 *blk) { return load_frag(blk + ln * 8); };
+        // K_restore^T's A fragment of row tile ct, k-step ks (lane (i, g):
+        // channel kperm(16 ct + i), tokens 32 ks + 16 h + 4 g + j at element
+        // 4 h + j) from the token-major copy, by two transposed reads: in
+        // each 16-lane group, lane 4 a + b of ds_read_b64_tr_b16 receives
+        // element b of the 4-element reads of lanes a, a + 4, a + 8, a + 12,
+        // so lane L reads token 32 ks + 16 h + 4 g + L / 4 from channel
+        // kperm(16 ct + 4 (L % 4)) on (kperm keeps runs of four channels)
+        auto kr_frag = [&](const bf16 *kr, int ct, int ks) {
+          typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+          const bf16 *p0 =
+              kr + (32 * ks + 4 * llg + (llr >> 2)) * kKrLd + kperm(16 * ct + 4 * (llr & 3));
+          const bf16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p0);
+          const bf16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p0 + 16 * kKrLd));
+          Frag<bf16> f;
+          f.v = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+          return f;
+        };
         // W = K_decay S and O^T = S^T Q_decay^T (K = channels; the packed
         // state is the B operand of the first and the A operand of the second),
         // then U by substitution.  MODE 1 runs W, the right-hand side and the
@@ -555,7 +576,7 @@ __device__ __forceinline__ void fused_body(
             Frag<bf16> ar[4];
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
-              ar[ct] = frag(&B.krt[2 * (4 * hf + ct) + s][0]);
+              ar[ct] = kr_frag(&B.kr[0][0], 4 * hf + ct, s);
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
@@ -747,21 +768,6 @@ __device__ __forceinline__ void fused_body(
         }
       }
     };
-    // selection matrices for K_restore^T: B operand h picks channels
-    // 16 h .. 16 h + 15 of a 32-channel k-step (lane (n, lg), element j: 1
-    // where 8 lg + j == 16 h + n; bf16 1.0 = 0x3f80)
-    auto selection = [&](int hsel) {
-      const int ln = opaque_lane(), llr = ln & 15, llg = ln >> 4;
-      const int kk = 16 * hsel + llr - 8 * llg;
-      const unsigned one = 0x3f80u << (16 * (kk & 1));
-      u32x4 w;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-        w[d] = (kk >= 0 && kk < 8 && (kk >> 1) == d) ? one : 0u;
-      Frag<bf16> f;
-      f.v = __builtin_bit_cast(bf16x8, w);
-      return f;
-    };
     // the off-diagonal pair (Ip, J): L_IJ = Diag(beta_I) K_loc,I B_IJ^T and
     // M_IJ = Q_loc,I B_IJ^T from the B_IJ fragment blocks and tile Ip's
     // K_loc / Q_loc fragments (lane (lr, lg): row 16 Ip + lr, token
@@ -810,7 +816,7 @@ __device__ __forceinline__ void fused_body(
         // K_decay (record, written once the state waves are done with the
         // previous chunk's), K_rs and the scaled pair operands, K_restore
         // (transposed into the record); the diagonal tile's products ----
-        Frag<bf16> fq[4], fk[4], fs[4], fre[4];
+        Frag<bf16> fq[4], fk[4], fs[4];
         bf16x8 pq[4], pk[4];
         f32x4 accLc = {0.f, 0.f, 0.f, 0.f}, accMr = accLc;
         float iq = 1.f, ik = 1.f; // 1 / |q|, 1 / |k| of this lane's token
@@ -874,7 +880,9 @@ __device__ __forceinline__ void fused_body(
           }
           fk[s] = pack8(xk);
           fs[s] = pack8(xs);
-          fre[s] = pack8(yre);
+          // K_restore into this chunk's token-major copy (the state waves
+          // read it transposed)
+          *reinterpret_cast<bf16x8 *>(&B.kr[16 * I + lr][32 * s + 8 * lg]) = pack8(yre).v;
           pk[s] = pack8(yk).v;
           // diagonal tile: L_II in the column layout; M_II swapped, in the
           // row layout (row r = lr)
@@ -926,29 +934,6 @@ __device__ __forceinline__ void fused_body(
           *reinterpret_cast<bf16x8 *>(&A.kd[4 * I + s][lane * 8]) = pk[s];
         }
         issue_qk(step + 1);
-        {
-          // K_restore^T: the selection products give lane (n, lg) channel
-          // 32 s + 16 hs + n of tokens 16 I + 4 lg .. + 3, which go to state
-          // row p = kperm_inv(channel), k-step I / 2, positions 4 (I % 2) ..
-          const Frag<bf16> sel0 = selection(0), sel1 = selection(1);
-          f32x4 tr[4][2];
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int hs = 0; hs < 2; ++hs) {
-              tr[s][hs] = f32x4{0.f, 0.f, 0.f, 0.f};
-              mma(tr[s][hs], fre[s], hs ? sel1 : sel0);
-            }
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int hs = 0; hs < 2; ++hs) {
-              const int p = kperm_inv(32 * s + 16 * hs + lr);
-              *reinterpret_cast<bf16x4 *>(
-                  &B.krt[2 * (p >> 4) + (I >> 1)][((lg << 4) + (p & 15)) * 8 + 4 * (I & 1)]) =
-                  pack4(tr[s][hs]);
-            }
-        }
         // next chunk's tile scan (its g was loaded a step ago)
         scan(step + 1);
         issue_g(step + 2);
