@@ -815,7 +815,8 @@ __device__ __forceinline__ void fused_body(
         // ---- elementwise: Q_loc, K_loc, K_st (tile products), Q_decay,
         // K_decay (record, written once the state waves are done with the
         // previous chunk's), K_rs and the scaled pair operands, K_restore
-        // (transposed into the record); the diagonal tile's products ----
+        // (token-major; the state waves read it transposed); the diagonal
+        // tile's products ----
         Frag<bf16> fq[4], fk[4], fs[4];
         bf16x8 pq[4], pk[4];
         f32x4 accLc = {0.f, 0.f, 0.f, 0.f}, accMr = accLc;
