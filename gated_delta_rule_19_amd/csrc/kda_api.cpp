@@ -207,7 +207,8 @@ void assign_ckpts(ChainDesc &c, const SeqCkpts &k, int64_t s0, int64_t cnt, int6
 bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_hint,
                         bool has_init, bool has_final, size_t es, Plan &p,
                         const int64_t *pos0 = nullptr, int64_t align = 0,
-                        bool all_ckpts = false, int32_t path = KDA_PATH_AUTO) {
+                        bool all_ckpts = false, int32_t path = KDA_PATH_AUTO,
+                        bool layer_steps = false) {
   int64_t ckpt_base = 0; // first checkpoint index of the current sequence
   if (!cu || cu[0] != 0)
     return false;
@@ -265,11 +266,28 @@ bool build_prefill_plan(int32_t N, const int64_t *cu, int32_t H, int32_t split_h
       assign_ckpts(p.chains.back(), ck, 0, nch, idx0);
       continue;
     }
-    // chunk-aligned segments of near-equal length; on the fused planner the
-    // first one is about 7/8 of the others (its workgroups carry the state
-    // and o, the slower of the first pass's two kinds)
-    const int64_t first = p.fused_split ? std::max<int64_t>(1, nch * 7 / (7 + 8 * (nseg - 1)))
-                                        : -1;
+    // chunk-aligned segments of near-equal length.  On the fused planner the
+    // first pass takes max(first, rho x the longest middle segment) chunk
+    // steps and the replay the longest later segment, where rho is a
+    // segment-pass step's cost over that of a step that carries the state
+    // and o: about 0.9, and 0.83 with the layer steps on (the output norm
+    // and gate run in the latter only).  The first segment's length
+    // minimises the sum of the two passes (the shortest of the ties).  The
+    // lengths do not change the workspace layout.
+    int64_t first = -1;
+    if (p.fused_split) {
+      const double rho = layer_steps ? 0.83 : 0.9;
+      double best = 0.0;
+      for (int64_t f = 1; f + nseg - 1 <= nch; ++f) {
+        const int64_t qm = (nch - f + nseg - 2) / (nseg - 1);
+        const double c = std::max(static_cast<double>(f), rho * static_cast<double>(qm)) +
+                         static_cast<double>(qm);
+        if (first < 0 || c < best - 1e-9) {
+          best = c;
+          first = f;
+        }
+      }
+    }
     const int64_t rest = p.fused_split ? nch - first : nch, nrest = p.fused_split ? nseg - 1 : nseg;
     const int64_t q = rest / nrest, r = rest % nrest;
     const int64_t pair0 = p.npairs, sin0 = p.nsin;
@@ -514,7 +532,7 @@ kda_status prefill_impl(int32_t num_seqs, const int64_t *cu_seqlens_host, int32_
   Plan p;
   if (!build_prefill_plan(num_seqs, cu_seqlens_host, H, split_hint, initial_state != nullptr,
                           final_state != nullptr, elt_size(dt), p, pos0, ckpt_align,
-                          all_ckpts, path))
+                          all_ckpts, path, pro.on() || epi.on()))
     return KDA_ERR_INVALID_ARG;
   if (p.path_unsupported)
     return KDA_ERR_UNSUPPORTED;

@@ -119,10 +119,8 @@ struct RecOnce {     // one copy (read early in a step)
 constexpr int kKrLd = kD + 32;
 struct RecTwice {      // two copies by chunk parity (read late in a step)
   bf16 kr[kC][kKrLd];  // K_restore, token-major (channels in order)
-  float beta[kC];      // beta, with the k norm: beta / |k|^2 (below)
-  float beta2[kC];     // with the k norm: beta / |k|
-  float iq[kC];        // with the q norm: 1 / |q|
-  float al[kD];        // a_last by state row
+  float beta[kC];
+  float al[kD];      // a_last by state row
 };
 
 struct PrepScratch {
@@ -257,7 +255,6 @@ __device__ __forceinline__ void fused_body(
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t rowstride = (int64_t)H * kD;
   const int nch = (cd.ntok + kC - 1) / kC;
-  const bool qk_on = PRO && qk_eps > 0.f; // L2 norm of q and k (wave-uniform)
 
   // M_qk blocks (and halves) above the diagonal are zero and never written
   // again; the counters start at 0
@@ -427,9 +424,6 @@ __device__ __forceinline__ void fused_body(
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) {
             const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&B.beta[16 * tt + 4 * llg]);
-            // with the k norm folded in: beta / |k|^2 on W, beta / |k| on V
-            const f32x4 bv = qk_on ? *reinterpret_cast<const f32x4 *>(&B.beta2[16 * tt + 4 * llg])
-                                   : b4;
 #pragma unroll
             for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -438,7 +432,7 @@ __device__ __forceinline__ void fused_body(
                     hv == 1 ? 0.f
                             : static_cast<float>(*reinterpret_cast<const bf16 *>(
                                   vs + vst_off(16 * tt + 4 * llg + i, 16 * c + llr)));
-                W[c][tt][i] = PRO ? b4[i] * W[c][tt][i] - bv[i] * vv : b4[i] * (W[c][tt][i] - vv);
+                W[c][tt][i] = b4[i] * (W[c][tt][i] - vv);
               }
           }
           if (hv == 0) {
@@ -539,11 +533,8 @@ __device__ __forceinline__ void fused_body(
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
               const int t = 16 * tt + llr;
-              // o = o' / |q| (q raw in the chunk's operands)
-              const float iqt = qk_on ? B.iq[t] : 1.f;
-              const float rs = iqt * __builtin_amdgcn_rsqf(
-                  (sm.ored[0][t] + sm.ored[1][t] + sm.ored[2][t] + sm.ored[3][t]) *
-                      (iqt * iqt * (1.f / kD)) +
+              const float rs = __builtin_amdgcn_rsqf(
+                  (sm.ored[0][t] + sm.ored[1][t] + sm.ored[2][t] + sm.ored[3][t]) * (1.f / kD) +
                   oeps);
 #pragma unroll
               for (int c = 0; c < 2; ++c) {
@@ -557,16 +548,6 @@ __device__ __forceinline__ void fused_body(
                   Ot[c][tt][i] *= rs * wn[c][i] *
                                   __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z[i] * kLog2e));
               }
-            }
-          }
-          if (!EPI && qk_on) {
-            // o = o' / |q| (q raw in the chunk's operands)
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-              const float iqt = B.iq[16 * tt + llr];
-#pragma unroll
-              for (int c = 0; c < 2; ++c)
-                Ot[c][tt] *= iqt;
             }
           }
 #pragma unroll
@@ -742,7 +723,7 @@ __device__ __forceinline__ void fused_body(
     // the tile, level by level over all 32 values so that no DPP step waits
     // on the one just issued); lane 15 of each row writes the tile totals
     float G[4][8];
-    const bool gate_on = PRO && A_log != nullptr;
+    const bool gate_on = PRO && A_log != nullptr, qk_on = PRO && qk_eps > 0.f;
     // the head's gate scale e^{A_h}, with log2(e) folded into the exponent's
     // scale and into g_min: the gated scan yields log2-unit decays directly
     const float ea = gate_on ? __expf(A_log[h]) : 1.f;
@@ -855,16 +836,6 @@ __device__ __forceinline__ void fused_body(
             sq = add_xor32(add_xor16(sq));
             iq = __builtin_amdgcn_rsqf(sq + qk_eps);
           }
-          // q and k stay raw: with k = k' / |k'| the recurrence equals the
-          // one over k' with beta' = beta / |k'|^2 and v' = v / |k'| (so
-          // the right-hand side becomes beta' W' - (beta / |k'|) V), and o
-          // is linear in q (its rows are scaled by 1 / |q| where stored)
-          if (lg == 0) {
-            const float b = B.beta[16 * I + lr];
-            B.beta[16 * I + lr] = b * ik * ik;
-            B.beta2[16 * I + lr] = b * ik;
-            B.iq[16 * I + lr] = iq;
-          }
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -886,6 +857,13 @@ __device__ __forceinline__ void fused_body(
               qv[j] = 0.f;
           }
           widen8(rk[s], kv);
+          if (qk_on) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              qv[j] *= iq;
+              kv[j] *= ik;
+            }
+          }
           float xq[8], xk[8], xs[8], yq[8], yk[8], yr[8], yre[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
